@@ -1,0 +1,219 @@
+"""Oracle attention (test infrastructure only; see the package docstring).
+
+Prefill ([TriAttention] abstract: the fused kernel skips omitted tiles and
+combines both QK precisions into one normalized attention output; [TileMix]
+abstract: FP16 and INT8 tile paths update one shared online-softmax state).
+An online softmax over any order of the executed tiles reaches, in exact
+arithmetic, the plain softmax over each row's executed key set, so that is what
+is computed here, row by row, in float64:
+
+* executed keys of row r (sequence-relative): c <= r whose tile is not SKIP;
+* INT8 / INT4 tile: a = sum_d cq[r, d] * ck[c, d] (exact integers),
+  score = a * sq(block of r) * sk(block of c) * tau;
+* FP16 tile: score = tau * sum_d q[r, d] * k[c, d] on the 16-bit values;
+* m = max score, p = exp(score - m), l = sum p, O_r = sum_c (p / l) v_c with the
+  unquantized 16-bit V; lse_r = m + ln l.
+
+tau = 1/sqrt(d) unless given.  Query head h reads key/value head h // (hq/hkv)
+(grouped-query attention, [TileMix] abstract).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import policy as P
+from .quant import BLOCK
+
+
+def _tau(d, tau):
+    return 1.0 / math.sqrt(d) if tau is None else float(tau)
+
+
+def _rows_scores(r0, r1, h, kv, tok0, grid_h, bq, bk, q64, k64, qq, kq, blk0, tau):
+    """Scores [r1-r0][r1] (float64, -inf where not executed) for sequence rows
+    r0..r1-1 of query head h; keys 0..r1-1 of the sequence."""
+    nrow, nkey = r1 - r0, r1
+    rows = np.arange(r0, r1)
+    keys = np.arange(nkey)
+    prec = grid_h[(rows // bq)[:, None], (keys // bk)[None, :]]           # [nrow][nkey]
+    S = np.full((nrow, nkey), -np.inf)
+    causal = keys[None, :] <= rows[:, None]
+    qb = blk0 + rows // BLOCK
+    kb = blk0 + keys // BLOCK
+    for pr, cq, ck, sq, sk in (
+        (P.INT8, qq["c8"], kq["c8"], qq["s8"], kq["s8"]),
+        (P.INT4, qq["c4"], kq["c4"], qq["s4"], kq["s4"]),
+    ):
+        sel = (prec == pr) & causal
+        if not sel.any():
+            continue
+        a = cq[h, qb, rows % BLOCK].astype(np.float64) @ ck[kv, kb, keys % BLOCK].astype(np.float64).T
+        sc = a * sq[h, qb].astype(np.float64)[:, None] * sk[kv, kb].astype(np.float64)[None, :] * tau
+        S = np.where(sel, sc, S)
+    sel = (prec == P.FP16) & causal
+    if sel.any():
+        sc = tau * (q64[tok0 + rows, h] @ k64[tok0 + keys, kv].T)
+        S = np.where(sel, sc, S)
+    return S
+
+
+def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
+            rows=None, return_p=False):
+    """Oracle prefill output.
+
+    q64 [T][hq][d], k64/v64 [T][hkv][d]: float64 copies of the 16-bit inputs.
+    qq, kq: oracle quantizer outputs (rows layout) for Q and K.
+    rows: None for every row, else an iterable of (seq, head, row) triples.
+    Returns (O, lse) with O [T][hq][d] and lse [hq][T] (NaN where not computed),
+    plus the list of probability rows when return_p is set.
+    """
+    tau = _tau(d, tau)
+    T = int(np.sum(seqlens))
+    grp = hq // hkv
+    O = np.full((T, hq, d), np.nan)
+    lse = np.full((hq, T), np.nan)
+    gs = P.grids(seqlens, hq, bq, bk, pol)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    plist = []
+    if rows is None:
+        work = [(s, h, None) for s in range(len(seqlens)) for h in range(hq)]
+    else:
+        by = {}
+        for s, h, r in rows:
+            by.setdefault((s, h), []).append(int(r))
+        work = [(s, h, sorted(set(rs))) for (s, h), rs in sorted(by.items())]
+    for s, h, rlist in work:
+        S_len = int(seqlens[s])
+        tok0 = int(cu[s])
+        kv = h // grp
+        blk0 = int(qq["blk_start"][s])
+        assert int(kq["blk_start"][s]) == blk0
+        g = gs[s][h]
+        chunks = ([(i * bq, min((i + 1) * bq, S_len)) for i in range(P.n_tiles(S_len, bq))]
+                  if rlist is None else [(r, r + 1) for r in rlist])
+        for r0, r1 in chunks:
+            Sc = _rows_scores(r0, r1, h, kv, tok0, g, bq, bk, q64, k64, qq, kq, blk0, tau)
+            m = np.max(Sc, axis=1)
+            assert np.all(np.isfinite(m)), "a row with no executed key"
+            p = np.exp(Sc - m[:, None])
+            l = np.sum(p, axis=1)
+            O[tok0 + r0:tok0 + r1, h] = (p / l[:, None]) @ v64[tok0:tok0 + r1, kv]
+            lse[h, tok0 + r0:tok0 + r1] = m + np.log(l)
+            if return_p:
+                plist.append(((s, h, r0, r1), p / l[:, None]))
+    if return_p:
+        return O, lse, plist
+    return O, lse
+
+
+def int_tile_scores(qq, kq, seq, head, kv, qtile, ktile, bq, bk, prec, seqlens):
+    """Exact integer QK scores of one INT8 or INT4 tile: int64 [bq][bk].
+
+    Rows/keys past the sequence end read the zero padding codes.  Entries above
+    the diagonal are included (the integer product is defined for the whole
+    tile; masking happens after scaling)."""
+    blk0 = int(qq["blk_start"][seq])
+    nb = -(-int(seqlens[seq]) // BLOCK)
+    c_q = qq["c8"] if prec == P.INT8 else qq["c4"]
+    c_k = kq["c8"] if prec == P.INT8 else kq["c4"]
+    d = c_q.shape[-1]
+
+    def rows_of(c, hh, first, n):
+        out = np.zeros((n, d), np.int64)
+        for t in range(n):
+            r = first + t
+            b = r // BLOCK
+            if b < nb:
+                out[t] = c[hh, blk0 + b, r % BLOCK]
+        return out
+
+    A = rows_of(c_q, head, qtile * bq, bq)
+    B = rows_of(c_k, kv, ktile * bk, bk)
+    out = np.zeros((bq, bk), np.int64)
+    for r in range(bq):
+        for c in range(bk):
+            out[r, c] = int(np.dot(A[r], B[c]))
+    return out
+
+
+def prefill_unquantized(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, tau=None,
+                        rows=None, dense=False):
+    """Error reference (reported, not gated): the same attention with every
+    executed tile computed on the unquantized values; with ``dense`` set, plain
+    causal attention with nothing skipped."""
+    tau = _tau(d, tau)
+    grp = hq // hkv
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    gs = P.grids(seqlens, hq, bq, bk, pol)
+    T = int(cu[-1])
+    O = np.full((T, hq, d), np.nan)
+    if rows is None:
+        rows = [(s, h, r) for s in range(len(seqlens)) for h in range(hq) for r in range(int(seqlens[s]))]
+    for s, h, r in rows:
+        tok0 = int(cu[s])
+        kv = h // grp
+        keys = np.arange(r + 1)
+        sc = tau * (k64[tok0 + keys, kv] @ q64[tok0 + r, h])
+        if not dense:
+            prec = gs[s][h][r // bq, keys // bk]
+            sc = np.where(prec == P.SKIP, -np.inf, sc)
+        m = np.max(sc)
+        p = np.exp(sc - m)
+        O[tok0 + r, h] = (p / p.sum()) @ v64[tok0 + keys, kv]
+    return O
+
+
+def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_tags=False):
+    """Oracle decode: one new query per sequence over its compressed cache.
+
+    seqlens: cache length L_b per sequence (the cache includes the new token);
+    q64 [B][hq][d]; kq: K quantized (rows layout), vq: V quantized (any layout:
+    the unpacked rows-layout codes are used); k64/v64 [T][hkv][d] hold the
+    16-bit cache values read for FP16 blocks.
+    Block tags follow policy.decode_block_tags with per-KV-head (b8, b4).
+    INT blocks: score = tau * sk * (q . ck), value = sv * cv; FP16 blocks:
+    score = tau * (q . k), value = v.  Returns O [B][hq][d].
+    """
+    tau = _tau(d, tau)
+    grp = hq // hkv
+    B = len(seqlens)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    O = np.zeros((B, hq, d))
+    tags_all = {}
+    for b in range(B):
+        L = int(seqlens[b])
+        blk0 = int(kq["blk_start"][b])
+        for h in range(hq):
+            kv = h // grp
+            tags = P.decode_block_tags(L, int(dpol["b8"][kv]), int(dpol["b4"][kv]),
+                                       int(dpol["sink"]), int(dpol["tail"]))
+            tags_all[(b, kv)] = tags
+            sc_list, val_list = [], []
+            for j, t in enumerate(tags):
+                n = min(BLOCK, L - j * BLOCK)
+                if t == P.SKIP:
+                    continue
+                if t == P.FP16:
+                    kk = k64[cu[b] + j * BLOCK: cu[b] + j * BLOCK + n, kv]
+                    vv = v64[cu[b] + j * BLOCK: cu[b] + j * BLOCK + n, kv]
+                    sc_list.append(tau * (kk @ q64[b, h]))
+                    val_list.append(vv)
+                else:
+                    ck = kq["c8"] if t == P.INT8 else kq["c4"]
+                    cv = vq["c8"] if t == P.INT8 else vq["c4"]
+                    sk = kq["s8"] if t == P.INT8 else kq["s4"]
+                    sv = vq["s8"] if t == P.INT8 else vq["s4"]
+                    kc = ck[kv, blk0 + j, :n].astype(np.float64)
+                    vc = cv[kv, blk0 + j, :n].astype(np.float64)
+                    sc_list.append(tau * float(sk[kv, blk0 + j]) * (kc @ q64[b, h]))
+                    val_list.append(float(sv[kv, blk0 + j]) * vc)
+            sc = np.concatenate(sc_list)
+            vals = np.concatenate(val_list, axis=0)
+            m = np.max(sc)
+            p = np.exp(sc - m)
+            O[b, h] = (p / p.sum()) @ vals
+    if return_tags:
+        return O, tags_all
+    return O

@@ -1,0 +1,179 @@
+"""Oracle tile-precision policy (test infrastructure only; see the package docstring).
+
+Sources:
+* [TriAttention] abstract: each query-key tile goes to skip, 4-bit or 8-bit
+  computation; each head's regions are encoded by two diagonal-distance
+  boundaries (storage independent of context length); the boundaries expand
+  into precision-grouped traversals and omitted tiles are skipped.
+* [TileMix] abstract: the score matrix is split into hardware-aligned tiles;
+  routing decisions are packed into compact bitmasks; one routing bit governs a
+  group of adjacent key tiles; each group runs FP16 or INT8 score computation;
+  all legal tile groups are routed (no skip); grouped-query attention and
+  variable-length batches are supported.
+
+Readings taken where the pages are silent:
+* tiles restart at each sequence start; tile (i, j) covers query rows
+  [i*bq, (i+1)*bq) and keys [j*bk, (j+1)*bk) of the sequence; it is legal iff
+  its first key is causally visible from its last valid row:
+  j*bk <= min((i+1)*bq, S) - 1;
+* diagonal distance in key-tile units from the query tile's first row, clipped
+  at zero: delta(i, j) = max(0, floor((i*bq - j*bk) / bk));
+* boundaries (b8, b4) per query head, 0 <= b8 <= b4: delta < b8 -> INT8,
+  b8 <= delta < b4 -> INT4, delta >= b4 -> SKIP; with ``sink`` set, key tile 0
+  is INT8 for every query tile;
+* bitmask: bit = 1 -> FP16, 0 -> INT8; group g covers key tiles
+  [g*G, (g+1)*G); each (sequence, query head, query tile) row holds
+  ceil(ceil(nk / G) / 32) uint32 words, LSB-first; rows are laid out
+  sequence-major, then head, then query tile; the legal tiles of a partly
+  legal group take the group's bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SKIP, INT4, INT8, FP16 = 0, 1, 2, 3
+ILLEGAL = -1
+
+
+def n_tiles(S: int, b: int) -> int:
+    return -(-int(S) // int(b))
+
+
+def is_legal(i: int, j: int, S: int, bq: int, bk: int) -> bool:
+    return j * bk <= min((i + 1) * bq, S) - 1
+
+
+def diag_distance(i: int, j: int, bq: int, bk: int) -> int:
+    return max(0, (i * bq - j * bk) // bk)
+
+
+def boundary_prec(i: int, j: int, bq: int, bk: int, b8: int, b4: int, sink: int) -> int:
+    if sink and j == 0:
+        return INT8
+    dl = diag_distance(i, j, bq, bk)
+    if dl < b8:
+        return INT8
+    if dl < b4:
+        return INT4
+    return SKIP
+
+
+def bitmask_words_per_row(S: int, bk: int, group: int) -> int:
+    ng = n_tiles(n_tiles(S, bk), group)
+    return n_tiles(ng, 32)
+
+
+def bitmask_row_base(seqlens, hq: int, bq: int, bk: int, group: int):
+    """Word offset of row (s, h=0, i=0) for each sequence, and the total."""
+    bases, acc = [], 0
+    for S in seqlens:
+        bases.append(acc)
+        acc += hq * n_tiles(S, bq) * bitmask_words_per_row(S, bk, group)
+    return bases, acc
+
+
+def bitmask_bit(words: np.ndarray, row_off: int, g: int) -> int:
+    return int((int(words[row_off + g // 32]) >> (g % 32)) & 1)
+
+
+def precision_grid_loop(S, bq, bk, head, pol, seq=0, seqlens=None, hq=None):
+    """Brute force over every (i, j) with plain Python loops: [nq][nk] int8."""
+    nq, nk = n_tiles(S, bq), n_tiles(S, bk)
+    g = np.full((nq, nk), ILLEGAL, np.int8)
+    if pol["kind"] == 1:
+        bases, _ = bitmask_row_base(seqlens, hq, bq, bk, pol["group"])
+        wpr = bitmask_words_per_row(S, bk, pol["group"])
+    for i in range(nq):
+        for j in range(nk):
+            if not is_legal(i, j, S, bq, bk):
+                continue
+            if pol["kind"] == 0:
+                g[i, j] = boundary_prec(i, j, bq, bk, int(pol["b8"][head]), int(pol["b4"][head]),
+                                        int(pol["sink"]))
+            else:
+                row = bases[seq] + (head * nq + i) * wpr
+                g[i, j] = FP16 if bitmask_bit(pol["words"], row, j // pol["group"]) else INT8
+    return g
+
+
+def precision_grid(S, bq, bk, head, pol, seq=0, seqlens=None, hq=None):
+    """Same map as precision_grid_loop, with the loops vectorized by numpy."""
+    nq, nk = n_tiles(S, bq), n_tiles(S, bk)
+    i = np.arange(nq)[:, None]
+    j = np.arange(nk)[None, :]
+    legal = j * bk <= np.minimum((i + 1) * bq, S) - 1
+    if pol["kind"] == 0:
+        dl = np.maximum(0, (i * bq - j * bk) // bk)
+        b8, b4 = int(pol["b8"][head]), int(pol["b4"][head])
+        p = np.where(dl < b8, INT8, np.where(dl < b4, INT4, SKIP))
+        if int(pol["sink"]):
+            p[:, 0] = INT8
+    else:
+        G = pol["group"]
+        bases, _ = bitmask_row_base(seqlens, hq, bq, bk, G)
+        wpr = bitmask_words_per_row(S, bk, G)
+        row = bases[seq] + (head * nq + np.arange(nq)) * wpr                # [nq]
+        gidx = np.arange(nk) // G                                          # [nk]
+        words = np.asarray(pol["words"], dtype=np.uint64)
+        w = words[row[:, None] + gidx[None, :] // 32]
+        bit = (w >> (gidx[None, :] % 32).astype(np.uint64)) & np.uint64(1)
+        p = np.where(bit == 1, FP16, INT8)
+    return np.where(legal, p, ILLEGAL).astype(np.int8)
+
+
+def grids(seqlens, hq, bq, bk, pol, loop=False):
+    """Precision grids for every (sequence, query head): list over sequences of
+    [hq][nq][nk] int8 arrays (ILLEGAL = -1 outside the causal region)."""
+    f = precision_grid_loop if loop else precision_grid
+    out = []
+    for s, S in enumerate(seqlens):
+        out.append(np.stack([f(int(S), bq, bk, h, pol, s, seqlens, hq) for h in range(hq)]))
+    return out
+
+
+def census(gs):
+    """Tile counts over all grids: legal, INT8, INT4, FP16, SKIP."""
+    c = dict(legal=0, int8=0, int4=0, fp16=0, skip=0)
+    for g in gs:
+        c["legal"] += int(np.sum(g != ILLEGAL))
+        c["int8"] += int(np.sum(g == INT8))
+        c["int4"] += int(np.sum(g == INT4))
+        c["fp16"] += int(np.sum(g == FP16))
+        c["skip"] += int(np.sum(g == SKIP))
+    return c
+
+
+def executed_tiles(gs):
+    """Set of (seq, head, qtile, ktile, prec) for every non-skipped legal tile."""
+    out = set()
+    for s, g in enumerate(gs):
+        h, i, j = np.nonzero((g != ILLEGAL) & (g != SKIP))
+        for a, b, c in zip(h.tolist(), i.tolist(), j.tolist()):
+            out.add((s, a, b, c, int(g[a, b, c])))
+    return out
+
+
+def decode_block_tags(L: int, b8: int, b4: int, sink: int, tail: int, block: int = 64):
+    """Precision of each 64-token block of a cache of L tokens, for the one new
+    query at position L - 1 (the cache includes the current token).
+
+    [HyQuant] section "How HyQuant works": recent tokens stay FP16 and the rest
+    is quantized, with dequantization fused into decode attention;
+    [TriAttention] abstract: the prefill codes are reused as the decode cache.
+    Reading taken: blocks overlapping the last ``tail`` tokens are FP16; every
+    other block j has distance delta = floor((L - 1) / 64) - j from the query's
+    block and is tagged by the boundary rule (INT8 below b8, INT4 below b4,
+    SKIP otherwise), with block 0 kept INT8 when ``sink`` is set.
+    """
+    nb = n_tiles(L, block)
+    tags = np.zeros(nb, np.int8)
+    last = (L - 1) // block
+    for j in range(nb):
+        if min(j * block + block, L) > L - tail:
+            tags[j] = FP16
+        elif sink and j == 0:
+            tags[j] = INT8
+        else:
+            dl = last - j
+            tags[j] = INT8 if dl < b8 else (INT4 if dl < b4 else SKIP)
+    return tags

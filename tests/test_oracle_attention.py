@@ -1,0 +1,294 @@
+"""Pins for the oracle attention (CPU only).
+
+* all-FP16 routing with nothing skipped is ordinary causal softmax attention:
+  checked against torch's scaled_dot_product_attention in float64;
+* all-INT8 (or all-INT4) routing is attention on the dequantized Q-hat, K-hat,
+  because a * sq * sk = Q-hat . K-hat exactly: checked against the same
+  library routine, with and without a skip band (boolean mask);
+* skipped tiles contribute nothing: perturbing K or V inside tiles that a
+  query tile skips leaves that query tile's rows bit-identical;
+* softmax rows sum to one; the first row of a sequence returns v_0 exactly;
+* varlen batches equal the sequences run one by one (and permute with them);
+* integer tile scores: with Q codes = 127 * unit vectors the tile product is a
+  known transposition of the K codes;
+* decode: an all-FP16 cache is one-query softmax attention (library routine);
+  an all-INT8 cache is attention on dequantized K-hat, V-hat; skipped cache
+  blocks do not matter; an FP16-everything decode equals the last row of an
+  all-FP16 prefill.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as A
+from oracle import policy as P
+from oracle import quant as Q
+
+
+def _inputs(seqlens, hq, hkv, d, seed, dtype="f16", scale_k=None):
+    rng = np.random.default_rng(seed)
+    T = sum(seqlens)
+    q = rng.standard_normal((T, hq, d)).astype(np.float32)
+    k = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    if scale_k is not None:
+        k[:, :, :4] *= scale_k
+    v = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    q = W.round16(q, dtype)[1]
+    k = W.round16(k, dtype)[1]
+    v = W.round16(v, dtype)[1]
+    return q, k, v
+
+
+def _sdpa(q, k, v, seqlens, hq, hkv, mask_fn=None, tau=None):
+    """Library causal attention per sequence, float64, GQA by repeating K/V heads."""
+    grp = hq // hkv
+    out = []
+    tok = 0
+    for s, S in enumerate(seqlens):
+        qs = torch.from_numpy(np.ascontiguousarray(q[tok:tok + S].transpose(1, 0, 2))).double()
+        ks = torch.from_numpy(np.ascontiguousarray(k[tok:tok + S].transpose(1, 0, 2))).double()
+        vs = torch.from_numpy(np.ascontiguousarray(v[tok:tok + S].transpose(1, 0, 2))).double()
+        ks = ks.repeat_interleave(grp, dim=0)
+        vs = vs.repeat_interleave(grp, dim=0)
+        if mask_fn is None:
+            o = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, is_causal=True, scale=tau)
+        else:
+            m = torch.from_numpy(mask_fn(s, S))
+            o = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, attn_mask=m, scale=tau)
+        out.append(o.numpy().transpose(1, 0, 2))
+        tok += S
+    return np.concatenate(out, axis=0)
+
+
+SEQ = [200, 77, 300]
+HQ, HKV, D = 4, 2, 64
+
+
+def _quant(q, k):
+    return Q.quantize(q, SEQ), Q.quantize(k, SEQ)
+
+
+def test_all_fp16_equals_causal_attention():
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 1)
+    qq, kq = _quant(q, k)
+    _, tot = P.bitmask_row_base(SEQ, HQ, 128, 64, 4)
+    pol = dict(kind=1, group=4, words=np.full(tot, 0xFFFFFFFF, np.uint32))
+    O, lse = A.prefill(SEQ, HQ, HKV, D, 128, 64, pol, q.astype(np.float64), k.astype(np.float64),
+                       v.astype(np.float64), qq, kq)
+    ref = _sdpa(q, k, v, SEQ, HQ, HKV)
+    assert np.max(np.abs(O - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_int_only_equals_dequantized_attention(bits):
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 2, dtype="bf16", scale_k=10.0)
+    qq, kq = _quant(q, k)
+    big = 10 ** 6
+    b8 = big if bits == 8 else 0
+    pol = dict(kind=0, b8=[b8] * HQ, b4=[big] * HQ, sink=0)
+    O, _ = A.prefill(SEQ, HQ, HKV, D, 128, 64, pol, q.astype(np.float64), k.astype(np.float64),
+                     v.astype(np.float64), qq, kq)
+    qh = Q.dequantize_rows(qq, bits, SEQ)
+    kh = Q.dequantize_rows(kq, bits, SEQ)
+    ref = _sdpa(qh, kh, v.astype(np.float64), SEQ, HQ, HKV)
+    assert np.max(np.abs(O - ref)) < 1e-12
+
+
+def test_int8_with_skip_band_equals_masked_attention():
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 3)
+    qq, kq = _quant(q, k)
+    b = [1, 2, 3, 1]
+    pol = dict(kind=0, b8=b, b4=b, sink=1)
+    O, _ = A.prefill(SEQ, HQ, HKV, D, 128, 64, pol, q.astype(np.float64), k.astype(np.float64),
+                     v.astype(np.float64), qq, kq)
+    qh = Q.dequantize_rows(qq, 8, SEQ)
+    kh = Q.dequantize_rows(kq, 8, SEQ)
+
+    def mask_fn(s, S):
+        r = np.arange(S)[:, None]
+        c = np.arange(S)[None, :]
+        m = np.zeros((HQ, S, S), bool)
+        for h in range(HQ):
+            dl = np.maximum(0, ((r // 128) * 128 - (c // 64) * 64) // 64)
+            keep = (dl < b[h]) | (c // 64 == 0)
+            m[h] = keep & (c <= r)
+        return m
+    ref = _sdpa(qh, kh, v.astype(np.float64), SEQ, HQ, HKV, mask_fn=mask_fn)
+    assert np.max(np.abs(O - ref)) < 1e-12
+
+
+def test_skipped_tiles_contribute_nothing():
+    seqlens = [640]
+    q, k, v = _inputs(seqlens, 2, 1, D, 4)
+    pol = dict(kind=0, b8=[1, 2], b4=[2, 4], sink=0)
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    qq, kq = Q.quantize(q, seqlens), Q.quantize(k, seqlens)
+    O0, _ = A.prefill(seqlens, 2, 1, D, 128, 64, pol, q64, k64, v64, qq, kq)
+    g = P.grids(seqlens, 2, 128, 64, pol)[0]
+    # key tile 0 is skipped by query tile 4 of both heads (delta = 8 >= b4)
+    assert g[0, 4, 0] == P.SKIP and g[1, 4, 0] == P.SKIP
+    k2, v2 = k.copy(), v.copy()
+    k2[0:64] = k2[0:64] * 3 + 1
+    v2[0:64] = -v2[0:64] + 5
+    kq2 = Q.quantize(k2, seqlens)
+    O1, _ = A.prefill(seqlens, 2, 1, D, 128, 64, pol, q64, k2.astype(np.float64),
+                      v2.astype(np.float64), qq, kq2)
+    rows = slice(4 * 128, 5 * 128)
+    assert np.array_equal(O0[rows], O1[rows])
+    assert not np.allclose(O0[64:128], O1[64:128])     # rows that do execute tile 0 change
+
+
+def test_rows_sum_to_one_and_first_row():
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 5)
+    qq, kq = _quant(q, k)
+    pol = dict(kind=0, b8=[1, 2, 0, 3], b4=[2, 3, 2, 3], sink=1)
+    O, lse, plist = A.prefill(SEQ, HQ, HKV, D, 128, 64, pol, q.astype(np.float64), k.astype(np.float64),
+                              v.astype(np.float64), qq, kq, return_p=True)
+    for _, p in plist:
+        assert np.allclose(p.sum(axis=1), 1.0, atol=1e-13)
+    tok = 0
+    for S in SEQ:
+        for h in range(HQ):
+            assert np.array_equal(O[tok, h], v[tok, h // 2].astype(np.float64))
+        tok += S
+
+
+def test_varlen_equals_separate_and_permutes():
+    seqlens = [130, 64, 257]
+    q, k, v = _inputs(seqlens, HQ, HKV, D, 6)
+    _, tot = P.bitmask_row_base(seqlens, HQ, 128, 64, 1)
+    words = np.random.default_rng(9).integers(0, 2 ** 32, size=tot, dtype=np.uint64).astype(np.uint32)
+    pol = dict(kind=1, group=1, words=words)
+    f64 = lambda x: x.astype(np.float64)
+    O, _ = A.prefill(seqlens, HQ, HKV, D, 128, 64, pol, f64(q), f64(k), f64(v),
+                     Q.quantize(q, seqlens), Q.quantize(k, seqlens))
+    bases, _ = P.bitmask_row_base(seqlens, HQ, 128, 64, 1)
+    tok = 0
+    outs = []
+    for s, S in enumerate(seqlens):
+        n = HQ * P.n_tiles(S, 128) * P.bitmask_words_per_row(S, 64, 1)
+        ps = dict(kind=1, group=1, words=words[bases[s]:bases[s] + n])
+        sl = slice(tok, tok + S)
+        Os, _ = A.prefill([S], HQ, HKV, D, 128, 64, ps, f64(q[sl]), f64(k[sl]), f64(v[sl]),
+                          Q.quantize(q[sl], [S]), Q.quantize(k[sl], [S]))
+        assert np.array_equal(Os, O[sl])
+        outs.append((S, sl, ps))
+        tok += S
+    # permuted batch: sequences in order 2, 0, 1
+    order = [2, 0, 1]
+    perm_len = [seqlens[i] for i in order]
+    qp = np.concatenate([q[outs[i][1]] for i in order])
+    kp = np.concatenate([k[outs[i][1]] for i in order])
+    vp = np.concatenate([v[outs[i][1]] for i in order])
+    wp = np.concatenate([outs[i][2]["words"] for i in order])
+    Op, _ = A.prefill(perm_len, HQ, HKV, D, 128, 64, dict(kind=1, group=1, words=wp), f64(qp), f64(kp),
+                      f64(vp), Q.quantize(qp, perm_len), Q.quantize(kp, perm_len))
+    assert np.array_equal(Op, np.concatenate([O[outs[i][1]] for i in order]))
+
+
+@pytest.mark.parametrize("prec", [P.INT8, P.INT4])
+def test_int_tile_scores_transposition(prec):
+    seqlens = [100, 200]
+    d, hq, hkv = 64, 2, 1
+    qmax = 127 if prec == P.INT8 else 7
+    rng = np.random.default_rng(10)
+    q = np.zeros((300, hq, d), np.float32)
+    for t in range(300):
+        r = t - (0 if t < 100 else 100)
+        q[t, :, r % d] = qmax                      # unit vector times qmax: scale 1, code qmax
+    k = rng.integers(-qmax, qmax + 1, size=(300, hkv, d)).astype(np.float32)
+    k[:, :, d - 1] = qmax                           # force amax = qmax in every block: codes = k
+    k[:, :, d - 1][::2] = -qmax
+    qq, kq = Q.quantize(q, seqlens), Q.quantize(k, seqlens)
+    for (seq, qtile, ktile) in [(0, 0, 0), (0, 0, 1), (1, 1, 0), (1, 1, 3)]:
+        a = A.int_tile_scores(qq, kq, seq, 1, 0, qtile, ktile, 128, 64, prec, seqlens)
+        S = seqlens[seq]
+        tok0 = 0 if seq == 0 else 100
+        for rr in range(128):
+            r = qtile * 128 + rr
+            for cc in range(64):
+                c = ktile * 64 + cc
+                want = 0 if (r >= S or c >= S) else qmax * int(k[tok0 + c, 0, r % d])
+                assert a[rr, cc] == want
+
+
+DQ_SEQ = [100, 1000, 700]
+
+
+def _decode_inputs(seed=12):
+    rng = np.random.default_rng(seed)
+    T = sum(DQ_SEQ)
+    k = W.round16(rng.standard_normal((T, HKV, D)).astype(np.float32), "f16")[1]
+    v = W.round16(rng.standard_normal((T, HKV, D)).astype(np.float32), "f16")[1]
+    q = W.round16(rng.standard_normal((len(DQ_SEQ), HQ, D)).astype(np.float32), "f16")[1]
+    return q, k, v
+
+
+def _sdpa_one(q, k, v):
+    """One query per (sequence, head) against all cache rows of the sequence."""
+    out = np.zeros(q.shape)
+    tok = 0
+    for b, L in enumerate(DQ_SEQ):
+        for h in range(HQ):
+            qs = torch.from_numpy(q[b, h][None, None, :]).double()
+            ks = torch.from_numpy(np.ascontiguousarray(k[tok:tok + L, h // 2]))[None].double()
+            vs = torch.from_numpy(np.ascontiguousarray(v[tok:tok + L, h // 2]))[None].double()
+            out[b, h] = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs)[0, 0].numpy()
+        tok += L
+    return out
+
+
+def test_decode_all_fp16_is_attention():
+    q, k, v = _decode_inputs()
+    kq, vq = Q.quantize(k, DQ_SEQ), Q.quantize(v, DQ_SEQ, layout="cols")
+    dpol = dict(b8=[0, 0], b4=[0, 0], sink=0, tail=10 ** 6)
+    O = A.decode(DQ_SEQ, HQ, HKV, D, q.astype(np.float64), kq, vq, k.astype(np.float64),
+                 v.astype(np.float64), dpol)
+    assert np.max(np.abs(O - _sdpa_one(q, k, v))) < 1e-12
+
+
+def test_decode_all_int8_is_dequantized_attention():
+    q, k, v = _decode_inputs(13)
+    kq, vq = Q.quantize(k, DQ_SEQ), Q.quantize(v, DQ_SEQ, layout="cols")
+    dpol = dict(b8=[10 ** 6] * 2, b4=[10 ** 6] * 2, sink=1, tail=0)
+    O = A.decode(DQ_SEQ, HQ, HKV, D, q.astype(np.float64), kq, vq, k.astype(np.float64),
+                 v.astype(np.float64), dpol)
+    kh = Q.dequantize_rows(kq, 8, DQ_SEQ)
+    vh = Q.dequantize_rows(vq, 8, DQ_SEQ)
+    assert np.max(np.abs(O - _sdpa_one(q, kh, vh))) < 1e-12
+
+
+def test_decode_skipped_blocks_do_not_matter():
+    q, k, v = _decode_inputs(14)
+    dpol = dict(b8=[2, 3], b4=[4, 5], sink=1, tail=128)
+    kq, vq = Q.quantize(k, DQ_SEQ), Q.quantize(v, DQ_SEQ, layout="cols")
+    O0, tags = A.decode(DQ_SEQ, HQ, HKV, D, q.astype(np.float64), kq, vq, k.astype(np.float64),
+                        v.astype(np.float64), dpol, return_tags=True)
+    t = tags[(1, 0)]
+    j = int(np.nonzero(t == P.SKIP)[0][0])
+    k2, v2 = k.copy(), v.copy()
+    rows = slice(100 + 64 * j, 100 + 64 * j + 64)
+    k2[rows] = 7.0
+    v2[rows] = -3.0
+    kq2, vq2 = Q.quantize(k2, DQ_SEQ), Q.quantize(v2, DQ_SEQ, layout="cols")
+    O1 = A.decode(DQ_SEQ, HQ, HKV, D, q.astype(np.float64), kq2, vq2, k2.astype(np.float64),
+                  v2.astype(np.float64), dpol)
+    assert np.array_equal(O0[1, :2], O1[1, :2])
+
+
+def test_decode_fp16_equals_last_prefill_row():
+    L = 300
+    rng = np.random.default_rng(15)
+    q = W.round16(rng.standard_normal((L, HQ, D)).astype(np.float32), "f16")[1]
+    k = W.round16(rng.standard_normal((L, HKV, D)).astype(np.float32), "f16")[1]
+    v = W.round16(rng.standard_normal((L, HKV, D)).astype(np.float32), "f16")[1]
+    _, tot = P.bitmask_row_base([L], HQ, 128, 64, 4)
+    pol = dict(kind=1, group=4, words=np.full(tot, 0xFFFFFFFF, np.uint32))
+    f64 = lambda x: x.astype(np.float64)
+    Op, _ = A.prefill([L], HQ, HKV, D, 128, 64, pol, f64(q), f64(k), f64(v),
+                      Q.quantize(q, [L]), Q.quantize(k, [L]), rows=[(0, h, L - 1) for h in range(HQ)])
+    dpol = dict(b8=[0, 0], b4=[0, 0], sink=0, tail=L)
+    Od = A.decode([L], HQ, HKV, D, f64(q[L - 1:L]), Q.quantize(k, [L]), Q.quantize(v, [L], layout="cols"),
+                  f64(k), f64(v), dpol)
+    assert np.max(np.abs(Od[0] - Op[L - 1])) < 1e-13
