@@ -1,0 +1,270 @@
+/*
+ * tm.h -- C ABI of the tile-routed mixed-precision causal attention library
+ * (libtm.so, HIP for gfx950 / MI355X).
+ *
+ * What it computes.  Causal prefill attention in which every query-key score
+ * tile is routed to SKIP, INT4, INT8 or FP16 computation by a compact per-head
+ * policy, with every executed tile updating one shared online-softmax state;
+ * and the decode step that reuses the quantized K/V produced for prefill as a
+ * compressed cache.  Sources (the method pages):
+ *   [TriAttention] "TriAttention: Unified Sparse Mixed-Precision Attention for
+ *     Long-Context LLM Inference", abstract: skip / 4-bit / 8-bit tile routing,
+ *     two diagonal-distance boundaries per head, precision-grouped traversals,
+ *     one fused kernel that skips omitted tiles and merges both QK precisions
+ *     into one normalized output, prefill codes reused as the decode KV cache.
+ *   [TileMix] "TileMix: Tile-Centric Mixed-Precision Attention for LLM
+ *     Inference Acceleration", abstract: hardware-aligned score tiles, routing
+ *     decisions packed in compact bitmasks with one bit per group of adjacent
+ *     key tiles, FP16 or INT8 score paths sharing one online-softmax state,
+ *     all legal groups routed, GQA, variable-length batches, INT8 K/V caches.
+ *   [HyQuant] "HyQuant Uses Hybrid Precision to Compress LLM Attention",
+ *     section "How HyQuant works": recent window kept FP16, the rest quantized,
+ *     dequantization fused into decode attention.
+ *
+ * Conventions common to every entry point.
+ *  - Pointers named *_dev or documented as "device" are device memory owned by
+ *    the caller (e.g. PyTorch tensors).  Pointers documented as "host" are host
+ *    memory read during the call only.  The library allocates nothing, frees
+ *    nothing and keeps no pointer after a call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    is asynchronous: buffers must stay valid until the stream has finished.
+ *    Calls on different streams are independent (the library has no mutable
+ *    global state apart from the lazily loaded code object).
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    a nonzero status nothing has been enqueued and outputs are untouched.
+ *    Launch failures return TM_E_HIP.  Faults inside kernels surface at the
+ *    caller's next synchronization of the stream.  Nothing throws across the
+ *    ABI.
+ *  - Token-major 16-bit inputs are [T][heads][d] row-major, T = total tokens
+ *    of all sequences; sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s+1]-1.
+ *  - Quantization blocks are 64 tokens and restart at each sequence start;
+ *    nblk = sum over s of ceil(len_s / 64).  Key tiles are one block (bk = 64).
+ */
+#ifndef TM_H
+#define TM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tm_status {
+  TM_OK = 0,
+  TM_E_ARG = 1,          /* NULL or out-of-range argument                      */
+  TM_E_SHAPE = 2,        /* inconsistent sizes / unsupported head dim / tiles   */
+  TM_E_POLICY = 3,       /* policy invalid (b8 > b4, a row with no key, ...)    */
+  TM_E_SPACE = 4,        /* caller buffer (traversal, workspace) too small      */
+  TM_E_UNSUPPORTED = 5,  /* valid request this build does not implement         */
+  TM_E_HIP = 6           /* a HIP launch or copy failed                         */
+} tm_status;
+
+typedef enum tm_dtype { TM_F16 = 0, TM_BF16 = 1, TM_F32 = 2 } tm_dtype;
+
+/* Per-tile precision.  INT4 tiles use 4-bit Q and K codes, INT8 tiles 8-bit
+ * codes ([TriAttention] abstract); FP16 tiles use the 16-bit Q and K
+ * ([TileMix] abstract; bf16 inputs run the bf16 MFMA on this path). */
+typedef enum tm_prec { TM_SKIP = 0, TM_INT4 = 1, TM_INT8 = 2, TM_FP16 = 3 } tm_prec;
+
+typedef enum tm_layout {
+  TM_ROWS = 0,  /* codes [heads][nblk][64][d] and [heads][nblk][64][d/2]        */
+  TM_COLS = 1   /* codes transposed per block: [heads][nblk][d][64], [d][32]   */
+} tm_layout;
+
+typedef enum tm_policy_kind { TM_POLICY_BOUNDARIES = 0, TM_POLICY_BITMASK = 1 } tm_policy_kind;
+
+/* Problem shape.  cu_seqlens (host) and cu_seqlens_dev (device) hold the same
+ * nseq+1 non-decreasing int32 prefix sums starting at 0.
+ * Supported: d in {64, 128}; bk == 64; bq in {64, 128}; hq % hkv == 0;
+ * dtype TM_F16 or TM_BF16.  softmax_scale <= 0 selects 1/sqrt(d). */
+typedef struct tm_shape {
+  int32_t nseq;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens_dev;
+  int32_t hq, hkv, d;
+  int32_t bq, bk;
+  int32_t dtype;
+  float softmax_scale;
+} tm_shape;
+
+/* Quantized tensor (device buffers, caller-allocated).  One symmetric scale
+ * per (head, 64-token block) over all d channels of the block's valid rows:
+ * s8 = amax / 127, s4 = amax / 7 (IEEE binary32 divisions);
+ * code = clamp(round_half_even(x / s), -qmax, qmax), binary32 division;
+ * amax == 0 gives scale 0 and zero codes; rows past a sequence's end are zero.
+ * INT4 codes are two's-complement nibbles packed along the last axis, element
+ * 2t in the low nibble of byte t and 2t+1 in the high nibble.
+ * ([TriAttention] abstract: keys and values quantized during prefill; the pages
+ * give no formula, this symmetric block reading is the library's definition.)
+ *   TM_ROWS: c8 [heads][nblk][64][d]   c4 [heads][nblk][64][d/2]
+ *   TM_COLS: c8 [heads][nblk][d][64]   c4 [heads][nblk][d][32]
+ *            t16 (optional, TM_COLS only): the block's values as fp16,
+ *            transposed, [heads][nblk][d][64] (bf16 input rounded to nearest
+ *            even fp16; zeros past the sequence end).
+ *   s8, s4 [heads][nblk] float.
+ * nblk must equal sum over sequences of ceil(len / 64) (tm_num_blocks). */
+typedef struct tm_qtensor {
+  int8_t* c8;
+  uint8_t* c4;
+  float* s8;
+  float* s4;
+  uint16_t* t16;
+  int32_t heads;
+  int32_t layout;
+  int64_t nblk;
+} tm_qtensor;
+
+/* Tile policy ([TriAttention] abstract: two diagonal-distance boundaries per
+ * head; [TileMix] abstract: packed group bitmask).  b8/b4 are host arrays
+ * (at most 256 query heads); bits is device memory read by the expansion
+ * kernel.
+ *  Boundaries: b8[hq], b4[hq] in key-tile units, 0 <= b8 <= b4.  For query
+ *   tile i and key tile j, delta = max(0, floor((i*bq - j*bk) / bk));
+ *   delta < b8 -> INT8, delta < b4 -> INT4, else SKIP; sink = 1 keeps key
+ *   tile 0 INT8 for every query tile.  b4 == 0 without a sink leaves rows with
+ *   no key and is rejected (TM_E_POLICY).
+ *  Bitmask: bits[n_words] uint32 (device).  Bit = 1 -> FP16, 0 -> INT8;
+ *   bit g of a row governs key tiles [g*group, (g+1)*group); each (sequence, query head,
+ *   query tile) row holds ceil(ceil(nk_s / group) / 32) words, LSB first, rows
+ *   ordered sequence, then head, then query tile.  Nothing is skipped.
+ *  A tile is legal iff j*bk <= min((i+1)*bq, len) - 1; inside a legal tile key
+ *  c is visible from row r iff c <= r. */
+typedef struct tm_policy {
+  int32_t kind;
+  const int32_t* b8;
+  const int32_t* b4;
+  int32_t sink;
+  const uint32_t* bits;
+  int64_t n_words;
+  int32_t group;
+} tm_policy;
+
+/* Tile counts of a traversal (host). */
+typedef struct tm_census {
+  int64_t legal, n_int8, n_int4, n_fp16, n_skip;
+  int64_t n_items, max_runs;
+} tm_census;
+
+/* Decode cache policy, per KV head (host arrays, at most 64 KV heads), in
+ * 64-token blocks.
+ * For a cache of L tokens (the new token included) and block j:
+ *  blocks overlapping the last tail_tokens tokens are FP16 (read from the
+ *  16-bit keys and the t16 copy of V); otherwise delta = floor((L-1)/64) - j,
+ *  INT8 if delta < b8 (or j == 0 with sink), INT4 if delta < b4, else SKIP.
+ * ([HyQuant] "How HyQuant works": recent window FP16, rest quantized;
+ * [TriAttention] abstract: prefill codes reused in the decode cache.) */
+typedef struct tm_dpolicy {
+  const int32_t* b8;
+  const int32_t* b4;
+  int32_t sink;
+  int32_t tail_tokens;
+} tm_dpolicy;
+
+/* Traversal buffer layout (device, written by tm_build_traversal, read by
+ * tm_prefill; documented so tests can decode it).  All fields little-endian.
+ *  [0, 256)        header: uint32 magic 0x564D5454 ('TTMV'), version, kind,
+ *                  n_items, max_runs, nseq, hq, hkv, bq, bk, d, nblk,
+ *                  seq_off, item_off, run_off, bits_off (bytes);
+ *                  at byte 128: int64 legal, int8, int4, fp16, skip.
+ *  seq_off:        nseq x uint32[4] {tok_start, len, blk_start, nq}.
+ *  item_off:       n_items x uint32[8] {seq, head, qtile, nruns,
+ *                  n_int8, n_int4, n_fp16, n_skip}, heavy-first: query tiles
+ *                  in descending index, then sequence, then head.
+ *  run_off:        n_items x max_runs x uint32[2] {first key tile,
+ *                  count | prec << 24}; an item's runs are grouped by
+ *                  precision (boundaries: INT8 band, sink, INT4 band;
+ *                  bitmask: FP16 runs, then INT8 runs); SKIP tiles are never
+ *                  listed ([TriAttention] abstract: precision-grouped
+ *                  traversals; omitted tiles are skipped).
+ *  bits_off:       0 (the bitmask stays in the caller's buffer). */
+#define TM_TRAV_MAGIC 0x564D5454u
+#define TM_TRAV_VERSION 1u
+#define TM_TRAV_HEADER_BYTES 256
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Human-readable name of a status code (static string). */
+const char* tm_status_string(int32_t status);
+
+/* Library version, (major << 16) | minor. */
+int32_t tm_version(void);
+
+/* nblk for a shape (host only, no GPU work); -1 if the shape is invalid. */
+int64_t tm_num_blocks(const tm_shape* shape);
+
+/* ------------------------------------------------------------ entry points */
+
+/* Quantize and pack x [T][heads][d] (shape->dtype, device) into `out`
+ * (device buffers sized for out->heads, out->layout, out->nblk).
+ * out->t16 may be NULL; it is written only for TM_COLS.
+ * Errors: TM_E_ARG (NULL pointers, heads <= 0, bad layout), TM_E_SHAPE (d,
+ * dtype, cu_seqlens, nblk mismatch).  ([TriAttention] abstract: quantized keys
+ * and values prepared during prefill.) */
+tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads,
+                           tm_qtensor* out, void* stream);
+
+/* Expand a policy into the precision-grouped traversal read by tm_prefill.
+ * trav == NULL: write the required size to *trav_bytes and return TM_OK
+ * without touching the GPU.  Otherwise *trav_bytes is the capacity of `trav`
+ * (device); TM_E_SPACE if too small.  census (host, may be NULL): when given,
+ * the call synchronizes `stream` and fills it.
+ * Errors: TM_E_SHAPE, TM_E_POLICY (b8 > b4, negative boundaries, b4 == 0
+ * without sink, group < 1, n_words too small), TM_E_SPACE, TM_E_HIP.
+ * ([TriAttention] abstract: boundaries generate precision-grouped traversals;
+ * [TileMix] abstract: compact bitmasks, one bit per group of key tiles.) */
+tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
+                             void* trav, size_t* trav_bytes, tm_census* census,
+                             void* stream);
+
+/* Fused tile-routed causal prefill.
+ *  trav: built by tm_build_traversal for this shape.
+ *  q [T][hq][d], k [T][hkv][d]: 16-bit inputs (device; read on FP16 tiles).
+ *  qq (TM_ROWS, hq heads), kq (TM_ROWS, hkv heads): quantized Q and K.
+ *  vq (TM_COLS, hkv heads) with t16 set: V in fp16, transposed per block (the
+ *    PV product always uses these unquantized values).
+ *  o [T][hq][d] of o_dtype (TM_F32, TM_F16 or TM_BF16, device).
+ *  lse [hq][T] float (device, may be NULL): natural-log sum of exponentials.
+ *  dbg_qk / dbg_tiles / n_dbg (device, may be NULL / 0): for each listed
+ *    integer tile {seq, head, qtile, ktile} the raw integer QK products of
+ *    the whole tile are written to dbg_qk[n][bq][bk] (int32, INT4 tiles in
+ *    code units) by the same kernel; listed tiles that are FP16 or skipped
+ *    are left untouched.
+ * Per row, the output is the softmax over the row's executed keys of the
+ * tile scores (INT tiles: a * sq * sk * scale with a the exact integer dot
+ * product of codes; FP16 tiles: scale * q . k), applied to V, with P rounded
+ * to fp16 for the PV product ([TriAttention] abstract: one normalized output
+ * from both QK precisions; [TileMix] abstract: shared online-softmax state).
+ * Errors: TM_E_ARG, TM_E_SHAPE (tensors not matching the shape), TM_E_HIP. */
+tm_status tm_prefill(const tm_shape* shape, const void* trav,
+                     const void* q, const void* k,
+                     const tm_qtensor* qq, const tm_qtensor* kq, const tm_qtensor* vq,
+                     void* o, int32_t o_dtype, float* lse,
+                     int32_t* dbg_qk, const int32_t* dbg_tiles, int32_t n_dbg,
+                     void* stream);
+
+/* Decode: one new query per sequence over the compressed cache.
+ *  cache: shape of the cached sequences (nseq = batch, len = cache length L
+ *    including the new token); dtype must be TM_F16; hq/hkv <= 16.
+ *  q [nseq][hq][d] fp16 (device).
+ *  kq (TM_ROWS, hkv heads), vq (TM_COLS, hkv heads, t16 set): the cache, as
+ *    produced by tm_quantize_pack over the cached tokens.
+ *  k16 [T][hkv][d] fp16 (device): keys read for FP16 blocks.
+ *  policy: per-KV-head tags (tm_dpolicy).
+ *  o [nseq][hq][d] of o_dtype (TM_F32 or TM_F16, device).
+ *  ws (device): workspace; ws == NULL writes the required size to *ws_bytes
+ *    and returns TM_OK without GPU work; otherwise *ws_bytes is its capacity.
+ * INT blocks: score = scale * sk * (q . ck), value = sv * cv; FP16 blocks:
+ * score = scale * (q . k), value = v ([HyQuant] "How HyQuant works":
+ * dequantization fused with attention).
+ * Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY, TM_E_SPACE, TM_E_UNSUPPORTED
+ * (bf16 cache, hq/hkv > 16), TM_E_HIP. */
+tm_status tm_decode(const tm_shape* cache, const void* q,
+                    const tm_qtensor* kq, const tm_qtensor* vq, const void* k16,
+                    const tm_dpolicy* policy, void* o, int32_t o_dtype,
+                    void* ws, size_t* ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TM_H */

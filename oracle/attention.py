@@ -165,7 +165,7 @@ def prefill_unquantized(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, tau=Non
     return O
 
 
-def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_tags=False):
+def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_tags=False, pairs=None):
     """Oracle decode: one new query per sequence over its compressed cache.
 
     seqlens: cache length L_b per sequence (the cache includes the new token);
@@ -174,7 +174,8 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
     16-bit cache values read for FP16 blocks.
     Block tags follow policy.decode_block_tags with per-KV-head (b8, b4).
     INT blocks: score = tau * sk * (q . ck), value = sv * cv; FP16 blocks:
-    score = tau * (q . k), value = v.  Returns O [B][hq][d].
+    score = tau * (q . k), value = v.  Returns O [B][hq][d]; with ``pairs`` (a
+    list of (b, h)) only those outputs are computed (the rest stay zero).
     """
     tau = _tau(d, tau)
     grp = hq // hkv
@@ -186,6 +187,8 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
         L = int(seqlens[b])
         blk0 = int(kq["blk_start"][b])
         for h in range(hq):
+            if pairs is not None and (b, h) not in pairs:
+                continue
             kv = h // grp
             tags = P.decode_block_tags(L, int(dpol["b8"][kv]), int(dpol["b4"][kv]),
                                        int(dpol["sink"]), int(dpol["tail"]))

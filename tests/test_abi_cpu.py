@@ -1,0 +1,222 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/tm.h declares, answers size queries, and rejects every invalid
+argument with the documented status before touching the device.
+
+Device pointers in these tests are fake non-NULL addresses: each call here
+fails host validation (or is a size query), so nothing is dereferenced or
+launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from tile_routed_mixed_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from tile_routed_mixed_amd import build
+        build.build()
+    _binding.lib()
+    return _binding
+
+
+FAKE = 0x10000
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "tm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(B):
+    names = declared_functions()
+    assert {"tm_quantize_pack", "tm_build_traversal", "tm_prefill", "tm_decode"} <= set(names)
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (tm_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings(B):
+    L = B.lib()
+    assert L.tm_version() >> 16 == 1
+    for s in range(7):
+        assert L.tm_status_string(s).decode().startswith("TM_")
+
+
+def _shape(B, seqlens, hq=4, hkv=2, d=64, bq=128, bk=64, dtype=0, dev=True):
+    s = B.Shape(seqlens, hq, hkv, d, bq, bk, dtype)
+    s.c.cu_seqlens_dev = FAKE if dev else None
+    return s
+
+
+def test_num_blocks(B):
+    assert _shape(B, [1, 63, 64, 65, 200]).nblk() == 1 + 1 + 1 + 2 + 4
+    assert _shape(B, [0, 64]).nblk() == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), 2), (dict(hq=3, hkv=2), 2), (dict(bq=96), 2), (dict(bk=32), 2), (dict(dtype=2), 2),
+])
+def test_bad_shapes(B, kw, status):
+    s = _shape(B, [100], **kw)
+    pol = B.Policy(dict(kind=0, b8=[1] * s.hq, b4=[2] * s.hq, sink=0))
+    n = ctypes.c_size_t(0)
+    assert B.lib().tm_build_traversal(ctypes.byref(s.c), ctypes.byref(pol.c), None, ctypes.byref(n), None,
+                                      None) == status
+
+
+def test_bad_cu_seqlens(B):
+    s = _shape(B, [100, 20])
+    s.cu_host[1] = 130          # non-monotone: 0, 130, 120
+    pol = B.Policy(dict(kind=0, b8=[1] * 4, b4=[2] * 4, sink=0))
+    n = ctypes.c_size_t(0)
+    assert B.lib().tm_build_traversal(ctypes.byref(s.c), ctypes.byref(pol.c), None, ctypes.byref(n), None,
+                                      None) == B.TM_E_SHAPE
+    s.cu_host[:] = [5, 105, 125]
+    assert B.lib().tm_num_blocks(ctypes.byref(s.c)) == -1
+
+
+@pytest.mark.parametrize("pol,status", [
+    (dict(kind=0, b8=[3, 1, 1, 1], b4=[2, 2, 2, 2], sink=0), 3),      # b8 > b4
+    (dict(kind=0, b8=[0, 1, 1, 1], b4=[0, 2, 2, 2], sink=0), 3),      # a row with no key
+    (dict(kind=0, b8=[-1, 1, 1, 1], b4=[2, 2, 2, 2], sink=0), 3),
+    (dict(kind=0, b8=[1] * 4, b4=[2] * 4, sink=2), 3),
+    (dict(kind=7, b8=[1] * 4, b4=[2] * 4, sink=0), 1),
+])
+def test_bad_boundary_policies(B, pol, status):
+    s = _shape(B, [300, 50])
+    p = B.Policy(pol) if pol["kind"] in (0,) else None
+    if p is None:
+        p = B.Policy(dict(kind=0, b8=pol["b8"], b4=pol["b4"], sink=0))
+        p.c.kind = pol["kind"]
+    n = ctypes.c_size_t(0)
+    assert B.lib().tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), None, ctypes.byref(n), None,
+                                      None) == status
+
+
+def test_zero_b4_with_sink_is_valid(B):
+    s = _shape(B, [300])
+    p = B.Policy(dict(kind=0, b8=[0] * 4, b4=[0] * 4, sink=1))
+    n = ctypes.c_size_t(0)
+    assert B.lib().tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), None, ctypes.byref(n), None,
+                                      None) == B.TM_OK
+
+
+def test_bitmask_validation_and_size(B):
+    from oracle import policy as P   # the word count the pages' layout implies
+    s = _shape(B, [1000, 10240], hq=2, hkv=1)
+    _, tot = P.bitmask_row_base([1000, 10240], 2, 128, 64, 4)
+    p = B.Policy(dict(kind=1, group=4, words=np.zeros(tot, np.uint32)))
+    p.c.bits = FAKE
+    n = ctypes.c_size_t(0)
+    L = B.lib()
+    assert L.tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), None, ctypes.byref(n), None, None) == 0
+    n_items = 2 * (8 + 80)
+    max_runs = (160 + 3) // 4
+    align = lambda x: (x + 255) // 256 * 256
+    want = align(align(align(256 + 2 * 16) + 32 * n_items) + 8 * n_items * max_runs)
+    assert n.value == want
+    p.c.n_words = tot - 1
+    assert L.tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), None, ctypes.byref(n), None, None) == 3
+    p.c.n_words = tot
+    p.c.group = 0
+    assert L.tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), None, ctypes.byref(n), None, None) == 3
+
+
+def test_traversal_capacity(B):
+    s = _shape(B, [512], hq=1, hkv=1, bq=64)
+    p = B.Policy(dict(kind=0, b8=[2], b4=[5], sink=1))
+    n = ctypes.c_size_t(0)
+    L = B.lib()
+    assert L.tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), None, ctypes.byref(n), None, None) == 0
+    need = n.value
+    assert need == 256 + 256 + 256 + 256        # header, seq table, 8 items, 8 x 3 runs (aligned)
+    small = ctypes.c_size_t(need - 1)
+    assert L.tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), FAKE, ctypes.byref(small), None,
+                                None) == B.TM_E_SPACE
+
+
+def _qt(B, heads, layout, nblk, t16=True):
+    return B.tm_qtensor(FAKE, FAKE, FAKE, FAKE, FAKE if t16 else None, heads, layout, nblk)
+
+
+def test_quantize_validation(B):
+    s = _shape(B, [100, 30])
+    L = B.lib()
+    nb = s.nblk()
+    q = _qt(B, 4, B.TM_ROWS, nb, t16=True)           # rows layout with t16 set
+    assert L.tm_quantize_pack(ctypes.byref(s.c), FAKE, 4, ctypes.byref(q), None) == B.TM_E_ARG
+    q = _qt(B, 4, B.TM_ROWS, nb + 1, t16=False)
+    assert L.tm_quantize_pack(ctypes.byref(s.c), FAKE, 4, ctypes.byref(q), None) == B.TM_E_SHAPE
+    q = _qt(B, 4, 5, nb, t16=False)
+    assert L.tm_quantize_pack(ctypes.byref(s.c), FAKE, 4, ctypes.byref(q), None) == B.TM_E_ARG
+    q = _qt(B, 3, B.TM_ROWS, nb, t16=False)
+    assert L.tm_quantize_pack(ctypes.byref(s.c), FAKE, 4, ctypes.byref(q), None) == B.TM_E_SHAPE
+    assert L.tm_quantize_pack(ctypes.byref(s.c), None, 4, ctypes.byref(q), None) == B.TM_E_ARG
+    s2 = _shape(B, [100, 30], dev=False)
+    q = _qt(B, 4, B.TM_ROWS, nb, t16=False)
+    assert L.tm_quantize_pack(ctypes.byref(s2.c), FAKE, 4, ctypes.byref(q), None) == B.TM_E_ARG
+
+
+def test_prefill_validation(B):
+    s = _shape(B, [100, 30])
+    L = B.lib()
+    nb = s.nblk()
+    qq, kq, vq = _qt(B, 4, 0, nb, False), _qt(B, 2, 0, nb, False), _qt(B, 2, 1, nb, True)
+    args = lambda **kw: dict(dict(trav=FAKE, q=FAKE, k=FAKE, qq=qq, kq=kq, vq=vq, o=FAKE, odt=0, ndbg=0), **kw)
+
+    def call(a):
+        return L.tm_prefill(ctypes.byref(s.c), a["trav"], a["q"], a["k"], ctypes.byref(a["qq"]),
+                            ctypes.byref(a["kq"]), ctypes.byref(a["vq"]), a["o"], a["odt"], None, None, None,
+                            a["ndbg"], None)
+    assert call(args(q=None)) == B.TM_E_ARG
+    assert call(args(trav=None)) == B.TM_E_ARG
+    assert call(args(odt=9)) == B.TM_E_ARG
+    assert call(args(ndbg=2)) == B.TM_E_ARG
+    assert call(args(vq=_qt(B, 2, 1, nb, False))) == B.TM_E_ARG
+    assert call(args(vq=_qt(B, 2, 0, nb, True))) == B.TM_E_SHAPE
+    assert call(args(kq=_qt(B, 4, 0, nb, False))) == B.TM_E_SHAPE
+    assert call(args(qq=_qt(B, 4, 0, nb - 1, False))) == B.TM_E_SHAPE
+
+
+def test_decode_validation_and_workspace(B):
+    L = B.lib()
+    s = _shape(B, [32768] * 16, hq=32, hkv=8, d=128)
+    dp = B.DPolicy(dict(b8=[128] * 8, b4=[320] * 8, sink=1, tail=128))
+    n = ctypes.c_size_t(0)
+    assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(dp.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_OK
+    # 16 x 8 (sequence, KV head) pairs -> 16 splits; ws = B * hq * splits * (d + 2) floats
+    assert n.value == 16 * 32 * 16 * 130 * 4
+    small = ctypes.c_size_t(n.value - 4)
+    nb = s.nblk()
+    kq, vq = _qt(B, 8, 0, nb, False), _qt(B, 8, 1, nb, True)
+    assert L.tm_decode(ctypes.byref(s.c), FAKE, ctypes.byref(kq), ctypes.byref(vq), FAKE, ctypes.byref(dp.c),
+                       FAKE, 2, FAKE, ctypes.byref(small), None) == B.TM_E_SPACE
+    bad = B.DPolicy(dict(b8=[300] * 8, b4=[200] * 8, sink=1, tail=128))
+    assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(bad.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_E_POLICY
+    empty = B.DPolicy(dict(b8=[0] * 8, b4=[0] * 8, sink=0, tail=0))
+    assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(empty.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_E_POLICY
+    sb = _shape(B, [64], hq=32, hkv=8, d=128, dtype=1)
+    assert L.tm_decode(ctypes.byref(sb.c), None, None, None, None, ctypes.byref(dp.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_E_UNSUPPORTED
+    sg = _shape(B, [64], hq=34, hkv=2, d=128)
+    dp2 = B.DPolicy(dict(b8=[1] * 2, b4=[2] * 2, sink=1, tail=128))
+    assert L.tm_decode(ctypes.byref(sg.c), None, None, None, None, ctypes.byref(dp2.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_E_UNSUPPORTED
+    sz = _shape(B, [64, 0], hq=4, hkv=2, d=128)
+    assert L.tm_decode(ctypes.byref(sz.c), None, None, None, None, ctypes.byref(dp2.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_E_SHAPE

@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Gates: quantized codes, scales, the fp16 V copy, the traversal and the integer
+QK tile scores bit-exact; fp32 attention outputs within max-abs 4e-3 and
+mean-abs 5e-4 of the float64 oracle computed from the oracle's own codes.
+Small cases span several tiles with ragged tails; the full-size workloads are
+checked on sampled rows (the oracle computes rows one by one).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+from oracle import policy as OP
+from oracle import quant as OQ
+
+from _gpu_helpers import (TOL_MAX, check_int_scores, compare, int_tiles, oracle_prefill, run_prefill, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import tile_routed_mixed_amd as T
+    T.lib()
+
+
+def _inputs(w):
+    return W.make_qkv(w)
+
+
+# ---------------------------------------------------------------------------- quantize
+
+@pytest.mark.parametrize("dtype,d,seqlens", [("f16", 64, [512]), ("bf16", 128, [1, 63, 64, 65, 300]),
+                                             ("f16", 128, [700, 129])])
+def test_quantize_bitexact(dtype, d, seqlens):
+    import torch
+    import tile_routed_mixed_amd as T
+    w = W.small("gqa8k", seqlens, d=d, dtype=dtype, hq=4, hkv=2)
+    q, k, v = _inputs(w)
+    p = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, dict(kind=0, b8=[1] * 4, b4=[2] * 4, sink=0))
+    p.upload(q[0], k[0], v[0])
+    say(f"[gpu] quantize {dtype} d={d} {seqlens}")
+    p.quantize()
+    torch.cuda.synchronize()
+    for x, qt, layout in ((q, p.qq, "rows"), (k, p.kq, "rows"), (v, p.vq, "cols")):
+        ref = OQ.quantize(x[1], w.seqlens, layout=layout, with_t16=(layout == "cols"))
+        assert np.array_equal(qt.s8.cpu().numpy().view(np.uint32), ref["s8"].view(np.uint32))
+        assert np.array_equal(qt.s4.cpu().numpy().view(np.uint32), ref["s4"].view(np.uint32))
+        assert np.array_equal(qt.c8.cpu().numpy(), ref["c8p"])
+        assert np.array_equal(qt.c4.cpu().numpy(), ref["c4p"])
+        if layout == "cols":
+            assert np.array_equal(qt.t16.cpu().numpy().view(np.uint16), ref["t16"].view(np.uint16))
+
+
+# ---------------------------------------------------------------------------- traversal
+
+def _check_traversal(w, pol, p, census):
+    import tile_routed_mixed_amd as T
+    tr = T.read_traversal(p.trav.cpu().numpy())
+    gs = OP.grids(w.seqlens, w.hq, w.bq, w.bk, pol)
+    c = OP.census(gs)
+    assert census["legal"] == c["legal"] and census["int8"] == c["int8"] and census["int4"] == c["int4"]
+    assert census["fp16"] == c["fp16"] and census["skip"] == c["skip"]
+    assert tr["census"] == c
+    assert tr["magic"] == T._binding.TRAV_MAGIC
+    got = set()
+    seen = set()
+    prev_q = None
+    for n in range(tr["n_items"]):
+        s, h, qt, nr = (int(x) for x in tr["items"][n, :4])
+        assert (s, h, qt) not in seen
+        seen.add((s, h, qt))
+        if prev_q is not None:
+            assert qt <= prev_q            # heavy-first: query tiles in descending order
+        prev_q = qt
+        precs = []
+        for r in range(nr):
+            first, cp = (int(x) for x in tr["runs"][n, r])
+            cnt, prec = cp & 0xFFFFFF, cp >> 24
+            precs.append(prec)
+            for j in range(first, first + cnt):
+                key = (s, h, qt, j, prec)
+                assert key not in got
+                got.add(key)
+        # runs are grouped by precision: each precision forms one contiguous stretch
+        groups = [x for i, x in enumerate(precs) if i == 0 or precs[i - 1] != x]
+        assert len(groups) == len(set(groups))
+    assert len(seen) == sum(w.hq * OP.n_tiles(S, w.bq) for S in w.seqlens)
+    assert got == OP.executed_tiles(gs)
+
+
+@pytest.mark.parametrize("case", ["toy", "boundaries_varlen", "bitmask_varlen", "sink_edge"])
+def test_traversal_bruteforce(case):
+    w, pol = _case(case)
+    q, k, v = _inputs(w)
+    p, census, o, lse, _ = run_prefill(w, pol, q, k, v)
+    _check_traversal(w, pol, p, census)
+
+
+# ---------------------------------------------------------------------------- prefill (small)
+
+def _case(case):
+    rng = np.random.default_rng(hash(case) % 2 ** 32)
+    if case == "toy":
+        w = W.get("toy512")
+        return w, W.make_policy(w)
+    if case == "boundaries_varlen":
+        w = W.small("gqa8k", [1000, 1, 130, 64], hq=8, hkv=2)
+        b4 = rng.integers(1, 9, size=8)
+        b8 = np.array([rng.integers(0, x + 1) for x in b4])
+        return w, dict(kind=0, b8=b8, b4=b4, sink=0)
+    if case == "bitmask_varlen":
+        w = W.small("varlen32k", [700, 64, 1, 1500, 129], hq=8, hkv=2)
+        _, tot = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 2)
+        words = (rng.random(tot * 32) < 0.35).reshape(tot, 32)
+        packed = (words * (1 << np.arange(32, dtype=np.uint64))).sum(axis=1).astype(np.uint32)
+        return w, dict(kind=1, group=2, words=packed)
+    if case == "sink_edge":
+        w = W.small("long128k", [2200, 333], hq=4, hkv=1, d=64)
+        return w, dict(kind=0, b8=[0, 2, 3, 0], b4=[0, 2, 9, 5], sink=1)
+    if case == "bq64_d128":
+        w = W.small("gqa8k", [900], hq=4, hkv=4, bq=64)
+        return w, dict(kind=0, b8=[1, 2, 3, 4], b4=[3, 4, 5, 6], sink=1)
+    if case == "bitmask_bf16":
+        w = W.small("varlen32k", [1100, 200], hq=4, hkv=1, dtype="bf16")
+        _, tot = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 4)
+        words = rng.integers(0, 2 ** 32, size=tot, dtype=np.uint64).astype(np.uint32)
+        return w, dict(kind=1, group=4, words=words)
+    raise KeyError(case)
+
+
+CASES = ["toy", "boundaries_varlen", "bitmask_varlen", "sink_edge", "bq64_d128", "bitmask_bf16"]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_prefill_small(case):
+    w, pol = _case(case)
+    q, k, v = _inputs(w)
+    tiles = int_tiles(w, pol, limit=24)
+    dbg_in = [t[:4] for t in tiles] if tiles else None
+    p, census, o, lse, dbg = run_prefill(w, pol, q, k, v, dbg_tiles=dbg_in)
+    O, L, qq, kq = oracle_prefill(w, pol, q, k, v)
+    compare(o, O, lse, L, what=case)
+    if tiles:
+        check_int_scores(w, tiles, dbg, qq, kq)
+    # the capture build of the kernel computes the same outputs bit for bit
+    _, _, o2, lse2, _ = run_prefill(w, pol, q, k, v)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_toy_all_int_tiles_bitexact():
+    w = W.get("toy512")
+    pol = W.make_policy(w)
+    q, k, v = _inputs(w)
+    tiles = int_tiles(w, pol)
+    assert len(tiles) == 33
+    _, census, o, lse, dbg = run_prefill(w, pol, q, k, v, dbg_tiles=[t[:4] for t in tiles])
+    assert (census["int8"], census["int4"], census["skip"]) == (21, 12, 3)
+    _, _, qq, kq = oracle_prefill(w, pol, q, k, v, rows=[(0, 0, 0)])
+    check_int_scores(w, tiles, dbg, qq, kq)
+
+
+def test_first_row_is_v0_and_rows_normalized():
+    w, pol = _case("boundaries_varlen")
+    q, k, v = _inputs(w)
+    _, _, o, lse, _ = run_prefill(w, pol, q, k, v)
+    cu = w.cu_seqlens
+    for s in range(len(w.seqlens)):
+        for h in range(w.hq):
+            ref = v[1][cu[s], h // (w.hq // w.hkv)]
+            assert np.max(np.abs(o[cu[s], h] - ref)) <= 1e-3     # fp16 probability 1.0 is exact
+    # sum_c exp(s_c - lse) == 1 per row, with the oracle's scores and the GPU's lse
+    O, L, qq, kq = oracle_prefill(w, pol, q, k, v, rows=[(0, 3, 999), (2, 5, 129), (3, 0, 63)])
+    for (s, h, r) in [(0, 3, 999), (2, 5, 129), (3, 0, 63)]:
+        t = cu[s] + r
+        assert abs(lse[h, t] - L[h, t]) <= 1e-4
+
+
+def test_skipped_tiles_do_not_matter_on_gpu():
+    w = W.small("gqa8k", [1024], hq=2, hkv=1)
+    pol = dict(kind=0, b8=[1, 2], b4=[2, 4], sink=0)
+    q, k, v = _inputs(w)
+    _, _, o0, _, _ = run_prefill(w, pol, q, k, v)
+    gs = OP.grids(w.seqlens, w.hq, w.bq, w.bk, pol)[0]
+    assert np.all(gs[:, 7, 0:2] == OP.SKIP)         # query tile 7 skips key tiles 0, 1 in both heads
+    k2 = (k[0].copy(), k[1].copy())
+    v2 = (v[0].copy(), v[1].copy())
+    rng = np.random.default_rng(1)
+    pert = W.round16(rng.standard_normal((128, 1, 128)).astype(np.float32) * 5, "bf16")
+    k2[0][:128], v2[0][:128] = pert[0], pert[0][:, :, ::-1].copy()
+    _, _, o1, _, _ = run_prefill(w, pol, q, k2, v2)
+    assert np.array_equal(o0[7 * 128:8 * 128], o1[7 * 128:8 * 128])
+    assert not np.array_equal(o0[128:256], o1[128:256])
+
+
+def test_prefill_16bit_outputs():
+    import tile_routed_mixed_amd as T
+    w, pol = _case("boundaries_varlen")
+    q, k, v = _inputs(w)
+    O, _, _, _ = oracle_prefill(w, pol, q, k, v)
+    for odt, ulp in ((T.TM_F16, 2.0 ** -11), (T.TM_BF16, 2.0 ** -8)):
+        _, _, o, _, _ = run_prefill(w, pol, q, k, v, o_dtype=odt)
+        err = np.abs(o - O)
+        assert np.all(err <= TOL_MAX + ulp * np.abs(O) + 1e-7), (odt, float(err.max()))
+
+
+def test_deterministic():
+    w, pol = _case("bitmask_varlen")
+    q, k, v = _inputs(w)
+    _, _, o1, l1, _ = run_prefill(w, pol, q, k, v)
+    _, _, o2, l2, _ = run_prefill(w, pol, q, k, v)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------- decode (small)
+
+def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, seed=3):
+    import torch
+    import tile_routed_mixed_amd as T
+    w = W.small("decode16x32k", seqlens, hq=hq, hkv=hkv, d=d)
+    q, k, v = W.make_qkv(w)
+    dq = W.make_decode_query(w)
+    say(f"[gpu] decode {seqlens} hq={hq} hkv={hkv} d={d} {dpol}")
+    p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol)
+    p.upload(dq[0], k[0], v[0])
+    p.build_cache()
+    o = p.decode()
+    torch.cuda.synchronize()
+    kq = OQ.quantize(k[1], w.seqlens)
+    vq = OQ.quantize(v[1], w.seqlens, layout="cols")
+    O = OA.decode(w.seqlens, hq, hkv, d, dq[1].astype(np.float64), kq, vq, k[1].astype(np.float64),
+                  v[1].astype(np.float64), dpol)
+    return o.cpu().numpy(), O
+
+
+@pytest.mark.parametrize("seqlens,dpol,d", [
+    ([1, 100, 1000, 2000], dict(b8=[2, 3], b4=[5, 9], sink=1, tail=128), 128),
+    ([64, 65, 4097], dict(b8=[1, 4], b4=[1, 40], sink=0, tail=128), 64),
+    ([3000, 777], dict(b8=[10 ** 6] * 2, b4=[10 ** 6] * 2, sink=0, tail=0), 128),
+    ([2500], dict(b8=[0, 0], b4=[30, 30], sink=1, tail=1), 128),
+])
+def test_decode_small(seqlens, dpol, d):
+    o, O = _decode_case(seqlens, dpol, d=d)
+    compare(o, O, what=f"decode {seqlens}")

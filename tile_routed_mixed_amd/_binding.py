@@ -1,0 +1,270 @@
+"""ctypes binding of libtm.so (include/tm.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the stream.
+The library must have been built (``__graft_entry__.build()`` or
+``python tile_routed_mixed_amd/build.py``); importing this module fails loudly
+otherwise -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtm.so")
+
+TM_OK, TM_E_ARG, TM_E_SHAPE, TM_E_POLICY, TM_E_SPACE, TM_E_UNSUPPORTED, TM_E_HIP = range(7)
+TM_F16, TM_BF16, TM_F32 = 0, 1, 2
+TM_SKIP, TM_INT4, TM_INT8, TM_FP16 = 0, 1, 2, 3
+TM_ROWS, TM_COLS = 0, 1
+TM_POLICY_BOUNDARIES, TM_POLICY_BITMASK = 0, 1
+TRAV_HEADER_BYTES = 256
+TRAV_MAGIC = 0x564D5454
+
+
+class tm_shape(ctypes.Structure):
+    _fields_ = [("nseq", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
+                ("cu_seqlens_dev", ctypes.c_void_p), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("bq", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class tm_qtensor(ctypes.Structure):
+    _fields_ = [("c8", ctypes.c_void_p), ("c4", ctypes.c_void_p), ("s8", ctypes.c_void_p),
+                ("s4", ctypes.c_void_p), ("t16", ctypes.c_void_p), ("heads", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("nblk", ctypes.c_int64)]
+
+
+class tm_policy(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("b8", ctypes.POINTER(ctypes.c_int32)),
+                ("b4", ctypes.POINTER(ctypes.c_int32)), ("sink", ctypes.c_int32),
+                ("bits", ctypes.c_void_p), ("n_words", ctypes.c_int64), ("group", ctypes.c_int32)]
+
+
+class tm_census(ctypes.Structure):
+    _fields_ = [("legal", ctypes.c_int64), ("n_int8", ctypes.c_int64), ("n_int4", ctypes.c_int64),
+                ("n_fp16", ctypes.c_int64), ("n_skip", ctypes.c_int64), ("n_items", ctypes.c_int64),
+                ("max_runs", ctypes.c_int64)]
+
+
+class tm_dpolicy(ctypes.Structure):
+    _fields_ = [("b8", ctypes.POINTER(ctypes.c_int32)), ("b4", ctypes.POINTER(ctypes.c_int32)),
+                ("sink", ctypes.c_int32), ("tail_tokens", ctypes.c_int32)]
+
+
+class TMError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib().tm_status_string(status).decode()}")
+        self.status = status
+
+
+_LIB = None
+
+
+def lib():
+    """Load libtm.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.tm_status_string.restype = ctypes.c_char_p
+        L.tm_status_string.argtypes = [i32]
+        L.tm_version.restype = i32
+        L.tm_version.argtypes = []
+        L.tm_num_blocks.restype = i64
+        L.tm_num_blocks.argtypes = [ctypes.POINTER(tm_shape)]
+        L.tm_quantize_pack.restype = i32
+        L.tm_quantize_pack.argtypes = [ctypes.POINTER(tm_shape), vp, i32, ctypes.POINTER(tm_qtensor), vp]
+        L.tm_build_traversal.restype = i32
+        L.tm_build_traversal.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp,
+                                         ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(tm_census), vp]
+        L.tm_prefill.restype = i32
+        L.tm_prefill.argtypes = [ctypes.POINTER(tm_shape), vp, vp, vp, ctypes.POINTER(tm_qtensor),
+                                 ctypes.POINTER(tm_qtensor), ctypes.POINTER(tm_qtensor), vp, i32, vp, vp, vp,
+                                 i32, vp]
+        L.tm_decode.restype = i32
+        L.tm_decode.argtypes = [ctypes.POINTER(tm_shape), vp, ctypes.POINTER(tm_qtensor),
+                                ctypes.POINTER(tm_qtensor), vp, ctypes.POINTER(tm_dpolicy), vp, i32, vp,
+                                ctypes.POINTER(ctypes.c_size_t), vp]
+        _LIB = L
+    return _LIB
+
+
+def _check(st: int, where: str):
+    if st != TM_OK:
+        raise TMError(st, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------------------- shapes
+
+class Shape:
+    """A tm_shape plus the host and device copies of cu_seqlens it points to."""
+
+    def __init__(self, seqlens, hq, hkv, d, bq=128, bk=64, dtype=TM_F16, softmax_scale=0.0, device=None):
+        self.seqlens = [int(s) for s in seqlens]
+        self.cu_host = np.ascontiguousarray(np.concatenate([[0], np.cumsum(self.seqlens)]).astype(np.int32))
+        self.cu_dev = None
+        if device is not None:
+            import torch
+            self.cu_dev = torch.from_numpy(self.cu_host.copy()).to(device)
+        self.c = tm_shape(len(self.seqlens), self.cu_host.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                          _ptr(self.cu_dev), hq, hkv, d, bq, bk, dtype, softmax_scale)
+        self.hq, self.hkv, self.d, self.bq, self.bk, self.dtype = hq, hkv, d, bq, bk, dtype
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_host[-1])
+
+    def nblk(self) -> int:
+        n = lib().tm_num_blocks(ctypes.byref(self.c))
+        if n < 0:
+            raise TMError(TM_E_SHAPE, "tm_num_blocks")
+        return int(n)
+
+
+class QTensor:
+    """Device buffers of one quantized tensor (see tm_qtensor in include/tm.h)."""
+
+    def __init__(self, shape: Shape, heads: int, layout: int, with_t16: bool, device):
+        import torch
+        nblk, d = shape.nblk(), shape.d
+        self.heads, self.layout, self.nblk = heads, layout, nblk
+        if layout == TM_ROWS:
+            self.c8 = torch.empty((heads, nblk, 64, d), dtype=torch.int8, device=device)
+            self.c4 = torch.empty((heads, nblk, 64, d // 2), dtype=torch.uint8, device=device)
+        else:
+            self.c8 = torch.empty((heads, nblk, d, 64), dtype=torch.int8, device=device)
+            self.c4 = torch.empty((heads, nblk, d, 32), dtype=torch.uint8, device=device)
+        self.s8 = torch.empty((heads, nblk), dtype=torch.float32, device=device)
+        self.s4 = torch.empty((heads, nblk), dtype=torch.float32, device=device)
+        self.t16 = (torch.empty((heads, nblk, d, 64), dtype=torch.float16, device=device)
+                    if with_t16 else None)
+        self.c = tm_qtensor(_ptr(self.c8), _ptr(self.c4), _ptr(self.s8), _ptr(self.s4), _ptr(self.t16),
+                            heads, layout, nblk)
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def tm_quantize_pack(shape: Shape, x, out: QTensor, stream=None) -> QTensor:
+    """x: [T][heads][d] 16-bit device tensor (fp16/bf16 or its uint16 bits)."""
+    assert x.is_contiguous() and x.element_size() == 2
+    _check(lib().tm_quantize_pack(ctypes.byref(shape.c), _ptr(x), out.heads, ctypes.byref(out.c),
+                                  _stream(stream)), "tm_quantize_pack")
+    return out
+
+
+class Policy:
+    def __init__(self, pol: dict, device=None):
+        self.kind = int(pol["kind"])
+        self.b8 = self.b4 = None
+        self.bits = None
+        if self.kind == TM_POLICY_BOUNDARIES:
+            self.b8 = np.ascontiguousarray(np.asarray(pol["b8"], dtype=np.int32))
+            self.b4 = np.ascontiguousarray(np.asarray(pol["b4"], dtype=np.int32))
+            self.c = tm_policy(0, self.b8.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                               self.b4.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(pol.get("sink", 0)),
+                               None, 0, 1)
+        else:
+            import torch
+            words = np.ascontiguousarray(np.asarray(pol["words"], dtype=np.uint32))
+            self.bits = torch.from_numpy(words.view(np.int32).copy()).to(device) if device is not None else None
+            self.c = tm_policy(1, None, None, 0, _ptr(self.bits), int(words.size), int(pol["group"]))
+
+
+def traversal_bytes(shape: Shape, policy: Policy) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().tm_build_traversal(ctypes.byref(shape.c), ctypes.byref(policy.c), None, ctypes.byref(n),
+                                    None, None), "tm_build_traversal(size)")
+    return int(n.value)
+
+
+def tm_build_traversal(shape: Shape, policy: Policy, trav=None, census: bool = True, stream=None):
+    """Returns (trav uint8 device tensor, census dict or None)."""
+    import torch
+    need = traversal_bytes(shape, policy)
+    if trav is None:
+        trav = torch.empty(need, dtype=torch.uint8, device=shape.cu_dev.device)
+    n = ctypes.c_size_t(trav.numel())
+    cen = tm_census()
+    _check(lib().tm_build_traversal(ctypes.byref(shape.c), ctypes.byref(policy.c), _ptr(trav), ctypes.byref(n),
+                                    ctypes.byref(cen) if census else None, _stream(stream)),
+           "tm_build_traversal")
+    out = None
+    if census:
+        out = dict(legal=cen.legal, int8=cen.n_int8, int4=cen.n_int4, fp16=cen.n_fp16, skip=cen.n_skip,
+                   n_items=cen.n_items, max_runs=cen.max_runs)
+    return trav, out
+
+
+def tm_prefill(shape: Shape, trav, q, k, qq: QTensor, kq: QTensor, vq: QTensor, o=None, o_dtype=TM_F32,
+               lse=None, dbg_tiles=None, stream=None):
+    """Returns (o, lse, dbg_qk).  dbg_tiles: int32 device tensor [n][4] or None."""
+    import torch
+    dev = q.device
+    if o is None:
+        tdt = {TM_F32: torch.float32, TM_F16: torch.float16, TM_BF16: torch.bfloat16}[o_dtype]
+        o = torch.empty((shape.T, shape.hq, shape.d), dtype=tdt, device=dev)
+    dbg = None
+    n_dbg = 0
+    if dbg_tiles is not None:
+        n_dbg = int(dbg_tiles.shape[0])
+        dbg = torch.zeros((n_dbg, shape.bq, 64), dtype=torch.int32, device=dev)
+    _check(lib().tm_prefill(ctypes.byref(shape.c), _ptr(trav), _ptr(q), _ptr(k), ctypes.byref(qq.c),
+                            ctypes.byref(kq.c), ctypes.byref(vq.c), _ptr(o), o_dtype, _ptr(lse), _ptr(dbg),
+                            _ptr(dbg_tiles), n_dbg, _stream(stream)), "tm_prefill")
+    return o, lse, dbg
+
+
+class DPolicy:
+    def __init__(self, dpol: dict):
+        self.b8 = np.ascontiguousarray(np.asarray(dpol["b8"], dtype=np.int32))
+        self.b4 = np.ascontiguousarray(np.asarray(dpol["b4"], dtype=np.int32))
+        self.c = tm_dpolicy(self.b8.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                            self.b4.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(dpol["sink"]),
+                            int(dpol["tail"]))
+
+
+def decode_ws_bytes(shape: Shape, dpol: DPolicy) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().tm_decode(ctypes.byref(shape.c), None, None, None, None, ctypes.byref(dpol.c), None, TM_F32,
+                           None, ctypes.byref(n), None), "tm_decode(size)")
+    return int(n.value)
+
+
+def tm_decode(shape: Shape, q, kq: QTensor, vq: QTensor, k16, dpol: DPolicy, o=None, o_dtype=TM_F32, ws=None,
+              stream=None):
+    import torch
+    dev = q.device
+    if o is None:
+        o = torch.empty((len(shape.seqlens), shape.hq, shape.d),
+                        dtype=torch.float32 if o_dtype == TM_F32 else torch.float16, device=dev)
+    need = decode_ws_bytes(shape, dpol)
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check(lib().tm_decode(ctypes.byref(shape.c), _ptr(q), ctypes.byref(kq.c), ctypes.byref(vq.c), _ptr(k16),
+                           ctypes.byref(dpol.c), _ptr(o), o_dtype, _ptr(ws), ctypes.byref(n), _stream(stream)),
+           "tm_decode")
+    return o
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,199 @@
+// Policy expansion: per-head boundaries or a packed group bitmask become the
+// precision-grouped traversal that the prefill kernel walks.
+//
+// [TriAttention] "TriAttention: Unified Sparse Mixed-Precision Attention for
+// Long-Context LLM Inference", abstract: two diagonal-distance boundaries per
+// head, storage independent of context length; the boundaries generate
+// precision-grouped traversals and omitted tiles are skipped.
+// [TileMix] "TileMix: Tile-Centric Mixed-Precision Attention for LLM Inference
+// Acceleration", abstract: routing decisions packed into compact bitmasks; one
+// bit governs a group of adjacent key tiles; FP16 or INT8 per group; all legal
+// groups routed; variable-length batches.
+//
+// One thread per work item (sequence, query head, query tile).  Items are
+// ordered heavy-first: query tiles in descending index (more legal key tiles),
+// then sequence, then head, so the 4 heads sharing a KV head are adjacent.
+#include "tm_kernels.h"
+
+namespace tmx {
+
+
+__device__ __forceinline__ int seq_nq(const int32_t* cu, int s, int bq) {
+  return (cu[s + 1] - cu[s] + bq - 1) / bq;
+}
+
+// Number of items in levels >= i (levels are query-tile indices).
+__device__ __forceinline__ int64_t items_at_or_above(const TravArgs& a, int i) {
+  int64_t n = 0;
+  for (int s = 0; s < a.nseq; ++s) {
+    const int nq = seq_nq(a.cu, s, a.bq);
+    if (nq > i) n += nq - i;
+  }
+  return n * a.hq;
+}
+
+__device__ __forceinline__ void put_run(RunEntry* runs, uint32_t& n, uint32_t first, uint32_t count,
+                                        uint32_t prec) {
+  if (count == 0) return;
+  runs[n].ktile = first;
+  runs[n].count_prec = count | (prec << 24);
+  ++n;
+}
+
+__global__ __launch_bounds__(256) void trav_items_kernel(TravArgs a) {
+  const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k == 0) {
+    TravHeader* h = reinterpret_cast<TravHeader*>(a.trav);
+    h->magic = TM_TRAV_MAGIC;
+    h->version = TM_TRAV_VERSION;
+    h->kind = a.kind;
+    h->n_items = a.n_items;
+    h->max_runs = a.max_runs;
+    h->nseq = a.nseq;
+    h->hq = a.hq;
+    h->hkv = a.hkv;
+    h->bq = a.bq;
+    h->bk = a.bk;
+    h->d = a.d;
+    h->nblk = a.nblk;
+    h->seq_off = a.seq_off;
+    h->item_off = a.item_off;
+    h->run_off = a.run_off;
+    h->bits_off = a.bits_off;
+  }
+  if (k < static_cast<uint32_t>(a.nseq)) {
+    SeqEntry* st = reinterpret_cast<SeqEntry*>(a.trav + a.seq_off);
+    int blk = 0;
+    for (int s = 0; s < static_cast<int>(k); ++s) blk += (a.cu[s + 1] - a.cu[s] + kBlock - 1) / kBlock;
+    st[k].tok_start = a.cu[k];
+    st[k].len = a.cu[k + 1] - a.cu[k];
+    st[k].blk_start = blk;
+    st[k].nq = seq_nq(a.cu, k, a.bq);
+  }
+  if (k >= a.n_items) return;
+
+  // level (query tile index) of item k: largest i with items_at_or_above(i) > k
+  int maxnq = 0;
+  for (int s = 0; s < a.nseq; ++s) maxnq = max(maxnq, seq_nq(a.cu, s, a.bq));
+  int lo = 0, hi = maxnq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (items_at_or_above(a, mid) > static_cast<int64_t>(k)) lo = mid; else hi = mid - 1;
+  }
+  const int qt = lo;
+  const int64_t idx = static_cast<int64_t>(k) - items_at_or_above(a, qt + 1);
+  const int rank = static_cast<int>(idx / a.hq);
+  const int head = static_cast<int>(idx % a.hq);
+  int seq = -1, cnt = 0;
+  for (int s = 0; s < a.nseq; ++s) {
+    if (seq_nq(a.cu, s, a.bq) > qt) {
+      if (cnt == rank) { seq = s; break; }
+      ++cnt;
+    }
+  }
+  const int len = a.cu[seq + 1] - a.cu[seq];
+  const int jmax = (min((qt + 1) * a.bq, len) - 1) / a.bk;
+  const int legal = jmax + 1;
+  RunEntry* runs = reinterpret_cast<RunEntry*>(a.trav + a.run_off) + static_cast<size_t>(k) * a.max_runs;
+  uint32_t nr = 0, n8 = 0, n4 = 0, n16 = 0;
+
+  if (a.kind == TM_POLICY_BOUNDARIES) {
+    const int b8 = a.b8[head], b4 = a.b4[head];
+    const int ri = qt * (a.bq / a.bk);
+    // INT8 band [lo8, jmax]; INT4 band [lo4, hi4]; SKIP [0, lo4)
+    const int lo8 = (b8 > 0) ? max(0, ri - b8 + 1) : legal;
+    int lo4 = (b4 > 0) ? max(0, ri - b4 + 1) : legal;
+    int hi4 = (b8 > 0) ? lo8 - 1 : jmax;
+    if (b4 == 0) hi4 = -1;
+    lo4 = min(lo4, legal);
+    hi4 = min(hi4, jmax);
+    const bool sink_extra = a.sink && lo8 > 0;
+    if (sink_extra && lo4 == 0) lo4 = 1;   // tile 0 leaves the INT4 band for the sink run
+    const uint32_t c8 = lo8 <= jmax ? static_cast<uint32_t>(jmax - lo8 + 1) : 0u;
+    const uint32_t c4 = hi4 >= lo4 ? static_cast<uint32_t>(hi4 - lo4 + 1) : 0u;
+    put_run(runs, nr, lo8, c8, TM_INT8);
+    if (sink_extra) put_run(runs, nr, 0, 1, TM_INT8);
+    put_run(runs, nr, lo4, c4, TM_INT4);
+    n8 = c8 + (sink_extra ? 1u : 0u);
+    n4 = c4;
+  } else {
+    const int G = a.group;
+    int base = 0;
+    for (int s = 0; s < seq; ++s) {
+      const int ln = a.cu[s + 1] - a.cu[s];
+      const int nk = (ln + a.bk - 1) / a.bk;
+      const int wpr = ((nk + G - 1) / G + 31) / 32;
+      base += a.hq * seq_nq(a.cu, s, a.bq) * wpr;
+    }
+    const int nk = (len + a.bk - 1) / a.bk;
+    const int wpr = ((nk + G - 1) / G + 31) / 32;
+    const int nq = seq_nq(a.cu, seq, a.bq);
+    const uint32_t* row = a.bits + base + static_cast<size_t>(head * nq + qt) * wpr;
+    const int ng = jmax / G + 1;
+    for (int pass = 0; pass < 2; ++pass) {        // FP16 runs first, then INT8
+      const uint32_t want = pass == 0 ? 1u : 0u;
+      int g = 0;
+      while (g < ng) {
+        const uint32_t bit = (row[g >> 5] >> (g & 31)) & 1u;
+        if (bit != want) { ++g; continue; }
+        int g1 = g;
+        while (g1 + 1 < ng && ((row[(g1 + 1) >> 5] >> ((g1 + 1) & 31)) & 1u) == want) ++g1;
+        const int first = g * G;
+        const int last = min((g1 + 1) * G - 1, jmax);
+        const uint32_t c = static_cast<uint32_t>(last - first + 1);
+        put_run(runs, nr, first, c, want ? TM_FP16 : TM_INT8);
+        if (want) n16 += c; else n8 += c;
+        g = g1 + 1;
+      }
+    }
+  }
+  ItemEntry* it = reinterpret_cast<ItemEntry*>(a.trav + a.item_off) + k;
+  it->seq = seq;
+  it->head = head;
+  it->qtile = qt;
+  it->nruns = nr;
+  it->n8 = n8;
+  it->n4 = n4;
+  it->n16 = n16;
+  it->nskip = static_cast<uint32_t>(legal) - n8 - n4 - n16;
+}
+
+// Deterministic census: one workgroup sums the per-item counts.
+__global__ __launch_bounds__(256) void trav_census_kernel(uint8_t* trav, uint32_t item_off, uint32_t n_items) {
+  const ItemEntry* it = reinterpret_cast<const ItemEntry*>(trav + item_off);
+  int64_t c[4] = {0, 0, 0, 0};
+  for (uint32_t k = threadIdx.x; k < n_items; k += blockDim.x) {
+    c[0] += it[k].n8;
+    c[1] += it[k].n4;
+    c[2] += it[k].n16;
+    c[3] += it[k].nskip;
+  }
+  __shared__ int64_t red[4][256];
+  for (int i = 0; i < 4; ++i) red[i][threadIdx.x] = c[i];
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (static_cast<int>(threadIdx.x) < s)
+      for (int i = 0; i < 4; ++i) red[i][threadIdx.x] += red[i][threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    TravHeader* h = reinterpret_cast<TravHeader*>(trav);
+    h->census[0] = red[0][0] + red[1][0] + red[2][0] + red[3][0];
+    h->census[1] = red[0][0];
+    h->census[2] = red[1][0];
+    h->census[3] = red[2][0];
+    h->census[4] = red[3][0];
+  }
+}
+
+hipError_t launch_traversal(const TravArgs& a, hipStream_t st) {
+  const unsigned n = max(a.n_items, static_cast<uint32_t>(a.nseq));
+  const unsigned blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(trav_items_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(trav_census_kernel, dim3(1), dim3(256), 0, st, a.trav, a.item_off, a.n_items);
+  return hipGetLastError();
+}
+
+}  // namespace tmx

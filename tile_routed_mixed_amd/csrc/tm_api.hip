@@ -1,0 +1,354 @@
+// C ABI of libtm: host-side validation, sizing and launches.  Every check runs
+// before anything is enqueued, so a nonzero status leaves outputs untouched.
+// The entry points follow include/tm.h (which cites the method pages).
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "tm_kernels.h"
+
+using namespace tmx;
+
+namespace {
+
+constexpr int32_t kVersion = (1 << 16) | 0;
+
+struct ShapeInfo {
+  int64_t T = 0;
+  int64_t nblk = 0;
+  int64_t n_items = 0;
+  int maxnq = 0;
+  int maxnk = 0;
+};
+
+tm_status check_shape(const tm_shape* s, bool tiles, ShapeInfo* info) {
+  if (s == nullptr || s->cu_seqlens == nullptr) return TM_E_ARG;
+  if (s->nseq < 1) return TM_E_SHAPE;
+  if (s->d != 64 && s->d != 128) return TM_E_SHAPE;
+  if (s->hq < 1 || s->hkv < 1 || s->hq % s->hkv != 0) return TM_E_SHAPE;
+  if (s->dtype != TM_F16 && s->dtype != TM_BF16) return TM_E_SHAPE;
+  if (tiles) {
+    if (s->bk != 64) return TM_E_SHAPE;
+    if (s->bq != 64 && s->bq != 128) return TM_E_SHAPE;
+  }
+  if (s->cu_seqlens[0] != 0) return TM_E_SHAPE;
+  ShapeInfo r;
+  for (int i = 0; i < s->nseq; ++i) {
+    const int64_t a = s->cu_seqlens[i], b = s->cu_seqlens[i + 1];
+    if (b < a) return TM_E_SHAPE;
+    const int64_t len = b - a;
+    r.nblk += (len + 63) / 64;
+    if (tiles) {
+      const int64_t nq = (len + s->bq - 1) / s->bq;
+      r.n_items += nq * s->hq;
+      r.maxnq = static_cast<int>(std::max<int64_t>(r.maxnq, nq));
+      r.maxnk = static_cast<int>(std::max<int64_t>(r.maxnk, (len + 63) / 64));
+    }
+  }
+  r.T = s->cu_seqlens[s->nseq];
+  if (r.T > (int64_t{1} << 30)) return TM_E_SHAPE;
+  if (r.n_items > 0x7FFFFFFF) return TM_E_SHAPE;
+  if (info) *info = r;
+  return TM_OK;
+}
+
+tm_status check_qtensor(const tm_qtensor* t, int heads, int layout, int64_t nblk, bool need_t16) {
+  if (t == nullptr || t->c8 == nullptr || t->c4 == nullptr || t->s8 == nullptr || t->s4 == nullptr)
+    return TM_E_ARG;
+  if (need_t16 && t->t16 == nullptr) return TM_E_ARG;
+  if (t->heads != heads || t->layout != layout || t->nblk != nblk) return TM_E_SHAPE;
+  return TM_OK;
+}
+
+float tau_log2e(const tm_shape* s) {
+  const float tau = s->softmax_scale > 0.0f ? s->softmax_scale : 1.0f / std::sqrt(static_cast<float>(s->d));
+  return tau * kLog2e;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct TravLayout {
+  size_t seq_off, item_off, run_off, bytes;
+  uint32_t max_runs;
+};
+
+TravLayout trav_layout(const tm_shape* s, const ShapeInfo& si, const tm_policy* p) {
+  TravLayout L;
+  L.max_runs = p->kind == TM_POLICY_BOUNDARIES ? 3u
+                                               : static_cast<uint32_t>(std::max(1, (si.maxnk + p->group - 1) / p->group));
+  L.seq_off = TM_TRAV_HEADER_BYTES;
+  L.item_off = align256(L.seq_off + sizeof(SeqEntry) * static_cast<size_t>(s->nseq));
+  L.run_off = align256(L.item_off + sizeof(ItemEntry) * static_cast<size_t>(si.n_items));
+  L.bytes = align256(L.run_off + sizeof(RunEntry) * static_cast<size_t>(si.n_items) * L.max_runs);
+  return L;
+}
+
+int64_t bitmask_words(const tm_shape* s, int group) {
+  int64_t w = 0;
+  for (int i = 0; i < s->nseq; ++i) {
+    const int64_t len = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
+    const int64_t nk = (len + s->bk - 1) / s->bk;
+    const int64_t ng = (nk + group - 1) / group;
+    w += static_cast<int64_t>(s->hq) * ((len + s->bq - 1) / s->bq) * ((ng + 31) / 32);
+  }
+  return w;
+}
+
+struct DecodePlan {
+  int nsplit;
+  size_t ws_bytes;
+};
+
+DecodePlan decode_plan(const tm_shape* s, const tm_dpolicy* p) {
+  int maxex = 1;
+  for (int b = 0; b < s->nseq; ++b) {
+    const int L = s->cu_seqlens[b + 1] - s->cu_seqlens[b];
+    const int nb = (L + 63) / 64;
+    const int jf = p->tail_tokens > 0 ? std::max(0, (L - p->tail_tokens) / 64) : nb;
+    for (int g = 0; g < s->hkv; ++g) {
+      const int jlo = std::max(0, nb - p->b4[g]);
+      const int js = std::min(jlo, jf);
+      const int nex = (nb - js) + ((p->sink && js > 0) ? 1 : 0);
+      maxex = std::max(maxex, nex);
+    }
+  }
+  const int pairs = s->nseq * s->hkv;
+  int ns = (2048 + pairs - 1) / pairs;
+  ns = std::min(ns, std::max(1, maxex / 4));
+  ns = std::max(1, std::min(ns, 256));
+  DecodePlan d;
+  d.nsplit = ns;
+  d.ws_bytes = static_cast<size_t>(s->nseq) * s->hq * ns * (s->d + 2) * sizeof(float);
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tm_status_string(int32_t st) {
+  switch (st) {
+    case TM_OK: return "TM_OK";
+    case TM_E_ARG: return "TM_E_ARG: NULL or out-of-range argument";
+    case TM_E_SHAPE: return "TM_E_SHAPE: inconsistent or unsupported shape";
+    case TM_E_POLICY: return "TM_E_POLICY: invalid policy";
+    case TM_E_SPACE: return "TM_E_SPACE: caller buffer too small";
+    case TM_E_UNSUPPORTED: return "TM_E_UNSUPPORTED: not implemented for these arguments";
+    case TM_E_HIP: return "TM_E_HIP: HIP launch or copy failed";
+    default: return "unknown tm_status";
+  }
+}
+
+int32_t tm_version(void) { return kVersion; }
+
+int64_t tm_num_blocks(const tm_shape* shape) {
+  ShapeInfo si;
+  if (check_shape(shape, false, &si) != TM_OK) return -1;
+  return si.nblk;
+}
+
+tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads, tm_qtensor* out, void* stream) {
+  ShapeInfo si;
+  tm_status st = check_shape(shape, false, &si);
+  if (st != TM_OK) return st;
+  if (shape->cu_seqlens_dev == nullptr || x == nullptr || out == nullptr || heads < 1) return TM_E_ARG;
+  if (out->layout != TM_ROWS && out->layout != TM_COLS) return TM_E_ARG;
+  if (out->layout == TM_ROWS && out->t16 != nullptr) return TM_E_ARG;
+  st = check_qtensor(out, heads, out->layout, si.nblk, false);
+  if (st != TM_OK) return st;
+  if (si.nblk == 0) return TM_OK;
+  QuantArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.cu = shape->cu_seqlens_dev;
+  a.nseq = shape->nseq;
+  a.heads = heads;
+  a.nblk = si.nblk;
+  a.c8 = out->c8;
+  a.c4 = out->c4;
+  a.s8 = out->s8;
+  a.s4 = out->s4;
+  a.t16 = out->t16;
+  const hipError_t e = launch_quantize(a, shape->d, shape->dtype == TM_BF16, out->layout == TM_COLS,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TM_OK : TM_E_HIP;
+}
+
+tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, void* trav, size_t* trav_bytes,
+                             tm_census* census, void* stream) {
+  ShapeInfo si;
+  tm_status st = check_shape(shape, true, &si);
+  if (st != TM_OK) return st;
+  if (policy == nullptr || trav_bytes == nullptr) return TM_E_ARG;
+  if (policy->kind == TM_POLICY_BOUNDARIES) {
+    if (policy->b8 == nullptr || policy->b4 == nullptr) return TM_E_ARG;
+    if (shape->hq > kMaxHeadsArg) return TM_E_UNSUPPORTED;
+    if (policy->sink != 0 && policy->sink != 1) return TM_E_POLICY;
+    for (int h = 0; h < shape->hq; ++h) {
+      const int b8 = policy->b8[h], b4 = policy->b4[h];
+      if (b8 < 0 || b4 < 0 || b8 > b4) return TM_E_POLICY;
+      if (b4 == 0 && !policy->sink) return TM_E_POLICY;
+    }
+  } else if (policy->kind == TM_POLICY_BITMASK) {
+    if (policy->group < 1) return TM_E_POLICY;
+    if (policy->n_words < bitmask_words(shape, policy->group)) return TM_E_POLICY;
+    if (policy->bits == nullptr && policy->n_words > 0) return TM_E_ARG;
+  } else {
+    return TM_E_ARG;
+  }
+  const TravLayout L = trav_layout(shape, si, policy);
+  if (trav == nullptr) {
+    *trav_bytes = L.bytes;
+    return TM_OK;
+  }
+  if (*trav_bytes < L.bytes) return TM_E_SPACE;
+  if (shape->cu_seqlens_dev == nullptr) return TM_E_ARG;
+  if (L.bytes > 0xFFFFFFFFull) return TM_E_SHAPE;
+
+  TravArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.trav = static_cast<uint8_t*>(trav);
+  a.cu = shape->cu_seqlens_dev;
+  a.bits = policy->bits;
+  a.nseq = shape->nseq;
+  a.hq = shape->hq;
+  a.hkv = shape->hkv;
+  a.d = shape->d;
+  a.bq = shape->bq;
+  a.bk = shape->bk;
+  a.kind = policy->kind;
+  a.sink = policy->kind == TM_POLICY_BOUNDARIES ? policy->sink : 0;
+  a.group = policy->kind == TM_POLICY_BITMASK ? policy->group : 1;
+  a.n_items = static_cast<uint32_t>(si.n_items);
+  a.max_runs = L.max_runs;
+  a.nblk = static_cast<uint32_t>(si.nblk);
+  a.seq_off = static_cast<uint32_t>(L.seq_off);
+  a.item_off = static_cast<uint32_t>(L.item_off);
+  a.run_off = static_cast<uint32_t>(L.run_off);
+  a.bits_off = 0;
+  if (policy->kind == TM_POLICY_BOUNDARIES) {
+    for (int h = 0; h < shape->hq; ++h) {
+      a.b8[h] = policy->b8[h];
+      a.b4[h] = policy->b4[h];
+    }
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (launch_traversal(a, hs) != hipSuccess) return TM_E_HIP;
+  if (census != nullptr) {
+    TravHeader h;
+    if (hipMemcpyAsync(&h, trav, sizeof(h), hipMemcpyDeviceToHost, hs) != hipSuccess) return TM_E_HIP;
+    if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;
+    census->legal = h.census[0];
+    census->n_int8 = h.census[1];
+    census->n_int4 = h.census[2];
+    census->n_fp16 = h.census[3];
+    census->n_skip = h.census[4];
+    census->n_items = si.n_items;
+    census->max_runs = L.max_runs;
+  }
+  return TM_OK;
+}
+
+tm_status tm_prefill(const tm_shape* shape, const void* trav, const void* q, const void* k,
+                     const tm_qtensor* qq, const tm_qtensor* kq, const tm_qtensor* vq, void* o, int32_t o_dtype,
+                     float* lse, int32_t* dbg_qk, const int32_t* dbg_tiles, int32_t n_dbg, void* stream) {
+  ShapeInfo si;
+  tm_status st = check_shape(shape, true, &si);
+  if (st != TM_OK) return st;
+  if (trav == nullptr || q == nullptr || k == nullptr || o == nullptr) return TM_E_ARG;
+  if (o_dtype != TM_F32 && o_dtype != TM_F16 && o_dtype != TM_BF16) return TM_E_ARG;
+  if (n_dbg < 0 || (n_dbg > 0 && (dbg_qk == nullptr || dbg_tiles == nullptr))) return TM_E_ARG;
+  if ((st = check_qtensor(qq, shape->hq, TM_ROWS, si.nblk, false)) != TM_OK) return st;
+  if ((st = check_qtensor(kq, shape->hkv, TM_ROWS, si.nblk, false)) != TM_OK) return st;
+  if ((st = check_qtensor(vq, shape->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
+  PrefillArgs a;
+  a.trav = static_cast<const uint8_t*>(trav);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.q8 = qq->c8;
+  a.q4 = qq->c4;
+  a.qs8 = qq->s8;
+  a.qs4 = qq->s4;
+  a.k8 = kq->c8;
+  a.k4 = kq->c4;
+  a.ks8 = kq->s8;
+  a.ks4 = kq->s4;
+  a.vt16 = vq->t16;
+  a.o = o;
+  a.lse = lse;
+  a.dbg_qk = dbg_qk;
+  a.dbg_tiles = dbg_tiles;
+  a.n_dbg = n_dbg;
+  a.o_dtype = o_dtype;
+  a.hq = shape->hq;
+  a.hkv = shape->hkv;
+  a.T = static_cast<int>(si.T);
+  a.nblk = si.nblk;
+  a.n_items = static_cast<uint32_t>(si.n_items);
+  a.tau_log2e = tau_log2e(shape);
+  const hipError_t e = launch_prefill(a, shape->d, shape->bq, shape->dtype == TM_BF16,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TM_OK : TM_E_HIP;
+}
+
+tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, const tm_qtensor* vq,
+                    const void* k16, const tm_dpolicy* policy, void* o, int32_t o_dtype, void* ws,
+                    size_t* ws_bytes, void* stream) {
+  ShapeInfo si;
+  tm_status st = check_shape(cache, false, &si);
+  if (st != TM_OK) return st;
+  if (cache->dtype != TM_F16) return TM_E_UNSUPPORTED;
+  if (cache->hq / cache->hkv > 16 || cache->hkv > kMaxKvArg) return TM_E_UNSUPPORTED;
+  if (policy == nullptr || policy->b8 == nullptr || policy->b4 == nullptr || ws_bytes == nullptr) return TM_E_ARG;
+  if (policy->sink != 0 && policy->sink != 1) return TM_E_POLICY;
+  if (policy->tail_tokens < 0) return TM_E_POLICY;
+  for (int g = 0; g < cache->hkv; ++g) {
+    const int b8 = policy->b8[g], b4 = policy->b4[g];
+    if (b8 < 0 || b4 < 0 || b8 > b4) return TM_E_POLICY;
+    if (b4 == 0 && policy->tail_tokens == 0 && !policy->sink) return TM_E_POLICY;
+  }
+  for (int b = 0; b < cache->nseq; ++b)
+    if (cache->cu_seqlens[b + 1] - cache->cu_seqlens[b] < 1) return TM_E_SHAPE;
+  const DecodePlan plan = decode_plan(cache, policy);
+  if (ws == nullptr) {
+    *ws_bytes = plan.ws_bytes;
+    return TM_OK;
+  }
+  if (*ws_bytes < plan.ws_bytes) return TM_E_SPACE;
+  if (cache->cu_seqlens_dev == nullptr || q == nullptr || k16 == nullptr || o == nullptr) return TM_E_ARG;
+  if (o_dtype != TM_F32 && o_dtype != TM_F16) return TM_E_ARG;
+  if ((st = check_qtensor(kq, cache->hkv, TM_ROWS, si.nblk, false)) != TM_OK) return st;
+  if ((st = check_qtensor(vq, cache->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.cu = cache->cu_seqlens_dev;
+  a.k8 = kq->c8;
+  a.k4 = kq->c4;
+  a.ks8 = kq->s8;
+  a.ks4 = kq->s4;
+  a.v8 = vq->c8;
+  a.v4 = vq->c4;
+  a.vs8 = vq->s8;
+  a.vs4 = vq->s4;
+  a.vt16 = vq->t16;
+  a.k16 = static_cast<const uint16_t*>(k16);
+  a.ws = static_cast<float*>(ws);
+  a.o = o;
+  a.o_dtype = o_dtype;
+  a.nseq = cache->nseq;
+  a.hq = cache->hq;
+  a.hkv = cache->hkv;
+  a.nsplit = plan.nsplit;
+  a.sink = policy->sink;
+  a.tail = policy->tail_tokens;
+  a.nblk = si.nblk;
+  a.tau_log2e = tau_log2e(cache);
+  for (int g = 0; g < cache->hkv; ++g) {
+    a.b8[g] = policy->b8[g];
+    a.b4[g] = policy->b4[g];
+  }
+  const hipError_t e = launch_decode(a, cache->d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TM_OK : TM_E_HIP;
+}
+
+}  // extern "C"

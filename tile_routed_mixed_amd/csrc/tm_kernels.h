@@ -1,0 +1,89 @@
+// Kernel argument blocks and launchers shared by the HIP sources and the C ABI.
+#pragma once
+
+#include "tm_common.h"
+
+namespace tmx {
+
+constexpr int kMaxHeadsArg = 256;   // boundary tables passed by value
+constexpr int kMaxKvArg = 64;
+
+struct QuantArgs {
+  const uint16_t* x;
+  const int32_t* cu;
+  int nseq;
+  int heads;
+  int64_t nblk;
+  int8_t* c8;
+  uint8_t* c4;
+  float* s8;
+  float* s4;
+  uint16_t* t16;
+};
+
+struct TravArgs {
+  uint8_t* trav;
+  const int32_t* cu;
+  const uint32_t* bits;     // device bitmask (bitmask policies)
+  int nseq, hq, hkv, d, bq, bk;
+  int kind, sink, group;
+  uint32_t n_items, max_runs, nblk;
+  uint32_t seq_off, item_off, run_off, bits_off;
+  int32_t b8[kMaxHeadsArg];
+  int32_t b4[kMaxHeadsArg];
+};
+
+struct PrefillArgs {
+  const uint8_t* trav;
+  const uint16_t* q;
+  const uint16_t* k;
+  const int8_t* q8;
+  const uint8_t* q4;
+  const float* qs8;
+  const float* qs4;
+  const int8_t* k8;
+  const uint8_t* k4;
+  const float* ks8;
+  const float* ks4;
+  const uint16_t* vt16;
+  void* o;
+  float* lse;
+  int32_t* dbg_qk;
+  const int32_t* dbg_tiles;
+  int n_dbg;
+  int o_dtype;
+  int hq, hkv, T;
+  int64_t nblk;
+  uint32_t n_items;   // grid size; the traversal header holds the rest
+  float tau_log2e;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;       // [B][hq][D] fp16
+  const int32_t* cu;
+  const int8_t* k8;        // rows  [hkv][nblk][64][D]
+  const uint8_t* k4;       // rows  [hkv][nblk][64][D/2]
+  const float* ks8;
+  const float* ks4;
+  const int8_t* v8;        // cols  [hkv][nblk][D][64]
+  const uint8_t* v4;       // cols  [hkv][nblk][D][32]
+  const float* vs8;
+  const float* vs4;
+  const uint16_t* vt16;    // cols  [hkv][nblk][D][64] fp16
+  const uint16_t* k16;     // [T][hkv][D] fp16
+  float* ws;               // [B][hq][nsplit][D + 2]
+  void* o;
+  int o_dtype;
+  int nseq, hq, hkv, nsplit, sink, tail;
+  int64_t nblk;
+  float tau_log2e;
+  int32_t b8[kMaxKvArg];
+  int32_t b4[kMaxKvArg];
+};
+
+hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
+hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, bool bf16, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t st);
+
+}  // namespace tmx

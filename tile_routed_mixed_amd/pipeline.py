@@ -1,0 +1,110 @@
+"""Device-buffer plumbing around the four entry points.
+
+PrefillPipeline holds the device copies of Q, K, V and every buffer the
+prefill path writes, and runs one pass of the path:
+  tm_quantize_pack(Q, rows)  tm_quantize_pack(K, rows)
+  tm_quantize_pack(V, cols + fp16 copy)   tm_build_traversal   tm_prefill.
+DecodePipeline does the same for one decode step over a quantized cache.
+Nothing here computes: buffers are allocated once and the C ABI is called.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import _binding as B
+
+
+def _dev_bits(bits: np.ndarray, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).to(device)
+
+
+class PrefillPipeline:
+    def __init__(self, seqlens, hq, hkv, d, bq, dtype: str, policy: dict, device="cuda:0", softmax_scale=0.0):
+        self.dt = B.TM_BF16 if dtype == "bf16" else B.TM_F16
+        self.shape = B.Shape(seqlens, hq, hkv, d, bq, 64, self.dt, softmax_scale, device=device)
+        self.device = device
+        self.policy = B.Policy(policy, device=device)
+        self.qq = B.QTensor(self.shape, hq, B.TM_ROWS, False, device)
+        self.kq = B.QTensor(self.shape, hkv, B.TM_ROWS, False, device)
+        self.vq = B.QTensor(self.shape, hkv, B.TM_COLS, True, device)
+        import torch
+        self.trav = torch.empty(B.traversal_bytes(self.shape, self.policy), dtype=torch.uint8, device=device)
+        self.q = self.k = self.v = None
+        self.o = None
+        self.lse = torch.empty((hq, self.shape.T), dtype=torch.float32, device=device)
+
+    def upload(self, q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray):
+        self.q = _dev_bits(q_bits, self.device)
+        self.k = _dev_bits(k_bits, self.device)
+        self.v = _dev_bits(v_bits, self.device)
+
+    def quantize(self, stream=None):
+        B.tm_quantize_pack(self.shape, self.q, self.qq, stream)
+        B.tm_quantize_pack(self.shape, self.k, self.kq, stream)
+        B.tm_quantize_pack(self.shape, self.v, self.vq, stream)
+
+    def traversal(self, census=False, stream=None):
+        _, c = B.tm_build_traversal(self.shape, self.policy, self.trav, census=census, stream=stream)
+        return c
+
+    def prefill(self, o_dtype=B.TM_F32, dbg_tiles=None, stream=None, with_lse=True):
+        if self.o is None or self.o_dtype != o_dtype:
+            import torch
+            tdt = {B.TM_F32: torch.float32, B.TM_F16: torch.float16, B.TM_BF16: torch.bfloat16}[o_dtype]
+            self.o = torch.empty((self.shape.T, self.shape.hq, self.shape.d), dtype=tdt, device=self.device)
+            self.o_dtype = o_dtype
+        _, _, dbg = B.tm_prefill(self.shape, self.trav, self.q, self.k, self.qq, self.kq, self.vq, o=self.o,
+                                 o_dtype=o_dtype, lse=self.lse if with_lse else None, dbg_tiles=dbg_tiles,
+                                 stream=stream)
+        return self.o, dbg
+
+    def step(self, o_dtype=B.TM_F32, stream=None):
+        self.quantize(stream)
+        self.traversal(False, stream)
+        return self.prefill(o_dtype, stream=stream)[0]
+
+
+class DecodePipeline:
+    """One decode step: the cache is K (rows) and V (cols + fp16 copy) quantized
+    over the cached tokens, plus the 16-bit keys for FP16 blocks."""
+
+    def __init__(self, seqlens, hq, hkv, d, dpolicy: dict, device="cuda:0", softmax_scale=0.0):
+        self.shape = B.Shape(seqlens, hq, hkv, d, 128, 64, B.TM_F16, softmax_scale, device=device)
+        self.device = device
+        self.dpol = B.DPolicy(dpolicy)
+        self.kq = B.QTensor(self.shape, hkv, B.TM_ROWS, False, device)
+        self.vq = B.QTensor(self.shape, hkv, B.TM_COLS, True, device)
+        import torch
+        self.ws = torch.empty(max(4, B.decode_ws_bytes(self.shape, self.dpol)), dtype=torch.uint8, device=device)
+        self.o = torch.empty((len(seqlens), hq, d), dtype=torch.float32, device=device)
+        self.q = self.k = self.v = None
+
+    def upload(self, q_bits, k_bits, v_bits):
+        self.q = _dev_bits(q_bits, self.device)
+        self.k = _dev_bits(k_bits, self.device)
+        self.v = _dev_bits(v_bits, self.device)
+
+    def build_cache(self, stream=None):
+        B.tm_quantize_pack(self.shape, self.k, self.kq, stream)
+        B.tm_quantize_pack(self.shape, self.v, self.vq, stream)
+
+    def decode(self, stream=None):
+        return B.tm_decode(self.shape, self.q, self.kq, self.vq, self.k, self.dpol, o=self.o, ws=self.ws,
+                           stream=stream)
+
+
+def read_traversal(trav_host: np.ndarray):
+    """Decode a traversal buffer copied to the host (layout in include/tm.h)."""
+    b = np.ascontiguousarray(trav_host).view(np.uint8)
+    h = b[:B.TRAV_HEADER_BYTES].view(np.uint32)
+    magic, version, kind, n_items, max_runs, nseq = (int(x) for x in h[:6])
+    seq_off, item_off, run_off = int(h[12]), int(h[13]), int(h[14])
+    census = b[128:128 + 40].view(np.int64)
+    seqs = b[seq_off:seq_off + 16 * nseq].view(np.uint32).reshape(nseq, 4)
+    items = b[item_off:item_off + 32 * n_items].view(np.uint32).reshape(n_items, 8)
+    runs = b[run_off:run_off + 8 * n_items * max_runs].view(np.uint32).reshape(n_items, max_runs, 2)
+    return dict(magic=magic, version=version, kind=kind, n_items=n_items, max_runs=max_runs, seqs=seqs,
+                items=items, runs=runs, census=dict(legal=int(census[0]), int8=int(census[1]),
+                                                    int4=int(census[2]), fp16=int(census[3]),
+                                                    skip=int(census[4])))

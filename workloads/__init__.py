@@ -112,11 +112,13 @@ def small(name: str, seqlens: List[int], **kw) -> Workload:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16, half to even; returns the uint16 bit patterns."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    nan = np.isnan(x)
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # uint32 cannot overflow here except for NaN patterns, which are fixed below
+    rounded = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     out = rounded.astype(np.uint16)
-    out[nan] = 0x7FC0
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = 0x7FC0
     return out
 
 
