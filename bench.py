@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the tile-routed mixed-precision attention hot path on one GPU.
+
+One step = one pass of the whole path over one batch of synthetic input that
+is already resident in HBM:
+  tm_quantize_pack(Q), tm_quantize_pack(K), tm_quantize_pack(V, transposed +
+  fp16 copy), tm_build_traversal, tm_prefill, and tm_decode of one new query
+  per sequence over the compressed cache the prefill just quantized.
+
+Default workload: one 8192-token sequence, 32 query / 8 KV heads, d = 128, bf16,
+128x64 tiles, K with 4 outlier channels x10, per-head random diagonal-distance
+boundaries (about 40 % of legal tiles skipped).  ``value`` is the effective
+dense-causal prefill rate of the whole step: 4*d*hq*S^2/2 FLOPs per step over
+the measured step time.  A decode sub-benchmark (16 sequences x 32768 cached
+tokens, rotating three caches so the read set exceeds the 256 MB last-level
+cache) reports compressed-cache read GB/s.
+
+Prints one JSON line.  --gpus N > 1 is refused: this path runs on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective prefill attn TFLOP/s (dense-causal) + MFMA util; decode KV GB/s"
+PEAK_F16 = 2.5e15     # MI355X dense MFMA, fp16/bf16 (FLOP/s)
+PEAK_I8 = 5.0e15      # MI355X dense MFMA, int8 (OP/s)
+PEAK_HBM = 8.0e12     # MI355X HBM3E (B/s)
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_gqa8k_pmc.json")
+PREFILL_SRC = os.path.join(ROOT, "tile_routed_mixed_amd", "csrc", "k_prefill.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def describe(w):
+    pol = "per-head diagonal-distance boundaries" if w.policy == "boundaries" else \
+        f"packed bitmask, {w.group} key tiles per bit, P(FP16)={w.p_fp16}"
+    return (f"{w.name}: seqs {w.seqlens if len(w.seqlens) <= 4 else str(len(w.seqlens)) + 'x' + str(w.seqlens[0])}"
+            f", {w.hq}/{w.hkv} heads, d={w.d}, {w.dtype}, {w.bq}x{w.bk} tiles, {pol}"
+            + (", key tile 0 INT8" if w.sink else "") + (f", K outliers {w.outliers}x{w.outlier_scale:g}"
+                                                          if w.outliers else ""))
+
+
+def dense_causal_flops(w):
+    return sum(4.0 * w.d * w.hq * S * S / 2.0 for S in w.seqlens)
+
+
+def decode_policy_for(S):
+    """Cache tags for the decode step after a prefill of S tokens: the toy
+    workload's bands (INT8 below 2/8, INT4 below 5/8 of the blocks) scaled to the
+    cache, first block INT8, last 128 tokens FP16."""
+    nb = -(-S // 64)
+    b8 = max(1, nb // 4)
+    return b8, max(b8, (nb * 5) // 8)
+
+
+def prefill_roofline(w, census, t_prefill):
+    qk = 2.0 * w.bq * w.bk * w.d
+    pv = 2.0 * w.bq * w.bk * w.d
+    n_int = census["int8"] + census["int4"]
+    n16 = census["fp16"]
+    ops = (n_int + n16) * (qk + pv)
+    t_peak = n_int * qk / PEAK_I8 + n16 * qk / PEAK_F16 + (n_int + n16) * pv / PEAK_F16
+    return ops, t_peak
+
+
+def pmc_traffic():
+    """HBM bytes per prefill launch from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        s = json.load(open(PMC_SUMMARY))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()
+    if s.get("kernel_source_sha256") != h:
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, pol, seconds):
+    """The oracle (numpy float64) on a bounded, seeded sample of whole query
+    tiles of the same workload, timed on this host's cores."""
+    import numpy as np
+    from oracle import attention as OA
+    from oracle import quant as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    qq = OQ.quantize(q[1], w.seqlens)
+    kq = OQ.quantize(k[1], w.seqlens)
+    q64, k64, v64 = (x[1].astype(np.float64) for x in (q, k, v))
+    rng = np.random.default_rng(12345)
+    items = [(s, h, i) for s, S in enumerate(w.seqlens) for h in range(w.hq) for i in range(-(-S // w.bq))]
+    order = rng.permutation(len(items))
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    for n in order:
+        s, h, i = items[n]
+        OA.prefill(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.bk, pol, q64, k64, v64, qq, kq, qtiles=[(s, h, i)])
+        r0, r1 = i * w.bq, min((i + 1) * w.bq, w.seqlens[s])
+        flops += sum(4.0 * w.d * (r + 1) for r in range(r0, r1))
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(items)} (sequence, head, query tile) items drawn with seed 12345, "
+                      f"{dt:.1f} s; attention rows only (codes precomputed); dense-causal FLOPs of those rows"}
+
+
+def decode_bench(steps, rotate=3):
+    """Decode over a 16 x 32768-token compressed cache; returns timing and bytes."""
+    import numpy as np
+    import torch
+    import tile_routed_mixed_amd as T
+    import workloads as W
+    from oracle import policy as OP
+    w = W.get("decode16x32k")
+    dpol = W.make_decode_policy(w)
+    _, k, v = W.make_qkv(w)
+    dq = W.make_decode_query(w)
+    caches = []
+    for c in range(rotate):
+        p = T.DecodePipeline(w.seqlens, w.hq, w.hkv, w.d, dpol, dtype=w.dtype)
+        p.upload(dq[0], k[0], v[0])
+        p.build_cache()
+        caches.append(p)
+    del k, v
+    torch.cuda.synchronize()
+    # algorithmic bytes: codes + two scales of every INT block (K and V), 16-bit K
+    # and V^T of every FP16 block, per (sequence, KV head); q and o are negligible
+    per = {OP.INT8: 64 * w.d * 2 + 8, OP.INT4: 64 * w.d + 8, OP.FP16: 64 * w.d * 2 * 2, OP.SKIP: 0}
+    nbytes = 0
+    counts = {OP.INT8: 0, OP.INT4: 0, OP.FP16: 0, OP.SKIP: 0}
+    for L in w.seqlens:
+        for g in range(w.hkv):
+            tags = OP.decode_block_tags(L, int(dpol["b8"][g]), int(dpol["b4"][g]), dpol["sink"], dpol["tail"])
+            for t in tags.tolist():
+                nbytes += per[t]
+                counts[t] += 1
+    for i in range(5):
+        caches[i % rotate].decode()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        caches[i % rotate].decode()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = sum(ms) / len(ms)
+    return {"workload": describe(w) + ", cache tags (b8, b4) = (128, 320) blocks, last 128 tokens FP16",
+            "bytes_per_step": nbytes, "ms_mean": mean, "ms_median": ms[len(ms) // 2],
+            "GBps": nbytes / (mean * 1e-3) / 1e9, "hbm_frac": nbytes / (mean * 1e-3) / PEAK_HBM,
+            "blocks": {"int8": counts[OP.INT8], "int4": counts[OP.INT4], "fp16": counts[OP.FP16],
+                       "skip": counts[OP.SKIP]}, "rotated_caches": rotate}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa8k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-bench", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this hot path runs on one GPU; --gpus N > 1 is not supported (see DESIGN.md for "
+              "how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import tile_routed_mixed_amd as T
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    T.lib()
+    w = W.get(args.workload)
+    log(f"[bench] workload {describe(w)}")
+    q, k, v = W.make_qkv(w)
+    pol = W.make_policy(w)
+    pp = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, pol)
+    pp.upload(q[0], k[0], v[0])
+    pp.quantize()
+    census = pp.traversal(census=True)
+    b8, b4 = decode_policy_for(w.seqlens[0])
+    dpol = dict(b8=[b8] * w.hkv, b4=[b4] * w.hkv, sink=1, tail=128)
+    dq = W.make_decode_query(w)
+    dp = T.DecodePipeline.from_prefill(pp, dpol, dq[0])
+    o_dtype = T.TM_BF16 if w.dtype == "bf16" else T.TM_F16
+    log(f"[bench] census {census}")
+
+    E = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pp.quantize()
+        if ev is not None:
+            ev[1].record()
+        pp.traversal(False)
+        if ev is not None:
+            ev[2].record()
+        pp.prefill(o_dtype)
+        if ev is not None:
+            ev[3].record()
+        dp.decode()
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[E() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    part = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
+    t_quant, t_trav, t_pref, t_dec = part(0, 1), part(1, 2), part(2, 3), part(3, 4)
+    log(f"[bench] ms/step {ms_step:.4f}: quantize {t_quant:.4f} traversal {t_trav:.4f} "
+        f"prefill {t_pref:.4f} decode {t_dec:.4f}")
+
+    flops = dense_causal_flops(w)
+    value = flops / (ms_step * 1e-3) / 1e12
+    ops, t_peak = prefill_roofline(w, census, t_pref * 1e-3)
+    achieved = ops / (t_pref * 1e-3) / 1e12
+    peak = ops / t_peak / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+            "traffic": pmc_traffic(), "kernel": "prefill_kernel",
+            "peak_note": "precision-weighted: INT8/INT4 QK at 5.0 POP/s, FP16 QK and every PV at 2.5 PFLOP/s, "
+                         "over the executed tiles of this workload"}
+    out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "i8+f16" if census["fp16"] == 0 else "i8+f16(+f16 QK)",
+           "data": "synthetic (seeded N(0,1), shapes of the pages' Llama-3-8B-class attention layers)",
+           "config": {"workload": describe(w), "global_batch": len(w.seqlens), "seq_len": max(w.seqlens),
+                      "parallelism": "none (1 GPU)", "decode_in_step": f"1 query/seq over the prompt cache, "
+                                                                       f"(b8, b4) = ({b8}, {b4}) blocks, sink, "
+                                                                       f"tail 128"},
+           "roofline": roof,
+           "mfma_util": achieved / peak,
+           "prefill_kernel_ms": t_pref, "prefill_only_tflops": flops / (t_pref * 1e-3) / 1e12,
+           "kernels_ms": {"quantize_qkv": t_quant, "traversal": t_trav, "prefill": t_pref, "decode": t_dec},
+           "census": census}
+    if not args.no_decode_bench:
+        del pp, dp
+        torch.cuda.empty_cache()
+        d = decode_bench(max(20, args.steps))
+        out["decode"] = d
+        out["decode_kv_gbs"] = d["GBps"]
+        log(f"[bench] decode {d['ms_mean']:.4f} ms, {d['GBps']:.1f} GB/s ({d['hbm_frac'] * 100:.1f} % of HBM)")
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, pol, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -245,11 +245,13 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav,
 
 /* Decode: one new query per sequence over the compressed cache.
  *  cache: shape of the cached sequences (nseq = batch, len = cache length L
- *    including the new token); dtype must be TM_F16; hq/hkv <= 16.
- *  q [nseq][hq][d] fp16 (device).
+ *    including the new token); dtype TM_F16 or TM_BF16 (type of q and k16;
+ *    bf16 values are widened to fp16 for the MFMA, exact for magnitudes in
+ *    [2^-14, 65504]); hq/hkv <= 16.
+ *  q [nseq][hq][d] 16-bit (device).
  *  kq (TM_ROWS, hkv heads), vq (TM_COLS, hkv heads, t16 set): the cache, as
  *    produced by tm_quantize_pack over the cached tokens.
- *  k16 [T][hkv][d] fp16 (device): keys read for FP16 blocks.
+ *  k16 [T][hkv][d] 16-bit (device): keys read for FP16 blocks.
  *  policy: per-KV-head tags (tm_dpolicy).
  *  o [nseq][hq][d] of o_dtype (TM_F32 or TM_F16, device).
  *  ws (device): workspace; ws == NULL writes the required size to *ws_bytes
@@ -258,7 +260,7 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav,
  * score = scale * (q . k), value = v ([HyQuant] "How HyQuant works":
  * dequantization fused with attention).
  * Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY, TM_E_SPACE, TM_E_UNSUPPORTED
- * (bf16 cache, hq/hkv > 16), TM_E_HIP. */
+ * (hq/hkv > 16, more than 64 KV heads), TM_E_HIP. */
 tm_status tm_decode(const tm_shape* cache, const void* q,
                     const tm_qtensor* kq, const tm_qtensor* vq, const void* k16,
                     const tm_dpolicy* policy, void* o, int32_t o_dtype,

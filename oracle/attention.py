@@ -60,12 +60,14 @@ def _rows_scores(r0, r1, h, kv, tok0, grid_h, bq, bk, q64, k64, qq, kq, blk0, ta
 
 
 def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
-            rows=None, return_p=False):
+            rows=None, return_p=False, qtiles=None):
     """Oracle prefill output.
 
     q64 [T][hq][d], k64/v64 [T][hkv][d]: float64 copies of the 16-bit inputs.
     qq, kq: oracle quantizer outputs (rows layout) for Q and K.
     rows: None for every row, else an iterable of (seq, head, row) triples.
+    qtiles: alternatively, an iterable of (seq, head, query tile) triples whose
+    rows are computed (used to time a bounded sample of a workload).
     Returns (O, lse) with O [T][hq][d] and lse [hq][T] (NaN where not computed),
     plus the list of probability rows when return_p is set.
     """
@@ -77,7 +79,9 @@ def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
     gs = P.grids(seqlens, hq, bq, bk, pol)
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     plist = []
-    if rows is None:
+    if qtiles is not None:
+        work = [(s, h, [i]) for s, h, i in qtiles]
+    elif rows is None:
         work = [(s, h, None) for s in range(len(seqlens)) for h in range(hq)]
     else:
         by = {}
@@ -91,8 +95,12 @@ def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
         blk0 = int(qq["blk_start"][s])
         assert int(kq["blk_start"][s]) == blk0
         g = gs[s][h]
-        chunks = ([(i * bq, min((i + 1) * bq, S_len)) for i in range(P.n_tiles(S_len, bq))]
-                  if rlist is None else [(r, r + 1) for r in rlist])
+        if rlist is None:
+            chunks = [(i * bq, min((i + 1) * bq, S_len)) for i in range(P.n_tiles(S_len, bq))]
+        elif qtiles is not None:
+            chunks = [(i * bq, min((i + 1) * bq, S_len)) for i in rlist]
+        else:
+            chunks = [(r, r + 1) for r in rlist]
         for r0, r1 in chunks:
             Sc = _rows_scores(r0, r1, h, kv, tok0, g, bq, bk, q64, k64, qq, kq, blk0, tau)
             m = np.max(Sc, axis=1)

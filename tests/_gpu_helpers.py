@@ -69,12 +69,18 @@ def int_tiles(w, pol, limit=None, seed=0):
     """Executed integer tiles (seq, head, qtile, ktile, prec) of a policy, a
     deterministic sample of at most `limit` (always with the first/last)."""
     gs = OP.grids(w.seqlens, w.hq, w.bq, w.bk, pol)
-    ex = sorted(t for t in OP.executed_tiles(gs) if t[4] in (OP.INT8, OP.INT4))
-    if limit is None or len(ex) <= limit:
-        return ex
-    rng = np.random.default_rng(seed)
-    pick = set([0, len(ex) - 1]) | set(rng.choice(len(ex), size=limit - 2, replace=False).tolist())
-    return [ex[i] for i in sorted(pick)]
+    parts = []
+    for s, g in enumerate(gs):
+        h, i, j = np.nonzero((g == OP.INT8) | (g == OP.INT4))
+        parts.append(np.stack([np.full_like(h, s), h, i, j, g[h, i, j].astype(h.dtype)], axis=1))
+    ex = np.concatenate(parts, axis=0) if parts else np.zeros((0, 5), np.int64)
+    n = len(ex)
+    if limit is None or n <= limit:
+        pick = range(n)
+    else:
+        rng = np.random.default_rng(seed)
+        pick = sorted(set([0, n - 1]) | set(rng.choice(n, size=limit - 2, replace=False).tolist()))
+    return [tuple(int(x) for x in ex[p]) for p in pick]
 
 
 def check_int_scores(w, tiles, dbg, qq, kq):

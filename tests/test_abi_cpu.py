@@ -210,8 +210,12 @@ def test_decode_validation_and_workspace(B):
     empty = B.DPolicy(dict(b8=[0] * 8, b4=[0] * 8, sink=0, tail=0))
     assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(empty.c), None, 2, None,
                        ctypes.byref(n), None) == B.TM_E_POLICY
-    sb = _shape(B, [64], hq=32, hkv=8, d=128, dtype=1)
+    sb = _shape(B, [64], hq=32, hkv=8, d=128, dtype=1)     # bf16 caches are supported
     assert L.tm_decode(ctypes.byref(sb.c), None, None, None, None, ctypes.byref(dp.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_OK
+    sk = _shape(B, [64], hq=65 * 2, hkv=65, d=128)
+    dp65 = B.DPolicy(dict(b8=[1] * 65, b4=[2] * 65, sink=1, tail=128))
+    assert L.tm_decode(ctypes.byref(sk.c), None, None, None, None, ctypes.byref(dp65.c), None, 2, None,
                        ctypes.byref(n), None) == B.TM_E_UNSUPPORTED
     sg = _shape(B, [64], hq=34, hkv=2, d=128)
     dp2 = B.DPolicy(dict(b8=[1] * 2, b4=[2] * 2, sink=1, tail=128))

@@ -1,0 +1,130 @@
+"""Full-size parity: the four workloads at their real sizes, in the launch
+configuration bench.py times, checked on sampled outputs the oracle computes
+one row (or one decode query) at a time.
+
+* traversal and census of the full policy against brute-force enumeration;
+* integer QK scores of sampled tiles bit-exact (debug capture);
+* sampled output rows (first and last rows of sequences, rows on either side
+  of query-tile and block boundaries, seeded random rows) within the gate, for
+  the fp32 output and the 16-bit output the bench writes (gate + half an ulp).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+from oracle import policy as OP
+from oracle import quant as OQ
+
+from _gpu_helpers import TOL_MAX, check_int_scores, compare, int_tiles, run_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(w, n_random=24, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    heads = sorted(set([0, w.hq - 1, w.hq // 2] + rng.integers(0, w.hq, size=3).tolist()))
+    for s, S in enumerate(w.seqlens):
+        fixed = [0, 1, 63, 64, min(127, S - 1), min(128, S - 1), S // 2, S - 2, S - 1]
+        for h in heads[:3]:
+            for r in fixed:
+                if 0 <= r < S:
+                    rows.add((s, h, r))
+    for _ in range(n_random):
+        s = int(rng.integers(0, len(w.seqlens)))
+        rows.add((s, int(rng.choice(heads)), int(rng.integers(0, w.seqlens[s]))))
+    return sorted(rows)
+
+
+def _sparse_q_codes(q32, seqlens, rows_blocks):
+    """Oracle codes of Q for the listed (sequence, block) pairs only; the
+    quantizer works per 64-token block, so quantizing a block's 64 tokens on
+    their own gives the same codes as quantizing the whole tensor."""
+    starts, nblk = OQ.block_starts(seqlens)
+    T, H, d = q32.shape
+    out = dict(c8=np.zeros((H, nblk, 64, d), np.int8), c4=np.zeros((H, nblk, 64, d), np.int8),
+               s8=np.zeros((H, nblk), np.float32), s4=np.zeros((H, nblk), np.float32), blk_start=starts,
+               nblk=nblk)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    for s, b in sorted(rows_blocks):
+        t0 = int(cu[s]) + 64 * b
+        t1 = min(t0 + 64, int(cu[s + 1]))
+        blk = OQ.quantize(q32[t0:t1], [t1 - t0])
+        g = int(starts[s]) + b
+        for key in ("c8", "c4", "s8", "s4"):
+            out[key][:, g] = blk[key][:, 0]
+    return out
+
+
+def _full_prefill(name, n_random=24, n_tiles=8):
+    import tile_routed_mixed_amd as T
+    w = W.get(name)
+    pol = W.make_policy(w)
+    say(f"[gpu] full-size {name}: generating inputs")
+    q, k, v = W.make_qkv(w)
+    tiles = int_tiles(w, pol, limit=n_tiles, seed=1)
+    p, census, o32, lse, dbg = run_prefill(w, pol, q, k, v, dbg_tiles=[t[:4] for t in tiles])
+    c = OP.census(OP.grids(w.seqlens, w.hq, w.bq, w.bk, pol))
+    assert {kk: census[kk] for kk in c} == c
+    o16_dtype = T.TM_BF16 if w.dtype == "bf16" else T.TM_F16
+    o16, _ = p.prefill(o16_dtype)
+    import torch
+    torch.cuda.synchronize()
+    o16 = o16.float().cpu().numpy()
+    rows = _sample_rows(w, n_random)
+    need = set((s, r // 64) for s, h, r in rows)
+    for s, h, i, j, prec in tiles:
+        need |= set((s, (i * w.bq + x) // 64) for x in range(0, w.bq, 64) if i * w.bq + x < w.seqlens[s])
+    qq = _sparse_q_codes(q[1], w.seqlens, need)
+    kq = OQ.quantize(k[1], w.seqlens)
+    check_int_scores(w, tiles, dbg, qq, kq)
+    say(f"[gpu] full-size {name}: oracle on {len(rows)} sampled rows")
+    O, L = OA.prefill(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.bk, pol, q[1].astype(np.float64),
+                      k[1].astype(np.float64), v[1].astype(np.float64), qq, kq, rows=rows)
+    cu = w.cu_seqlens
+    idx = [(int(cu[s]) + r, h) for s, h, r in rows]
+    ti = np.array([a for a, _ in idx])
+    hi = np.array([b for _, b in idx])
+    compare(o32[ti, hi], O[ti, hi], lse[hi, ti], L[hi, ti], what=f"{name} fp32")
+    ulp = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -11
+    err16 = np.abs(o16[ti, hi] - O[ti, hi])
+    assert np.all(err16 <= TOL_MAX + ulp * np.abs(O[ti, hi]) + 1e-7), float(err16.max())
+    return p
+
+
+def test_gqa8k_full():
+    _full_prefill("gqa8k")
+
+
+def test_varlen32k_full():
+    _full_prefill("varlen32k")
+
+
+def test_long128k_full():
+    _full_prefill("long128k", n_random=40, n_tiles=6)
+
+
+def test_decode16x32k_full():
+    import torch
+    import tile_routed_mixed_amd as T
+    w = W.get("decode16x32k")
+    dpol = W.make_decode_policy(w)
+    say("[gpu] full-size decode16x32k: generating inputs")
+    _, k, v = W.make_qkv(w)
+    dq = W.make_decode_query(w)
+    p = T.DecodePipeline(w.seqlens, w.hq, w.hkv, w.d, dpol, dtype=w.dtype)
+    p.upload(dq[0], k[0], v[0])
+    p.build_cache()
+    o = p.decode()
+    torch.cuda.synchronize()
+    o = o.cpu().numpy()
+    cu = w.cu_seqlens
+    for b in (0, 7, 15):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        L = w.seqlens[b]
+        kq = OQ.quantize(k[1][sl], [L])
+        vq = OQ.quantize(v[1][sl], [L], layout="cols")
+        O = OA.decode([L], w.hq, w.hkv, w.d, dq[1][b:b + 1].astype(np.float64), kq, vq,
+                      k[1][sl].astype(np.float64), v[1][sl].astype(np.float64), dpol)
+        compare(o[b], O[0], what=f"decode16x32k seq {b}")

@@ -6,6 +6,8 @@ mean-abs 5e-4 of the float64 oracle computed from the oracle's own codes.
 Small cases span several tiles with ragged tails; the full-size workloads are
 checked on sampled rows (the oracle computes rows one by one).
 """
+import zlib
+
 import numpy as np
 import pytest
 
@@ -103,7 +105,7 @@ def test_traversal_bruteforce(case):
 # ---------------------------------------------------------------------------- prefill (small)
 
 def _case(case):
-    rng = np.random.default_rng(hash(case) % 2 ** 32)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
     if case == "toy":
         w = W.get("toy512")
         return w, W.make_policy(w)
@@ -217,14 +219,14 @@ def test_deterministic():
 
 # ---------------------------------------------------------------------------- decode (small)
 
-def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, seed=3):
+def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, dtype="f16"):
     import torch
     import tile_routed_mixed_amd as T
-    w = W.small("decode16x32k", seqlens, hq=hq, hkv=hkv, d=d)
+    w = W.small("decode16x32k", seqlens, hq=hq, hkv=hkv, d=d, dtype=dtype)
     q, k, v = W.make_qkv(w)
     dq = W.make_decode_query(w)
-    say(f"[gpu] decode {seqlens} hq={hq} hkv={hkv} d={d} {dpol}")
-    p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol)
+    say(f"[gpu] decode {seqlens} hq={hq} hkv={hkv} d={d} {dtype} {dpol}")
+    p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol, dtype=dtype)
     p.upload(dq[0], k[0], v[0])
     p.build_cache()
     o = p.decode()
@@ -236,12 +238,13 @@ def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, seed=3):
     return o.cpu().numpy(), O
 
 
-@pytest.mark.parametrize("seqlens,dpol,d", [
-    ([1, 100, 1000, 2000], dict(b8=[2, 3], b4=[5, 9], sink=1, tail=128), 128),
-    ([64, 65, 4097], dict(b8=[1, 4], b4=[1, 40], sink=0, tail=128), 64),
-    ([3000, 777], dict(b8=[10 ** 6] * 2, b4=[10 ** 6] * 2, sink=0, tail=0), 128),
-    ([2500], dict(b8=[0, 0], b4=[30, 30], sink=1, tail=1), 128),
+@pytest.mark.parametrize("seqlens,dpol,d,dtype", [
+    ([1, 100, 1000, 2000], dict(b8=[2, 3], b4=[5, 9], sink=1, tail=128), 128, "f16"),
+    ([64, 65, 4097], dict(b8=[1, 4], b4=[1, 40], sink=0, tail=128), 64, "f16"),
+    ([3000, 777], dict(b8=[10 ** 6] * 2, b4=[10 ** 6] * 2, sink=0, tail=0), 128, "f16"),
+    ([2500], dict(b8=[0, 0], b4=[30, 30], sink=1, tail=1), 128, "f16"),
+    ([1500, 3000], dict(b8=[4, 8], b4=[20, 30], sink=1, tail=128), 128, "bf16"),
 ])
-def test_decode_small(seqlens, dpol, d):
-    o, O = _decode_case(seqlens, dpol, d=d)
-    compare(o, O, what=f"decode {seqlens}")
+def test_decode_small(seqlens, dpol, d, dtype):
+    o, O = _decode_case(seqlens, dpol, d=d, dtype=dtype)
+    compare(o, O, what=f"decode {seqlens} {dtype}")

@@ -64,7 +64,24 @@ __device__ __forceinline__ f16x8 widen_i4x8(uint32_t c) {
   return v - off;
 }
 
-template <int D>
+// Eight 16-bit values (fp16, or bf16 widened to fp16: exact for magnitudes in
+// [2^-14, 65504], the range of normal fp16 numbers) as an fp16 MFMA operand.
+template <bool BF16>
+__device__ __forceinline__ f16x8 to_f16x8(u32x4 raw) {
+  f16x8 v;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = static_cast<_Float16>(__uint_as_float(raw[e] << 16));
+      v[2 * e + 1] = static_cast<_Float16>(__uint_as_float(raw[e] & 0xFFFF0000u));
+    }
+  } else {
+    __builtin_memcpy(&v, &raw, 16);
+  }
+  return v;
+}
+
+template <int D, bool BF16>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;      // f16 MFMA k-chunks over d
   constexpr int ND = D / 16;      // output channel blocks
@@ -94,7 +111,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(qs + 8 * c) : u32x4{0, 0, 0, 0};
-      __builtin_memcpy(&qop[c], &raw, 16);
+      qop[c] = to_f16x8<BF16>(raw);
     }
   }
 
@@ -143,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           u32x4 raw = tk < L ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0, 0, 0, 0};
-          __builtin_memcpy(&kop[kb][c], &raw, 16);
+          kop[kb][c] = to_f16x8<BF16>(raw);
         }
       }
     }
@@ -278,10 +295,15 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t st) {
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st) {
   dim3 grid(a.nsplit, a.hkv, a.nseq);
-  if (d == 128) hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(256), 0, st, a);
+  if (d == 128) {
+    if (bf16) hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, dim3(256), 0, st, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.nseq * a.hq), dim3(128), 0, st, a);

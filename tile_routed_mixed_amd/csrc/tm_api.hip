@@ -296,7 +296,6 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   ShapeInfo si;
   tm_status st = check_shape(cache, false, &si);
   if (st != TM_OK) return st;
-  if (cache->dtype != TM_F16) return TM_E_UNSUPPORTED;
   if (cache->hq / cache->hkv > 16 || cache->hkv > kMaxKvArg) return TM_E_UNSUPPORTED;
   if (policy == nullptr || policy->b8 == nullptr || policy->b4 == nullptr || ws_bytes == nullptr) return TM_E_ARG;
   if (policy->sink != 0 && policy->sink != 1) return TM_E_POLICY;
@@ -347,7 +346,7 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     a.b8[g] = policy->b8[g];
     a.b4[g] = policy->b4[g];
   }
-  const hipError_t e = launch_decode(a, cache->d, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_decode(a, cache->d, cache->dtype == TM_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TM_OK : TM_E_HIP;
 }
 

@@ -59,7 +59,7 @@ struct PrefillArgs {
 };
 
 struct DecodeArgs {
-  const uint16_t* q;       // [B][hq][D] fp16
+  const uint16_t* q;       // [B][hq][D] 16-bit
   const int32_t* cu;
   const int8_t* k8;        // rows  [hkv][nblk][64][D]
   const uint8_t* k4;       // rows  [hkv][nblk][64][D/2]
@@ -70,7 +70,7 @@ struct DecodeArgs {
   const float* vs8;
   const float* vs4;
   const uint16_t* vt16;    // cols  [hkv][nblk][D][64] fp16
-  const uint16_t* k16;     // [T][hkv][D] fp16
+  const uint16_t* k16;     // [T][hkv][D] 16-bit
   float* ws;               // [B][hq][nsplit][D + 2]
   void* o;
   int o_dtype;
@@ -84,6 +84,6 @@ struct DecodeArgs {
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, bool bf16, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st);
 
 }  // namespace tmx

@@ -69,8 +69,9 @@ class DecodePipeline:
     """One decode step: the cache is K (rows) and V (cols + fp16 copy) quantized
     over the cached tokens, plus the 16-bit keys for FP16 blocks."""
 
-    def __init__(self, seqlens, hq, hkv, d, dpolicy: dict, device="cuda:0", softmax_scale=0.0):
-        self.shape = B.Shape(seqlens, hq, hkv, d, 128, 64, B.TM_F16, softmax_scale, device=device)
+    def __init__(self, seqlens, hq, hkv, d, dpolicy: dict, device="cuda:0", softmax_scale=0.0, dtype="f16"):
+        dt = B.TM_BF16 if dtype == "bf16" else B.TM_F16
+        self.shape = B.Shape(seqlens, hq, hkv, d, 128, 64, dt, softmax_scale, device=device)
         self.device = device
         self.dpol = B.DPolicy(dpolicy)
         self.kq = B.QTensor(self.shape, hkv, B.TM_ROWS, False, device)
@@ -92,6 +93,24 @@ class DecodePipeline:
     def decode(self, stream=None):
         return B.tm_decode(self.shape, self.q, self.kq, self.vq, self.k, self.dpol, o=self.o, ws=self.ws,
                            stream=stream)
+
+    @classmethod
+    def from_prefill(cls, pp: "PrefillPipeline", dpolicy: dict, q_bits):
+        """Decode over the cache a PrefillPipeline just quantized (its K rows and
+        V cols + fp16 copy are the compressed cache); q_bits [nseq][hq][d]."""
+        self = cls.__new__(cls)
+        self.shape = pp.shape
+        self.device = pp.device
+        self.dpol = B.DPolicy(dpolicy)
+        self.kq, self.vq = pp.kq, pp.vq
+        import torch
+        self.ws = torch.empty(max(4, B.decode_ws_bytes(self.shape, self.dpol)), dtype=torch.uint8,
+                              device=self.device)
+        self.o = torch.empty((len(self.shape.seqlens), self.shape.hq, self.shape.d), dtype=torch.float32,
+                             device=self.device)
+        self.q = _dev_bits(q_bits, self.device)
+        self.k, self.v = pp.k, pp.v
+        return self
 
 
 def read_traversal(trav_host: np.ndarray):
