@@ -218,7 +218,9 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
                              void* stream);
 
 /* Fused tile-routed causal prefill.
- *  trav: built by tm_build_traversal for this shape.
+ *  trav: built by tm_build_traversal for this shape; policy_kind: the kind
+ *    of the policy it was built from (selects the kernel specialization; a
+ *    traversal of another kind leaves o untouched).
  *  q [T][hq][d], k [T][hkv][d]: 16-bit inputs (device; read on FP16 tiles).
  *  qq (TM_ROWS, hq heads), kq (TM_ROWS, hkv heads): quantized Q and K.
  *  vq (TM_COLS, hkv heads) with t16 set: V in fp16, transposed per block (the
@@ -236,7 +238,7 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
  * to fp16 for the PV product ([TriAttention] abstract: one normalized output
  * from both QK precisions; [TileMix] abstract: shared online-softmax state).
  * Errors: TM_E_ARG, TM_E_SHAPE (tensors not matching the shape), TM_E_HIP. */
-tm_status tm_prefill(const tm_shape* shape, const void* trav,
+tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kind,
                      const void* q, const void* k,
                      const tm_qtensor* qq, const tm_qtensor* kq, const tm_qtensor* vq,
                      void* o, int32_t o_dtype, float* lse,

@@ -174,13 +174,15 @@ def test_prefill_validation(B):
     L = B.lib()
     nb = s.nblk()
     qq, kq, vq = _qt(B, 4, 0, nb, False), _qt(B, 2, 0, nb, False), _qt(B, 2, 1, nb, True)
-    args = lambda **kw: dict(dict(trav=FAKE, q=FAKE, k=FAKE, qq=qq, kq=kq, vq=vq, o=FAKE, odt=0, ndbg=0), **kw)
+    args = lambda **kw: dict(dict(trav=FAKE, kind=0, q=FAKE, k=FAKE, qq=qq, kq=kq, vq=vq, o=FAKE, odt=0, ndbg=0),
+                             **kw)
 
     def call(a):
-        return L.tm_prefill(ctypes.byref(s.c), a["trav"], a["q"], a["k"], ctypes.byref(a["qq"]),
+        return L.tm_prefill(ctypes.byref(s.c), a["trav"], a["kind"], a["q"], a["k"], ctypes.byref(a["qq"]),
                             ctypes.byref(a["kq"]), ctypes.byref(a["vq"]), a["o"], a["odt"], None, None, None,
                             a["ndbg"], None)
     assert call(args(q=None)) == B.TM_E_ARG
+    assert call(args(kind=2)) == B.TM_E_ARG
     assert call(args(trav=None)) == B.TM_E_ARG
     assert call(args(odt=9)) == B.TM_E_ARG
     assert call(args(ndbg=2)) == B.TM_E_ARG

@@ -86,7 +86,7 @@ def lib():
         L.tm_build_traversal.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp,
                                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(tm_census), vp]
         L.tm_prefill.restype = i32
-        L.tm_prefill.argtypes = [ctypes.POINTER(tm_shape), vp, vp, vp, ctypes.POINTER(tm_qtensor),
+        L.tm_prefill.argtypes = [ctypes.POINTER(tm_shape), vp, i32, vp, vp, ctypes.POINTER(tm_qtensor),
                                  ctypes.POINTER(tm_qtensor), ctypes.POINTER(tm_qtensor), vp, i32, vp, vp, vp,
                                  i32, vp]
         L.tm_decode.restype = i32
@@ -214,8 +214,8 @@ def tm_build_traversal(shape: Shape, policy: Policy, trav=None, census: bool = T
     return trav, out
 
 
-def tm_prefill(shape: Shape, trav, q, k, qq: QTensor, kq: QTensor, vq: QTensor, o=None, o_dtype=TM_F32,
-               lse=None, dbg_tiles=None, stream=None):
+def tm_prefill(shape: Shape, trav, policy_kind: int, q, k, qq: QTensor, kq: QTensor, vq: QTensor, o=None,
+               o_dtype=TM_F32, lse=None, dbg_tiles=None, stream=None):
     """Returns (o, lse, dbg_qk).  dbg_tiles: int32 device tensor [n][4] or None."""
     import torch
     dev = q.device
@@ -227,7 +227,7 @@ def tm_prefill(shape: Shape, trav, q, k, qq: QTensor, kq: QTensor, vq: QTensor, 
     if dbg_tiles is not None:
         n_dbg = int(dbg_tiles.shape[0])
         dbg = torch.zeros((n_dbg, shape.bq, 64), dtype=torch.int32, device=dev)
-    _check(lib().tm_prefill(ctypes.byref(shape.c), _ptr(trav), _ptr(q), _ptr(k), ctypes.byref(qq.c),
+    _check(lib().tm_prefill(ctypes.byref(shape.c), _ptr(trav), int(policy_kind), _ptr(q), _ptr(k), ctypes.byref(qq.c),
                             ctypes.byref(kq.c), ctypes.byref(vq.c), _ptr(o), o_dtype, _ptr(lse), _ptr(dbg),
                             _ptr(dbg_tiles), n_dbg, _stream(stream)), "tm_prefill")
     return o, lse, dbg

@@ -248,13 +248,14 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   return TM_OK;
 }
 
-tm_status tm_prefill(const tm_shape* shape, const void* trav, const void* q, const void* k,
+tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kind, const void* q, const void* k,
                      const tm_qtensor* qq, const tm_qtensor* kq, const tm_qtensor* vq, void* o, int32_t o_dtype,
                      float* lse, int32_t* dbg_qk, const int32_t* dbg_tiles, int32_t n_dbg, void* stream) {
   ShapeInfo si;
   tm_status st = check_shape(shape, true, &si);
   if (st != TM_OK) return st;
   if (trav == nullptr || q == nullptr || k == nullptr || o == nullptr) return TM_E_ARG;
+  if (policy_kind != TM_POLICY_BOUNDARIES && policy_kind != TM_POLICY_BITMASK) return TM_E_ARG;
   if (o_dtype != TM_F32 && o_dtype != TM_F16 && o_dtype != TM_BF16) return TM_E_ARG;
   if (n_dbg < 0 || (n_dbg > 0 && (dbg_qk == nullptr || dbg_tiles == nullptr))) return TM_E_ARG;
   if ((st = check_qtensor(qq, shape->hq, TM_ROWS, si.nblk, false)) != TM_OK) return st;
@@ -285,7 +286,7 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, const void* q, con
   a.nblk = si.nblk;
   a.n_items = static_cast<uint32_t>(si.n_items);
   a.tau_log2e = tau_log2e(shape);
-  const hipError_t e = launch_prefill(a, shape->d, shape->bq, shape->dtype == TM_BF16,
+  const hipError_t e = launch_prefill(a, shape->d, shape->bq, policy_kind, shape->dtype == TM_BF16,
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TM_OK : TM_E_HIP;
 }

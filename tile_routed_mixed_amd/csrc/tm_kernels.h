@@ -83,7 +83,7 @@ struct DecodeArgs {
 
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
-hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, bool bf16, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st);
 
 }  // namespace tmx

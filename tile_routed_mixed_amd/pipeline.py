@@ -54,7 +54,7 @@ class PrefillPipeline:
             tdt = {B.TM_F32: torch.float32, B.TM_F16: torch.float16, B.TM_BF16: torch.bfloat16}[o_dtype]
             self.o = torch.empty((self.shape.T, self.shape.hq, self.shape.d), dtype=tdt, device=self.device)
             self.o_dtype = o_dtype
-        _, _, dbg = B.tm_prefill(self.shape, self.trav, self.q, self.k, self.qq, self.kq, self.vq, o=self.o,
+        _, _, dbg = B.tm_prefill(self.shape, self.trav, self.policy.kind, self.q, self.k, self.qq, self.kq, self.vq, o=self.o,
                                  o_dtype=o_dtype, lse=self.lse if with_lse else None, dbg_tiles=dbg_tiles,
                                  stream=stream)
         return self.o, dbg
