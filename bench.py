@@ -174,7 +174,20 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-bench", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain elementwise copy of BYTES bytes (read BYTES, write BYTES) 5 times, "
+                         "to scale HBM byte counters; prints nothing else")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this hot path runs on one GPU; --gpus N > 1 is not supported (see DESIGN.md for "

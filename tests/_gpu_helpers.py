@@ -15,7 +15,10 @@ from oracle import quant as OQ
 
 TOL_MAX = 4e-3     # max-abs gate on fp32 outputs against the float64 oracle
 TOL_MEAN = 5e-4    # mean-abs gate
-TOL_LSE = 1e-4     # log-sum-exp: fp32 scores, exp2 and sums over <= 2^17 keys
+# log-sum-exp: the kernel's row sum adds the same fp16-rounded probabilities
+# the PV product uses (round to nearest: relative error <= 2^-11 per term), so
+# ln(sum) may be off by up to ~2^-11 = 4.9e-4, plus fp32 score/exp2 rounding.
+TOL_LSE = 6e-4
 
 
 def say(*a):

@@ -16,7 +16,7 @@ from oracle import attention as OA
 from oracle import policy as OP
 from oracle import quant as OQ
 
-from _gpu_helpers import (TOL_MAX, check_int_scores, compare, int_tiles, oracle_prefill, run_prefill, say)
+from _gpu_helpers import (TOL_LSE, TOL_MAX, check_int_scores, compare, int_tiles, oracle_prefill, run_prefill, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -178,7 +178,7 @@ def test_first_row_is_v0_and_rows_normalized():
     O, L, qq, kq = oracle_prefill(w, pol, q, k, v, rows=[(0, 3, 999), (2, 5, 129), (3, 0, 63)])
     for (s, h, r) in [(0, 3, 999), (2, 5, 129), (3, 0, 63)]:
         t = cu[s] + r
-        assert abs(lse[h, t] - L[h, t]) <= 1e-4
+        assert abs(lse[h, t] - L[h, t]) <= TOL_LSE
 
 
 def test_skipped_tiles_do_not_matter_on_gpu():

@@ -16,24 +16,28 @@
 //    INT8 and INT4 tiles on v_mfma_i32_16x16x64_i8 (INT4 nibbles are widened
 //    in registers to int8 holding 16x the code, so the product is exact and
 //    256x the code product), FP16 tiles on v_mfma_f32_16x16x32_{f16,bf16};
-//    every lane then holds keys of one query row, so the online-softmax max,
-//    sum and rescale are lane-local up to a 4-lane reduction, and the fp16
-//    probabilities are already in the B-operand layout of the PV product;
-//  * PV runs as O^T += V^T P^T on v_mfma_f32_16x16x32_f16.  V arrives
-//    transposed per 64-token block in fp16 (written once by the quantize
-//    pass), K rows are fed to the QK MFMA in an interleaved order (sigma) that
-//    makes each lane's 8 probabilities per 32-key chunk contiguous keys, so a
-//    single 16-byte LDS read fetches the matching V^T operand;
+//    every lane then holds keys of one query row, so the online-softmax
+//    bookkeeping is lane-local up to a 4-lane max (two lane-swap VALU ops),
+//    and the fp16 probabilities are already in the B-operand layout of PV;
+//  * PV runs as O^T += V^T P^T on v_mfma_f32_16x16x32_f16, plus one more MFMA
+//    per 32-key chunk with an all-ones A operand that accumulates the row sum
+//    of the same fp16 probabilities (no VALU adds; numerator and denominator
+//    see identical rounding).  V arrives transposed per 64-token block in fp16
+//    (written once by the quantize pass); K rows are fed to the QK MFMA in an
+//    interleaved order (sigma) that makes each lane's 8 probabilities per
+//    32-key chunk contiguous keys, so one 16-byte LDS read fetches the matching
+//    V^T operand;
 //  * K and V^T tiles are copied global -> LDS with the direct-to-LDS 16-byte
-//    load (no register staging) into two buffers: the next tile streams in
-//    while the current one is computed, with one barrier per tile.  16-byte
-//    chunks are XOR-swizzled by row so the MFMA operand reads are free of
-//    bank conflicts;
-//  * the running max is updated lazily: the probabilities are re-based (and O
-//    and the sum rescaled) only when a row's max grows by more than 8 in log2
-//    units, so p <= 256 stays exact enough in fp16 and rescales are rare;
-//  * row maxima of integer tiles are taken on the int32 accumulators (the
-//    per-row scale is positive), before any conversion;
+//    load (no register staging, per-lane source offsets computed once per
+//    item) into two buffers: the next tile streams in while the current one is
+//    computed, with one barrier per tile.  16-byte chunks are XOR-swizzled by
+//    row so the MFMA operand reads are free of bank conflicts;
+//  * scores enter exp2 through one FMA, x * scale - m (scale = sq sk tau log2e
+//    for integer tiles, tau log2e for FP16 tiles); the running max is updated
+//    lazily: probabilities are re-based (O and the sum rescaled) only when a
+//    row's max grows by more than 8 in log2 units, so p <= 256;
+//  * the item's run list sits one entry per lane and is read with readlane,
+//    so advancing the traversal needs no memory access;
 //  * workgroups are remapped so the 4 query heads of a GQA group run on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share K/V in L2.
 #include "tm_kernels.h"
@@ -72,6 +76,37 @@ __device__ __forceinline__ i32x4 widen_nibbles(uint32_t p0, uint32_t p1) {
   return r;
 }
 
+// max over the 4 lanes {l, l^16, l^32, l^48} (the lane groups of one row).
+__device__ __forceinline__ float max4(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (n <= 15).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
+// Scalar (constant address space) load of a uniform float: counted by
+// lgkmcnt, so vector-memory counts of the tile copies stay exact.
+__device__ __forceinline__ float sload(const float* p, size_t i) {
+  typedef const __attribute__((address_space(4))) float cfloat;
+  return ((cfloat*)(p))[i];
+}
+
 __device__ __forceinline__ uint32_t remap_block(uint32_t b, uint32_t n) {
   constexpr uint32_t kXcd = 8, kGroup = 4, kChunk = kXcd * kGroup;
   const uint32_t full = (n / kChunk) * kChunk;
@@ -80,31 +115,52 @@ __device__ __forceinline__ uint32_t remap_block(uint32_t b, uint32_t n) {
   return c * kChunk + (r % kXcd) * kGroup + r / kXcd;
 }
 
-// Copy a tile region of ROWS rows x NCH 16-byte chunks from global memory into
-// swizzled LDS with direct-to-LDS loads.  Instruction n (of ROWS*NCH/64) moves
-// LDS bytes [n*1024, n*1024+1024); lane L lands at n*1024 + 16*L, which is row
-// (n*1024 + 16L) / (16 NCH), swizzled slot (L mod NCH): it loads the logical
-// chunk slot ^ swz(row).  `src(row)` gives the row's global address.
-template <int ROWS, int NCH, bool VT, typename SrcFn>
-__device__ __forceinline__ void load_tile(uint8_t* lds, int w, int lane, SrcFn src) {
-  constexpr int NI = ROWS * NCH / 64;   // 1 KiB instructions for the region
-  auto one = [&](int n) {
-    const int off = n * 1024 + lane * 16;
-    const int row = off / (NCH * 16);
-    const int slot = (off / 16) % NCH;
-    const int c = slot ^ swz<NCH, VT>(row);
-    const uint8_t* g = src(row) + c * 16;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), reinterpret_cast<void*>(lds + n * 1024),
-                                     16, 0, 0);
-  };
-  if constexpr (NI >= 4) {
-    static_assert(NI % 4 == 0, "tile regions are whole multiples of 4 KiB");
+// Per-lane layout of a direct-to-LDS tile copy: a region of ROWS rows x NCH
+// 16-byte chunks is moved by ROWS*NCH/64 instructions of 1 KiB; instruction n
+// fills LDS bytes [n*1024, n*1024+1024) and lane L lands at n*1024 + 16L, which
+// is row (n*1024 + 16L) / (16 NCH), swizzled slot L mod NCH, i.e. it must load
+// logical chunk slot ^ swz(row).  Wave w issues instructions n = 4i + w.
+template <int ROWS, int NCH, bool VT>
+struct TileCopy {
+  static constexpr int NI = ROWS * NCH / 64;
+  static constexpr int PER = NI >= 4 ? NI / 4 : 1;
+  static_assert(NI < 4 || NI % 4 == 0, "tile regions are whole multiples of 4 KiB");
+  uint32_t row[PER], col[PER];   // source row and byte column of each of this lane's loads
+  // vector-memory instructions wave w issues for one copy of the region
+  __device__ __forceinline__ static int count(int w) { return NI >= 4 ? PER : (w < NI ? 1 : 0); }
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-    for (int i = 0; i < NI / 4; ++i) one(i * 4 + w);
-  } else {
-    if (w < NI) one(w);
+    for (int i = 0; i < PER; ++i) {
+      const int n = i * 4 + w;
+      const int off = n * 1024 + lane * 16;
+      const int r = off / (NCH * 16);
+      const int slot = (off / 16) % NCH;
+      row[i] = r;
+      col[i] = static_cast<uint32_t>((slot ^ swz<NCH, VT>(r)) * 16);
+    }
   }
-}
+  // src + row * pitch + col  ->  lds + n * 1024
+  __device__ __forceinline__ void issue(const uint8_t* src, uint32_t pitch, uint8_t* lds, int w) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (NI < 4 && w >= NI) break;
+      const uint8_t* g = src + (row[i] * pitch + col[i]);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
+                                       reinterpret_cast<void*>(lds + (i * 4 + w) * 1024), 16, 0, 0);
+    }
+  }
+  // same, with source rows clamped to `last` (rows past a sequence end)
+  __device__ __forceinline__ void issue_clamped(const uint8_t* src, uint32_t pitch, uint8_t* lds, int w,
+                                                uint32_t last) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (NI < 4 && w >= NI) break;
+      const uint8_t* g = src + (min(row[i], last) * pitch + col[i]);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
+                                       reinterpret_cast<void*>(lds + (i * 4 + w) * 1024), 16, 0, 0);
+    }
+  }
+};
 
 template <int D, int BQ, int KIND, bool BF16, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
@@ -120,7 +176,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr bool HAS16 = KIND == TM_POLICY_BITMASK;
   typedef typename std::conditional<BF16, bf16x8, f16x8>::type q16_t;
 
-  __shared__ __align__(1024) uint8_t lds[2 * BUF];
+  // pipeline depth: tiles resident or in flight (LDS: STAGES * BUF bytes).  Two
+  // measured faster than three on MI355X: the deeper ring adds per-tile
+  // scalar bookkeeping and the loads mostly hit L2.
+  constexpr int STAGES = 2;
+  __shared__ __align__(1024) uint8_t lds[STAGES * BUF];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -139,45 +199,104 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool qblk_ok = qblk < nbs;
   const size_t qblk_g = static_cast<size_t>(head) * a.nblk + se.blk_start + qblk;
   const size_t kv_blk0 = static_cast<size_t>(kv) * a.nblk + se.blk_start;
+  const uint32_t kpitch16 = static_cast<uint32_t>(a.hkv) * D * 2;   // bytes between key rows of k
 
-  // ---- tile iterator over the runs (uniform across the workgroup)
+  // ---- run list: one entry per lane, 64 runs per chunk
   const int nruns = static_cast<int>(it.nruns);
-  int ri = 0, roff = 0;
-  int r_first = 0, r_count = 0, r_prec = 0;
-  if (nruns > 0) {
-    const RunEntry r0 = runs[0];
-    r_first = static_cast<int>(r0.ktile);
-    r_count = static_cast<int>(r0.count_prec & 0xFFFFFFu);
-    r_prec = static_cast<int>(r0.count_prec >> 24);
-  }
+  int run_base = 0;
+  RunEntry run_lane = RunEntry{0u, 0u};
+  if (lane < nruns) run_lane = runs[lane];
+  auto run_at = [&](int r) {   // uniform r in [run_base, run_base + 64)
+    RunEntry e;
+    e.ktile = __builtin_amdgcn_readlane(run_lane.ktile, r - run_base);
+    e.count_prec = __builtin_amdgcn_readlane(run_lane.count_prec, r - run_base);
+    return e;
+  };
+
+  TileCopy<D, 8, true> cp_v;
+  TileCopy<kBlock, D / 16, false> cp_k8;
+  TileCopy<kBlock, D / 32, false> cp_k4;
+  TileCopy<kBlock, D / 8, false> cp_k16;
+  cp_v.init(w, lane);
+  cp_k8.init(w, lane);
+  if constexpr (HAS4) cp_k4.init(w, lane);
+  if constexpr (HAS16) cp_k16.init(w, lane);
 
   // Start loading tile j into `buf` and fetch its K scale (read after the next
   // barrier, when every load of the tile has been waited for).
   auto issue = [&](int j, int prec, uint8_t* buf, float& sk) {
     const size_t kb = kv_blk0 + j;
-    sk = prec == TM_INT8 ? a.ks8[kb] : ((HAS4 && prec == TM_INT4) ? a.ks4[kb] : 0.0f);
-    uint8_t* kl = buf;
-    uint8_t* vl = buf + KBYTES;
-    const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.vt16) + kb * VBYTES;
-    load_tile<D, 8, true>(vl, w, lane, [&](int row) { return vsrc + row * 128; });
+    sk = prec == TM_INT8 ? sload(a.ks8, kb) : ((HAS4 && prec == TM_INT4) ? sload(a.ks4, kb) : 0.0f);
+    cp_v.issue(reinterpret_cast<const uint8_t*>(a.vt16) + kb * VBYTES, 128, buf + KBYTES, w);
     if (prec == TM_INT8) {
-      const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k8) + kb * kBlock * D;
-      load_tile<kBlock, D / 16, false>(kl, w, lane, [&](int row) { return ks + row * D; });
+      cp_k8.issue(reinterpret_cast<const uint8_t*>(a.k8) + kb * kBlock * D, D, buf, w);
     } else if (HAS4 && prec == TM_INT4) {
-      const uint8_t* ks = a.k4 + kb * kBlock * (D / 2);
-      load_tile<kBlock, D / 32, false>(kl, w, lane, [&](int row) { return ks + row * (D / 2); });
+      cp_k4.issue(a.k4 + kb * kBlock * (D / 2), D / 2, buf, w);
     } else if (HAS16) {
-      const int last = len - 1 - j * kBlock;   // clamp rows past the sequence end (masked later)
       const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k) +
                           (static_cast<size_t>(se.tok_start + j * kBlock) * a.hkv + kv) * D * 2;
-      const size_t pitch = static_cast<size_t>(a.hkv) * D * 2;
-      load_tile<kBlock, D / 8, false>(kl, w, lane, [&](int row) { return ks + min(row, last) * pitch; });
+      if (j * kBlock + kBlock <= len) cp_k16.issue(ks, kpitch16, buf, w);
+      else cp_k16.issue_clamped(ks, kpitch16, buf, w, static_cast<uint32_t>(len - 1 - j * kBlock));
     }
   };
 
-  // issue the first tile before the Q loads so both are in flight together
-  float sk_cur = 0.0f, sk_nxt = 0.0f;
-  if (nruns > 0) issue(r_first, r_prec, lds, sk_nxt);
+  // vector-memory instructions this wave issues for one tile of precision prec
+  auto tile_vm = [&](int prec) {
+    int n = decltype(cp_v)::count(w);
+    if (prec == TM_INT8) n += decltype(cp_k8)::count(w);
+    else if (HAS4 && prec == TM_INT4) n += decltype(cp_k4)::count(w);
+    else if (HAS16) n += decltype(cp_k16)::count(w);
+    return n;
+  };
+
+  // ---- traversal iterator: produce() yields the next tile (j = -1 at the end)
+  int ri = 0, roff = 0;
+  int r_first = 0, r_count = 0, r_prec = 0;
+  if (nruns > 0) {
+    const RunEntry e = run_at(0);
+    r_first = static_cast<int>(e.ktile);
+    r_count = static_cast<int>(e.count_prec & 0xFFFFFFu);
+    r_prec = static_cast<int>(e.count_prec >> 24);
+  }
+  auto produce = [&](int& j, int& p) {
+    if (ri >= nruns) {
+      j = -1;
+      p = 0;
+      return;
+    }
+    j = r_first + roff;
+    p = r_prec;
+    if (++roff >= r_count) {
+      ++ri;
+      roff = 0;
+      if (ri < nruns) {
+        if (ri - run_base >= 64) {   // next chunk of the run list (items with more than 64 runs)
+          run_base += 64;
+          run_lane = RunEntry{0u, 0u};
+          if (run_base + lane < nruns) run_lane = runs[run_base + lane];
+        }
+        const RunEntry e = run_at(ri);
+        r_first = static_cast<int>(e.ktile);
+        r_count = static_cast<int>(e.count_prec & 0xFFFFFFu);
+        r_prec = static_cast<int>(e.count_prec >> 24);
+      }
+    }
+  };
+
+  // prologue: the first STAGES-1 tiles are requested before the Q loads
+  int tj[STAGES], tp[STAGES];
+  float tsk[STAGES];
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) {
+    tj[s] = -1;
+    tp[s] = 0;
+    tsk[s] = 0.0f;
+  }
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    produce(tj[s], tp[s]);
+    if (tj[s] >= 0) issue(tj[s], tp[s], lds + s * BUF, tsk[s]);
+  }
 
   // ---- resident Q operands (B operand of S^T = K Q^T)
   i32x4 q8[QB][NC8];
@@ -218,87 +337,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float sq8 = qblk_ok ? a.qs8[qblk_g] : 0.0f;
   const float sq4 = (HAS4 && qblk_ok) ? a.qs4[qblk_g] : 0.0f;
 
-  float m_use[QB], l_run[QB];
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<_Float16>(1.0f);
+  float m_use[QB];
+  f32x4 lacc[QB];                // row sums (all 4 entries equal)
   f32x4 oacc[ND][QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_use[qb] = kNegBig;
-    l_run[qb] = 0.0f;
+    lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < ND; ++db) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  int cur_j = r_first, cur_p = r_prec;
-  bool have = nruns > 0;
   int buf = 0;
-  while (have) {
-    // next tile of the traversal
-    int nxt_j = -1, nxt_p = 0;
-    if (++roff >= r_count) {
-      ++ri;
-      roff = 0;
-      if (ri < nruns) {
-        const RunEntry rr = runs[ri];
-        r_first = static_cast<int>(rr.ktile);
-        r_count = static_cast<int>(rr.count_prec & 0xFFFFFFu);
-        r_prec = static_cast<int>(rr.count_prec >> 24);
-      }
+  while (tj[0] >= 0) {
+    // request tile t+STAGES-1 once tile t has landed everywhere: wait until only
+    // this wave's loads of the younger in-flight tiles are outstanding (vector
+    // memory completes in issue order), then a barrier for the other waves;
+    // after it the buffer computed in the previous iteration is free.
+    produce(tj[STAGES - 1], tp[STAGES - 1]);
+    int younger = 0;
+#pragma unroll
+    for (int s = 1; s < STAGES - 1; ++s)
+      if (tj[s] >= 0) younger += tile_vm(tp[s]);
+    wait_vm(younger);
+    __syncthreads();
+    if (tj[STAGES - 1] >= 0) {
+      int nb = buf + STAGES - 1;
+      if (nb >= STAGES) nb -= STAGES;
+      issue(tj[STAGES - 1], tp[STAGES - 1], lds + nb * BUF, tsk[STAGES - 1]);
     }
-    if (ri < nruns) {
-      nxt_j = r_first + roff;
-      nxt_p = r_prec;
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the current tile have landed
-    __syncthreads();                 // ... and everyone's; the other buffer is free
-    sk_cur = sk_nxt;
-    if (nxt_j >= 0) issue(nxt_j, nxt_p, lds + (buf ^ 1) * BUF, sk_nxt);
 
     const uint8_t* kl = lds + buf * BUF;
     const uint8_t* vl = kl + KBYTES;
-    const int j = cur_j;
-    const int prec = cur_p;
+    const int j = tj[0];
+    const int prec = tp[0];
+    const float sk_cur = tsk[0];
     const bool need_mask = (j * kBlock + kBlock - 1 > qrow0) || (j * kBlock + kBlock > len);
 
-    // ---- S^T = K Q^T, then scores in log2 units
-    float s[4][QB][4];
-    float mx[QB];
+    // ---- S^T = K Q^T as fp32 values x (integers converted exactly), scale cs
+    f32x4 xf[4][QB];
+    float cs;
     if (HAS16 && prec == TM_FP16) {
-      f32x4 acc[4][QB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int row = sigma(kb, l16);
+        for (int qb = 0; qb < QB; ++qb) xf[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      q16_t av[4][NC16];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int c = 0; c < NC16; ++c) {
-          q16_t av;
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(kl + lds_off<D / 8, false>(row, 4 * c + g));
-          __builtin_memcpy(&av, &raw, 16);
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(kl + lds_off<D / 8, false>(sigma(kb, l16), 4 * c + g));
+          __builtin_memcpy(&av[kb][c], &raw, 16);
+        }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int c = 0; c < NC16; ++c)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             if constexpr (BF16)
-              acc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, q16[qb][c], acc[kb][qb], 0, 0, 0);
+              xf[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kb][c], q16[qb][c], xf[kb][qb], 0, 0, 0);
             else
-              acc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, q16[qb][c], acc[kb][qb], 0, 0, 0);
+              xf[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kb][c], q16[qb][c], xf[kb][qb], 0, 0, 0);
           }
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        mx[qb] = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = acc[kb][qb][i] * a.tau_log2e;
-            if (need_mask) {
-              const int key = j * kBlock + sigma(kb, 4 * g + i);
-              if (key > qrow0 + qb * 16 + l16 || key >= len) x = -INFINITY;
-            }
-            s[kb][qb][i] = x;
-            mx[qb] = fmaxf(mx[qb], x);
-          }
-      }
+      cs = a.tau_log2e;
     } else {
       const bool is8 = !HAS4 || prec == TM_INT8;
       i32x4 acc[4][QB];
@@ -365,77 +471,103 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
         }
       }
-      const float cs = is8 ? (sq8 * sk_cur) * a.tau_log2e : (sq4 * sk_cur) * (a.tau_log2e * (1.0f / 256.0f));
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          mx[qb] = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = j * kBlock + sigma(kb, 4 * g + i);
-              float x = static_cast<float>(acc[kb][qb][i]) * cs;
-              if (key > qrow0 + qb * 16 + l16 || key >= len) x = -INFINITY;
-              s[kb][qb][i] = x;
-              mx[qb] = fmaxf(mx[qb], x);
-            }
-        }
-      } else {
-        // scale >= 0: the row max of the scores is the scaled max of the integers
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          int im = acc[0][qb][0];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              im = max(im, acc[kb][qb][i]);
-              s[kb][qb][i] = static_cast<float>(acc[kb][qb][i]) * cs;
-            }
-          mx[qb] = static_cast<float>(im) * cs;
-        }
-      }
-    }
-
-    // ---- shared online softmax (log2 domain, lazily re-based)
-    bool rebase = false;
-    float alpha[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float m = fmaxf(mx[qb], __shfl_xor(mx[qb], 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      alpha[qb] = 1.0f;
-      if (m > m_use[qb] + 8.0f) {
-        alpha[qb] = __builtin_amdgcn_exp2f(m_use[qb] - m);
-        m_use[qb] = m;
-        rebase = true;
-      }
-    }
-    if (__any(rebase)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        l_run[qb] *= alpha[qb];
-#pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha[qb];
-      }
-    }
-    f16x8 pb[2][QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float ps = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[kb][qb][i] - m_use[qb]);
-          ps += p;
-          pb[kb >> 1][qb][4 * (kb & 1) + i] = static_cast<_Float16>(p);
-        }
-      l_run[qb] += ps;
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xf[kb][qb][i] = static_cast<float>(acc[kb][qb][i]);
+      cs = is8 ? (sq8 * sk_cur) * a.tau_log2e : (sq4 * sk_cur) * (a.tau_log2e * (1.0f / 256.0f));
     }
 
-    // ---- O^T += V^T P^T
+    // ---- shared online softmax (log2 domain, lazily re-based).  cs >= 0.
+    f16x8 pb[2][QB];
+    if (need_mask) {
+      // tiles crossing the diagonal or the sequence end: explicit masked scores
+      float sm[4][QB][4];
+      bool rebase = false;
+      float alpha[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j * kBlock + sigma(kb, 4 * g + i);
+            float x = xf[kb][qb][i] * cs;
+            if (key > qrow0 + qb * 16 + l16 || key >= len) x = -INFINITY;
+            sm[kb][qb][i] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = max4(mx);
+        alpha[qb] = 1.0f;
+        if (mx > m_use[qb] + 8.0f) {
+          alpha[qb] = __builtin_amdgcn_exp2f(m_use[qb] - mx);
+          m_use[qb] = mx;
+          rebase = true;
+        }
+      }
+      if (__any(rebase)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          lacc[qb] *= alpha[qb];
+#pragma unroll
+          for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha[qb];
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pb[kb >> 1][qb][4 * (kb & 1) + i] =
+                static_cast<_Float16>(__builtin_amdgcn_exp2f(sm[kb][qb][i] - m_use[qb]));
+    } else {
+      bool rebase = false;
+      float alpha[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = xf[0][qb][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, xf[kb][qb][i]);
+        mx = max4(mx) * cs;
+        alpha[qb] = 1.0f;
+        if (mx > m_use[qb] + 8.0f) {
+          alpha[qb] = __builtin_amdgcn_exp2f(m_use[qb] - mx);
+          m_use[qb] = mx;
+          rebase = true;
+        }
+      }
+      if (__any(rebase)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          lacc[qb] *= alpha[qb];
+#pragma unroll
+          for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha[qb];
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float nm = -m_use[qb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pb[kb >> 1][qb][4 * (kb & 1) + i] =
+                static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][qb][i], cs, nm)));
+      }
+    }
+
+    // ---- O^T += V^T P^T; row sums += 1^T P^T
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[c2][qb], lacc[qb], 0, 0, 0);
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       const int dv = db * 16 + l16;
@@ -450,17 +582,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
 
-    buf ^= 1;
-    have = nxt_j >= 0;
-    cur_j = nxt_j;
-    cur_p = nxt_p;
+    if (++buf == STAGES) buf = 0;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+      tj[s] = tj[s + 1];
+      tp[s] = tp[s + 1];
+      tsk[s] = tsk[s + 1];
+    }
   }
 
   // ---- epilogue: O = O / l, lse
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float lt = l_run[qb] + __shfl_xor(l_run[qb], 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = lacc[qb][0];
     const int r = qrow0 + qb * 16 + l16;
     if (r >= len) continue;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
