@@ -237,7 +237,9 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
  * product of codes; FP16 tiles: scale * q . k), applied to V, with P rounded
  * to fp16 for the PV product ([TriAttention] abstract: one normalized output
  * from both QK precisions; [TileMix] abstract: shared online-softmax state).
- * Errors: TM_E_ARG, TM_E_SHAPE (tensors not matching the shape), TM_E_HIP. */
+ * Errors: TM_E_ARG, TM_E_SHAPE (tensors not matching the shape),
+ * TM_E_UNSUPPORTED (a sequence whose 16-bit keys of one KV head span 2 GiB or
+ * more, i.e. len * hkv * d * 2 >= 2^31), TM_E_HIP. */
 tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kind,
                      const void* q, const void* k,
                      const tm_qtensor* qq, const tm_qtensor* kq, const tm_qtensor* vq,

@@ -40,6 +40,8 @@
 //    so advancing the traversal needs no memory access;
 //  * workgroups are remapped so the 4 query heads of a GQA group run on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share K/V in L2.
+#include <climits>
+
 #include "tm_kernels.h"
 
 namespace tmx {
@@ -48,6 +50,9 @@ namespace tmx {
 __device__ __forceinline__ int sigma(int kb, int m) {
   return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
 }
+
+// sigma(kb, m) - sigma(0, m): the part of the key row that depends on kb only.
+__host__ __device__ constexpr int krow(int kb) { return 32 * (kb >> 1) + 4 * (kb & 1); }
 
 // Swizzle key of a row for a tile whose rows hold NCH 16-byte chunks: rows read
 // together by 8 lanes (sigma rows base+{0..3, 8..11} for K, consecutive rows
@@ -84,6 +89,14 @@ __device__ __forceinline__ float max4(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// the same for int32 values
+__device__ __forceinline__ int max4i(int v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  const int m = max(static_cast<int>(s[0]), static_cast<int>(s[1]));
+  const auto r = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(m), static_cast<uint32_t>(m), false, false);
+  return max(static_cast<int>(r[0]), static_cast<int>(r[1]));
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (n <= 15).
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
@@ -115,49 +128,45 @@ __device__ __forceinline__ uint32_t remap_block(uint32_t b, uint32_t n) {
   return c * kChunk + (r % kXcd) * kGroup + r / kXcd;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
 // Per-lane layout of a direct-to-LDS tile copy: a region of ROWS rows x NCH
-// 16-byte chunks is moved by ROWS*NCH/64 instructions of 1 KiB; instruction n
-// fills LDS bytes [n*1024, n*1024+1024) and lane L lands at n*1024 + 16L, which
-// is row (n*1024 + 16L) / (16 NCH), swizzled slot L mod NCH, i.e. it must load
-// logical chunk slot ^ swz(row).  Wave w issues instructions n = 4i + w.
+// 16-byte chunks is moved by ROWS*NCH/64 buffer loads of 1 KiB; load n fills
+// LDS bytes [n*1024, n*1024+1024) and lane L lands at n*1024 + 16L, which is
+// row (n*1024 + 16L) / (16 NCH), swizzled slot L mod NCH, i.e. it must fetch
+// logical chunk slot ^ swz(row).  Wave w issues loads n = 4i + w.  The lane's
+// source offset inside a tile is fixed for the whole item; the tile's own
+// offset goes in the scalar offset of the load.
 template <int ROWS, int NCH, bool VT>
 struct TileCopy {
   static constexpr int NI = ROWS * NCH / 64;
   static constexpr int PER = NI >= 4 ? NI / 4 : 1;
   static_assert(NI < 4 || NI % 4 == 0, "tile regions are whole multiples of 4 KiB");
-  uint32_t row[PER], col[PER];   // source row and byte column of each of this lane's loads
-  // vector-memory instructions wave w issues for one copy of the region
-  __device__ __forceinline__ static int count(int w) { return NI >= 4 ? PER : (w < NI ? 1 : 0); }
-  __device__ __forceinline__ void init(int w, int lane) {
+  uint32_t voff[PER];
+  __device__ __forceinline__ void init(int w, int lane, uint32_t pitch) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int n = i * 4 + w;
       const int off = n * 1024 + lane * 16;
       const int r = off / (NCH * 16);
       const int slot = (off / 16) % NCH;
-      row[i] = r;
-      col[i] = static_cast<uint32_t>((slot ^ swz<NCH, VT>(r)) * 16);
+      voff[i] = static_cast<uint32_t>(r) * pitch + static_cast<uint32_t>((slot ^ swz<NCH, VT>(r)) * 16);
     }
   }
-  // src + row * pitch + col  ->  lds + n * 1024
-  __device__ __forceinline__ void issue(const uint8_t* src, uint32_t pitch, uint8_t* lds, int w) const {
+  // tile at byte `soff` of `rs` -> LDS [dst, dst + ROWS * NCH * 16)
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t soff, uint8_t* dst, int w) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       if (NI < 4 && w >= NI) break;
-      const uint8_t* g = src + (row[i] * pitch + col[i]);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
-                                       reinterpret_cast<void*>(lds + (i * 4 + w) * 1024), 16, 0, 0);
-    }
-  }
-  // same, with source rows clamped to `last` (rows past a sequence end)
-  __device__ __forceinline__ void issue_clamped(const uint8_t* src, uint32_t pitch, uint8_t* lds, int w,
-                                                uint32_t last) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (NI < 4 && w >= NI) break;
-      const uint8_t* g = src + (min(row[i], last) * pitch + col[i]);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
-                                       reinterpret_cast<void*>(lds + (i * 4 + w) * 1024), 16, 0, 0);
+#if defined(__HIP_DEVICE_COMPILE__)   // (the host pass never runs this body)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (i * 4 + w) * 1024), 16, voff[i], soff, 0, 0);
+#endif
     }
   }
 };
@@ -176,14 +185,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr bool HAS16 = KIND == TM_POLICY_BITMASK;
   typedef typename std::conditional<BF16, bf16x8, f16x8>::type q16_t;
 
-  // pipeline depth: tiles resident or in flight (LDS: STAGES * BUF bytes).  Two
-  // measured faster than three on MI355X: the deeper ring adds per-tile
-  // scalar bookkeeping and the loads mostly hit L2.
-  constexpr int STAGES = 2;
-  __shared__ __align__(1024) uint8_t lds[STAGES * BUF];
+  // two tile buffers, at LDS offsets 0 and kBufStride: the next tile streams
+  // in while the current one is used; switching buffers flips one address bit
+  constexpr int kBufStride = 32768;
+  static_assert(BUF <= kBufStride, "tile buffer larger than its slot");
+  __shared__ __align__(1024) uint8_t lds[kBufStride + BUF];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const TravHeader* th = reinterpret_cast<const TravHeader*>(a.trav);
   if (th->kind != static_cast<uint32_t>(KIND)) return;   // traversal of another policy kind
   const uint32_t item_idx = remap_block(blockIdx.x, a.n_items);
@@ -194,108 +204,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int head = it.head, kv = head / (a.hq / a.hkv);
   const int len = se.len;
   const int nbs = (len + kBlock - 1) / kBlock;
+  const int ntiles = static_cast<int>(it.n8 + it.n4 + it.n16);
   const int qrow0 = it.qtile * BQ + w * RW;
   const int qblk = qrow0 / kBlock;
   const bool qblk_ok = qblk < nbs;
   const size_t qblk_g = static_cast<size_t>(head) * a.nblk + se.blk_start + qblk;
   const size_t kv_blk0 = static_cast<size_t>(kv) * a.nblk + se.blk_start;
   const uint32_t kpitch16 = static_cast<uint32_t>(a.hkv) * D * 2;   // bytes between key rows of k
+  const float sq8 = qblk_ok ? a.qs8[qblk_g] : 0.0f;
+  const float sq4 = (HAS4 && qblk_ok) ? a.qs4[qblk_g] : 0.0f;
+  const float tau = a.tau_log2e;
+
+  // buffer resources over this (sequence, KV head): tile j starts at j * tile bytes
+  const __amdgpu_buffer_rsrc_t rs_v =
+      make_rsrc(reinterpret_cast<const uint8_t*>(a.vt16) + kv_blk0 * VBYTES, static_cast<uint32_t>(nbs) * VBYTES);
+  const __amdgpu_buffer_rsrc_t rs_k8 = make_rsrc(reinterpret_cast<const uint8_t*>(a.k8) + kv_blk0 * (kBlock * D),
+                                                 static_cast<uint32_t>(nbs) * (kBlock * D));
+  __amdgpu_buffer_rsrc_t rs_k4 = rs_k8, rs_k16 = rs_k8;
+  if constexpr (HAS4)
+    rs_k4 = make_rsrc(a.k4 + kv_blk0 * (kBlock * D / 2), static_cast<uint32_t>(nbs) * (kBlock * D / 2));
+  if constexpr (HAS16)   // rows past the sequence end fall outside the range and read as zeros
+    rs_k16 = make_rsrc(reinterpret_cast<const uint8_t*>(a.k) + (static_cast<size_t>(se.tok_start) * a.hkv + kv) * D * 2,
+                       static_cast<uint32_t>(len - 1) * kpitch16 + D * 2);
+
+  TileCopy<D, 8, true> cp_v;
+  TileCopy<kBlock, D / 16, false> cp_k8;
+  TileCopy<kBlock, D / 32, false> cp_k4;
+  TileCopy<kBlock, D / 8, false> cp_k16;
+  cp_v.init(w, lane, 128);
+  cp_k8.init(w, lane, D);
+  if constexpr (HAS4) cp_k4.init(w, lane, D / 2);
+  if constexpr (HAS16) cp_k16.init(w, lane, kpitch16);
+
+  // ---- per-lane LDS read offsets.  Key rows are read in the order
+  // sigma(kb, l16) = sigma(0, l16) + 32 (kb >> 1) + 4 (kb & 1); the swizzle
+  // depends on row bits the kb terms leave alone, so every 16-key block kb and
+  // both buffers are constant offsets from one per-lane base per 16-byte chunk
+  // column; likewise V^T rows db * 16 + l16 for every channel block db.
+  const int r0 = sigma(0, l16);
+  int kb8[NC8], kb16[NC16], kb4, vb[2];
+#pragma unroll
+  for (int c = 0; c < NC8; ++c) kb8[c] = lds_off<D / 16, false>(r0, 4 * c + g);
+#pragma unroll
+  for (int c = 0; c < NC16; ++c) kb16[c] = lds_off<D / 8, false>(r0, 4 * c + g);
+  if constexpr (D == 128) kb4 = lds_off<4, false>(r0, g);
+  else kb4 = lds_off<2, false>(r0, g >> 1) + (g & 1) * 8;
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) vb[c2] = lds_off<8, true>(l16, 4 * c2 + g);
 
   // ---- run list: one entry per lane, 64 runs per chunk
   const int nruns = static_cast<int>(it.nruns);
   int run_base = 0;
   RunEntry run_lane = RunEntry{0u, 0u};
   if (lane < nruns) run_lane = runs[lane];
-  auto run_at = [&](int r) {   // uniform r in [run_base, run_base + 64)
-    RunEntry e;
-    e.ktile = __builtin_amdgcn_readlane(run_lane.ktile, r - run_base);
-    e.count_prec = __builtin_amdgcn_readlane(run_lane.count_prec, r - run_base);
-    return e;
-  };
 
-  TileCopy<D, 8, true> cp_v;
-  TileCopy<kBlock, D / 16, false> cp_k8;
-  TileCopy<kBlock, D / 32, false> cp_k4;
-  TileCopy<kBlock, D / 8, false> cp_k16;
-  cp_v.init(w, lane);
-  cp_k8.init(w, lane);
-  if constexpr (HAS4) cp_k4.init(w, lane);
-  if constexpr (HAS16) cp_k16.init(w, lane);
-
-  // Start loading tile j into `buf` and fetch its K scale (read after the next
-  // barrier, when every load of the tile has been waited for).
-  auto issue = [&](int j, int prec, uint8_t* buf, float& sk) {
-    const size_t kb = kv_blk0 + j;
-    sk = prec == TM_INT8 ? sload(a.ks8, kb) : ((HAS4 && prec == TM_INT4) ? sload(a.ks4, kb) : 0.0f);
-    cp_v.issue(reinterpret_cast<const uint8_t*>(a.vt16) + kb * VBYTES, 128, buf + KBYTES, w);
-    if (prec == TM_INT8) {
-      cp_k8.issue(reinterpret_cast<const uint8_t*>(a.k8) + kb * kBlock * D, D, buf, w);
-    } else if (HAS4 && prec == TM_INT4) {
-      cp_k4.issue(a.k4 + kb * kBlock * (D / 2), D / 2, buf, w);
-    } else if (HAS16) {
-      const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k) +
-                          (static_cast<size_t>(se.tok_start + j * kBlock) * a.hkv + kv) * D * 2;
-      if (j * kBlock + kBlock <= len) cp_k16.issue(ks, kpitch16, buf, w);
-      else cp_k16.issue_clamped(ks, kpitch16, buf, w, static_cast<uint32_t>(len - 1 - j * kBlock));
-    }
-  };
-
-  // vector-memory instructions this wave issues for one tile of precision prec
-  auto tile_vm = [&](int prec) {
-    int n = decltype(cp_v)::count(w);
-    if (prec == TM_INT8) n += decltype(cp_k8)::count(w);
-    else if (HAS4 && prec == TM_INT4) n += decltype(cp_k4)::count(w);
-    else if (HAS16) n += decltype(cp_k16)::count(w);
-    return n;
-  };
-
-  // ---- traversal iterator: produce() yields the next tile (j = -1 at the end)
-  int ri = 0, roff = 0;
-  int r_first = 0, r_count = 0, r_prec = 0;
-  if (nruns > 0) {
-    const RunEntry e = run_at(0);
-    r_first = static_cast<int>(e.ktile);
-    r_count = static_cast<int>(e.count_prec & 0xFFFFFFu);
-    r_prec = static_cast<int>(e.count_prec >> 24);
-  }
-  auto produce = [&](int& j, int& p) {
-    if (ri >= nruns) {
-      j = -1;
-      p = 0;
-      return;
-    }
-    j = r_first + roff;
-    p = r_prec;
-    if (++roff >= r_count) {
-      ++ri;
-      roff = 0;
-      if (ri < nruns) {
-        if (ri - run_base >= 64) {   // next chunk of the run list (items with more than 64 runs)
-          run_base += 64;
-          run_lane = RunEntry{0u, 0u};
-          if (run_base + lane < nruns) run_lane = runs[run_base + lane];
-        }
-        const RunEntry e = run_at(ri);
-        r_first = static_cast<int>(e.ktile);
-        r_count = static_cast<int>(e.count_prec & 0xFFFFFFu);
-        r_prec = static_cast<int>(e.count_prec >> 24);
+  // ---- tile list: after expand(c), lane L describes executed tile 64c + L of
+  // the item: key tile | precision << 24, and its score scale (log2 units).
+  uint32_t tl_jp = 0u;
+  float tl_cs = 0.0f;
+  int rr = 0, rcum = 0;   // first run not wholly consumed, tiles before it
+  auto expand = [&](int c) {
+    const int t = c * 64 + lane;
+    const int cend = c * 64 + 64;
+    uint32_t jp = 0u;
+    while (rr < nruns && rcum < cend) {
+      if (rr - run_base >= 64) {   // next chunk of the run list (items with more than 64 runs)
+        run_base += 64;
+        run_lane = RunEntry{0u, 0u};
+        if (run_base + lane < nruns) run_lane = runs[run_base + lane];
       }
+      const uint32_t kt = __builtin_amdgcn_readlane(run_lane.ktile, rr - run_base);
+      const uint32_t cp = __builtin_amdgcn_readlane(run_lane.count_prec, rr - run_base);
+      const int cnt = static_cast<int>(cp & 0xFFFFFFu);
+      if (t >= rcum && t < rcum + cnt) jp = (kt + static_cast<uint32_t>(t - rcum)) | (cp & 0xFF000000u);
+      if (rcum + cnt > cend) break;
+      rcum += cnt;
+      ++rr;
     }
+    tl_jp = jp;
+    const uint32_t pj = jp >> 24;
+    const size_t kb = kv_blk0 + (jp & 0xFFFFFFu);
+    float cs = tau;
+    if (pj == TM_INT8) cs = (sq8 * a.ks8[kb]) * tau;
+    else if (HAS4 && pj == TM_INT4) cs = (sq4 * a.ks4[kb]) * (tau * (1.0f / 256.0f));
+    tl_cs = cs;
   };
 
-  // prologue: the first STAGES-1 tiles are requested before the Q loads
-  int tj[STAGES], tp[STAGES];
-  float tsk[STAGES];
-#pragma unroll
-  for (int s = 0; s < STAGES; ++s) {
-    tj[s] = -1;
-    tp[s] = 0;
-    tsk[s] = 0.0f;
-  }
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
-    produce(tj[s], tp[s]);
-    if (tj[s] >= 0) issue(tj[s], tp[s], lds + s * BUF, tsk[s]);
+  // start loading tile j (precision prec) into buffer BUFC
+  auto issue = [&](uint32_t j, uint32_t prec, int boff) {
+    uint8_t* dst = lds + boff;
+    cp_v.issue(rs_v, j * VBYTES, dst + KBYTES, w);
+    if (prec == TM_INT8) cp_k8.issue(rs_k8, j * (kBlock * D), dst, w);
+    else if (HAS4 && prec == TM_INT4) cp_k4.issue(rs_k4, j * (kBlock * D / 2), dst, w);
+    else if (HAS16) cp_k16.issue(rs_k16, j * (kBlock * kpitch16), dst, w);
+  };
+
+  uint32_t jp_cur = 0u;
+  if (ntiles > 0) {
+    expand(0);
+    jp_cur = __builtin_amdgcn_readlane(tl_jp, 0);
+    issue(jp_cur & 0xFFFFFFu, jp_cur >> 24, 0);
   }
 
   // ---- resident Q operands (B operand of S^T = K Q^T)
@@ -334,8 +342,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
-  const float sq8 = qblk_ok ? a.qs8[qblk_g] : 0.0f;
-  const float sq4 = (HAS4 && qblk_ok) ? a.qs4[qblk_g] : 0.0f;
 
   f16x8 ones;
 #pragma unroll
@@ -351,35 +357,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < ND; ++db) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  int buf = 0;
-  while (tj[0] >= 0) {
-    // request tile t+STAGES-1 once tile t has landed everywhere: wait until only
-    // this wave's loads of the younger in-flight tiles are outstanding (vector
-    // memory completes in issue order), then a barrier for the other waves;
-    // after it the buffer computed in the previous iteration is free.
-    produce(tj[STAGES - 1], tp[STAGES - 1]);
-    int younger = 0;
-#pragma unroll
-    for (int s = 1; s < STAGES - 1; ++s)
-      if (tj[s] >= 0) younger += tile_vm(tp[s]);
-    wait_vm(younger);
+  // One tile: wait for it (and free the other buffer), start the next tile's
+  // loads into the other buffer, then compute this one from buffer BUFC.
+  int t = 0;
+  auto body = [&]() {
+    const int boff = (t & 1) * kBufStride;
+    wait_vm(0);
     __syncthreads();
-    if (tj[STAGES - 1] >= 0) {
-      int nb = buf + STAGES - 1;
-      if (nb >= STAGES) nb -= STAGES;
-      issue(tj[STAGES - 1], tp[STAGES - 1], lds + nb * BUF, tsk[STAGES - 1]);
+    const int j = static_cast<int>(jp_cur & 0xFFFFFFu);
+    const uint32_t prec = jp_cur >> 24;
+    const float cs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(tl_cs), t & 63));
+    if (t + 1 < ntiles) {
+      if (((t + 1) & 63) == 0) expand((t + 1) >> 6);
+      jp_cur = __builtin_amdgcn_readlane(tl_jp, (t + 1) & 63);
+      issue(jp_cur & 0xFFFFFFu, jp_cur >> 24, boff ^ kBufStride);
     }
 
-    const uint8_t* kl = lds + buf * BUF;
+    const uint8_t* kl = lds + boff;
     const uint8_t* vl = kl + KBYTES;
-    const int j = tj[0];
-    const int prec = tp[0];
-    const float sk_cur = tsk[0];
     const bool need_mask = (j * kBlock + kBlock - 1 > qrow0) || (j * kBlock + kBlock > len);
 
-    // ---- S^T = K Q^T as fp32 values x (integers converted exactly), scale cs
+    // ---- S^T = K Q^T as fp32 values x (integers converted exactly), score = x * cs
     f32x4 xf[4][QB];
-    float cs;
+    float tmax[QB];   // the row's largest score in this tile (-inf if none)
     if (HAS16 && prec == TM_FP16) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int c = 0; c < NC16; ++c) {
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(kl + lds_off<D / 8, false>(sigma(kb, l16), 4 * c + g));
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(kl + krow(kb) * (D * 2) + kb16[c]);
           __builtin_memcpy(&av[kb][c], &raw, 16);
         }
 #pragma unroll
@@ -404,7 +404,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             else
               xf[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kb][c], q16[qb][c], xf[kb][qb], 0, 0, 0);
           }
-      cs = a.tau_log2e;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = qrow0 + qb * 16 + l16;
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = j * kBlock + sigma(kb, 4 * g + i);
+              if (key > row || key >= len) xf[kb][qb][i] = -INFINITY;
+            }
+        }
+        float mf = xf[0][qb][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mf = fmaxf(mf, xf[e >> 2][qb][e & 3]);
+        tmax[qb] = max4(mf) * cs;
+      }
     } else {
       const bool is8 = !HAS4 || prec == TM_INT8;
       i32x4 acc[4][QB];
@@ -418,7 +434,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int c = 0; c < NC8; ++c)
-            av[kb][c] = *reinterpret_cast<const i32x4*>(kl + lds_off<D / 16, false>(sigma(kb, l16), 4 * c + g));
+            av[kb][c] = *reinterpret_cast<const i32x4*>(kl + krow(kb) * D + kb8[c]);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -431,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           u32x4 pk[4];
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
-            pk[kb] = *reinterpret_cast<const u32x4*>(kl + lds_off<4, false>(sigma(kb, l16), g));
+            pk[kb] = *reinterpret_cast<const u32x4*>(kl + krow(kb) * (D / 2) + kb4);
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             const i32x4 a0 = widen_nibbles(pk[kb][0], pk[kb][1]);
@@ -446,8 +462,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           // D == 64: rows of 32 packed bytes = 2 chunks; lane group g reads 8 bytes
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
-            const int row = sigma(kb, l16);
-            const u32x2 p = *reinterpret_cast<const u32x2*>(kl + lds_off<2, false>(row, g >> 1) + (g & 1) * 8);
+            const u32x2 p = *reinterpret_cast<const u32x2*>(kl + krow(kb) * (D / 2) + kb4);
             const i32x4 a0 = widen_nibbles(p[0], p[1]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
@@ -457,65 +472,97 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       if constexpr (DBG) {
         for (int e = 0; e < a.n_dbg; ++e) {
-          const int32_t* t = a.dbg_tiles + 4 * e;
-          if (t[0] == static_cast<int>(it.seq) && t[1] == head && t[2] == static_cast<int>(it.qtile) && t[3] == j) {
+          const int32_t* tt = a.dbg_tiles + 4 * e;
+          if (tt[0] == static_cast<int>(it.seq) && tt[1] == head && tt[2] == static_cast<int>(it.qtile) && tt[3] == j) {
             int32_t* dst = a.dbg_qk + static_cast<size_t>(e) * BQ * kBlock;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
               for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  dst[(w * RW + qb * 16 + l16) * kBlock + sigma(kb, 4 * g + i)] =
-                      is8 ? acc[kb][qb][i] : (acc[kb][qb][i] >> 8);
+                for (int i = 0; i < 4; ++i) {
+                  const int v = acc[kb][qb][i];
+                  dst[(w * RW + qb * 16 + l16) * kBlock + sigma(kb, 4 * g + i)] = is8 ? v : (v >> 8);
+                }
           }
         }
       }
+      // row maxima on the integer products (cs >= 0 keeps the order); masked
+      // keys count as INT_MIN, below every product (|a| <= 2^21)
+      int mrow[QB];
+      if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
+          const int row = qrow0 + qb * 16 + l16;
+          int mi = INT_MIN;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+          for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) xf[kb][qb][i] = static_cast<float>(acc[kb][qb][i]);
-      cs = is8 ? (sq8 * sk_cur) * a.tau_log2e : (sq4 * sk_cur) * (a.tau_log2e * (1.0f / 256.0f));
-    }
-
-    // ---- shared online softmax (log2 domain, lazily re-based).  cs >= 0.
-    f16x8 pb[2][QB];
-    if (need_mask) {
-      // tiles crossing the diagonal or the sequence end: explicit masked scores
-      float sm[4][QB][4];
-      bool rebase = false;
-      float alpha[QB];
+            for (int i = 0; i < 4; ++i) {
+              const int key = j * kBlock + sigma(kb, 4 * g + i);
+              mi = max(mi, (key > row || key >= len) ? INT_MIN : acc[kb][qb][i]);
+            }
+          mrow[qb] = mi;
+        }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          int mi = acc[0][qb][0];
+#pragma unroll
+          for (int e = 1; e < 16; ++e) mi = max(mi, acc[e >> 2][qb][e & 3]);
+          mrow[qb] = mi;
+        }
+      }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
+        const int mi = max4i(mrow[qb]);
+        tmax[qb] = mi == INT_MIN ? -INFINITY : static_cast<float>(mi) * cs;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xf[kb][qb][i] = static_cast<float>(acc[kb][qb][i]);
+      }
+    }
+
+    // ---- shared online softmax (log2 domain, lazily re-based): probabilities
+    // are taken against m_use, which moves only when a row's max grows by more
+    // than 8, so p <= 256.
+    f16x8 pb[2][QB];
+    bool rebase = false;
+    float alpha[QB], nb[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      alpha[qb] = 1.0f;
+      if (tmax[qb] > m_use[qb] + 8.0f) {
+        alpha[qb] = __builtin_amdgcn_exp2f(m_use[qb] - tmax[qb]);
+        m_use[qb] = tmax[qb];
+        rebase = true;
+      }
+      nb[qb] = -m_use[qb];
+    }
+    if (__any(rebase)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        lacc[qb] *= alpha[qb];
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha[qb];
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = qrow0 + qb * 16 + l16;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = j * kBlock + sigma(kb, 4 * g + i);
-            float x = xf[kb][qb][i] * cs;
-            if (key > qrow0 + qb * 16 + l16 || key >= len) x = -INFINITY;
-            sm[kb][qb][i] = x;
-            mx = fmaxf(mx, x);
+            const float s = __builtin_fmaf(xf[kb][qb][i], cs, nb[qb]);
+            pb[kb >> 1][qb][4 * (kb & 1) + i] =
+                static_cast<_Float16>(__builtin_amdgcn_exp2f((key > row || key >= len) ? -INFINITY : s));
           }
-        mx = max4(mx);
-        alpha[qb] = 1.0f;
-        if (mx > m_use[qb] + 8.0f) {
-          alpha[qb] = __builtin_amdgcn_exp2f(m_use[qb] - mx);
-          m_use[qb] = mx;
-          rebase = true;
-        }
       }
-      if (__any(rebase)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          lacc[qb] *= alpha[qb];
-#pragma unroll
-          for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha[qb];
-        }
-      }
+    } else {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -523,73 +570,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             pb[kb >> 1][qb][4 * (kb & 1) + i] =
-                static_cast<_Float16>(__builtin_amdgcn_exp2f(sm[kb][qb][i] - m_use[qb]));
-    } else {
-      bool rebase = false;
-      float alpha[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = xf[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, xf[kb][qb][i]);
-        mx = max4(mx) * cs;
-        alpha[qb] = 1.0f;
-        if (mx > m_use[qb] + 8.0f) {
-          alpha[qb] = __builtin_amdgcn_exp2f(m_use[qb] - mx);
-          m_use[qb] = mx;
-          rebase = true;
-        }
-      }
-      if (__any(rebase)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          lacc[qb] *= alpha[qb];
-#pragma unroll
-          for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha[qb];
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float nm = -m_use[qb];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pb[kb >> 1][qb][4 * (kb & 1) + i] =
-                static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][qb][i], cs, nm)));
-      }
+                static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][qb][i], cs, nb[qb])));
     }
 
-    // ---- O^T += V^T P^T; row sums += 1^T P^T
+    // ---- O^T += V^T P^T; row sums += 1^T P^T.  V^T operands are read one
+    // channel block ahead of the MFMAs that use them (pinned below, which also
+    // keeps the scheduler from hoisting every read and running out of VGPRs).
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[c2][qb], lacc[qb], 0, 0, 0);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int dv = db * 16 + l16;
+    f16x8 va[2][2];
+    auto read_v = [&](int db, f16x8* dst) {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        f16x8 va;
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(vl + lds_off<8, true>(dv, 4 * c2 + g));
-        __builtin_memcpy(&va, &raw, 16);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(vl + db * 2048 + vb[c2]);
+        __builtin_memcpy(&dst[c2], &raw, 16);
+      }
+    };
+    read_v(0, va[0]);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      if (db + 1 < ND) read_v(db + 1, va[(db + 1) & 1]);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[c2][qb], oacc[db][qb], 0, 0, 0);
-      }
+          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[db & 1][c2], pb[c2][qb], oacc[db][qb], 0, 0, 0);
     }
-
-    if (++buf == STAGES) buf = 0;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 0);
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-      tj[s] = tj[s + 1];
-      tp[s] = tp[s + 1];
-      tsk[s] = tsk[s + 1];
+    for (int db = 1; db < ND; ++db) {
+      if (db + 1 < ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 0);
     }
-  }
+  };
+
+  for (; t < ntiles; ++t) body();
 
   // ---- epilogue: O = O / l, lse
 #pragma unroll

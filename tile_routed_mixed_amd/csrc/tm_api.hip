@@ -261,6 +261,14 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
   if ((st = check_qtensor(qq, shape->hq, TM_ROWS, si.nblk, false)) != TM_OK) return st;
   if ((st = check_qtensor(kq, shape->hkv, TM_ROWS, si.nblk, false)) != TM_OK) return st;
   if ((st = check_qtensor(vq, shape->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
+  // the kernel addresses one (sequence, KV head)'s K and V^T tiles through
+  // 32-bit buffer offsets: keep every such range below 2 GiB
+  for (int s = 0; s < shape->nseq; ++s) {
+    const int64_t len = shape->cu_seqlens[s + 1] - shape->cu_seqlens[s];
+    const int64_t nb = (len + 63) / 64;
+    const int64_t k16 = len * shape->hkv * shape->d * 2;
+    if (nb * 64 * shape->d * 2 >= (int64_t(1) << 31) || k16 >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
+  }
   PrefillArgs a;
   a.trav = static_cast<const uint8_t*>(trav);
   a.q = static_cast<const uint16_t*>(q);
