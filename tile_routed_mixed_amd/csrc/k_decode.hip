@@ -81,29 +81,118 @@ __device__ __forceinline__ f16x8 to_f16x8(u32x4 raw) {
   return v;
 }
 
+// Cache blocks of one (sequence, KV head), in the order a split walks them:
+// the sink block (when it lies outside the band), then blocks jstart .. nb-1
+// in ascending order: the INT4 band, the INT8 band, then the FP16 window.
+struct DecodeList {
+  int nb, jstart, jf, b8, sink, sink_extra, n_ex;
+  __device__ __forceinline__ int block(int e) const {
+    return sink_extra ? (e == 0 ? 0 : jstart + e - 1) : jstart + e;
+  }
+  __device__ __forceinline__ int prec(int j) const {
+    if (j >= jf) return TM_FP16;
+    if ((sink && j == 0) || nb - 1 - j < b8) return TM_INT8;
+    return TM_INT4;
+  }
+  // HBM cost of entries [0, e) in units of an INT4 block (INT8 2, FP16 4)
+  __device__ __forceinline__ int64_t weight(int e) const {
+    int64_t wsum = 0;
+    if (sink_extra && e > 0) {
+      wsum += 2;
+      --e;
+    }
+    const int hi = jstart + e;                        // blocks [jstart, hi)
+    const int qend = min(hi, jf);                     // quantized part [jstart, qend)
+    const int n16 = max(0, hi - max(jf, jstart));
+    int n8 = max(0, qend - max(jstart, nb - b8));
+    int n4 = max(0, qend - jstart) - n8;
+    if (sink && jstart == 0 && qend > 0 && nb - b8 > 0) {   // block 0 inside the INT4 range is INT8
+      ++n8;
+      --n4;
+    }
+    return wsum + 2 * n8 + n4 + 4 * n16;
+  }
+  // first entry e with weight(e) * parts >= total * c
+  __device__ __forceinline__ int split(int c, int parts) const {
+    const int64_t target = weight(n_ex) * c;
+    int lo = 0, hi = n_ex;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (weight(mid) * parts >= target) hi = mid;
+      else lo = mid + 1;
+    }
+    return lo;
+  }
+  // list index of the first FP16 block (n_ex if none)
+  __device__ __forceinline__ int first_fp16() const {
+    return jf < nb ? (sink_extra ? 1 : 0) + (jf - jstart) : n_ex;
+  }
+};
+
+// Swizzle of 16-byte chunk columns in the LDS copies of a block: K rows of
+// NCH chunks (rows read 16 at a time by one lane group) and V^T rows (16
+// channel rows read together at one key offset).
+template <int NCH>
+__device__ __forceinline__ int kswz(int row) { return row & (NCH - 1) & 7; }
+template <int NCH>
+__device__ __forceinline__ int vswz(int row) { return NCH >= 4 ? (row >> 2) & 3 : (row >> 3) & 1; }
+
+// Direct-to-LDS copy of a contiguous region of ROWS rows of NCH chunks with
+// the chunk columns of row r permuted by SW(r) (see TileCopy in the prefill).
+template <int ROWS, int NCH, int SWK>
+struct BlockCopy {
+  static constexpr int NI = ROWS * NCH / 64;            // 1 KiB loads per region
+  static constexpr int PER = (NI + 3) / 4;
+  uint32_t voff[PER];
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int off = (i * 4 + w) * 1024 + lane * 16;
+      const int r = off / (NCH * 16), slot = (off / 16) % NCH;
+      const int sw = SWK == 0 ? kswz<NCH>(r) : vswz<NCH>(r);
+      voff[i] = static_cast<uint32_t>(r * NCH * 16 + ((slot ^ sw) << 4));
+    }
+  }
+  __device__ __forceinline__ static int count(int w) { return w < NI % 4 || NI % 4 == 0 ? PER : PER - 1; }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t soff, uint8_t* dst, int w) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i * 4 + w < NI) lds_dma16(rs, dst + (i * 4 + w) * 1024, voff[i], soff);
+  }
+};
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  constexpr int NC = D / 32;      // f16 MFMA k-chunks over d
-  constexpr int ND = D / 16;      // output channel blocks
-  constexpr int DG = D / 4;       // channels per lane group in the QK operand
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  constexpr int NC = D / 32;          // k-chunks of the QK MFMA (lane group g owns channels DG*g ..)
+  constexpr int ND = D / 16;          // output channel blocks
+  constexpr int DG = D / 4;
+  constexpr int SLOT = 128 * D;       // bytes of one INT8 block: K rows then V^T rows
+  constexpr int S = 4;                // ring depth: S - 1 blocks stream in while one is used
+  constexpr int NCK8 = D / 16, NCK4 = D / 32;   // 16-byte chunks per K row
+  __shared__ __align__(1024) uint8_t lds[S * SLOT];
+
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int grp = a.hq / a.hkv;
 
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
-  const int blk0 = seq_blk_start(a.cu, b);
-  const int nb = (L + kBlock - 1) / kBlock;
-  const int b8 = a.b8[kv], b4 = a.b4[kv];
-  const int jf = a.tail > 0 ? max(0, (L - a.tail) / kBlock) : nb;    // first FP16 block
-  const int jlo = max(0, nb - b4);                                   // first block with delta < b4
-  const int jstart = min(jlo, jf);
-  const bool sink_extra = a.sink && jstart > 0;
-  const int n_ex = (nb - jstart) + (sink_extra ? 1 : 0);
-  const int e0 = static_cast<int>(static_cast<int64_t>(chunk) * n_ex / a.nsplit);
-  const int e1 = static_cast<int>(static_cast<int64_t>(chunk + 1) * n_ex / a.nsplit);
+  const int blk0 = __builtin_amdgcn_readfirstlane(seq_blk_start(a.cu, b));
+  DecodeList dl;
+  dl.nb = (L + kBlock - 1) / kBlock;
+  dl.b8 = __builtin_amdgcn_readfirstlane(a.b8[kv]);
+  dl.sink = a.sink;
+  dl.jf = a.tail > 0 ? max(0, (L - a.tail) / kBlock) : dl.nb;            // first FP16 block
+  dl.jstart = min(max(0, dl.nb - __builtin_amdgcn_readfirstlane(a.b4[kv])), dl.jf);                     // first block with delta < b4
+  dl.sink_extra = (a.sink && dl.jstart > 0) ? 1 : 0;
+  dl.n_ex = (dl.nb - dl.jstart) + dl.sink_extra;
+  const int e0 = dl.split(chunk, a.nsplit), e1 = dl.split(chunk + 1, a.nsplit);
+  const int eF = max(e0, min(e1, dl.first_fp16()));
+  const int nI = eF - e0;                                                 // quantized blocks of this split
+  const size_t kvb0 = static_cast<size_t>(kv) * a.nblk + blk0;
 
-  // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group).
+  // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group)
   f16x8 qop[NC];
   {
     const bool ok = l16 < grp;
@@ -115,156 +204,232 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  float m_run = kNegBig, l_run = 0.0f;
+  // buffer resources over this (sequence, KV head)'s blocks
+  const uint32_t nbs = static_cast<uint32_t>(dl.nb);
+  const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(a.k8 + kvb0 * (kBlock * D), nbs * (kBlock * D));
+  const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(a.v8 + kvb0 * (kBlock * D), nbs * (kBlock * D));
+  const __amdgpu_buffer_rsrc_t rk4 = make_rsrc(a.k4 + kvb0 * (kBlock * D / 2), nbs * (kBlock * D / 2));
+  const __amdgpu_buffer_rsrc_t rv4 = make_rsrc(a.v4 + kvb0 * (kBlock * D / 2), nbs * (kBlock * D / 2));
+  BlockCopy<kBlock, NCK8, 0> ck8;
+  BlockCopy<D, 4, 1> cv8;
+  BlockCopy<kBlock, NCK4, 0> ck4;
+  BlockCopy<D, 2, 1> cv4;
+  ck8.init(w, lane);
+  cv8.init(w, lane);
+  ck4.init(w, lane);
+  cv4.init(w, lane);
+  // list entry e -> cache block j, and whether it is an INT4 block (entries
+  // before eF are INT8 or INT4; see DecodeList)
+  const int eS = dl.sink_extra;
+  const int j4hi = min(dl.nb - dl.b8, dl.jf);
+  auto jof = [&](int e) { return e < eS ? 0 : dl.jstart + (e - eS); };
+  auto is4 = [&](int j) { return j >= dl.jstart && j < j4hi && !(dl.sink && j == 0); };
+  auto loads_of = [&](bool four) {   // vector-memory instructions this wave issues for one block
+    return four ? decltype(ck4)::count(w) + decltype(cv4)::count(w)
+                : decltype(ck8)::count(w) + decltype(cv8)::count(w);
+  };
+  auto issue = [&](int t) {
+    const int j = jof(e0 + t);
+    uint8_t* dst = lds + (t & (S - 1)) * SLOT;
+    if (!is4(j)) {
+      ck8.issue(rk8, j * (kBlock * D), dst, w);
+      cv8.issue(rv8, j * (kBlock * D), dst + kBlock * D, w);
+    } else {
+      ck4.issue(rk4, j * (kBlock * D / 2), dst, w);
+      cv4.issue(rv4, j * (kBlock * D / 2), dst + kBlock * D, w);
+    }
+  };
+
+  // per-lane LDS read offsets inside a ring slot: K row 16w + l16 (chunks of
+  // lane group g), V^T rows l16 + 16 db at keys 16w + 4g (db adds a constant)
+  const int krow = 16 * w + l16;
+  int k8off[NC / 2 > 0 ? NC / 2 : 1];
+#pragma unroll
+  for (int c2 = 0; c2 < NC / 2; ++c2) k8off[c2] = krow * D + ((((DG / 16) * g + c2) ^ kswz<NCK8>(krow)) << 4);
+  const int k4off = D == 128 ? krow * (D / 2) + ((g ^ kswz<NCK4>(krow)) << 4)
+                             : krow * (D / 2) + (((g >> 1) ^ kswz<NCK4>(krow)) << 4) + 8 * (g & 1);
+  const int v8off = kBlock * D + l16 * 64 + ((w ^ vswz<4>(l16)) << 4) + 4 * g;
+  const int v4off = kBlock * D + l16 * 32 + (((w >> 1) ^ vswz<2>(l16)) << 4) + 8 * (w & 1) + 2 * g;
+
+  float m_run = kNegBig, l_run = 0.0f;   // per lane: head l16, keys of lane group g
   f32x4 oacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int e = e0 + w; e < e1; e += 4) {
-    const int j = sink_extra ? (e == 0 ? 0 : jstart + e - 1) : jstart + e;
-    int prec;
-    if (j >= jf) prec = TM_FP16;
-    else if ((a.sink && j == 0) || (nb - 1 - j) < b8) prec = TM_INT8;
-    else prec = TM_INT4;
-    const size_t kblk = static_cast<size_t>(kv) * a.nblk + blk0 + j;
+  // One block's keys 16w .. 16w+15 given S^T scores (already scaled, log2
+  // units) in lane (g, head) for keys 4g + i, and the V^T operands.
+  auto softmax_pv = [&](float (&s)[4], const f16x4 (&va)[ND], float sv) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    {   // max over the 4 lane groups of the head (lanes l, l^16, l^32, l^48)
+      const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+    }
+    // re-base when a head's max passes m_run, to 2 above it: p <= 1/4, so
+    // p * sv stays inside the fp16 range, and small later rises need no re-base
+    const bool up = mx > m_run;
+    if (__any(up)) {
+      const float mn = up ? mx + 2.0f : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+    }
+    f16x4 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(s[i] - m_run);
+      l_run += p;
+      pb[i] = static_cast<_Float16>(p * sv);
+    }
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pb, oacc[db], 0, 0, 0);
+  };
 
-    // ---- K operands (A of S^T = K Q^T): lane (g, m) holds key dsigma(kb, m), channels DG*g ..
-    f16x8 kop[4][NC];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = dsigma(kb, l16);
-      if (prec == TM_INT8) {
-        const int8_t* src = a.k8 + (kblk * kBlock + key) * D + DG * g;
-#pragma unroll
-        for (int c2 = 0; c2 < NC / 2; ++c2) {
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(src + 16 * c2);
-          kop[kb][2 * c2] = fix_i8(widen_i8x4(raw[0]), widen_i8x4(raw[1]));
-          kop[kb][2 * c2 + 1] = fix_i8(widen_i8x4(raw[2]), widen_i8x4(raw[3]));
-        }
-      } else if (prec == TM_INT4) {
-        const uint8_t* src = a.k4 + (kblk * kBlock + key) * (D / 2) + (DG / 2) * g;
-#pragma unroll
-        for (int c4 = 0; c4 < NC / 4; ++c4) {
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(src + 16 * c4);
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) kop[kb][4 * c4 + e2] = widen_i4x8(raw[e2]);
-        }
-        if constexpr (NC % 4 != 0) {
-          const u32x2 raw = *reinterpret_cast<const u32x2*>(src + 16 * (NC / 4));
-          kop[kb][NC - 2] = widen_i4x8(raw[0]);
-          kop[kb][NC - 1] = widen_i4x8(raw[1]);
-        }
-      } else {
-        const int tk = j * kBlock + key;
-        const uint16_t* src = a.k16 + (static_cast<size_t>(tok0 + (tk < L ? tk : 0)) * a.hkv + kv) * D + DG * g;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          u32x4 raw = tk < L ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0, 0, 0, 0};
-          kop[kb][c] = to_f16x8<BF16>(raw);
-        }
-      }
+  // scale factors of a quantized block: cs = tau log2e sk, sv (scalar loads,
+  // fetched one block ahead)
+  auto scales = [&](int t, float& cs, float& sv) {
+    const int j = jof(e0 + t);
+    const size_t kblk = kvb0 + j;
+    if (!is4(j)) {
+      cs = sload(a.ks8, kblk);
+      sv = sload(a.vs8, kblk);
+    } else {
+      cs = sload(a.ks4, kblk);
+      sv = sload(a.vs4, kblk);
     }
-    // ---- V^T operands (A of O^T = V^T P^T): lane (g, dv) holds keys 16g .. 16g+15
-    f16x8 vop[ND][2];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int dv = db * 16 + l16;
-      if (prec == TM_INT8) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(a.v8 + (kblk * D + dv) * kBlock + 16 * g);
-        vop[db][0] = fix_i8(widen_i8x4(raw[0]), widen_i8x4(raw[1]));
-        vop[db][1] = fix_i8(widen_i8x4(raw[2]), widen_i8x4(raw[3]));
-      } else if (prec == TM_INT4) {
-        const u32x2 raw = *reinterpret_cast<const u32x2*>(a.v4 + (kblk * D + dv) * (kBlock / 2) + 8 * g);
-        vop[db][0] = widen_i4x8(raw[0]);
-        vop[db][1] = widen_i4x8(raw[1]);
-      } else {
-        const uint16_t* src = a.vt16 + (kblk * D + dv) * kBlock + 16 * g;
-        u32x4 r0 = *reinterpret_cast<const u32x4*>(src);
-        u32x4 r1 = *reinterpret_cast<const u32x4*>(src + 8);
-        __builtin_memcpy(&vop[db][0], &r0, 16);
-        __builtin_memcpy(&vop[db][1], &r1, 16);
-      }
-    }
+  };
+  float cs_n = 0.0f, sv_n = 0.0f;
+  if (nI > 0) scales(0, cs_n, sv_n);
 
-    // ---- scores
-    f32x4 acc[4];
+  // ---- quantized blocks through the LDS ring
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < S - 1; ++t)
+    if (t < nI) issue(t);
+  for (int t = 0; t < nI; ++t) {
+    // wait for block t: only this wave's loads of blocks t+1 .. t+S-2 may remain
+    int younger = 0;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][c], qop[c], acc[kb], 0, 0, 0);
-    }
-    float cs = a.tau_log2e, vsc = 1.0f;
-    if (prec == TM_INT8) {
-      cs *= a.ks8[kblk];
-      vsc = a.vs8[kblk];
-    } else if (prec == TM_INT4) {
-      cs *= a.ks4[kblk];
-      vsc = a.vs4[kblk];
-    }
-    float s[4][4];
-    const bool tailblk = j * kBlock + kBlock > L;
+    for (int u = 1; u <= S - 2; ++u)
+      if (t + u < nI) younger += loads_of(is4(jof(e0 + t + u)));
+    wait_vm(younger);
+    lds_barrier();   // block t landed for every wave; block t-1's slot is free
+    if (t + S - 1 < nI) issue(t + S - 1);
+    const float cs = a.tau_log2e * cs_n, sv = sv_n;
+    if (t + 1 < nI) scales(t + 1, cs_n, sv_n);
+
+    const int j = jof(e0 + t);
+    const uint8_t* sl0 = lds + (t & (S - 1)) * SLOT;
+    f16x8 kop[NC];
+    f16x4 va[ND];
+    if (!is4(j)) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = acc[kb][i] * cs;
-        if (tailblk && j * kBlock + dsigma(kb, 4 * g + i) >= L) x = -INFINITY;
-        s[kb][i] = x;
+      for (int c2 = 0; c2 < NC / 2; ++c2) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(sl0 + k8off[c2]);
+        kop[2 * c2] = fix_i8(widen_i8x4(raw[0]), widen_i8x4(raw[1]));
+        kop[2 * c2 + 1] = fix_i8(widen_i8x4(raw[2]), widen_i8x4(raw[3]));
       }
-    float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-    m_run = mn;
-    float ps = 0.0f;
-    f16x8 pb[2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][i] - mn);
-        ps += p;
-        pb[kb >> 1][4 * (kb & 1) + i] = static_cast<_Float16>(p);
+      for (int db = 0; db < ND; ++db) {
+        const uint32_t raw = *reinterpret_cast<const uint32_t*>(sl0 + v8off + db * 1024);
+        const u32x2 h = widen_i8x4(raw);
+        f16x4 v;
+        __builtin_memcpy(&v, &h, 8);
+        const f16x4 off = {1152, 1152, 1152, 1152};
+        va[db] = v - off;
       }
-    l_run = l_run * alpha + ps;
+    } else {
+      if constexpr (D == 128) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(sl0 + k4off);
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db][0], pb[0], t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db][1], pb[1], t, 0, 0, 0);
-      oacc[db] = oacc[db] * alpha + t * vsc;
+        for (int e2 = 0; e2 < 4; ++e2) kop[e2] = widen_i4x8(raw[e2]);
+      } else {
+        const u32x2 raw = *reinterpret_cast<const u32x2*>(sl0 + k4off);
+        kop[0] = widen_i4x8(raw[0]);
+        kop[1] = widen_i4x8(raw[1]);
+      }
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const uint32_t raw = *reinterpret_cast<const uint16_t*>(sl0 + v4off + db * 512);
+        const f16x8 v8 = widen_i4x8(raw);
+        va[db] = f16x4{v8[0], v8[1], v8[2], v8[3]};
+      }
     }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[c], qop[c], acc, 0, 0, 0);
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = acc[i] * cs;
+    if (j * kBlock + kBlock > L) {   // partial last block (no FP16 window)
+      const int kbase = j * kBlock + 16 * w + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kbase + i >= L) s[i] = -INFINITY;
+    }
+    softmax_pv(s, va, sv);
   }
 
-  // ---- merge the 4 waves, write the chunk's partial (m, l, O) per query head
-  __shared__ float sm[4][16], sl[4][16];
-  __shared__ float so[4][16][D + 1];
+  // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy, from global memory
+  for (int e = eF; e < e1; ++e) {
+    const int j = dl.block(e);
+    const size_t kblk = kvb0 + j;
+    const int key = j * kBlock + 16 * w + l16;   // K row of this lane (MFMA row l16)
+    f16x8 kop[NC];
+    {
+      const uint16_t* src = a.k16 + (static_cast<size_t>(tok0 + (key < L ? key : 0)) * a.hkv + kv) * D + DG * g;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4 raw = key < L ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0, 0, 0, 0};
+        kop[c] = to_f16x8<BF16>(raw);
+      }
+    }
+    f16x4 va[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int d = db * 16 + l16;
+      const u32x2 raw = *reinterpret_cast<const u32x2*>(a.vt16 + (kblk * D + d) * kBlock + 16 * w + 4 * g);
+      __builtin_memcpy(&va[db], &raw, 8);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[c], qop[c], acc, 0, 0, 0);
+    float s[4];
+    const int kbase = j * kBlock + 16 * w + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = kbase + i < L ? acc[i] * a.tau_log2e : -INFINITY;
+    softmax_pv(s, va, 1.0f);
+  }
+
+  // ---- merge the 4 waves (reusing the ring), write the split's (m, l, O) per query head
+  __syncthreads();
+  float* sm = reinterpret_cast<float*>(lds);            // [4][16]
+  float* sl = sm + 64;                                  // [4][16]
+  float* so = sl + 64;                                  // [4][16][D + 1]
   float lt = l_run + __shfl_xor(l_run, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
   if (g == 0) {
-    sm[w][l16] = m_run;
-    sl[w][l16] = lt;
+    sm[w * 16 + l16] = m_run;
+    sl[w * 16 + l16] = lt;
   }
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) so[w][l16][db * 16 + 4 * g + i] = oacc[db][i];
+    for (int i = 0; i < 4; ++i) so[(w * 16 + l16) * (D + 1) + db * 16 + 4 * g + i] = oacc[db][i];
   __syncthreads();
   for (int x = tid; x < grp * D; x += 256) {
     const int qh = x / D, dv = x % D;
-    float M = fmaxf(fmaxf(sm[0][qh], sm[1][qh]), fmaxf(sm[2][qh], sm[3][qh]));
+    float M = kNegBig;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm[ww * 16 + qh]);
     float lsum = 0.0f, ov = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float f = __builtin_amdgcn_exp2f(sm[ww][qh] - M);
-      lsum += sl[ww][qh] * f;
-      ov += so[ww][qh][dv] * f;
+      const float f = __builtin_amdgcn_exp2f(sm[ww * 16 + qh] - M);
+      lsum += sl[ww * 16 + qh] * f;
+      ov += so[(ww * 16 + qh) * (D + 1) + dv] * f;
     }
     float* dst = a.ws + ((static_cast<size_t>(b) * a.hq + kv * grp + qh) * a.nsplit + chunk) * (D + 2);
     dst[2 + dv] = ov;

@@ -97,43 +97,12 @@ __device__ __forceinline__ int max4i(int v) {
   return max(static_cast<int>(r[0]), static_cast<int>(r[1]));
 }
 
-// s_waitcnt vmcnt(n) with the other counters left alone (n <= 15).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-  }
-}
-
-// Scalar (constant address space) load of a uniform float: counted by
-// lgkmcnt, so vector-memory counts of the tile copies stay exact.
-__device__ __forceinline__ float sload(const float* p, size_t i) {
-  typedef const __attribute__((address_space(4))) float cfloat;
-  return ((cfloat*)(p))[i];
-}
-
 __device__ __forceinline__ uint32_t remap_block(uint32_t b, uint32_t n) {
   constexpr uint32_t kXcd = 8, kGroup = 4, kChunk = kXcd * kGroup;
   const uint32_t full = (n / kChunk) * kChunk;
   if (b >= full) return b;
   const uint32_t c = b / kChunk, r = b % kChunk;
   return c * kChunk + (r % kXcd) * kGroup + r / kXcd;
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                           0x00020000);
 }
 
 // Per-lane layout of a direct-to-LDS tile copy: a region of ROWS rows x NCH
@@ -164,9 +133,7 @@ struct TileCopy {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       if (NI < 4 && w >= NI) break;
-#if defined(__HIP_DEVICE_COMPILE__)   // (the host pass never runs this body)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (i * 4 + w) * 1024), 16, voff[i], soff, 0, 0);
-#endif
+      lds_dma16(rs, dst + (i * 4 + w) * 1024, voff[i], soff);
     }
   }
 };

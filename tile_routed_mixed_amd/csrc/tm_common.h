@@ -96,6 +96,61 @@ __device__ inline SeqOfBlock find_block_seq(const int32_t* __restrict__ cu, int 
 }
 
 // Block start of sequence `seq` (sum of ceil(len/64) over earlier sequences).
+// s_waitcnt vmcnt(n) with the other counters left alone (n <= 15).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// 16-byte buffer load of each lane straight into LDS: lane L's bytes land at
+// dst + 16 L (dst is wave-uniform); the source is rs at voff (per lane) + soff.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* dst, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)   // (the host pass never runs device bodies)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst), 16, voff, soff, 0, 0);
+#endif
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for outstanding global or LDS-DMA loads (callers wait for the
+// loads they need with wait_vm first), so deeper load pipelines survive it.
+// (The barrier is written as inline asm because the compiler puts a full
+// s_waitcnt in front of every s_barrier it emits on this target.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Scalar (constant address space) load of a uniform float: counted by
+// lgkmcnt, so the vector-memory counts of tile copies stay exact.
+__device__ __forceinline__ float sload(const float* p, size_t i) {
+  typedef const __attribute__((address_space(4))) float cfloat;
+  return ((cfloat*)(p))[i];
+}
+
 __device__ inline int seq_blk_start(const int32_t* __restrict__ cu, int seq) {
   const int lane = threadIdx.x & 63;
   int acc = 0;
