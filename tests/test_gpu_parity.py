@@ -248,3 +248,32 @@ def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, dtype="f16"):
 def test_decode_small(seqlens, dpol, d, dtype):
     o, O = _decode_case(seqlens, dpol, d=d, dtype=dtype)
     compare(o, O, what=f"decode {seqlens} {dtype}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_deterministic_long_splits(d):
+    """Splits that walk dozens of mixed INT4/INT8 blocks through the LDS ring
+    (the pipeline's wait counts decide correctness there): bitwise identical
+    over repeated calls, and within the gate against the oracle."""
+    import torch
+    import tile_routed_mixed_amd as T
+    seqlens = [12000, 9000]
+    dpol = dict(b8=[40, 60], b4=[150, 140], sink=1, tail=128)
+    w = W.small("decode16x32k", seqlens, hq=8, hkv=2, d=d, dtype="f16")
+    q, k, v = W.make_qkv(w)
+    dq = W.make_decode_query(w)
+    say(f"[gpu] decode determinism {seqlens} d={d} {dpol}")
+    p = T.DecodePipeline(w.seqlens, 8, 2, d, dpol, dtype="f16")
+    p.upload(dq[0], k[0], v[0])
+    p.build_cache()
+    outs = []
+    for _ in range(3):
+        o = p.decode()
+        torch.cuda.synchronize()
+        outs.append(o.cpu().numpy().copy())
+    assert all(np.array_equal(outs[0], x) for x in outs[1:])
+    kq = OQ.quantize(k[1], w.seqlens)
+    vq = OQ.quantize(v[1], w.seqlens, layout="cols")
+    O = OA.decode(w.seqlens, 8, 2, d, dq[1].astype(np.float64), kq, vq, k[1].astype(np.float64),
+                  v[1].astype(np.float64), dpol)
+    compare(outs[0], O, what=f"decode determinism d={d}")

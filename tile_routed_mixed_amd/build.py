@@ -31,6 +31,9 @@ def hipcc() -> str:
 def flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in ordinary VGPRs: the kernels rescale them
+            # with VALU ops, which would otherwise copy them out of AGPRs
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", os.path.join(ROOT, "include")]
 
 

@@ -8,61 +8,25 @@
 // rest is quantized, and dequantization is fused with the attention math.
 // [TileMix] abstract: grouped-query attention and INT8 K/V caches.
 //
-// The step is bound by HBM bytes (each cached code is read once per step), so
-// the kernel streams blocks straight from global memory into MFMA operand
-// registers without LDS.  Work: one workgroup of 4 waves per
-// (sequence, KV head, chunk of executed cache blocks); each wave owns whole
-// 64-token blocks.  The GQA query heads of the KV head are the (up to 16)
-// columns of v_mfma_f32_16x16x32_f16:
-//   S^T = Kcodes Q^T   (codes widened exactly to fp16, per-block scale applied
-//                       to the fp32 scores),
-//   O^T += sv * (Vcodes^T P^T)   (V codes stored transposed per block).
-// INT8 codes widen with the exponent trick: byte u = c ^ 0x80 placed under
-// the fp16 exponent of 1024 gives 1024 + u exactly, and one packed subtract of
-// 1152 returns c.  INT4 nibbles use 1024 + (n ^ 8) - 1032.
-// A second kernel merges the chunks' (max, sum, O) by log-sum-exp.
+// The step is bound by HBM bytes (every cached code is read once per step).
+// One workgroup of 4 waves walks a split of one (sequence, KV head)'s cache
+// blocks; the blocks stream global -> LDS through a 4-deep ring of direct
+// (buffer-to-LDS) loads, so three blocks are in flight while one is used, and
+// each wave scores 16 keys of the current block against the (up to 16) GQA
+// query heads, which are the columns of 16x16 fp16 MFMAs:
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_f16),   O^T += V^T P^T (16x16x16).
+// Codes enter the MFMAs as fp16 subnormals: the byte b = c + 128 (INT8) or
+// the nibble n = c + 8 (INT4) placed in the low bits of a zero-exponent fp16
+// is exactly b * 2^-24, so two perms (or a mask) per pair of codes build an
+// operand, with no arithmetic.  The offsets come back out exactly where they
+// are cheap: for scores, 2^24 S' - off * sum(q) in the FMA that scales them;
+// for outputs, one extra MFMA per block accumulates off * 2^-24 * sum(p) per
+// head, subtracted once at the end.  MFMA products and sums of these values
+// are exact fp32 (no flush of fp16 subnormals on this path).
+// A second kernel merges the splits' (max, sum, O) by log-sum-exp.
 #include "tm_kernels.h"
 
 namespace tmx {
-
-
-// Key row of block kb / MFMA row m such that lane group g of the PV product
-// sees keys 16g .. 16g+15 (8 per 32-key chunk).
-__device__ __forceinline__ int dsigma(int kb, int m) {
-  return 16 * (m >> 2) + 8 * (kb >> 1) + 4 * (kb & 1) + (m & 3);
-}
-
-__device__ __forceinline__ u32x2 widen_i8x4(uint32_t c) {
-  const uint32_t t = c ^ 0x80808080u;
-  u32x2 r;
-  r[0] = __builtin_amdgcn_perm(0x64646464u, t, 0x07010600u);   // bytes: t0, 64, t1, 64
-  r[1] = __builtin_amdgcn_perm(0x64646464u, t, 0x07030602u);   // bytes: t2, 64, t3, 64
-  return r;
-}
-
-__device__ __forceinline__ f16x8 fix_i8(u32x2 a, u32x2 b) {
-  f16x8 v;
-  u32x4 raw = {a[0], a[1], b[0], b[1]};
-  __builtin_memcpy(&v, &raw, 16);
-  const f16x8 off = {1152, 1152, 1152, 1152, 1152, 1152, 1152, 1152};
-  return v - off;
-}
-
-// 8 nibbles (elements 2t low / 2t+1 high of byte t) -> 8 fp16 values in order.
-__device__ __forceinline__ f16x8 widen_i4x8(uint32_t c) {
-  const uint32_t t = c ^ 0x88888888u;
-  const uint32_t lo = t & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
-  const uint32_t hi = (t >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
-  u32x4 raw;
-  raw[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;
-  raw[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
-  raw[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
-  raw[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
-  f16x8 v;
-  __builtin_memcpy(&v, &raw, 16);
-  const f16x8 off = {1032, 1032, 1032, 1032, 1032, 1032, 1032, 1032};
-  return v - off;
-}
 
 // Eight 16-bit values (fp16, or bf16 widened to fp16: exact for magnitudes in
 // [2^-14, 65504], the range of normal fp16 numbers) as an fp16 MFMA operand.
@@ -81,6 +45,36 @@ __device__ __forceinline__ f16x8 to_f16x8(u32x4 raw) {
   return v;
 }
 
+// Four INT8 codes (one dword) -> four fp16 (c + 128) * 2^-24, in order.
+__device__ __forceinline__ u32x2 sub_i8x4(uint32_t c) {
+  const uint32_t t = c ^ 0x80808080u;
+  return u32x2{__builtin_amdgcn_perm(t, t, 0x0c010c00u), __builtin_amdgcn_perm(t, t, 0x0c030c02u)};
+}
+
+// Eight INT4 codes (one dword, element 2t in the low nibble of byte t) ->
+// eight fp16 (c + 8) * 2^-24, in order.
+__device__ __forceinline__ u32x4 sub_i4x8(uint32_t c) {
+  const uint32_t t = c ^ 0x88888888u;
+  const uint32_t lo = t & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const uint32_t hi = (t >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  return u32x4{__builtin_amdgcn_perm(hi, lo, 0x0c040c00u), __builtin_amdgcn_perm(hi, lo, 0x0c050c01u),
+               __builtin_amdgcn_perm(hi, lo, 0x0c060c02u), __builtin_amdgcn_perm(hi, lo, 0x0c070c03u)};
+}
+
+// Four INT4 codes (16 bits) -> four fp16 (c + 8) * 2^-24, in order.
+__device__ __forceinline__ u32x2 sub_i4x4(uint32_t x) {
+  const uint32_t y = x >> 8;
+  const uint32_t t0 = x | (x << 12), t1 = y | (y << 12);   // nibbles 0, 1 (2, 3) at bits 0 and 16
+  return u32x2{(t0 & 0x000F000Fu) ^ 0x00080008u, (t1 & 0x000F000Fu) ^ 0x00080008u};
+}
+
+template <typename T, typename S>
+__device__ __forceinline__ T as(const S& s) {
+  T t;
+  __builtin_memcpy(&t, &s, sizeof(T));
+  return t;
+}
+
 // Cache blocks of one (sequence, KV head), in the order a split walks them:
 // the sink block (when it lies outside the band), then blocks jstart .. nb-1
 // in ascending order: the INT4 band, the INT8 band, then the FP16 window.
@@ -88,11 +82,6 @@ struct DecodeList {
   int nb, jstart, jf, b8, sink, sink_extra, n_ex;
   __device__ __forceinline__ int block(int e) const {
     return sink_extra ? (e == 0 ? 0 : jstart + e - 1) : jstart + e;
-  }
-  __device__ __forceinline__ int prec(int j) const {
-    if (j >= jf) return TM_FP16;
-    if ((sink && j == 0) || nb - 1 - j < b8) return TM_INT8;
-    return TM_INT4;
   }
   // HBM cost of entries [0, e) in units of an INT4 block (INT8 2, FP16 4)
   __device__ __forceinline__ int64_t weight(int e) const {
@@ -129,19 +118,24 @@ struct DecodeList {
   }
 };
 
-// Swizzle of 16-byte chunk columns in the LDS copies of a block: K rows of
-// NCH chunks (rows read 16 at a time by one lane group) and V^T rows (16
-// channel rows read together at one key offset).
+// Swizzle of the 16-byte chunk columns of a block's rows in LDS.  K rows (NCH
+// chunks, 16/NCH rows per 256 bytes of banks) are read 16 at a time at one
+// logical chunk, so the chunk moves with the row's position in the bank
+// cycle; V^T rows are read 16 at a time at one key offset.
 template <int NCH>
-__device__ __forceinline__ int kswz(int row) { return row & (NCH - 1) & 7; }
+__device__ __forceinline__ int kswz(int row) {
+  return NCH >= 16 ? row & 15 : (row >> (NCH == 8 ? 1 : NCH == 4 ? 2 : 3)) & (NCH - 1);
+}
 template <int NCH>
 __device__ __forceinline__ int vswz(int row) { return NCH >= 4 ? (row >> 2) & 3 : (row >> 3) & 1; }
 
 // Direct-to-LDS copy of a contiguous region of ROWS rows of NCH chunks with
-// the chunk columns of row r permuted by SW(r) (see TileCopy in the prefill).
-template <int ROWS, int NCH, int SWK>
+// the chunk columns of row r permuted (load n fills LDS bytes
+// [n*1024, n*1024+1024), lane L lands at n*1024 + 16L and fetches the chunk
+// that belongs there); wave w issues loads n = 4i + w.
+template <int ROWS, int NCH, bool VT>
 struct BlockCopy {
-  static constexpr int NI = ROWS * NCH / 64;            // 1 KiB loads per region
+  static constexpr int NI = ROWS * NCH / 64;
   static constexpr int PER = (NI + 3) / 4;
   uint32_t voff[PER];
   __device__ __forceinline__ void init(int w, int lane) {
@@ -149,15 +143,17 @@ struct BlockCopy {
     for (int i = 0; i < PER; ++i) {
       const int off = (i * 4 + w) * 1024 + lane * 16;
       const int r = off / (NCH * 16), slot = (off / 16) % NCH;
-      const int sw = SWK == 0 ? kswz<NCH>(r) : vswz<NCH>(r);
+      const int sw = VT ? vswz<NCH>(r) : kswz<NCH>(r);
       voff[i] = static_cast<uint32_t>(r * NCH * 16 + ((slot ^ sw) << 4));
     }
   }
-  __device__ __forceinline__ static int count(int w) { return w < NI % 4 || NI % 4 == 0 ? PER : PER - 1; }
+  __device__ __forceinline__ static constexpr int count(int w) {
+    return NI % 4 == 0 ? PER : (w < NI % 4 ? PER : PER - 1);
+  }
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t soff, uint8_t* dst, int w) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if (i * 4 + w < NI) lds_dma16(rs, dst + (i * 4 + w) * 1024, voff[i], soff);
+      if (NI % 4 == 0 || i * 4 + w < NI) lds_dma16(rs, dst + (i * 4 + w) * 1024, voff[i], soff);
   }
 };
 
@@ -166,9 +162,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;          // k-chunks of the QK MFMA (lane group g owns channels DG*g ..)
   constexpr int ND = D / 16;          // output channel blocks
   constexpr int DG = D / 4;
-  constexpr int SLOT = 128 * D;       // bytes of one INT8 block: K rows then V^T rows
+  constexpr int SLOT = 128 * D;       // bytes of one INT8 block: K rows, then V^T rows
   constexpr int S = 4;                // ring depth: S - 1 blocks stream in while one is used
   constexpr int NCK8 = D / 16, NCK4 = D / 32;   // 16-byte chunks per K row
+  constexpr float kTwo24 = 16777216.0f;
   __shared__ __align__(1024) uint8_t lds[S * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -183,17 +180,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   dl.nb = (L + kBlock - 1) / kBlock;
   dl.b8 = __builtin_amdgcn_readfirstlane(a.b8[kv]);
   dl.sink = a.sink;
-  dl.jf = a.tail > 0 ? max(0, (L - a.tail) / kBlock) : dl.nb;            // first FP16 block
-  dl.jstart = min(max(0, dl.nb - __builtin_amdgcn_readfirstlane(a.b4[kv])), dl.jf);                     // first block with delta < b4
+  dl.jf = a.tail > 0 ? max(0, (L - a.tail) / kBlock) : dl.nb;                                    // first FP16 block
+  dl.jstart = min(max(0, dl.nb - __builtin_amdgcn_readfirstlane(a.b4[kv])), dl.jf);             // delta < b4
   dl.sink_extra = (a.sink && dl.jstart > 0) ? 1 : 0;
   dl.n_ex = (dl.nb - dl.jstart) + dl.sink_extra;
   const int e0 = dl.split(chunk, a.nsplit), e1 = dl.split(chunk + 1, a.nsplit);
   const int eF = max(e0, min(e1, dl.first_fp16()));
-  const int nI = eF - e0;                                                 // quantized blocks of this split
+  const int nI = eF - e0;                                                                        // quantized blocks
   const size_t kvb0 = static_cast<size_t>(kv) * a.nblk + blk0;
 
-  // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group)
+  // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group);
+  // qsum: the head's sum of q over all channels (for the code offsets)
   f16x8 qop[NC];
+  float qsum = 0.0f;
   {
     const bool ok = l16 < grp;
     const uint16_t* qs = a.q + (static_cast<size_t>(b) * a.hq + kv * grp + (ok ? l16 : 0)) * D + DG * g;
@@ -201,7 +200,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int c = 0; c < NC; ++c) {
       u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(qs + 8 * c) : u32x4{0, 0, 0, 0};
       qop[c] = to_f16x8<BF16>(raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qsum += static_cast<float>(qop[c][e]);
     }
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(qsum), __float_as_uint(qsum), false, false);
+    qsum = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(qsum), __float_as_uint(qsum), false, false);
+    qsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
   }
 
   // buffer resources over this (sequence, KV head)'s blocks
@@ -210,24 +215,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(a.v8 + kvb0 * (kBlock * D), nbs * (kBlock * D));
   const __amdgpu_buffer_rsrc_t rk4 = make_rsrc(a.k4 + kvb0 * (kBlock * D / 2), nbs * (kBlock * D / 2));
   const __amdgpu_buffer_rsrc_t rv4 = make_rsrc(a.v4 + kvb0 * (kBlock * D / 2), nbs * (kBlock * D / 2));
-  BlockCopy<kBlock, NCK8, 0> ck8;
-  BlockCopy<D, 4, 1> cv8;
-  BlockCopy<kBlock, NCK4, 0> ck4;
-  BlockCopy<D, 2, 1> cv4;
+  BlockCopy<kBlock, NCK8, false> ck8;
+  BlockCopy<D, 4, true> cv8;
+  BlockCopy<kBlock, NCK4, false> ck4;
+  BlockCopy<D, 2, true> cv4;
   ck8.init(w, lane);
   cv8.init(w, lane);
   ck4.init(w, lane);
   cv4.init(w, lane);
-  // list entry e -> cache block j, and whether it is an INT4 block (entries
-  // before eF are INT8 or INT4; see DecodeList)
+  // Every block costs each wave the same number of vector-memory
+  // instructions: INT4 blocks pad with re-reads of their first KiB into the
+  // slot space INT4 leaves unused, so the ring's waits are constants.
+  const int n8 = ck8.count(w) + cv8.count(w);
+  const int npad = n8 - (ck4.count(w) + cv4.count(w));
+
+  // list entry e -> cache block j; quantized entries are INT4 or INT8
   const int eS = dl.sink_extra;
   const int j4hi = min(dl.nb - dl.b8, dl.jf);
   auto jof = [&](int e) { return e < eS ? 0 : dl.jstart + (e - eS); };
   auto is4 = [&](int j) { return j >= dl.jstart && j < j4hi && !(dl.sink && j == 0); };
-  auto loads_of = [&](bool four) {   // vector-memory instructions this wave issues for one block
-    return four ? decltype(ck4)::count(w) + decltype(cv4)::count(w)
-                : decltype(ck8)::count(w) + decltype(cv8)::count(w);
-  };
   auto issue = [&](int t) {
     const int j = jof(e0 + t);
     uint8_t* dst = lds + (t & (S - 1)) * SLOT;
@@ -237,11 +243,27 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     } else {
       ck4.issue(rk4, j * (kBlock * D / 2), dst, w);
       cv4.issue(rv4, j * (kBlock * D / 2), dst + kBlock * D, w);
+      // (distinct sources and targets, so the compiler cannot fold them:
+      // the ring's wait counts rely on every one being issued)
+      for (int k = 0; k < npad; ++k)
+        lds_dma16(rk4, dst + (k == 0 ? kBlock * D / 2 : kBlock * D + kBlock * D / 2) + (w % (D / 32)) * 1024,
+                  k * 1024 + lane * 16, j * (kBlock * D / 2));
     }
   };
+  // scale factors of a quantized block (scalar loads, fetched one block ahead)
+  const float* const ks8 = pin_sgpr(a.ks8 + kvb0);
+  const float* const vs8 = pin_sgpr(a.vs8 + kvb0);
+  const float* const ks4 = pin_sgpr(a.ks4 + kvb0);
+  const float* const vs4 = pin_sgpr(a.vs4 + kvb0);
+  auto scales = [&](int t, float& sk, float& sv) {
+    const int j = jof(e0 + t);
+    const bool four = is4(j);
+    sk = sload(four ? ks4 : ks8, j);
+    sv = sload(four ? vs4 : vs8, j);
+  };
 
-  // per-lane LDS read offsets inside a ring slot: K row 16w + l16 (chunks of
-  // lane group g), V^T rows l16 + 16 db at keys 16w + 4g (db adds a constant)
+  // per-lane LDS read offsets inside a ring slot: K row 16w + l16 (the chunks
+  // of lane group g), V^T rows l16 + 16 db at keys 16w + 4g (db adds a constant)
   const int krow = 16 * w + l16;
   int k8off[NC / 2 > 0 ? NC / 2 : 1];
 #pragma unroll
@@ -252,13 +274,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int v4off = kBlock * D + l16 * 32 + (((w >> 1) ^ vswz<2>(l16)) << 4) + 8 * (w & 1) + 2 * g;
 
   float m_run = kNegBig, l_run = 0.0f;   // per lane: head l16, keys of lane group g
-  f32x4 oacc[ND];
+  f32x4 oacc[ND], ocorr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One block's keys 16w .. 16w+15 given S^T scores (already scaled, log2
-  // units) in lane (g, head) for keys 4g + i, and the V^T operands.
-  auto softmax_pv = [&](float (&s)[4], const f16x4 (&va)[ND], float sv) {
+  // One block's keys 16w .. 16w+15: s holds the lane's 4 scores (log2 units)
+  // of head l16 for keys 4g + i.  Returns the fp16 P^T operand (p * sv).
+  auto softmax = [&](float (&s)[4], float sv) {
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     {   // max over the 4 lane groups of the head (lanes l, l^16, l^32, l^48)
       const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -274,6 +296,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;
+      ocorr *= alpha;
 #pragma unroll
       for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
     }
@@ -284,93 +307,87 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       l_run += p;
       pb[i] = static_cast<_Float16>(p * sv);
     }
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pb, oacc[db], 0, 0, 0);
+    return pb;
   };
 
-  // scale factors of a quantized block: cs = tau log2e sk, sv (scalar loads,
-  // fetched one block ahead)
-  auto scales = [&](int t, float& cs, float& sv) {
-    const int j = jof(e0 + t);
-    const size_t kblk = kvb0 + j;
-    if (!is4(j)) {
-      cs = sload(a.ks8, kblk);
-      sv = sload(a.vs8, kblk);
-    } else {
-      cs = sload(a.ks4, kblk);
-      sv = sload(a.vs4, kblk);
-    }
-  };
-  float cs_n = 0.0f, sv_n = 0.0f;
-  if (nI > 0) scales(0, cs_n, sv_n);
+  float sk_n = 0.0f, sv_n = 0.0f;
+  if (nI > 0) scales(0, sk_n, sv_n);
 
   // ---- quantized blocks through the LDS ring
 #pragma unroll
   for (int t = 0; t < S - 1; ++t)
     if (t < nI) issue(t);
   for (int t = 0; t < nI; ++t) {
-    // wait for block t: only this wave's loads of blocks t+1 .. t+S-2 may remain
-    int younger = 0;
-#pragma unroll
-    for (int u = 1; u <= S - 2; ++u)
-      if (t + u < nI) younger += loads_of(is4(jof(e0 + t + u)));
-    wait_vm(younger);
-    lds_barrier();   // block t landed for every wave; block t-1's slot is free
+    // wait for block t (loads complete in order; each later block in flight
+    // holds n8 loads of this wave), then a barrier so every wave's share landed
+    // and block t-1's slot (the next issue's target) is free
+    const int ahead = min(S - 2, nI - 1 - t);
+    if (ahead >= 2) wait_vm(2 * n8);
+    else if (ahead == 1) wait_vm(n8);
+    else wait_vm(0);
+    lds_barrier();
     if (t + S - 1 < nI) issue(t + S - 1);
-    const float cs = a.tau_log2e * cs_n, sv = sv_n;
-    if (t + 1 < nI) scales(t + 1, cs_n, sv_n);
+    const float sk = sk_n, sv = sv_n;
+    if (t + 1 < nI) scales(t + 1, sk_n, sv_n);
 
     const int j = jof(e0 + t);
+    const bool four = is4(j);
     const uint8_t* sl0 = lds + (t & (S - 1)) * SLOT;
     f16x8 kop[NC];
     f16x4 va[ND];
-    if (!is4(j)) {
+    if (!four) {
 #pragma unroll
       for (int c2 = 0; c2 < NC / 2; ++c2) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(sl0 + k8off[c2]);
-        kop[2 * c2] = fix_i8(widen_i8x4(raw[0]), widen_i8x4(raw[1]));
-        kop[2 * c2 + 1] = fix_i8(widen_i8x4(raw[2]), widen_i8x4(raw[3]));
+        kop[2 * c2] = as<f16x8>(u32x4{sub_i8x4(raw[0])[0], sub_i8x4(raw[0])[1], sub_i8x4(raw[1])[0],
+                                      sub_i8x4(raw[1])[1]});
+        kop[2 * c2 + 1] = as<f16x8>(u32x4{sub_i8x4(raw[2])[0], sub_i8x4(raw[2])[1], sub_i8x4(raw[3])[0],
+                                          sub_i8x4(raw[3])[1]});
       }
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const uint32_t raw = *reinterpret_cast<const uint32_t*>(sl0 + v8off + db * 1024);
-        const u32x2 h = widen_i8x4(raw);
-        f16x4 v;
-        __builtin_memcpy(&v, &h, 8);
-        const f16x4 off = {1152, 1152, 1152, 1152};
-        va[db] = v - off;
-      }
+      for (int db = 0; db < ND; ++db)
+        va[db] = as<f16x4>(sub_i8x4(*reinterpret_cast<const uint32_t*>(sl0 + v8off + db * 1024)));
     } else {
       if constexpr (D == 128) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(sl0 + k4off);
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) kop[e2] = widen_i4x8(raw[e2]);
+        for (int e2 = 0; e2 < 4; ++e2) kop[e2] = as<f16x8>(sub_i4x8(raw[e2]));
       } else {
         const u32x2 raw = *reinterpret_cast<const u32x2*>(sl0 + k4off);
-        kop[0] = widen_i4x8(raw[0]);
-        kop[1] = widen_i4x8(raw[1]);
+        kop[0] = as<f16x8>(sub_i4x8(raw[0]));
+        kop[1] = as<f16x8>(sub_i4x8(raw[1]));
       }
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const uint32_t raw = *reinterpret_cast<const uint16_t*>(sl0 + v4off + db * 512);
-        const f16x8 v8 = widen_i4x8(raw);
-        va[db] = f16x4{v8[0], v8[1], v8[2], v8[3]};
-      }
+      for (int db = 0; db < ND; ++db)
+        va[db] = as<f16x4>(sub_i4x4(*reinterpret_cast<const uint16_t*>(sl0 + v4off + db * 512)));
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[c], qop[c], acc, 0, 0, 0);
+    // score = tau log2e sk (2^24 acc - off sum(q)), off = 128 (INT8) or 8 (INT4)
+    const float cs = a.tau_log2e * sk;
+    const float m1 = cs * kTwo24, m0 = -(four ? 8.0f : 128.0f) * qsum * cs;
     float s[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = acc[i] * cs;
+    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(acc[i], m1, m0);
     if (j * kBlock + kBlock > L) {   // partial last block (no FP16 window)
       const int kbase = j * kBlock + 16 * w + 4 * g;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (kbase + i >= L) s[i] = -INFINITY;
     }
-    softmax_pv(s, va, sv);
+    const f16x4 pb = softmax(s, sv);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pb, oacc[db], 0, 0, 0);
+    // every row of this A operand is off * 2^-24: accumulates the offsets' share
+    const f16x4 offa = as<f16x4>(u32x2{four ? 0x00080008u : 0x00800080u, four ? 0x00080008u : 0x00800080u});
+    ocorr = __builtin_amdgcn_mfma_f32_16x16x16f16(offa, pb, ocorr, 0, 0, 0);
   }
+  // back to value units: O = 2^24 (O' - offsets)
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oacc[db][i] = (oacc[db][i] - ocorr[i]) * kTwo24;
 
   // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy, from global memory
   for (int e = eF; e < e1; ++e) {
@@ -391,7 +408,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int db = 0; db < ND; ++db) {
       const int d = db * 16 + l16;
       const u32x2 raw = *reinterpret_cast<const u32x2*>(a.vt16 + (kblk * D + d) * kBlock + 16 * w + 4 * g);
-      __builtin_memcpy(&va[db], &raw, 8);
+      va[db] = as<f16x4>(raw);
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -400,7 +417,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int kbase = j * kBlock + 16 * w + 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = kbase + i < L ? acc[i] * a.tau_log2e : -INFINITY;
-    softmax_pv(s, va, 1.0f);
+    const f16x4 pb = softmax(s, 1.0f);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pb, oacc[db], 0, 0, 0);
   }
 
   // ---- merge the 4 waves (reusing the ring), write the split's (m, l, O) per query head
@@ -408,8 +427,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   float* sm = reinterpret_cast<float*>(lds);            // [4][16]
   float* sl = sm + 64;                                  // [4][16]
   float* so = sl + 64;                                  // [4][16][D + 1]
-  float lt = l_run + __shfl_xor(l_run, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  float lt = l_run;
+  {
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
+    lt = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
+    lt = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  }
   if (g == 0) {
     sm[w * 16 + l16] = m_run;
     sl[w * 16 + l16] = lt;

@@ -135,6 +135,15 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* dst, 
 #endif
 }
 
+// A uniform pointer pinned in scalar registers: the empty asm hides where it
+// came from, so the compiler keeps it instead of reloading it from the kernel
+// arguments (and waiting on that load) inside a loop.
+template <typename T>
+__device__ __forceinline__ T* pin_sgpr(T* p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
 // does not wait for outstanding global or LDS-DMA loads (callers wait for the
 // loads they need with wait_vm first), so deeper load pipelines survive it.
