@@ -199,8 +199,8 @@ def test_decode_validation_and_workspace(B):
     n = ctypes.c_size_t(0)
     assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(dp.c), None, 2, None,
                        ctypes.byref(n), None) == B.TM_OK
-    # 16 x 8 (sequence, KV head) pairs -> 4 splits (512 workgroups); ws = B * hq * splits * (d + 2) floats
-    assert n.value == 16 * 32 * 4 * 130 * 4
+    # 16 x 8 (sequence, KV head) pairs -> 16 splits (2048 waves); ws = B * hq * splits * (d + 2) floats
+    assert n.value == 16 * 32 * 16 * 130 * 4
     small = ctypes.c_size_t(n.value - 4)
     nb = s.nblk()
     kq, vq = _qt(B, 8, 0, nb, False), _qt(B, 8, 1, nb, True)

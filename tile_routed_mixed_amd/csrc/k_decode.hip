@@ -118,59 +118,40 @@ struct DecodeList {
   }
 };
 
-// Swizzle of the 16-byte chunk columns of a block's rows in LDS.  K rows (NCH
-// chunks, 16/NCH rows per 256 bytes of banks) are read 16 at a time at one
-// logical chunk, so the chunk moves with the row's position in the bank
-// cycle; V^T rows are read 16 at a time at one key offset.
-template <int NCH>
-__device__ __forceinline__ int kswz(int row) {
-  return NCH >= 16 ? row & 15 : (row >> (NCH == 8 ? 1 : NCH == 4 ? 2 : 3)) & (NCH - 1);
-}
-template <int NCH>
-__device__ __forceinline__ int vswz(int row) { return NCH >= 4 ? (row >> 2) & 3 : (row >> 3) & 1; }
+// Key that feeds MFMA row m of 16-key block kb (kb = 0..3 of a 64-key cache
+// block): lane group g of every block kb holds keys 16g + 4kb + i, so a lane
+// group owns keys 16g .. 16g+15 of the block, and for the 32-key chunk c2 of
+// the PV product it holds keys 16g + 8c2 .. 16g + 8c2 + 7, the B-operand slice
+// (chunk c2's k index e maps to key 16 (e / 8) + 8 c2 + e % 8).
+__device__ __forceinline__ int dsig(int kb, int m) { return 16 * (m >> 2) + 4 * kb + (m & 3); }
 
-// Direct-to-LDS copy of a contiguous region of ROWS rows of NCH chunks with
-// the chunk columns of row r permuted (load n fills LDS bytes
-// [n*1024, n*1024+1024), lane L lands at n*1024 + 16L and fetches the chunk
-// that belongs there); wave w issues loads n = 4i + w.
-template <int ROWS, int NCH, bool VT>
-struct BlockCopy {
-  static constexpr int NI = ROWS * NCH / 64;
-  static constexpr int PER = (NI + 3) / 4;
-  uint32_t voff[PER];
-  __device__ __forceinline__ void init(int w, int lane) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int off = (i * 4 + w) * 1024 + lane * 16;
-      const int r = off / (NCH * 16), slot = (off / 16) % NCH;
-      const int sw = VT ? vswz<NCH>(r) : kswz<NCH>(r);
-      voff[i] = static_cast<uint32_t>(r * NCH * 16 + ((slot ^ sw) << 4));
-    }
-  }
-  __device__ __forceinline__ static constexpr int count(int w) {
-    return NI % 4 == 0 ? PER : (w < NI % 4 ? PER : PER - 1);
-  }
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t soff, uint8_t* dst, int w) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (NI % 4 == 0 || i * 4 + w < NI) lds_dma16(rs, dst + (i * 4 + w) * 1024, voff[i], soff);
-  }
+// One unit of streamed codes in a lane's registers: one INT8 block, or two
+// consecutive INT4 blocks, which take the same bytes and the same load
+// instructions (so the loads never sit under a precision branch).
+//  K: 8 pieces of KW bytes.  INT8: piece 2 kb + h = channels DG g + (KW h) ..
+//     of key row dsig(kb, l16).  INT4: piece 4 bb + kb = the lane's DG/2
+//     bytes (DG channels) of key row dsig(kb, l16) of block bb.
+//  V: 2 ND pieces of 8 bytes.  INT8: piece 2 db + h = keys 16g + 8h .. +7 of
+//     V^T row 16 db + l16.  INT4: piece 2 db + bb = keys 16g .. 16g+15 of
+//     that row of block bb.
+template <int D>
+struct UnitRegs {
+  u32x4 k[8];
+  u32x2 v[D / 8];
+  float sk[2], sv[2];
 };
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;          // k-chunks of the QK MFMA (lane group g owns channels DG*g ..)
   constexpr int ND = D / 16;          // output channel blocks
   constexpr int DG = D / 4;
-  constexpr int SLOT = 128 * D;       // bytes of one INT8 block: K rows, then V^T rows
-  constexpr int S = 4;                // ring depth: S - 1 blocks stream in while one is used
-  constexpr int NCK8 = D / 16, NCK4 = D / 32;   // 16-byte chunks per K row
+  constexpr int KW = D / 8;           // bytes of one K piece (INT8: half a lane's row slice)
   constexpr float kTwo24 = 16777216.0f;
-  __shared__ __align__(1024) uint8_t lds[S * SLOT];
+  typedef UnitRegs<D> Regs;
 
-  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int chunk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int grp = a.hq / a.hkv;
 
   const int tok0 = a.cu[b];
@@ -184,9 +165,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   dl.jstart = min(max(0, dl.nb - __builtin_amdgcn_readfirstlane(a.b4[kv])), dl.jf);             // delta < b4
   dl.sink_extra = (a.sink && dl.jstart > 0) ? 1 : 0;
   dl.n_ex = (dl.nb - dl.jstart) + dl.sink_extra;
-  const int e0 = dl.split(chunk, a.nsplit), e1 = dl.split(chunk + 1, a.nsplit);
-  const int eF = max(e0, min(e1, dl.first_fp16()));
-  const int nI = eF - e0;                                                                        // quantized blocks
+  const int e0 = dl.split(split, a.nsplit), e1 = dl.split(split + 1, a.nsplit);
+  const int eF = max(e0, min(e1, dl.first_fp16()));                                             // quantized: [e0, eF)
   const size_t kvb0 = static_cast<size_t>(kv) * a.nblk + blk0;
 
   // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group);
@@ -209,79 +189,82 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     qsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
   }
 
-  // buffer resources over this (sequence, KV head)'s blocks
+  // buffer resources over this (sequence, KV head)'s blocks (a unit's second
+  // INT4 block may lie past the last block: such loads return zeros and the
+  // block is not computed)
   const uint32_t nbs = static_cast<uint32_t>(dl.nb);
   const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(a.k8 + kvb0 * (kBlock * D), nbs * (kBlock * D));
   const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(a.v8 + kvb0 * (kBlock * D), nbs * (kBlock * D));
   const __amdgpu_buffer_rsrc_t rk4 = make_rsrc(a.k4 + kvb0 * (kBlock * D / 2), nbs * (kBlock * D / 2));
   const __amdgpu_buffer_rsrc_t rv4 = make_rsrc(a.v4 + kvb0 * (kBlock * D / 2), nbs * (kBlock * D / 2));
-  BlockCopy<kBlock, NCK8, false> ck8;
-  BlockCopy<D, 4, true> cv8;
-  BlockCopy<kBlock, NCK4, false> ck4;
-  BlockCopy<D, 2, true> cv4;
-  ck8.init(w, lane);
-  cv8.init(w, lane);
-  ck4.init(w, lane);
-  cv4.init(w, lane);
-  // Every block costs each wave the same number of vector-memory
-  // instructions: INT4 blocks pad with re-reads of their first KiB into the
-  // slot space INT4 leaves unused, so the ring's waits are constants.
-  const int n8 = ck8.count(w) + cv8.count(w);
-  const int npad = n8 - (ck4.count(w) + cv4.count(w));
-
-  // list entry e -> cache block j; quantized entries are INT4 or INT8
-  const int eS = dl.sink_extra;
-  const int j4hi = min(dl.nb - dl.b8, dl.jf);
-  auto jof = [&](int e) { return e < eS ? 0 : dl.jstart + (e - eS); };
-  auto is4 = [&](int j) { return j >= dl.jstart && j < j4hi && !(dl.sink && j == 0); };
-  auto issue = [&](int t) {
-    const int j = jof(e0 + t);
-    uint8_t* dst = lds + (t & (S - 1)) * SLOT;
-    if (!is4(j)) {
-      ck8.issue(rk8, j * (kBlock * D), dst, w);
-      cv8.issue(rv8, j * (kBlock * D), dst + kBlock * D, w);
-    } else {
-      ck4.issue(rk4, j * (kBlock * D / 2), dst, w);
-      cv4.issue(rv4, j * (kBlock * D / 2), dst + kBlock * D, w);
-      // (distinct sources and targets, so the compiler cannot fold them:
-      // the ring's wait counts rely on every one being issued)
-      for (int k = 0; k < npad; ++k)
-        lds_dma16(rk4, dst + (k == 0 ? kBlock * D / 2 : kBlock * D + kBlock * D / 2) + (w % (D / 32)) * 1024,
-                  k * 1024 + lane * 16, j * (kBlock * D / 2));
-    }
-  };
-  // scale factors of a quantized block (scalar loads, fetched one block ahead)
   const float* const ks8 = pin_sgpr(a.ks8 + kvb0);
   const float* const vs8 = pin_sgpr(a.vs8 + kvb0);
   const float* const ks4 = pin_sgpr(a.ks4 + kvb0);
   const float* const vs4 = pin_sgpr(a.vs4 + kvb0);
-  auto scales = [&](int t, float& sk, float& sv) {
-    const int j = jof(e0 + t);
-    const bool four = is4(j);
-    sk = sload(four ? ks4 : ks8, j);
-    sv = sload(four ? vs4 : vs8, j);
+  const uint32_t kb8 = static_cast<uint32_t>(dsig(0, l16) * D + DG * g);
+  const uint32_t kb4 = static_cast<uint32_t>(dsig(0, l16) * (D / 2) + (DG / 2) * g);
+  const uint32_t vb8 = static_cast<uint32_t>(l16 * 64 + 16 * g);
+  const uint32_t vb4 = static_cast<uint32_t>(l16 * 32 + 8 * g);
+
+  // list entry e -> cache block j; quantized entries are INT4 or INT8, and a
+  // unit is one INT8 block or up to two consecutive INT4 blocks
+  const int eS = dl.sink_extra;
+  const int j4hi = min(dl.nb - dl.b8, dl.jf);
+  auto jof = [&](int e) { return e < eS ? 0 : dl.jstart + (e - eS); };
+  auto is4 = [&](int j) { return j >= dl.jstart && j < j4hi && !(dl.sink && j == 0); };
+
+  // start loading the unit at entry e (four: INT4 pair) into r
+  auto load = [&](int e, bool four, Regs& r) {
+    const int j = jof(e);
+    const __amdgpu_buffer_rsrc_t rk = four ? rk4 : rk8;
+    const __amdgpu_buffer_rsrc_t rv = four ? rv4 : rv8;
+    const uint32_t kbase = four ? kb4 : kb8, vbase = four ? vb4 : vb8;
+    const uint32_t j8 = static_cast<uint32_t>(j) * (kBlock * D), j4 = static_cast<uint32_t>(j) * (kBlock * D / 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t so = four ? j4 + (i >> 2) * (kBlock * D / 2) + dsig(i & 3, 0) * (D / 2)
+                               : j8 + dsig(i >> 1, 0) * D + (i & 1) * KW;
+      if constexpr (KW == 16) {
+        r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk, kbase, so, 0));
+      } else {
+        const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk, kbase, so, 0));
+        r.k[i] = u32x4{x[0], x[1], 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * ND; ++i) {
+      const uint32_t so = four ? j4 + (i & 1) * (kBlock * D / 2) + (i >> 1) * 512 : j8 + (i >> 1) * 1024 + (i & 1) * 8;
+      r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rv, vbase, so, 0));
+    }
+    const float* kp = four ? ks4 : ks8;
+    const float* vp = four ? vs4 : vs8;
+    r.sk[0] = sload(kp, j);
+    r.sv[0] = sload(vp, j);
+    r.sk[1] = four ? sload(ks4, j + 1 < dl.nb ? j + 1 : j) : 0.0f;
+    r.sv[1] = four ? sload(vs4, j + 1 < dl.nb ? j + 1 : j) : 0.0f;
   };
 
-  // per-lane LDS read offsets inside a ring slot: K row 16w + l16 (the chunks
-  // of lane group g), V^T rows l16 + 16 db at keys 16w + 4g (db adds a constant)
-  const int krow = 16 * w + l16;
-  int k8off[NC / 2 > 0 ? NC / 2 : 1];
-#pragma unroll
-  for (int c2 = 0; c2 < NC / 2; ++c2) k8off[c2] = krow * D + ((((DG / 16) * g + c2) ^ kswz<NCK8>(krow)) << 4);
-  const int k4off = D == 128 ? krow * (D / 2) + ((g ^ kswz<NCK4>(krow)) << 4)
-                             : krow * (D / 2) + (((g >> 1) ^ kswz<NCK4>(krow)) << 4) + 8 * (g & 1);
-  const int v8off = kBlock * D + l16 * 64 + ((w ^ vswz<4>(l16)) << 4) + 4 * g;
-  const int v4off = kBlock * D + l16 * 32 + (((w >> 1) ^ vswz<2>(l16)) << 4) + 8 * (w & 1) + 2 * g;
-
-  float m_run = kNegBig, l_run = 0.0f;   // per lane: head l16, keys of lane group g
+  float m_run = kNegBig, l_run = 0.0f;   // per lane: head l16, the keys of lane group g
   f32x4 oacc[ND], ocorr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One block's keys 16w .. 16w+15: s holds the lane's 4 scores (log2 units)
-  // of head l16 for keys 4g + i.  Returns the fp16 P^T operand (p * sv).
-  auto softmax = [&](float (&s)[4], float sv) {
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  // Online softmax over one 64-key block given its S^T accumulators (16 per
+  // lane), score = acc * m1 + m0; keys at index >= L are dropped.  Leaves the
+  // fp16 P^T operands (p * sv) of the two 32-key chunks in pb.
+  auto softmax = [&](const f32x4 (&acc)[4], float m1, float m0, float sv, int j, f16x8 (&pb)[2]) {
+    float s[4][4];
+    const bool tail = j * kBlock + kBlock > L;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[kb][i] = __builtin_fmaf(acc[kb][i], m1, m0);
+        if (tail && j * kBlock + dsig(kb, 4 * g + i) >= L) s[kb][i] = -INFINITY;
+      }
+    float mx = s[0][0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e >> 2][e & 3]);
     {   // max over the 4 lane groups of the head (lanes l, l^16, l^32, l^48)
       const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
@@ -300,88 +283,89 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
     }
-    f16x4 pb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(s[i] - m_run);
-      l_run += p;
-      pb[i] = static_cast<_Float16>(p * sv);
-    }
-    return pb;
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_run);
+        l_run += p;
+        pb[kb >> 1][4 * (kb & 1) + i] = static_cast<_Float16>(p * sv);
+      }
   };
 
-  float sk_n = 0.0f, sv_n = 0.0f;
-  if (nI > 0) scales(0, sk_n, sv_n);
-
-  // ---- quantized blocks through the LDS ring
+  // one quantized block of a unit: bb = which block of an INT4 pair
+  auto compute = [&](const Regs& r, bool four, int bb, int j) {
+    f32x4 acc[4];
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t)
-    if (t < nI) issue(t);
-  for (int t = 0; t < nI; ++t) {
-    // wait for block t (loads complete in order; each later block in flight
-    // holds n8 loads of this wave), then a barrier so every wave's share landed
-    // and block t-1's slot (the next issue's target) is free
-    const int ahead = min(S - 2, nI - 1 - t);
-    if (ahead >= 2) wait_vm(2 * n8);
-    else if (ahead == 1) wait_vm(n8);
-    else wait_vm(0);
-    lds_barrier();
-    if (t + S - 1 < nI) issue(t + S - 1);
-    const float sk = sk_n, sv = sv_n;
-    if (t + 1 < nI) scales(t + 1, sk_n, sv_n);
-
-    const int j = jof(e0 + t);
-    const bool four = is4(j);
-    const uint8_t* sl0 = lds + (t & (S - 1)) * SLOT;
-    f16x8 kop[NC];
-    f16x4 va[ND];
-    if (!four) {
+    for (int kb = 0; kb < 4; ++kb) {
+      acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c2 = 0; c2 < NC / 2; ++c2) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(sl0 + k8off[c2]);
-        kop[2 * c2] = as<f16x8>(u32x4{sub_i8x4(raw[0])[0], sub_i8x4(raw[0])[1], sub_i8x4(raw[1])[0],
-                                      sub_i8x4(raw[1])[1]});
-        kop[2 * c2 + 1] = as<f16x8>(u32x4{sub_i8x4(raw[2])[0], sub_i8x4(raw[2])[1], sub_i8x4(raw[3])[0],
-                                          sub_i8x4(raw[3])[1]});
+      for (int c = 0; c < NC; ++c) {
+        f16x8 kop;
+        if (!four) {   // channels DG g + 8c ..
+          const u32x4 w4 = r.k[2 * kb + (KW == 16 ? c >> 1 : c)];
+          const int d0 = KW == 16 ? 2 * (c & 1) : 0;
+          const u32x2 lo = sub_i8x4(w4[d0]), hi = sub_i8x4(w4[d0 + 1]);
+          kop = as<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        } else {
+          kop = as<f16x8>(sub_i4x8(r.k[4 * bb + kb][c]));
+        }
+        acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[c], acc[kb], 0, 0, 0);
       }
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-        va[db] = as<f16x4>(sub_i8x4(*reinterpret_cast<const uint32_t*>(sl0 + v8off + db * 1024)));
-    } else {
-      if constexpr (D == 128) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(sl0 + k4off);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) kop[e2] = as<f16x8>(sub_i4x8(raw[e2]));
-      } else {
-        const u32x2 raw = *reinterpret_cast<const u32x2*>(sl0 + k4off);
-        kop[0] = as<f16x8>(sub_i4x8(raw[0]));
-        kop[1] = as<f16x8>(sub_i4x8(raw[1]));
-      }
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-        va[db] = as<f16x4>(sub_i4x4(*reinterpret_cast<const uint16_t*>(sl0 + v4off + db * 512)));
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[c], qop[c], acc, 0, 0, 0);
     // score = tau log2e sk (2^24 acc - off sum(q)), off = 128 (INT8) or 8 (INT4)
-    const float cs = a.tau_log2e * sk;
-    const float m1 = cs * kTwo24, m0 = -(four ? 8.0f : 128.0f) * qsum * cs;
-    float s[4];
+    const float cs = a.tau_log2e * r.sk[bb];
+    f16x8 pb[2];
+    softmax(acc, cs * kTwo24, -(four ? 8.0f : 128.0f) * qsum * cs, r.sv[bb], j, pb);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(acc[i], m1, m0);
-    if (j * kBlock + kBlock > L) {   // partial last block (no FP16 window)
-      const int kbase = j * kBlock + 16 * w + 4 * g;
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (kbase + i >= L) s[i] = -INFINITY;
-    }
-    const f16x4 pb = softmax(s, sv);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pb, oacc[db], 0, 0, 0);
+      for (int c2 = 0; c2 < 2; ++c2) {
+        f16x8 va;
+        if (!four) {
+          const u32x2 lo = sub_i8x4(r.v[2 * db + c2][0]), hi = sub_i8x4(r.v[2 * db + c2][1]);
+          va = as<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        } else {
+          va = as<f16x8>(sub_i4x8(r.v[2 * db + bb][c2]));
+        }
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[c2], oacc[db], 0, 0, 0);
+      }
     // every row of this A operand is off * 2^-24: accumulates the offsets' share
-    const f16x4 offa = as<f16x4>(u32x2{four ? 0x00080008u : 0x00800080u, four ? 0x00080008u : 0x00800080u});
-    ocorr = __builtin_amdgcn_mfma_f32_16x16x16f16(offa, pb, ocorr, 0, 0, 0);
+    const uint32_t o2 = four ? 0x00080008u : 0x00800080u;
+    const f16x8 offa = as<f16x8>(u32x4{o2, o2, o2, o2});
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) ocorr = __builtin_amdgcn_mfma_f32_16x16x32_f16(offa, pb[c2], ocorr, 0, 0, 0);
+  };
+
+  // ---- quantized units, registers double-buffered: the next unit's loads are
+  // in flight while the current one is computed
+  {
+    auto unit_n = [&](int e, bool four) {   // blocks in the unit starting at entry e
+      return (four && e + 1 < eF && is4(jof(e + 1))) ? 2 : 1;
+    };
+    auto run = [&](const Regs& r, int e, bool four, int n) {
+      compute(r, four, 0, jof(e));
+      if (n == 2) compute(r, four, 1, jof(e + 1));
+    };
+    Regs ra, rb;
+    int e = e0;
+    bool fa = e < eF && is4(jof(e));
+    if (e < eF) load(e, fa, ra);
+    while (e < eF) {
+      const int na = unit_n(e, fa);
+      const int eb = e + na;
+      const bool fb = eb < eF && is4(jof(eb));
+      if (eb < eF) load(eb, fb, rb);
+      run(ra, e, fa, na);
+      e = eb;
+      if (e >= eF) break;
+      const int nb2 = unit_n(e, fb);
+      const int ea = e + nb2;
+      fa = ea < eF && is4(jof(ea));
+      if (ea < eF) load(ea, fa, ra);
+      run(rb, e, fb, nb2);
+      e = ea;
+    }
   }
   // back to value units: O = 2^24 (O' - offsets)
 #pragma unroll
@@ -389,44 +373,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) oacc[db][i] = (oacc[db][i] - ocorr[i]) * kTwo24;
 
-  // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy, from global memory
+  // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy
   for (int e = eF; e < e1; ++e) {
     const int j = dl.block(e);
     const size_t kblk = kvb0 + j;
-    const int key = j * kBlock + 16 * w + l16;   // K row of this lane (MFMA row l16)
-    f16x8 kop[NC];
-    {
+    f32x4 acc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = j * kBlock + dsig(kb, l16);   // K row of this lane (MFMA row l16)
       const uint16_t* src = a.k16 + (static_cast<size_t>(tok0 + (key < L ? key : 0)) * a.hkv + kv) * D + DG * g;
+      acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         u32x4 raw = key < L ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0, 0, 0, 0};
-        kop[c] = to_f16x8<BF16>(raw);
+        acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(to_f16x8<BF16>(raw), qop[c], acc[kb], 0, 0, 0);
       }
     }
-    f16x4 va[ND];
+    f16x8 pb[2];
+    softmax(acc, a.tau_log2e, 0.0f, 1.0f, j, pb);
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int d = db * 16 + l16;
-      const u32x2 raw = *reinterpret_cast<const u32x2*>(a.vt16 + (kblk * D + d) * kBlock + 16 * w + 4 * g);
-      va[db] = as<f16x4>(raw);
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[c], qop[c], acc, 0, 0, 0);
-    float s[4];
-    const int kbase = j * kBlock + 16 * w + 4 * g;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = kbase + i < L ? acc[i] * a.tau_log2e : -INFINITY;
-    const f16x4 pb = softmax(s, 1.0f);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pb, oacc[db], 0, 0, 0);
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int d = db * 16 + l16;
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(a.vt16 + (kblk * D + d) * kBlock + 16 * g + 8 * c2);
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as<f16x8>(raw), pb[c2], oacc[db], 0, 0, 0);
+      }
   }
 
-  // ---- merge the 4 waves (reusing the ring), write the split's (m, l, O) per query head
-  __syncthreads();
-  float* sm = reinterpret_cast<float*>(lds);            // [4][16]
-  float* sl = sm + 64;                                  // [4][16]
-  float* so = sl + 64;                                  // [4][16][D + 1]
+  // ---- the split's (m, l, O) per query head
   float lt = l_run;
   {
     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
@@ -434,33 +409,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
     lt = __uint_as_float(y[0]) + __uint_as_float(y[1]);
   }
-  if (g == 0) {
-    sm[w * 16 + l16] = m_run;
-    sl[w * 16 + l16] = lt;
-  }
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) so[(w * 16 + l16) * (D + 1) + db * 16 + 4 * g + i] = oacc[db][i];
-  __syncthreads();
-  for (int x = tid; x < grp * D; x += 256) {
-    const int qh = x / D, dv = x % D;
-    float M = kNegBig;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm[ww * 16 + qh]);
-    float lsum = 0.0f, ov = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float f = __builtin_amdgcn_exp2f(sm[ww * 16 + qh] - M);
-      lsum += sl[ww * 16 + qh] * f;
-      ov += so[(ww * 16 + qh) * (D + 1) + dv] * f;
+  if (l16 < grp) {
+    float* dst = a.ws + ((static_cast<size_t>(b) * a.hq + kv * grp + l16) * a.nsplit + split) * (D + 2);
+    if (g == 0) {
+      dst[0] = m_run;
+      dst[1] = lt;
     }
-    float* dst = a.ws + ((static_cast<size_t>(b) * a.hq + kv * grp + qh) * a.nsplit + chunk) * (D + 2);
-    dst[2 + dv] = ov;
-    if (dv == 0) {
-      dst[0] = M;
-      dst[1] = lsum;
-    }
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[2 + db * 16 + 4 * g + i] = oacc[db][i];
   }
 }
 
@@ -487,11 +445,11 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st) {
   dim3 grid(a.nsplit, a.hkv, a.nseq);
   if (d == 128) {
-    if (bf16) hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, dim3(256), 0, st, a);
+    if (bf16) hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, dim3(64), 0, st, a);
   } else {
-    if (bf16) hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, dim3(256), 0, st, a);
+    if (bf16) hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, dim3(64), 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

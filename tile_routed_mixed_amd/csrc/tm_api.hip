@@ -112,11 +112,12 @@ DecodePlan decode_plan(const tm_shape* s, const tm_dpolicy* p) {
       maxex = std::max(maxex, nex);
     }
   }
-  // one wave of workgroups: two per compute unit (each holds a 4-deep ring of
-  // cache blocks in LDS), each walking at least 8 blocks
+  // one wave per split, two per SIMD (each computes one unit of cache blocks
+  // while the next streams into its registers): about 2048 splits, each
+  // walking at least 6 blocks
   const int pairs = s->nseq * s->hkv;
-  int ns = (512 + pairs - 1) / pairs;
-  ns = std::min(ns, std::max(1, maxex / 8));
+  int ns = (2048 + pairs - 1) / pairs;
+  ns = std::min(ns, std::max(1, maxex / 6));
   ns = std::max(1, std::min(ns, 256));
   DecodePlan d;
   d.nsplit = ns;
