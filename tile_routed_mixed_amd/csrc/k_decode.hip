@@ -211,37 +211,51 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int eS = dl.sink_extra;
   const int j4hi = min(dl.nb - dl.b8, dl.jf);
   auto jof = [&](int e) { return e < eS ? 0 : dl.jstart + (e - eS); };
-  auto is4 = [&](int j) { return j >= dl.jstart && j < j4hi && !(dl.sink && j == 0); };
 
-  // start loading the unit at entry e (four: INT4 pair) into r
-  auto load = [&](int e, bool four, Regs& r) {
+  // start loading the unit at entry e (an INT4 pair when FOUR) into r
+  auto load = [&](int e, auto tag, Regs& r) {
+    constexpr bool FOUR = decltype(tag)::value;
     const int j = jof(e);
-    const __amdgpu_buffer_rsrc_t rk = four ? rk4 : rk8;
-    const __amdgpu_buffer_rsrc_t rv = four ? rv4 : rv8;
-    const uint32_t kbase = four ? kb4 : kb8, vbase = four ? vb4 : vb8;
-    const uint32_t j8 = static_cast<uint32_t>(j) * (kBlock * D), j4 = static_cast<uint32_t>(j) * (kBlock * D / 2);
+    if constexpr (!FOUR) {
+      const uint32_t so = static_cast<uint32_t>(j) * (kBlock * D);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t so = four ? j4 + (i >> 2) * (kBlock * D / 2) + dsig(i & 3, 0) * (D / 2)
-                               : j8 + dsig(i >> 1, 0) * D + (i & 1) * KW;
-      if constexpr (KW == 16) {
-        r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk, kbase, so, 0));
-      } else {
-        const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk, kbase, so, 0));
-        r.k[i] = u32x4{x[0], x[1], 0u, 0u};
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t o = so + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * KW);
+        if constexpr (KW == 16) {
+          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk8, kb8, o, 0));
+        } else {
+          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk8, kb8, o, 0));
+          r.k[i] = u32x4{x[0], x[1], 0u, 0u};
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 2 * ND; ++i) {
-      const uint32_t so = four ? j4 + (i & 1) * (kBlock * D / 2) + (i >> 1) * 512 : j8 + (i >> 1) * 1024 + (i & 1) * 8;
-      r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rv, vbase, so, 0));
+      for (int i = 0; i < 2 * ND; ++i)
+        r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(
+            rv8, vb8, so + static_cast<uint32_t>((i >> 1) * 1024 + (i & 1) * 8), 0));
+      r.sk[0] = sload(ks8, j);
+      r.sv[0] = sload(vs8, j);
+    } else {
+      const uint32_t so = static_cast<uint32_t>(j) * (kBlock * D / 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t o = so + static_cast<uint32_t>((i >> 2) * (kBlock * D / 2) + dsig(i & 3, 0) * (D / 2));
+        if constexpr (KW == 16) {
+          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk4, kb4, o, 0));
+        } else {
+          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk4, kb4, o, 0));
+          r.k[i] = u32x4{x[0], x[1], 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * ND; ++i)
+        r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(
+            rv4, vb4, so + static_cast<uint32_t>((i & 1) * (kBlock * D / 2) + (i >> 1) * 512), 0));
+      const int j1 = j + 1 < dl.nb ? j + 1 : j;
+      r.sk[0] = sload(ks4, j);
+      r.sv[0] = sload(vs4, j);
+      r.sk[1] = sload(ks4, j1);
+      r.sv[1] = sload(vs4, j1);
     }
-    const float* kp = four ? ks4 : ks8;
-    const float* vp = four ? vs4 : vs8;
-    r.sk[0] = sload(kp, j);
-    r.sv[0] = sload(vp, j);
-    r.sk[1] = four ? sload(ks4, j + 1 < dl.nb ? j + 1 : j) : 0.0f;
-    r.sv[1] = four ? sload(vs4, j + 1 < dl.nb ? j + 1 : j) : 0.0f;
   };
 
   float m_run = kNegBig, l_run = 0.0f;   // per lane: head l16, the keys of lane group g
@@ -294,7 +308,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   };
 
   // one quantized block of a unit: bb = which block of an INT4 pair
-  auto compute = [&](const Regs& r, bool four, int bb, int j) {
+  auto compute = [&](const Regs& r, auto tag, int bb, int j) {
+    constexpr bool four = decltype(tag)::value;
     f32x4 acc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -302,7 +317,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         f16x8 kop;
-        if (!four) {   // channels DG g + 8c ..
+        if constexpr (!four) {   // channels DG g + 8c ..
           const u32x4 w4 = r.k[2 * kb + (KW == 16 ? c >> 1 : c)];
           const int d0 = KW == 16 ? 2 * (c & 1) : 0;
           const u32x2 lo = sub_i8x4(w4[d0]), hi = sub_i8x4(w4[d0 + 1]);
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         f16x8 va;
-        if (!four) {
+        if constexpr (!four) {
           const u32x2 lo = sub_i8x4(r.v[2 * db + c2][0]), hi = sub_i8x4(r.v[2 * db + c2][1]);
           va = as<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
         } else {
@@ -338,34 +353,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   };
 
   // ---- quantized units, registers double-buffered: the next unit's loads are
-  // in flight while the current one is computed
-  {
-    auto unit_n = [&](int e, bool four) {   // blocks in the unit starting at entry e
-      return (four && e + 1 < eF && is4(jof(e + 1))) ? 2 : 1;
-    };
-    auto run = [&](const Regs& r, int e, bool four, int n) {
-      compute(r, four, 0, jof(e));
-      if (n == 2) compute(r, four, 1, jof(e + 1));
-    };
+  // in flight while the current one is computed.  The list runs in three
+  // phases of one precision each (sink block, INT4 band, INT8 band), so the
+  // loads and the dequantization are specialized per phase.
+  auto phase = [&](auto tag, int ea, int eb) {
+    constexpr int U = decltype(tag)::value ? 2 : 1;   // blocks per unit
+    if (ea >= eb) return;
     Regs ra, rb;
-    int e = e0;
-    bool fa = e < eF && is4(jof(e));
-    if (e < eF) load(e, fa, ra);
-    while (e < eF) {
-      const int na = unit_n(e, fa);
-      const int eb = e + na;
-      const bool fb = eb < eF && is4(jof(eb));
-      if (eb < eF) load(eb, fb, rb);
-      run(ra, e, fa, na);
-      e = eb;
-      if (e >= eF) break;
-      const int nb2 = unit_n(e, fb);
-      const int ea = e + nb2;
-      fa = ea < eF && is4(jof(ea));
-      if (ea < eF) load(ea, fa, ra);
-      run(rb, e, fb, nb2);
-      e = ea;
+    int e = ea;
+    load(e, tag, ra);
+    while (true) {
+      const int na = min(U, eb - e), e2 = e + na;
+      if (e2 < eb) load(e2, tag, rb);
+      compute(ra, tag, 0, jof(e));
+      if (na == 2) compute(ra, tag, 1, jof(e + 1));
+      e = e2;
+      if (e >= eb) break;
+      const int nb2 = min(U, eb - e), e3 = e + nb2;
+      if (e3 < eb) load(e3, tag, ra);
+      compute(rb, tag, 0, jof(e));
+      if (nb2 == 2) compute(rb, tag, 1, jof(e + 1));
+      e = e3;
+      if (e >= eb) break;
     }
+  };
+  {
+    // list entries [0, lead) are INT8 (the sink), then the INT4 band [e4lo,
+    // e4hi), then INT8 up to the FP16 window
+    const bool sink0 = dl.sink && dl.jstart == 0 && j4hi > 0;   // block 0 heads the band but is INT8
+    const int lead = sink0 ? 1 : eS;
+    const int n4 = max(0, j4hi - dl.jstart - (sink0 ? 1 : 0));
+    const int e4lo = lead, e4hi = lead + n4;
+    typedef std::integral_constant<bool, false> Int8;
+    typedef std::integral_constant<bool, true> Int4;
+    phase(Int8{}, max(e0, 0), min(eF, lead));
+    phase(Int4{}, max(e0, e4lo), min(eF, e4hi));
+    phase(Int8{}, max(e0, e4hi), eF);
   }
   // back to value units: O = 2^24 (O' - offsets)
 #pragma unroll
