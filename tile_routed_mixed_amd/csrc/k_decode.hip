@@ -169,20 +169,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int eF = max(e0, min(e1, dl.first_fp16()));                                             // quantized: [e0, eF)
   const size_t kvb0 = static_cast<size_t>(kv) * a.nblk + blk0;
 
-  // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group);
-  // qsum: the head's sum of q over all channels (for the code offsets)
-  f16x8 qop[NC];
-  float qsum = 0.0f;
-  {
-    const bool ok = l16 < grp;
-    const uint16_t* qs = a.q + (static_cast<size_t>(b) * a.hq + kv * grp + (ok ? l16 : 0)) * D + DG * g;
+  // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group).
+  // Chunk c of lane group g holds 8 channels; the K operands use the same
+  // channel map.  INT4 / 16-bit K: channels DG g + 8c ..  INT8 K: channels
+  // (D/2) h + KW g + 8 sub .. with c = h (KW/8) + sub, so the four lane groups
+  // of a row read one contiguous span per load.  qsum: the head's sum of q
+  // (for the code offsets).
+  const bool qok = l16 < grp;
+  const uint16_t* const qrow = a.q + (static_cast<size_t>(b) * a.hq + kv * grp + (qok ? l16 : 0)) * D;
+  auto q_operand = [&](bool map8, f16x8 (&qop)[NC]) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(qs + 8 * c) : u32x4{0, 0, 0, 0};
+      const int ch = map8 ? (D / 2) * (c / (KW / 8)) + KW * g + 8 * (c % (KW / 8)) : DG * g + 8 * c;
+      u32x4 raw = qok ? *reinterpret_cast<const u32x4*>(qrow + ch) : u32x4{0, 0, 0, 0};
       qop[c] = to_f16x8<BF16>(raw);
+    }
+  };
+  float qsum = 0.0f;
+  {
+    f16x8 qop[NC];
+    q_operand(false, qop);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qsum += static_cast<float>(qop[c][e]);
-    }
     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(qsum), __float_as_uint(qsum), false, false);
     qsum = __uint_as_float(x[0]) + __uint_as_float(x[1]);
     const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(qsum), __float_as_uint(qsum), false, false);
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const float* const vs8 = pin_sgpr(a.vs8 + kvb0);
   const float* const ks4 = pin_sgpr(a.ks4 + kvb0);
   const float* const vs4 = pin_sgpr(a.vs4 + kvb0);
-  const uint32_t kb8 = static_cast<uint32_t>(dsig(0, l16) * D + DG * g);
+  const uint32_t kb8 = static_cast<uint32_t>(dsig(0, l16) * D + KW * g);
   const uint32_t kb4 = static_cast<uint32_t>(dsig(0, l16) * (D / 2) + (DG / 2) * g);
   const uint32_t vb8 = static_cast<uint32_t>(l16 * 64 + 16 * g);
   const uint32_t vb4 = static_cast<uint32_t>(l16 * 32 + 8 * g);
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       const uint32_t so = static_cast<uint32_t>(j) * (kBlock * D);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t o = so + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * KW);
+        const uint32_t o = so + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * (D / 2));
         if constexpr (KW == 16) {
           r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk8, kb8, o, 0));
         } else {
@@ -229,9 +239,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         }
       }
 #pragma unroll
-      for (int i = 0; i < 2 * ND; ++i)
-        r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(
-            rv8, vb8, so + static_cast<uint32_t>((i >> 1) * 1024 + (i & 1) * 8), 0));
+      for (int db = 0; db < ND; ++db) {   // keys 16g .. 16g+15 of V^T row 16 db + l16: one 16-byte load
+        const u32x4 x = as<u32x4>(
+            __builtin_amdgcn_raw_buffer_load_b128(rv8, vb8, so + static_cast<uint32_t>(db * 1024), 0));
+        r.v[2 * db] = u32x2{x[0], x[1]};
+        r.v[2 * db + 1] = u32x2{x[2], x[3]};
+      }
       r.sk[0] = sload(ks8, j);
       r.sv[0] = sload(vs8, j);
     } else {
@@ -308,7 +321,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   };
 
   // one quantized block of a unit: bb = which block of an INT4 pair
-  auto compute = [&](const Regs& r, auto tag, int bb, int j) {
+  auto compute = [&](const Regs& r, auto tag, int bb, int j, const f16x8 (&qop)[NC]) {
     constexpr bool four = decltype(tag)::value;
     f32x4 acc[4];
 #pragma unroll
@@ -317,7 +330,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         f16x8 kop;
-        if constexpr (!four) {   // channels DG g + 8c ..
+        if constexpr (!four) {   // piece h = c / (KW / 8) of the lane's row, dwords of sub = c % (KW / 8)
           const u32x4 w4 = r.k[2 * kb + (KW == 16 ? c >> 1 : c)];
           const int d0 = KW == 16 ? 2 * (c & 1) : 0;
           const u32x2 lo = sub_i8x4(w4[d0]), hi = sub_i8x4(w4[d0 + 1]);
@@ -359,20 +372,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   auto phase = [&](auto tag, int ea, int eb) {
     constexpr int U = decltype(tag)::value ? 2 : 1;   // blocks per unit
     if (ea >= eb) return;
+    f16x8 qop[NC];
+    q_operand(!decltype(tag)::value, qop);
     Regs ra, rb;
     int e = ea;
     load(e, tag, ra);
     while (true) {
       const int na = min(U, eb - e), e2 = e + na;
       if (e2 < eb) load(e2, tag, rb);
-      compute(ra, tag, 0, jof(e));
-      if (na == 2) compute(ra, tag, 1, jof(e + 1));
+      compute(ra, tag, 0, jof(e), qop);
+      if (na == 2) compute(ra, tag, 1, jof(e + 1), qop);
       e = e2;
       if (e >= eb) break;
       const int nb2 = min(U, eb - e), e3 = e + nb2;
       if (e3 < eb) load(e3, tag, ra);
-      compute(rb, tag, 0, jof(e));
-      if (nb2 == 2) compute(rb, tag, 1, jof(e + 1));
+      compute(rb, tag, 0, jof(e), qop);
+      if (nb2 == 2) compute(rb, tag, 1, jof(e + 1), qop);
       e = e3;
       if (e >= eb) break;
     }
@@ -397,6 +412,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     for (int i = 0; i < 4; ++i) oacc[db][i] = (oacc[db][i] - ocorr[i]) * kTwo24;
 
   // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy
+  f16x8 qop[NC];
+  if (eF < e1) q_operand(false, qop);
   for (int e = eF; e < e1; ++e) {
     const int j = dl.block(e);
     const size_t kblk = kvb0 + j;
