@@ -68,8 +68,8 @@ typedef enum tm_dtype { TM_F16 = 0, TM_BF16 = 1, TM_F32 = 2 } tm_dtype;
 typedef enum tm_prec { TM_SKIP = 0, TM_INT4 = 1, TM_INT8 = 2, TM_FP16 = 3 } tm_prec;
 
 typedef enum tm_layout {
-  TM_ROWS = 0,  /* codes [heads][nblk][64][d] and [heads][nblk][64][d/2]        */
-  TM_COLS = 1   /* codes transposed per block: [heads][nblk][d][64], [d][32]   */
+  TM_ROWS = 0,  /* codes [nblk][heads][64][d] and [nblk][heads][64][d/2]        */
+  TM_COLS = 1   /* codes transposed per block: [nblk][heads][d][64], [d][32]   */
 } tm_layout;
 
 typedef enum tm_policy_kind { TM_POLICY_BOUNDARIES = 0, TM_POLICY_BITMASK = 1 } tm_policy_kind;
@@ -89,7 +89,7 @@ typedef struct tm_shape {
 } tm_shape;
 
 /* Quantized tensor (device buffers, caller-allocated).  One symmetric scale
- * per (head, 64-token block) over all d channels of the block's valid rows:
+ * per (64-token block, head) over all d channels of the block's valid rows:
  * s8 = amax / 127, s4 = amax / 7 (IEEE binary32 divisions);
  * code = clamp(round_half_even(x / s), -qmax, qmax), binary32 division;
  * amax == 0 gives scale 0 and zero codes; rows past a sequence's end are zero.
@@ -97,12 +97,15 @@ typedef struct tm_shape {
  * 2t in the low nibble of byte t and 2t+1 in the high nibble.
  * ([TriAttention] abstract: keys and values quantized during prefill; the pages
  * give no formula, this symmetric block reading is the library's definition.)
- *   TM_ROWS: c8 [heads][nblk][64][d]   c4 [heads][nblk][64][d/2]
- *   TM_COLS: c8 [heads][nblk][d][64]   c4 [heads][nblk][d][32]
+ * Block-major: all heads of one 64-token block are adjacent, so the blocks a
+ * decode step reads are dense in memory, and one block of every head is a
+ * contiguous slice (entries [j*heads, (j+1)*heads)).
+ *   TM_ROWS: c8 [nblk][heads][64][d]   c4 [nblk][heads][64][d/2]
+ *   TM_COLS: c8 [nblk][heads][d][64]   c4 [nblk][heads][d][32]
  *            t16 (optional, TM_COLS only): the block's values as fp16,
- *            transposed, [heads][nblk][d][64] (bf16 input rounded to nearest
+ *            transposed, [nblk][heads][d][64] (bf16 input rounded to nearest
  *            even fp16; zeros past the sequence end).
- *   s8, s4 [heads][nblk] float.
+ *   s8, s4 [nblk][heads] float.
  * nblk must equal sum over sequences of ceil(len / 64) (tm_num_blocks). */
 typedef struct tm_qtensor {
   int8_t* c8;
@@ -238,8 +241,9 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
  * to fp16 for the PV product ([TriAttention] abstract: one normalized output
  * from both QK precisions; [TileMix] abstract: shared online-softmax state).
  * Errors: TM_E_ARG, TM_E_SHAPE (tensors not matching the shape),
- * TM_E_UNSUPPORTED (a sequence whose 16-bit keys of one KV head span 2 GiB or
- * more, i.e. len * hkv * d * 2 >= 2^31), TM_E_HIP. */
+ * TM_E_UNSUPPORTED (a sequence whose 16-bit keys, or whose fp16 V copy, span
+ * 2 GiB or more: len * hkv * d * 2 >= 2^31, or ceil(len / 64) * 64 * hkv * d
+ * * 2 >= 2^31), TM_E_HIP. */
 tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kind,
                      const void* q, const void* k,
                      const tm_qtensor* qq, const tm_qtensor* kq, const tm_qtensor* vq,
@@ -264,7 +268,8 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
  * score = scale * (q . k), value = v ([HyQuant] "How HyQuant works":
  * dequantization fused with attention).
  * Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY, TM_E_SPACE, TM_E_UNSUPPORTED
- * (hq/hkv > 16, more than 64 KV heads), TM_E_HIP. */
+ * (hq/hkv > 16, more than 64 KV heads, or a sequence whose INT8 codes span
+ * 2 GiB or more: ceil(len / 64) * 64 * hkv * d >= 2^31), TM_E_HIP. */
 tm_status tm_decode(const tm_shape* cache, const void* q,
                     const tm_qtensor* kq, const tm_qtensor* vq, const void* k16,
                     const tm_dpolicy* policy, void* o, int32_t o_dtype,

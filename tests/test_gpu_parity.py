@@ -49,12 +49,15 @@ def test_quantize_bitexact(dtype, d, seqlens):
     torch.cuda.synchronize()
     for x, qt, layout in ((q, p.qq, "rows"), (k, p.kq, "rows"), (v, p.vq, "cols")):
         ref = OQ.quantize(x[1], w.seqlens, layout=layout, with_t16=(layout == "cols"))
-        assert np.array_equal(qt.s8.cpu().numpy().view(np.uint32), ref["s8"].view(np.uint32))
-        assert np.array_equal(qt.s4.cpu().numpy().view(np.uint32), ref["s4"].view(np.uint32))
-        assert np.array_equal(qt.c8.cpu().numpy(), ref["c8p"])
-        assert np.array_equal(qt.c4.cpu().numpy(), ref["c4p"])
+        # the library stores blocks block-major ([nblk][heads]...), the oracle head-major
+        def hm(t):
+            return np.swapaxes(t.cpu().numpy(), 0, 1)
+        assert np.array_equal(hm(qt.s8).view(np.uint32), ref["s8"].view(np.uint32))
+        assert np.array_equal(hm(qt.s4).view(np.uint32), ref["s4"].view(np.uint32))
+        assert np.array_equal(hm(qt.c8), ref["c8p"])
+        assert np.array_equal(hm(qt.c4), ref["c4p"])
         if layout == "cols":
-            assert np.array_equal(qt.t16.cpu().numpy().view(np.uint16), ref["t16"].view(np.uint16))
+            assert np.array_equal(hm(qt.t16).view(np.uint16), ref["t16"].view(np.uint16))
 
 
 # ---------------------------------------------------------------------------- traversal

@@ -147,15 +147,16 @@ class QTensor:
         import torch
         nblk, d = shape.nblk(), shape.d
         self.heads, self.layout, self.nblk = heads, layout, nblk
+        # block-major: [nblk][heads][...]
         if layout == TM_ROWS:
-            self.c8 = torch.empty((heads, nblk, 64, d), dtype=torch.int8, device=device)
-            self.c4 = torch.empty((heads, nblk, 64, d // 2), dtype=torch.uint8, device=device)
+            self.c8 = torch.empty((nblk, heads, 64, d), dtype=torch.int8, device=device)
+            self.c4 = torch.empty((nblk, heads, 64, d // 2), dtype=torch.uint8, device=device)
         else:
-            self.c8 = torch.empty((heads, nblk, d, 64), dtype=torch.int8, device=device)
-            self.c4 = torch.empty((heads, nblk, d, 32), dtype=torch.uint8, device=device)
-        self.s8 = torch.empty((heads, nblk), dtype=torch.float32, device=device)
-        self.s4 = torch.empty((heads, nblk), dtype=torch.float32, device=device)
-        self.t16 = (torch.empty((heads, nblk, d, 64), dtype=torch.float16, device=device)
+            self.c8 = torch.empty((nblk, heads, d, 64), dtype=torch.int8, device=device)
+            self.c4 = torch.empty((nblk, heads, d, 32), dtype=torch.uint8, device=device)
+        self.s8 = torch.empty((nblk, heads), dtype=torch.float32, device=device)
+        self.s4 = torch.empty((nblk, heads), dtype=torch.float32, device=device)
+        self.t16 = (torch.empty((nblk, heads, d, 64), dtype=torch.float16, device=device)
                     if with_t16 else None)
         self.c = tm_qtensor(_ptr(self.c8), _ptr(self.c4), _ptr(self.s8), _ptr(self.s4), _ptr(self.t16),
                             heads, layout, nblk)

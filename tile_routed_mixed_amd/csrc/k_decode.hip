@@ -167,7 +167,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   dl.n_ex = (dl.nb - dl.jstart) + dl.sink_extra;
   const int e0 = dl.split(split, a.nsplit), e1 = dl.split(split + 1, a.nsplit);
   const int eF = max(e0, min(e1, dl.first_fp16()));                                             // quantized: [e0, eF)
-  const size_t kvb0 = static_cast<size_t>(kv) * a.nblk + blk0;
+  // codes and scales are block-major ([nblk][hkv]...): cache block j of this
+  // (sequence, KV head) is entry kvb0 + j * hkv
+  const size_t kvb0 = static_cast<size_t>(blk0) * a.hkv + kv;
+  const uint32_t hkv = static_cast<uint32_t>(a.hkv);
 
   // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group).
   // Chunk c of lane group g holds 8 channels; the K operands use the same
@@ -202,11 +205,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // buffer resources over this (sequence, KV head)'s blocks (a unit's second
   // INT4 block may lie past the last block: such loads return zeros and the
   // block is not computed)
-  const uint32_t nbs = static_cast<uint32_t>(dl.nb);
-  const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(a.k8 + kvb0 * (kBlock * D), nbs * (kBlock * D));
-  const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(a.v8 + kvb0 * (kBlock * D), nbs * (kBlock * D));
-  const __amdgpu_buffer_rsrc_t rk4 = make_rsrc(a.k4 + kvb0 * (kBlock * D / 2), nbs * (kBlock * D / 2));
-  const __amdgpu_buffer_rsrc_t rv4 = make_rsrc(a.v4 + kvb0 * (kBlock * D / 2), nbs * (kBlock * D / 2));
+  const uint32_t span = static_cast<uint32_t>(max(dl.nb, 1) - 1) * hkv + 1;   // entries kvb0 .. last block
+  const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(a.k8 + kvb0 * (kBlock * D), span * (kBlock * D));
+  const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(a.v8 + kvb0 * (kBlock * D), span * (kBlock * D));
+  const __amdgpu_buffer_rsrc_t rk4 = make_rsrc(a.k4 + kvb0 * (kBlock * D / 2), span * (kBlock * D / 2));
+  const __amdgpu_buffer_rsrc_t rv4 = make_rsrc(a.v4 + kvb0 * (kBlock * D / 2), span * (kBlock * D / 2));
   const float* const ks8 = pin_sgpr(a.ks8 + kvb0);
   const float* const vs8 = pin_sgpr(a.vs8 + kvb0);
   const float* const ks4 = pin_sgpr(a.ks4 + kvb0);
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     constexpr bool FOUR = decltype(tag)::value;
     const int j = jof(e);
     if constexpr (!FOUR) {
-      const uint32_t so = static_cast<uint32_t>(j) * (kBlock * D);
+      const uint32_t so = static_cast<uint32_t>(j) * hkv * (kBlock * D);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t o = so + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * (D / 2));
@@ -245,13 +248,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         r.v[2 * db] = u32x2{x[0], x[1]};
         r.v[2 * db + 1] = u32x2{x[2], x[3]};
       }
-      r.sk[0] = sload(ks8, j);
-      r.sv[0] = sload(vs8, j);
+      r.sk[0] = sload(ks8, static_cast<size_t>(j) * hkv);
+      r.sv[0] = sload(vs8, static_cast<size_t>(j) * hkv);
     } else {
-      const uint32_t so = static_cast<uint32_t>(j) * (kBlock * D / 2);
+      const uint32_t so = static_cast<uint32_t>(j) * hkv * (kBlock * D / 2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t o = so + static_cast<uint32_t>((i >> 2) * (kBlock * D / 2) + dsig(i & 3, 0) * (D / 2));
+        const uint32_t o = so + static_cast<uint32_t>(i >> 2) * hkv * (kBlock * D / 2) + static_cast<uint32_t>(dsig(i & 3, 0) * (D / 2));
         if constexpr (KW == 16) {
           r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk4, kb4, o, 0));
         } else {
@@ -262,12 +265,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
       for (int i = 0; i < 2 * ND; ++i)
         r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(
-            rv4, vb4, so + static_cast<uint32_t>((i & 1) * (kBlock * D / 2) + (i >> 1) * 512), 0));
+            rv4, vb4, so + static_cast<uint32_t>(i & 1) * hkv * (kBlock * D / 2) + static_cast<uint32_t>((i >> 1) * 512), 0));
       const int j1 = j + 1 < dl.nb ? j + 1 : j;
-      r.sk[0] = sload(ks4, j);
-      r.sv[0] = sload(vs4, j);
-      r.sk[1] = sload(ks4, j1);
-      r.sv[1] = sload(vs4, j1);
+      r.sk[0] = sload(ks4, static_cast<size_t>(j) * hkv);
+      r.sv[0] = sload(vs4, static_cast<size_t>(j) * hkv);
+      r.sk[1] = sload(ks4, static_cast<size_t>(j1) * hkv);
+      r.sv[1] = sload(vs4, static_cast<size_t>(j1) * hkv);
     }
   };
 
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   if (eF < e1) q_operand(false, qop);
   for (int e = eF; e < e1; ++e) {
     const int j = dl.block(e);
-    const size_t kblk = kvb0 + j;
+    const size_t kblk = kvb0 + static_cast<size_t>(j) * hkv;
     f32x4 acc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -462,21 +465,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   }
 }
 
+// Merge of one query head's split results by log-sum-exp: one wave per head;
+// the splits' maxima and sums are reduced across lanes, then every lane sums
+// its output channels over the splits with all loads of a group of 8 splits
+// in flight together.
 template <int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
-  const float* src = a.ws + static_cast<size_t>(bh) * a.nsplit * (D + 2);
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;
+  const int bh = blockIdx.x, lane = threadIdx.x, ns = a.nsplit;
+  const float* src = a.ws + static_cast<size_t>(bh) * ns * (D + 2);
   float M = kNegBig;
-  for (int c = 0; c < a.nsplit; ++c) M = fmaxf(M, src[c * (D + 2)]);
-  for (int dv = threadIdx.x; dv < D; dv += blockDim.x) {
-    float lsum = 0.0f, ov = 0.0f;
-    for (int c = 0; c < a.nsplit; ++c) {
-      const float f = __builtin_amdgcn_exp2f(src[c * (D + 2)] - M);
-      lsum += src[c * (D + 2) + 1] * f;
-      ov += src[c * (D + 2) + 2 + dv] * f;
+  for (int c = lane; c < ns; c += 64) M = fmaxf(M, src[c * (D + 2)]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float lsum = 0.0f;
+  for (int c = lane; c < ns; c += 64) lsum += src[c * (D + 2) + 1] * __builtin_amdgcn_exp2f(src[c * (D + 2)] - M);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+  float ov[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) ov[p] = 0.0f;
+  for (int c0 = 0; c0 < ns; c0 += 8) {
+    float f[8], x[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = min(c0 + u, ns - 1);
+      f[u] = c0 + u < ns ? __builtin_amdgcn_exp2f(src[c * (D + 2)] - M) : 0.0f;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) x[u][p] = src[c * (D + 2) + 2 + 64 * p + lane];
     }
-    const float r = lsum > 0.0f ? ov / lsum : 0.0f;
-    const size_t off = static_cast<size_t>(bh) * D + dv;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int p = 0; p < PER; ++p) ov[p] += x[u][p] * f[u];
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const float r = lsum > 0.0f ? ov[p] / lsum : 0.0f;
+    const size_t off = static_cast<size_t>(bh) * D + 64 * p + lane;
     if (a.o_dtype == TM_F32) static_cast<float*>(a.o)[off] = r;
     else static_cast<_Float16*>(a.o)[off] = static_cast<_Float16>(r);
   }
@@ -493,8 +519,8 @@ hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st) 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.nseq * a.hq), dim3(128), 0, st, a);
-  else hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.nseq * a.hq), dim3(128), 0, st, a);
+  if (d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.nseq * a.hq), dim3(64), 0, st, a);
+  else hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.nseq * a.hq), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

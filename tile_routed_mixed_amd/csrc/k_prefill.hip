@@ -175,21 +175,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qrow0 = it.qtile * BQ + w * RW;
   const int qblk = qrow0 / kBlock;
   const bool qblk_ok = qblk < nbs;
-  const size_t qblk_g = static_cast<size_t>(head) * a.nblk + se.blk_start + qblk;
-  const size_t kv_blk0 = static_cast<size_t>(kv) * a.nblk + se.blk_start;
+  // codes and scales are block-major ([nblk][heads]...): cache block j of this
+  // (sequence, KV head) is entry kv_blk0 + j * hkv
+  const size_t qblk_g = (static_cast<size_t>(se.blk_start) + qblk) * a.hq + head;
+  const size_t kv_blk0 = static_cast<size_t>(se.blk_start) * a.hkv + kv;
+  const uint32_t hkv = static_cast<uint32_t>(a.hkv);
+  const uint32_t span = static_cast<uint32_t>(max(nbs, 1) - 1) * hkv + 1;   // entries kv_blk0 .. last block
   const uint32_t kpitch16 = static_cast<uint32_t>(a.hkv) * D * 2;   // bytes between key rows of k
   const float sq8 = qblk_ok ? a.qs8[qblk_g] : 0.0f;
   const float sq4 = (HAS4 && qblk_ok) ? a.qs4[qblk_g] : 0.0f;
   const float tau = a.tau_log2e;
 
-  // buffer resources over this (sequence, KV head): tile j starts at j * tile bytes
+  // buffer resources over this (sequence, KV head): tile j starts at j * hkv * tile bytes
   const __amdgpu_buffer_rsrc_t rs_v =
-      make_rsrc(reinterpret_cast<const uint8_t*>(a.vt16) + kv_blk0 * VBYTES, static_cast<uint32_t>(nbs) * VBYTES);
-  const __amdgpu_buffer_rsrc_t rs_k8 = make_rsrc(reinterpret_cast<const uint8_t*>(a.k8) + kv_blk0 * (kBlock * D),
-                                                 static_cast<uint32_t>(nbs) * (kBlock * D));
+      make_rsrc(reinterpret_cast<const uint8_t*>(a.vt16) + kv_blk0 * VBYTES, span * VBYTES);
+  const __amdgpu_buffer_rsrc_t rs_k8 =
+      make_rsrc(reinterpret_cast<const uint8_t*>(a.k8) + kv_blk0 * (kBlock * D), span * (kBlock * D));
   __amdgpu_buffer_rsrc_t rs_k4 = rs_k8, rs_k16 = rs_k8;
-  if constexpr (HAS4)
-    rs_k4 = make_rsrc(a.k4 + kv_blk0 * (kBlock * D / 2), static_cast<uint32_t>(nbs) * (kBlock * D / 2));
+  if constexpr (HAS4) rs_k4 = make_rsrc(a.k4 + kv_blk0 * (kBlock * D / 2), span * (kBlock * D / 2));
   if constexpr (HAS16)   // rows past the sequence end fall outside the range and read as zeros
     rs_k16 = make_rsrc(reinterpret_cast<const uint8_t*>(a.k) + (static_cast<size_t>(se.tok_start) * a.hkv + kv) * D * 2,
                        static_cast<uint32_t>(len - 1) * kpitch16 + D * 2);
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     tl_jp = jp;
     const uint32_t pj = jp >> 24;
-    const size_t kb = kv_blk0 + (jp & 0xFFFFFFu);
+    const size_t kb = kv_blk0 + static_cast<size_t>(jp & 0xFFFFFFu) * hkv;
     float cs = tau;
     if (pj == TM_INT8) cs = (sq8 * a.ks8[kb]) * tau;
     else if (HAS4 && pj == TM_INT4) cs = (sq4 * a.ks4[kb]) * (tau * (1.0f / 256.0f));
@@ -260,9 +263,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // start loading tile j (precision prec) into buffer BUFC
   auto issue = [&](uint32_t j, uint32_t prec, int boff) {
     uint8_t* dst = lds + boff;
-    cp_v.issue(rs_v, j * VBYTES, dst + KBYTES, w);
-    if (prec == TM_INT8) cp_k8.issue(rs_k8, j * (kBlock * D), dst, w);
-    else if (HAS4 && prec == TM_INT4) cp_k4.issue(rs_k4, j * (kBlock * D / 2), dst, w);
+    const uint32_t jh = j * hkv;
+    cp_v.issue(rs_v, jh * VBYTES, dst + KBYTES, w);
+    if (prec == TM_INT8) cp_k8.issue(rs_k8, jh * (kBlock * D), dst, w);
+    else if (HAS4 && prec == TM_INT4) cp_k4.issue(rs_k4, jh * (kBlock * D / 2), dst, w);
     else if (HAS16) cp_k16.issue(rs_k16, j * (kBlock * kpitch16), dst, w);
   };
 

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float sc8 = __fdiv_rn(amax, 127.0f);
   const float sc4 = __fdiv_rn(amax, 7.0f);
-  const size_t blk = static_cast<size_t>(h) * a.nblk + b;
+  const size_t blk = static_cast<size_t>(b) * a.heads + h;   // block-major: [nblk][heads]
   if (tid == 0) {
     a.s8[blk] = sc8;
     a.s4[blk] = sc4;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   }
 
   if constexpr (!COLS) {
-    // rows layout: c8 [h][nblk][64][D], c4 [h][nblk][64][D/2]
+    // rows layout: c8 [nblk][heads][64][D], c4 [nblk][heads][64][D/2]
     int8_t* d8 = a.c8 + (blk * kBlock + row) * D + col0;
 #pragma unroll
     for (int v = 0; v < EPT / 16; ++v) {

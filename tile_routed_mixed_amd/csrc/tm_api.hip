@@ -270,7 +270,8 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
     const int64_t len = shape->cu_seqlens[s + 1] - shape->cu_seqlens[s];
     const int64_t nb = (len + 63) / 64;
     const int64_t k16 = len * shape->hkv * shape->d * 2;
-    if (nb * 64 * shape->d * 2 >= (int64_t(1) << 31) || k16 >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
+    if (nb * shape->hkv * 64 * shape->d * 2 >= (int64_t(1) << 31) || k16 >= (int64_t(1) << 31))
+      return TM_E_UNSUPPORTED;
   }
   PrefillArgs a;
   a.trav = static_cast<const uint8_t*>(trav);
@@ -317,8 +318,12 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     if (b8 < 0 || b4 < 0 || b8 > b4) return TM_E_POLICY;
     if (b4 == 0 && policy->tail_tokens == 0 && !policy->sink) return TM_E_POLICY;
   }
-  for (int b = 0; b < cache->nseq; ++b)
-    if (cache->cu_seqlens[b + 1] - cache->cu_seqlens[b] < 1) return TM_E_SHAPE;
+  for (int b = 0; b < cache->nseq; ++b) {
+    const int64_t len = cache->cu_seqlens[b + 1] - cache->cu_seqlens[b];
+    if (len < 1) return TM_E_SHAPE;
+    // a sequence's blocks of one KV head must lie within 2 GiB of its first (32-bit offsets)
+    if ((len + 63) / 64 * cache->hkv * 64 * cache->d >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
+  }
   const DecodePlan plan = decode_plan(cache, policy);
   if (ws == nullptr) {
     *ws_bytes = plan.ws_bytes;
