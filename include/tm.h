@@ -268,8 +268,9 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
  * score = scale * (q . k), value = v ([HyQuant] "How HyQuant works":
  * dequantization fused with attention).
  * Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY, TM_E_SPACE, TM_E_UNSUPPORTED
- * (hq/hkv > 16, more than 64 KV heads, or a sequence whose INT8 codes span
- * 2 GiB or more: ceil(len / 64) * 64 * hkv * d >= 2^31), TM_E_HIP. */
+ * (hq/hkv > 16, more than 64 KV heads, or a sequence whose 16-bit keys or
+ * fp16 V copy span 2 GiB or more: ceil(len / 64) * 64 * hkv * d * 2 >= 2^31),
+ * TM_E_HIP. */
 tm_status tm_decode(const tm_shape* cache, const void* q,
                     const tm_qtensor* kq, const tm_qtensor* vq, const void* k16,
                     const tm_dpolicy* policy, void* o, int32_t o_dtype,

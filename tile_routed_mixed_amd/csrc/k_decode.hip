@@ -225,48 +225,60 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int j4hi = min(dl.nb - dl.b8, dl.jf);
   auto jof = [&](int e) { return e < eS ? 0 : dl.jstart + (e - eS); };
 
-  // start loading the unit at entry e (an INT4 pair when FOUR) into r
-  auto load = [&](int e, auto tag, Regs& r) {
+  // Start loading the unit at entry e (an INT4 pair when FOUR) into r.  The
+  // unit's byte offset rides in the per-lane offset, so that a unit that does
+  // not exist (valid false, or the second block of an INT4 pair past the
+  // sequence end) sits at kNone, beyond every buffer range, and its loads
+  // return zeros without touching memory.  Every unit is loaded by the same
+  // instruction sequence, whether or not it exists: the loads never sit under
+  // a branch, so the count of loads in flight is the same on every path and
+  // computing one unit waits only for that unit's loads.
+  constexpr uint32_t kNone = 0x80000000u;
+  auto load = [&](int e, bool valid, auto tag, Regs& r) {
     constexpr bool FOUR = decltype(tag)::value;
-    const int j = jof(e);
+    const int j = valid ? jof(e) : 0;
     if constexpr (!FOUR) {
-      const uint32_t so = static_cast<uint32_t>(j) * hkv * (kBlock * D);
+      const uint32_t so = valid ? static_cast<uint32_t>(j) * hkv * (kBlock * D) : kNone;
+      const uint32_t vk = kb8 + so, vv = vb8 + so;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t o = so + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * (D / 2));
+        const uint32_t o = vk + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * (D / 2));
         if constexpr (KW == 16) {
-          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk8, kb8, o, 0));
+          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk8, o, 0, 0));
         } else {
-          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk8, kb8, o, 0));
+          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk8, o, 0, 0));
           r.k[i] = u32x4{x[0], x[1], 0u, 0u};
         }
       }
 #pragma unroll
       for (int db = 0; db < ND; ++db) {   // keys 16g .. 16g+15 of V^T row 16 db + l16: one 16-byte load
         const u32x4 x = as<u32x4>(
-            __builtin_amdgcn_raw_buffer_load_b128(rv8, vb8, so + static_cast<uint32_t>(db * 1024), 0));
+            __builtin_amdgcn_raw_buffer_load_b128(rv8, vv + static_cast<uint32_t>(db * 1024), 0, 0));
         r.v[2 * db] = u32x2{x[0], x[1]};
         r.v[2 * db + 1] = u32x2{x[2], x[3]};
       }
       r.sk[0] = sload(ks8, static_cast<size_t>(j) * hkv);
       r.sv[0] = sload(vs8, static_cast<size_t>(j) * hkv);
     } else {
-      const uint32_t so = static_cast<uint32_t>(j) * hkv * (kBlock * D / 2);
+      const bool two = valid && j + 1 < dl.nb;
+      const uint32_t so0 = valid ? static_cast<uint32_t>(j) * hkv * (kBlock * D / 2) : kNone;
+      const uint32_t so1 = two ? static_cast<uint32_t>(j + 1) * hkv * (kBlock * D / 2) : kNone;
+      const uint32_t vk0 = kb4 + so0, vk1 = kb4 + so1, vv0 = vb4 + so0, vv1 = vb4 + so1;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t o = so + static_cast<uint32_t>(i >> 2) * hkv * (kBlock * D / 2) + static_cast<uint32_t>(dsig(i & 3, 0) * (D / 2));
+        const uint32_t o = ((i >> 2) ? vk1 : vk0) + static_cast<uint32_t>(dsig(i & 3, 0) * (D / 2));
         if constexpr (KW == 16) {
-          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk4, kb4, o, 0));
+          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk4, o, 0, 0));
         } else {
-          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk4, kb4, o, 0));
+          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk4, o, 0, 0));
           r.k[i] = u32x4{x[0], x[1], 0u, 0u};
         }
       }
 #pragma unroll
       for (int i = 0; i < 2 * ND; ++i)
         r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(
-            rv4, vb4, so + static_cast<uint32_t>(i & 1) * hkv * (kBlock * D / 2) + static_cast<uint32_t>((i >> 1) * 512), 0));
-      const int j1 = j + 1 < dl.nb ? j + 1 : j;
+            rv4, ((i & 1) ? vv1 : vv0) + static_cast<uint32_t>((i >> 1) * 512), 0, 0));
+      const int j1 = two ? j + 1 : j;
       r.sk[0] = sload(ks4, static_cast<size_t>(j) * hkv);
       r.sv[0] = sload(vs4, static_cast<size_t>(j) * hkv);
       r.sk[1] = sload(ks4, static_cast<size_t>(j1) * hkv);
@@ -379,16 +391,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     q_operand(!decltype(tag)::value, qop);
     Regs ra, rb;
     int e = ea;
-    load(e, tag, ra);
+    load(e, true, tag, ra);
     while (true) {
       const int na = min(U, eb - e), e2 = e + na;
-      if (e2 < eb) load(e2, tag, rb);
+      load(e2, e2 < eb, tag, rb);
       compute(ra, tag, 0, jof(e), qop);
       if (na == 2) compute(ra, tag, 1, jof(e + 1), qop);
       e = e2;
       if (e >= eb) break;
       const int nb2 = min(U, eb - e), e3 = e + nb2;
-      if (e3 < eb) load(e3, tag, ra);
+      load(e3, e3 < eb, tag, ra);
       compute(rb, tag, 0, jof(e), qop);
       if (nb2 == 2) compute(rb, tag, 1, jof(e + 1), qop);
       e = e3;
@@ -414,34 +426,50 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
     for (int i = 0; i < 4; ++i) oacc[db][i] = (oacc[db][i] - ocorr[i]) * kTwo24;
 
-  // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy
-  f16x8 qop[NC];
-  if (eF < e1) q_operand(false, qop);
-  for (int e = eF; e < e1; ++e) {
-    const int j = dl.block(e);
-    const size_t kblk = kvb0 + static_cast<size_t>(j) * hkv;
-    f32x4 acc[4];
+  // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy, all of a
+  // block's loads issued before its first product; key rows at or past L
+  // fall outside the K range and read as zeros (their scores are dropped)
+  if (eF < e1) {
+    f16x8 qop[NC];
+    q_operand(false, qop);
+    const uint32_t pitch = hkv * (D * 2);   // bytes between key rows of k16
+    const __amdgpu_buffer_rsrc_t rk16 =
+        make_rsrc(a.k16 + (static_cast<size_t>(tok0) * hkv + kv) * D, static_cast<uint32_t>(L - 1) * pitch + D * 2);
+    const __amdgpu_buffer_rsrc_t rt16 = make_rsrc(a.vt16 + kvb0 * (D * kBlock), span * (D * kBlock * 2));
+    for (int e = eF; e < e1; ++e) {
+      const int j = dl.block(e);
+      u32x4 kraw[4][NC], vraw[ND][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = j * kBlock + dsig(kb, l16);   // K row of this lane (MFMA row l16)
-      const uint16_t* src = a.k16 + (static_cast<size_t>(tok0 + (key < L ? key : 0)) * a.hkv + kv) * D + DG * g;
-      acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint32_t row = static_cast<uint32_t>(j * kBlock + dsig(kb, l16));   // K row of MFMA row l16
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        u32x4 raw = key < L ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0, 0, 0, 0};
-        acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(to_f16x8<BF16>(raw), qop[c], acc[kb], 0, 0, 0);
+        for (int c = 0; c < NC; ++c)
+          kraw[kb][c] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(
+              rk16, row * pitch + static_cast<uint32_t>((DG * g + 8 * c) * 2), 0, 0));
       }
+      const uint32_t vo = static_cast<uint32_t>(j) * hkv * (D * kBlock * 2) + static_cast<uint32_t>(l16 * kBlock * 2 + 32 * g);
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)   // V^T row 16 db + l16, keys 16g + 8c2 ..
+          vraw[db][c2] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(
+              rt16, vo + static_cast<uint32_t>(db * 16 * kBlock * 2 + 16 * c2), 0, 0));
+      f32x4 acc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(to_f16x8<BF16>(kraw[kb][c]), qop[c], acc[kb], 0, 0, 0);
+      }
+      f16x8 pb[2];
+      softmax(acc, a.tau_log2e, 0.0f, 1.0f, j, pb);
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as<f16x8>(vraw[db][c2]), pb[c2], oacc[db], 0, 0, 0);
     }
-    f16x8 pb[2];
-    softmax(acc, a.tau_log2e, 0.0f, 1.0f, j, pb);
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int d = db * 16 + l16;
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(a.vt16 + (kblk * D + d) * kBlock + 16 * g + 8 * c2);
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as<f16x8>(raw), pb[c2], oacc[db], 0, 0, 0);
-      }
   }
 
   // ---- the split's (m, l, O) per query head

@@ -321,8 +321,8 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   for (int b = 0; b < cache->nseq; ++b) {
     const int64_t len = cache->cu_seqlens[b + 1] - cache->cu_seqlens[b];
     if (len < 1) return TM_E_SHAPE;
-    // a sequence's blocks of one KV head must lie within 2 GiB of its first (32-bit offsets)
-    if ((len + 63) / 64 * cache->hkv * 64 * cache->d >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
+    // a sequence's 16-bit rows (and fp16 V copy) must lie within 2 GiB of its first (32-bit offsets)
+    if ((len + 63) / 64 * cache->hkv * 64 * cache->d * 2 >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
   }
   const DecodePlan plan = decode_plan(cache, policy);
   if (ws == nullptr) {

@@ -61,15 +61,15 @@ struct PrefillArgs {
 struct DecodeArgs {
   const uint16_t* q;       // [B][hq][D] 16-bit
   const int32_t* cu;
-  const int8_t* k8;        // rows  [hkv][nblk][64][D]
-  const uint8_t* k4;       // rows  [hkv][nblk][64][D/2]
+  const int8_t* k8;        // rows  [nblk][hkv][64][D]
+  const uint8_t* k4;       // rows  [nblk][hkv][64][D/2]
   const float* ks8;
   const float* ks4;
-  const int8_t* v8;        // cols  [hkv][nblk][D][64]
-  const uint8_t* v4;       // cols  [hkv][nblk][D][32]
+  const int8_t* v8;        // cols  [nblk][hkv][D][64]
+  const uint8_t* v4;       // cols  [nblk][hkv][D][32]
   const float* vs8;
   const float* vs4;
-  const uint16_t* vt16;    // cols  [hkv][nblk][D][64] fp16
+  const uint16_t* vt16;    // cols  [nblk][hkv][D][64] fp16
   const uint16_t* k16;     // [T][hkv][D] 16-bit
   float* ws;               // [B][hq][nsplit][D + 2]
   void* o;
