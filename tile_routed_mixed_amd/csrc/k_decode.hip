@@ -75,19 +75,26 @@ __device__ __forceinline__ T as(const S& s) {
   return t;
 }
 
+// Relative cost of one cache block in a split, as measured on MI355X: an
+// INT4 block (half the bytes of an INT8 block, but the same MFMA and softmax
+// work) costs about 0.85 of an INT8 block; an FP16 block (twice the bytes,
+// loaded without look-ahead at the end of a split) about 3.
+constexpr int kW4 = 17, kW8 = 20, kW16 = 60;
+
 // Cache blocks of one (sequence, KV head), in the order a split walks them:
 // the sink block (when it lies outside the band), then blocks jstart .. nb-1
 // in ascending order: the INT4 band, the INT8 band, then the FP16 window.
+// Splits take contiguous runs of equal cost.
 struct DecodeList {
   int nb, jstart, jf, b8, sink, sink_extra, n_ex;
   __device__ __forceinline__ int block(int e) const {
     return sink_extra ? (e == 0 ? 0 : jstart + e - 1) : jstart + e;
   }
-  // HBM cost of entries [0, e) in units of an INT4 block (INT8 2, FP16 4)
+  // cost of entries [0, e) in the units of kW4 / kW8 / kW16
   __device__ __forceinline__ int64_t weight(int e) const {
     int64_t wsum = 0;
     if (sink_extra && e > 0) {
-      wsum += 2;
+      wsum += kW8;
       --e;
     }
     const int hi = jstart + e;                        // blocks [jstart, hi)
@@ -99,7 +106,7 @@ struct DecodeList {
       ++n8;
       --n4;
     }
-    return wsum + 2 * n8 + n4 + 4 * n16;
+    return wsum + kW8 * n8 + kW4 * n4 + kW16 * n16;
   }
   // first entry e with weight(e) * parts >= total * c
   __device__ __forceinline__ int split(int c, int parts) const {
@@ -154,15 +161,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int grp = a.hq / a.hkv;
 
+  // this sequence's extent (kernel-argument tables: scalar loads)
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
-  const int blk0 = __builtin_amdgcn_readfirstlane(seq_blk_start(a.cu, b));
+  const int blk0 = a.blk[b];
   DecodeList dl;
   dl.nb = (L + kBlock - 1) / kBlock;
-  dl.b8 = __builtin_amdgcn_readfirstlane(a.b8[kv]);
+  dl.b8 = a.b8[kv];
   dl.sink = a.sink;
   dl.jf = a.tail > 0 ? max(0, (L - a.tail) / kBlock) : dl.nb;                                    // first FP16 block
-  dl.jstart = min(max(0, dl.nb - __builtin_amdgcn_readfirstlane(a.b4[kv])), dl.jf);             // delta < b4
+  dl.jstart = min(max(0, dl.nb - a.b4[kv]), dl.jf);             // delta < b4
   dl.sink_extra = (a.sink && dl.jstart > 0) ? 1 : 0;
   dl.n_ex = (dl.nb - dl.jstart) + dl.sink_extra;
   const int e0 = dl.split(split, a.nsplit), e1 = dl.split(split + 1, a.nsplit);
@@ -188,19 +196,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       qop[c] = to_f16x8<BF16>(raw);
     }
   };
+  // qsum: sum over all d channels of the head's q (either channel map holds
+  // each channel once per lane column), taken from the first phase's operand
   float qsum = 0.0f;
-  {
-    f16x8 qop[NC];
-    q_operand(false, qop);
+  bool have_qsum = false;
+  auto take_qsum = [&](const f16x8 (&qop)[NC]) {
+    float t = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qsum += static_cast<float>(qop[c][e]);
-    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(qsum), __float_as_uint(qsum), false, false);
-    qsum = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(qsum), __float_as_uint(qsum), false, false);
+      for (int e = 0; e < 8; ++e) t += static_cast<float>(qop[c][e]);
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    t = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
     qsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-  }
+    have_qsum = true;
+  };
 
   // buffer resources over this (sequence, KV head)'s blocks (a unit's second
   // INT4 block may lie past the last block: such loads return zeros and the
@@ -387,11 +398,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   auto phase = [&](auto tag, int ea, int eb) {
     constexpr int U = decltype(tag)::value ? 2 : 1;   // blocks per unit
     if (ea >= eb) return;
-    f16x8 qop[NC];
-    q_operand(!decltype(tag)::value, qop);
     Regs ra, rb;
     int e = ea;
-    load(e, true, tag, ra);
+    load(e, true, tag, ra);   // the first unit's loads go out before q is read
+    f16x8 qop[NC];
+    q_operand(!decltype(tag)::value, qop);
+    if (!have_qsum) take_qsum(qop);
     while (true) {
       const int na = min(U, eb - e), e2 = e + na;
       load(e2, e2 < eb, tag, rb);

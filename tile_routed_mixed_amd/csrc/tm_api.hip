@@ -337,7 +337,6 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = static_cast<const uint16_t*>(q);
-  a.cu = cache->cu_seqlens_dev;
   a.k8 = kq->c8;
   a.k4 = kq->c4;
   a.ks8 = kq->s8;
@@ -363,8 +362,26 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     a.b8[g] = policy->b8[g];
     a.b4[g] = policy->b4[g];
   }
-  const hipError_t e = launch_decode(a, cache->d, cache->dtype == TM_BF16, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? TM_OK : TM_E_HIP;
+  // launches of at most kMaxSeqArg sequences, each with its sequences'
+  // offsets in the kernel arguments
+  const size_t osz = o_dtype == TM_F32 ? 4 : 2;
+  int64_t blk = 0;
+  for (int s0 = 0; s0 < cache->nseq; s0 += kMaxSeqArg) {
+    const int n = std::min(kMaxSeqArg, cache->nseq - s0);
+    DecodeArgs c = a;
+    c.nseq = n;
+    for (int i = 0; i <= n; ++i) c.cu[i] = cache->cu_seqlens[s0 + i];
+    for (int i = 0; i < n; ++i) {
+      c.blk[i] = static_cast<int32_t>(blk);
+      blk += (cache->cu_seqlens[s0 + i + 1] - cache->cu_seqlens[s0 + i] + 63) / 64;
+    }
+    c.q = a.q + static_cast<size_t>(s0) * cache->hq * cache->d;
+    c.o = static_cast<uint8_t*>(o) + static_cast<size_t>(s0) * cache->hq * cache->d * osz;
+    c.ws = a.ws + static_cast<size_t>(s0) * cache->hq * plan.nsplit * (cache->d + 2);
+    const hipError_t e = launch_decode(c, cache->d, cache->dtype == TM_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return TM_E_HIP;
+  }
+  return TM_OK;
 }
 
 }  // extern "C"

@@ -7,6 +7,7 @@ namespace tmx {
 
 constexpr int kMaxHeadsArg = 256;   // boundary tables passed by value
 constexpr int kMaxKvArg = 64;
+constexpr int kMaxSeqArg = 128;    // sequences per decode launch (tables passed by value)
 
 struct QuantArgs {
   const uint16_t* x;
@@ -60,7 +61,6 @@ struct PrefillArgs {
 
 struct DecodeArgs {
   const uint16_t* q;       // [B][hq][D] 16-bit
-  const int32_t* cu;
   const int8_t* k8;        // rows  [nblk][hkv][64][D]
   const uint8_t* k4;       // rows  [nblk][hkv][64][D/2]
   const float* ks8;
@@ -79,6 +79,8 @@ struct DecodeArgs {
   float tau_log2e;
   int32_t b8[kMaxKvArg];
   int32_t b4[kMaxKvArg];
+  int32_t cu[kMaxSeqArg + 1];   // token offsets of this launch's sequences (absolute)
+  int32_t blk[kMaxSeqArg];      // their first cache block (absolute)
 };
 
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
