@@ -75,56 +75,6 @@ __device__ __forceinline__ T as(const S& s) {
   return t;
 }
 
-// Relative cost of one cache block in a split, as measured on MI355X: an
-// INT4 block (half the bytes of an INT8 block, but the same MFMA and softmax
-// work) costs about 0.85 of an INT8 block; an FP16 block (twice the bytes,
-// loaded without look-ahead at the end of a split) about 3.
-constexpr int kW4 = 17, kW8 = 20, kW16 = 60;
-
-// Cache blocks of one (sequence, KV head), in the order a split walks them:
-// the sink block (when it lies outside the band), then blocks jstart .. nb-1
-// in ascending order: the INT4 band, the INT8 band, then the FP16 window.
-// Splits take contiguous runs of equal cost.
-struct DecodeList {
-  int nb, jstart, jf, b8, sink, sink_extra, n_ex;
-  __device__ __forceinline__ int block(int e) const {
-    return sink_extra ? (e == 0 ? 0 : jstart + e - 1) : jstart + e;
-  }
-  // cost of entries [0, e) in the units of kW4 / kW8 / kW16
-  __device__ __forceinline__ int64_t weight(int e) const {
-    int64_t wsum = 0;
-    if (sink_extra && e > 0) {
-      wsum += kW8;
-      --e;
-    }
-    const int hi = jstart + e;                        // blocks [jstart, hi)
-    const int qend = min(hi, jf);                     // quantized part [jstart, qend)
-    const int n16 = max(0, hi - max(jf, jstart));
-    int n8 = max(0, qend - max(jstart, nb - b8));
-    int n4 = max(0, qend - jstart) - n8;
-    if (sink && jstart == 0 && qend > 0 && nb - b8 > 0) {   // block 0 inside the INT4 range is INT8
-      ++n8;
-      --n4;
-    }
-    return wsum + kW8 * n8 + kW4 * n4 + kW16 * n16;
-  }
-  // first entry e with weight(e) * parts >= total * c
-  __device__ __forceinline__ int split(int c, int parts) const {
-    const int64_t target = weight(n_ex) * c;
-    int lo = 0, hi = n_ex;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (weight(mid) * parts >= target) hi = mid;
-      else lo = mid + 1;
-    }
-    return lo;
-  }
-  // list index of the first FP16 block (n_ex if none)
-  __device__ __forceinline__ int first_fp16() const {
-    return jf < nb ? (sink_extra ? 1 : 0) + (jf - jstart) : n_ex;
-  }
-};
-
 // Key that feeds MFMA row m of 16-key block kb (kb = 0..3 of a 64-key cache
 // block): lane group g of every block kb holds keys 16g + 4kb + i, so a lane
 // group owns keys 16g .. 16g+15 of the block, and for the 32-key chunk c2 of
@@ -165,16 +115,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
   const int blk0 = a.blk[b];
-  DecodeList dl;
-  dl.nb = (L + kBlock - 1) / kBlock;
-  dl.b8 = a.b8[kv];
-  dl.sink = a.sink;
-  dl.jf = a.tail > 0 ? max(0, (L - a.tail) / kBlock) : dl.nb;                                    // first FP16 block
-  dl.jstart = min(max(0, dl.nb - a.b4[kv]), dl.jf);             // delta < b4
-  dl.sink_extra = (a.sink && dl.jstart > 0) ? 1 : 0;
-  dl.n_ex = (dl.nb - dl.jstart) + dl.sink_extra;
-  const int e0 = dl.split(split, a.nsplit), e1 = dl.split(split + 1, a.nsplit);
-  const int eF = max(e0, min(e1, dl.first_fp16()));                                             // quantized: [e0, eF)
+  // this KV head's bands, in 64-token blocks
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int jf = a.tail > 0 ? max(0, (L - a.tail) / kBlock) : nb;    // FP16 window [jf, nb)
+  const int jst = min(max(0, nb - a.b4[kv]), jf);                    // delta < b4 from here
+  const int j8lo = min(max(jst, nb - a.b8[kv]), jf);                 // INT8 band [j8lo, jf)
+  const bool sinkb = a.sink && j8lo > 0;                             // block 0 INT8, ahead of the bands
+  const int j4lo = (sinkb && jst == 0) ? 1 : jst;                    // INT4 band [j4lo, j8lo)
+  // Each split takes an even share of the INT4 band and an even share of the
+  // rest ([j8lo, nb): the INT8 band, then the FP16 window, whose blocks count
+  // as kW16 INT8 blocks: twice the bytes, read without look-ahead), so every
+  // split carries the same mix of work; split 0 also takes the sink.
+  constexpr int kW16 = 3;
+  const int ns = a.nsplit;
+  const int i4a = j4lo + (j8lo - j4lo) * split / ns, i4b = j4lo + (j8lo - j4lo) * (split + 1) / ns;
+  const int n8 = jf - j8lo, wt = n8 + kW16 * (nb - jf);
+  auto tail_at = [&](int s) {   // first tail entry of split s: INT8 entries [0, n8), then FP16
+    const int t = wt * s / ns;
+    return t <= n8 ? t : n8 + (t - n8 + kW16 - 1) / kW16;
+  };
+  const int ta = tail_at(split), tb = tail_at(split + 1);
+  const int i8a = j8lo + min(ta, n8), i8b = j8lo + min(tb, n8);         // INT8 blocks
+  const int ifa = jf + max(ta - n8, 0), ifb = jf + max(tb - n8, 0);     // FP16 blocks
   // codes and scales are block-major ([nblk][hkv]...): cache block j of this
   // (sequence, KV head) is entry kvb0 + j * hkv
   const size_t kvb0 = static_cast<size_t>(blk0) * a.hkv + kv;
@@ -216,7 +178,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // buffer resources over this (sequence, KV head)'s blocks (a unit's second
   // INT4 block may lie past the last block: such loads return zeros and the
   // block is not computed)
-  const uint32_t span = static_cast<uint32_t>(max(dl.nb, 1) - 1) * hkv + 1;   // entries kvb0 .. last block
+  const uint32_t span = static_cast<uint32_t>(max(nb, 1) - 1) * hkv + 1;   // entries kvb0 .. last block
   const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(a.k8 + kvb0 * (kBlock * D), span * (kBlock * D));
   const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(a.v8 + kvb0 * (kBlock * D), span * (kBlock * D));
   const __amdgpu_buffer_rsrc_t rk4 = make_rsrc(a.k4 + kvb0 * (kBlock * D / 2), span * (kBlock * D / 2));
@@ -230,24 +192,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const uint32_t vb8 = static_cast<uint32_t>(l16 * 64 + 16 * g);
   const uint32_t vb4 = static_cast<uint32_t>(l16 * 32 + 8 * g);
 
-  // list entry e -> cache block j; quantized entries are INT4 or INT8, and a
-  // unit is one INT8 block or up to two consecutive INT4 blocks
-  const int eS = dl.sink_extra;
-  const int j4hi = min(dl.nb - dl.b8, dl.jf);
-  auto jof = [&](int e) { return e < eS ? 0 : dl.jstart + (e - eS); };
-
-  // Start loading the unit at entry e (an INT4 pair when FOUR) into r.  The
-  // unit's byte offset rides in the per-lane offset, so that a unit that does
-  // not exist (valid false, or the second block of an INT4 pair past the
-  // sequence end) sits at kNone, beyond every buffer range, and its loads
-  // return zeros without touching memory.  Every unit is loaded by the same
-  // instruction sequence, whether or not it exists: the loads never sit under
-  // a branch, so the count of loads in flight is the same on every path and
-  // computing one unit waits only for that unit's loads.
+  // Start loading the unit at block j (an INT4 pair j, j+1 when FOUR, the
+  // pair ending before jend) into r.  The unit's byte offset rides in the
+  // per-lane offset, so that a unit that does not exist (valid false, or the
+  // second block of an INT4 pair at jend) sits at kNone, beyond every buffer
+  // range, and its loads return zeros without touching memory.  Every unit is
+  // loaded by the same instruction sequence, whether or not it exists: the
+  // loads never sit under a branch, so the count of loads in flight is the
+  // same on every path and computing one unit waits only for that unit's
+  // loads.
   constexpr uint32_t kNone = 0x80000000u;
-  auto load = [&](int e, bool valid, auto tag, Regs& r) {
+  auto load = [&](int jj, bool valid, int jend, auto tag, Regs& r) {
     constexpr bool FOUR = decltype(tag)::value;
-    const int j = valid ? jof(e) : 0;
+    const int j = valid ? jj : 0;
     if constexpr (!FOUR) {
       const uint32_t so = valid ? static_cast<uint32_t>(j) * hkv * (kBlock * D) : kNone;
       const uint32_t vk = kb8 + so, vv = vb8 + so;
@@ -271,7 +228,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       r.sk[0] = sload(ks8, static_cast<size_t>(j) * hkv);
       r.sv[0] = sload(vs8, static_cast<size_t>(j) * hkv);
     } else {
-      const bool two = valid && j + 1 < dl.nb;
+      const bool two = valid && j + 1 < jend;
       const uint32_t so0 = valid ? static_cast<uint32_t>(j) * hkv * (kBlock * D / 2) : kNone;
       const uint32_t so1 = two ? static_cast<uint32_t>(j + 1) * hkv * (kBlock * D / 2) : kNone;
       const uint32_t vk0 = kb4 + so0, vk1 = kb4 + so1, vv0 = vb4 + so0, vv1 = vb4 + so1;
@@ -392,45 +349,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   };
 
   // ---- quantized units, registers double-buffered: the next unit's loads are
-  // in flight while the current one is computed.  The list runs in three
-  // phases of one precision each (sink block, INT4 band, INT8 band), so the
-  // loads and the dequantization are specialized per phase.
-  auto phase = [&](auto tag, int ea, int eb) {
+  // in flight while the current one is computed.  A split runs up to three
+  // phases of one precision each (sink block, its INT4 share, its INT8
+  // share), so the loads and the dequantization are specialized per phase.
+  auto phase = [&](auto tag, int ja, int jb) {
     constexpr int U = decltype(tag)::value ? 2 : 1;   // blocks per unit
-    if (ea >= eb) return;
+    if (ja >= jb) return;
     Regs ra, rb;
-    int e = ea;
-    load(e, true, tag, ra);   // the first unit's loads go out before q is read
+    int j = ja;
+    load(j, true, jb, tag, ra);   // the first unit's loads go out before q is read
     f16x8 qop[NC];
     q_operand(!decltype(tag)::value, qop);
     if (!have_qsum) take_qsum(qop);
     while (true) {
-      const int na = min(U, eb - e), e2 = e + na;
-      load(e2, e2 < eb, tag, rb);
-      compute(ra, tag, 0, jof(e), qop);
-      if (na == 2) compute(ra, tag, 1, jof(e + 1), qop);
-      e = e2;
-      if (e >= eb) break;
-      const int nb2 = min(U, eb - e), e3 = e + nb2;
-      load(e3, e3 < eb, tag, ra);
-      compute(rb, tag, 0, jof(e), qop);
-      if (nb2 == 2) compute(rb, tag, 1, jof(e + 1), qop);
-      e = e3;
-      if (e >= eb) break;
+      const int na = min(U, jb - j), j2 = j + na;
+      load(j2, j2 < jb, jb, tag, rb);
+      __builtin_amdgcn_sched_barrier(0);   // the next unit's loads go out before this unit's math
+      compute(ra, tag, 0, j, qop);
+      if (na == 2) compute(ra, tag, 1, j + 1, qop);
+      j = j2;
+      if (j >= jb) break;
+      const int nb2 = min(U, jb - j), j3 = j + nb2;
+      load(j3, j3 < jb, jb, tag, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(rb, tag, 0, j, qop);
+      if (nb2 == 2) compute(rb, tag, 1, j + 1, qop);
+      j = j3;
+      if (j >= jb) break;
     }
   };
   {
-    // list entries [0, lead) are INT8 (the sink), then the INT4 band [e4lo,
-    // e4hi), then INT8 up to the FP16 window
-    const bool sink0 = dl.sink && dl.jstart == 0 && j4hi > 0;   // block 0 heads the band but is INT8
-    const int lead = sink0 ? 1 : eS;
-    const int n4 = max(0, j4hi - dl.jstart - (sink0 ? 1 : 0));
-    const int e4lo = lead, e4hi = lead + n4;
     typedef std::integral_constant<bool, false> Int8;
     typedef std::integral_constant<bool, true> Int4;
-    phase(Int8{}, max(e0, 0), min(eF, lead));
-    phase(Int4{}, max(e0, e4lo), min(eF, e4hi));
-    phase(Int8{}, max(e0, e4hi), eF);
+    if (sinkb && split == 0) phase(Int8{}, 0, 1);
+    phase(Int4{}, i4a, i4b);
+    phase(Int8{}, i8a, i8b);
   }
   // back to value units: O = 2^24 (O' - offsets)
 #pragma unroll
@@ -441,15 +394,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy, all of a
   // block's loads issued before its first product; key rows at or past L
   // fall outside the K range and read as zeros (their scores are dropped)
-  if (eF < e1) {
+  if (ifa < ifb) {
     f16x8 qop[NC];
     q_operand(false, qop);
     const uint32_t pitch = hkv * (D * 2);   // bytes between key rows of k16
     const __amdgpu_buffer_rsrc_t rk16 =
         make_rsrc(a.k16 + (static_cast<size_t>(tok0) * hkv + kv) * D, static_cast<uint32_t>(L - 1) * pitch + D * 2);
     const __amdgpu_buffer_rsrc_t rt16 = make_rsrc(a.vt16 + kvb0 * (D * kBlock), span * (D * kBlock * 2));
-    for (int e = eF; e < e1; ++e) {
-      const int j = dl.block(e);
+    for (int j = ifa; j < ifb; ++j) {
       u32x4 kraw[4][NC], vraw[ND][2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
