@@ -148,13 +148,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // (D/2) h + KW g + 8 sub .. with c = h (KW/8) + sub, so the four lane groups
   // of a row read one contiguous span per load.  qsum: the head's sum of q
   // (for the code offsets).
-  const bool qok = l16 < grp;
-  const uint16_t* const qrow = a.q + (static_cast<size_t>(b) * a.hq + kv * grp + (qok ? l16 : 0)) * D;
+  // (rows past the group lie outside the resource and read as zeros)
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(a.q + (static_cast<size_t>(b) * a.hq + kv * grp) * D, static_cast<uint32_t>(grp * D * 2));
   auto q_operand = [&](bool map8, f16x8 (&qop)[NC]) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int ch = map8 ? (D / 2) * (c / (KW / 8)) + KW * g + 8 * (c % (KW / 8)) : DG * g + 8 * c;
-      u32x4 raw = qok ? *reinterpret_cast<const u32x4*>(qrow + ch) : u32x4{0, 0, 0, 0};
+      const u32x4 raw = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rq, static_cast<uint32_t>((l16 * D + ch) * 2), 0, 0));
       qop[c] = to_f16x8<BF16>(raw);
     }
   };
@@ -179,10 +180,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // INT4 block may lie past the last block: such loads return zeros and the
   // block is not computed)
   const uint32_t span = static_cast<uint32_t>(max(nb, 1) - 1) * hkv + 1;   // entries kvb0 .. last block
-  const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(a.k8 + kvb0 * (kBlock * D), span * (kBlock * D));
-  const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(a.v8 + kvb0 * (kBlock * D), span * (kBlock * D));
-  const __amdgpu_buffer_rsrc_t rk4 = make_rsrc(a.k4 + kvb0 * (kBlock * D / 2), span * (kBlock * D / 2));
-  const __amdgpu_buffer_rsrc_t rv4 = make_rsrc(a.v4 + kvb0 * (kBlock * D / 2), span * (kBlock * D / 2));
+  const int8_t* const k8p = pin_sgpr(a.k8 + kvb0 * (kBlock * D));
+  const int8_t* const v8p = pin_sgpr(a.v8 + kvb0 * (kBlock * D));
+  const uint8_t* const k4p = pin_sgpr(a.k4 + kvb0 * (kBlock * D / 2));
+  const uint8_t* const v4p = pin_sgpr(a.v4 + kvb0 * (kBlock * D / 2));
   const float* const ks8 = pin_sgpr(a.ks8 + kvb0);
   const float* const vs8 = pin_sgpr(a.vs8 + kvb0);
   const float* const ks4 = pin_sgpr(a.ks4 + kvb0);
@@ -193,64 +194,68 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const uint32_t vb4 = static_cast<uint32_t>(l16 * 32 + 8 * g);
 
   // Start loading the unit at block j (an INT4 pair j, j+1 when FOUR, the
-  // pair ending before jend) into r.  The unit's byte offset rides in the
-  // per-lane offset, so that a unit that does not exist (valid false, or the
-  // second block of an INT4 pair at jend) sits at kNone, beyond every buffer
-  // range, and its loads return zeros without touching memory.  Every unit is
-  // loaded by the same instruction sequence, whether or not it exists: the
-  // loads never sit under a branch, so the count of loads in flight is the
-  // same on every path and computing one unit waits only for that unit's
-  // loads.
-  constexpr uint32_t kNone = 0x80000000u;
+  // pair ending before jend) into r.  Each cache block of the unit gets a
+  // buffer resource of its own (scalar registers), sized 0 when the block
+  // does not exist (valid false, or the second block of an INT4 pair at
+  // jend), so its loads return zeros without touching memory; the per-lane
+  // offsets are loop-invariant and the piece offsets immediate, so no vector
+  // register is written between a unit's loads.  Every unit is loaded by the
+  // same instruction sequence, whether or not it exists: the loads never sit
+  // under a branch, so the count of loads in flight is the same on every path
+  // and computing one unit waits only for that unit's loads.
   auto load = [&](int jj, bool valid, int jend, auto tag, Regs& r) {
     constexpr bool FOUR = decltype(tag)::value;
     const int j = valid ? jj : 0;
+    const size_t jo = static_cast<size_t>(j) * hkv;   // entry offset of block j
     if constexpr (!FOUR) {
-      const uint32_t so = valid ? static_cast<uint32_t>(j) * hkv * (kBlock * D) : kNone;
-      const uint32_t vk = kb8 + so, vv = vb8 + so;
+      const uint32_t nr = valid ? kBlock * D : 0u;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k8p + jo * (kBlock * D), nr);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(v8p + jo * (kBlock * D), nr);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t o = vk + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * (D / 2));
+        const uint32_t o = kb8 + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * (D / 2));
         if constexpr (KW == 16) {
-          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk8, o, 0, 0));
+          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
         } else {
-          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk8, o, 0, 0));
+          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0));
           r.k[i] = u32x4{x[0], x[1], 0u, 0u};
         }
       }
 #pragma unroll
       for (int db = 0; db < ND; ++db) {   // keys 16g .. 16g+15 of V^T row 16 db + l16: one 16-byte load
         const u32x4 x = as<u32x4>(
-            __builtin_amdgcn_raw_buffer_load_b128(rv8, vv + static_cast<uint32_t>(db * 1024), 0, 0));
+            __builtin_amdgcn_raw_buffer_load_b128(rv, vb8 + static_cast<uint32_t>(db * 1024), 0, 0));
         r.v[2 * db] = u32x2{x[0], x[1]};
         r.v[2 * db + 1] = u32x2{x[2], x[3]};
       }
-      r.sk[0] = sload(ks8, static_cast<size_t>(j) * hkv);
-      r.sv[0] = sload(vs8, static_cast<size_t>(j) * hkv);
+      r.sk[0] = sload(ks8, jo);
+      r.sv[0] = sload(vs8, jo);
     } else {
       const bool two = valid && j + 1 < jend;
-      const uint32_t so0 = valid ? static_cast<uint32_t>(j) * hkv * (kBlock * D / 2) : kNone;
-      const uint32_t so1 = two ? static_cast<uint32_t>(j + 1) * hkv * (kBlock * D / 2) : kNone;
-      const uint32_t vk0 = kb4 + so0, vk1 = kb4 + so1, vv0 = vb4 + so0, vv1 = vb4 + so1;
+      const uint32_t nr0 = valid ? kBlock * D / 2 : 0u, nr1 = two ? kBlock * D / 2 : 0u;
+      const size_t jo1 = two ? jo + hkv : jo;
+      const __amdgpu_buffer_rsrc_t rk0 = make_rsrc(k4p + jo * (kBlock * D / 2), nr0);
+      const __amdgpu_buffer_rsrc_t rk1 = make_rsrc(k4p + jo1 * (kBlock * D / 2), nr1);
+      const __amdgpu_buffer_rsrc_t rv0 = make_rsrc(v4p + jo * (kBlock * D / 2), nr0);
+      const __amdgpu_buffer_rsrc_t rv1 = make_rsrc(v4p + jo1 * (kBlock * D / 2), nr1);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t o = ((i >> 2) ? vk1 : vk0) + static_cast<uint32_t>(dsig(i & 3, 0) * (D / 2));
+        const uint32_t o = kb4 + static_cast<uint32_t>(dsig(i & 3, 0) * (D / 2));
         if constexpr (KW == 16) {
-          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk4, o, 0, 0));
+          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128((i >> 2) ? rk1 : rk0, o, 0, 0));
         } else {
-          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk4, o, 0, 0));
+          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64((i >> 2) ? rk1 : rk0, o, 0, 0));
           r.k[i] = u32x4{x[0], x[1], 0u, 0u};
         }
       }
 #pragma unroll
       for (int i = 0; i < 2 * ND; ++i)
-        r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(
-            rv4, ((i & 1) ? vv1 : vv0) + static_cast<uint32_t>((i >> 1) * 512), 0, 0));
-      const int j1 = two ? j + 1 : j;
-      r.sk[0] = sload(ks4, static_cast<size_t>(j) * hkv);
-      r.sv[0] = sload(vs4, static_cast<size_t>(j) * hkv);
-      r.sk[1] = sload(ks4, static_cast<size_t>(j1) * hkv);
-      r.sv[1] = sload(vs4, static_cast<size_t>(j1) * hkv);
+        r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64((i & 1) ? rv1 : rv0,
+                                                                vb4 + static_cast<uint32_t>((i >> 1) * 512), 0, 0));
+      r.sk[0] = sload(ks4, jo);
+      r.sv[0] = sload(vs4, jo);
+      r.sk[1] = sload(ks4, jo1);
+      r.sv[1] = sload(vs4, jo1);
     }
   };
 
