@@ -253,11 +253,20 @@ def test_decode_small(seqlens, dpol, d, dtype):
     compare(o, O, what=f"decode {seqlens} {dtype}")
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(2, 2, 128), (6, 2, 128), (16, 2, 128), (16, 1, 64)])
+def test_decode_group_sizes(hq, hkv, d):
+    """Query groups of 1, 3, 8 and 16 heads per KV head: groups of up to 4
+    heads take the compacted softmax, larger ones the full-width one."""
+    dpol = dict(b8=[3] * hkv, b4=[11] * hkv, sink=1, tail=128)
+    o, O = _decode_case([700, 1900, 65], dpol, hq=hq, hkv=hkv, d=d)
+    compare(o, O, what=f"decode group {hq}/{hkv} d={d}")
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_decode_deterministic_long_splits(d):
-    """Splits that walk dozens of mixed INT4/INT8 blocks through the LDS ring
-    (the pipeline's wait counts decide correctness there): bitwise identical
-    over repeated calls, and within the gate against the oracle."""
+    """Splits that walk dozens of mixed INT4/INT8 blocks in a register
+    double buffer (the loads' wait counts decide correctness there): bitwise
+    identical over repeated calls, and within the gate against the oracle."""
     import torch
     import tile_routed_mixed_amd as T
     seqlens = [12000, 9000]

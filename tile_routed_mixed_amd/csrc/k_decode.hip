@@ -98,7 +98,24 @@ struct UnitRegs {
   float sk[2], sv[2];
 };
 
-template <int D, bool BF16>
+// Cross-lane moves within rows of 16 lanes (DPP): lane i of a row takes the
+// value of lane i - n (shr), i + n (shl) or (i - n) mod 16 (ror); lanes of
+// banks (groups of 4 lanes of a row) outside bank_mask keep `old`.
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_f(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANKS, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t src) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(src), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowShr = 0x110, kRowShl = 0x100, kRowRor = 0x120;
+
+// SMALLG: at most 4 query heads per KV head.  The QK product leaves head
+// l16's scores in lanes l16 < 4 only (16 values a lane); they are first moved
+// four to a lane, so that the softmax works on every lane and on a quarter of
+// the values.
+template <int D, bool BF16, bool SMALLG>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;          // k-chunks of the QK MFMA (lane group g owns channels DG*g ..)
   constexpr int ND = D / 16;          // output channel blocks
@@ -173,6 +190,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     t = __uint_as_float(x[0]) + __uint_as_float(x[1]);
     const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
     qsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    if constexpr (SMALLG) {   // the compacted softmax holds head l16 & 3 in lane l16
+      float qc = qsum;
+      qc = dpp_f<kRowShr + 4, 0x2>(qc, qsum);
+      qc = dpp_f<kRowShr + 8, 0x4>(qc, qsum);
+      qc = dpp_f<kRowShr + 12, 0x8>(qc, qsum);
+      qsum = qc;
+    }
     have_qsum = true;
   };
 
@@ -268,6 +292,59 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // lane), score = acc * m1 + m0; keys at index >= L are dropped.  Leaves the
   // fp16 P^T operands (p * sv) of the two 32-key chunks in pb.
   auto softmax = [&](const f32x4 (&acc)[4], float m1, float m0, float sv, int j, f16x8 (&pb)[2]) {
+    if constexpr (SMALLG) {
+      // lane (4a + h, g) takes head h's keys 16g + 4a + i (i = 0..3): the
+      // values acc[a][i] of lane (h, g)
+      const int a4 = l16 >> 2;
+      float c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = acc[0][i];
+        c[i] = dpp_f<kRowShr + 4, 0x2>(c[i], acc[1][i]);
+        c[i] = dpp_f<kRowShr + 8, 0x4>(c[i], acc[2][i]);
+        c[i] = dpp_f<kRowShr + 12, 0x8>(c[i], acc[3][i]);
+      }
+      const bool tail = j * kBlock + kBlock > L;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = __builtin_fmaf(c[i], m1, m0);
+        if (tail && j * kBlock + dsig(a4, 4 * g + i) >= L) c[i] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
+      mx = fmaxf(mx, dpp_f<kRowRor + 4, 0xF>(mx, mx));   // over the 4 banks of the row
+      mx = fmaxf(mx, dpp_f<kRowRor + 8, 0xF>(mx, mx));
+      {   // over the 4 rows (lane groups)
+        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+        const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+      }
+      const bool up = mx > m_run;
+      if (__any(up)) {
+        const float mn = up ? mx + 2.0f : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        m_run = mn;
+        l_run *= alpha;
+        ocorr *= alpha;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+      }
+      _Float16 ph[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(c[i] - m_run);
+        l_run += p;
+        ph[i] = static_cast<_Float16>(p * sv);
+      }
+      const uint32_t w0 = as<uint16_t>(ph[0]) | (static_cast<uint32_t>(as<uint16_t>(ph[1])) << 16);
+      const uint32_t w1 = as<uint16_t>(ph[2]) | (static_cast<uint32_t>(as<uint16_t>(ph[3])) << 16);
+      // back to the B-operand slices of lane (h, g): keys 16g + 8c2 + e live
+      // in lane 4 (2c2 + e/4) + h, value e % 4
+      pb[0] = as<f16x8>(u32x4{w0, w1, dpp_u<kRowShl + 4>(w0), dpp_u<kRowShl + 4>(w1)});
+      pb[1] = as<f16x8>(u32x4{dpp_u<kRowShl + 8>(w0), dpp_u<kRowShl + 8>(w1), dpp_u<kRowShl + 12>(w0),
+                              dpp_u<kRowShl + 12>(w1)});
+      return;
+    }
     float s[4][4];
     const bool tail = j * kBlock + kBlock > L;
 #pragma unroll
@@ -443,6 +520,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   // ---- the split's (m, l, O) per query head
   float lt = l_run;
+  if constexpr (SMALLG) {   // head h's sums sit in the 4 banks of every row
+    lt += dpp_f<kRowRor + 4, 0xF>(lt, lt);
+    lt += dpp_f<kRowRor + 8, 0xF>(lt, lt);
+  }
   {
     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
     lt = __uint_as_float(x[0]) + __uint_as_float(x[1]);
@@ -505,14 +586,21 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, bool BF16>
+static void launch_split(bool small, dim3 grid, const DecodeArgs& a, hipStream_t st) {
+  if (small) hipLaunchKernelGGL((decode_split_kernel<D, BF16, true>), grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((decode_split_kernel<D, BF16, false>), grid, dim3(64), 0, st, a);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st) {
   dim3 grid(a.nsplit, a.hkv, a.nseq);
+  const bool small = a.hq / a.hkv <= 4;
   if (d == 128) {
-    if (bf16) hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, dim3(64), 0, st, a);
+    if (bf16) launch_split<128, true>(small, grid, a, st);
+    else launch_split<128, false>(small, grid, a, st);
   } else {
-    if (bf16) hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, dim3(64), 0, st, a);
+    if (bf16) launch_split<64, true>(small, grid, a, st);
+    else launch_split<64, false>(small, grid, a, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
