@@ -185,6 +185,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-bench", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only run the decode sub-benchmark (16 x 32768-token cache) and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain elementwise copy of BYTES bytes (read BYTES, write BYTES) 5 times, "
                          "to scale HBM byte counters; prints nothing else")
@@ -198,6 +200,9 @@ def main():
             torch.neg(x, out=y)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
+        return
+    if args.decode_only:
+        print(json.dumps(decode_bench(max(5, args.steps))), flush=True)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
