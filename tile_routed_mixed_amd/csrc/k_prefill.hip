@@ -40,7 +40,6 @@
 //    so advancing the traversal needs no memory access;
 //  * workgroups are remapped so the 4 query heads of a GQA group run on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share K/V in L2.
-#include <atomic>
 #include <climits>
 
 #include "tm_kernels.h"
@@ -164,17 +163,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const TravHeader* th = reinterpret_cast<const TravHeader*>(a.trav);
   if (th->kind != static_cast<uint32_t>(KIND)) return;   // traversal of another policy kind
-
-  // Persistent workgroups: workgroup b takes virtual items b, 2G-1-b, 2G+b,
-  // 4G-1-b, ... (G workgroups, a multiple of 8, all resident), so the heavy
-  // first items and the light last ones pair up.  A virtual item keeps the
-  // XCD of the workgroup that runs it, and the 4 query heads of a GQA group
-  // (virtual items 8 apart in a chunk of 32) stay on one XCD.
-  for (uint32_t round = 0; round * gridDim.x < a.n_items; ++round) {
-  const uint32_t vitem = round * gridDim.x + ((round & 1) ? gridDim.x - 1 - blockIdx.x : blockIdx.x);
-  if (vitem >= a.n_items) continue;
-  __syncthreads();   // every wave is done with the previous item's tile buffers
-  const uint32_t item_idx = remap_block(vitem, a.n_items);
+  const uint32_t item_idx = remap_block(blockIdx.x, a.n_items);
   const ItemEntry it = reinterpret_cast<const ItemEntry*>(a.trav + th->item_off)[item_idx];
   const SeqEntry se = reinterpret_cast<const SeqEntry*>(a.trav + th->seq_off)[it.seq];
   const RunEntry* runs = reinterpret_cast<const RunEntry*>(a.trav + th->run_off) +
@@ -627,31 +616,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (a.lse != nullptr && g == 0)
       a.lse[static_cast<size_t>(head) * a.T + tok] = (m_use[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
   }
-  }   // items
-}
-
-// Workgroups of the persistent prefill: two per CU (the LDS and register
-// budget of one CU), rounded down to a multiple of 8 XCDs, at most one per item.
-static unsigned prefill_grid(uint32_t n_items) {
-  static std::atomic<int> cu_count[64];   // per device, 0 until first asked
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) cus = cu_count[dev].load(std::memory_order_relaxed);
-  if (cus <= 0) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (dev >= 0 && dev < 64) cu_count[dev].store(cus, std::memory_order_relaxed);
-  }
-  unsigned g = static_cast<unsigned>(2 * cus) & ~7u;
-  if (g == 0) g = 8;
-  return n_items < g ? n_items : g;
 }
 
 template <int D, int BQ, int KIND, bool BF16>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  const unsigned grid = prefill_grid(a.n_items);
   if (a.n_dbg > 0)
-    hipLaunchKernelGGL((prefill_kernel<D, BQ, KIND, BF16, true>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BQ, KIND, BF16, true>), dim3(a.n_items), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BQ, KIND, BF16, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BQ, KIND, BF16, false>), dim3(a.n_items), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
