@@ -201,6 +201,42 @@ def test_skipped_tiles_do_not_matter_on_gpu():
     assert not np.array_equal(o0[128:256], o1[128:256])
 
 
+def test_boundaries_all_int8_equals_zero_bitmask():
+    """Both policy encodings routing every legal tile to INT8 (boundaries
+    b8 = b4 = infinity; a bitmask of zeros) give the same census, and outputs
+    equal within the fp32 rounding of their different tile orders."""
+    w = W.small("varlen32k", [700, 64, 1, 1300], hq=4, hkv=2, dtype="f16")
+    q, k, v = _inputs(w)
+    big = 10 ** 6
+    pol_b = dict(kind=0, b8=[big] * w.hq, b4=[big] * w.hq, sink=0)
+    _, tot = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 4)
+    pol_m = dict(kind=1, group=4, words=np.zeros(tot, np.uint32))
+    _, cb, ob, lb, _ = run_prefill(w, pol_b, q, k, v)
+    _, cm, om, lm, _ = run_prefill(w, pol_m, q, k, v)
+    for key in ("legal", "int8", "int4", "fp16", "skip"):
+        assert cb[key] == cm[key], key
+    assert cb["int8"] == cb["legal"] and cb["skip"] == 0
+    compare(ob, om.astype(np.float64), lb, lm.astype(np.float64), what="all-INT8 encodings")
+
+
+def test_varlen_permutation_equivariance():
+    """Permuting the sequences of a varlen batch permutes the outputs: every
+    sequence's rows come out bit for bit the same."""
+    seqs = [700, 64, 1, 1300, 129]
+    perm = [3, 0, 4, 2, 1]
+    w = W.small("gqa8k", seqs, hq=8, hkv=2)
+    pol = dict(kind=0, b8=[1, 2, 3, 4, 1, 2, 3, 4], b4=[3, 5, 7, 9, 4, 6, 8, 10], sink=1)
+    q, k, v = _inputs(w)
+    cu = np.concatenate([[0], np.cumsum(seqs)])
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in perm])
+    wp = W.small("gqa8k", [seqs[s] for s in perm], hq=8, hkv=2)
+    qp, kp, vp = ((x[0][idx], x[1][idx]) for x in (q, k, v))
+    _, _, o, lse, _ = run_prefill(w, pol, q, k, v)
+    _, _, op, lsep, _ = run_prefill(wp, pol, qp, kp, vp)
+    assert np.array_equal(o[idx], op)
+    assert np.array_equal(lse[:, idx], lsep)
+
+
 def test_prefill_16bit_outputs():
     import tile_routed_mixed_amd as T
     w, pol = _case("boundaries_varlen")
