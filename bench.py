@@ -117,6 +117,42 @@ def cpu_baseline(w, q, k, v, pol, seconds):
                       f"{dt:.1f} s; attention rows only (codes precomputed); dense-causal FLOPs of those rows"}
 
 
+def decode_loop_bench(steps=64):
+    """Generation loop over the 16 x 32768-token workload: the caches start
+    `steps` tokens short of 32768 and every step decodes one query per
+    sequence, then appends that step's token (tm_cache_append for K and V,
+    the new rows already in device memory).  Returns time per step."""
+    import numpy as np
+    import torch
+    import tile_routed_mixed_amd as T
+    import workloads as W
+    from tile_routed_mixed_amd import _binding as B
+    w = W.get("decode16x32k")
+    dpol = W.make_decode_policy(w)
+    _, k, v = W.make_qkv(w)
+    dq = W.make_decode_query(w)
+    p = T.DecodePipeline(w.seqlens, w.hq, w.hkv, w.d, dpol, dtype=w.dtype)
+    p.upload(dq[0], k[0], v[0])
+    del k, v
+    L0 = np.array(w.seqlens, np.int64) - steps
+    p.start(L0)
+    torch.cuda.synchronize()
+    lens = [L0 + i for i in range(steps + 1)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        p.decode()
+        p.dpol.set_lengths(lens[i + 1])
+        B.tm_cache_append(p.shape, lens[i + 1], p.k, p.kq)
+        B.tm_cache_append(p.shape, lens[i + 1], p.v, p.vq)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    return {"workload": "decode16x32k generation loop: decode + K/V cache append per step, lengths "
+                        f"{int(L0[0])} -> {int(lens[-1][0])}", "steps": steps, "ms_per_step": ms,
+            "tokens_per_s": len(w.seqlens) / (ms * 1e-3)}
+
+
 def decode_bench(steps, rotate=3):
     """Decode over a 16 x 32768-token compressed cache; returns timing and bytes."""
     import numpy as np
@@ -295,6 +331,11 @@ def main():
         out["decode"] = d
         out["decode_kv_gbs"] = d["GBps"]
         log(f"[bench] decode {d['ms_mean']:.4f} ms, {d['GBps']:.1f} GB/s ({d['hbm_frac'] * 100:.1f} % of HBM)")
+        torch.cuda.empty_cache()
+        dl = decode_loop_bench()
+        out["decode_loop"] = dl
+        log(f"[bench] decode loop {dl['ms_per_step']:.4f} ms/step (decode + cache append), "
+            f"{dl['tokens_per_s']:.0f} tokens/s")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, pol, args.cpu_seconds)

@@ -162,6 +162,8 @@ typedef struct tm_dpolicy {
   const int32_t* b4;
   int32_t sink;
   int32_t tail_tokens;
+  const int32_t* lengths;   /* host [nseq] or NULL: current lengths, 1 <= lengths[s] <= the
+                               cache shape's length of s (its capacity); NULL: the capacity */
 } tm_dpolicy;
 
 /* Traversal buffer layout (device, written by tm_build_traversal, read by
@@ -253,17 +255,20 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
 
 /* Decode: one new query per sequence over the compressed cache.
  *  cache: shape of the cached sequences (nseq = batch, len = cache length L
- *    including the new token); dtype TM_F16 or TM_BF16 (type of q and k16;
+ *    including the new token, or the capacity of a growing cache whose
+ *    current lengths policy->lengths gives); dtype TM_F16 or TM_BF16 (type of q and k16;
  *    bf16 values are widened to fp16 for the MFMA, exact for magnitudes in
  *    [2^-14, 65504]); hq/hkv <= 16.
  *  q [nseq][hq][d] 16-bit (device).
  *  kq (TM_ROWS, hkv heads), vq (TM_COLS, hkv heads, t16 set): the cache, as
  *    produced by tm_quantize_pack over the cached tokens.
  *  k16 [T][hkv][d] 16-bit (device): keys read for FP16 blocks.
- *  policy: per-KV-head tags (tm_dpolicy).
+ *  policy: per-KV-head tags (tm_dpolicy); with lengths set, the tags and the
+ *    keys follow each sequence's current length.
  *  o [nseq][hq][d] of o_dtype (TM_F32 or TM_F16, device).
  *  ws (device): workspace; ws == NULL writes the required size to *ws_bytes
  *    and returns TM_OK without GPU work; otherwise *ws_bytes is its capacity.
+ *    The size depends on the cache shape (capacities), not on lengths.
  * INT blocks: score = scale * sk * (q . ck), value = sv * cv; FP16 blocks:
  * score = scale * (q . k), value = v ([HyQuant] "How HyQuant works":
  * dequantization fused with attention).
@@ -275,6 +280,26 @@ tm_status tm_decode(const tm_shape* cache, const void* q,
                     const tm_qtensor* kq, const tm_qtensor* vq, const void* k16,
                     const tm_dpolicy* policy, void* o, int32_t o_dtype,
                     void* ws, size_t* ws_bytes, void* stream);
+
+/* Cache append during generation ([TriAttention] abstract: the codes made
+ * during prefill are reused as the decode cache; [HyQuant] "How HyQuant
+ * works": the recent tokens stay FP16 and older ones are quantized).
+ *  cache: the cache shape with each sequence's capacity as its length (the
+ *    layout of the quantized tensors and of x's rows).
+ *  lengths (host [nseq]): current lengths after the append, 1 <= lengths[s]
+ *    <= capacity; the caller has written the new tokens' rows of x.
+ *  x [T][heads][d] 16-bit (device): K (out TM_ROWS) or V (out TM_COLS with
+ *    t16) in the capacity layout.
+ *  out: the cache tensor to update.
+ * For every sequence, the 64-token block holding its newest token is
+ * quantized again over the sequence's current length (the codes and scales
+ * tm_quantize_pack would give for that length; V's fp16 copy too), so after
+ * appending tokens one at a time the cache equals the one built from
+ * scratch at the new lengths.  One launch per 128 sequences.
+ * Errors: TM_E_ARG, TM_E_SHAPE (tensors not matching the shape, a length out
+ * of range), TM_E_HIP. */
+tm_status tm_cache_append(const tm_shape* cache, const int32_t* lengths, const void* x, int32_t heads,
+                          tm_qtensor* out, void* stream);
 
 #ifdef __cplusplus
 }

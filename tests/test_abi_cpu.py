@@ -226,3 +226,36 @@ def test_decode_validation_and_workspace(B):
     sz = _shape(B, [64, 0], hq=4, hkv=2, d=128)
     assert L.tm_decode(ctypes.byref(sz.c), None, None, None, None, ctypes.byref(dp2.c), None, 2, None,
                        ctypes.byref(n), None) == B.TM_E_SHAPE
+
+
+def test_growing_cache_validation(B):
+    """Lengths of a growing cache are checked against the capacities before any
+    GPU work: tm_decode through tm_dpolicy.lengths, tm_cache_append directly."""
+    L = B.lib()
+    s = _shape(B, [256, 100], hq=8, hkv=2, d=128)
+    n = ctypes.c_size_t(0)
+    dp = B.DPolicy(dict(b8=[1] * 2, b4=[2] * 2, sink=1, tail=128), lengths=[200, 100])
+    assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(dp.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_OK
+    full = ctypes.c_size_t(0)
+    dp_full = B.DPolicy(dict(b8=[1] * 2, b4=[2] * 2, sink=1, tail=128))
+    assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(dp_full.c), None, 2, None,
+                       ctypes.byref(full), None) == B.TM_OK
+    assert n.value == full.value            # the workspace follows the capacities
+    for bad in ([257, 100], [200, 0]):
+        dp.set_lengths(bad)
+        assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(dp.c), None, 2, None,
+                           ctypes.byref(n), None) == B.TM_E_SHAPE
+    nb = s.nblk()
+    kq = _qt(B, 2, 0, nb, False)
+    ln = np.array([200, 100], np.int32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert L.tm_cache_append(ctypes.byref(s.c), None, FAKE, 2, ctypes.byref(kq), None) == B.TM_E_ARG
+    assert L.tm_cache_append(ctypes.byref(s.c), ptr(ln), None, 2, ctypes.byref(kq), None) == B.TM_E_ARG
+    for bad in ([0, 100], [200, 101]):
+        b = np.array(bad, np.int32)
+        assert L.tm_cache_append(ctypes.byref(s.c), ptr(b), FAKE, 2, ctypes.byref(kq), None) == B.TM_E_SHAPE
+    wrong = _qt(B, 2, 0, nb - 1, False)
+    assert L.tm_cache_append(ctypes.byref(s.c), ptr(ln), FAKE, 2, ctypes.byref(wrong), None) == B.TM_E_SHAPE
+    vrows_t16 = _qt(B, 2, 0, nb, True)       # rows layout with an fp16 copy is not a valid target
+    assert L.tm_cache_append(ctypes.byref(s.c), ptr(ln), FAKE, 2, ctypes.byref(vrows_t16), None) == B.TM_E_ARG

@@ -325,3 +325,41 @@ def test_decode_deterministic_long_splits(d):
     O = OA.decode(w.seqlens, 8, 2, d, dq[1].astype(np.float64), kq, vq, k[1].astype(np.float64),
                   v[1].astype(np.float64), dpol)
     compare(outs[0], O, what=f"decode determinism d={d}")
+
+
+def test_decode_growing_cache_matches_rebuilt_oracle():
+    """Generation loop: caches of 1000- and 950-token prompts grow by one token
+    per step for 140 steps (crossing two 64-token block boundaries, so blocks
+    leave the 128-token FP16 window and become INT8/INT4), each step through
+    tm_cache_append; at every 20th step the decode equals the oracle over the
+    cache quantized from scratch at the current lengths."""
+    import torch
+    import tile_routed_mixed_amd as T
+    caps, L0, steps = [1200, 1100], np.array([1000, 950]), 140
+    hq, hkv, d = 8, 2, 128
+    dpol = dict(b8=[4, 6], b4=[10, 12], sink=1, tail=128)
+    w = W.small("decode16x32k", caps, hq=hq, hkv=hkv, d=d, dtype="f16")
+    _, k, v = W.make_qkv(w)                        # rows past the prompts are the generated tokens
+    rng = np.random.default_rng(77)
+    queries = [W.round16(rng.standard_normal((2, hq, d)).astype(np.float32), "f16") for _ in range(steps + 1)]
+    cu = w.cu_seqlens
+    say(f"[gpu] growing cache {caps} from {L0.tolist()}, {steps} steps")
+    p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol, dtype="f16")
+    p.upload(queries[0][0], k[0], v[0])
+    p.start(L0)
+    for step in range(steps + 1):
+        L = L0 + step
+        if step % 20 == 0:
+            o = p.decode()
+            torch.cuda.synchronize()
+            o = o.cpu().numpy()
+            for b in range(2):
+                sl = slice(int(cu[b]), int(cu[b]) + int(L[b]))
+                kq = OQ.quantize(k[1][sl], [int(L[b])])
+                vq = OQ.quantize(v[1][sl], [int(L[b])], layout="cols")
+                O = OA.decode([int(L[b])], hq, hkv, d, queries[step][1][b:b + 1].astype(np.float64), kq, vq,
+                              k[1][sl].astype(np.float64), v[1][sl].astype(np.float64), dpol)
+                compare(o[b], O[0], what=f"growing cache step {step} seq {b} L={int(L[b])}")
+        if step < steps:
+            rows = cu[:-1] + L
+            p.append(k[0][rows], v[0][rows], q_bits=queries[step + 1][0])

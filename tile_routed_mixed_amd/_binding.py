@@ -54,7 +54,8 @@ class tm_census(ctypes.Structure):
 
 class tm_dpolicy(ctypes.Structure):
     _fields_ = [("b8", ctypes.POINTER(ctypes.c_int32)), ("b4", ctypes.POINTER(ctypes.c_int32)),
-                ("sink", ctypes.c_int32), ("tail_tokens", ctypes.c_int32)]
+                ("sink", ctypes.c_int32), ("tail_tokens", ctypes.c_int32),
+                ("lengths", ctypes.POINTER(ctypes.c_int32))]
 
 
 class TMError(RuntimeError):
@@ -89,6 +90,9 @@ def lib():
         L.tm_prefill.argtypes = [ctypes.POINTER(tm_shape), vp, i32, vp, vp, ctypes.POINTER(tm_qtensor),
                                  ctypes.POINTER(tm_qtensor), ctypes.POINTER(tm_qtensor), vp, i32, vp, vp, vp,
                                  i32, vp]
+        L.tm_cache_append.restype = i32
+        L.tm_cache_append.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(ctypes.c_int32), vp, i32,
+                                      ctypes.POINTER(tm_qtensor), vp]
         L.tm_decode.restype = i32
         L.tm_decode.argtypes = [ctypes.POINTER(tm_shape), vp, ctypes.POINTER(tm_qtensor),
                                 ctypes.POINTER(tm_qtensor), vp, ctypes.POINTER(tm_dpolicy), vp, i32, vp,
@@ -235,12 +239,34 @@ def tm_prefill(shape: Shape, trav, policy_kind: int, q, k, qq: QTensor, kq: QTen
 
 
 class DPolicy:
-    def __init__(self, dpol: dict):
+    def __init__(self, dpol: dict, lengths=None):
         self.b8 = np.ascontiguousarray(np.asarray(dpol["b8"], dtype=np.int32))
         self.b4 = np.ascontiguousarray(np.asarray(dpol["b4"], dtype=np.int32))
         self.c = tm_dpolicy(self.b8.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                             self.b4.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(dpol["sink"]),
-                            int(dpol["tail"]))
+                            int(dpol["tail"]), None)
+        self.lengths = None
+        if lengths is not None:
+            self.set_lengths(lengths)
+
+    def set_lengths(self, lengths):
+        """Current lengths of a growing cache (host int32 [nseq]), or None."""
+        if lengths is None:
+            self.lengths = None
+            self.c.lengths = None
+        else:
+            self.lengths = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+            self.c.lengths = self.lengths.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def tm_cache_append(shape: Shape, lengths: np.ndarray, x, out: QTensor, stream=None):
+    """Re-quantize the block holding each sequence's newest token (lengths:
+    host int32 [nseq], current lengths; x: [T][heads][d] in the capacity
+    layout of `shape`)."""
+    ln = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    assert x.is_contiguous() and x.element_size() == 2
+    _check(lib().tm_cache_append(ctypes.byref(shape.c), ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(x),
+                                 out.heads, ctypes.byref(out.c), _stream(stream)), "tm_cache_append")
 
 
 def decode_ws_bytes(shape: Shape, dpol: DPolicy) -> int:

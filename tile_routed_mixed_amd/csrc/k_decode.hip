@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   // this sequence's extent (kernel-argument tables: scalar loads)
   const int tok0 = a.cu[b];
-  const int L = a.cu[b + 1] - tok0;
+  const int L = a.len[b];
   const int blk0 = a.blk[b];
   // this KV head's bands, in 64-token blocks
   const int nb = (L + kBlock - 1) / kBlock;

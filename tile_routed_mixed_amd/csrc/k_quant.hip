@@ -22,21 +22,18 @@ __device__ __forceinline__ int8_t quant_code(float x, float s, float qmax) {
   return static_cast<int8_t>(c);
 }
 
+// Quantize cache block b (global index) of head h: its first token is row
+// tok_first of x, and its first nvalid rows are valid (the rest count as 0).
 template <int D, bool BF16, bool COLS>
-__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+__device__ __forceinline__ void quant_block(const QuantArgs& a, int b, int h, size_t tok_first, int nvalid) {
   constexpr int EPT = D / 4;            // elements per thread (one quarter row)
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  const int h = blockIdx.y;
-  const SeqOfBlock so = find_block_seq(a.cu, a.nseq, b);
-  const int lb = b - so.blk_start;
-  const int nvalid = min(kBlock, so.len - lb * kBlock);
   const int row = tid >> 2;
   const int col0 = (tid & 3) * EPT;
 
   float xv[EPT];
   if (row < nvalid) {
-    const size_t tok = static_cast<size_t>(so.tok_start) + lb * kBlock + row;
+    const size_t tok = tok_first + row;
     const uint16_t* src = a.x + (tok * a.heads + h) * D + col0;
 #pragma unroll
     for (int v = 0; v < EPT / 8; ++v) {
@@ -176,6 +173,40 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
       }
     }
   }
+}
+
+template <int D, bool BF16, bool COLS>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+  const int b = blockIdx.x, h = blockIdx.y;
+  const SeqOfBlock so = find_block_seq(a.cu, a.nseq, b);
+  const int lb = b - so.blk_start;
+  quant_block<D, BF16, COLS>(a, b, h, static_cast<size_t>(so.tok_start) + lb * kBlock,
+                             min(kBlock, so.len - lb * kBlock));
+}
+
+// Cache append: workgroup (i, h) re-quantizes the block that holds sequence
+// i's newest token, over the sequence's current length (codes and scales of
+// a partial block cover its valid rows, as tm_quantize_pack would).
+template <int D, bool BF16, bool COLS>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs p) {
+  const int i = blockIdx.x, h = blockIdx.y;
+  quant_block<D, BF16, COLS>(p.q, p.blk[i], h, static_cast<size_t>(p.tok[i]), p.nvalid[i]);
+}
+
+template <int D, bool BF16, bool COLS>
+static hipError_t launch_append_t(const AppendArgs& p, hipStream_t st) {
+  hipLaunchKernelGGL((append_kernel<D, BF16, COLS>), dim3(p.n, p.q.heads), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st) {
+  if (p.n == 0) return hipSuccess;
+  if (d == 128) {
+    if (bf16) return cols ? launch_append_t<128, true, true>(p, st) : launch_append_t<128, true, false>(p, st);
+    return cols ? launch_append_t<128, false, true>(p, st) : launch_append_t<128, false, false>(p, st);
+  }
+  if (bf16) return cols ? launch_append_t<64, true, true>(p, st) : launch_append_t<64, true, false>(p, st);
+  return cols ? launch_append_t<64, false, true>(p, st) : launch_append_t<64, false, false>(p, st);
 }
 
 template <int D, bool BF16, bool COLS>

@@ -321,6 +321,7 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   for (int b = 0; b < cache->nseq; ++b) {
     const int64_t len = cache->cu_seqlens[b + 1] - cache->cu_seqlens[b];
     if (len < 1) return TM_E_SHAPE;
+    if (policy->lengths != nullptr && (policy->lengths[b] < 1 || policy->lengths[b] > len)) return TM_E_SHAPE;
     // a sequence's 16-bit rows (and fp16 V copy) must lie within 2 GiB of its first (32-bit offsets)
     if ((len + 63) / 64 * cache->hkv * 64 * cache->d * 2 >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
   }
@@ -372,13 +373,58 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     c.nseq = n;
     for (int i = 0; i <= n; ++i) c.cu[i] = cache->cu_seqlens[s0 + i];
     for (int i = 0; i < n; ++i) {
+      const int32_t cap = cache->cu_seqlens[s0 + i + 1] - cache->cu_seqlens[s0 + i];
+      c.len[i] = policy->lengths != nullptr ? policy->lengths[s0 + i] : cap;
       c.blk[i] = static_cast<int32_t>(blk);
-      blk += (cache->cu_seqlens[s0 + i + 1] - cache->cu_seqlens[s0 + i] + 63) / 64;
+      blk += (cap + 63) / 64;
     }
     c.q = a.q + static_cast<size_t>(s0) * cache->hq * cache->d;
     c.o = static_cast<uint8_t*>(o) + static_cast<size_t>(s0) * cache->hq * cache->d * osz;
     c.ws = a.ws + static_cast<size_t>(s0) * cache->hq * plan.nsplit * (cache->d + 2);
     const hipError_t e = launch_decode(c, cache->d, cache->dtype == TM_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return TM_E_HIP;
+  }
+  return TM_OK;
+}
+
+tm_status tm_cache_append(const tm_shape* cache, const int32_t* lengths, const void* x, int32_t heads,
+                          tm_qtensor* out, void* stream) {
+  ShapeInfo si;
+  tm_status st = check_shape(cache, false, &si);
+  if (st != TM_OK) return st;
+  if (lengths == nullptr || x == nullptr || out == nullptr || heads < 1) return TM_E_ARG;
+  if (out->layout != TM_ROWS && out->layout != TM_COLS) return TM_E_ARG;
+  if (out->layout == TM_ROWS && out->t16 != nullptr) return TM_E_ARG;
+  if ((st = check_qtensor(out, heads, out->layout, si.nblk, false)) != TM_OK) return st;
+  for (int b = 0; b < cache->nseq; ++b) {
+    const int32_t cap = cache->cu_seqlens[b + 1] - cache->cu_seqlens[b];
+    if (lengths[b] < 1 || lengths[b] > cap) return TM_E_SHAPE;
+  }
+  AppendArgs p;
+  std::memset(&p, 0, sizeof(p));
+  p.q.x = static_cast<const uint16_t*>(x);
+  p.q.heads = heads;
+  p.q.nblk = si.nblk;
+  p.q.c8 = out->c8;
+  p.q.c4 = out->c4;
+  p.q.s8 = out->s8;
+  p.q.s4 = out->s4;
+  p.q.t16 = out->t16;
+  int64_t blk = 0;
+  for (int s0 = 0; s0 < cache->nseq; s0 += kMaxSeqArg) {
+    const int n = std::min(kMaxSeqArg, cache->nseq - s0);
+    AppendArgs c = p;
+    c.n = n;
+    for (int i = 0; i < n; ++i) {
+      const int s = s0 + i;
+      const int32_t j = (lengths[s] - 1) / 64;   // block of the newest token
+      c.blk[i] = static_cast<int32_t>(blk + j);
+      c.tok[i] = cache->cu_seqlens[s] + 64 * j;
+      c.nvalid[i] = lengths[s] - 64 * j;
+      blk += (cache->cu_seqlens[s + 1] - cache->cu_seqlens[s] + 63) / 64;
+    }
+    const hipError_t e = launch_append(c, cache->d, cache->dtype == TM_BF16, out->layout == TM_COLS,
+                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return TM_E_HIP;
   }
   return TM_OK;

@@ -22,6 +22,14 @@ struct QuantArgs {
   uint16_t* t16;
 };
 
+struct AppendArgs {
+  QuantArgs q;                  // x, heads, nblk and the outputs (cu and nseq unused)
+  int n;                        // sequences of this launch
+  int32_t blk[kMaxSeqArg];      // global block holding each sequence's newest token
+  int32_t tok[kMaxSeqArg];      // its first token row in x
+  int32_t nvalid[kMaxSeqArg];   // its valid rows
+};
+
 struct TravArgs {
   uint8_t* trav;
   const int32_t* cu;
@@ -80,10 +88,12 @@ struct DecodeArgs {
   int32_t b8[kMaxKvArg];
   int32_t b4[kMaxKvArg];
   int32_t cu[kMaxSeqArg + 1];   // token offsets of this launch's sequences (absolute)
+  int32_t len[kMaxSeqArg];      // their current lengths (at most cu[i + 1] - cu[i])
   int32_t blk[kMaxSeqArg];      // their first cache block (absolute)
 };
 
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
+hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st);

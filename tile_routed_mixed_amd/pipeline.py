@@ -1,10 +1,11 @@
-"""Device-buffer plumbing around the four entry points.
+"""Device-buffer plumbing around the entry points.
 
 PrefillPipeline holds the device copies of Q, K, V and every buffer the
 prefill path writes, and runs one pass of the path:
   tm_quantize_pack(Q, rows)  tm_quantize_pack(K, rows)
   tm_quantize_pack(V, cols + fp16 copy)   tm_build_traversal   tm_prefill.
-DecodePipeline does the same for one decode step over a quantized cache.
+DecodePipeline does the same for decode steps over a quantized cache, and
+for a growing one (start / append: tm_cache_append per step).
 Nothing here computes: buffers are allocated once and the C ABI is called.
 """
 from __future__ import annotations
@@ -93,6 +94,37 @@ class DecodePipeline:
     def decode(self, stream=None):
         return B.tm_decode(self.shape, self.q, self.kq, self.vq, self.k, self.dpol, o=self.o, ws=self.ws,
                            stream=stream)
+
+    # ---- generation: the shape's lengths are capacities; the cache holds
+    # the first `lengths[s]` tokens of sequence s
+    def start(self, lengths, stream=None):
+        """Cache the first lengths[s] tokens of every sequence (the uploaded K/V
+        rows past them are ignored) and decode at those lengths from now on."""
+        self.dpol.set_lengths(lengths)
+        B.tm_quantize_pack(self.shape, self.k, self.kq, stream)
+        B.tm_quantize_pack(self.shape, self.v, self.vq, stream)
+        # the block holding each sequence's last cached token, over the cached rows only
+        L = self.dpol.lengths
+        B.tm_cache_append(self.shape, L, self.k, self.kq, stream)
+        B.tm_cache_append(self.shape, L, self.v, self.vq, stream)
+
+    def append(self, k_bits, v_bits, q_bits=None, stream=None):
+        """Append one token per sequence: k_bits, v_bits [nseq][hkv][d] (16-bit
+        patterns) go to row lengths[s] of each sequence, the cache blocks are
+        brought up to date, and q_bits [nseq][hq][d] (if given) becomes the
+        next query."""
+        import torch
+        L = self.dpol.lengths.copy()
+        cu = self.shape.cu_host
+        rows = torch.as_tensor((cu[:-1] + L).astype(np.int64), device=self.device)
+        self.k[rows] = _dev_bits(k_bits, self.device)
+        self.v[rows] = _dev_bits(v_bits, self.device)
+        L += 1
+        self.dpol.set_lengths(L)
+        B.tm_cache_append(self.shape, L, self.k, self.kq, stream)
+        B.tm_cache_append(self.shape, L, self.v, self.vq, stream)
+        if q_bits is not None:
+            self.q = _dev_bits(q_bits, self.device)
 
     @classmethod
     def from_prefill(cls, pp: "PrefillPipeline", dpolicy: dict, q_bits):
