@@ -117,6 +117,42 @@ def cpu_baseline(w, q, k, v, pol, seconds):
                       f"{dt:.1f} s; attention rows only (codes precomputed); dense-causal FLOPs of those rows"}
 
 
+def prefill_config_line(name, steps=10, warmup=2):
+    """Prefill alone on another of the five workloads: time per launch (HIP
+    events on the launch stream, back to back), effective dense-causal rate,
+    and the fraction of the precision-weighted MFMA peak of its executed tiles."""
+    import torch
+    import tile_routed_mixed_amd as T
+    import workloads as W
+    w = W.get(name)
+    q, k, v = W.make_qkv(w)
+    pol = W.make_policy(w)
+    pp = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, pol)
+    pp.upload(q[0], k[0], v[0])
+    del q, k, v
+    pp.quantize()
+    census = pp.traversal(census=True)
+    o_dtype = T.TM_BF16 if w.dtype == "bf16" else T.TM_F16
+    for _ in range(warmup):
+        pp.prefill(o_dtype)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        pp.prefill(o_dtype)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps
+    ops, t_peak = prefill_roofline(w, census, t * 1e-3)
+    res = {"workload": describe(w), "prefill_ms": t,
+           "effective_tflops_dense_causal": dense_causal_flops(w) / (t * 1e-3) / 1e12,
+           "mfma_frac_precision_weighted": (ops / (t * 1e-3)) / (ops / t_peak),
+           "census": census}
+    del pp
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_loop_bench(steps=64):
     """Generation loop over the 16 x 32768-token workload: the caches start
     `steps` tokens short of 32768 and every step decodes one query per
@@ -221,6 +257,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-bench", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the prefill-only lines for the toy, varlen and 128K workloads")
     ap.add_argument("--decode-only", action="store_true",
                     help="only run the decode sub-benchmark (16 x 32768-token cache) and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -336,6 +374,13 @@ def main():
         out["decode_loop"] = dl
         log(f"[bench] decode loop {dl['ms_per_step']:.4f} ms/step (decode + cache append), "
             f"{dl['tokens_per_s']:.0f} tokens/s")
+    if not args.no_other_configs and args.workload == "gqa8k":
+        out["other_configs"] = []
+        for name in ("toy512", "varlen32k", "long128k"):
+            r = prefill_config_line(name)
+            out["other_configs"].append(r)
+            log(f"[bench] {name}: prefill {r['prefill_ms']:.4f} ms, {r['effective_tflops_dense_causal']:.1f} "
+                f"TFLOP/s dense-causal, {r['mfma_frac_precision_weighted'] * 100:.1f} % of the weighted MFMA peak")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, pol, args.cpu_seconds)
