@@ -543,39 +543,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   }
 }
 
-// Merge of one query head's split results by log-sum-exp: one wave per head;
-// the splits' maxima and sums are reduced across lanes, then every lane sums
-// its output channels over the splits with all loads of a group of 8 splits
-// in flight together.
+// Merge of one query head's split results by log-sum-exp: one wave per head.
+// Splits are taken 16 at a time with every load of a group (their maxima and
+// sums through scalar loads, the lane's output channels through vector loads)
+// in flight together, and folded into a running (max, sum, O) state.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int PER = D / 64;
+  constexpr int PER = D / 64, G = 16;
   const int bh = blockIdx.x, lane = threadIdx.x, ns = a.nsplit;
-  const float* src = a.ws + static_cast<size_t>(bh) * ns * (D + 2);
-  float M = kNegBig;
-  for (int c = lane; c < ns; c += 64) M = fmaxf(M, src[c * (D + 2)]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float lsum = 0.0f;
-  for (int c = lane; c < ns; c += 64) lsum += src[c * (D + 2) + 1] * __builtin_amdgcn_exp2f(src[c * (D + 2)] - M);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
-  float ov[PER];
+  const float* const src = pin_sgpr(a.ws + static_cast<size_t>(bh) * ns * (D + 2));
+  float M = kNegBig, lsum = 0.0f, ov[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) ov[p] = 0.0f;
-  for (int c0 = 0; c0 < ns; c0 += 8) {
-    float f[8], x[8][PER];
+  for (int c0 = 0; c0 < ns; c0 += G) {
+    float m[G], l[G], x[G][PER];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < G; ++u) {
       const int c = min(c0 + u, ns - 1);
-      f[u] = c0 + u < ns ? __builtin_amdgcn_exp2f(src[c * (D + 2)] - M) : 0.0f;
+      m[u] = c0 + u < ns ? sload(src, static_cast<size_t>(c) * (D + 2)) : kNegBig;
+      l[u] = sload(src, static_cast<size_t>(c) * (D + 2) + 1);
 #pragma unroll
       for (int p = 0; p < PER; ++p) x[u][p] = src[c * (D + 2) + 2 + 64 * p + lane];
     }
+    float mc = m[0];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 1; u < G; ++u) mc = fmaxf(mc, m[u]);
+    const float mn = fmaxf(M, mc);
+    const float sc = __builtin_amdgcn_exp2f(M - mn);
+    lsum *= sc;
 #pragma unroll
-      for (int p = 0; p < PER; ++p) ov[p] += x[u][p] * f[u];
+    for (int p = 0; p < PER; ++p) ov[p] *= sc;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const float f = c0 + u < ns ? __builtin_amdgcn_exp2f(m[u] - mn) : 0.0f;
+      lsum += l[u] * f;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) ov[p] += x[u][p] * f;
+    }
+    M = mn;
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
