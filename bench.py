@@ -189,13 +189,31 @@ def decode_loop_bench(steps=64):
             "tokens_per_s": len(w.seqlens) / (ms * 1e-3)}
 
 
+def decode_block_counts(L, b8, b4, sink, tail):
+    """Blocks of each precision that one decode step reads for a cache of L
+    tokens (the query at L - 1): blocks reaching into the last `tail` tokens
+    are FP16, block 0 is INT8 under a sink, and block j otherwise sits at
+    distance last - j from the query's block (INT8 below b8, INT4 below b4,
+    else skipped).  Byte accounting for the bench line only."""
+    nb = -(-L // 64)
+    last = (L - 1) // 64
+    first_tail = max(0, (L - tail) // 64) if tail > 0 else nb   # first block reaching the tail
+    c = {"int8": 0, "int4": 0, "fp16": nb - first_tail, "skip": 0}
+    for j in range(first_tail):
+        if sink and j == 0:
+            c["int8"] += 1
+            continue
+        dl = last - j
+        c["int8" if dl < b8 else ("int4" if dl < b4 else "skip")] += 1
+    return c
+
+
 def decode_bench(steps, rotate=3):
     """Decode over a 16 x 32768-token compressed cache; returns timing and bytes."""
     import numpy as np
     import torch
     import tile_routed_mixed_amd as T
     import workloads as W
-    from oracle import policy as OP
     w = W.get("decode16x32k")
     dpol = W.make_decode_policy(w)
     _, k, v = W.make_qkv(w)
@@ -210,15 +228,14 @@ def decode_bench(steps, rotate=3):
     torch.cuda.synchronize()
     # algorithmic bytes: codes + two scales of every INT block (K and V), 16-bit K
     # and V^T of every FP16 block, per (sequence, KV head); q and o are negligible
-    per = {OP.INT8: 64 * w.d * 2 + 8, OP.INT4: 64 * w.d + 8, OP.FP16: 64 * w.d * 2 * 2, OP.SKIP: 0}
-    nbytes = 0
-    counts = {OP.INT8: 0, OP.INT4: 0, OP.FP16: 0, OP.SKIP: 0}
+    per = {"int8": 64 * w.d * 2 + 8, "int4": 64 * w.d + 8, "fp16": 64 * w.d * 2 * 2, "skip": 0}
+    counts = {"int8": 0, "int4": 0, "fp16": 0, "skip": 0}
     for L in w.seqlens:
         for g in range(w.hkv):
-            tags = OP.decode_block_tags(L, int(dpol["b8"][g]), int(dpol["b4"][g]), dpol["sink"], dpol["tail"])
-            for t in tags.tolist():
-                nbytes += per[t]
-                counts[t] += 1
+            for t, n in decode_block_counts(L, int(dpol["b8"][g]), int(dpol["b4"][g]), dpol["sink"],
+                                            dpol["tail"]).items():
+                counts[t] += n
+    nbytes = sum(per[t] * n for t, n in counts.items())
     for i in range(5):
         caches[i % rotate].decode()
     torch.cuda.synchronize()
@@ -244,8 +261,7 @@ def decode_bench(steps, rotate=3):
             "bytes_per_step": nbytes, "ms_mean": mean, "ms_median_single": ms[len(ms) // 2],
             "ms_min_single": ms[0],
             "GBps": nbytes / (mean * 1e-3) / 1e9, "hbm_frac": nbytes / (mean * 1e-3) / PEAK_HBM,
-            "blocks": {"int8": counts[OP.INT8], "int4": counts[OP.INT4], "fp16": counts[OP.FP16],
-                       "skip": counts[OP.SKIP]}, "rotated_caches": rotate}
+            "blocks": counts, "rotated_caches": rotate}
 
 
 def main():
