@@ -35,6 +35,15 @@ class PrefillPipeline:
         self.o = None
         self.lse = torch.empty((hq, self.shape.T), dtype=torch.float32, device=device)
 
+    def set_policy(self, policy: dict):
+        """Route the same quantized inputs under another policy (the next
+        traversal() builds its traversal)."""
+        import torch
+        self.policy = B.Policy(policy, device=self.device)
+        need = B.traversal_bytes(self.shape, self.policy)
+        if self.trav.numel() < need:
+            self.trav = torch.empty(need, dtype=torch.uint8, device=self.device)
+
     def upload(self, q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray):
         self.q = _dev_bits(q_bits, self.device)
         self.k = _dev_bits(k_bits, self.device)
