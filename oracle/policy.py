@@ -25,7 +25,15 @@ Readings taken where the pages are silent:
   [g*G, (g+1)*G); each (sequence, query head, query tile) row holds
   ceil(ceil(nk / G) / 32) uint32 words, LSB-first; rows are laid out
   sequence-major, then head, then query tile; the legal tiles of a partly
-  legal group take the group's bit.
+  legal group take the group's bit;
+* four-way (both encodings in one): the boundaries (b8, b4, sink) of a head
+  plus a 2-bit code per group of G key tiles, 16 codes per uint32 word
+  (group g in bits 2(g mod 16) .. 2(g mod 16) + 1 of the row's word g div 16),
+  ceil(ceil(nk / G) / 16) words per row in the bitmask's row order; code 0
+  leaves the tile to the boundary rule (so SKIP comes only from there),
+  codes 1, 2, 3 set INT4, INT8, FP16.  All-zero codes give the boundary
+  policy; codes drawn from {2, 3} give the bitmask policy with bit = (code
+  == 3).
 """
 from __future__ import annotations
 
@@ -76,6 +84,27 @@ def bitmask_bit(words: np.ndarray, row_off: int, g: int) -> int:
     return int((int(words[row_off + g // 32]) >> (g % 32)) & 1)
 
 
+def fourway_words_per_row(S: int, bk: int, group: int) -> int:
+    ng = n_tiles(n_tiles(S, bk), group)
+    return n_tiles(ng, 16)
+
+
+def fourway_row_base(seqlens, hq: int, bq: int, bk: int, group: int):
+    """Word offset of row (s, h=0, i=0) of a four-way code map, and the total."""
+    bases, acc = [], 0
+    for S in seqlens:
+        bases.append(acc)
+        acc += hq * n_tiles(S, bq) * fourway_words_per_row(S, bk, group)
+    return bases, acc
+
+
+def fourway_code(words: np.ndarray, row_off: int, g: int) -> int:
+    return int((int(words[row_off + g // 16]) >> (2 * (g % 16))) & 3)
+
+
+CODE_PREC = {1: INT4, 2: INT8, 3: FP16}
+
+
 def precision_grid_loop(S, bq, bk, head, pol, seq=0, seqlens=None, hq=None):
     """Brute force over every (i, j) with plain Python loops: [nq][nk] int8."""
     nq, nk = n_tiles(S, bq), n_tiles(S, bk)
@@ -83,13 +112,20 @@ def precision_grid_loop(S, bq, bk, head, pol, seq=0, seqlens=None, hq=None):
     if pol["kind"] == 1:
         bases, _ = bitmask_row_base(seqlens, hq, bq, bk, pol["group"])
         wpr = bitmask_words_per_row(S, bk, pol["group"])
+    if pol["kind"] == 2:
+        bases, _ = fourway_row_base(seqlens, hq, bq, bk, pol["group"])
+        wpr = fourway_words_per_row(S, bk, pol["group"])
     for i in range(nq):
         for j in range(nk):
             if not is_legal(i, j, S, bq, bk):
                 continue
-            if pol["kind"] == 0:
+            if pol["kind"] in (0, 2):
                 g[i, j] = boundary_prec(i, j, bq, bk, int(pol["b8"][head]), int(pol["b4"][head]),
                                         int(pol["sink"]))
+                if pol["kind"] == 2:
+                    code = fourway_code(pol["words"], bases[seq] + (head * nq + i) * wpr, j // pol["group"])
+                    if code:
+                        g[i, j] = CODE_PREC[code]
             else:
                 row = bases[seq] + (head * nq + i) * wpr
                 g[i, j] = FP16 if bitmask_bit(pol["words"], row, j // pol["group"]) else INT8
@@ -102,12 +138,22 @@ def precision_grid(S, bq, bk, head, pol, seq=0, seqlens=None, hq=None):
     i = np.arange(nq)[:, None]
     j = np.arange(nk)[None, :]
     legal = j * bk <= np.minimum((i + 1) * bq, S) - 1
-    if pol["kind"] == 0:
+    if pol["kind"] in (0, 2):
         dl = np.maximum(0, (i * bq - j * bk) // bk)
         b8, b4 = int(pol["b8"][head]), int(pol["b4"][head])
         p = np.where(dl < b8, INT8, np.where(dl < b4, INT4, SKIP))
         if int(pol["sink"]):
             p[:, 0] = INT8
+        if pol["kind"] == 2:
+            G = pol["group"]
+            bases, _ = fourway_row_base(seqlens, hq, bq, bk, G)
+            wpr = fourway_words_per_row(S, bk, G)
+            row = bases[seq] + (head * nq + np.arange(nq)) * wpr           # [nq]
+            gidx = np.arange(nk) // G                                      # [nk]
+            words = np.asarray(pol["words"], dtype=np.uint64)
+            w = words[row[:, None] + gidx[None, :] // 16]
+            code = (w >> (2 * (gidx[None, :] % 16)).astype(np.uint64)) & np.uint64(3)
+            p = np.where(code == 1, INT4, np.where(code == 2, INT8, np.where(code == 3, FP16, p)))
     else:
         G = pol["group"]
         bases, _ = bitmask_row_base(seqlens, hq, bq, bk, G)

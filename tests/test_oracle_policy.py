@@ -7,7 +7,10 @@
 * hand-set bitmask words give the tile precisions worked out by hand in
   tests/golden/bitmask_small.json (multi-word rows, partial groups, varlen);
 * the two encodings agree where they describe the same policy (all INT8);
-* decode cache tags match the hand-worked counts in tests/golden/decode_tags.json.
+* decode cache tags match the hand-worked counts in tests/golden/decode_tags.json;
+* the four-way code map gives the hand-worked precisions of
+  tests/golden/fourway_small.json, reduces to the boundary policy when every
+  code is 0 and to the bitmask policy when codes are drawn from {2, 3}.
 """
 import json
 import os
@@ -21,6 +24,11 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def _rand_pol(rng, hq, kind, seqlens=None, bq=128, bk=64, G=4, sink=0):
+    if kind == 2:
+        b = _rand_pol(rng, hq, 0, sink=sink)
+        _, tot = P.fourway_row_base(seqlens, hq, bq, bk, G)
+        return dict(kind=2, b8=b["b8"], b4=b["b4"], sink=sink, group=G,
+                    words=rng.integers(0, 2 ** 32, size=tot, dtype=np.uint64).astype(np.uint32))
     if kind == 0:
         b4 = rng.integers(0, 12, size=hq)
         b8 = np.array([rng.integers(0, x + 1) for x in b4])
@@ -29,7 +37,7 @@ def _rand_pol(rng, hq, kind, seqlens=None, bq=128, bk=64, G=4, sink=0):
     return dict(kind=1, group=G, words=rng.integers(0, 2 ** 32, size=tot, dtype=np.uint64).astype(np.uint32))
 
 
-@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("kind", [0, 1, 2])
 @pytest.mark.parametrize("bq", [64, 128])
 def test_vectorized_equals_loop(kind, bq):
     rng = np.random.default_rng(3 + kind + bq)
@@ -168,3 +176,51 @@ def test_long_policy_mix():
     assert abs(c["int8"] / c["legal"] - 0.15) < 0.02
     assert abs(c["int4"] / c["legal"] - 0.25) < 0.02
     assert abs(c["skip"] / c["legal"] - 0.60) < 0.02
+
+
+def test_fourway_hand_worked():
+    gold = json.load(open(os.path.join(GOLD, "fourway_small.json")))
+    _, tot = P.fourway_row_base(gold["seqlens"], gold["hq"], gold["bq"], gold["bk"], gold["group"])
+    assert tot == gold["total_words"]
+    words = np.zeros(tot, np.uint32)
+    for k, v in gold["set_words"].items():
+        words[int(k)] = v
+    pol = dict(kind=2, b8=gold["b8"], b4=gold["b4"], sink=gold["sink"], group=gold["group"], words=words)
+    for loop in (True, False):
+        gs = P.grids(gold["seqlens"], gold["hq"], gold["bq"], gold["bk"], pol, loop=loop)
+        for e in gold["expect"]:
+            row = gs[e["seq"]][0][e["qtile"]]
+            legal = np.nonzero(row != P.ILLEGAL)[0].tolist()
+            assert sorted(e["fp16"] + e["int8"] + e["int4"] + e["skip"]) == legal, e
+            for key, prec in (("fp16", P.FP16), ("int8", P.INT8), ("int4", P.INT4), ("skip", P.SKIP)):
+                assert np.nonzero(row == prec)[0].tolist() == e[key], (e, key)
+
+
+@pytest.mark.parametrize("sink", [0, 1])
+def test_fourway_reduces_to_the_two_encodings(sink):
+    rng = np.random.default_rng(41 + sink)
+    seqlens, hq, G = [1, 200, 1000, 3000], 3, 3
+    b = _rand_pol(rng, hq, 0, sink=sink)
+    _, tot = P.fourway_row_base(seqlens, hq, 128, 64, G)
+    zero = dict(kind=2, b8=b["b8"], b4=b["b4"], sink=sink, group=G, words=np.zeros(tot, np.uint32))
+    for x, y in zip(P.grids(seqlens, hq, 128, 64, zero), P.grids(seqlens, hq, 128, 64, b)):
+        assert np.array_equal(x, y)
+    # codes from {2, 3}: bit (code == 3) of the same group in a bitmask row
+    bases4, _ = P.fourway_row_base(seqlens, hq, 128, 64, G)
+    bases1, tot1 = P.bitmask_row_base(seqlens, hq, 128, 64, G)
+    w4 = np.zeros(tot, np.uint32)
+    w1 = np.zeros(tot1, np.uint32)
+    for s, S in enumerate(seqlens):
+        nq, ng = P.n_tiles(S, 128), P.n_tiles(P.n_tiles(S, 64), G)
+        for h in range(hq):
+            for i in range(nq):
+                r4 = bases4[s] + (h * nq + i) * P.fourway_words_per_row(S, 64, G)
+                r1 = bases1[s] + (h * nq + i) * P.bitmask_words_per_row(S, 64, G)
+                for g in range(ng):
+                    fp = int(rng.integers(0, 2))
+                    w4[r4 + g // 16] |= np.uint32((3 if fp else 2) << (2 * (g % 16)))
+                    w1[r1 + g // 32] |= np.uint32(fp << (g % 32))
+    four = dict(kind=2, b8=b["b8"], b4=b["b4"], sink=sink, group=G, words=w4)
+    bm = dict(kind=1, group=G, words=w1)
+    for x, y in zip(P.grids(seqlens, hq, 128, 64, four), P.grids(seqlens, hq, 128, 64, bm)):
+        assert np.array_equal(x, y)
