@@ -72,7 +72,11 @@ typedef enum tm_layout {
   TM_COLS = 1   /* codes transposed per block: [nblk][heads][d][64], [d][32]   */
 } tm_layout;
 
-typedef enum tm_policy_kind { TM_POLICY_BOUNDARIES = 0, TM_POLICY_BITMASK = 1 } tm_policy_kind;
+typedef enum tm_policy_kind {
+  TM_POLICY_BOUNDARIES = 0,
+  TM_POLICY_BITMASK = 1,
+  TM_POLICY_FOURWAY = 2
+} tm_policy_kind;
 
 /* Problem shape.  cu_seqlens (host) and cu_seqlens_dev (device) hold the same
  * nseq+1 non-decreasing int32 prefix sums starting at 0.
@@ -119,9 +123,9 @@ typedef struct tm_qtensor {
 } tm_qtensor;
 
 /* Tile policy ([TriAttention] abstract: two diagonal-distance boundaries per
- * head; [TileMix] abstract: packed group bitmask).  b8/b4 are host arrays
- * (at most 256 query heads); bits is device memory read by the expansion
- * kernel.
+ * head; [TileMix] abstract: packed group bitmask; the four-way kind combines
+ * the two).  b8/b4 are host arrays (at most 256 query heads); bits is device
+ * memory read by the expansion kernel.
  *  Boundaries: b8[hq], b4[hq] in key-tile units, 0 <= b8 <= b4.  For query
  *   tile i and key tile j, delta = max(0, floor((i*bq - j*bk) / bk));
  *   delta < b8 -> INT8, delta < b4 -> INT4, else SKIP; sink = 1 keeps key
@@ -131,6 +135,13 @@ typedef struct tm_qtensor {
  *   bit g of a row governs key tiles [g*group, (g+1)*group); each (sequence, query head,
  *   query tile) row holds ceil(ceil(nk_s / group) / 32) words, LSB first, rows
  *   ordered sequence, then head, then query tile.  Nothing is skipped.
+ *  Four-way: b8, b4 and sink as for boundaries (same checks), plus bits with
+ *   a 2-bit code per group: group g of a row is bits 2(g%16) .. 2(g%16)+1 of
+ *   the row's word g/16; rows of ceil(ceil(nk_s / group) / 16) words in the
+ *   bitmask's row order.  Code 0 leaves the group's tiles to the boundary
+ *   rule (the only source of SKIP), codes 1, 2, 3 make them INT4, INT8, FP16.
+ *   All-zero codes give the boundary policy; codes 2/3 only give the bitmask
+ *   policy.
  *  A tile is legal iff j*bk <= min((i+1)*bq, len) - 1; inside a legal tile key
  *  c is visible from row r iff c <= r. */
 typedef struct tm_policy {
@@ -179,7 +190,9 @@ typedef struct tm_dpolicy {
  *  run_off:        n_items x max_runs x uint32[2] {first key tile,
  *                  count | prec << 24}; an item's runs are grouped by
  *                  precision (boundaries: INT8 band, sink, INT4 band;
- *                  bitmask: FP16 runs, then INT8 runs); SKIP tiles are never
+ *                  bitmask: FP16 runs, then INT8 runs; four-way: FP16,
+ *                  then INT8, then INT4 runs, each in ascending key
+ *                  order, adjacent equal tiles merged); SKIP tiles are never
  *                  listed ([TriAttention] abstract: precision-grouped
  *                  traversals; omitted tiles are skipped).
  *  bits_off:       0 (the bitmask stays in the caller's buffer). */
@@ -214,8 +227,9 @@ tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads,
  * without touching the GPU.  Otherwise *trav_bytes is the capacity of `trav`
  * (device); TM_E_SPACE if too small.  census (host, may be NULL): when given,
  * the call synchronizes `stream` and fills it.
- * Errors: TM_E_SHAPE, TM_E_POLICY (b8 > b4, negative boundaries, b4 == 0
- * without sink, group < 1, n_words too small), TM_E_SPACE, TM_E_HIP.
+ * Errors: TM_E_ARG (unknown kind, NULL arrays), TM_E_SHAPE, TM_E_POLICY
+ * (b8 > b4, negative boundaries, b4 == 0 without sink, group < 1, n_words too
+ * small), TM_E_SPACE, TM_E_HIP.
  * ([TriAttention] abstract: boundaries generate precision-grouped traversals;
  * [TileMix] abstract: compact bitmasks, one bit per group of key tiles.) */
 tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,

@@ -134,6 +134,47 @@ def test_bitmask_validation_and_size(B):
     assert L.tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), None, ctypes.byref(n), None, None) == 3
 
 
+def test_fourway_validation_and_size(B):
+    from oracle import policy as P   # the word count the four-way layout implies
+    s = _shape(B, [1000, 10240], hq=2, hkv=1)
+    _, tot = P.fourway_row_base([1000, 10240], 2, 128, 64, 4)
+    p = B.Policy(dict(kind=2, b8=[1, 2], b4=[3, 4], sink=0, group=4, words=np.zeros(tot, np.uint32)))
+    p.c.bits = FAKE
+    n = ctypes.c_size_t(0)
+    L = B.lib()
+
+    def st():
+        return L.tm_build_traversal(ctypes.byref(s.c), ctypes.byref(p.c), None, ctypes.byref(n), None, None)
+
+    assert st() == 0
+    n_items = 2 * (8 + 80)
+    max_runs = (160 + 3) // 4 + 3          # one run per group plus the three boundary edges
+    align = lambda x: (x + 255) // 256 * 256
+    assert n.value == align(align(align(256 + 2 * 16) + 32 * n_items) + 8 * n_items * max_runs)
+    p.c.n_words = tot - 1                  # 16 codes per word: a bitmask-sized map is too small
+    assert st() == B.TM_E_POLICY
+    p.c.n_words = tot
+    p.c.group = 0
+    assert st() == B.TM_E_POLICY
+    p.c.group = 4
+    p.b8[0] = 5                            # b8 > b4
+    assert st() == B.TM_E_POLICY
+    p.b8[0] = 1
+    p.b8[1] = p.b4[1] = 0                  # b4 == 0 without a sink
+    assert st() == B.TM_E_POLICY
+    p.c.sink = 1
+    assert st() == B.TM_OK
+    p.c.sink = 2
+    assert st() == B.TM_E_POLICY
+    p.c.sink = 0
+    p.b8[1], p.b4[1] = 2, 4
+    p.c.bits = None                        # no code map
+    assert st() == B.TM_E_ARG
+    p.c.bits = FAKE
+    p.c.b8 = None
+    assert st() == B.TM_E_ARG
+
+
 def test_traversal_capacity(B):
     s = _shape(B, [512], hq=1, hkv=1, bq=64)
     p = B.Policy(dict(kind=0, b8=[2], b4=[5], sink=1))
@@ -182,7 +223,7 @@ def test_prefill_validation(B):
                             ctypes.byref(a["kq"]), ctypes.byref(a["vq"]), a["o"], a["odt"], None, None, None,
                             a["ndbg"], None)
     assert call(args(q=None)) == B.TM_E_ARG
-    assert call(args(kind=2)) == B.TM_E_ARG
+    assert call(args(kind=3)) == B.TM_E_ARG
     assert call(args(trav=None)) == B.TM_E_ARG
     assert call(args(odt=9)) == B.TM_E_ARG
     assert call(args(ndbg=2)) == B.TM_E_ARG

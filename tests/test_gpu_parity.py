@@ -97,7 +97,8 @@ def _check_traversal(w, pol, p, census):
     assert got == OP.executed_tiles(gs)
 
 
-@pytest.mark.parametrize("case", ["toy", "boundaries_varlen", "bitmask_varlen", "sink_edge"])
+@pytest.mark.parametrize("case", ["toy", "boundaries_varlen", "bitmask_varlen", "sink_edge", "fourway_varlen",
+                                  "fourway_d64"])
 def test_traversal_bruteforce(case):
     w, pol = _case(case)
     q, k, v = _inputs(w)
@@ -134,10 +135,28 @@ def _case(case):
         _, tot = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 4)
         words = rng.integers(0, 2 ** 32, size=tot, dtype=np.uint64).astype(np.uint32)
         return w, dict(kind=1, group=4, words=words)
+    if case == "fourway_varlen":
+        w = W.small("gqa8k", [1000, 1, 130, 64, 2200], hq=8, hkv=2)
+        b4 = rng.integers(1, 12, size=8)
+        b8 = np.array([rng.integers(0, x + 1) for x in b4])
+        return w, _fourway(rng, w, b8, b4, sink=1, group=3, p_zero=0.4)
+    if case == "fourway_d64":
+        w = W.small("long128k", [1500, 333, 64], hq=4, hkv=1, d=64)
+        return w, _fourway(rng, w, [0, 1, 2, 5], [1, 3, 6, 40], sink=0, group=1, p_zero=0.6)
     raise KeyError(case)
 
 
-CASES = ["toy", "boundaries_varlen", "bitmask_varlen", "sink_edge", "bq64_d128", "bitmask_bf16"]
+def _fourway(rng, w, b8, b4, sink, group, p_zero):
+    """Four-way policy with random 2-bit codes: 0 with probability p_zero, else
+    1, 2 or 3 uniformly."""
+    _, tot = OP.fourway_row_base(w.seqlens, w.hq, w.bq, w.bk, group)
+    codes = np.where(rng.random((tot, 16)) < p_zero, 0, rng.integers(1, 4, size=(tot, 16))).astype(np.uint64)
+    words = (codes << (2 * np.arange(16, dtype=np.uint64))).sum(axis=1).astype(np.uint32)
+    return dict(kind=2, b8=np.asarray(b8), b4=np.asarray(b4), sink=sink, group=group, words=words)
+
+
+CASES = ["toy", "boundaries_varlen", "bitmask_varlen", "sink_edge", "bq64_d128", "bitmask_bf16", "fourway_varlen",
+         "fourway_d64"]
 
 
 @pytest.mark.parametrize("case", CASES)
@@ -217,6 +236,39 @@ def test_boundaries_all_int8_equals_zero_bitmask():
         assert cb[key] == cm[key], key
     assert cb["int8"] == cb["legal"] and cb["skip"] == 0
     compare(ob, om.astype(np.float64), lb, lm.astype(np.float64), what="all-INT8 encodings")
+
+
+def test_fourway_reduces_to_boundaries_and_bitmask():
+    """The four-way kernel on all-zero codes computes the boundary policy, and
+    on codes from {2, 3} the bitmask policy: same outputs bit for bit as the
+    kernels of those kinds."""
+    rng = np.random.default_rng(77)
+    w = W.small("gqa8k", [900, 300], hq=4, hkv=2)
+    q, k, v = _inputs(w)
+    b = dict(kind=0, b8=[1, 2, 0, 3], b4=[2, 5, 4, 3], sink=1)
+    _, tot = OP.fourway_row_base(w.seqlens, w.hq, w.bq, w.bk, 2)
+    zero = dict(b, kind=2, group=2, words=np.zeros(tot, np.uint32))
+    _, _, o0, l0, _ = run_prefill(w, b, q, k, v)
+    _, _, o2, l2, _ = run_prefill(w, zero, q, k, v)
+    assert np.array_equal(o0, o2) and np.array_equal(l0, l2)
+    # codes 2/3 <-> bitmask bits 0/1 of the same groups
+    _, tot1 = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 2)
+    bases4, _ = OP.fourway_row_base(w.seqlens, w.hq, w.bq, w.bk, 2)
+    bases1, _ = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 2)
+    w4, w1 = np.zeros(tot, np.uint32), np.zeros(tot1, np.uint32)
+    for s_, S in enumerate(w.seqlens):
+        nq, ng = OP.n_tiles(S, w.bq), OP.n_tiles(OP.n_tiles(S, w.bk), 2)
+        for h in range(w.hq):
+            for i in range(nq):
+                r4 = bases4[s_] + (h * nq + i) * OP.fourway_words_per_row(S, w.bk, 2)
+                r1 = bases1[s_] + (h * nq + i) * OP.bitmask_words_per_row(S, w.bk, 2)
+                for g in range(ng):
+                    fp = int(rng.integers(0, 2))
+                    w4[r4 + g // 16] |= np.uint32((3 if fp else 2) << (2 * (g % 16)))
+                    w1[r1 + g // 32] |= np.uint32(fp << (g % 32))
+    _, _, o1, l1, _ = run_prefill(w, dict(kind=1, group=2, words=w1), q, k, v)
+    _, _, o3, l3, _ = run_prefill(w, dict(b, kind=2, group=2, words=w4), q, k, v)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
 
 
 def test_varlen_permutation_equivariance():

@@ -22,7 +22,7 @@ TM_OK, TM_E_ARG, TM_E_SHAPE, TM_E_POLICY, TM_E_SPACE, TM_E_UNSUPPORTED, TM_E_HIP
 TM_F16, TM_BF16, TM_F32 = 0, 1, 2
 TM_SKIP, TM_INT4, TM_INT8, TM_FP16 = 0, 1, 2, 3
 TM_ROWS, TM_COLS = 0, 1
-TM_POLICY_BOUNDARIES, TM_POLICY_BITMASK = 0, 1
+TM_POLICY_BOUNDARIES, TM_POLICY_BITMASK, TM_POLICY_FOURWAY = 0, 1, 2
 TRAV_HEADER_BYTES = 256
 TRAV_MAGIC = 0x564D5454
 
@@ -177,21 +177,28 @@ def tm_quantize_pack(shape: Shape, x, out: QTensor, stream=None) -> QTensor:
 
 
 class Policy:
+    """Host/device copies of a tile policy: dict(kind=0, b8, b4, sink),
+    dict(kind=1, group, words) or dict(kind=2, b8, b4, sink, group, words)."""
+
     def __init__(self, pol: dict, device=None):
         self.kind = int(pol["kind"])
         self.b8 = self.b4 = None
         self.bits = None
-        if self.kind == TM_POLICY_BOUNDARIES:
+        b8p = b4p = None
+        sink = 0
+        if self.kind != TM_POLICY_BITMASK:
             self.b8 = np.ascontiguousarray(np.asarray(pol["b8"], dtype=np.int32))
             self.b4 = np.ascontiguousarray(np.asarray(pol["b4"], dtype=np.int32))
-            self.c = tm_policy(0, self.b8.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                               self.b4.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(pol.get("sink", 0)),
-                               None, 0, 1)
-        else:
+            b8p = self.b8.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+            b4p = self.b4.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+            sink = int(pol.get("sink", 0))
+        n_words, group = 0, 1
+        if self.kind != TM_POLICY_BOUNDARIES:
             import torch
             words = np.ascontiguousarray(np.asarray(pol["words"], dtype=np.uint32))
             self.bits = torch.from_numpy(words.view(np.int32).copy()).to(device) if device is not None else None
-            self.c = tm_policy(1, None, None, 0, _ptr(self.bits), int(words.size), int(pol["group"]))
+            n_words, group = int(words.size), int(pol["group"])
+        self.c = tm_policy(self.kind, b8p, b4p, sink, _ptr(self.bits), n_words, group)
 
 
 def traversal_bytes(shape: Shape, policy: Policy) -> int:

@@ -148,8 +148,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int KBYTES = KIND == 0 ? kBlock * D : kBlock * 2 * D;   // largest K tile
   constexpr int VBYTES = D * kBlock * 2;
   constexpr int BUF = KBYTES + VBYTES;
-  constexpr bool HAS4 = KIND == TM_POLICY_BOUNDARIES;
-  constexpr bool HAS16 = KIND == TM_POLICY_BITMASK;
+  constexpr bool HAS4 = KIND != TM_POLICY_BITMASK;      // boundaries and four-way
+  constexpr bool HAS16 = KIND != TM_POLICY_BOUNDARIES;  // bitmask and four-way
   typedef typename std::conditional<BF16, bf16x8, f16x8>::type q16_t;
 
   // two tile buffers, at LDS offsets 0 and kBufStride: the next tile streams
@@ -631,7 +631,9 @@ template <int D, int BQ>
 static hipError_t launch_prefill_k(const PrefillArgs& a, int kind, bool bf16, hipStream_t st) {
   if (kind == TM_POLICY_BOUNDARIES)
     return bf16 ? launch_prefill_t<D, BQ, 0, true>(a, st) : launch_prefill_t<D, BQ, 0, false>(a, st);
-  return bf16 ? launch_prefill_t<D, BQ, 1, true>(a, st) : launch_prefill_t<D, BQ, 1, false>(a, st);
+  if (kind == TM_POLICY_BITMASK)
+    return bf16 ? launch_prefill_t<D, BQ, 1, true>(a, st) : launch_prefill_t<D, BQ, 1, false>(a, st);
+  return bf16 ? launch_prefill_t<D, BQ, 2, true>(a, st) : launch_prefill_t<D, BQ, 2, false>(a, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st) {

@@ -9,6 +9,8 @@
 // Acceleration", abstract: routing decisions packed into compact bitmasks; one
 // bit governs a group of adjacent key tiles; FP16 or INT8 per group; all legal
 // groups routed; variable-length batches.
+// The four-way kind puts the two together: a 2-bit code per group either
+// leaves its tiles to the boundary rule (code 0) or sets INT4, INT8 or FP16.
 //
 // One thread per work item (sequence, query head, query tile).  Items are
 // ordered heavy-first: query tiles in descending index (more legal key tiles),
@@ -33,8 +35,10 @@ __device__ __forceinline__ int64_t items_at_or_above(const TravArgs& a, int i) {
 }
 
 __device__ __forceinline__ void put_run(RunEntry* runs, uint32_t& n, uint32_t first, uint32_t count,
-                                        uint32_t prec) {
-  if (count == 0) return;
+                                        uint32_t prec, uint32_t max_runs) {
+  // max_runs bounds every item's runs by construction; the check keeps a
+  // wrong bound from writing into the next item's slots
+  if (count == 0 || n >= max_runs) return;
   runs[n].ktile = first;
   runs[n].count_prec = count | (prec << 24);
   ++n;
@@ -111,39 +115,98 @@ __global__ __launch_bounds__(256) void trav_items_kernel(TravArgs a) {
     if (sink_extra && lo4 == 0) lo4 = 1;   // tile 0 leaves the INT4 band for the sink run
     const uint32_t c8 = lo8 <= jmax ? static_cast<uint32_t>(jmax - lo8 + 1) : 0u;
     const uint32_t c4 = hi4 >= lo4 ? static_cast<uint32_t>(hi4 - lo4 + 1) : 0u;
-    put_run(runs, nr, lo8, c8, TM_INT8);
-    if (sink_extra) put_run(runs, nr, 0, 1, TM_INT8);
-    put_run(runs, nr, lo4, c4, TM_INT4);
+    put_run(runs, nr, lo8, c8, TM_INT8, a.max_runs);
+    if (sink_extra) put_run(runs, nr, 0, 1, TM_INT8, a.max_runs);
+    put_run(runs, nr, lo4, c4, TM_INT4, a.max_runs);
     n8 = c8 + (sink_extra ? 1u : 0u);
     n4 = c4;
   } else {
     const int G = a.group;
+    const bool four = a.kind == TM_POLICY_FOURWAY;
+    const int per_word = four ? 16 : 32;
     int base = 0;
     for (int s = 0; s < seq; ++s) {
       const int ln = a.cu[s + 1] - a.cu[s];
       const int nk = (ln + a.bk - 1) / a.bk;
-      const int wpr = ((nk + G - 1) / G + 31) / 32;
+      const int wpr = ((nk + G - 1) / G + per_word - 1) / per_word;
       base += a.hq * seq_nq(a.cu, s, a.bq) * wpr;
     }
     const int nk = (len + a.bk - 1) / a.bk;
-    const int wpr = ((nk + G - 1) / G + 31) / 32;
+    const int wpr = ((nk + G - 1) / G + per_word - 1) / per_word;
     const int nq = seq_nq(a.cu, seq, a.bq);
     const uint32_t* row = a.bits + base + static_cast<size_t>(head * nq + qt) * wpr;
     const int ng = jmax / G + 1;
-    for (int pass = 0; pass < 2; ++pass) {        // FP16 runs first, then INT8
-      const uint32_t want = pass == 0 ? 1u : 0u;
-      int g = 0;
-      while (g < ng) {
-        const uint32_t bit = (row[g >> 5] >> (g & 31)) & 1u;
-        if (bit != want) { ++g; continue; }
-        int g1 = g;
-        while (g1 + 1 < ng && ((row[(g1 + 1) >> 5] >> ((g1 + 1) & 31)) & 1u) == want) ++g1;
-        const int first = g * G;
-        const int last = min((g1 + 1) * G - 1, jmax);
-        const uint32_t c = static_cast<uint32_t>(last - first + 1);
-        put_run(runs, nr, first, c, want ? TM_FP16 : TM_INT8);
-        if (want) n16 += c; else n8 += c;
-        g = g1 + 1;
+    if (!four) {
+      for (int pass = 0; pass < 2; ++pass) {        // FP16 runs first, then INT8
+        const uint32_t want = pass == 0 ? 1u : 0u;
+        int g = 0;
+        while (g < ng) {
+          const uint32_t bit = (row[g >> 5] >> (g & 31)) & 1u;
+          if (bit != want) { ++g; continue; }
+          int g1 = g;
+          while (g1 + 1 < ng && ((row[(g1 + 1) >> 5] >> ((g1 + 1) & 31)) & 1u) == want) ++g1;
+          const int first = g * G;
+          const int last = min((g1 + 1) * G - 1, jmax);
+          const uint32_t c = static_cast<uint32_t>(last - first + 1);
+          put_run(runs, nr, first, c, want ? TM_FP16 : TM_INT8, a.max_runs);
+          if (want) n16 += c; else n8 += c;
+          g = g1 + 1;
+        }
+      }
+    } else {
+      // boundary rule of this head: key tile j is INT8 from lo8, INT4 from lo4
+      // (by diagonal distance ri - j), the sink tile 0 INT8, the rest SKIP
+      const int b8 = a.b8[head], b4 = a.b4[head];
+      const int ri = qt * (a.bq / a.bk);
+      const int lo8 = b8 > 0 ? max(0, ri - b8 + 1) : (1 << 30);
+      const int lo4 = b4 > 0 ? max(0, ri - b4 + 1) : (1 << 30);
+      auto rule = [&](int j) -> uint32_t {
+        if (a.sink && j == 0) return TM_INT8;
+        return j >= lo8 ? TM_INT8 : (j >= lo4 ? TM_INT4 : TM_SKIP);
+      };
+      // one pass per precision (FP16, INT8, INT4) over constant pieces: a
+      // piece ends at a group edge or where the boundary rule may change.  A
+      // sink tile outside the INT8 band runs after the other INT8 tiles, the
+      // order of the boundary traversal, so all-zero codes reproduce it.
+      const bool late_sink = a.sink && lo8 > 0 && (row[0] & 3u) == 0u;
+      const uint32_t order[3] = {TM_FP16, TM_INT8, TM_INT4};
+      for (int pass = 0; pass < 3; ++pass) {
+        const uint32_t want = order[pass];
+        int rfirst = 0, rcount = 0;
+        for (int g = 0; g < ng; ++g) {
+          const uint32_t code = (row[g >> 4] >> (2 * (g & 15))) & 3u;
+          const int gend = min(g * G + G - 1, jmax);
+          int j = (late_sink && g == 0) ? 1 : g * G;
+          while (j <= gend) {
+            uint32_t p;
+            int pend = gend;
+            if (code != 0) {
+              p = code == 1 ? TM_INT4 : (code == 2 ? TM_INT8 : TM_FP16);
+            } else {
+              p = rule(j);
+              if (j == 0) pend = 0;                       // the sink tile stands alone
+              if (lo4 > j && lo4 <= pend) pend = lo4 - 1;
+              if (lo8 > j && lo8 <= pend) pend = lo8 - 1;
+            }
+            if (p == want) {
+              if (rcount > 0 && rfirst + rcount == j) {
+                rcount += pend - j + 1;
+              } else {
+                put_run(runs, nr, rfirst, static_cast<uint32_t>(rcount), want, a.max_runs);
+                rfirst = j;
+                rcount = pend - j + 1;
+              }
+            }
+            j = pend + 1;
+          }
+        }
+        put_run(runs, nr, rfirst, static_cast<uint32_t>(rcount), want, a.max_runs);
+        if (want == TM_INT8 && late_sink) put_run(runs, nr, 0, 1, TM_INT8, a.max_runs);
+        // counts of this pass
+        uint32_t cnt = 0;
+        for (uint32_t r = 0; r < nr; ++r)
+          if ((runs[r].count_prec >> 24) == want) cnt += runs[r].count_prec & 0xFFFFFFu;
+        if (want == TM_FP16) n16 = cnt; else if (want == TM_INT8) n8 = cnt; else n4 = cnt;
       }
     }
   }

@@ -74,8 +74,13 @@ struct TravLayout {
 
 TravLayout trav_layout(const tm_shape* s, const ShapeInfo& si, const tm_policy* p) {
   TravLayout L;
+  // boundaries: INT8 band, sink, INT4 band.  Bitmask: at most one run per
+  // group.  Four-way: runs split at group edges and, inside code-0 groups, at
+  // the three points where the boundary rule changes (sink, INT4, INT8 band).
+  const int ngmax = p->kind == TM_POLICY_BOUNDARIES ? 0 : (si.maxnk + p->group - 1) / p->group;
   L.max_runs = p->kind == TM_POLICY_BOUNDARIES ? 3u
-                                               : static_cast<uint32_t>(std::max(1, (si.maxnk + p->group - 1) / p->group));
+               : p->kind == TM_POLICY_BITMASK ? static_cast<uint32_t>(std::max(1, ngmax))
+                                              : static_cast<uint32_t>(ngmax + 3);
   L.seq_off = TM_TRAV_HEADER_BYTES;
   L.item_off = align256(L.seq_off + sizeof(SeqEntry) * static_cast<size_t>(s->nseq));
   L.run_off = align256(L.item_off + sizeof(ItemEntry) * static_cast<size_t>(si.n_items));
@@ -83,13 +88,15 @@ TravLayout trav_layout(const tm_shape* s, const ShapeInfo& si, const tm_policy* 
   return L;
 }
 
-int64_t bitmask_words(const tm_shape* s, int group) {
+// Words of a bitmask (per_word = 32 one-bit codes) or four-way code map
+// (per_word = 16 two-bit codes) for this shape.
+int64_t policy_words(const tm_shape* s, int group, int per_word) {
   int64_t w = 0;
   for (int i = 0; i < s->nseq; ++i) {
     const int64_t len = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
     const int64_t nk = (len + s->bk - 1) / s->bk;
     const int64_t ng = (nk + group - 1) / group;
-    w += static_cast<int64_t>(s->hq) * ((len + s->bq - 1) / s->bq) * ((ng + 31) / 32);
+    w += static_cast<int64_t>(s->hq) * ((len + s->bq - 1) / s->bq) * ((ng + per_word - 1) / per_word);
   }
   return w;
 }
@@ -182,7 +189,9 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   tm_status st = check_shape(shape, true, &si);
   if (st != TM_OK) return st;
   if (policy == nullptr || trav_bytes == nullptr) return TM_E_ARG;
-  if (policy->kind == TM_POLICY_BOUNDARIES) {
+  const int kind = policy->kind;
+  if (kind != TM_POLICY_BOUNDARIES && kind != TM_POLICY_BITMASK && kind != TM_POLICY_FOURWAY) return TM_E_ARG;
+  if (kind != TM_POLICY_BITMASK) {   // boundaries, alone or under the four-way codes
     if (policy->b8 == nullptr || policy->b4 == nullptr) return TM_E_ARG;
     if (shape->hq > kMaxHeadsArg) return TM_E_UNSUPPORTED;
     if (policy->sink != 0 && policy->sink != 1) return TM_E_POLICY;
@@ -191,12 +200,12 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
       if (b8 < 0 || b4 < 0 || b8 > b4) return TM_E_POLICY;
       if (b4 == 0 && !policy->sink) return TM_E_POLICY;
     }
-  } else if (policy->kind == TM_POLICY_BITMASK) {
+  }
+  if (kind != TM_POLICY_BOUNDARIES) {   // a packed per-group map
     if (policy->group < 1) return TM_E_POLICY;
-    if (policy->n_words < bitmask_words(shape, policy->group)) return TM_E_POLICY;
+    if (policy->n_words < policy_words(shape, policy->group, kind == TM_POLICY_BITMASK ? 32 : 16))
+      return TM_E_POLICY;
     if (policy->bits == nullptr && policy->n_words > 0) return TM_E_ARG;
-  } else {
-    return TM_E_ARG;
   }
   const TravLayout L = trav_layout(shape, si, policy);
   if (trav == nullptr) {
@@ -219,8 +228,8 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   a.bq = shape->bq;
   a.bk = shape->bk;
   a.kind = policy->kind;
-  a.sink = policy->kind == TM_POLICY_BOUNDARIES ? policy->sink : 0;
-  a.group = policy->kind == TM_POLICY_BITMASK ? policy->group : 1;
+  a.sink = kind != TM_POLICY_BITMASK ? policy->sink : 0;
+  a.group = kind != TM_POLICY_BOUNDARIES ? policy->group : 1;
   a.n_items = static_cast<uint32_t>(si.n_items);
   a.max_runs = L.max_runs;
   a.nblk = static_cast<uint32_t>(si.nblk);
@@ -228,7 +237,7 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   a.item_off = static_cast<uint32_t>(L.item_off);
   a.run_off = static_cast<uint32_t>(L.run_off);
   a.bits_off = 0;
-  if (policy->kind == TM_POLICY_BOUNDARIES) {
+  if (kind != TM_POLICY_BITMASK) {
     for (int h = 0; h < shape->hq; ++h) {
       a.b8[h] = policy->b8[h];
       a.b4[h] = policy->b4[h];
@@ -258,7 +267,8 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
   tm_status st = check_shape(shape, true, &si);
   if (st != TM_OK) return st;
   if (trav == nullptr || q == nullptr || k == nullptr || o == nullptr) return TM_E_ARG;
-  if (policy_kind != TM_POLICY_BOUNDARIES && policy_kind != TM_POLICY_BITMASK) return TM_E_ARG;
+  if (policy_kind != TM_POLICY_BOUNDARIES && policy_kind != TM_POLICY_BITMASK && policy_kind != TM_POLICY_FOURWAY)
+    return TM_E_ARG;
   if (o_dtype != TM_F32 && o_dtype != TM_F16 && o_dtype != TM_BF16) return TM_E_ARG;
   if (n_dbg < 0 || (n_dbg > 0 && (dbg_qk == nullptr || dbg_tiles == nullptr))) return TM_E_ARG;
   if ((st = check_qtensor(qq, shape->hq, TM_ROWS, si.nblk, false)) != TM_OK) return st;

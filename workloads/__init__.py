@@ -6,8 +6,9 @@ classification, no scores).  Every array is drawn with
 ``numpy.random.default_rng([workload_id, stream])`` so that the HIP path and the
 CPU oracle receive identical bits.
 
-Streams: Q = 1, K = 2, V = 3, policy = 4, outlier channels = 5, decode query = 6.
-Values are N(0, 1) in float32, rounded half-to-even to the 16-bit input type.
+Streams: Q = 1, K = 2, V = 3, policy = 4, outlier channels = 5, decode query = 6,
+locality = 7.  Values are N(0, 1) in float32, rounded half-to-even to the
+16-bit input type.
 
 Workloads (the shapes are those of the attention layers the pages benchmark:
 Llama-3-8B-like heads, 32 query heads over 8 key/value heads, d = 128):
@@ -23,6 +24,10 @@ Llama-3-8B-like heads, 32 query heads over 8 key/value heads, d = 128):
 * ``long128k``    1 x 131072 tokens, 32/8 heads, d = 128, bf16, 128x64 tiles,
                   K outliers as gqa8k, per-head boundaries giving about
                   15 % INT8 / 25 % INT4 / 60 % skipped tiles, sink tile INT8.
+* ``local8k``     the gqa8k shape without outliers, plus a position signal
+                  shared by Q and K that gives every query head its own
+                  preference for nearby keys (see ``make_qkv``); the input of
+                  the boundary-calibration demonstration.
 * ``decode16x32k`` 16 sequences x 32768 cached tokens, 32/8 heads, d = 128,
                   fp16 cache and one fp16 query per sequence; cache blocks
                   tagged by boundaries (128, 320) in 64-token blocks with the
@@ -35,8 +40,8 @@ from typing import List, Optional
 
 import numpy as np
 
-WORKLOAD_IDS = {"toy512": 1, "gqa8k": 2, "varlen32k": 3, "long128k": 4, "decode16x32k": 5}
-STREAM_Q, STREAM_K, STREAM_V, STREAM_POLICY, STREAM_OUTLIER, STREAM_DQ = 1, 2, 3, 4, 5, 6
+WORKLOAD_IDS = {"toy512": 1, "gqa8k": 2, "varlen32k": 3, "long128k": 4, "decode16x32k": 5, "local8k": 6}
+STREAM_Q, STREAM_K, STREAM_V, STREAM_POLICY, STREAM_OUTLIER, STREAM_DQ, STREAM_LOCAL = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass
@@ -53,6 +58,7 @@ class Workload:
     sink: int = 0
     outliers: int = 0
     outlier_scale: float = 10.0
+    locality: float = 0.0         # largest per-head strength of the position signal
     # boundaries: draw ranges (inclusive) in key-tile units; or fixed lists
     b8_fixed: Optional[List[int]] = None
     b4_fixed: Optional[List[int]] = None
@@ -95,6 +101,8 @@ def get(name: str) -> Workload:
         # b8 in [145, 175], b4 - b8 in [296, 306]: about 15 % INT8, 25 % INT4, 60 % skip
         return Workload("long128k", [131072], 32, 8, 128, "bf16", outliers=4, sink=1,
                         b8_range=(145, 175), b4_gap=(296, 306))
+    if name == "local8k":
+        return Workload("local8k", [8192], 32, 8, 128, "bf16", locality=0.6, b4_range=(36, 57))
     if name == "decode16x32k":
         return Workload("decode16x32k", [32768] * 16, 32, 8, 128, "f16", decode=True,
                         dec_b8=128, dec_b4=320, sink=1, dec_tail=128)
@@ -158,6 +166,20 @@ def make_qkv(w: Workload):
     if len(ch):
         k[:, :, ch] *= np.float32(w.outlier_scale)
     v = _normal(w, STREAM_V, (T, w.hkv, w.d))
+    if w.locality > 0:
+        # r(t)[c] = sqrt(2) cos(w_c t + phi_c) with w_c log-uniform over periods
+        # of 128 .. 8192 tokens, added to every key and, times a per-head
+        # strength a_h ~ U[0, locality], to every query: the logit of key s for
+        # query t gains a_h * sum_c 2 cos(w_c t + phi_c) cos(w_c s + phi_c),
+        # about a_h * d at s = t and fading as |t - s| grows
+        rng = np.random.default_rng([w.wid, STREAM_LOCAL])
+        om = 2.0 * np.pi / np.exp(rng.uniform(np.log(128.0), np.log(8192.0), w.d))
+        ph = rng.uniform(0.0, 2.0 * np.pi, w.d)
+        a = rng.uniform(0.0, w.locality, w.hq).astype(np.float32)
+        pos = np.concatenate([np.arange(n) for n in w.seqlens]).astype(np.float64)
+        r = (np.sqrt(2.0) * np.cos(pos[:, None] * om[None, :] + ph[None, :])).astype(np.float32)
+        q += a[None, :, None] * r[:, None, :]
+        k += r[:, None, :]
     return round16(q, w.dtype), round16(k, w.dtype), round16(v, w.dtype)
 
 
