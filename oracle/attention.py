@@ -180,7 +180,9 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
     q64 [B][hq][d]; kq: K quantized (rows layout), vq: V quantized (any layout:
     the unpacked rows-layout codes are used); k64/v64 [T][hkv][d] hold the
     16-bit cache values read for FP16 blocks.
-    Block tags follow policy.decode_block_tags with per-KV-head (b8, b4).
+    Block tags follow policy.decode_block_tags with (b8, b4) of the query's KV
+    head, or of the query head itself when dpol["per_q_head"] is set (b8, b4
+    then have hq entries; the reading of a per-query-head decode map).
     INT blocks: score = tau * sk * (q . ck), value = sv * cv; FP16 blocks:
     score = tau * (q . k), value = v.  Returns O [B][hq][d]; with ``pairs`` (a
     list of (b, h)) only those outputs are computed (the rest stay zero).
@@ -198,9 +200,10 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
             if pairs is not None and (b, h) not in pairs:
                 continue
             kv = h // grp
-            tags = P.decode_block_tags(L, int(dpol["b8"][kv]), int(dpol["b4"][kv]),
+            mi = h if dpol.get("per_q_head", 0) else kv     # whose map tags the blocks
+            tags = P.decode_block_tags(L, int(dpol["b8"][mi]), int(dpol["b4"][mi]),
                                        int(dpol["sink"]), int(dpol["tail"]))
-            tags_all[(b, kv)] = tags
+            tags_all[(b, mi)] = tags
             sc_list, val_list = [], []
             for j, t in enumerate(tags):
                 n = min(BLOCK, L - j * BLOCK)

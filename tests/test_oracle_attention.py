@@ -292,3 +292,22 @@ def test_decode_fp16_equals_last_prefill_row():
     Od = A.decode([L], HQ, HKV, D, f64(q[L - 1:L]), Q.quantize(k, [L]), Q.quantize(v, [L], layout="cols"),
                   f64(k), f64(v), dpol)
     assert np.max(np.abs(Od[0] - Op[L - 1])) < 1e-13
+
+
+def test_decode_per_query_head_maps_reduce_to_per_kv_maps():
+    """A per-query-head map tags head h's blocks as a per-KV-head map holding
+    head h's (b8, b4) for every KV head would; heads of one KV group may
+    differ."""
+    q, k, v = _decode_inputs(16)
+    kq, vq = Q.quantize(k, DQ_SEQ), Q.quantize(v, DQ_SEQ, layout="cols")
+    f64 = lambda x: x.astype(np.float64)
+    b8, b4 = [1, 3, 0, 2], [2, 5, 4, 2]
+    dq = dict(b8=b8, b4=b4, sink=1, tail=100, per_q_head=1)
+    O = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dq)
+    for h in range(HQ):
+        dk = dict(b8=[b8[h]] * HKV, b4=[b4[h]] * HKV, sink=1, tail=100)
+        Oh = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dk)
+        assert np.array_equal(O[:, h], Oh[:, h])
+    # heads 0 and 1 share a KV head but not a map: their tags differ
+    _, tags = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dq, return_tags=True)
+    assert not np.array_equal(tags[(1, 0)], tags[(1, 1)])
