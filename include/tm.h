@@ -160,14 +160,20 @@ typedef struct tm_census {
   int64_t n_items, max_runs;
 } tm_census;
 
-/* Decode cache policy, per KV head (host arrays, at most 64 KV heads), in
- * 64-token blocks.
+/* Decode cache policy (host arrays; at most 64 KV heads and 256 query heads),
+ * in 64-token blocks.
  * For a cache of L tokens (the new token included) and block j:
  *  blocks overlapping the last tail_tokens tokens are FP16 (read from the
  *  16-bit keys and the t16 copy of V); otherwise delta = floor((L-1)/64) - j,
  *  INT8 if delta < b8 (or j == 0 with sink), INT4 if delta < b4, else SKIP.
+ * per_q_head = 0: b8, b4 hold one map per KV head (hkv entries), shared by
+ *  the KV head's query heads.  per_q_head = 1: one map per query head (hq
+ *  entries).  Consecutive query heads of a KV head with equal maps are
+ *  decoded together and share each cache block read; a group whose maps
+ *  differ reads its blocks once per distinct run of maps.
  * ([HyQuant] "How HyQuant works": recent window FP16, rest quantized;
- * [TriAttention] abstract: prefill codes reused in the decode cache.) */
+ * [TriAttention] abstract: prefill codes reused in the decode cache, two
+ * boundaries per head.) */
 typedef struct tm_dpolicy {
   const int32_t* b8;
   const int32_t* b4;
@@ -175,6 +181,7 @@ typedef struct tm_dpolicy {
   int32_t tail_tokens;
   const int32_t* lengths;   /* host [nseq] or NULL: current lengths, 1 <= lengths[s] <= the
                                cache shape's length of s (its capacity); NULL: the capacity */
+  int32_t per_q_head;       /* 0: b8/b4 per KV head; 1: per query head */
 } tm_dpolicy;
 
 /* Traversal buffer layout (device, written by tm_build_traversal, read by
@@ -277,8 +284,10 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
  *  kq (TM_ROWS, hkv heads), vq (TM_COLS, hkv heads, t16 set): the cache, as
  *    produced by tm_quantize_pack over the cached tokens.
  *  k16 [T][hkv][d] 16-bit (device): keys read for FP16 blocks.
- *  policy: per-KV-head tags (tm_dpolicy); with lengths set, the tags and the
- *    keys follow each sequence's current length.
+ *  policy: block tags per KV head or per query head (tm_dpolicy); with
+ *    lengths set, the tags and the keys follow each sequence's current length.
+ *    The workspace size depends on the maps only through their runs of equal
+ *    maps (query the size with the policy that will be used).
  *  o [nseq][hq][d] of o_dtype (TM_F32 or TM_F16, device).
  *  ws (device): workspace; ws == NULL writes the required size to *ws_bytes
  *    and returns TM_OK without GPU work; otherwise *ws_bytes is its capacity.
@@ -286,8 +295,9 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
  * INT blocks: score = scale * sk * (q . ck), value = sv * cv; FP16 blocks:
  * score = scale * (q . k), value = v ([HyQuant] "How HyQuant works":
  * dequantization fused with attention).
- * Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY, TM_E_SPACE, TM_E_UNSUPPORTED
- * (hq/hkv > 16, more than 64 KV heads, or a sequence whose 16-bit keys or
+ * Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY (bad boundaries, sink, tail or
+ * per_q_head), TM_E_SPACE, TM_E_UNSUPPORTED
+ * (hq/hkv > 16, more than 64 KV heads or 256 query heads, or a sequence whose 16-bit keys or
  * fp16 V copy span 2 GiB or more: ceil(len / 64) * 64 * hkv * d * 2 >= 2^31),
  * TM_E_HIP. */
 tm_status tm_decode(const tm_shape* cache, const void* q,

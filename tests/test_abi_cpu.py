@@ -269,6 +269,29 @@ def test_decode_validation_and_workspace(B):
                        ctypes.byref(n), None) == B.TM_E_SHAPE
 
 
+def test_decode_per_query_head_maps_validation_and_workspace(B):
+    L = B.lib()
+    s = _shape(B, [32768] * 16, hq=32, hkv=8, d=128)
+    n = ctypes.c_size_t(0)
+
+    def size(dp):
+        return L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(dp.c), None, 2, None,
+                           ctypes.byref(n), None)
+
+    # maps that agree inside every group: one class per KV head, the per-KV workspace
+    same = B.DPolicy(dict(b8=[128] * 32, b4=[320] * 32, sink=1, tail=128, per_q_head=1))
+    assert size(same) == B.TM_OK and n.value == 16 * 32 * 16 * 130 * 4
+    # all maps distinct: 32 classes -> 16 x 32 pairs -> 4 splits
+    mixed = B.DPolicy(dict(b8=list(range(100, 132)), b4=[400] * 32, sink=1, tail=128, per_q_head=1))
+    assert size(mixed) == B.TM_OK and n.value == 16 * 32 * 4 * 130 * 4
+    # the query-head maps are all checked (head 20 is past the 8 KV heads)
+    bad = B.DPolicy(dict(b8=[1] * 20 + [9] + [1] * 11, b4=[4] * 32, sink=1, tail=128, per_q_head=1))
+    assert size(bad) == B.TM_E_POLICY
+    flag = B.DPolicy(dict(b8=[1] * 32, b4=[4] * 32, sink=1, tail=128, per_q_head=1))
+    flag.c.per_q_head = 2
+    assert size(flag) == B.TM_E_POLICY
+
+
 def test_growing_cache_validation(B):
     """Lengths of a growing cache are checked against the capacities before any
     GPU work: tm_decode through tm_dpolicy.lengths, tm_cache_append directly."""

@@ -341,6 +341,28 @@ def test_decode_small(seqlens, dpol, d, dtype):
     compare(o, O, what=f"decode {seqlens} {dtype}")
 
 
+@pytest.mark.parametrize("hq,hkv,b8,b4", [
+    # groups of 4 with maps that differ inside a group, runs of equal maps, and
+    # one group whose maps agree
+    (8, 2, [1, 1, 3, 0, 2, 2, 2, 2], [4, 9, 9, 2, 6, 6, 6, 6]),
+    # groups of 8 (the unpacked softmax) cut into classes of 1, 3 and 4 heads
+    (16, 2, [0] + [2] * 3 + [5] * 4 + [1] * 8, [3] + [8] * 3 + [40] * 4 + [2] * 8),
+])
+def test_decode_per_query_head_maps(hq, hkv, b8, b4):
+    dpol = dict(b8=b8, b4=b4, sink=1, tail=100, per_q_head=1)
+    o, O = _decode_case([300, 2100, 64, 1000], dpol, hq=hq, hkv=hkv)
+    compare(o, O, what=f"decode per-query-head maps hq={hq}")
+
+
+def test_decode_uniform_per_query_head_maps_equal_per_kv_maps():
+    """Per-query-head maps that agree inside each group take the per-KV-head
+    launch: the same outputs bit for bit."""
+    seqlens = [1500, 3000]
+    o1, _ = _decode_case(seqlens, dict(b8=[3, 5], b4=[9, 20], sink=1, tail=128))
+    o2, _ = _decode_case(seqlens, dict(b8=[3] * 4 + [5] * 4, b4=[9] * 4 + [20] * 4, sink=1, tail=128, per_q_head=1))
+    assert np.array_equal(o1, o2)
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(2, 2, 128), (6, 2, 128), (16, 2, 128), (16, 1, 64)])
 def test_decode_group_sizes(hq, hkv, d):
     """Query groups of 1, 3, 8 and 16 heads per KV head: groups of up to 4

@@ -55,7 +55,7 @@ class tm_census(ctypes.Structure):
 class tm_dpolicy(ctypes.Structure):
     _fields_ = [("b8", ctypes.POINTER(ctypes.c_int32)), ("b4", ctypes.POINTER(ctypes.c_int32)),
                 ("sink", ctypes.c_int32), ("tail_tokens", ctypes.c_int32),
-                ("lengths", ctypes.POINTER(ctypes.c_int32))]
+                ("lengths", ctypes.POINTER(ctypes.c_int32)), ("per_q_head", ctypes.c_int32)]
 
 
 class TMError(RuntimeError):
@@ -251,7 +251,7 @@ class DPolicy:
         self.b4 = np.ascontiguousarray(np.asarray(dpol["b4"], dtype=np.int32))
         self.c = tm_dpolicy(self.b8.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                             self.b4.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(dpol["sink"]),
-                            int(dpol["tail"]), None)
+                            int(dpol["tail"]), None, int(dpol.get("per_q_head", 0)))
         self.lengths = None
         if lengths is not None:
             self.set_lengths(lengths)

@@ -125,18 +125,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   typedef UnitRegs<D> Regs;
 
   const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int grp = a.hq / a.hkv;
+  const int split = blockIdx.x, cl = blockIdx.y, b = blockIdx.z;
+  // head class: grp consecutive query heads from h0, all reading KV head kv
+  const int cls = a.cls[cl];
+  const int kv = cls & 1023, h0 = (cls >> 10) & 1023, grp = cls >> 20;
 
   // this sequence's extent (kernel-argument tables: scalar loads)
   const int tok0 = a.cu[b];
   const int L = a.len[b];
   const int blk0 = a.blk[b];
-  // this KV head's bands, in 64-token blocks
+  // this class's bands, in 64-token blocks
   const int nb = (L + kBlock - 1) / kBlock;
   const int jf = a.tail > 0 ? max(0, (L - a.tail) / kBlock) : nb;    // FP16 window [jf, nb)
-  const int jst = min(max(0, nb - a.b4[kv]), jf);                    // delta < b4 from here
-  const int j8lo = min(max(jst, nb - a.b8[kv]), jf);                 // INT8 band [j8lo, jf)
+  const int jst = min(max(0, nb - a.b4[cl]), jf);                    // delta < b4 from here
+  const int j8lo = min(max(jst, nb - a.b8[cl]), jf);                 // INT8 band [j8lo, jf)
   const bool sinkb = a.sink && j8lo > 0;                             // block 0 INT8, ahead of the bands
   const int j4lo = (sinkb && jst == 0) ? 1 : jst;                    // INT4 band [j4lo, j8lo)
   // Each split takes an even share of the INT4 band and an even share of the
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const size_t kvb0 = static_cast<size_t>(blk0) * a.hkv + kv;
   const uint32_t hkv = static_cast<uint32_t>(a.hkv);
 
-  // Q^T operand: column l16 = query head kv*grp + l16 (zero past the group).
+  // Q^T operand: column l16 = query head h0 + l16 (zero past the class).
   // Chunk c of lane group g holds 8 channels; the K operands use the same
   // channel map.  INT4 / 16-bit K: channels DG g + 8c ..  INT8 K: channels
   // (D/2) h + KW g + 8 sub .. with c = h (KW/8) + sub, so the four lane groups
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // (for the code offsets).
   // (rows past the group lie outside the resource and read as zeros)
   const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc(a.q + (static_cast<size_t>(b) * a.hq + kv * grp) * D, static_cast<uint32_t>(grp * D * 2));
+      make_rsrc(a.q + (static_cast<size_t>(b) * a.hq + h0) * D, static_cast<uint32_t>(grp * D * 2));
   auto q_operand = [&](bool map8, f16x8 (&qop)[NC]) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -531,7 +533,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     lt = __uint_as_float(y[0]) + __uint_as_float(y[1]);
   }
   if (l16 < grp) {
-    float* dst = a.ws + ((static_cast<size_t>(b) * a.hq + kv * grp + l16) * a.nsplit + split) * (D + 2);
+    float* dst = a.ws + ((static_cast<size_t>(b) * a.hq + h0 + l16) * a.nsplit + split) * (D + 2);
     if (g == 0) {
       dst[0] = m_run;
       dst[1] = lt;
@@ -597,9 +599,10 @@ static void launch_split(bool small, dim3 grid, const DecodeArgs& a, hipStream_t
   else hipLaunchKernelGGL((decode_split_kernel<D, BF16, false>), grid, dim3(64), 0, st, a);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st) {
-  dim3 grid(a.nsplit, a.hkv, a.nseq);
-  const bool small = a.hq / a.hkv <= 4;
+// Splits of `ncls` head classes (a.cls) over a.nseq sequences; small: every
+// class has at most 4 heads (the compacted softmax).
+hipError_t launch_decode_split(const DecodeArgs& a, int ncls, bool small, int d, bool bf16, hipStream_t st) {
+  dim3 grid(a.nsplit, ncls, a.nseq);
   if (d == 128) {
     if (bf16) launch_split<128, true>(small, grid, a, st);
     else launch_split<128, false>(small, grid, a, st);
@@ -607,8 +610,10 @@ hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st) 
     if (bf16) launch_split<64, true>(small, grid, a, st);
     else launch_split<64, false>(small, grid, a, st);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a, int d, hipStream_t st) {
   if (d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.nseq * a.hq), dim3(64), 0, st, a);
   else hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.nseq * a.hq), dim3(64), 0, st, a);
   return hipGetLastError();

@@ -106,14 +106,38 @@ struct DecodePlan {
   size_t ws_bytes;
 };
 
-DecodePlan decode_plan(const tm_shape* s, const tm_dpolicy* p) {
+// Decode head classes: the query heads of each KV head, cut into runs of
+// consecutive heads with the same cache map (one class per KV head when the
+// maps are per KV head, or when a group's per-query-head maps all agree).
+struct HeadClass {
+  int kv, h0, n, b8, b4;
+};
+
+std::vector<HeadClass> head_classes(const tm_shape* s, const tm_dpolicy* p) {
+  std::vector<HeadClass> out;
+  const int grp = s->hq / s->hkv;
+  for (int kv = 0; kv < s->hkv; ++kv) {
+    for (int r = 0; r < grp;) {
+      const int h = kv * grp + r;
+      const int mi = p->per_q_head ? h : kv;
+      int n = 1;
+      while (r + n < grp && p->per_q_head && p->b8[h + n] == p->b8[h] && p->b4[h + n] == p->b4[h]) ++n;
+      if (!p->per_q_head) n = grp;
+      out.push_back(HeadClass{kv, h, n, p->b8[mi], p->b4[mi]});
+      r += n;
+    }
+  }
+  return out;
+}
+
+DecodePlan decode_plan(const tm_shape* s, const tm_dpolicy* p, const std::vector<HeadClass>& cls) {
   int maxex = 1;
   for (int b = 0; b < s->nseq; ++b) {
     const int L = s->cu_seqlens[b + 1] - s->cu_seqlens[b];
     const int nb = (L + 63) / 64;
     const int jf = p->tail_tokens > 0 ? std::max(0, (L - p->tail_tokens) / 64) : nb;
-    for (int g = 0; g < s->hkv; ++g) {
-      const int jlo = std::max(0, nb - p->b4[g]);
+    for (const HeadClass& c : cls) {
+      const int jlo = std::max(0, nb - c.b4);
       const int js = std::min(jlo, jf);
       const int nex = (nb - js) + ((p->sink && js > 0) ? 1 : 0);
       maxex = std::max(maxex, nex);
@@ -122,7 +146,7 @@ DecodePlan decode_plan(const tm_shape* s, const tm_dpolicy* p) {
   // one wave per split, two per SIMD (each computes one unit of cache blocks
   // while the next streams into its registers): about 2048 splits, each
   // walking at least 6 blocks
-  const int pairs = s->nseq * s->hkv;
+  const int pairs = s->nseq * static_cast<int>(cls.size());
   int ns = (2048 + pairs - 1) / pairs;
   ns = std::min(ns, std::max(1, maxex / 6));
   ns = std::max(1, std::min(ns, 256));
@@ -319,11 +343,13 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   ShapeInfo si;
   tm_status st = check_shape(cache, false, &si);
   if (st != TM_OK) return st;
-  if (cache->hq / cache->hkv > 16 || cache->hkv > kMaxKvArg) return TM_E_UNSUPPORTED;
+  if (cache->hq / cache->hkv > 16 || cache->hkv > kMaxKvArg || cache->hq > kMaxHeadsArg) return TM_E_UNSUPPORTED;
   if (policy == nullptr || policy->b8 == nullptr || policy->b4 == nullptr || ws_bytes == nullptr) return TM_E_ARG;
   if (policy->sink != 0 && policy->sink != 1) return TM_E_POLICY;
   if (policy->tail_tokens < 0) return TM_E_POLICY;
-  for (int g = 0; g < cache->hkv; ++g) {
+  if (policy->per_q_head != 0 && policy->per_q_head != 1) return TM_E_POLICY;
+  const int nmaps = policy->per_q_head ? cache->hq : cache->hkv;
+  for (int g = 0; g < nmaps; ++g) {
     const int b8 = policy->b8[g], b4 = policy->b4[g];
     if (b8 < 0 || b4 < 0 || b8 > b4) return TM_E_POLICY;
     if (b4 == 0 && policy->tail_tokens == 0 && !policy->sink) return TM_E_POLICY;
@@ -335,7 +361,8 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     // a sequence's 16-bit rows (and fp16 V copy) must lie within 2 GiB of its first (32-bit offsets)
     if ((len + 63) / 64 * cache->hkv * 64 * cache->d * 2 >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
   }
-  const DecodePlan plan = decode_plan(cache, policy);
+  const std::vector<HeadClass> cls = head_classes(cache, policy);
+  const DecodePlan plan = decode_plan(cache, policy, cls);
   if (ws == nullptr) {
     *ws_bytes = plan.ws_bytes;
     return TM_OK;
@@ -369,10 +396,8 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   a.tail = policy->tail_tokens;
   a.nblk = si.nblk;
   a.tau_log2e = tau_log2e(cache);
-  for (int g = 0; g < cache->hkv; ++g) {
-    a.b8[g] = policy->b8[g];
-    a.b4[g] = policy->b4[g];
-  }
+  bool small = true;
+  for (const HeadClass& c : cls) small = small && c.n <= 4;
   // launches of at most kMaxSeqArg sequences, each with its sequences'
   // offsets in the kernel arguments
   const size_t osz = o_dtype == TM_F32 ? 4 : 2;
@@ -391,8 +416,20 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     c.q = a.q + static_cast<size_t>(s0) * cache->hq * cache->d;
     c.o = static_cast<uint8_t*>(o) + static_cast<size_t>(s0) * cache->hq * cache->d * osz;
     c.ws = a.ws + static_cast<size_t>(s0) * cache->hq * plan.nsplit * (cache->d + 2);
-    const hipError_t e = launch_decode(c, cache->d, cache->dtype == TM_BF16, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return TM_E_HIP;
+    // split launches of at most kMaxClsArg head classes, then one merge
+    for (size_t c0 = 0; c0 < cls.size(); c0 += kMaxClsArg) {
+      const int nc = static_cast<int>(std::min<size_t>(kMaxClsArg, cls.size() - c0));
+      for (int i = 0; i < nc; ++i) {
+        const HeadClass& h = cls[c0 + i];
+        c.cls[i] = h.kv | (h.h0 << 10) | (h.n << 20);
+        c.b8[i] = h.b8;
+        c.b4[i] = h.b4;
+      }
+      if (launch_decode_split(c, nc, small, cache->d, cache->dtype == TM_BF16, static_cast<hipStream_t>(stream)) !=
+          hipSuccess)
+        return TM_E_HIP;
+    }
+    if (launch_decode_combine(c, cache->d, static_cast<hipStream_t>(stream)) != hipSuccess) return TM_E_HIP;
   }
   return TM_OK;
 }

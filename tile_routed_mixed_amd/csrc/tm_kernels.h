@@ -7,6 +7,7 @@ namespace tmx {
 
 constexpr int kMaxHeadsArg = 256;   // boundary tables passed by value
 constexpr int kMaxKvArg = 64;
+constexpr int kMaxClsArg = 64;     // decode head classes per launch (tables passed by value)
 constexpr int kMaxSeqArg = 128;    // sequences per decode launch (tables passed by value)
 
 struct QuantArgs {
@@ -85,8 +86,12 @@ struct DecodeArgs {
   int nseq, hq, hkv, nsplit, sink, tail;
   int64_t nblk;
   float tau_log2e;
-  int32_t b8[kMaxKvArg];
-  int32_t b4[kMaxKvArg];
+  // head classes: class c (grid y) is `n` consecutive query heads from h0,
+  // all of KV head kv, with one cache map (b8[c], b4[c]);
+  // cls[c] = kv | h0 << 10 | n << 20
+  int32_t cls[kMaxClsArg];
+  int32_t b8[kMaxClsArg];
+  int32_t b4[kMaxClsArg];
   int32_t cu[kMaxSeqArg + 1];   // token offsets of this launch's sequences (absolute)
   int32_t len[kMaxSeqArg];      // their current lengths (at most cu[i + 1] - cu[i])
   int32_t blk[kMaxSeqArg];      // their first cache block (absolute)
@@ -96,6 +101,7 @@ hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipS
 hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t st);
+hipError_t launch_decode_split(const DecodeArgs& a, int ncls, bool small, int d, bool bf16, hipStream_t st);
+hipError_t launch_decode_combine(const DecodeArgs& a, int d, hipStream_t st);
 
 }  // namespace tmx
