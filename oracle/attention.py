@@ -7,7 +7,8 @@ An online softmax over any order of the executed tiles reaches, in exact
 arithmetic, the plain softmax over each row's executed key set, so that is what
 is computed here, row by row, in float64:
 
-* executed keys of row r (sequence-relative): c <= r whose tile is not SKIP;
+* executed keys of row r (sequence-relative): c <= r whose tile is not SKIP
+  (under the hybrid policy every c <= r, each with its own precision);
 * INT8 / INT4 tile: a = sum_d cq[r, d] * ck[c, d] (exact integers),
   score = a * sq(block of r) * sk(block of c) * tau;
 * FP16 tile: score = tau * sum_d q[r, d] * k[c, d] on the 16-bit values;
@@ -31,13 +32,18 @@ def _tau(d, tau):
     return 1.0 / math.sqrt(d) if tau is None else float(tau)
 
 
-def _rows_scores(r0, r1, h, kv, tok0, grid_h, bq, bk, q64, k64, qq, kq, blk0, tau):
+def _rows_scores(r0, r1, h, kv, tok0, grid_h, bq, bk, q64, k64, qq, kq, blk0, tau, hybrid=None):
     """Scores [r1-r0][r1] (float64, -inf where not executed) for sequence rows
-    r0..r1-1 of query head h; keys 0..r1-1 of the sequence."""
+    r0..r1-1 of query head h; keys 0..r1-1 of the sequence.  The precision of
+    (row, key) is its tile's entry of grid_h, or, with hybrid = (selected
+    keys, window), the hybrid policy's per-key precision."""
     nrow, nkey = r1 - r0, r1
     rows = np.arange(r0, r1)
     keys = np.arange(nkey)
-    prec = grid_h[(rows // bq)[:, None], (keys // bk)[None, :]]           # [nrow][nkey]
+    if hybrid is None:
+        prec = grid_h[(rows // bq)[:, None], (keys // bk)[None, :]]       # [nrow][nkey]
+    else:
+        prec = P.hybrid_prec(rows, keys, hybrid[0], hybrid[1])
     S = np.full((nrow, nkey), -np.inf)
     causal = keys[None, :] <= rows[:, None]
     qb = blk0 + rows // BLOCK
@@ -76,7 +82,8 @@ def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
     grp = hq // hkv
     O = np.full((T, hq, d), np.nan)
     lse = np.full((hq, T), np.nan)
-    gs = P.grids(seqlens, hq, bq, bk, pol)
+    hyb = int(pol["kind"]) == 3
+    gs = None if hyb else P.grids(seqlens, hq, bq, bk, pol)
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     plist = []
     if qtiles is not None:
@@ -94,7 +101,8 @@ def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
         kv = h // grp
         blk0 = int(qq["blk_start"][s])
         assert int(kq["blk_start"][s]) == blk0
-        g = gs[s][h]
+        g = None if hyb else gs[s][h]
+        hy = (P.hybrid_selected(pol, s, h, hq), int(pol["window"])) if hyb else None
         if rlist is None:
             chunks = [(i * bq, min((i + 1) * bq, S_len)) for i in range(P.n_tiles(S_len, bq))]
         elif qtiles is not None:
@@ -102,7 +110,7 @@ def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
         else:
             chunks = [(r, r + 1) for r in rlist]
         for r0, r1 in chunks:
-            Sc = _rows_scores(r0, r1, h, kv, tok0, g, bq, bk, q64, k64, qq, kq, blk0, tau)
+            Sc = _rows_scores(r0, r1, h, kv, tok0, g, bq, bk, q64, k64, qq, kq, blk0, tau, hy)
             m = np.max(Sc, axis=1)
             assert np.all(np.isfinite(m)), "a row with no executed key"
             p = np.exp(Sc - m[:, None])

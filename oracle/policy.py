@@ -34,6 +34,14 @@ Readings taken where the pages are silent:
   codes 1, 2, 3 set INT4, INT8, FP16.  All-zero codes give the boundary
   policy; codes drawn from {2, 3} give the bitmask policy with bit = (code
   == 3).
+* hybrid ([HyQuant] "How HyQuant works": selected vertical-line tokens and a
+  local sliding window stay FP16, the rest of the context is quantized):
+  precision is per (row, key) rather than per tile.  Key c of row r (c <= r)
+  is FP16 if c is in the selected set of the row's (sequence, query head) or
+  r - c < window, else INT8 (the rest is read as INT8, the cache precision the
+  other pages name; nothing is skipped).  Selected sets are index lists:
+  sel_off [nseq * hq + 1] row offsets (sequence-major, then query head) into
+  sel_idx, each list strictly increasing positions within its sequence.
 """
 from __future__ import annotations
 
@@ -223,3 +231,53 @@ def decode_block_tags(L: int, b8: int, b4: int, sink: int, tail: int, block: int
             dl = last - j
             tags[j] = INT8 if dl < b8 else (INT4 if dl < b4 else SKIP)
     return tags
+
+
+# ---------------------------------------------------------------- hybrid
+
+def hybrid_selected(pol, seq: int, head: int, hq: int) -> np.ndarray:
+    """Selected key positions of (sequence, query head), ascending."""
+    r = seq * hq + head
+    off = pol["sel_off"]
+    return np.asarray(pol["sel_idx"][int(off[r]):int(off[r + 1])], dtype=np.int64)
+
+
+def hybrid_prec(rows: np.ndarray, keys: np.ndarray, sel: np.ndarray, window: int) -> np.ndarray:
+    """[len(rows)][len(keys)] int8: FP16 where the key is selected or lies
+    within `window` tokens before the row, else INT8 (causality is the
+    caller's)."""
+    fp = np.isin(keys, sel)[None, :] | ((rows[:, None] - keys[None, :]) < window)
+    return np.where(fp, FP16, INT8).astype(np.int8)
+
+
+def hybrid_prec_loop(S: int, sel, window: int) -> np.ndarray:
+    """Brute force over every (r, c) with plain loops: [S][S] int8, ILLEGAL
+    above the diagonal."""
+    chosen = set(int(x) for x in sel)
+    g = np.full((S, S), ILLEGAL, np.int8)
+    for r in range(S):
+        for c in range(r + 1):
+            g[r, c] = FP16 if (c in chosen or r - c < window) else INT8
+    return g
+
+
+WIN_NONE, WIN_EDGE, WIN_FULL = 0, 1, 2
+
+
+def hybrid_tile_classes(S: int, bq: int, bk: int, window: int) -> np.ndarray:
+    """Window class of every legal tile, from the causal (row, key) pairs it
+    holds (rows and keys inside the sequence): FULL if all are within the
+    window, NONE if none is, else EDGE.  [nq][nk] int8, ILLEGAL outside."""
+    nq, nk = n_tiles(S, bq), n_tiles(S, bk)
+    out = np.full((nq, nk), ILLEGAL, np.int8)
+    for i in range(nq):
+        for j in range(nk):
+            if not is_legal(i, j, S, bq, bk):
+                continue
+            r = np.arange(i * bq, min((i + 1) * bq, S))[:, None]
+            c = np.arange(j * bk, min((j + 1) * bk, S))[None, :]
+            causal = c <= r
+            inwin = (r - c < window) & causal
+            n_in, n_all = int(inwin.sum()), int(causal.sum())
+            out[i, j] = WIN_FULL if n_in == n_all else (WIN_NONE if n_in == 0 else WIN_EDGE)
+    return out
