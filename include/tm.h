@@ -75,7 +75,8 @@ typedef enum tm_layout {
 typedef enum tm_policy_kind {
   TM_POLICY_BOUNDARIES = 0,
   TM_POLICY_BITMASK = 1,
-  TM_POLICY_FOURWAY = 2
+  TM_POLICY_FOURWAY = 2,
+  TM_POLICY_HYBRID = 3
 } tm_policy_kind;
 
 /* Problem shape.  cu_seqlens (host) and cu_seqlens_dev (device) hold the same
@@ -124,7 +125,7 @@ typedef struct tm_qtensor {
 
 /* Tile policy ([TriAttention] abstract: two diagonal-distance boundaries per
  * head; [TileMix] abstract: packed group bitmask; the four-way kind combines
- * the two).  b8/b4 are host arrays (at most 256 query heads); bits is device
+ * the two; [HyQuant] "How HyQuant works": token-granular FP16 retention).  b8/b4 are host arrays (at most 256 query heads); bits is device
  * memory read by the expansion kernel.
  *  Boundaries: b8[hq], b4[hq] in key-tile units, 0 <= b8 <= b4.  For query
  *   tile i and key tile j, delta = max(0, floor((i*bq - j*bk) / bk));
@@ -142,6 +143,16 @@ typedef struct tm_qtensor {
  *   rule (the only source of SKIP), codes 1, 2, 3 make them INT4, INT8, FP16.
  *   All-zero codes give the boundary policy; codes 2/3 only give the bitmask
  *   policy.
+ *  Hybrid: precision per (row, key) instead of per tile: key c of row r
+ *   (c <= r) is FP16 if c is in the selected list of the row's (sequence,
+ *   query head) or r - c < window, else INT8; nothing is skipped.  The
+ *   traversal holds, per work item, the tiles wholly inside the window
+ *   (FP16), those wholly outside (INT8), the tiles the window edge crosses
+ *   (run twice: FP16 on the pairs inside, INT8 on the rest), and the
+ *   item's visible selected keys gathered into compact FP16 tiles of 64;
+ *   selected keys are masked out of the regular tiles.  Lists are copied
+ *   into the traversal buffer; tm_gather_selected fills the gathered tiles
+ *   before tm_prefill.
  *  A tile is legal iff j*bk <= min((i+1)*bq, len) - 1; inside a legal tile key
  *  c is visible from row r iff c <= r. */
 typedef struct tm_policy {
@@ -152,6 +163,11 @@ typedef struct tm_policy {
   const uint32_t* bits;
   int64_t n_words;
   int32_t group;
+  /* TM_POLICY_HYBRID only (host arrays, read during tm_build_traversal and
+   * tm_gather_selected): */
+  const int32_t* sel_off;   /* [nseq*hq + 1]: list of row s*hq + h is sel_idx[sel_off[r], sel_off[r+1]) */
+  const int32_t* sel_idx;   /* selected key positions within the sequence, strictly increasing per list */
+  int32_t window;           /* sliding-window length in tokens, >= 0 */
 } tm_policy;
 
 /* Tile counts of a traversal (host). */
@@ -202,7 +218,22 @@ typedef struct tm_dpolicy {
  *                  order, adjacent equal tiles merged); SKIP tiles are never
  *                  listed ([TriAttention] abstract: precision-grouped
  *                  traversals; omitted tiles are skipped).
- *  bits_off:       0 (the bitmask stays in the caller's buffer). */
+ *  bits_off:       0 (the bitmask stays in the caller's buffer).
+ *  Hybrid traversals also hold (header words 16..23: window, n_gtiles and
+ *  the byte offsets of the tables below):
+ *   sel table      nseq*hq x uint32[4] {list start, list length, first
+ *                  gathered tile, first column-mask word};
+ *   sel idx        the selected positions (int32);
+ *   column masks   u64 per (sequence, query head, key tile): bit k set when
+ *                  key 64j + k is selected (masked out of regular tiles);
+ *   gathered tiles per tile: a uint32[4] {tok_start, blk_start, kv head,
+ *                  keys} entry, int32[64] key positions (INT32_MAX past the
+ *                  list), K rows [64][d] 16-bit and V^T [d][64] fp16.
+ *  Hybrid runs: prec 3 (FP16, whole tile in the window), 7 (FP16, window
+ *  part of an edge tile), 2 (INT8, whole tile outside), 6 (INT8, outside part
+ *  of an edge tile), 11 (gathered FP16 tiles: first = global gathered tile
+ *  index); the census counts tile passes (edge tiles twice, gathered tiles
+ *  as FP16) and no skips. */
 #define TM_TRAV_MAGIC 0x564D5454u
 #define TM_TRAV_VERSION 1u
 #define TM_TRAV_HEADER_BYTES 256
@@ -236,12 +267,24 @@ tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads,
  * the call synchronizes `stream` and fills it.
  * Errors: TM_E_ARG (unknown kind, NULL arrays), TM_E_SHAPE, TM_E_POLICY
  * (b8 > b4, negative boundaries, b4 == 0 without sink, group < 1, n_words too
- * small), TM_E_SPACE, TM_E_HIP.
+ * small; hybrid: window < 0, offsets not starting at 0 or decreasing, a list
+ * not strictly increasing or outside its sequence), TM_E_SPACE, TM_E_HIP.
+ * Hybrid policies synchronize `stream` (the lists are staged from the host).
  * ([TriAttention] abstract: boundaries generate precision-grouped traversals;
  * [TileMix] abstract: compact bitmasks, one bit per group of key tiles.) */
 tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
                              void* trav, size_t* trav_bytes, tm_census* census,
                              void* stream);
+
+/* Hybrid policies only: copy each selected key's 16-bit K row (from k
+ * [T][hkv][d], device) and fp16 V column (from vq->t16, TM_COLS) into the
+ * gathered tiles of a traversal built from `policy` for this shape.  Call
+ * after tm_quantize_pack of V and before tm_prefill; K and V must not change
+ * in between.  ([HyQuant] "How HyQuant works": selected tokens kept in FP16.)
+ * Errors: TM_E_ARG (NULL pointers, policy not hybrid), TM_E_SHAPE, TM_E_POLICY
+ * (invalid lists), TM_E_HIP. */
+tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, void* trav,
+                             const void* k, const tm_qtensor* vq, void* stream);
 
 /* Fused tile-routed causal prefill.
  *  trav: built by tm_build_traversal for this shape; policy_kind: the kind

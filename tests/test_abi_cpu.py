@@ -175,6 +175,54 @@ def test_fourway_validation_and_size(B):
     assert st() == B.TM_E_ARG
 
 
+def _hybrid(B, window, lists):
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    idx = np.concatenate([np.asarray(x, np.int32) for x in lists]).astype(np.int32)
+    return B.Policy(dict(kind=3, window=window, sel_off=off, sel_idx=idx))
+
+
+def test_hybrid_validation_and_size(B):
+    L = B.lib()
+    s = _shape(B, [1000, 130], hq=2, hkv=1, d=128)
+    lists = [[0, 5, 999], list(range(70)), [], [129]]     # rows (seq 0, h 0), (0, 1), (1, 0), (1, 1)
+    p = _hybrid(B, 128, lists)
+    n = ctypes.c_size_t(0)
+
+    def st(pp):
+        return L.tm_build_traversal(ctypes.byref(s.c), ctypes.byref(pp.c), None, ctypes.byref(n), None, None)
+
+    assert st(p) == B.TM_OK
+    align = lambda x: (x + 255) // 256 * 256
+    n_items = 2 * (8 + 2)
+    end = align(align(align(256 + 2 * 16) + 32 * n_items) + 8 * n_items * 5)   # 5 runs per item
+    n_gt = 1 + 2 + 0 + 1                                   # ceil(len / 64) per list
+    end = align(end + 16 * 4)                              # list table
+    end = align(end + 4 * (3 + 70 + 0 + 1))                # positions
+    end = align(end + 8 * (2 * 16 + 2 * 3))                # column masks: hq * nk per sequence
+    end = align(end + 512 * n_gt)                          # gathered tile headers
+    end = align(end + n_gt * 64 * 128 * 2)                 # K rows
+    end = align(end + n_gt * 128 * 64 * 2)                 # V^T
+    assert n.value == end
+    assert st(_hybrid(B, -1, lists)) == B.TM_E_POLICY                       # negative window
+    assert st(_hybrid(B, 0, [[0, 5, 5], [], [], []])) == B.TM_E_POLICY      # not strictly increasing
+    assert st(_hybrid(B, 0, [[], [], [130], []])) == B.TM_E_POLICY          # past the sequence end
+    assert st(_hybrid(B, 0, [[-1], [], [], []])) == B.TM_E_POLICY           # negative position
+    bad = _hybrid(B, 0, lists)
+    bad.sel_off[0] = 1
+    assert st(bad) == B.TM_E_POLICY                                        # offsets not from 0
+    bad = _hybrid(B, 0, lists)
+    bad.c.sel_off = None
+    assert st(bad) == B.TM_E_ARG
+    # gather: hybrid policies only, device pointers required
+    nb = s.nblk()
+    vq = _qt(B, 1, 1, nb, True)
+    assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(p.c), FAKE, None, ctypes.byref(vq), None) == \
+        B.TM_E_ARG
+    b = B.Policy(dict(kind=0, b8=[1, 1], b4=[2, 2], sink=0))
+    assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(b.c), FAKE, FAKE, ctypes.byref(vq), None) == \
+        B.TM_E_ARG
+
+
 def test_traversal_capacity(B):
     s = _shape(B, [512], hq=1, hkv=1, bq=64)
     p = B.Policy(dict(kind=0, b8=[2], b4=[5], sink=1))
@@ -223,7 +271,7 @@ def test_prefill_validation(B):
                             ctypes.byref(a["kq"]), ctypes.byref(a["vq"]), a["o"], a["odt"], None, None, None,
                             a["ndbg"], None)
     assert call(args(q=None)) == B.TM_E_ARG
-    assert call(args(kind=3)) == B.TM_E_ARG
+    assert call(args(kind=7)) == B.TM_E_ARG
     assert call(args(trav=None)) == B.TM_E_ARG
     assert call(args(odt=9)) == B.TM_E_ARG
     assert call(args(ndbg=2)) == B.TM_E_ARG

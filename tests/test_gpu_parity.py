@@ -271,6 +271,96 @@ def test_fourway_reduces_to_boundaries_and_bitmask():
     assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
 
 
+# ---------------------------------------------------------------------------- hybrid (token-granular)
+
+HYBRID_CASES = {
+    # name: (workload, seqlens, overrides, selected fraction, window)
+    "hyb_gqa": ("gqa8k", [700, 1, 300, 64], dict(hq=4, hkv=2), 0.1, 128),
+    "hyb_d64_bq64_bf16": ("long128k", [1000, 333], dict(hq=2, hkv=1, d=64, bq=64), 0.05, 100),
+    "hyb_nowindow": ("varlen32k", [900, 65], dict(hq=4, hkv=1), 0.2, 0),
+    "hyb_allwindow": ("varlen32k", [500, 129], dict(hq=2, hkv=2), 0.1, 10 ** 6),
+    "hyb_mask_bits": ("gqa8k", [700], dict(hq=2, hkv=1), None, 40),
+}
+
+
+def _hyb_case(name):
+    wl, seqlens, kw, frac, win = HYBRID_CASES[name]
+    w = W.small(wl, seqlens, **kw)
+    if frac is None:   # keys at the sign bit and the top bit of the 64-bit column masks
+        lists = [[14, 31, 39, 63, 64, 95, 127, 300, 351]] * w.hq
+        off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+        return w, dict(kind=3, window=win, sel_off=off, sel_idx=np.concatenate(lists).astype(np.int32))
+    return w, W.make_selection(w, frac, win)
+
+
+def _check_hybrid_traversal(w, pol, p, census):
+    import tile_routed_mixed_amd as T
+    tr = T.read_traversal(p.trav.cpu().numpy())
+    want = {}
+    n_full = n_edge = n_none = n_g = 0
+    gbase, g = {}, 0
+    for s_, S in enumerate(w.seqlens):
+        cls = OP.hybrid_tile_classes(S, w.bq, w.bk, pol["window"])
+        for h in range(w.hq):
+            sel = OP.hybrid_selected(pol, s_, h, w.hq)
+            gbase[(s_, h)] = g
+            g += -(-len(sel) // 64)
+            for i in range(cls.shape[0]):
+                rl = min((i + 1) * w.bq, S) - 1
+                ng = -(-int(np.sum(sel <= rl)) // 64)
+                want[(s_, h, i)] = (set(np.nonzero(cls[i] == OP.WIN_FULL)[0].tolist()),
+                                    set(np.nonzero(cls[i] == OP.WIN_EDGE)[0].tolist()),
+                                    set(np.nonzero(cls[i] == OP.WIN_NONE)[0].tolist()), ng)
+                n_full += len(want[(s_, h, i)][0])
+                n_edge += len(want[(s_, h, i)][1])
+                n_none += len(want[(s_, h, i)][2])
+                n_g += ng
+    assert census["fp16"] == n_full + n_edge + n_g and census["int8"] == n_edge + n_none
+    assert census["int4"] == 0 and census["skip"] == 0
+    assert tr["n_items"] == len(want)
+    for n in range(tr["n_items"]):
+        s_, h, qt, nr = (int(x) for x in tr["items"][n, :4])
+        got = {3: set(), 7: set(), 6: set(), 2: set()}
+        ng = 0
+        for r in range(nr):
+            first, cp = (int(x) for x in tr["runs"][n, r])
+            cnt, prec = cp & 0xFFFFFF, cp >> 24
+            if prec == 11:
+                assert first == gbase[(s_, h)]
+                ng += cnt
+            else:
+                got[prec] |= set(range(first, first + cnt))
+        full, edge, none, wng = want[(s_, h, qt)]
+        assert got[3] == full and got[7] == edge and got[6] == edge and got[2] == none, (s_, h, qt)
+        assert ng == wng
+
+
+@pytest.mark.parametrize("case", list(HYBRID_CASES))
+def test_hybrid_prefill(case):
+    w, pol = _hyb_case(case)
+    q, k, v = _inputs(w)
+    p, census, o, lse, _ = run_prefill(w, pol, q, k, v)
+    _check_hybrid_traversal(w, pol, p, census)
+    O, L, _, _ = oracle_prefill(w, pol, q, k, v)
+    compare(o, O, lse, L, what=case)
+
+
+def test_hybrid_reduces_to_fp16_and_int8_kernels():
+    """No selected key: a window covering every row runs the bitmask kernel's
+    all-FP16 work, a zero window the boundary kernel's all-INT8 work, tile for
+    tile in the same order: same outputs bit for bit."""
+    w = W.small("gqa8k", [900, 300], hq=4, hkv=2)
+    q, k, v = _inputs(w)
+    none = dict(kind=3, sel_off=np.zeros(len(w.seqlens) * w.hq + 1, np.int32), sel_idx=np.zeros(0, np.int32))
+    _, tot = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 4)
+    _, _, o1, l1, _ = run_prefill(w, dict(kind=1, group=4, words=np.full(tot, 0xFFFFFFFF, np.uint32)), q, k, v)
+    _, _, o2, l2, _ = run_prefill(w, dict(none, window=10 ** 6), q, k, v)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    _, _, o3, l3, _ = run_prefill(w, dict(kind=0, b8=[10 ** 6] * 4, b4=[10 ** 6] * 4, sink=0), q, k, v)
+    _, _, o4, l4, _ = run_prefill(w, dict(none, window=0), q, k, v)
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+
+
 def test_varlen_permutation_equivariance():
     """Permuting the sequences of a varlen batch permutes the outputs: every
     sequence's rows come out bit for bit the same."""

@@ -22,7 +22,7 @@ TM_OK, TM_E_ARG, TM_E_SHAPE, TM_E_POLICY, TM_E_SPACE, TM_E_UNSUPPORTED, TM_E_HIP
 TM_F16, TM_BF16, TM_F32 = 0, 1, 2
 TM_SKIP, TM_INT4, TM_INT8, TM_FP16 = 0, 1, 2, 3
 TM_ROWS, TM_COLS = 0, 1
-TM_POLICY_BOUNDARIES, TM_POLICY_BITMASK, TM_POLICY_FOURWAY = 0, 1, 2
+TM_POLICY_BOUNDARIES, TM_POLICY_BITMASK, TM_POLICY_FOURWAY, TM_POLICY_HYBRID = 0, 1, 2, 3
 TRAV_HEADER_BYTES = 256
 TRAV_MAGIC = 0x564D5454
 
@@ -43,7 +43,9 @@ class tm_qtensor(ctypes.Structure):
 class tm_policy(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("b8", ctypes.POINTER(ctypes.c_int32)),
                 ("b4", ctypes.POINTER(ctypes.c_int32)), ("sink", ctypes.c_int32),
-                ("bits", ctypes.c_void_p), ("n_words", ctypes.c_int64), ("group", ctypes.c_int32)]
+                ("bits", ctypes.c_void_p), ("n_words", ctypes.c_int64), ("group", ctypes.c_int32),
+                ("sel_off", ctypes.POINTER(ctypes.c_int32)), ("sel_idx", ctypes.POINTER(ctypes.c_int32)),
+                ("window", ctypes.c_int32)]
 
 
 class tm_census(ctypes.Structure):
@@ -86,6 +88,9 @@ def lib():
         L.tm_build_traversal.restype = i32
         L.tm_build_traversal.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp,
                                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(tm_census), vp]
+        L.tm_gather_selected.restype = i32
+        L.tm_gather_selected.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp, vp,
+                                         ctypes.POINTER(tm_qtensor), vp]
         L.tm_prefill.restype = i32
         L.tm_prefill.argtypes = [ctypes.POINTER(tm_shape), vp, i32, vp, vp, ctypes.POINTER(tm_qtensor),
                                  ctypes.POINTER(tm_qtensor), ctypes.POINTER(tm_qtensor), vp, i32, vp, vp, vp,
@@ -178,27 +183,42 @@ def tm_quantize_pack(shape: Shape, x, out: QTensor, stream=None) -> QTensor:
 
 class Policy:
     """Host/device copies of a tile policy: dict(kind=0, b8, b4, sink),
-    dict(kind=1, group, words) or dict(kind=2, b8, b4, sink, group, words)."""
+    dict(kind=1, group, words), dict(kind=2, b8, b4, sink, group, words) or
+    dict(kind=3, window, sel_off, sel_idx)."""
 
     def __init__(self, pol: dict, device=None):
         self.kind = int(pol["kind"])
         self.b8 = self.b4 = None
         self.bits = None
+        self.sel_off = self.sel_idx = None
         b8p = b4p = None
         sink = 0
-        if self.kind != TM_POLICY_BITMASK:
+        if self.kind in (TM_POLICY_BOUNDARIES, TM_POLICY_FOURWAY):
             self.b8 = np.ascontiguousarray(np.asarray(pol["b8"], dtype=np.int32))
             self.b4 = np.ascontiguousarray(np.asarray(pol["b4"], dtype=np.int32))
             b8p = self.b8.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
             b4p = self.b4.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
             sink = int(pol.get("sink", 0))
         n_words, group = 0, 1
-        if self.kind != TM_POLICY_BOUNDARIES:
+        if self.kind in (TM_POLICY_BITMASK, TM_POLICY_FOURWAY):
             import torch
             words = np.ascontiguousarray(np.asarray(pol["words"], dtype=np.uint32))
             self.bits = torch.from_numpy(words.view(np.int32).copy()).to(device) if device is not None else None
             n_words, group = int(words.size), int(pol["group"])
         self.c = tm_policy(self.kind, b8p, b4p, sink, _ptr(self.bits), n_words, group)
+        if self.kind == TM_POLICY_HYBRID:
+            self.sel_off = np.ascontiguousarray(np.asarray(pol["sel_off"], dtype=np.int32))
+            self.sel_idx = np.ascontiguousarray(np.asarray(pol["sel_idx"], dtype=np.int32))
+            self.c.sel_off = self.sel_off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+            self.c.sel_idx = self.sel_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+            self.c.window = int(pol["window"])
+
+
+def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, vq: "QTensor", stream=None):
+    """Hybrid policies: copy the selected keys' K rows and V columns into the
+    traversal's gathered tiles."""
+    _check(lib().tm_gather_selected(ctypes.byref(shape.c), ctypes.byref(policy.c), _ptr(trav), _ptr(k),
+                                    ctypes.byref(vq.c), _stream(stream)), "tm_gather_selected")
 
 
 def traversal_bytes(shape: Shape, policy: Policy) -> int:

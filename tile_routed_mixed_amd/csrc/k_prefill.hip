@@ -148,8 +148,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int KBYTES = KIND == 0 ? kBlock * D : kBlock * 2 * D;   // largest K tile
   constexpr int VBYTES = D * kBlock * 2;
   constexpr int BUF = KBYTES + VBYTES;
-  constexpr bool HAS4 = KIND != TM_POLICY_BITMASK;      // boundaries and four-way
-  constexpr bool HAS16 = KIND != TM_POLICY_BOUNDARIES;  // bitmask and four-way
+  constexpr bool HAS4 = KIND == TM_POLICY_BOUNDARIES || KIND == TM_POLICY_FOURWAY;
+  constexpr bool HAS16 = KIND != TM_POLICY_BOUNDARIES;  // bitmask, four-way, hybrid
+  constexpr bool HYB = KIND == TM_POLICY_HYBRID;        // per-key precision (see below)
   typedef typename std::conditional<BF16, bf16x8, f16x8>::type q16_t;
 
   // two tile buffers, at LDS offsets 0 and kBufStride: the next tile streams
@@ -206,6 +207,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if constexpr (HAS4) cp_k4.init(w, lane, D / 2);
   if constexpr (HAS16) cp_k16.init(w, lane, kpitch16);
 
+  // ---- hybrid policies: key c of row r is FP16 if c is selected or r - c <
+  // window, else INT8.  Regular tiles mask the selected keys out (one 64-bit
+  // column mask per key tile) and, on tiles the window edge crosses, keep
+  // only the pairs inside (FP16 pass) or outside (INT8 pass) the window; the
+  // selected keys run as gathered FP16 tiles, masked by their positions.
+  TileCopy<kBlock, D / 8, false> cp_kg;
+  __amdgpu_buffer_rsrc_t rs_kg = rs_v, rs_vg = rs_v;
+  const uint64_t* cmask = nullptr;
+  int win = 0;
+  if constexpr (HYB) {
+    win = static_cast<int>(th->window);
+    const SelEntry sel = reinterpret_cast<const SelEntry*>(a.trav + th->sel_tab_off)[it.seq * a.hq + head];
+    cmask = reinterpret_cast<const uint64_t*>(a.trav + th->cm_off) + sel.cm_base;
+    rs_kg = make_rsrc(a.trav + th->gk_off, th->n_gtiles * (kBlock * D * 2));
+    rs_vg = make_rsrc(a.trav + th->gv_off, th->n_gtiles * VBYTES);
+    cp_kg.init(w, lane, D * 2);
+  }
+
   // ---- per-lane LDS read offsets.  Key rows are read in the order
   // sigma(kb, l16) = sigma(0, l16) + 32 (kb >> 1) + 4 (kb & 1); the swizzle
   // depends on row bits the kb terms leave alone, so every 16-key block kb and
@@ -232,6 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the item: key tile | precision << 24, and its score scale (log2 units).
   uint32_t tl_jp = 0u;
   float tl_cs = 0.0f;
+  uint32_t tl_cm0 = 0u, tl_cm1 = 0u;   // hybrid: the tile's column mask
   int rr = 0, rcum = 0;   // first run not wholly consumed, tiles before it
   auto expand = [&](int c) {
     const int t = c * 64 + lane;
@@ -252,21 +272,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ++rr;
     }
     tl_jp = jp;
-    const uint32_t pj = jp >> 24;
+    const uint32_t pj = jp >> 24, pc = pj & 3u;
     const size_t kb = kv_blk0 + static_cast<size_t>(jp & 0xFFFFFFu) * hkv;
     float cs = tau;
-    if (pj == TM_INT8) cs = (sq8 * a.ks8[kb]) * tau;
-    else if (HAS4 && pj == TM_INT4) cs = (sq4 * a.ks4[kb]) * (tau * (1.0f / 256.0f));
+    if (pc == TM_INT8) cs = (sq8 * a.ks8[kb]) * tau;
+    else if (HAS4 && pc == TM_INT4) cs = (sq4 * a.ks4[kb]) * (tau * (1.0f / 256.0f));
     tl_cs = cs;
+    if constexpr (HYB) {
+      uint64_t m = 0;
+      if (pj != 0u && !(pj & kRunGather)) m = cmask[jp & 0xFFFFFFu];
+      tl_cm0 = static_cast<uint32_t>(m);
+      tl_cm1 = static_cast<uint32_t>(m >> 32);
+    }
   };
 
   // start loading tile j (precision prec) into buffer BUFC
   auto issue = [&](uint32_t j, uint32_t prec, int boff) {
     uint8_t* dst = lds + boff;
+    if (HYB && (prec & kRunGather)) {   // gathered tile j: K rows and V^T packed per tile
+      cp_v.issue(rs_vg, j * VBYTES, dst + KBYTES, w);
+      cp_kg.issue(rs_kg, j * (kBlock * D * 2), dst, w);
+      return;
+    }
+    const uint32_t pc = prec & 3u;
     const uint32_t jh = j * hkv;
     cp_v.issue(rs_v, jh * VBYTES, dst + KBYTES, w);
-    if (prec == TM_INT8) cp_k8.issue(rs_k8, jh * (kBlock * D), dst, w);
-    else if (HAS4 && prec == TM_INT4) cp_k4.issue(rs_k4, jh * (kBlock * D / 2), dst, w);
+    if (pc == TM_INT8) cp_k8.issue(rs_k8, jh * (kBlock * D), dst, w);
+    else if (HAS4 && pc == TM_INT4) cp_k4.issue(rs_k4, jh * (kBlock * D / 2), dst, w);
     else if (HAS16) cp_k16.issue(rs_k16, j * (kBlock * kpitch16), dst, w);
   };
 
@@ -336,8 +368,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vm(0);
     __syncthreads();
     const int j = static_cast<int>(jp_cur & 0xFFFFFFu);
-    const uint32_t prec = jp_cur >> 24;
+    const uint32_t pflags = jp_cur >> 24, prec = pflags & 3u;
     const float cs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(tl_cs), t & 63));
+    const bool gath = HYB && (pflags & kRunGather);
+    const bool edge = HYB && (pflags & kRunEdge);
+    uint64_t cm = 0;
+    if constexpr (HYB)
+      cm = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(tl_cm1, t & 63))) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(tl_cm0, t & 63));   // (readlane is signed)
     if (t + 1 < ntiles) {
       if (((t + 1) & 63) == 0) expand((t + 1) >> 6);
       jp_cur = __builtin_amdgcn_readlane(tl_jp, (t + 1) & 63);
@@ -346,7 +384,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const uint8_t* kl = lds + boff;
     const uint8_t* vl = kl + KBYTES;
-    const bool need_mask = (j * kBlock + kBlock - 1 > qrow0) || (j * kBlock + kBlock > len);
+    const bool need_mask = (j * kBlock + kBlock - 1 > qrow0) || (j * kBlock + kBlock > len) ||
+                           (HYB && (gath || edge || cm != 0));
+    // gathered tiles: the key positions of this lane's 16 slots sigma(kb, 4g + i)
+    i32x4 gpos[4];
+    if (gath) {
+      const int32_t* gp = reinterpret_cast<const int32_t*>(a.trav + th->gh_off + static_cast<size_t>(j) * kGatherHdr + 16);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) gpos[kb] = *reinterpret_cast<const i32x4*>(gp + krow(kb) + 8 * g);
+    }
+    // (row, slot) excluded from this tile pass
+    auto masked = [&](int kb, int i, int row) -> bool {
+      const int sg = sigma(kb, 4 * g + i);
+      if constexpr (HYB) {
+        if (gath) return gpos[kb][i] > row;
+        const int key = j * kBlock + sg;
+        bool m = key > row || key >= len || ((cm >> sg) & 1u);
+        if (edge) m = m || ((row - key < win) != (prec == TM_FP16));
+        return m;
+      } else {
+        const int key = j * kBlock + sg;
+        return key > row || key >= len;
+      }
+    };
 
     // ---- S^T = K Q^T as fp32 values x (integers converted exactly), score = x * cs
     f32x4 xf[4][QB];
@@ -382,10 +442,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = j * kBlock + sigma(kb, 4 * g + i);
-              if (key > row || key >= len) xf[kb][qb][i] = -INFINITY;
-            }
+            for (int i = 0; i < 4; ++i)
+              if (masked(kb, i, row)) xf[kb][qb][i] = -INFINITY;
         }
         float mf = xf[0][qb][0];
 #pragma unroll
@@ -469,10 +527,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = j * kBlock + sigma(kb, 4 * g + i);
-              mi = max(mi, (key > row || key >= len) ? INT_MIN : acc[kb][qb][i]);
-            }
+            for (int i = 0; i < 4; ++i) mi = max(mi, masked(kb, i, row) ? INT_MIN : acc[kb][qb][i]);
           mrow[qb] = mi;
         }
       } else {
@@ -527,10 +582,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = j * kBlock + sigma(kb, 4 * g + i);
             const float s = __builtin_fmaf(xf[kb][qb][i], cs, nb[qb]);
             pb[kb >> 1][qb][4 * (kb & 1) + i] =
-                static_cast<_Float16>(__builtin_amdgcn_exp2f((key > row || key >= len) ? -INFINITY : s));
+                static_cast<_Float16>(__builtin_amdgcn_exp2f(masked(kb, i, row) ? -INFINITY : s));
           }
       }
     } else {
@@ -633,7 +687,9 @@ static hipError_t launch_prefill_k(const PrefillArgs& a, int kind, bool bf16, hi
     return bf16 ? launch_prefill_t<D, BQ, 0, true>(a, st) : launch_prefill_t<D, BQ, 0, false>(a, st);
   if (kind == TM_POLICY_BITMASK)
     return bf16 ? launch_prefill_t<D, BQ, 1, true>(a, st) : launch_prefill_t<D, BQ, 1, false>(a, st);
-  return bf16 ? launch_prefill_t<D, BQ, 2, true>(a, st) : launch_prefill_t<D, BQ, 2, false>(a, st);
+  if (kind == TM_POLICY_FOURWAY)
+    return bf16 ? launch_prefill_t<D, BQ, 2, true>(a, st) : launch_prefill_t<D, BQ, 2, false>(a, st);
+  return bf16 ? launch_prefill_t<D, BQ, 3, true>(a, st) : launch_prefill_t<D, BQ, 3, false>(a, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st) {

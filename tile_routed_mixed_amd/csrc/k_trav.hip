@@ -64,6 +64,14 @@ __global__ __launch_bounds__(256) void trav_items_kernel(TravArgs a) {
     h->item_off = a.item_off;
     h->run_off = a.run_off;
     h->bits_off = a.bits_off;
+    h->window = a.window;
+    h->n_gtiles = a.n_gtiles;
+    h->sel_tab_off = a.sel_tab_off;
+    h->sel_idx_off = a.sel_idx_off;
+    h->cm_off = a.cm_off;
+    h->gh_off = a.gh_off;
+    h->gk_off = a.gk_off;
+    h->gv_off = a.gv_off;
   }
   if (k < static_cast<uint32_t>(a.nseq)) {
     SeqEntry* st = reinterpret_cast<SeqEntry*>(a.trav + a.seq_off);
@@ -101,7 +109,32 @@ __global__ __launch_bounds__(256) void trav_items_kernel(TravArgs a) {
   RunEntry* runs = reinterpret_cast<RunEntry*>(a.trav + a.run_off) + static_cast<size_t>(k) * a.max_runs;
   uint32_t nr = 0, n8 = 0, n4 = 0, n16 = 0;
 
-  if (a.kind == TM_POLICY_BOUNDARIES) {
+  if (a.kind == TM_POLICY_HYBRID) {
+    // window classes are contiguous in j: every causal (row, key) pair of key
+    // tile j lies within the window from jfull on, none of them before jedge
+    const int W = static_cast<int>(a.window);
+    const int r0 = qt * a.bq, rl = min((qt + 1) * a.bq, len) - 1;
+    auto fdiv = [](int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); };
+    const int jfull = min(legal, max(0, fdiv(rl - W, a.bk) + 1));
+    const int jedge = W > 0 ? min(jfull, max(0, fdiv(r0 - W - (a.bk - 1), a.bk) + 1)) : jfull;
+    const uint32_t ce = static_cast<uint32_t>(jfull - jedge);
+    put_run(runs, nr, jfull, static_cast<uint32_t>(legal - jfull), TM_FP16, a.max_runs);
+    put_run(runs, nr, jedge, ce, TM_FP16 | kRunEdge, a.max_runs);
+    put_run(runs, nr, jedge, ce, TM_INT8 | kRunEdge, a.max_runs);
+    put_run(runs, nr, 0, static_cast<uint32_t>(jedge), TM_INT8, a.max_runs);
+    // selected keys visible from this query tile (positions <= rl), gathered
+    const SelEntry se = reinterpret_cast<const SelEntry*>(a.trav + a.sel_tab_off)[seq * a.hq + head];
+    const int32_t* idx = reinterpret_cast<const int32_t*>(a.trav + a.sel_idx_off) + se.start;
+    uint32_t lo = 0, hi = se.count;                 // first entry > rl
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (idx[mid] <= rl) lo = mid + 1; else hi = mid;
+    }
+    const uint32_t ng = (lo + 63) / 64;
+    put_run(runs, nr, se.gbase, ng, TM_FP16 | kRunGather, a.max_runs);
+    n16 = static_cast<uint32_t>(legal - jfull) + ce + ng;
+    n8 = ce + static_cast<uint32_t>(jedge);
+  } else if (a.kind == TM_POLICY_BOUNDARIES) {
     const int b8 = a.b8[head], b4 = a.b4[head];
     const int ri = qt * (a.bq / a.bk);
     // INT8 band [lo8, jmax]; INT4 band [lo4, hi4]; SKIP [0, lo4)
@@ -218,7 +251,7 @@ __global__ __launch_bounds__(256) void trav_items_kernel(TravArgs a) {
   it->n8 = n8;
   it->n4 = n4;
   it->n16 = n16;
-  it->nskip = static_cast<uint32_t>(legal) - n8 - n4 - n16;
+  it->nskip = a.kind == TM_POLICY_HYBRID ? 0u : static_cast<uint32_t>(legal) - n8 - n4 - n16;
 }
 
 // Deterministic census: one workgroup sums the per-item counts.
@@ -247,6 +280,43 @@ __global__ __launch_bounds__(256) void trav_census_kernel(uint8_t* trav, uint32_
     h->census[3] = red[2][0];
     h->census[4] = red[3][0];
   }
+}
+
+// Hybrid policies: fill gathered tile t with its selected keys' 16-bit K rows
+// ([64][D]) and fp16 V columns (V^T [D][64]); slots past the list are zero.
+template <int D>
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  const uint32_t t = blockIdx.x;
+  const uint8_t* gh = a.trav + a.gh_off + static_cast<size_t>(t) * kGatherHdr;
+  const GatherEntry ge = *reinterpret_cast<const GatherEntry*>(gh);
+  const int32_t* pos = reinterpret_cast<const int32_t*>(gh + 16);
+  uint16_t* gk = reinterpret_cast<uint16_t*>(a.trav + a.gk_off) + static_cast<size_t>(t) * kBlock * D;
+  uint16_t* gv = reinterpret_cast<uint16_t*>(a.trav + a.gv_off) + static_cast<size_t>(t) * D * kBlock;
+  // K: 64 rows of D 16-bit values, 16 bytes per thread step
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  for (int u = threadIdx.x; u < kBlock * CPR; u += 256) {
+    const int row = u / CPR, ch = u % CPR;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (row < static_cast<int>(ge.keys)) {
+      const size_t tok = static_cast<size_t>(ge.tok_start) + pos[row];
+      v = *reinterpret_cast<const u32x4*>(a.k + (tok * a.hkv + ge.kv) * D + ch * 8);
+    }
+    *reinterpret_cast<u32x4*>(gk + row * D + ch * 8) = v;
+  }
+  // V^T: channel rows of 64 slots; thread (slot, channel quarter) copies D/4 channels
+  const int slot = threadIdx.x & 63, c0 = threadIdx.x >> 6;
+  const bool ok = slot < static_cast<int>(ge.keys);
+  const int key = ok ? pos[slot] : 0;
+  const uint16_t* src = a.vt16 + ((static_cast<size_t>(ge.blk_start) + key / kBlock) * a.hkv + ge.kv) * D * kBlock +
+                        key % kBlock;
+  for (int c = c0; c < D; c += 4) gv[c * kBlock + slot] = ok ? src[c * kBlock] : static_cast<uint16_t>(0);
+}
+
+hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st) {
+  if (a.n_gtiles == 0) return hipSuccess;
+  if (d == 128) hipLaunchKernelGGL(gather_kernel<128>, dim3(a.n_gtiles), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(gather_kernel<64>, dim3(a.n_gtiles), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_traversal(const TravArgs& a, hipStream_t st) {

@@ -1,6 +1,8 @@
 // C ABI of libtm: host-side validation, sizing and launches.  Every check runs
 // before anything is enqueued, so a nonzero status leaves outputs untouched.
 // The entry points follow include/tm.h (which cites the method pages).
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -69,23 +71,114 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct TravLayout {
   size_t seq_off, item_off, run_off, bytes;
+  size_t sel_tab_off = 0, sel_idx_off = 0, cm_off = 0, gh_off = 0, gk_off = 0, gv_off = 0;
   uint32_t max_runs;
 };
 
-TravLayout trav_layout(const tm_shape* s, const ShapeInfo& si, const tm_policy* p) {
+// Hybrid policy tables, built on the host from the selected lists.
+struct HybridPlan {
+  std::vector<SelEntry> rows;   // per (sequence, query head)
+  int64_t n_sel = 0, n_gt = 0, n_cm = 0;
+};
+
+tm_status hybrid_plan(const tm_shape* s, const tm_policy* p, HybridPlan* hp) {
+  if (p->sel_off == nullptr) return TM_E_ARG;
+  if (p->window < 0 || p->sel_off[0] != 0) return TM_E_POLICY;
+  const int64_t nr = static_cast<int64_t>(s->nseq) * s->hq;
+  hp->rows.assign(static_cast<size_t>(nr), SelEntry{0, 0, 0, 0});
+  int64_t gt = 0, cm = 0;
+  for (int sq = 0; sq < s->nseq; ++sq) {
+    const int64_t len = s->cu_seqlens[sq + 1] - s->cu_seqlens[sq];
+    const int64_t nk = (len + 63) / 64;
+    for (int h = 0; h < s->hq; ++h) {
+      const int64_t r = static_cast<int64_t>(sq) * s->hq + h;
+      const int64_t a = p->sel_off[r], b = p->sel_off[r + 1];
+      if (b < a) return TM_E_POLICY;
+      if (b > a && p->sel_idx == nullptr) return TM_E_ARG;
+      for (int64_t e = a; e < b; ++e) {
+        const int64_t c = p->sel_idx[e];
+        if (c < 0 || c >= len || (e > a && c <= p->sel_idx[e - 1])) return TM_E_POLICY;
+      }
+      hp->rows[static_cast<size_t>(r)] =
+          SelEntry{static_cast<uint32_t>(a), static_cast<uint32_t>(b - a), static_cast<uint32_t>(gt),
+                   static_cast<uint32_t>(cm)};
+      gt += (b - a + 63) / 64;
+      cm += nk;
+    }
+  }
+  hp->n_sel = p->sel_off[nr];
+  hp->n_gt = gt;
+  hp->n_cm = cm;
+  if (hp->n_sel >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
+  return TM_OK;
+}
+
+TravLayout trav_layout(const tm_shape* s, const ShapeInfo& si, const tm_policy* p, const HybridPlan* hp) {
   TravLayout L;
   // boundaries: INT8 band, sink, INT4 band.  Bitmask: at most one run per
   // group.  Four-way: runs split at group edges and, inside code-0 groups, at
   // the three points where the boundary rule changes (sink, INT4, INT8 band).
-  const int ngmax = p->kind == TM_POLICY_BOUNDARIES ? 0 : (si.maxnk + p->group - 1) / p->group;
+  // Hybrid: FP16 tiles, FP16 and INT8 parts of the edge tiles, INT8 tiles,
+  // gathered tiles.
+  const bool grouped = p->kind == TM_POLICY_BITMASK || p->kind == TM_POLICY_FOURWAY;
+  const int ngmax = grouped ? (si.maxnk + p->group - 1) / p->group : 0;
   L.max_runs = p->kind == TM_POLICY_BOUNDARIES ? 3u
-               : p->kind == TM_POLICY_BITMASK ? static_cast<uint32_t>(std::max(1, ngmax))
-                                              : static_cast<uint32_t>(ngmax + 3);
+               : p->kind == TM_POLICY_BITMASK  ? static_cast<uint32_t>(std::max(1, ngmax))
+               : p->kind == TM_POLICY_FOURWAY  ? static_cast<uint32_t>(ngmax + 3)
+                                               : 5u;
   L.seq_off = TM_TRAV_HEADER_BYTES;
   L.item_off = align256(L.seq_off + sizeof(SeqEntry) * static_cast<size_t>(s->nseq));
   L.run_off = align256(L.item_off + sizeof(ItemEntry) * static_cast<size_t>(si.n_items));
-  L.bytes = align256(L.run_off + sizeof(RunEntry) * static_cast<size_t>(si.n_items) * L.max_runs);
+  size_t end = align256(L.run_off + sizeof(RunEntry) * static_cast<size_t>(si.n_items) * L.max_runs);
+  if (p->kind == TM_POLICY_HYBRID) {
+    const size_t d = static_cast<size_t>(s->d);
+    L.sel_tab_off = end;
+    end = align256(end + sizeof(SelEntry) * hp->rows.size());
+    L.sel_idx_off = end;
+    end = align256(end + 4 * static_cast<size_t>(hp->n_sel));
+    L.cm_off = end;
+    end = align256(end + 8 * static_cast<size_t>(hp->n_cm));
+    L.gh_off = end;
+    end = align256(end + kGatherHdr * static_cast<size_t>(hp->n_gt));
+    L.gk_off = end;
+    end = align256(end + static_cast<size_t>(hp->n_gt) * 64 * d * 2);
+    L.gv_off = end;
+    end = align256(end + static_cast<size_t>(hp->n_gt) * d * 64 * 2);
+  }
+  L.bytes = end;
   return L;
+}
+
+// The hybrid tables staged on the host, in traversal order from sel_tab_off
+// to gk_off: list entries, positions, column masks, gathered-tile headers.
+std::vector<uint8_t> hybrid_tables(const tm_shape* s, const tm_policy* p, const HybridPlan& hp,
+                                   const TravLayout& L) {
+  std::vector<uint8_t> buf(L.gk_off - L.sel_tab_off, 0);
+  uint8_t* base = buf.data() - L.sel_tab_off;
+  std::memcpy(base + L.sel_tab_off, hp.rows.data(), sizeof(SelEntry) * hp.rows.size());
+  if (hp.n_sel > 0) std::memcpy(base + L.sel_idx_off, p->sel_idx, 4 * static_cast<size_t>(hp.n_sel));
+  uint64_t* cm = reinterpret_cast<uint64_t*>(base + L.cm_off);
+  const int grp = s->hq / s->hkv;
+  int64_t blk = 0;
+  for (int sq = 0; sq < s->nseq; ++sq) {
+    const int64_t len = s->cu_seqlens[sq + 1] - s->cu_seqlens[sq];
+    for (int h = 0; h < s->hq; ++h) {
+      const SelEntry& e = hp.rows[static_cast<size_t>(sq) * s->hq + h];
+      const int32_t* idx = p->sel_idx + e.start;
+      for (uint32_t u = 0; u < e.count; ++u) cm[e.cm_base + idx[u] / 64] |= uint64_t(1) << (idx[u] % 64);
+      for (uint32_t t = 0; t * 64 < e.count; ++t) {
+        uint8_t* gh = base + L.gh_off + static_cast<size_t>(e.gbase + t) * kGatherHdr;
+        const uint32_t keys = std::min<uint32_t>(64, e.count - 64 * t);
+        const GatherEntry ge{static_cast<uint32_t>(s->cu_seqlens[sq]), static_cast<uint32_t>(blk),
+                             static_cast<uint32_t>(h / grp), keys};
+        std::memcpy(gh, &ge, sizeof(ge));
+        int32_t* pos = reinterpret_cast<int32_t*>(gh + 16);
+        for (uint32_t k = 0; k < 64; ++k) pos[k] = k < keys ? idx[64 * t + k] : INT32_MAX;
+      }
+    }
+    blk += (len + 63) / 64;
+  }
+  return buf;
 }
 
 // Words of a bitmask (per_word = 32 one-bit codes) or four-way code map
@@ -214,8 +307,13 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   if (st != TM_OK) return st;
   if (policy == nullptr || trav_bytes == nullptr) return TM_E_ARG;
   const int kind = policy->kind;
-  if (kind != TM_POLICY_BOUNDARIES && kind != TM_POLICY_BITMASK && kind != TM_POLICY_FOURWAY) return TM_E_ARG;
-  if (kind != TM_POLICY_BITMASK) {   // boundaries, alone or under the four-way codes
+  if (kind != TM_POLICY_BOUNDARIES && kind != TM_POLICY_BITMASK && kind != TM_POLICY_FOURWAY &&
+      kind != TM_POLICY_HYBRID)
+    return TM_E_ARG;
+  HybridPlan hp;
+  if (kind == TM_POLICY_HYBRID) {
+    if ((st = hybrid_plan(shape, policy, &hp)) != TM_OK) return st;
+  } else if (kind != TM_POLICY_BITMASK) {   // boundaries, alone or under the four-way codes
     if (policy->b8 == nullptr || policy->b4 == nullptr) return TM_E_ARG;
     if (shape->hq > kMaxHeadsArg) return TM_E_UNSUPPORTED;
     if (policy->sink != 0 && policy->sink != 1) return TM_E_POLICY;
@@ -225,13 +323,13 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
       if (b4 == 0 && !policy->sink) return TM_E_POLICY;
     }
   }
-  if (kind != TM_POLICY_BOUNDARIES) {   // a packed per-group map
+  if (kind == TM_POLICY_BITMASK || kind == TM_POLICY_FOURWAY) {   // a packed per-group map
     if (policy->group < 1) return TM_E_POLICY;
     if (policy->n_words < policy_words(shape, policy->group, kind == TM_POLICY_BITMASK ? 32 : 16))
       return TM_E_POLICY;
     if (policy->bits == nullptr && policy->n_words > 0) return TM_E_ARG;
   }
-  const TravLayout L = trav_layout(shape, si, policy);
+  const TravLayout L = trav_layout(shape, si, policy, &hp);
   if (trav == nullptr) {
     *trav_bytes = L.bytes;
     return TM_OK;
@@ -252,8 +350,8 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   a.bq = shape->bq;
   a.bk = shape->bk;
   a.kind = policy->kind;
-  a.sink = kind != TM_POLICY_BITMASK ? policy->sink : 0;
-  a.group = kind != TM_POLICY_BOUNDARIES ? policy->group : 1;
+  a.sink = (kind == TM_POLICY_BOUNDARIES || kind == TM_POLICY_FOURWAY) ? policy->sink : 0;
+  a.group = (kind == TM_POLICY_BITMASK || kind == TM_POLICY_FOURWAY) ? policy->group : 1;
   a.n_items = static_cast<uint32_t>(si.n_items);
   a.max_runs = L.max_runs;
   a.nblk = static_cast<uint32_t>(si.nblk);
@@ -261,13 +359,32 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   a.item_off = static_cast<uint32_t>(L.item_off);
   a.run_off = static_cast<uint32_t>(L.run_off);
   a.bits_off = 0;
-  if (kind != TM_POLICY_BITMASK) {
+  if (kind == TM_POLICY_BOUNDARIES || kind == TM_POLICY_FOURWAY) {
     for (int h = 0; h < shape->hq; ++h) {
       a.b8[h] = policy->b8[h];
       a.b4[h] = policy->b4[h];
     }
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (kind == TM_POLICY_HYBRID) {
+    a.window = static_cast<uint32_t>(policy->window);
+    a.n_gtiles = static_cast<uint32_t>(hp.n_gt);
+    a.sel_tab_off = static_cast<uint32_t>(L.sel_tab_off);
+    a.sel_idx_off = static_cast<uint32_t>(L.sel_idx_off);
+    a.cm_off = static_cast<uint32_t>(L.cm_off);
+    a.gh_off = static_cast<uint32_t>(L.gh_off);
+    a.gk_off = static_cast<uint32_t>(L.gk_off);
+    a.gv_off = static_cast<uint32_t>(L.gv_off);
+    // stage the list tables (pageable host memory: wait for the copy before
+    // the staging buffer goes away)
+    const std::vector<uint8_t> tab = hybrid_tables(shape, policy, hp, L);
+    if (!tab.empty()) {
+      if (hipMemcpyAsync(static_cast<uint8_t*>(trav) + L.sel_tab_off, tab.data(), tab.size(), hipMemcpyHostToDevice,
+                         hs) != hipSuccess)
+        return TM_E_HIP;
+      if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;
+    }
+  }
   if (launch_traversal(a, hs) != hipSuccess) return TM_E_HIP;
   if (census != nullptr) {
     TravHeader h;
@@ -284,6 +401,30 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   return TM_OK;
 }
 
+tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, void* trav, const void* k,
+                             const tm_qtensor* vq, void* stream) {
+  ShapeInfo si;
+  tm_status st = check_shape(shape, true, &si);
+  if (st != TM_OK) return st;
+  if (policy == nullptr || trav == nullptr || k == nullptr || policy->kind != TM_POLICY_HYBRID) return TM_E_ARG;
+  if ((st = check_qtensor(vq, shape->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
+  HybridPlan hp;
+  if ((st = hybrid_plan(shape, policy, &hp)) != TM_OK) return st;
+  const TravLayout L = trav_layout(shape, si, policy, &hp);
+  if (L.bytes > 0xFFFFFFFFull) return TM_E_SHAPE;
+  if (hp.n_gt == 0) return TM_OK;
+  GatherArgs g;
+  g.trav = static_cast<uint8_t*>(trav);
+  g.k = static_cast<const uint16_t*>(k);
+  g.vt16 = vq->t16;
+  g.hkv = shape->hkv;
+  g.n_gtiles = static_cast<uint32_t>(hp.n_gt);
+  g.gh_off = static_cast<uint32_t>(L.gh_off);
+  g.gk_off = static_cast<uint32_t>(L.gk_off);
+  g.gv_off = static_cast<uint32_t>(L.gv_off);
+  return launch_gather(g, shape->d, static_cast<hipStream_t>(stream)) == hipSuccess ? TM_OK : TM_E_HIP;
+}
+
 tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kind, const void* q, const void* k,
                      const tm_qtensor* qq, const tm_qtensor* kq, const tm_qtensor* vq, void* o, int32_t o_dtype,
                      float* lse, int32_t* dbg_qk, const int32_t* dbg_tiles, int32_t n_dbg, void* stream) {
@@ -291,7 +432,8 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
   tm_status st = check_shape(shape, true, &si);
   if (st != TM_OK) return st;
   if (trav == nullptr || q == nullptr || k == nullptr || o == nullptr) return TM_E_ARG;
-  if (policy_kind != TM_POLICY_BOUNDARIES && policy_kind != TM_POLICY_BITMASK && policy_kind != TM_POLICY_FOURWAY)
+  if (policy_kind != TM_POLICY_BOUNDARIES && policy_kind != TM_POLICY_BITMASK && policy_kind != TM_POLICY_FOURWAY &&
+      policy_kind != TM_POLICY_HYBRID)
     return TM_E_ARG;
   if (o_dtype != TM_F32 && o_dtype != TM_F16 && o_dtype != TM_BF16) return TM_E_ARG;
   if (n_dbg < 0 || (n_dbg > 0 && (dbg_qk == nullptr || dbg_tiles == nullptr))) return TM_E_ARG;

@@ -29,7 +29,9 @@ constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for running max
 struct TravHeader {
   uint32_t magic, version, kind, n_items, max_runs, nseq, hq, hkv, bq, bk, d, nblk;
   uint32_t seq_off, item_off, run_off, bits_off;
-  uint32_t pad[16];
+  // hybrid policies: window (tokens), gathered tiles, table offsets (bytes)
+  uint32_t window, n_gtiles, sel_tab_off, sel_idx_off, cm_off, gh_off, gk_off, gv_off;
+  uint32_t pad[8];
   int64_t census[8];  // legal, int8, int4, fp16, skip
   int64_t pad2[8];
 };
@@ -38,6 +40,12 @@ static_assert(sizeof(TravHeader) == TM_TRAV_HEADER_BYTES, "traversal header size
 struct SeqEntry { uint32_t tok_start, len, blk_start, nq; };
 struct ItemEntry { uint32_t seq, head, qtile, nruns, n8, n4, n16, nskip; };
 struct RunEntry { uint32_t ktile, count_prec; };
+// hybrid: one per (sequence, query head) list; one header per gathered tile
+struct SelEntry { uint32_t start, count, gbase, cm_base; };
+struct GatherEntry { uint32_t tok_start, blk_start, kv, keys; };
+constexpr int kGatherHdr = 512;     // bytes per gathered tile header: entry + int32[64] positions
+// hybrid run precisions: the compute precision in bits 0-1, edge and gathered flags
+constexpr uint32_t kRunEdge = 4u, kRunGather = 8u;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

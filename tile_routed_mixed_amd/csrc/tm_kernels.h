@@ -39,8 +39,19 @@ struct TravArgs {
   int kind, sink, group;
   uint32_t n_items, max_runs, nblk;
   uint32_t seq_off, item_off, run_off, bits_off;
+  // hybrid policies (the tables are already in trav; the items kernel records
+  // the offsets in the header)
+  uint32_t window, n_gtiles, sel_tab_off, sel_idx_off, cm_off, gh_off, gk_off, gv_off;
   int32_t b8[kMaxHeadsArg];
   int32_t b4[kMaxHeadsArg];
+};
+
+struct GatherArgs {
+  uint8_t* trav;
+  const uint16_t* k;        // [T][hkv][D] 16-bit
+  const uint16_t* vt16;     // [nblk][hkv][D][64] fp16
+  int hkv;
+  uint32_t n_gtiles, gh_off, gk_off, gv_off;
 };
 
 struct PrefillArgs {
@@ -100,6 +111,7 @@ struct DecodeArgs {
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
 hipError_t launch_decode_split(const DecodeArgs& a, int ncls, bool small, int d, bool bf16, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, int d, hipStream_t st);

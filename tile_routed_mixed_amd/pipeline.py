@@ -3,7 +3,8 @@
 PrefillPipeline holds the device copies of Q, K, V and every buffer the
 prefill path writes, and runs one pass of the path:
   tm_quantize_pack(Q, rows)  tm_quantize_pack(K, rows)
-  tm_quantize_pack(V, cols + fp16 copy)   tm_build_traversal   tm_prefill.
+  tm_quantize_pack(V, cols + fp16 copy)   tm_build_traversal
+  (tm_gather_selected under a hybrid policy)   tm_prefill.
 DecodePipeline does the same for decode steps over a quantized cache, and
 for a growing one (start / append: tm_cache_append per step).
 Nothing here computes: buffers are allocated once and the C ABI is called.
@@ -55,7 +56,11 @@ class PrefillPipeline:
         B.tm_quantize_pack(self.shape, self.v, self.vq, stream)
 
     def traversal(self, census=False, stream=None):
+        """Build the traversal; under a hybrid policy also gather the selected
+        keys' K rows and V columns (after quantize())."""
         _, c = B.tm_build_traversal(self.shape, self.policy, self.trav, census=census, stream=stream)
+        if self.policy.kind == B.TM_POLICY_HYBRID:
+            B.tm_gather_selected(self.shape, self.policy, self.trav, self.k, self.vq, stream)
         return c
 
     def prefill(self, o_dtype=B.TM_F32, dbg_tiles=None, stream=None, with_lse=True):

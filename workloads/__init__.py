@@ -7,7 +7,7 @@ classification, no scores).  Every array is drawn with
 CPU oracle receive identical bits.
 
 Streams: Q = 1, K = 2, V = 3, policy = 4, outlier channels = 5, decode query = 6,
-locality = 7.  Values are N(0, 1) in float32, rounded half-to-even to the
+locality = 7, selected keys = 8.  Values are N(0, 1) in float32, rounded half-to-even to the
 16-bit input type.
 
 Workloads (the shapes are those of the attention layers the pages benchmark:
@@ -41,7 +41,7 @@ from typing import List, Optional
 import numpy as np
 
 WORKLOAD_IDS = {"toy512": 1, "gqa8k": 2, "varlen32k": 3, "long128k": 4, "decode16x32k": 5, "local8k": 6}
-STREAM_Q, STREAM_K, STREAM_V, STREAM_POLICY, STREAM_OUTLIER, STREAM_DQ, STREAM_LOCAL = 1, 2, 3, 4, 5, 6, 7
+STREAM_Q, STREAM_K, STREAM_V, STREAM_POLICY, STREAM_OUTLIER, STREAM_DQ, STREAM_LOCAL, STREAM_SEL = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 @dataclasses.dataclass
@@ -225,3 +225,18 @@ def make_decode_policy(w: Workload):
     """Decode cache tags: per KV head (b8, b4) in 64-token blocks, sink, FP16 tail."""
     return dict(b8=np.full(w.hkv, w.dec_b8, np.int32), b4=np.full(w.hkv, w.dec_b4, np.int32),
                 sink=int(w.sink), tail=int(w.dec_tail))
+
+
+def make_selection(w: Workload, frac: float, window: int, stream_offset: int = 0):
+    """Hybrid policy input: for every (sequence, query head), round(frac * len)
+    key positions drawn without replacement (sorted), as index lists
+    dict(kind=3, window, sel_off [nseq*hq + 1], sel_idx)."""
+    rng = np.random.default_rng([w.wid, STREAM_SEL, stream_offset])
+    lists = []
+    for S in w.seqlens:
+        for _ in range(w.hq):
+            n = int(round(frac * S))
+            lists.append(np.sort(rng.choice(S, size=n, replace=False)).astype(np.int32))
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    idx = np.concatenate(lists).astype(np.int32) if lists else np.zeros(0, np.int32)
+    return dict(kind=3, window=int(window), sel_off=off, sel_idx=idx)
