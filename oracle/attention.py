@@ -191,6 +191,11 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
     Block tags follow policy.decode_block_tags with (b8, b4) of the query's KV
     head, or of the query head itself when dpol["per_q_head"] is set (b8, b4
     then have hq entries; the reading of a per-query-head decode map).
+    Selected tokens ([HyQuant] "How HyQuant works": selected tokens stay FP16
+    in the decode cache too): with dpol["sel_off"] ([nseq * hkv + 1], rows
+    sequence-major then KV head) and dpol["sel_idx"] (positions < L, strictly
+    increasing per list), a selected key is read in FP16 whatever its block's
+    tag, SKIP included; the other keys follow their block's tag.
     INT blocks: score = tau * sk * (q . ck), value = sv * cv; FP16 blocks:
     score = tau * (q . k), value = v.  Returns O [B][hq][d]; with ``pairs`` (a
     list of (b, h)) only those outputs are computed (the rest stay zero).
@@ -212,16 +217,22 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
             tags = P.decode_block_tags(L, int(dpol["b8"][mi]), int(dpol["b4"][mi]),
                                        int(dpol["sink"]), int(dpol["tail"]))
             tags_all[(b, mi)] = tags
+            chosen = np.zeros(L, bool)
+            if "sel_off" in dpol:
+                r = b * hkv + kv
+                lst = dpol["sel_idx"][int(dpol["sel_off"][r]):int(dpol["sel_off"][r + 1])]
+                chosen[np.asarray(lst, np.int64)] = True
             sc_list, val_list = [], []
             for j, t in enumerate(tags):
                 n = min(BLOCK, L - j * BLOCK)
+                keep = ~chosen[j * BLOCK: j * BLOCK + n]      # selected keys are read in FP16 below
                 if t == P.SKIP:
                     continue
                 if t == P.FP16:
                     kk = k64[cu[b] + j * BLOCK: cu[b] + j * BLOCK + n, kv]
                     vv = v64[cu[b] + j * BLOCK: cu[b] + j * BLOCK + n, kv]
-                    sc_list.append(tau * (kk @ q64[b, h]))
-                    val_list.append(vv)
+                    sc_list.append((tau * (kk @ q64[b, h]))[keep])
+                    val_list.append(vv[keep])
                 else:
                     ck = kq["c8"] if t == P.INT8 else kq["c4"]
                     cv = vq["c8"] if t == P.INT8 else vq["c4"]
@@ -229,8 +240,12 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
                     sv = vq["s8"] if t == P.INT8 else vq["s4"]
                     kc = ck[kv, blk0 + j, :n].astype(np.float64)
                     vc = cv[kv, blk0 + j, :n].astype(np.float64)
-                    sc_list.append(tau * float(sk[kv, blk0 + j]) * (kc @ q64[b, h]))
-                    val_list.append(float(sv[kv, blk0 + j]) * vc)
+                    sc_list.append((tau * float(sk[kv, blk0 + j]) * (kc @ q64[b, h]))[keep])
+                    val_list.append((float(sv[kv, blk0 + j]) * vc)[keep])
+            sel = np.nonzero(chosen)[0]
+            if len(sel):
+                sc_list.append(tau * (k64[cu[b] + sel, kv] @ q64[b, h]))
+                val_list.append(v64[cu[b] + sel, kv])
             sc = np.concatenate(sc_list)
             vals = np.concatenate(val_list, axis=0)
             m = np.max(sc)

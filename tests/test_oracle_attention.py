@@ -311,3 +311,72 @@ def test_decode_per_query_head_maps_reduce_to_per_kv_maps():
     # heads 0 and 1 share a KV head but not a map: their tags differ
     _, tags = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dq, return_tags=True)
     assert not np.array_equal(tags[(1, 0)], tags[(1, 1)])
+
+
+def _dsel(lists):
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    idx = np.concatenate([np.asarray(x, np.int64) for x in lists]).astype(np.int32)
+    return off, idx
+
+
+def test_decode_selected_tokens():
+    """Selected decode tokens: none changes nothing; every key selected is the
+    all-FP16 decode; selecting keys of FP16 blocks changes nothing; selecting a
+    key of a skipped block adds exactly that key in FP16 (checked against a
+    softmax written out for that row)."""
+    q, k, v = _decode_inputs(17)
+    kq, vq = Q.quantize(k, DQ_SEQ), Q.quantize(v, DQ_SEQ, layout="cols")
+    f64 = lambda x: x.astype(np.float64)
+    base = dict(b8=[2, 3], b4=[4, 5], sink=1, tail=128)
+    O = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), base)
+    nl = len(DQ_SEQ) * HKV
+    off, idx = _dsel([[] for _ in range(nl)])
+    O0 = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dict(base, sel_off=off, sel_idx=idx))
+    assert np.array_equal(O, O0)
+    every = [list(range(L)) for L in DQ_SEQ for _ in range(HKV)]
+    off, idx = _dsel(every)
+    Oa = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dict(base, sel_off=off, sel_idx=idx))
+    O16 = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dict(base, tail=10 ** 6))
+    assert np.max(np.abs(Oa - O16)) < 1e-12
+    # keys inside the FP16 tail of sequence 1 (length L1): selecting them changes nothing
+    L1 = DQ_SEQ[1]
+    lists = [[] for _ in range(nl)]
+    lists[1 * HKV + 0] = [L1 - 3, L1 - 1]
+    off, idx = _dsel(lists)
+    Ot = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dict(base, sel_off=off, sel_idx=idx))
+    assert np.max(np.abs(Ot - O)) < 1e-12
+    # a key of a skipped block of sequence 1, KV head 0: only heads 0, 1 of sequence 1 change
+    _, tags = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), base, return_tags=True)
+    j = int(np.nonzero(tags[(1, 0)] == P.SKIP)[0][0])
+    c = 64 * j + 5
+    lists[1 * HKV + 0] = [c]
+    off, idx = _dsel(lists)
+    Os = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dict(base, sel_off=off, sel_idx=idx))
+    changed = {(b, h) for b in range(len(DQ_SEQ)) for h in range(HQ) if not np.array_equal(Os[b, h], O[b, h])}
+    assert changed == {(1, 0), (1, 1)}
+    # head 0 of sequence 1 written out: the unselected softmax plus key c at 16-bit precision
+    tok0 = DQ_SEQ[0]
+    tau = 1 / np.sqrt(D)
+    t = tags[(1, 0)]
+    sc, vals = [], []
+    for jj, tg in enumerate(t):
+        n = min(64, L1 - 64 * jj)
+        if tg == P.SKIP:
+            continue
+        if tg == P.FP16:
+            sc += list(tau * (f64(k)[tok0 + 64 * jj: tok0 + 64 * jj + n, 0] @ f64(q)[1, 0]))
+            vals += list(f64(v)[tok0 + 64 * jj: tok0 + 64 * jj + n, 0])
+        else:
+            c8 = kq["c8"] if tg == P.INT8 else kq["c4"]
+            v8 = vq["c8"] if tg == P.INT8 else vq["c4"]
+            s8 = kq["s8"] if tg == P.INT8 else kq["s4"]
+            w8 = vq["s8"] if tg == P.INT8 else vq["s4"]
+            b0 = int(kq["blk_start"][1])
+            sc += list(tau * float(s8[0, b0 + jj]) * (c8[0, b0 + jj, :n].astype(np.float64) @ f64(q)[1, 0]))
+            vals += list(float(w8[0, b0 + jj]) * v8[0, b0 + jj, :n].astype(np.float64))
+    sc.append(tau * float(f64(k)[tok0 + c, 0] @ f64(q)[1, 0]))
+    vals.append(f64(v)[tok0 + c, 0])
+    sc = np.array(sc)
+    pr = np.exp(sc - sc.max())
+    pr /= pr.sum()
+    assert np.max(np.abs(Os[1, 0] - pr @ np.array(vals))) < 1e-12
