@@ -117,16 +117,18 @@ def cpu_baseline(w, q, k, v, pol, seconds):
                       f"{dt:.1f} s; attention rows only (codes precomputed); dense-causal FLOPs of those rows"}
 
 
-def prefill_config_line(name, steps=10, warmup=2):
+def prefill_config_line(name, steps=10, warmup=2, hybrid=None):
     """Prefill alone on another of the five workloads: time per launch (HIP
     events on the launch stream, back to back), effective dense-causal rate,
-    and the fraction of the precision-weighted MFMA peak of its executed tiles."""
+    and the fraction of the precision-weighted MFMA peak of its executed tiles.
+    hybrid = (fraction selected, window): the workload's shape under the
+    token-granular policy instead of its own."""
     import torch
     import tile_routed_mixed_amd as T
     import workloads as W
     w = W.get(name)
     q, k, v = W.make_qkv(w)
-    pol = W.make_policy(w)
+    pol = W.make_policy(w) if hybrid is None else W.make_selection(w, hybrid[0], hybrid[1])
     pp = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, pol)
     pp.upload(q[0], k[0], v[0])
     del q, k, v
@@ -144,7 +146,11 @@ def prefill_config_line(name, steps=10, warmup=2):
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / steps
     ops, t_peak = prefill_roofline(w, census, t * 1e-3)
-    res = {"workload": describe(w), "prefill_ms": t,
+    desc = describe(w) if hybrid is None else describe(w).replace(
+        "per-head diagonal-distance boundaries",
+        f"hybrid: {hybrid[0] * 100:.0f} % of keys per head selected (seeded), {hybrid[1]}-token window in FP16, "
+        f"the rest INT8")
+    res = {"workload": desc, "prefill_ms": t,
            "effective_tflops_dense_causal": dense_causal_flops(w) / (t * 1e-3) / 1e12,
            "mfma_frac_precision_weighted": (ops / (t * 1e-3)) / (ops / t_peak),
            "census": census}
@@ -392,8 +398,8 @@ def main():
             f"{dl['tokens_per_s']:.0f} tokens/s")
     if not args.no_other_configs and args.workload == "gqa8k":
         out["other_configs"] = []
-        for name in ("toy512", "varlen32k", "long128k"):
-            r = prefill_config_line(name)
+        for name, hyb in (("toy512", None), ("varlen32k", None), ("long128k", None), ("gqa8k", (0.05, 128))):
+            r = prefill_config_line(name, hybrid=hyb)
             out["other_configs"].append(r)
             log(f"[bench] {name}: prefill {r['prefill_ms']:.4f} ms, {r['effective_tflops_dense_causal']:.1f} "
                 f"TFLOP/s dense-causal, {r['mfma_frac_precision_weighted'] * 100:.1f} % of the weighted MFMA peak")

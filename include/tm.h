@@ -198,6 +198,17 @@ typedef struct tm_dpolicy {
   const int32_t* lengths;   /* host [nseq] or NULL: current lengths, 1 <= lengths[s] <= the
                                cache shape's length of s (its capacity); NULL: the capacity */
   int32_t per_q_head;       /* 0: b8/b4 per KV head; 1: per query head */
+  /* Selected tokens kept in FP16, or sel_off == NULL for none.  List of row
+   * s*hkv + g (sequence s, KV head g) is sel_idx[sel_off[r], sel_off[r+1]):
+   * positions below the sequence's current length, strictly increasing.  A
+   * selected key is read in FP16 whatever its block's tag (SKIP included);
+   * the other keys follow their block's tag.  sel_buf: device buffer that
+   * tm_decode_select filled for these lists (host arrays read during the
+   * calls).  ([HyQuant] "How HyQuant works": selected tokens and the recent
+   * window stay FP16 in the decode cache.) */
+  const int32_t* sel_off;
+  const int32_t* sel_idx;
+  const void* sel_buf;
 } tm_dpolicy;
 
 /* Traversal buffer layout (device, written by tm_build_traversal, read by
@@ -343,6 +354,18 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
  * (hq/hkv > 16, more than 64 KV heads or 256 query heads, or a sequence whose 16-bit keys or
  * fp16 V copy span 2 GiB or more: ceil(len / 64) * 64 * hkv * d * 2 >= 2^31),
  * TM_E_HIP. */
+/* Build the selected-token buffer of `policy` (its sel_off / sel_idx lists)
+ * for a cache: column masks of every cache block and the selected keys'
+ * 16-bit K rows (from k16 [T][hkv][d]) and fp16 V columns (from vq->t16)
+ * gathered into tiles of 64.  sel_buf == NULL: write the required size to
+ * *sel_bytes and return TM_OK without GPU work; otherwise *sel_bytes is its
+ * capacity (TM_E_SPACE if too small).  Call again after the listed tokens'
+ * K or V change.  Synchronizes `stream` (the tables are staged from the
+ * host).  Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY (lists), TM_E_SPACE,
+ * TM_E_HIP. */
+tm_status tm_decode_select(const tm_shape* cache, const tm_dpolicy* policy, const void* k16,
+                           const tm_qtensor* vq, void* sel_buf, size_t* sel_bytes, void* stream);
+
 tm_status tm_decode(const tm_shape* cache, const void* q,
                     const tm_qtensor* kq, const tm_qtensor* vq, const void* k16,
                     const tm_dpolicy* policy, void* o, int32_t o_dtype,

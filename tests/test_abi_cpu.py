@@ -340,6 +340,51 @@ def test_decode_per_query_head_maps_validation_and_workspace(B):
     assert size(flag) == B.TM_E_POLICY
 
 
+def test_decode_selection_validation_and_size(B):
+    L = B.lib()
+    s = _shape(B, [1000, 130], hq=4, hkv=2, d=128)
+    n = ctypes.c_size_t(0)
+    dp = B.DPolicy(dict(b8=[2, 2], b4=[5, 5], sink=1, tail=128))
+    lists = [[0, 31, 999], list(range(70)), [], [129]]      # (seq 0, kv 0), (0, 1), (1, 0), (1, 1)
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    idx = np.concatenate([np.asarray(x, np.int32) for x in lists]).astype(np.int32)
+
+    def size(o, x):
+        dp.set_selection(o, x)
+        return L.tm_decode_select(ctypes.byref(s.c), ctypes.byref(dp.c), None, None, None, ctypes.byref(n), None)
+
+    assert size(off, idx) == B.TM_OK
+    align = lambda v: (v + 255) // 256 * 256
+    n_gt = 1 + 2 + 0 + 1
+    nblk = 16 + 3
+    end = align(4 * 2 * 4)                    # {first tile, keys} per list
+    end = align(end + 8 * nblk * 2)           # column masks [nblk][hkv]
+    end = align(end + 512 * n_gt)             # tile headers
+    end = align(end + n_gt * 64 * 128 * 2)    # K rows
+    end = align(end + n_gt * 128 * 64 * 2)    # V^T
+    assert n.value == end
+    bad = idx.copy()
+    bad[1] = 0                                # not strictly increasing
+    assert size(off, bad) == B.TM_E_POLICY
+    bad = idx.copy()
+    bad[-1] = 130                             # past sequence 1's length
+    assert size(off, bad) == B.TM_E_POLICY
+    lens = np.array([500, 130], np.int32)     # a growing cache: the lists follow the current lengths
+    dp.set_lengths(lens)
+    assert size(off, idx) == B.TM_E_POLICY    # 999 >= 500
+    dp.set_lengths(None)
+    dp.set_selection(None, None)
+    assert L.tm_decode_select(ctypes.byref(s.c), ctypes.byref(dp.c), None, None, None, ctypes.byref(n),
+                              None) == B.TM_E_ARG
+    # a decode step with lists but no buffer
+    dp.set_selection(off, idx)
+    ws = ctypes.c_size_t(1 << 30)
+    nb = s.nblk()
+    kq, vq = _qt(B, 2, 0, nb, False), _qt(B, 2, 1, nb, True)
+    assert L.tm_decode(ctypes.byref(s.c), FAKE, ctypes.byref(kq), ctypes.byref(vq), FAKE, ctypes.byref(dp.c),
+                       FAKE, 2, FAKE, ctypes.byref(ws), None) == B.TM_E_ARG
+
+
 def test_growing_cache_validation(B):
     """Lengths of a growing cache are checked against the capacities before any
     GPU work: tm_decode through tm_dpolicy.lengths, tm_cache_append directly."""

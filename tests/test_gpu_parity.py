@@ -400,16 +400,21 @@ def test_deterministic():
 
 # ---------------------------------------------------------------------------- decode (small)
 
-def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, dtype="f16"):
+def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, dtype="f16", sel=None):
+    """sel: (sel_off, sel_idx) selected tokens per (sequence, KV head), or None."""
     import torch
     import tile_routed_mixed_amd as T
     w = W.small("decode16x32k", seqlens, hq=hq, hkv=hkv, d=d, dtype=dtype)
     q, k, v = W.make_qkv(w)
     dq = W.make_decode_query(w)
-    say(f"[gpu] decode {seqlens} hq={hq} hkv={hkv} d={d} {dtype} {dpol}")
+    say(f"[gpu] decode {seqlens} hq={hq} hkv={hkv} d={d} {dtype} {dpol} "
+        f"{'' if sel is None else str(len(sel[1])) + ' selected'}")
     p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol, dtype=dtype)
     p.upload(dq[0], k[0], v[0])
     p.build_cache()
+    if sel is not None:
+        p.select(*sel)
+        dpol = dict(dpol, sel_off=sel[0], sel_idx=sel[1])
     o = p.decode()
     torch.cuda.synchronize()
     kq = OQ.quantize(k[1], w.seqlens)
@@ -442,6 +447,63 @@ def test_decode_per_query_head_maps(hq, hkv, b8, b4):
     dpol = dict(b8=b8, b4=b4, sink=1, tail=100, per_q_head=1)
     o, O = _decode_case([300, 2100, 64, 1000], dpol, hq=hq, hkv=hkv)
     compare(o, O, what=f"decode per-query-head maps hq={hq}")
+
+
+@pytest.mark.parametrize("seqlens,hq,hkv,d,dtype,dpol", [
+    ([1, 100, 1000, 2000], 8, 2, 128, "f16", dict(b8=[2, 3], b4=[5, 9], sink=1, tail=128)),
+    ([3000, 777], 16, 2, 128, "f16", dict(b8=[1] * 8 + [3] * 8, b4=[4] * 8 + [12] * 8, sink=0, tail=100,
+                                          per_q_head=1)),
+    ([1500, 64, 65], 4, 1, 64, "bf16", dict(b8=[4], b4=[10], sink=1, tail=128)),
+])
+def test_decode_selected_tokens(seqlens, hq, hkv, d, dtype, dpol):
+    w = W.small("decode16x32k", seqlens, hq=hq, hkv=hkv, d=d, dtype=dtype)
+    sel = W.make_decode_selection(w, 0.05)
+    o, O = _decode_case(seqlens, dpol, hq=hq, hkv=hkv, d=d, dtype=dtype, sel=sel)
+    compare(o, O, what=f"decode selected tokens {seqlens} hq={hq}")
+
+
+def test_decode_selected_tokens_growing_cache():
+    """Selected tokens in a cache grown one token per step: every step matches
+    the oracle at the current lengths."""
+    import torch
+    import tile_routed_mixed_amd as T
+    seqlens, hq, hkv, d = [700, 1300], 8, 2, 128
+    w = W.small("decode16x32k", seqlens, hq=hq, hkv=hkv, d=d)
+    q, k, v = W.make_qkv(w)
+    dq = W.make_decode_query(w)
+    dpol = dict(b8=[2, 3], b4=[5, 9], sink=1, tail=128)
+    start = np.array([S - 3 for S in seqlens], np.int32)
+    sel = W.make_decode_selection(w, 0.05, lengths=start)
+    say(f"[gpu] decode growing cache with {len(sel[1])} selected tokens")
+    p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol)
+    p.upload(dq[0], k[0], v[0])
+    p.start(start)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    L = start.copy()
+    for step in range(3):
+        p.select(*sel)
+        o = p.decode()
+        torch.cuda.synchronize()
+        rows = np.concatenate([np.arange(cu[s_], cu[s_] + L[s_]) for s_ in range(len(seqlens))])
+        kq = OQ.quantize(k[1][rows], list(L))
+        vq = OQ.quantize(v[1][rows], list(L), layout="cols")
+        O = OA.decode(list(L), hq, hkv, d, dq[1].astype(np.float64), kq, vq, k[1][rows].astype(np.float64),
+                      v[1][rows].astype(np.float64), dict(dpol, sel_off=sel[0], sel_idx=sel[1]))
+        compare(o.cpu().numpy(), O, what=f"growing cache with selection, step {step}")
+        nxt = cu[:-1] + L
+        p.append(k[0][nxt], v[0][nxt])
+        L = L + 1
+
+
+def test_decode_empty_selection_equals_none():
+    """The selection variant of the kernel with empty lists computes the same
+    outputs bit for bit as the plain one."""
+    seqlens = [1500, 3000]
+    dpol = dict(b8=[3, 5], b4=[9, 20], sink=1, tail=128)
+    o1, _ = _decode_case(seqlens, dpol)
+    n = len(seqlens) * 2
+    o2, _ = _decode_case(seqlens, dpol, sel=(np.zeros(n + 1, np.int32), np.zeros(0, np.int32)))
+    assert np.array_equal(o1, o2)
 
 
 def test_decode_uniform_per_query_head_maps_equal_per_kv_maps():

@@ -57,7 +57,9 @@ class tm_census(ctypes.Structure):
 class tm_dpolicy(ctypes.Structure):
     _fields_ = [("b8", ctypes.POINTER(ctypes.c_int32)), ("b4", ctypes.POINTER(ctypes.c_int32)),
                 ("sink", ctypes.c_int32), ("tail_tokens", ctypes.c_int32),
-                ("lengths", ctypes.POINTER(ctypes.c_int32)), ("per_q_head", ctypes.c_int32)]
+                ("lengths", ctypes.POINTER(ctypes.c_int32)), ("per_q_head", ctypes.c_int32),
+                ("sel_off", ctypes.POINTER(ctypes.c_int32)), ("sel_idx", ctypes.POINTER(ctypes.c_int32)),
+                ("sel_buf", ctypes.c_void_p)]
 
 
 class TMError(RuntimeError):
@@ -98,6 +100,9 @@ def lib():
         L.tm_cache_append.restype = i32
         L.tm_cache_append.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(ctypes.c_int32), vp, i32,
                                       ctypes.POINTER(tm_qtensor), vp]
+        L.tm_decode_select.restype = i32
+        L.tm_decode_select.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_dpolicy), vp,
+                                       ctypes.POINTER(tm_qtensor), vp, ctypes.POINTER(ctypes.c_size_t), vp]
         L.tm_decode.restype = i32
         L.tm_decode.argtypes = [ctypes.POINTER(tm_shape), vp, ctypes.POINTER(tm_qtensor),
                                 ctypes.POINTER(tm_qtensor), vp, ctypes.POINTER(tm_dpolicy), vp, i32, vp,
@@ -284,6 +289,36 @@ class DPolicy:
         else:
             self.lengths = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
             self.c.lengths = self.lengths.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def set_selection(self, sel_off, sel_idx):
+        """Selected tokens kept in FP16: lists per (sequence, KV head), or
+        sel_off None for none.  The device buffer comes from tm_decode_select."""
+        if sel_off is None:
+            self.sel_off = self.sel_idx = None
+            self.c.sel_off = self.c.sel_idx = None
+            self.c.sel_buf = None
+            return
+        self.sel_off = np.ascontiguousarray(np.asarray(sel_off, dtype=np.int32))
+        self.sel_idx = np.ascontiguousarray(np.asarray(sel_idx, dtype=np.int32))
+        self.c.sel_off = self.sel_off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        self.c.sel_idx = self.sel_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def decode_sel_bytes(shape: "Shape", dpol: "DPolicy") -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().tm_decode_select(ctypes.byref(shape.c), ctypes.byref(dpol.c), None, None, None, ctypes.byref(n),
+                                  None), "tm_decode_select(size)")
+    return int(n.value)
+
+
+def tm_decode_select(shape: "Shape", dpol: "DPolicy", k16, vq: "QTensor", buf, stream=None):
+    """Fill `buf` (uint8 device tensor) with the selected-token tables and
+    gathered tiles of dpol's lists; the policy then points at it."""
+    n = ctypes.c_size_t(buf.numel())
+    _check(lib().tm_decode_select(ctypes.byref(shape.c), ctypes.byref(dpol.c), _ptr(k16), ctypes.byref(vq.c),
+                                  _ptr(buf), ctypes.byref(n), _stream(stream)), "tm_decode_select")
+    dpol.sel_buf = buf
+    dpol.c.sel_buf = _ptr(buf)
 
 
 def tm_cache_append(shape: Shape, lengths: np.ndarray, x, out: QTensor, stream=None):

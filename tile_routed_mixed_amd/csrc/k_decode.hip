@@ -9,12 +9,14 @@
 // [TileMix] abstract: grouped-query attention and INT8 K/V caches.
 //
 // The step is bound by HBM bytes (every cached code is read once per step).
-// One workgroup of 4 waves walks a split of one (sequence, KV head)'s cache
-// blocks; the blocks stream global -> LDS through a 4-deep ring of direct
-// (buffer-to-LDS) loads, so three blocks are in flight while one is used, and
-// each wave scores 16 keys of the current block against the (up to 16) GQA
-// query heads, which are the columns of 16x16 fp16 MFMAs:
-//   S^T = K Q^T   (v_mfma_f32_16x16x32_f16),   O^T += V^T P^T (16x16x16).
+// One wave (64 lanes) per (split, head class, sequence): a split is an even
+// share of one (sequence, KV head)'s cache blocks, and a head class is a run
+// of query heads of that KV head with one cache map; the class's query heads
+// are the columns of 16x16 fp16 MFMAs:
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_f16),   O^T += V^T P^T (same shape).
+// Codes stream from HBM straight into registers, one unit (an INT8 block, or
+// two INT4 blocks, the same bytes) at a time, double-buffered: the next
+// unit's loads are in flight while the current one is computed.  No LDS.
 // Codes enter the MFMAs as fp16 subnormals: the byte b = c + 128 (INT8) or
 // the nibble n = c + 8 (INT4) placed in the low bits of a zero-exponent fp16
 // is exactly b * 2^-24, so two perms (or a mask) per pair of codes build an
@@ -23,6 +25,9 @@
 // for outputs, one extra MFMA per block accumulates off * 2^-24 * sum(p) per
 // head, subtracted once at the end.  MFMA products and sums of these values
 // are exact fp32 (no flush of fp16 subnormals on this path).
+// FP16 window blocks read the 16-bit keys and the fp16 V^T copy.  Selected
+// tokens (when given) are masked out of their blocks and read in FP16 from
+// gathered tiles, shared among the splits.
 // A second kernel merges the splits' (max, sum, O) by log-sum-exp.
 #include "tm_kernels.h"
 
@@ -96,6 +101,7 @@ struct UnitRegs {
   u32x4 k[8];
   u32x2 v[D / 8];
   float sk[2], sv[2];
+  uint64_t xm[2];   // selected-token masks of the unit's blocks (scalar)
 };
 
 // Cross-lane moves within rows of 16 lanes (DPP): lane i of a row takes the
@@ -114,8 +120,8 @@ constexpr int kRowShr = 0x110, kRowShl = 0x100, kRowRor = 0x120;
 // SMALLG: at most 4 query heads per KV head.  The QK product leaves head
 // l16's scores in lanes l16 < 4 only (16 values a lane); they are first moved
 // four to a lane, so that the softmax works on every lane and on a quarter of
-// the values.
-template <int D, bool BF16, bool SMALLG>
+// the values.  SEL: the step reads selected tokens (a.sel).
+template <int D, bool BF16, bool SMALLG, bool SEL>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;          // k-chunks of the QK MFMA (lane group g owns channels DG*g ..)
   constexpr int ND = D / 16;          // output channel blocks
@@ -214,6 +220,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const float* const vs8 = pin_sgpr(a.vs8 + kvb0);
   const float* const ks4 = pin_sgpr(a.ks4 + kvb0);
   const float* const vs4 = pin_sgpr(a.vs4 + kvb0);
+  // selected tokens: block j's mask is entry kvb0 + j * hkv of [nblk][hkv]
+  const uint64_t* const xmp = SEL ? pin_sgpr(reinterpret_cast<const uint64_t*>(a.sel + a.sel_cm) + kvb0) : nullptr;
   const uint32_t kb8 = static_cast<uint32_t>(dsig(0, l16) * D + KW * g);
   const uint32_t kb4 = static_cast<uint32_t>(dsig(0, l16) * (D / 2) + (DG / 2) * g);
   const uint32_t vb8 = static_cast<uint32_t>(l16 * 64 + 16 * g);
@@ -256,6 +264,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       }
       r.sk[0] = sload(ks8, jo);
       r.sv[0] = sload(vs8, jo);
+      if constexpr (SEL) r.xm[0] = sload64(xmp, jo);
     } else {
       const bool two = valid && j + 1 < jend;
       const uint32_t nr0 = valid ? kBlock * D / 2 : 0u, nr1 = two ? kBlock * D / 2 : 0u;
@@ -282,6 +291,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       r.sv[0] = sload(vs4, jo);
       r.sk[1] = sload(ks4, jo1);
       r.sv[1] = sload(vs4, jo1);
+      if constexpr (SEL) {
+        r.xm[0] = sload64(xmp, jo);
+        r.xm[1] = sload64(xmp, jo1);
+      }
     }
   };
 
@@ -291,9 +304,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   for (int db = 0; db < ND; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Online softmax over one 64-key block given its S^T accumulators (16 per
-  // lane), score = acc * m1 + m0; keys at index >= L are dropped.  Leaves the
-  // fp16 P^T operands (p * sv) of the two 32-key chunks in pb.
-  auto softmax = [&](const f32x4 (&acc)[4], float m1, float m0, float sv, int j, f16x8 (&pb)[2]) {
+  // lane), score = acc * m1 + m0; key slot k stands for key kbase + k, and
+  // keys at index >= klim, or whose bit of xm is set, are dropped.  Leaves
+  // the fp16 P^T operands (p * sv) of the two 32-key chunks in pb.
+  auto softmax = [&](const f32x4 (&acc)[4], float m1, float m0, float sv, int kbase, int klim, uint64_t xm,
+                     f16x8 (&pb)[2]) {
     if constexpr (SMALLG) {
       // lane (4a + h, g) takes head h's keys 16g + 4a + i (i = 0..3): the
       // values acc[a][i] of lane (h, g)
@@ -306,11 +321,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         c[i] = dpp_f<kRowShr + 8, 0x4>(c[i], acc[2][i]);
         c[i] = dpp_f<kRowShr + 12, 0x8>(c[i], acc[3][i]);
       }
-      const bool tail = j * kBlock + kBlock > L;
+      const bool tail = kbase + kBlock > klim;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         c[i] = __builtin_fmaf(c[i], m1, m0);
-        if (tail && j * kBlock + dsig(a4, 4 * g + i) >= L) c[i] = -INFINITY;
+        if (tail && kbase + dsig(a4, 4 * g + i) >= klim) c[i] = -INFINITY;
+        if (SEL && xm != 0 && ((xm >> dsig(a4, 4 * g + i)) & 1u)) c[i] = -INFINITY;
       }
       float mx = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
       mx = fmaxf(mx, dpp_f<kRowRor + 4, 0xF>(mx, mx));   // over the 4 banks of the row
@@ -348,13 +364,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       return;
     }
     float s[4][4];
-    const bool tail = j * kBlock + kBlock > L;
+    const bool tail = kbase + kBlock > klim;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[kb][i] = __builtin_fmaf(acc[kb][i], m1, m0);
-        if (tail && j * kBlock + dsig(kb, 4 * g + i) >= L) s[kb][i] = -INFINITY;
+        if (tail && kbase + dsig(kb, 4 * g + i) >= klim) s[kb][i] = -INFINITY;
+        if (SEL && xm != 0 && ((xm >> dsig(kb, 4 * g + i)) & 1u)) s[kb][i] = -INFINITY;
       }
     float mx = s[0][0];
 #pragma unroll
@@ -411,7 +428,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     // score = tau log2e sk (2^24 acc - off sum(q)), off = 128 (INT8) or 8 (INT4)
     const float cs = a.tau_log2e * r.sk[bb];
     f16x8 pb[2];
-    softmax(acc, cs * kTwo24, -(four ? 8.0f : 128.0f) * qsum * cs, r.sv[bb], j, pb);
+    softmax(acc, cs * kTwo24, -(four ? 8.0f : 128.0f) * qsum * cs, r.sv[bb], j * kBlock, L, SEL ? r.xm[bb] : 0ull,
+            pb);
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -475,48 +493,80 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
     for (int i = 0; i < 4; ++i) oacc[db][i] = (oacc[db][i] - ocorr[i]) * kTwo24;
 
-  // ---- FP16 window blocks: 16-bit K rows and the fp16 V^T copy, all of a
-  // block's loads issued before its first product; key rows at or past L
-  // fall outside the K range and read as zeros (their scores are dropped)
-  if (ifa < ifb) {
+  // ---- FP16 blocks: 16-bit K rows (row kr0 + k of rk, `pitch` bytes apart,
+  // for key slot k) and fp16 V^T (rows of 64 slots from byte vo of rt), all
+  // of a block's loads issued before its first product; rows past the K
+  // range read as zeros (their scores are dropped by klim)
+  auto fp16_block = [&](const __amdgpu_buffer_rsrc_t& rk, uint32_t kr0, uint32_t pitch,
+                        const __amdgpu_buffer_rsrc_t& rt, uint32_t vo, int kbase, int klim, uint64_t xm,
+                        const f16x8 (&qop)[NC]) {
+    u32x4 kraw[4][NC], vraw[ND][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t row = kr0 + static_cast<uint32_t>(dsig(kb, l16));   // K row of MFMA row l16
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kraw[kb][c] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(
+            rk, row * pitch + static_cast<uint32_t>((DG * g + 8 * c) * 2), 0, 0));
+    }
+    const uint32_t vl = vo + static_cast<uint32_t>(l16 * kBlock * 2 + 32 * g);
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)   // V^T row 16 db + l16, keys 16g + 8c2 ..
+        vraw[db][c2] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(
+            rt, vl + static_cast<uint32_t>(db * 16 * kBlock * 2 + 16 * c2), 0, 0));
+    f32x4 acc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(to_f16x8<BF16>(kraw[kb][c]), qop[c], acc[kb], 0, 0, 0);
+    }
+    f16x8 pb[2];
+    softmax(acc, a.tau_log2e, 0.0f, 1.0f, kbase, klim, xm, pb);
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as<f16x8>(vraw[db][c2]), pb[c2], oacc[db], 0, 0, 0);
+  };
+
+  // the FP16 window: 16-bit keys of this sequence and the fp16 V^T copy
+  int ga = 0, gb = 0;
+  uint32_t gbase = 0, gkeys = 0;
+  if constexpr (SEL) {   // this split's share of the gathered selected tokens
+    const uint32_t* te = reinterpret_cast<const uint32_t*>(a.sel + a.sel_tab) +
+                         2 * (static_cast<size_t>(a.seq0 + b) * a.hkv + kv);
+    gbase = te[0];
+    gkeys = te[1];
+    const int ng = static_cast<int>((gkeys + kBlock - 1) / kBlock);
+    ga = ng * split / ns;
+    gb = ng * (split + 1) / ns;
+  }
+  if (ifa < ifb || ga < gb) {
     f16x8 qop[NC];
     q_operand(false, qop);
-    const uint32_t pitch = hkv * (D * 2);   // bytes between key rows of k16
-    const __amdgpu_buffer_rsrc_t rk16 =
-        make_rsrc(a.k16 + (static_cast<size_t>(tok0) * hkv + kv) * D, static_cast<uint32_t>(L - 1) * pitch + D * 2);
-    const __amdgpu_buffer_rsrc_t rt16 = make_rsrc(a.vt16 + kvb0 * (D * kBlock), span * (D * kBlock * 2));
-    for (int j = ifa; j < ifb; ++j) {
-      u32x4 kraw[4][NC], vraw[ND][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint32_t row = static_cast<uint32_t>(j * kBlock + dsig(kb, l16));   // K row of MFMA row l16
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          kraw[kb][c] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(
-              rk16, row * pitch + static_cast<uint32_t>((DG * g + 8 * c) * 2), 0, 0));
+    if (ifa < ifb) {
+      const uint32_t pitch = hkv * (D * 2);   // bytes between key rows of k16
+      const __amdgpu_buffer_rsrc_t rk16 = make_rsrc(a.k16 + (static_cast<size_t>(tok0) * hkv + kv) * D,
+                                                    static_cast<uint32_t>(L - 1) * pitch + D * 2);
+      const __amdgpu_buffer_rsrc_t rt16 = make_rsrc(a.vt16 + kvb0 * (D * kBlock), span * (D * kBlock * 2));
+      for (int j = ifa; j < ifb; ++j)
+        fp16_block(rk16, static_cast<uint32_t>(j * kBlock), pitch, rt16,
+                   static_cast<uint32_t>(j) * hkv * (D * kBlock * 2), j * kBlock, L,
+                   SEL ? sload64(xmp, static_cast<size_t>(j) * hkv) : 0ull, qop);
+    }
+    if constexpr (SEL) {
+      for (int t = ga; t < gb; ++t) {
+        const size_t tile = gbase + static_cast<uint32_t>(t);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(
+            reinterpret_cast<const uint16_t*>(a.sel + a.sel_gk) + tile * (kBlock * D), kBlock * D * 2);
+        const __amdgpu_buffer_rsrc_t rt = make_rsrc(
+            reinterpret_cast<const uint16_t*>(a.sel + a.sel_gv) + tile * (D * kBlock), D * kBlock * 2);
+        fp16_block(rk, 0u, D * 2, rt, 0u, 0, static_cast<int>(gkeys) - t * kBlock, 0ull, qop);
       }
-      const uint32_t vo = static_cast<uint32_t>(j) * hkv * (D * kBlock * 2) + static_cast<uint32_t>(l16 * kBlock * 2 + 32 * g);
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)   // V^T row 16 db + l16, keys 16g + 8c2 ..
-          vraw[db][c2] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(
-              rt16, vo + static_cast<uint32_t>(db * 16 * kBlock * 2 + 16 * c2), 0, 0));
-      f32x4 acc[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(to_f16x8<BF16>(kraw[kb][c]), qop[c], acc[kb], 0, 0, 0);
-      }
-      f16x8 pb[2];
-      softmax(acc, a.tau_log2e, 0.0f, 1.0f, j, pb);
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as<f16x8>(vraw[db][c2]), pb[c2], oacc[db], 0, 0, 0);
     }
   }
 
@@ -595,8 +645,13 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 
 template <int D, bool BF16>
 static void launch_split(bool small, dim3 grid, const DecodeArgs& a, hipStream_t st) {
-  if (small) hipLaunchKernelGGL((decode_split_kernel<D, BF16, true>), grid, dim3(64), 0, st, a);
-  else hipLaunchKernelGGL((decode_split_kernel<D, BF16, false>), grid, dim3(64), 0, st, a);
+  if (a.sel != nullptr) {
+    if (small) hipLaunchKernelGGL((decode_split_kernel<D, BF16, true, true>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, BF16, false, true>), grid, dim3(64), 0, st, a);
+  } else {
+    if (small) hipLaunchKernelGGL((decode_split_kernel<D, BF16, true, false>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, BF16, false, false>), grid, dim3(64), 0, st, a);
+  }
 }
 
 // Splits of `ncls` head classes (a.cls) over a.nseq sequences; small: every

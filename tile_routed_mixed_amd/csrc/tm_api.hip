@@ -479,6 +479,107 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
   return e == hipSuccess ? TM_OK : TM_E_HIP;
 }
 
+// Selected decode tokens: per (sequence, KV head) list {first gathered tile,
+// keys}, column masks [nblk][hkv], gathered-tile headers, K rows, V^T.
+struct DecodeSel {
+  std::vector<uint32_t> tab;    // 2 per list
+  int64_t n_gt = 0;
+  size_t tab_off = 0, cm_off = 0, gh_off = 0, gk_off = 0, gv_off = 0, bytes = 0;
+};
+
+tm_status decode_sel_plan(const tm_shape* s, const tm_dpolicy* p, const ShapeInfo& si, DecodeSel* ds) {
+  if (p->sel_idx == nullptr && p->sel_off[static_cast<size_t>(s->nseq) * s->hkv] > 0) return TM_E_ARG;
+  if (p->sel_off[0] != 0) return TM_E_POLICY;
+  ds->tab.assign(2 * static_cast<size_t>(s->nseq) * s->hkv, 0u);
+  int64_t gt = 0;
+  for (int b = 0; b < s->nseq; ++b) {
+    const int64_t cap = s->cu_seqlens[b + 1] - s->cu_seqlens[b];
+    const int64_t L = p->lengths != nullptr ? p->lengths[b] : cap;
+    for (int g = 0; g < s->hkv; ++g) {
+      const size_t r = static_cast<size_t>(b) * s->hkv + g;
+      const int64_t lo = p->sel_off[r], hi = p->sel_off[r + 1];
+      if (hi < lo) return TM_E_POLICY;
+      for (int64_t e = lo; e < hi; ++e) {
+        const int64_t c = p->sel_idx[e];
+        if (c < 0 || c >= L || (e > lo && c <= p->sel_idx[e - 1])) return TM_E_POLICY;
+      }
+      ds->tab[2 * r] = static_cast<uint32_t>(gt);
+      ds->tab[2 * r + 1] = static_cast<uint32_t>(hi - lo);
+      gt += (hi - lo + 63) / 64;
+    }
+  }
+  ds->n_gt = gt;
+  const size_t d = static_cast<size_t>(s->d);
+  ds->tab_off = 0;
+  ds->cm_off = align256(4 * ds->tab.size());
+  ds->gh_off = align256(ds->cm_off + 8 * static_cast<size_t>(si.nblk) * s->hkv);
+  ds->gk_off = align256(ds->gh_off + kGatherHdr * static_cast<size_t>(gt));
+  ds->gv_off = align256(ds->gk_off + static_cast<size_t>(gt) * 64 * d * 2);
+  ds->bytes = align256(ds->gv_off + static_cast<size_t>(gt) * d * 64 * 2);
+  if (ds->bytes > 0xFFFFFFFFull) return TM_E_UNSUPPORTED;
+  return TM_OK;
+}
+
+tm_status tm_decode_select(const tm_shape* cache, const tm_dpolicy* policy, const void* k16, const tm_qtensor* vq,
+                           void* sel_buf, size_t* sel_bytes, void* stream) {
+  ShapeInfo si;
+  tm_status st = check_shape(cache, false, &si);
+  if (st != TM_OK) return st;
+  if (policy == nullptr || policy->sel_off == nullptr || sel_bytes == nullptr) return TM_E_ARG;
+  for (int b = 0; b < cache->nseq; ++b) {
+    const int64_t cap = cache->cu_seqlens[b + 1] - cache->cu_seqlens[b];
+    if (cap < 1) return TM_E_SHAPE;
+    if (policy->lengths != nullptr && (policy->lengths[b] < 1 || policy->lengths[b] > cap)) return TM_E_SHAPE;
+  }
+  DecodeSel ds;
+  if ((st = decode_sel_plan(cache, policy, si, &ds)) != TM_OK) return st;
+  if (sel_buf == nullptr) {
+    *sel_bytes = ds.bytes;
+    return TM_OK;
+  }
+  if (*sel_bytes < ds.bytes) return TM_E_SPACE;
+  if (k16 == nullptr) return TM_E_ARG;
+  if ((st = check_qtensor(vq, cache->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
+  // host staging of the list table, the column masks and the tile headers
+  std::vector<uint8_t> buf(ds.gk_off, 0);
+  std::memcpy(buf.data() + ds.tab_off, ds.tab.data(), 4 * ds.tab.size());
+  uint64_t* cm = reinterpret_cast<uint64_t*>(buf.data() + ds.cm_off);
+  int64_t blk = 0;
+  for (int b = 0; b < cache->nseq; ++b) {
+    const int64_t cap = cache->cu_seqlens[b + 1] - cache->cu_seqlens[b];
+    for (int g = 0; g < cache->hkv; ++g) {
+      const size_t r = static_cast<size_t>(b) * cache->hkv + g;
+      const int32_t* idx = policy->sel_idx + policy->sel_off[r];
+      const uint32_t n = ds.tab[2 * r + 1];
+      for (uint32_t u = 0; u < n; ++u)
+        cm[(blk + idx[u] / 64) * cache->hkv + g] |= uint64_t(1) << (idx[u] % 64);
+      for (uint32_t t = 0; t * 64 < n; ++t) {
+        uint8_t* gh = buf.data() + ds.gh_off + static_cast<size_t>(ds.tab[2 * r] + t) * kGatherHdr;
+        const uint32_t keys = std::min<uint32_t>(64, n - 64 * t);
+        const GatherEntry ge{static_cast<uint32_t>(cache->cu_seqlens[b]), static_cast<uint32_t>(blk),
+                             static_cast<uint32_t>(g), keys};
+        std::memcpy(gh, &ge, sizeof(ge));
+        int32_t* pos = reinterpret_cast<int32_t*>(gh + 16);
+        for (uint32_t k = 0; k < 64; ++k) pos[k] = k < keys ? idx[64 * t + k] : INT32_MAX;
+      }
+    }
+    blk += (cap + 63) / 64;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(sel_buf, buf.data(), buf.size(), hipMemcpyHostToDevice, hs) != hipSuccess) return TM_E_HIP;
+  if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;
+  GatherArgs g;
+  g.trav = static_cast<uint8_t*>(sel_buf);
+  g.k = static_cast<const uint16_t*>(k16);
+  g.vt16 = vq->t16;
+  g.hkv = cache->hkv;
+  g.n_gtiles = static_cast<uint32_t>(ds.n_gt);
+  g.gh_off = static_cast<uint32_t>(ds.gh_off);
+  g.gk_off = static_cast<uint32_t>(ds.gk_off);
+  g.gv_off = static_cast<uint32_t>(ds.gv_off);
+  return launch_gather(g, cache->d, hs) == hipSuccess ? TM_OK : TM_E_HIP;
+}
+
 tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, const tm_qtensor* vq,
                     const void* k16, const tm_dpolicy* policy, void* o, int32_t o_dtype, void* ws,
                     size_t* ws_bytes, void* stream) {
@@ -503,6 +604,8 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     // a sequence's 16-bit rows (and fp16 V copy) must lie within 2 GiB of its first (32-bit offsets)
     if ((len + 63) / 64 * cache->hkv * 64 * cache->d * 2 >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
   }
+  DecodeSel ds;
+  if (policy->sel_off != nullptr && (st = decode_sel_plan(cache, policy, si, &ds)) != TM_OK) return st;
   const std::vector<HeadClass> cls = head_classes(cache, policy);
   const DecodePlan plan = decode_plan(cache, policy, cls);
   if (ws == nullptr) {
@@ -511,6 +614,7 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   }
   if (*ws_bytes < plan.ws_bytes) return TM_E_SPACE;
   if (cache->cu_seqlens_dev == nullptr || q == nullptr || k16 == nullptr || o == nullptr) return TM_E_ARG;
+  if (policy->sel_off != nullptr && policy->sel_buf == nullptr) return TM_E_ARG;
   if (o_dtype != TM_F32 && o_dtype != TM_F16) return TM_E_ARG;
   if ((st = check_qtensor(kq, cache->hkv, TM_ROWS, si.nblk, false)) != TM_OK) return st;
   if ((st = check_qtensor(vq, cache->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
@@ -538,6 +642,13 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   a.tail = policy->tail_tokens;
   a.nblk = si.nblk;
   a.tau_log2e = tau_log2e(cache);
+  if (policy->sel_off != nullptr) {
+    a.sel = static_cast<const uint8_t*>(policy->sel_buf);
+    a.sel_tab = static_cast<uint32_t>(ds.tab_off);
+    a.sel_cm = static_cast<uint32_t>(ds.cm_off);
+    a.sel_gk = static_cast<uint32_t>(ds.gk_off);
+    a.sel_gv = static_cast<uint32_t>(ds.gv_off);
+  }
   bool small = true;
   for (const HeadClass& c : cls) small = small && c.n <= 4;
   // launches of at most kMaxSeqArg sequences, each with its sequences'
@@ -548,6 +659,7 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     const int n = std::min(kMaxSeqArg, cache->nseq - s0);
     DecodeArgs c = a;
     c.nseq = n;
+    c.seq0 = s0;
     for (int i = 0; i <= n; ++i) c.cu[i] = cache->cu_seqlens[s0 + i];
     for (int i = 0; i < n; ++i) {
       const int32_t cap = cache->cu_seqlens[s0 + i + 1] - cache->cu_seqlens[s0 + i];

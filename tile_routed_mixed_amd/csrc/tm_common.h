@@ -168,6 +168,12 @@ __device__ __forceinline__ float sload(const float* p, size_t i) {
   return ((cfloat*)(p))[i];
 }
 
+// The same for a uniform 64-bit word.
+__device__ __forceinline__ uint64_t sload64(const uint64_t* p, size_t i) {
+  typedef const __attribute__((address_space(4))) uint64_t cu64;
+  return ((cu64*)(p))[i];
+}
+
 __device__ inline int seq_blk_start(const int32_t* __restrict__ cu, int seq) {
   const int lane = threadIdx.x & 63;
   int acc = 0;

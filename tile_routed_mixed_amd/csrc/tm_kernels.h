@@ -103,6 +103,12 @@ struct DecodeArgs {
   int32_t cls[kMaxClsArg];
   int32_t b8[kMaxClsArg];
   int32_t b4[kMaxClsArg];
+  // selected tokens (kept in FP16): buffer written by tm_decode_select, or
+  // null; list entries {first gathered tile, keys} per (sequence, KV head),
+  // column masks [nblk][hkv] u64, gathered K rows and V^T (byte offsets)
+  const uint8_t* sel;
+  uint32_t sel_tab, sel_cm, sel_gk, sel_gv;
+  int seq0;                     // first sequence of this launch
   int32_t cu[kMaxSeqArg + 1];   // token offsets of this launch's sequences (absolute)
   int32_t len[kMaxSeqArg];      // their current lengths (at most cu[i + 1] - cu[i])
   int32_t blk[kMaxSeqArg];      // their first cache block (absolute)
@@ -114,6 +120,7 @@ hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
 hipError_t launch_decode_split(const DecodeArgs& a, int ncls, bool small, int d, bool bf16, hipStream_t st);
+// (a.sel selects the variant that reads selected tokens)
 hipError_t launch_decode_combine(const DecodeArgs& a, int d, hipStream_t st);
 
 }  // namespace tmx

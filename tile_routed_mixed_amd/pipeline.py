@@ -105,6 +105,20 @@ class DecodePipeline:
         B.tm_quantize_pack(self.shape, self.k, self.kq, stream)
         B.tm_quantize_pack(self.shape, self.v, self.vq, stream)
 
+    def select(self, sel_off, sel_idx, stream=None):
+        """Keep the listed tokens in FP16 (lists per (sequence, KV head), after
+        build_cache / start); call again when the lists or lengths change."""
+        import torch
+        self.dpol.set_selection(sel_off, sel_idx)
+        if sel_off is None:
+            return
+        n = B.decode_sel_bytes(self.shape, self.dpol)
+        buf = getattr(self, "sel_buf", None)
+        if buf is None or buf.numel() < n:
+            buf = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        self.sel_buf = buf
+        B.tm_decode_select(self.shape, self.dpol, self.k, self.vq, buf, stream)
+
     def decode(self, stream=None):
         return B.tm_decode(self.shape, self.q, self.kq, self.vq, self.k, self.dpol, o=self.o, ws=self.ws,
                            stream=stream)

@@ -7,7 +7,7 @@ classification, no scores).  Every array is drawn with
 CPU oracle receive identical bits.
 
 Streams: Q = 1, K = 2, V = 3, policy = 4, outlier channels = 5, decode query = 6,
-locality = 7, selected keys = 8.  Values are N(0, 1) in float32, rounded half-to-even to the
+locality = 7, selected keys = 8, selected decode tokens = 9.  Values are N(0, 1) in float32, rounded half-to-even to the
 16-bit input type.
 
 Workloads (the shapes are those of the attention layers the pages benchmark:
@@ -42,6 +42,7 @@ import numpy as np
 
 WORKLOAD_IDS = {"toy512": 1, "gqa8k": 2, "varlen32k": 3, "long128k": 4, "decode16x32k": 5, "local8k": 6}
 STREAM_Q, STREAM_K, STREAM_V, STREAM_POLICY, STREAM_OUTLIER, STREAM_DQ, STREAM_LOCAL, STREAM_SEL = 1, 2, 3, 4, 5, 6, 7, 8
+STREAM_DSEL = 9
 
 
 @dataclasses.dataclass
@@ -240,3 +241,18 @@ def make_selection(w: Workload, frac: float, window: int, stream_offset: int = 0
     off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
     idx = np.concatenate(lists).astype(np.int32) if lists else np.zeros(0, np.int32)
     return dict(kind=3, window=int(window), sel_off=off, sel_idx=idx)
+
+
+def make_decode_selection(w: Workload, frac: float, lengths=None):
+    """Selected decode tokens: for every (sequence, KV head), round(frac * L)
+    positions below the sequence's length L (or lengths[s]) drawn without
+    replacement, sorted; returns (sel_off [nseq*hkv + 1], sel_idx)."""
+    rng = np.random.default_rng([w.wid, STREAM_DSEL])
+    lists = []
+    for s, S in enumerate(w.seqlens):
+        L = int(S if lengths is None else lengths[s])
+        for _ in range(w.hkv):
+            lists.append(np.sort(rng.choice(L, size=int(round(frac * L)), replace=False)).astype(np.int32))
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    idx = np.concatenate(lists).astype(np.int32) if lists else np.zeros(0, np.int32)
+    return off, idx
