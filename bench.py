@@ -214,8 +214,10 @@ def decode_block_counts(L, b8, b4, sink, tail):
     return c
 
 
-def decode_bench(steps, rotate=3):
-    """Decode over a 16 x 32768-token compressed cache; returns timing and bytes."""
+def decode_bench(steps, rotate=3, select_frac=None):
+    """Decode over a 16 x 32768-token compressed cache; returns timing and bytes.
+    select_frac: that fraction of every (sequence, KV head)'s tokens (seeded)
+    is kept in FP16 as selected tokens."""
     import numpy as np
     import torch
     import tile_routed_mixed_amd as T
@@ -229,6 +231,8 @@ def decode_bench(steps, rotate=3):
         p = T.DecodePipeline(w.seqlens, w.hq, w.hkv, w.d, dpol, dtype=w.dtype)
         p.upload(dq[0], k[0], v[0])
         p.build_cache()
+        if select_frac is not None:
+            p.select(*W.make_decode_selection(w, select_frac))
         caches.append(p)
     del k, v
     torch.cuda.synchronize()
@@ -242,6 +246,12 @@ def decode_bench(steps, rotate=3):
                                             dpol["tail"]).items():
                 counts[t] += n
     nbytes = sum(per[t] * n for t, n in counts.items())
+    n_sel = 0
+    if select_frac is not None:
+        # selected tokens: their 16-bit K row and fp16 V column, plus one 8-byte
+        # mask per read block (their codes are still read with their blocks)
+        n_sel = int(caches[0].dpol.sel_idx.size)
+        nbytes += n_sel * w.d * 2 * 2 + 8 * (counts["int8"] + counts["int4"] + counts["fp16"])
     for i in range(5):
         caches[i % rotate].decode()
     torch.cuda.synchronize()
@@ -263,7 +273,10 @@ def decode_bench(steps, rotate=3):
         ev[i][1].record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    return {"workload": describe(w) + ", cache tags (b8, b4) = (128, 320) blocks, last 128 tokens FP16",
+    desc = describe(w) + ", cache tags (b8, b4) = (128, 320) blocks, last 128 tokens FP16"
+    if select_frac is not None:
+        desc += f", {select_frac * 100:g} % of tokens per (sequence, KV head) selected and read in FP16 ({n_sel} in all)"
+    return {"workload": desc,
             "bytes_per_step": nbytes, "ms_mean": mean, "ms_median_single": ms[len(ms) // 2],
             "ms_min_single": ms[0],
             "GBps": nbytes / (mean * 1e-3) / 1e9, "hbm_frac": nbytes / (mean * 1e-3) / PEAK_HBM,
@@ -391,6 +404,11 @@ def main():
         out["decode"] = d
         out["decode_kv_gbs"] = d["GBps"]
         log(f"[bench] decode {d['ms_mean']:.4f} ms, {d['GBps']:.1f} GB/s ({d['hbm_frac'] * 100:.1f} % of HBM)")
+        torch.cuda.empty_cache()
+        torch.cuda.empty_cache()
+        ds = decode_bench(max(20, args.steps), select_frac=0.05)
+        out["decode_selected"] = ds
+        log(f"[bench] decode with 5 % selected tokens {ds['ms_mean']:.4f} ms, {ds['GBps']:.1f} GB/s")
         torch.cuda.empty_cache()
         dl = decode_loop_bench()
         out["decode_loop"] = dl
