@@ -384,26 +384,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const uint8_t* kl = lds + boff;
     const uint8_t* vl = kl + KBYTES;
-    const bool need_mask = (j * kBlock + kBlock - 1 > qrow0) || (j * kBlock + kBlock > len) ||
-                           (HYB && (gath || edge || cm != 0));
-    // gathered tiles: the key positions of this lane's 16 slots sigma(kb, 4g + i)
-    i32x4 gpos[4];
-    if (gath) {
-      const int32_t* gp = reinterpret_cast<const int32_t*>(a.trav + th->gh_off + static_cast<size_t>(j) * kGatherHdr + 16);
+    // need_mmask: pairs to drop from the row maxima too (causal, sequence end,
+    // window edge, gathered slots); need_mask: any pair to drop.  Selected
+    // keys masked out of a regular tile still count in its maxima: each is a
+    // score of the row (computed again in FP16 in a gathered tile).
+    const bool need_mmask = (j * kBlock + kBlock - 1 > qrow0) || (j * kBlock + kBlock > len) || gath || edge;
+    const bool need_mask = need_mmask || (HYB && cm != 0);
+    // hybrid: this tile pass's excluded (row, slot) pairs as one 16-bit mask
+    // per row block, bit 4 kb + i for slot sigma(kb, 4g + i)
+    uint32_t xmask[QB], mmask[QB];
+    if constexpr (HYB) {
+      if (need_mask) {
+        if (gath) {   // gathered tile: the slots' key positions, compared with the rows
+          const int32_t* gp =
+              reinterpret_cast<const int32_t*>(a.trav + th->gh_off + static_cast<size_t>(j) * kGatherHdr + 16);
+          i32x4 gpos[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) gpos[kb] = *reinterpret_cast<const i32x4*>(gp + krow(kb) + 8 * g);
+          for (int kb = 0; kb < 4; ++kb) gpos[kb] = *reinterpret_cast<const i32x4*>(gp + krow(kb) + 8 * g);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int row = qrow0 + qb * 16 + l16;
+            uint32_t m = 0;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) m |= static_cast<uint32_t>(gpos[kb][i] > row) << (4 * kb + i);
+            xmask[qb] = mmask[qb] = m;
+          }
+        } else {
+          // the selected keys of the lane's slots: bits 8g + {0..7, 32..39} of cm
+          const uint64_t t64 = cm >> (8 * g);
+          const uint32_t lm = static_cast<uint32_t>(t64 & 0xFFu) | (static_cast<uint32_t>(t64 >> 24) & 0xFF00u);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int row = qrow0 + qb * 16 + l16;
+            uint32_t m = 0;
+            if (need_mmask) {
+#pragma unroll
+              for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int key = j * kBlock + sigma(kb, 4 * g + i);
+                  bool x = key > row || key >= len;
+                  if (edge) x = x || ((row - key < win) != (prec == TM_FP16));
+                  m |= static_cast<uint32_t>(x) << (4 * kb + i);
+                }
+            }
+            mmask[qb] = m;
+            xmask[qb] = m | lm;
+          }
+        }
+      }
     }
-    // (row, slot) excluded from this tile pass
-    auto masked = [&](int kb, int i, int row) -> bool {
-      const int sg = sigma(kb, 4 * g + i);
+    // (row block qb, slot) excluded from this tile pass (mx: from the row maxima)
+    auto masked = [&](int kb, int i, int qb, bool mx = false) -> bool {
       if constexpr (HYB) {
-        if (gath) return gpos[kb][i] > row;
-        const int key = j * kBlock + sg;
-        bool m = key > row || key >= len || ((cm >> sg) & 1u);
-        if (edge) m = m || ((row - key < win) != (prec == TM_FP16));
-        return m;
+        return ((mx ? mmask[qb] : xmask[qb]) >> (4 * kb + i)) & 1u;
       } else {
-        const int key = j * kBlock + sg;
+        const int row = qrow0 + qb * 16 + l16;
+        const int key = j * kBlock + sigma(kb, 4 * g + i);
         return key > row || key >= len;
       }
     };
@@ -437,13 +476,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int row = qrow0 + qb * 16 + l16;
-        if (need_mask) {
+        if (need_mmask) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (masked(kb, i, row)) xf[kb][qb][i] = -INFINITY;
+              if (masked(kb, i, qb, true)) xf[kb][qb][i] = -INFINITY;
         }
         float mf = xf[0][qb][0];
 #pragma unroll
@@ -519,15 +557,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // row maxima on the integer products (cs >= 0 keeps the order); masked
       // keys count as INT_MIN, below every product (|a| <= 2^21)
       int mrow[QB];
-      if (need_mask) {
+      if (need_mmask) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int row = qrow0 + qb * 16 + l16;
           int mi = INT_MIN;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mi = max(mi, masked(kb, i, row) ? INT_MIN : acc[kb][qb][i]);
+            for (int i = 0; i < 4; ++i) mi = max(mi, masked(kb, i, qb, true) ? INT_MIN : acc[kb][qb][i]);
           mrow[qb] = mi;
         }
       } else {
@@ -577,14 +614,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int row = qrow0 + qb * 16 + l16;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float s = __builtin_fmaf(xf[kb][qb][i], cs, nb[qb]);
             pb[kb >> 1][qb][4 * (kb & 1) + i] =
-                static_cast<_Float16>(__builtin_amdgcn_exp2f(masked(kb, i, row) ? -INFINITY : s));
+                static_cast<_Float16>(__builtin_amdgcn_exp2f(masked(kb, i, qb) ? -INFINITY : s));
           }
       }
     } else {
