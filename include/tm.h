@@ -204,8 +204,10 @@ typedef struct tm_dpolicy {
    * selected key is read in FP16 whatever its block's tag (SKIP included);
    * the other keys follow their block's tag.  sel_buf: device buffer that
    * tm_decode_select filled for these lists (host arrays read during the
-   * calls).  ([HyQuant] "How HyQuant works": selected tokens and the recent
-   * window stay FP16 in the decode cache.) */
+   * calls).  tm_decode reads only the list lengths and trusts the positions
+   * that tm_decode_select checked: after the lists or the lengths change,
+   * call tm_decode_select again.  ([HyQuant] "How HyQuant works": selected
+   * tokens and the recent window stay FP16 in the decode cache.) */
   const int32_t* sel_off;
   const int32_t* sel_idx;
   const void* sel_buf;

@@ -487,7 +487,11 @@ struct DecodeSel {
   size_t tab_off = 0, cm_off = 0, gh_off = 0, gk_off = 0, gv_off = 0, bytes = 0;
 };
 
-tm_status decode_sel_plan(const tm_shape* s, const tm_dpolicy* p, const ShapeInfo& si, DecodeSel* ds) {
+// positions: check every listed position (tm_decode_select); the decode step
+// itself needs only the list lengths (its reads are bounded by the buffer the
+// select call built)
+tm_status decode_sel_plan(const tm_shape* s, const tm_dpolicy* p, const ShapeInfo& si, DecodeSel* ds,
+                          bool positions) {
   if (p->sel_idx == nullptr && p->sel_off[static_cast<size_t>(s->nseq) * s->hkv] > 0) return TM_E_ARG;
   if (p->sel_off[0] != 0) return TM_E_POLICY;
   ds->tab.assign(2 * static_cast<size_t>(s->nseq) * s->hkv, 0u);
@@ -498,8 +502,8 @@ tm_status decode_sel_plan(const tm_shape* s, const tm_dpolicy* p, const ShapeInf
     for (int g = 0; g < s->hkv; ++g) {
       const size_t r = static_cast<size_t>(b) * s->hkv + g;
       const int64_t lo = p->sel_off[r], hi = p->sel_off[r + 1];
-      if (hi < lo) return TM_E_POLICY;
-      for (int64_t e = lo; e < hi; ++e) {
+      if (hi < lo || hi - lo > L) return TM_E_POLICY;
+      for (int64_t e = lo; positions && e < hi; ++e) {
         const int64_t c = p->sel_idx[e];
         if (c < 0 || c >= L || (e > lo && c <= p->sel_idx[e - 1])) return TM_E_POLICY;
       }
@@ -532,7 +536,7 @@ tm_status tm_decode_select(const tm_shape* cache, const tm_dpolicy* policy, cons
     if (policy->lengths != nullptr && (policy->lengths[b] < 1 || policy->lengths[b] > cap)) return TM_E_SHAPE;
   }
   DecodeSel ds;
-  if ((st = decode_sel_plan(cache, policy, si, &ds)) != TM_OK) return st;
+  if ((st = decode_sel_plan(cache, policy, si, &ds, true)) != TM_OK) return st;
   if (sel_buf == nullptr) {
     *sel_bytes = ds.bytes;
     return TM_OK;
@@ -605,7 +609,7 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
     if ((len + 63) / 64 * cache->hkv * 64 * cache->d * 2 >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
   }
   DecodeSel ds;
-  if (policy->sel_off != nullptr && (st = decode_sel_plan(cache, policy, si, &ds)) != TM_OK) return st;
+  if (policy->sel_off != nullptr && (st = decode_sel_plan(cache, policy, si, &ds, false)) != TM_OK) return st;
   const std::vector<HeadClass> cls = head_classes(cache, policy);
   const DecodePlan plan = decode_plan(cache, policy, cls);
   if (ws == nullptr) {
