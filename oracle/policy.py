@@ -281,3 +281,29 @@ def hybrid_tile_classes(S: int, bq: int, bk: int, window: int) -> np.ndarray:
             n_in, n_all = int(inwin.sum()), int(causal.sum())
             out[i, j] = WIN_FULL if n_in == n_all else (WIN_NONE if n_in == 0 else WIN_EDGE)
     return out
+
+
+# ---------------------------------------------------------------- selection
+
+def vline_importance(q64: np.ndarray, k64: np.ndarray, n_obs: int, tau: float) -> np.ndarray:
+    """Vertical-line signal of one (sequence, query head) ([HyQuant] "How
+    HyQuant works": tokens are picked from attention-pattern signals; section
+    "The observation behind the method": a few key positions are attended by
+    many queries).  Reading: the attention mass each key receives from the
+    last n_obs query rows of the sequence, with 16-bit scores (float64 here):
+    I(c) = sum over probe rows r >= c of softmax_r(tau q_r . k)[c].
+    q64 [S][d], k64 [S][d] of one head; returns I [S]."""
+    S = q64.shape[0]
+    imp = np.zeros(S)
+    for r in range(max(0, S - n_obs), S):
+        s = tau * (k64[:r + 1] @ q64[r])
+        p = np.exp(s - s.max())
+        imp[:r + 1] += p / p.sum()
+    return imp
+
+
+def top_k_positions(imp: np.ndarray, k: int) -> np.ndarray:
+    """The k positions of largest importance (ties to the lower position),
+    ascending."""
+    order = np.lexsort((np.arange(len(imp)), -imp))
+    return np.sort(order[:k]).astype(np.int64)
