@@ -299,6 +299,28 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
 tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, void* trav,
                              const void* k, const tm_qtensor* vq, void* stream);
 
+/* Vertical-line token selection for the hybrid policies ([HyQuant] "The
+ * observation behind the method" and "How HyQuant works": a few key positions
+ * are attended by many queries; tokens to keep in FP16 are picked from
+ * attention-pattern signals).  For every (sequence s, query head h) the
+ * attention mass each key receives from the last min(n_obs, len_s) query rows
+ * (softmax over each row's keys of scale * q . k on the 16-bit values, fp32):
+ *   mass[t][h] (device float [T][hq], written).
+ * sel_idx (device int32, may be NULL): the counts[s] keys of largest mass of
+ * each list, ascending (ties to the lower position); lists are per query head
+ * (per_kv_head = 0: mass of the head) or per KV head (per_kv_head = 1: mass
+ * summed over the KV head's query heads), ordered sequence, then head, each of
+ * counts[s] entries -- the layout of the hybrid policy lists (sel_off follows
+ * from counts).  q [T][hq][d], k [T][hkv][d] 16-bit (device); counts host
+ * [nseq], 0 <= counts[s] <= len_s; 1 <= n_obs <= 64.
+ * ws: workspace; ws == NULL writes the size to *ws_bytes and returns TM_OK.
+ * Synchronizes `stream` (small per-sequence tables are staged from the host).
+ * Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY (counts, n_obs), TM_E_SPACE,
+ * TM_E_HIP. */
+tm_status tm_select_vertical(const tm_shape* shape, const void* q, const void* k, int32_t n_obs,
+                             const int32_t* counts, int32_t per_kv_head, float* mass, int32_t* sel_idx,
+                             void* ws, size_t* ws_bytes, void* stream);
+
 /* Fused tile-routed causal prefill.
  *  trav: built by tm_build_traversal for this shape; policy_kind: the kind
  *    of the policy it was built from (selects the kernel specialization; a

@@ -1,0 +1,93 @@
+"""GPU: vertical-line token selection (tm_select_vertical) against the oracle.
+
+The attention mass of every key (fp32 on the GPU, float64 in the oracle) must
+agree within 1e-5 + 1e-4 x mass; the selected lists must be valid top-k sets
+of the oracle's masses (where masses sit within that tolerance of the k-th
+largest, either choice is correct): ascending, unique, no unselected key
+clearly above the k-th largest and no selected key clearly below it.  The
+lists then drive a hybrid prefill, checked against the oracle on the same
+lists.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import policy as OP
+
+from _gpu_helpers import compare, oracle_prefill, run_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, n_obs, counts, per_kv):
+    import torch
+    import tile_routed_mixed_amd as T
+    q, k, v = W.make_qkv(w)
+    shape = T.Shape(w.seqlens, w.hq, w.hkv, w.d, w.bq, 64, T.TM_BF16 if w.dtype == "bf16" else T.TM_F16,
+                    device="cuda:0")
+    dq = torch.from_numpy(q[0].view(np.int16).copy()).to("cuda:0")
+    dk = torch.from_numpy(k[0].view(np.int16).copy()).to("cuda:0")
+    say(f"[gpu] select seqlens={w.seqlens} hq={w.hq} hkv={w.hkv} d={w.d} n_obs={n_obs} counts={counts} per_kv={per_kv}")
+    mass, off, idx = T.tm_select_vertical(shape, dq, dk, n_obs, counts, per_kv)
+    torch.cuda.synchronize()
+    return (q, k, v), mass.cpu().numpy(), off, idx
+
+
+def _check(w, qkv, mass, off, idx, n_obs, counts, per_kv):
+    q, k, _ = qkv
+    tau = 1 / math.sqrt(w.d)
+    cu = w.cu_seqlens
+    grp = w.hq // w.hkv
+    nl = w.hkv if per_kv else w.hq
+    for s, S in enumerate(w.seqlens):
+        imps = []
+        for h in range(w.hq):
+            ref = OP.vline_importance(q[1][cu[s]:cu[s + 1], h].astype(np.float64),
+                                      k[1][cu[s]:cu[s + 1], h // grp].astype(np.float64), n_obs, tau)
+            got = mass[cu[s]:cu[s + 1], h]
+            assert np.all(np.abs(got - ref) <= 1e-5 + 1e-4 * ref), (s, h, float(np.abs(got - ref).max()))
+            imps.append(ref)
+        for g in range(nl):
+            ref = sum(imps[g * grp:(g + 1) * grp]) if per_kv else imps[g]
+            r = s * nl + g
+            sel = idx[off[r]:off[r + 1]]
+            kk = counts[s]
+            assert len(sel) == kk
+            if kk == 0:
+                continue
+            assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < S
+            kth = np.sort(ref)[::-1][kk - 1]
+            tol = 1e-5 * (grp if per_kv else 1) + 1e-4 * kth
+            chosen = np.zeros(S, bool)
+            chosen[sel] = True
+            assert np.all(ref[chosen] >= kth - tol), (s, g)
+            assert np.all(ref[~chosen] <= kth + tol), (s, g)
+
+
+@pytest.mark.parametrize("name,seqlens,kw,n_obs,frac,per_kv", [
+    ("gqa8k", [1000, 30, 2100], dict(hq=4, hkv=2), 64, 0.05, False),
+    ("gqa8k", [1000, 30, 2100], dict(hq=4, hkv=2), 64, 0.05, True),
+    ("long128k", [700, 64], dict(hq=2, hkv=1, d=64), 17, 0.2, False),
+    ("varlen32k", [129, 1], dict(hq=2, hkv=2), 64, 1.0, False),
+])
+def test_vertical_selection(name, seqlens, kw, n_obs, frac, per_kv):
+    w = W.small(name, seqlens, **kw)
+    counts = [int(round(frac * S)) for S in seqlens]
+    qkv, mass, off, idx = _run(w, n_obs, counts, per_kv)
+    _check(w, qkv, mass, off, idx, n_obs, counts, per_kv)
+
+
+def test_selection_on_locality_inputs_drives_hybrid_prefill():
+    """On inputs with a position signal the selected keys differ by head;
+    the lists feed the hybrid prefill, which matches the oracle on them."""
+    w = W.small("local8k", [1500, 600], hq=4, hkv=2)
+    counts = [int(round(0.05 * S)) for S in w.seqlens]
+    qkv, mass, off, idx = _run(w, 64, counts, False)
+    _check(w, qkv, mass, off, idx, 64, counts, False)
+    pol = dict(kind=3, window=128, sel_off=off, sel_idx=idx)
+    q, k, v = qkv
+    _, _, o, lse, _ = run_prefill(w, pol, q, k, v)
+    O, L, _, _ = oracle_prefill(w, pol, q, k, v)
+    compare(o, O, lse, L, what="hybrid prefill on selected keys")

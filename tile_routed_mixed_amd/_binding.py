@@ -93,6 +93,9 @@ def lib():
         L.tm_gather_selected.restype = i32
         L.tm_gather_selected.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp, vp,
                                          ctypes.POINTER(tm_qtensor), vp]
+        L.tm_select_vertical.restype = i32
+        L.tm_select_vertical.argtypes = [ctypes.POINTER(tm_shape), vp, vp, i32, ctypes.POINTER(ctypes.c_int32), i32,
+                                         vp, vp, vp, ctypes.POINTER(ctypes.c_size_t), vp]
         L.tm_prefill.restype = i32
         L.tm_prefill.argtypes = [ctypes.POINTER(tm_shape), vp, i32, vp, vp, ctypes.POINTER(tm_qtensor),
                                  ctypes.POINTER(tm_qtensor), ctypes.POINTER(tm_qtensor), vp, i32, vp, vp, vp,
@@ -224,6 +227,32 @@ def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, vq: "QTensor", s
     traversal's gathered tiles."""
     _check(lib().tm_gather_selected(ctypes.byref(shape.c), ctypes.byref(policy.c), _ptr(trav), _ptr(k),
                                     ctypes.byref(vq.c), _stream(stream)), "tm_gather_selected")
+
+
+def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bool = False, stream=None):
+    """Attention mass of each key from the last n_obs query rows, and the
+    counts[s] keys of largest mass per list.  Returns (mass [T][hq] float32
+    device tensor, sel_off (host int32), sel_idx (host int32)): the index
+    lists of a hybrid prefill policy (per query head) or of a decode selection
+    (per KV head)."""
+    import torch
+    cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+    cp = cnt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    n = ctypes.c_size_t(0)
+    _check(lib().tm_select_vertical(ctypes.byref(shape.c), None, None, int(n_obs), cp, int(per_kv_head), None, None,
+                                    None, ctypes.byref(n), None), "tm_select_vertical(size)")
+    dev = q.device
+    ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+    mass = torch.empty((shape.T, shape.hq), dtype=torch.float32, device=dev)
+    nl = shape.hkv if per_kv_head else shape.hq
+    total = int(nl * cnt.astype(np.int64).sum())
+    sel = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    _check(lib().tm_select_vertical(ctypes.byref(shape.c), _ptr(q), _ptr(k), int(n_obs), cp, int(per_kv_head),
+                                    _ptr(mass), _ptr(sel), _ptr(ws), ctypes.byref(n), _stream(stream)),
+           "tm_select_vertical")
+    per_list = np.repeat(cnt, nl)
+    sel_off = np.concatenate([[0], np.cumsum(per_list)]).astype(np.int32)
+    return mass, sel_off, sel[:total].cpu().numpy().astype(np.int32)
 
 
 def traversal_bytes(shape: Shape, policy: Policy) -> int:

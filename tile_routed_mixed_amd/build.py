@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtm.so")
-SOURCES = ["tm_api.hip", "k_quant.hip", "k_trav.hip", "k_prefill.hip", "k_decode.hip"]
+SOURCES = ["tm_api.hip", "k_quant.hip", "k_trav.hip", "k_prefill.hip", "k_decode.hip", "k_select.hip"]
 ARCH = "gfx950"
 
 

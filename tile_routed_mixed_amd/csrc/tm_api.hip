@@ -425,6 +425,66 @@ tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, voi
   return launch_gather(g, shape->d, static_cast<hipStream_t>(stream)) == hipSuccess ? TM_OK : TM_E_HIP;
 }
 
+tm_status tm_select_vertical(const tm_shape* shape, const void* q, const void* k, int32_t n_obs,
+                             const int32_t* counts, int32_t per_kv_head, float* mass, int32_t* sel_idx, void* ws,
+                             size_t* ws_bytes, void* stream) {
+  ShapeInfo si;
+  tm_status st = check_shape(shape, false, &si);
+  if (st != TM_OK) return st;
+  if (counts == nullptr || ws_bytes == nullptr) return TM_E_ARG;
+  if (n_obs < 1 || n_obs > 64 || (per_kv_head != 0 && per_kv_head != 1)) return TM_E_POLICY;
+  const int nl = per_kv_head ? shape->hkv : shape->hq;
+  int64_t tiles = 0, sel_total = 0;
+  int maxnt = 0;
+  std::vector<int32_t> tab(3 * static_cast<size_t>(shape->nseq));
+  for (int b = 0; b < shape->nseq; ++b) {
+    const int64_t len = shape->cu_seqlens[b + 1] - shape->cu_seqlens[b];
+    if (counts[b] < 0 || counts[b] > len) return TM_E_POLICY;
+    const int nt = static_cast<int>((len + 63) / 64);
+    tab[b] = static_cast<int32_t>(tiles);
+    tab[shape->nseq + b] = counts[b];
+    tab[2 * shape->nseq + b] = static_cast<int32_t>(sel_total);
+    tiles += nt;
+    sel_total += static_cast<int64_t>(nl) * counts[b];
+    maxnt = std::max(maxnt, nt);
+  }
+  if (sel_total >= (int64_t(1) << 31)) return TM_E_UNSUPPORTED;
+  const size_t part_b = static_cast<size_t>(tiles) * shape->hq * 128 * 4;
+  const size_t rows_b = static_cast<size_t>(shape->nseq) * shape->hq * 128 * 4;
+  const size_t tab_off = align256(part_b + rows_b);
+  const size_t need = align256(tab_off + 4 * tab.size());
+  if (ws == nullptr) {
+    *ws_bytes = need;
+    return TM_OK;
+  }
+  if (*ws_bytes < need) return TM_E_SPACE;
+  if (q == nullptr || k == nullptr || mass == nullptr || shape->cu_seqlens_dev == nullptr) return TM_E_ARG;
+  if (maxnt == 0) return TM_OK;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  if (hipMemcpyAsync(w + tab_off, tab.data(), 4 * tab.size(), hipMemcpyHostToDevice, hs) != hipSuccess) return TM_E_HIP;
+  if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;
+  SelectArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.cu = shape->cu_seqlens_dev;
+  a.nseq = shape->nseq;
+  a.hq = shape->hq;
+  a.hkv = shape->hkv;
+  a.n_obs = n_obs;
+  a.bf16 = shape->dtype == TM_BF16;
+  a.per_kv = per_kv_head;
+  a.tau_log2e = tau_log2e(shape);
+  a.part = reinterpret_cast<float*>(w);
+  a.rows = reinterpret_cast<float*>(w + part_b);
+  a.mass = mass;
+  a.tile0 = reinterpret_cast<const int32_t*>(w + tab_off);
+  a.kcount = a.tile0 + shape->nseq;
+  a.sel_base = a.tile0 + 2 * shape->nseq;
+  a.sel = sel_idx;
+  return launch_select(a, shape->d, maxnt, hs) == hipSuccess ? TM_OK : TM_E_HIP;
+}
+
 tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kind, const void* q, const void* k,
                      const tm_qtensor* qq, const tm_qtensor* kq, const tm_qtensor* vq, void* o, int32_t o_dtype,
                      float* lse, int32_t* dbg_qk, const int32_t* dbg_tiles, int32_t n_dbg, void* stream) {

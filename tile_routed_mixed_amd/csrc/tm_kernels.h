@@ -114,10 +114,26 @@ struct DecodeArgs {
   int32_t blk[kMaxSeqArg];      // their first cache block (absolute)
 };
 
+struct SelectArgs {
+  const uint16_t* q;        // [T][hq][D] 16-bit
+  const uint16_t* k;        // [T][hkv][D] 16-bit
+  const int32_t* cu;        // device prefix sums
+  int nseq, hq, hkv, n_obs, bf16, per_kv;
+  float tau_log2e;
+  float* part;              // [tiles][hq][64][2] partial (max, sum) per probe row
+  float* rows;              // [nseq][hq][64][2] each probe row's (max, sum)
+  float* mass;              // [T][hq] attention mass of each key
+  const int32_t* tile0;     // [nseq] first tile of each sequence (device, in the workspace)
+  const int32_t* kcount;    // [nseq] keys to select per list
+  const int32_t* sel_base;  // [nseq] first output entry of each sequence's lists
+  int32_t* sel;             // output positions, or null (mass only)
+};
+
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, int d, int maxnt, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
 hipError_t launch_decode_split(const DecodeArgs& a, int ncls, bool small, int d, bool bf16, hipStream_t st);
 // (a.sel selects the variant that reads selected tokens)

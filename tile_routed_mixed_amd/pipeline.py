@@ -45,6 +45,14 @@ class PrefillPipeline:
         if self.trav.numel() < need:
             self.trav = torch.empty(need, dtype=torch.uint8, device=self.device)
 
+    def vertical_policy(self, frac: float, window: int, n_obs: int = 64, stream=None):
+        """Hybrid policy whose selected keys are, per (sequence, query head),
+        the round(frac * len) keys of largest attention mass from the last
+        n_obs query rows (tm_select_vertical over the uploaded Q and K)."""
+        counts = [int(round(frac * S)) for S in self.shape.seqlens]
+        _, off, idx = B.tm_select_vertical(self.shape, self.q, self.k, n_obs, counts, False, stream)
+        return dict(kind=B.TM_POLICY_HYBRID, window=int(window), sel_off=off, sel_idx=idx)
+
     def upload(self, q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray):
         self.q = _dev_bits(q_bits, self.device)
         self.k = _dev_bits(k_bits, self.device)
