@@ -122,7 +122,8 @@ def prefill_config_line(name, steps=10, warmup=2, hybrid=None):
     events on the launch stream, back to back), effective dense-causal rate,
     and the fraction of the precision-weighted MFMA peak of its executed tiles.
     hybrid = (fraction selected, window): the workload's shape under the
-    token-granular policy instead of its own."""
+    token-granular policy instead of its own, with the selected keys picked
+    on the GPU by the vertical-line pass (tm_select_vertical, timed apart)."""
     import torch
     import tile_routed_mixed_amd as T
     import workloads as W
@@ -133,6 +134,18 @@ def prefill_config_line(name, steps=10, warmup=2, hybrid=None):
     pp.upload(q[0], k[0], v[0])
     del q, k, v
     pp.quantize()
+    t_sel = None
+    if hybrid is not None:
+        pol = pp.vertical_policy(hybrid[0], hybrid[1])
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(5):
+            pp.vertical_policy(hybrid[0], hybrid[1])
+        s1.record()
+        torch.cuda.synchronize()
+        t_sel = s0.elapsed_time(s1) / 5
+        pp.set_policy(pol)
     census = pp.traversal(census=True)
     o_dtype = T.TM_BF16 if w.dtype == "bf16" else T.TM_F16
     for _ in range(warmup):
@@ -148,9 +161,10 @@ def prefill_config_line(name, steps=10, warmup=2, hybrid=None):
     ops, t_peak = prefill_roofline(w, census, t * 1e-3)
     desc = describe(w) if hybrid is None else describe(w).replace(
         "per-head diagonal-distance boundaries",
-        f"hybrid: {hybrid[0] * 100:.0f} % of keys per head selected (seeded), {hybrid[1]}-token window in FP16, "
-        f"the rest INT8")
+        f"hybrid: {hybrid[0] * 100:.0f} % of keys per head selected by the vertical-line pass (attention mass "
+        f"from the last 64 rows), {hybrid[1]}-token window in FP16, the rest INT8")
     res = {"workload": desc, "prefill_ms": t,
+           **({} if t_sel is None else {"selection_ms_incl_host": t_sel}),
            "effective_tflops_dense_causal": dense_causal_flops(w) / (t * 1e-3) / 1e12,
            "mfma_frac_precision_weighted": (ops / (t * 1e-3)) / (ops / t_peak),
            "census": census}

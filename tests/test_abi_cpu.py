@@ -385,6 +385,30 @@ def test_decode_selection_validation_and_size(B):
                        FAKE, 2, FAKE, ctypes.byref(ws), None) == B.TM_E_ARG
 
 
+def test_select_vertical_validation_and_size(B):
+    L = B.lib()
+    s = _shape(B, [1000, 130], hq=4, hkv=2, d=128)
+    n = ctypes.c_size_t(0)
+
+    def size(counts, n_obs=64, per_kv=0):
+        c = np.asarray(counts, np.int32)
+        return L.tm_select_vertical(ctypes.byref(s.c), None, None, n_obs,
+                                    c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), per_kv, None, None, None,
+                                    ctypes.byref(n), None)
+
+    assert size([50, 7]) == B.TM_OK
+    align = lambda v: (v + 255) // 256 * 256
+    tiles = 16 + 3
+    assert n.value == align(align(tiles * 4 * 128 * 4 + 2 * 4 * 128 * 4) + 4 * 3 * 2)
+    assert size([1001, 7]) == B.TM_E_POLICY        # more keys than the sequence has
+    assert size([-1, 7]) == B.TM_E_POLICY
+    assert size([5, 5], n_obs=0) == B.TM_E_POLICY
+    assert size([5, 5], n_obs=65) == B.TM_E_POLICY
+    assert size([5, 5], per_kv=2) == B.TM_E_POLICY
+    assert L.tm_select_vertical(ctypes.byref(s.c), None, None, 64, None, 0, None, None, None, ctypes.byref(n),
+                                None) == B.TM_E_ARG
+
+
 def test_growing_cache_validation(B):
     """Lengths of a growing cache are checked against the capacities before any
     GPU work: tm_decode through tm_dpolicy.lengths, tm_cache_append directly."""

@@ -24,10 +24,11 @@ namespace tmx {
 constexpr int kProbe = 64;   // most probe rows per sequence
 
 // Scores of probe rows x the 64 keys of tile j, for (sequence b, head h):
-// thread t takes row t / 4 and keys (t % 4) + 4i, i = 0..15.  Keys past the
-// row (causal) or the sequence end score -inf.
+// thread t takes rows 4 (t / 16) + u and keys (t % 16) + 16 i (u, i = 0..3),
+// s[4u + i]; per channel it reads 4 Q and 4 K values from LDS for 16 FMAs.
+// Keys past the row (causal) or the sequence end score -inf.
 template <int D>
-__device__ __forceinline__ void probe_scores(const SelectArgs& a, int b, int h, int j, float (&s)[16], int& row,
+__device__ __forceinline__ void probe_scores(const SelectArgs& a, int b, int h, int j, float (&s)[16], int& row0,
                                              int& nobs) {
   __shared__ float qs[kProbe][D + 1];
   __shared__ float ks[kBlock][D + 1];
@@ -55,22 +56,30 @@ __device__ __forceinline__ void probe_scores(const SelectArgs& a, int b, int h, 
     ks[r][c] = x;
   }
   __syncthreads();
-  const int rr = threadIdx.x >> 2, kc = threadIdx.x & 3;
-  row = rr;
+  const int rg = threadIdx.x >> 4, kc = threadIdx.x & 15;
+  row0 = 4 * rg;
   float acc[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
   for (int c = 0; c < D; ++c) {
-    const float qv = qs[rr][c];
+    float qv[4], kvv[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(qv, ks[kc + 4 * i][c], acc[i]);
+    for (int u = 0; u < 4; ++u) qv[u] = qs[row0 + u][c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kvv[i] = ks[kc + 16 * i][c];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[4 * u + i] = __builtin_fmaf(qv[u], kvv[i], acc[4 * u + i]);
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int key = j * kBlock + kc + 4 * i;
-    const bool ok = rr < nobs && key <= r0 + rr && key < len;
-    s[i] = ok ? acc[i] * a.tau_log2e : -INFINITY;
-  }
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = row0 + u, key = j * kBlock + kc + 16 * i;
+      const bool ok = rr < nobs && key <= r0 + rr && key < len;
+      s[4 * u + i] = ok ? acc[4 * u + i] * a.tau_log2e : -INFINITY;
+    }
 }
 
 // pass 1: per (row, tile) partial max and sum (log2 units)
@@ -80,24 +89,26 @@ __global__ __launch_bounds__(256) void probe_partial_kernel(SelectArgs a) {
   const int len = a.cu[b + 1] - a.cu[b];
   if (j * kBlock >= len) return;
   float s[16];
-  int row, nobs;
-  probe_scores<D>(a, b, h, j, s, row, nobs);
-  float m = -INFINITY;
+  int row0, nobs;
+  probe_scores<D>(a, b, h, j, s, row0, nobs);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m = fmaxf(m, s[i]);
-  m = fmaxf(m, __shfl_xor(m, 1, 64));
-  m = fmaxf(m, __shfl_xor(m, 2, 64));
-  float l = 0.0f;
-  if (m > -INFINITY) {
+  for (int u = 0; u < 4; ++u) {   // row row0 + u: its 64 keys sit in the 16 lanes of this key group
+    float m = fmaxf(fmaxf(s[4 * u], s[4 * u + 1]), fmaxf(s[4 * u + 2], s[4 * u + 3]));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(s[i] - m);
-  }
-  l += __shfl_xor(l, 1, 64);
-  l += __shfl_xor(l, 2, 64);
-  if ((threadIdx.x & 3) == 0 && row < nobs) {
-    float* dst = a.part + ((static_cast<size_t>(a.tile0[b]) + j) * a.hq + h) * (2 * kProbe) + 2 * row;
-    dst[0] = m;
-    dst[1] = l;
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float l = 0.0f;
+    if (m > -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l += __builtin_amdgcn_exp2f(s[4 * u + i] - m);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
+    const int row = row0 + u;
+    if ((threadIdx.x & 15) == 0 && row < nobs) {
+      float* dst = a.part + ((static_cast<size_t>(a.tile0[b]) + j) * a.hq + h) * (2 * kProbe) + 2 * row;
+      dst[0] = m;
+      dst[1] = l;
+    }
   }
 }
 
@@ -129,16 +140,22 @@ __global__ __launch_bounds__(256) void probe_mass_kernel(SelectArgs a) {
   __shared__ float mass[kBlock];
   if (threadIdx.x < kBlock) mass[threadIdx.x] = 0.0f;
   float s[16];
-  int row, nobs;
-  probe_scores<D>(a, b, h, j, s, row, nobs);   // (its barrier also orders the clear above)
-  if (row < nobs) {
-    const float* st = a.rows + (static_cast<size_t>(b) * a.hq + h) * (2 * kProbe) + 2 * row;
-    const float m = st[0], inv = 1.0f / st[1];
-    const int kc = threadIdx.x & 3;
+  int row0, nobs;
+  probe_scores<D>(a, b, h, j, s, row0, nobs);   // (its barrier also orders the clear above)
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};     // this thread's 4 keys, summed over its 4 rows
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (s[i] > -INFINITY) atomicAdd(&mass[kc + 4 * i], __builtin_amdgcn_exp2f(s[i] - m) * inv);
+  for (int u = 0; u < 4; ++u) {
+    if (row0 + u >= nobs) continue;
+    const float* st = a.rows + (static_cast<size_t>(b) * a.hq + h) * (2 * kProbe) + 2 * (row0 + u);
+    const float m = st[0], inv = 1.0f / st[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (s[4 * u + i] > -INFINITY) part[i] += __builtin_amdgcn_exp2f(s[4 * u + i] - m) * inv;
   }
+  const int kc = threadIdx.x & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (part[i] != 0.0f) atomicAdd(&mass[kc + 16 * i], part[i]);
   __syncthreads();
   const int c = threadIdx.x;
   if (c < kBlock && j * kBlock + c < len)
