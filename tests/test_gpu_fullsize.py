@@ -128,3 +128,87 @@ def test_decode16x32k_full():
         O = OA.decode([L], w.hq, w.hkv, w.d, dq[1][b:b + 1].astype(np.float64), kq, vq,
                       k[1][sl].astype(np.float64), v[1][sl].astype(np.float64), dpol)
         compare(o[b], O[0], what=f"decode16x32k seq {b}")
+
+
+def test_gqa8k_hybrid_full():
+    """The bench's hybrid line: 8K, 32/8 heads, keys selected on the GPU by the
+    vertical-line pass (5 % per head, 64 probe rows), 128-token window; the
+    selection checked against the oracle's masses on sampled heads, the
+    traversal census against the oracle's window classes, sampled rows
+    against the oracle prefill on the same lists."""
+    import math
+    import torch
+    import tile_routed_mixed_amd as T
+    w = W.get("gqa8k")
+    say("[gpu] full-size hybrid gqa8k: generating inputs")
+    q, k, v = W.make_qkv(w)
+    p = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, W.make_policy(w))
+    p.upload(q[0], k[0], v[0])
+    p.quantize()
+    pol = p.vertical_policy(0.05, 128)
+    S = w.seqlens[0]
+    grp = w.hq // w.hkv
+    for h in (0, 13, w.hq - 1):
+        imp = OP.vline_importance(q[1][:, h].astype(np.float64), k[1][:, h // grp].astype(np.float64), 64,
+                                  1 / math.sqrt(w.d))
+        sel = pol["sel_idx"][pol["sel_off"][h]:pol["sel_off"][h + 1]]
+        kk = int(round(0.05 * S))
+        assert len(sel) == kk and np.all(np.diff(sel) > 0)
+        kth = np.sort(imp)[::-1][kk - 1]
+        chosen = np.zeros(S, bool)
+        chosen[sel] = True
+        tol = 1e-5 + 1e-4 * kth
+        assert np.all(imp[chosen] >= kth - tol) and np.all(imp[~chosen] <= kth + tol), h
+    p.set_policy(pol)
+    census = p.traversal(census=True)
+    cls = OP.hybrid_tile_classes(S, w.bq, w.bk, 128)
+    n_full, n_edge, n_none = int((cls == OP.WIN_FULL).sum()), int((cls == OP.WIN_EDGE).sum()), \
+        int((cls == OP.WIN_NONE).sum())
+    assert census["int8"] == w.hq * (n_edge + n_none)
+    o32, _ = p.prefill(T.TM_F32)
+    torch.cuda.synchronize()
+    o32 = o32.cpu().numpy()
+    lse = p.lse.cpu().numpy()
+    rows = _sample_rows(w, 24)
+    need = set((s, r // 64) for s, h, r in rows)
+    qq = _sparse_q_codes(q[1], w.seqlens, need)
+    kq = OQ.quantize(k[1], w.seqlens)
+    say(f"[gpu] full-size hybrid gqa8k: oracle on {len(rows)} sampled rows")
+    O, L = OA.prefill(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.bk, pol, q[1].astype(np.float64),
+                      k[1].astype(np.float64), v[1].astype(np.float64), qq, kq, rows=rows)
+    ti = np.array([r for s, h, r in rows])
+    hi = np.array([h for s, h, r in rows])
+    compare(o32[ti, hi], O[ti, hi], lse[hi, ti], L[hi, ti], what="hybrid gqa8k fp32")
+
+
+def test_decode16x32k_selected_full():
+    """The bench's decode with 5 % of every (sequence, KV head)'s tokens
+    selected and read in FP16, on three sequences."""
+    import torch
+    import tile_routed_mixed_amd as T
+    w = W.get("decode16x32k")
+    dpol = W.make_decode_policy(w)
+    say("[gpu] full-size decode16x32k with selected tokens: generating inputs")
+    _, k, v = W.make_qkv(w)
+    dq = W.make_decode_query(w)
+    sel_off, sel_idx = W.make_decode_selection(w, 0.05)
+    p = T.DecodePipeline(w.seqlens, w.hq, w.hkv, w.d, dpol, dtype=w.dtype)
+    p.upload(dq[0], k[0], v[0])
+    p.build_cache()
+    p.select(sel_off, sel_idx)
+    o = p.decode()
+    torch.cuda.synchronize()
+    o = o.cpu().numpy()
+    cu = w.cu_seqlens
+    for b in (0, 9, 15):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        L = w.seqlens[b]
+        kq = OQ.quantize(k[1][sl], [L])
+        vq = OQ.quantize(v[1][sl], [L], layout="cols")
+        r0 = b * w.hkv
+        off = (sel_off[r0:r0 + w.hkv + 1] - sel_off[r0]).astype(np.int32)
+        idx = sel_idx[sel_off[r0]:sel_off[r0 + w.hkv]]
+        O = OA.decode([L], w.hq, w.hkv, w.d, dq[1][b:b + 1].astype(np.float64), kq, vq,
+                      k[1][sl].astype(np.float64), v[1][sl].astype(np.float64),
+                      dict(dpol, sel_off=off, sel_idx=idx))
+        compare(o[b], O[0], what=f"decode16x32k with selected tokens, seq {b}")
