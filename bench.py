@@ -112,9 +112,18 @@ def cpu_baseline(w, q, k, v, pol, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    cpu = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {len(items)} (sequence, head, query tile) items drawn with seed 12345, "
-                      f"{dt:.1f} s; attention rows only (codes precomputed); dense-causal FLOPs of those rows"}
+                      f"{dt:.1f} s; attention rows only (codes precomputed); dense-causal FLOPs of those rows; "
+                      f"{cpu}, os.cpu_count() = {os.cpu_count()}, BLAS threads = {int(threads)}"}
 
 
 def prefill_config_line(name, steps=10, warmup=2, hybrid=None):
@@ -228,7 +237,7 @@ def decode_block_counts(L, b8, b4, sink, tail):
     return c
 
 
-def decode_bench(steps, rotate=3, select_frac=None):
+def decode_bench(steps, rotate=3, select_frac=None, tags=None):
     """Decode over a 16 x 32768-token compressed cache; returns timing and bytes.
     select_frac: that fraction of every (sequence, KV head)'s tokens (seeded)
     is kept in FP16 as selected tokens."""
@@ -238,6 +247,8 @@ def decode_bench(steps, rotate=3, select_frac=None):
     import workloads as W
     w = W.get("decode16x32k")
     dpol = W.make_decode_policy(w)
+    if tags is not None:   # another reading of the cache tags: (b8, b4) in blocks
+        dpol = dict(dpol, b8=np.full(w.hkv, tags[0], np.int32), b4=np.full(w.hkv, tags[1], np.int32))
     _, k, v = W.make_qkv(w)
     dq = W.make_decode_query(w)
     caches = []
@@ -287,7 +298,9 @@ def decode_bench(steps, rotate=3, select_frac=None):
         ev[i][1].record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    desc = describe(w) + ", cache tags (b8, b4) = (128, 320) blocks, last 128 tokens FP16"
+    b8t, b4t = int(dpol["b8"][0]), int(dpol["b4"][0])
+    desc = describe(w) + f", cache tags (b8, b4) = ({b8t}, {b4t if b4t < 1 << 20 else 'never'}) blocks, " \
+                         f"last 128 tokens FP16"
     if select_frac is not None:
         desc += f", {select_frac * 100:g} % of tokens per (sequence, KV head) selected and read in FP16 ({n_sel} in all)"
     return {"workload": desc,
@@ -423,6 +436,12 @@ def main():
         ds = decode_bench(max(20, args.steps), select_frac=0.05)
         out["decode_selected"] = ds
         log(f"[bench] decode with 5 % selected tokens {ds['ms_mean']:.4f} ms, {ds['GBps']:.1f} GB/s")
+        out["decode_tag_variants"] = []
+        for tg in ((2, 5), (128, 1 << 30)):   # the literal toy bands; no skipped block
+            torch.cuda.empty_cache()
+            dv = decode_bench(max(20, args.steps), tags=tg)
+            out["decode_tag_variants"].append(dv)
+            log(f"[bench] decode tags {tg}: {dv['ms_mean']:.4f} ms, {dv['GBps']:.1f} GB/s")
         torch.cuda.empty_cache()
         dl = decode_loop_bench()
         out["decode_loop"] = dl
