@@ -18,14 +18,22 @@
  *     key tiles, FP16 or INT8 score paths sharing one online-softmax state,
  *     all legal groups routed, GQA, variable-length batches, INT8 K/V caches.
  *   [HyQuant] "HyQuant Uses Hybrid Precision to Compress LLM Attention",
- *     section "How HyQuant works": recent window kept FP16, the rest quantized,
- *     dequantization fused into decode attention.
+ *     sections "The observation behind the method" and "How HyQuant works":
+ *     selected (vertical-line) tokens and a recent window kept FP16, the rest
+ *     quantized, in prefill and in the decode cache, with dequantization
+ *     fused into decode attention.
+ * Policies: per-head boundaries, packed group bitmasks, the four-way
+ * combination of the two, and the token-granular hybrid policy (with a
+ * selection pass, tm_select_vertical).  Generation: tm_cache_append keeps a
+ * growing cache quantized as if built from scratch.
  *
  * Conventions common to every entry point.
  *  - Pointers named *_dev or documented as "device" are device memory owned by
  *    the caller (e.g. PyTorch tensors).  Pointers documented as "host" are host
- *    memory read during the call only.  The library allocates nothing, frees
- *    nothing and keeps no pointer after a call returns.
+ *    memory read during the call only.  The library allocates no device
+ *    memory, frees nothing and keeps no pointer after a call returns (calls
+ *    that stage small host tables copy them into caller buffers and
+ *    synchronize the stream before returning).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    is asynchronous: buffers must stay valid until the stream has finished.
  *    Calls on different streams are independent (the library has no mutable

@@ -7,6 +7,11 @@
 // [TileMix] "TileMix: Tile-Centric Mixed-Precision Attention for LLM Inference
 // Acceleration", abstract: FP16 or INT8 score tiles, both paths updating one
 // shared online-softmax state; grouped-query attention; variable lengths.
+// [HyQuant] "HyQuant Uses Hybrid Precision to Compress LLM Attention", section
+// "How HyQuant works": selected tokens and a sliding window in FP16, the rest
+// quantized (the hybrid kind: per-pair masks inside tiles, gathered tiles).
+// One specialization per policy kind: boundaries (INT8/INT4), bitmask
+// (FP16/INT8), four-way (all three) and hybrid (FP16/INT8 with masks).
 //
 // Design (gfx950, 64-wide waves):
 //  * one workgroup of 4 waves per work item (sequence, query head, query tile
