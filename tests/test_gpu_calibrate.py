@@ -25,7 +25,7 @@ def calib():
     w = W.small("gqa8k", [700, 300], hq=4, hkv=2)
     q, k, v = W.make_qkv(w)
     bits = (q[0], k[0], v[0])
-    cands = C.default_candidates(max(w.seqlens), w.bq)
+    cands = C.default_candidates(max(w.seqlens))
     say(f"[gpu] calibrate seqlens={w.seqlens} hq={w.hq} hkv={w.hkv} candidates={len(cands)}")
     pol, rep = C.calibrate(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, bits, cands, 0.5)
     return w, (q, k, v), cands, pol, rep

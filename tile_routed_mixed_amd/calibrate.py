@@ -47,7 +47,6 @@ class _Runner:
         self.pp = PrefillPipeline(seqlens, hq, hkv, d, bq, dtype, policy)
         self.pp.upload(*bits)
         self.pp.quantize()
-        self.hq = hq
 
     def run(self, policy, steps=0):
         """Prefill under `policy`; returns (output copy [T][hq][d] f32, census,
@@ -121,7 +120,7 @@ def head_errors(seqlens, hq, hkv, d, bq, dtype, bits, candidates, sink=0, runner
     return err, census
 
 
-def default_candidates(max_len, bq=128, bk=64):
+def default_candidates(max_len, bk=64):
     """Boundary pairs (b8, b4) in key-tile units: b8 from a doubling ladder,
     b4 >= b8 from the same ladder, plus "never" (2**30) for either; the pair
     (never, never) is the all-INT8 policy."""
@@ -233,7 +232,7 @@ def _main():
     line = {"workload": args.workload, "ns_per_tile": {"int8": costs[B.TM_INT8], "int4": costs[B.TM_INT4],
                                                         "fp16": costs[B.TM_FP16]}}
     if not args.costs_only:
-        cands = default_candidates(max(w.seqlens), w.bq)
+        cands = default_candidates(max(w.seqlens))
         pol, rep = calibrate(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, bits, cands, args.budget,
                              sink=int(w.sink), costs=costs)
         line.update(budget=args.budget, b8=pol["b8"], b4=pol["b4"], spent_frac=rep["spent_ns"] / rep["full_int8_ns"],
