@@ -322,7 +322,9 @@ tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, voi
  * from counts).  q [T][hq][d], k [T][hkv][d] 16-bit (device); counts host
  * [nseq], 0 <= counts[s] <= len_s; 1 <= n_obs <= 64.
  * ws: workspace; ws == NULL writes the size to *ws_bytes and returns TM_OK.
- * Synchronizes `stream` (small per-sequence tables are staged from the host).
+ * Up to 64 sequences the per-sequence table travels in the kernel arguments
+ * and the call does not wait; with more it is staged from the host into ws
+ * and the call synchronizes `stream`.
  * Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY (counts, n_obs), TM_E_SPACE,
  * TM_E_HIP. */
 tm_status tm_select_vertical(const tm_shape* shape, const void* q, const void* k, int32_t n_obs,

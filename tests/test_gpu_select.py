@@ -71,6 +71,8 @@ def _check(w, qkv, mass, off, idx, n_obs, counts, per_kv):
     ("gqa8k", [1000, 30, 2100], dict(hq=4, hkv=2), 64, 0.05, True),
     ("long128k", [700, 64], dict(hq=2, hkv=1, d=64), 17, 0.2, False),
     ("varlen32k", [129, 1], dict(hq=2, hkv=2), 64, 1.0, False),
+    # more sequences than the kernel arguments carry: the table is staged
+    ("varlen32k", [1 + (37 * i) % 150 for i in range(70)], dict(hq=2, hkv=1), 16, 0.1, True),
 ])
 def test_vertical_selection(name, seqlens, kw, n_obs, frac, per_kv):
     w = W.small(name, seqlens, **kw)

@@ -462,9 +462,17 @@ tm_status tm_select_vertical(const tm_shape* shape, const void* q, const void* k
   if (maxnt == 0) return TM_OK;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   uint8_t* w = static_cast<uint8_t*>(ws);
-  if (hipMemcpyAsync(w + tab_off, tab.data(), 4 * tab.size(), hipMemcpyHostToDevice, hs) != hipSuccess) return TM_E_HIP;
-  if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;
   SelectArgs a;
+  if (shape->nseq <= kSelInline) {
+    // small tables ride in the kernel arguments: no copy, no wait
+    a.tab = nullptr;
+    std::copy(tab.begin(), tab.end(), a.itab);
+  } else {
+    if (hipMemcpyAsync(w + tab_off, tab.data(), 4 * tab.size(), hipMemcpyHostToDevice, hs) != hipSuccess)
+      return TM_E_HIP;
+    if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;   // tab is freed on return
+    a.tab = reinterpret_cast<const int32_t*>(w + tab_off);
+  }
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.cu = shape->cu_seqlens_dev;
@@ -478,9 +486,6 @@ tm_status tm_select_vertical(const tm_shape* shape, const void* q, const void* k
   a.part = reinterpret_cast<float*>(w);
   a.rows = reinterpret_cast<float*>(w + part_b);
   a.mass = mass;
-  a.tile0 = reinterpret_cast<const int32_t*>(w + tab_off);
-  a.kcount = a.tile0 + shape->nseq;
-  a.sel_base = a.tile0 + 2 * shape->nseq;
   a.sel = sel_idx;
   return launch_select(a, shape->d, maxnt, hs) == hipSuccess ? TM_OK : TM_E_HIP;
 }

@@ -114,6 +114,7 @@ struct DecodeArgs {
   int32_t blk[kMaxSeqArg];      // their first cache block (absolute)
 };
 
+constexpr int kSelInline = 64;   // most sequences whose table travels in the kernel arguments
 struct SelectArgs {
   const uint16_t* q;        // [T][hq][D] 16-bit
   const uint16_t* k;        // [T][hkv][D] 16-bit
@@ -123,11 +124,17 @@ struct SelectArgs {
   float* part;              // [tiles][hq][64][2] partial (max, sum) per probe row
   float* rows;              // [nseq][hq][64][2] each probe row's (max, sum)
   float* mass;              // [T][hq] attention mass of each key
-  const int32_t* tile0;     // [nseq] first tile of each sequence (device, in the workspace)
-  const int32_t* kcount;    // [nseq] keys to select per list
-  const int32_t* sel_base;  // [nseq] first output entry of each sequence's lists
+  // per sequence: first tile, keys to select per list, first output entry of
+  // its lists; as tab[3][nseq] in the workspace, or (nseq <= kSelInline,
+  // tab == null) in itab, carried by the kernel arguments
+  const int32_t* tab;
   int32_t* sel;             // output positions, or null (mass only)
+  int32_t itab[3 * kSelInline];
 };
+
+__device__ __forceinline__ int sel_tab(const SelectArgs& a, int which, int b) {
+  return a.tab != nullptr ? a.tab[which * a.nseq + b] : a.itab[which * a.nseq + b];
+}
 
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st);
