@@ -399,6 +399,10 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     part = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
     t_quant, t_trav, t_pref, t_dec = part(0, 1), part(1, 2), part(2, 3), part(3, 4)
+    stages = (("quantize_qkv", 0, 1), ("traversal", 1, 2), ("prefill", 2, 3), ("decode", 3, 4))
+    per_step = {n: sorted(e[a].elapsed_time(e[b]) for e in evs) for n, a, b in stages}
+    k_median = {n: v[len(v) // 2] for n, v in per_step.items()}
+    k_min = {n: v[0] for n, v in per_step.items()}
     log(f"[bench] ms/step {ms_step:.4f}: quantize {t_quant:.4f} traversal {t_trav:.4f} "
         f"prefill {t_pref:.4f} decode {t_dec:.4f}")
 
@@ -423,6 +427,7 @@ def main():
            "mfma_util": achieved / peak,
            "prefill_kernel_ms": t_pref, "prefill_only_tflops": flops / (t_pref * 1e-3) / 1e12,
            "kernels_ms": {"quantize_qkv": t_quant, "traversal": t_trav, "prefill": t_pref, "decode": t_dec},
+           "kernels_ms_median": k_median, "kernels_ms_min": k_min,
            "census": census}
     if not args.no_decode_bench:
         del pp, dp

@@ -93,3 +93,13 @@ def test_selection_on_locality_inputs_drives_hybrid_prefill():
     _, _, o, lse, _ = run_prefill(w, pol, q, k, v)
     O, L, _, _ = oracle_prefill(w, pol, q, k, v)
     compare(o, O, lse, L, what="hybrid prefill on selected keys")
+
+
+def test_vertical_selection_full_size():
+    """The 8K x 32-head workload in the configuration the bench's hybrid line
+    times (64 probe rows, 5 % of the keys per query head): every key's mass
+    and every list against the oracle."""
+    w = W.get("gqa8k")
+    counts = [int(round(0.05 * S)) for S in w.seqlens]
+    qkv, mass, off, idx = _run(w, 64, counts, False)
+    _check(w, qkv, mass, off, idx, 64, counts, False)
