@@ -289,7 +289,6 @@ __global__ __launch_bounds__(1024) void topk_kernel(SelectArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int tok0 = a.cu[b], len = a.cu[b + 1] - a.cu[b];
   const int k = sel_tab(a, 1, b);
-  const int nlist = a.per_kv ? a.hkv : a.hq;
   int32_t* out = a.sel + sel_tab(a, 2, b) + static_cast<size_t>(g) * k;
   const int grp = a.hq / a.hkv;
   auto value = [&](int c) -> uint32_t {
@@ -302,7 +301,6 @@ __global__ __launch_bounds__(1024) void topk_kernel(SelectArgs a) {
     }
     return __float_as_uint(fmaxf(v, 0.0f));   // non-negative: the bits order as the values
   };
-  (void)nlist;
   if (k <= 0) return;
   constexpr int NT = kTopkThreads;
   const int lane = threadIdx.x & 63;
