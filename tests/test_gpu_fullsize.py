@@ -212,3 +212,30 @@ def test_decode16x32k_selected_full():
                       k[1][sl].astype(np.float64), v[1][sl].astype(np.float64),
                       dict(dpol, sel_off=off, sel_idx=idx))
         compare(o[b], O[0], what=f"decode16x32k with selected tokens, seq {b}")
+
+
+@pytest.mark.parametrize("name", ["gqa8k", "varlen32k"])
+def test_quantize_full_bitexact(name):
+    """Every code and scale of Q, K and V at full size (bf16 8K x 32/8 heads;
+    fp16 varlen 32K), bit for bit against the oracle's binary32 quantizer."""
+    import torch
+    import tile_routed_mixed_amd as T
+    w = W.get(name)
+    q, k, v = W.make_qkv(w)
+    p = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, W.make_policy(w))
+    p.upload(q[0], k[0], v[0])
+    say(f"[gpu] full-size quantize {name}")
+    p.quantize()
+    torch.cuda.synchronize()
+    for x, qt, layout in ((q, p.qq, "rows"), (k, p.kq, "rows"), (v, p.vq, "cols")):
+        ref = OQ.quantize(x[1], w.seqlens, layout=layout, with_t16=(layout == "cols"))
+
+        def hm(t):   # block-major on the GPU, head-major in the oracle
+            return np.swapaxes(t.cpu().numpy(), 0, 1)
+        assert np.array_equal(hm(qt.s8).view(np.uint32), ref["s8"].view(np.uint32)), (name, layout)
+        assert np.array_equal(hm(qt.s4).view(np.uint32), ref["s4"].view(np.uint32)), (name, layout)
+        assert np.array_equal(hm(qt.c8), ref["c8p"]), (name, layout, "c8")
+        assert np.array_equal(hm(qt.c4), ref["c4p"]), (name, layout, "c4")
+        if layout == "cols":
+            assert np.array_equal(hm(qt.t16).view(np.uint16), ref["t16"].view(np.uint16)), name
+        del ref

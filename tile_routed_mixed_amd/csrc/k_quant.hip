@@ -22,6 +22,22 @@ __device__ __forceinline__ int8_t quant_code(float x, float s, float qmax) {
   return static_cast<int8_t>(c);
 }
 
+// The same code from y = RN(1/s), with the IEEE division only near an edge.
+// q0 = RN(x y) is within |x/s| (2^-23 + 2^-48) of x/s.  When q0 lies more
+// than |q0| 2^-20 + 2^-22 inside the half-integer edges around c = rint(q0),
+// x/s lies farther than 2^-24 (|x/s| + 1) inside them, more than half an ulp
+// of either edge, so the IEEE quotient RN(x/s) stays strictly between the
+// edges and its code is c as well.  The caller passes base = 0.5 - 2^-22 and
+// y = RN(1/s) for s >= 2^-100 (normal, and the residual argument holds), else
+// base = -1, which sends every element to quant_code.
+__device__ __forceinline__ int8_t quant_code_recip(float x, float s, float y, float base, float qmax) {
+  const float q0 = x * y;
+  const float c = __builtin_rintf(q0);
+  const float t = __builtin_fmaf(-fabsf(q0), 0x1p-20f, base);
+  if (!(fabsf(q0 - c) <= t)) return quant_code(x, s, qmax);
+  return static_cast<int8_t>(fminf(fmaxf(c, -qmax), qmax));
+}
+
 // Quantize cache block b (global index) of head h: its first token is row
 // tok_first of x, and its first nvalid rows are valid (the rest count as 0).
 template <int D, bool BF16, bool COLS>
@@ -67,11 +83,14 @@ __device__ __forceinline__ void quant_block(const QuantArgs& a, int b, int h, si
     a.s4[blk] = sc4;
   }
 
+  const bool f8 = sc8 >= 0x1p-100f, f4 = sc4 >= 0x1p-100f;   // (false for a zero scale)
+  const float y8 = f8 ? __fdiv_rn(1.0f, sc8) : 0.0f, y4 = f4 ? __fdiv_rn(1.0f, sc4) : 0.0f;
+  const float base8 = f8 ? 0.5f - 0x1p-22f : -1.0f, base4 = f4 ? 0.5f - 0x1p-22f : -1.0f;
   int8_t c8v[EPT], c4v[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    c8v[e] = quant_code(xv[e], sc8, 127.0f);
-    c4v[e] = quant_code(xv[e], sc4, 7.0f);
+    c8v[e] = quant_code_recip(xv[e], sc8, y8, base8, 127.0f);
+    c4v[e] = quant_code_recip(xv[e], sc4, y4, base4, 7.0f);
   }
 
   if constexpr (!COLS) {
