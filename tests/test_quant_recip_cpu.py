@@ -6,7 +6,7 @@ RN(x / s) otherwise, equals rint(RN(x / s)) for every input.
 The kernel's steps are emulated in binary32 with numpy (products and
 quotients round to nearest even; the threshold's fused multiply-add is exact
 in float64 before its one rounding to float32), over every finite bf16 value
-of x and a spread of scales: the scales a block of amax values produces
+or fp16 value of x and a spread of scales: the scales a block of amax values produces
 (amax / 127 and amax / 7 in binary32), scales down to 2^-100, and random
 24-bit significands.  Where the fast path is taken its code must equal the
 one from IEEE division; the fallback must stay rare.
@@ -18,6 +18,12 @@ def _all_bf16():
     bits = np.arange(1 << 16, dtype=np.uint32) << 16
     x = bits.view(np.float32)
     return x[np.isfinite(x)]
+
+
+def _all_inputs():
+    """Every finite bf16 and fp16 value, widened exactly to binary32."""
+    h = np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float32)
+    return np.unique(np.concatenate([_all_bf16(), h[np.isfinite(h)]]))
 
 
 def _scales(rng):
@@ -47,7 +53,7 @@ def _codes(x, s, qmax):
 
 def test_reciprocal_codes_equal_ieee_codes():
     rng = np.random.default_rng(20)
-    xs = _all_bf16()
+    xs = _all_inputs()
     n = taken = 0
     for s in _scales(rng):
         for qmax in (127.0, 7.0):
