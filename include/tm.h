@@ -285,7 +285,9 @@ tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads,
  * trav == NULL: write the required size to *trav_bytes and return TM_OK
  * without touching the GPU.  Otherwise *trav_bytes is the capacity of `trav`
  * (device); TM_E_SPACE if too small.  census (host, may be NULL): when given,
- * the call synchronizes `stream` and fills it.
+ * the counts are also summed on the GPU (into the traversal's header) and the
+ * call synchronizes `stream` and fills it; without it the header's counts are
+ * left as they were.
  * Errors: TM_E_ARG (unknown kind, NULL arrays), TM_E_SHAPE, TM_E_POLICY
  * (b8 > b4, negative boundaries, b4 == 0 without sink, group < 1, n_words too
  * small; hybrid: window < 0, offsets not starting at 0 or decreasing, a list

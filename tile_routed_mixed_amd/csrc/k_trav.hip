@@ -319,12 +319,12 @@ hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_traversal(const TravArgs& a, hipStream_t st) {
+hipError_t launch_traversal(const TravArgs& a, bool census, hipStream_t st) {
   const unsigned n = max(a.n_items, static_cast<uint32_t>(a.nseq));
   const unsigned blocks = (n + 255) / 256;
   hipLaunchKernelGGL(trav_items_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !census) return e;
   hipLaunchKernelGGL(trav_census_kernel, dim3(1), dim3(256), 0, st, a.trav, a.item_off, a.n_items);
   return hipGetLastError();
 }

@@ -385,7 +385,7 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
       if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;
     }
   }
-  if (launch_traversal(a, hs) != hipSuccess) return TM_E_HIP;
+  if (launch_traversal(a, census != nullptr, hs) != hipSuccess) return TM_E_HIP;
   if (census != nullptr) {
     TravHeader h;
     if (hipMemcpyAsync(&h, trav, sizeof(h), hipMemcpyDeviceToHost, hs) != hipSuccess) return TM_E_HIP;

@@ -138,7 +138,7 @@ __device__ __forceinline__ int sel_tab(const SelectArgs& a, int which, int b) {
 
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st);
-hipError_t launch_traversal(const TravArgs& a, hipStream_t st);
+hipError_t launch_traversal(const TravArgs& a, bool census, hipStream_t st);   // census: also sum the counts into the header
 hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int d, int maxnt, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
