@@ -229,24 +229,34 @@ def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, vq: "QTensor", s
                                     ctypes.byref(vq.c), _stream(stream)), "tm_gather_selected")
 
 
-def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bool = False, stream=None):
+def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bool = False, stream=None,
+                       cache: Optional[dict] = None):
     """Attention mass of each key from the last n_obs query rows, and the
     counts[s] keys of largest mass per list.  Returns (mass [T][hq] float32
     device tensor, sel_off (host int32), sel_idx (host int32)): the index
     lists of a hybrid prefill policy (per query head) or of a decode selection
-    (per KV head)."""
+    (per KV head).  `cache` (a dict the caller keeps) holds the workspace and
+    output buffers between calls of the same sizes; a returned mass tensor is
+    then overwritten by the next call."""
     import torch
     cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
     cp = cnt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    n = ctypes.c_size_t(0)
-    _check(lib().tm_select_vertical(ctypes.byref(shape.c), None, None, int(n_obs), cp, int(per_kv_head), None, None,
-                                    None, ctypes.byref(n), None), "tm_select_vertical(size)")
-    dev = q.device
-    ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
-    mass = torch.empty((shape.T, shape.hq), dtype=torch.float32, device=dev)
     nl = shape.hkv if per_kv_head else shape.hq
     total = int(nl * cnt.astype(np.int64).sum())
-    sel = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    key = (int(n_obs), cnt.tobytes(), bool(per_kv_head), tuple(shape.seqlens), shape.hq, shape.hkv, shape.d)
+    if cache is not None and cache.get("key") == key:
+        ws, mass, sel, n = cache["ws"], cache["mass"], cache["sel"], ctypes.c_size_t(cache["ws_bytes"])
+    else:
+        n = ctypes.c_size_t(0)
+        _check(lib().tm_select_vertical(ctypes.byref(shape.c), None, None, int(n_obs), cp, int(per_kv_head), None,
+                                        None, None, ctypes.byref(n), None), "tm_select_vertical(size)")
+        dev = q.device
+        ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+        mass = torch.empty((shape.T, shape.hq), dtype=torch.float32, device=dev)
+        sel = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+        if cache is not None:
+            cache.clear()
+            cache.update(key=key, ws=ws, mass=mass, sel=sel, ws_bytes=int(n.value))
     _check(lib().tm_select_vertical(ctypes.byref(shape.c), _ptr(q), _ptr(k), int(n_obs), cp, int(per_kv_head),
                                     _ptr(mass), _ptr(sel), _ptr(ws), ctypes.byref(n), _stream(stream)),
            "tm_select_vertical")

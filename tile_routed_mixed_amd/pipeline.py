@@ -34,6 +34,7 @@ class PrefillPipeline:
         self.trav = torch.empty(B.traversal_bytes(self.shape, self.policy), dtype=torch.uint8, device=device)
         self.q = self.k = self.v = None
         self.o = None
+        self._sel_cache = {}
         self.lse = torch.empty((hq, self.shape.T), dtype=torch.float32, device=device)
 
     def set_policy(self, policy: dict):
@@ -50,7 +51,8 @@ class PrefillPipeline:
         the round(frac * len) keys of largest attention mass from the last
         n_obs query rows (tm_select_vertical over the uploaded Q and K)."""
         counts = [int(round(frac * S)) for S in self.shape.seqlens]
-        _, off, idx = B.tm_select_vertical(self.shape, self.q, self.k, n_obs, counts, False, stream)
+        _, off, idx = B.tm_select_vertical(self.shape, self.q, self.k, n_obs, counts, False, stream,
+                                           cache=self._sel_cache)
         return dict(kind=B.TM_POLICY_HYBRID, window=int(window), sel_off=off, sel_idx=idx)
 
     def upload(self, q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray):
