@@ -103,3 +103,20 @@ def test_vertical_selection_full_size():
     counts = [int(round(0.05 * S)) for S in w.seqlens]
     qkv, mass, off, idx = _run(w, 64, counts, False)
     _check(w, qkv, mass, off, idx, 64, counts, False)
+
+
+def test_pipeline_selection_buffers_follow_the_sizes():
+    """The pipeline keeps the selection buffers between calls: calls with
+    other counts (other buffer sizes) and back give the same lists as calls
+    on fresh buffers."""
+    import tile_routed_mixed_amd as T
+    w = W.small("local8k", [700, 300], hq=4, hkv=2)
+    q, k, v = W.make_qkv(w)
+    pp = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, W.make_policy(w))
+    pp.upload(q[0], k[0], v[0])
+    say("[gpu] pipeline selection buffer reuse")
+    got = [pp.vertical_policy(f, 64) for f in (0.05, 0.2, 0.05)]
+    for f, pol in zip((0.05, 0.2, 0.05), got):
+        counts = [int(round(f * S)) for S in w.seqlens]
+        _, off, idx = T.tm_select_vertical(pp.shape, pp.q, pp.k, 64, counts, False)
+        assert np.array_equal(pol["sel_off"], off) and np.array_equal(pol["sel_idx"], idx), f
