@@ -156,13 +156,23 @@ def int_tile_scores(qq, kq, seq, head, kv, qtile, ktile, bq, bk, prec, seqlens):
 
 def prefill_unquantized(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, tau=None,
                         rows=None, dense=False):
-    """Error reference (reported, not gated): the same attention with every
-    executed tile computed on the unquantized values; with ``dense`` set, plain
-    causal attention with nothing skipped."""
+    """Error reference, reported and never gated: softmax attention computed
+    on the unquantized 16-bit values ([TriAttention] abstract: the routed
+    attention keeps quality comparable to the original model; these figures
+    measure how far the quantized scores move the output on synthetic inputs).
+
+    dense=False: each row attends to the keys its policy executes (every key
+    c <= r whose tile is not SKIP), so the difference to ``prefill`` is the
+    quantization error alone.  dense=True: every key c <= r (plain causal
+    attention), which adds the error of the skipped tiles.  Bitmask and
+    hybrid policies skip nothing, so both readings coincide for them.
+    rows: iterable of (seq, head, row); None for every row.  Returns O
+    [T][hq][d] (NaN where not computed)."""
     tau = _tau(d, tau)
     grp = hq // hkv
     cu = np.concatenate([[0], np.cumsum(seqlens)])
-    gs = P.grids(seqlens, hq, bq, bk, pol)
+    skips = (not dense) and int(pol["kind"]) in (0, 2)
+    gs = P.grids(seqlens, hq, bq, bk, pol) if skips else None
     T = int(cu[-1])
     O = np.full((T, hq, d), np.nan)
     if rows is None:
@@ -172,12 +182,47 @@ def prefill_unquantized(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, tau=Non
         kv = h // grp
         keys = np.arange(r + 1)
         sc = tau * (k64[tok0 + keys, kv] @ q64[tok0 + r, h])
-        if not dense:
+        if skips:
             prec = gs[s][h][r // bq, keys // bk]
             sc = np.where(prec == P.SKIP, -np.inf, sc)
         m = np.max(sc)
         p = np.exp(sc - m)
         O[tok0 + r, h] = (p / p.sum()) @ v64[tok0 + keys, kv]
+    return O
+
+
+def decode_unquantized(seqlens, hq, hkv, d, q64, k64, v64, dpol, tau=None, dense=False, pairs=None):
+    """Decode error reference, reported and never gated: one-query softmax
+    attention over the unquantized 16-bit cache.  dense=False keeps the keys
+    the cache policy reads (keys of blocks not tagged SKIP, plus selected
+    tokens), dense=True every key of the cache.  Tags as in ``decode``.
+    Returns O [B][hq][d]; with ``pairs`` only those (b, h) are computed."""
+    tau = _tau(d, tau)
+    grp = hq // hkv
+    B = len(seqlens)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    O = np.zeros((B, hq, d))
+    for b in range(B):
+        L = int(seqlens[b])
+        for h in range(hq):
+            if pairs is not None and (b, h) not in pairs:
+                continue
+            kv = h // grp
+            keep = np.ones(L, bool)
+            if not dense:
+                mi = h if dpol.get("per_q_head", 0) else kv
+                tags = P.decode_block_tags(L, int(dpol["b8"][mi]), int(dpol["b4"][mi]), int(dpol["sink"]),
+                                           int(dpol["tail"]))
+                keep = np.repeat(tags != P.SKIP, BLOCK)[:L]
+                if "sel_off" in dpol:
+                    r = b * hkv + kv
+                    lst = dpol["sel_idx"][int(dpol["sel_off"][r]):int(dpol["sel_off"][r + 1])]
+                    keep[np.asarray(lst, np.int64)] = True
+            keys = np.nonzero(keep)[0]
+            sc = tau * (k64[cu[b] + keys, kv] @ q64[b, h])
+            m = np.max(sc)
+            p = np.exp(sc - m)
+            O[b, h] = (p / p.sum()) @ v64[cu[b] + keys, kv]
     return O
 
 

@@ -380,3 +380,106 @@ def test_decode_selected_tokens():
     pr = np.exp(sc - sc.max())
     pr /= pr.sum()
     assert np.max(np.abs(Os[1, 0] - pr @ np.array(vals))) < 1e-12
+
+
+# ---------------------------------------------------------------- error references
+
+def _band_mask(b8, b4, sink, hq):
+    """Executed keys of each row under per-head boundaries, written out from the
+    diagonal-distance reading for 128-row query tiles and 64-key tiles."""
+    def mask_fn(s, S):
+        r = np.arange(S)[:, None]
+        c = np.arange(S)[None, :]
+        m = np.zeros((hq, S, S), bool)
+        for h in range(hq):
+            dl = np.maximum(0, ((r // 128) * 128 - (c // 64) * 64) // 64)
+            keep = dl < b4[h]
+            if sink:
+                keep = keep | (c // 64 == 0)
+            m[h] = keep & (c <= r)
+        return m
+    return mask_fn
+
+
+def test_unquantized_dense_is_causal_attention():
+    """prefill_unquantized(dense=True) ignores the policy: plain causal softmax
+    attention on the 16-bit values (library routine, float64)."""
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 21, dtype="bf16", scale_k=10.0)
+    pol = dict(kind=0, b8=[1, 0, 2, 1], b4=[2, 1, 3, 2], sink=0)
+    f64 = lambda x: x.astype(np.float64)
+    O = A.prefill_unquantized(SEQ, HQ, HKV, D, 128, 64, pol, f64(q), f64(k), f64(v), dense=True)
+    assert np.max(np.abs(O - _sdpa(q, k, v, SEQ, HQ, HKV))) < 1e-12
+
+
+@pytest.mark.parametrize("sink", [0, 1])
+def test_unquantized_same_skip_is_band_masked_attention(sink):
+    """prefill_unquantized(dense=False) keeps exactly the keys whose tiles are
+    executed: attention on the 16-bit values under the band mask of the
+    boundaries (and the sink tile)."""
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 22)
+    b8, b4 = [1, 0, 2, 1], [2, 1, 3, 2]
+    pol = dict(kind=0, b8=b8, b4=b4, sink=sink)
+    f64 = lambda x: x.astype(np.float64)
+    O = A.prefill_unquantized(SEQ, HQ, HKV, D, 128, 64, pol, f64(q), f64(k), f64(v))
+    ref = _sdpa(q, k, v, SEQ, HQ, HKV, mask_fn=_band_mask(b8, b4, sink, HQ))
+    assert np.max(np.abs(O - ref)) < 1e-12
+    # and it differs from the dense reference (some tiles are skipped)
+    Od = A.prefill_unquantized(SEQ, HQ, HKV, D, 128, 64, pol, f64(q), f64(k), f64(v), dense=True)
+    assert np.max(np.abs(O - Od)) > 1e-3
+
+
+def test_unquantized_equals_quantized_oracle_on_all_fp16():
+    """With every tile FP16 and nothing skipped, the quantized oracle, the
+    same-skip reference and the dense reference are one computation."""
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 23)
+    qq, kq = _quant(q, k)
+    _, tot = P.bitmask_row_base(SEQ, HQ, 128, 64, 4)
+    pol = dict(kind=1, group=4, words=np.full(tot, 0xFFFFFFFF, np.uint32))
+    f64 = lambda x: x.astype(np.float64)
+    O, _ = A.prefill(SEQ, HQ, HKV, D, 128, 64, pol, f64(q), f64(k), f64(v), qq, kq)
+    Ou = A.prefill_unquantized(SEQ, HQ, HKV, D, 128, 64, pol, f64(q), f64(k), f64(v))
+    assert np.max(np.abs(O - Ou)) < 1e-12
+
+
+def test_decode_all_int4_is_dequantized_attention():
+    """Every cache block INT4 (b8 = 0, no sink, no FP16 window): one-query
+    attention on K-hat = s4 * c4 and V-hat = s4 * c4 (library routine)."""
+    q, k, v = _decode_inputs(18)
+    kq, vq = Q.quantize(k, DQ_SEQ), Q.quantize(v, DQ_SEQ, layout="cols")
+    dpol = dict(b8=[0, 0], b4=[10 ** 6] * 2, sink=0, tail=0)
+    O = A.decode(DQ_SEQ, HQ, HKV, D, q.astype(np.float64), kq, vq, k.astype(np.float64),
+                 v.astype(np.float64), dpol)
+    kh = Q.dequantize_rows(kq, 4, DQ_SEQ)
+    vh = Q.dequantize_rows(vq, 4, DQ_SEQ)
+    assert np.max(np.abs(O - _sdpa_one(q, kh, vh))) < 1e-12
+    # the INT8 reading of the same cache is a different computation
+    vh8 = Q.dequantize_rows(vq, 8, DQ_SEQ)
+    assert np.max(np.abs(O - _sdpa_one(q, Q.dequantize_rows(kq, 8, DQ_SEQ), vh8))) > 1e-3
+
+
+def test_decode_unquantized_references():
+    """decode_unquantized: dense = one-query attention over the whole cache;
+    same-skip = attention over the keys of the blocks the tags read, with the
+    block mask written out from the decode reading (last `tail` tokens FP16,
+    block 0 under a sink, distance floor((L-1)/64) - j below b4)."""
+    q, k, v = _decode_inputs(19)
+    f64 = lambda x: x.astype(np.float64)
+    dpol = dict(b8=[2, 3], b4=[4, 6], sink=1, tail=100)
+    Od = A.decode_unquantized(DQ_SEQ, HQ, HKV, D, f64(q), f64(k), f64(v), dpol, dense=True)
+    assert np.max(np.abs(Od - _sdpa_one(q, k, v))) < 1e-12
+    Os = A.decode_unquantized(DQ_SEQ, HQ, HKV, D, f64(q), f64(k), f64(v), dpol)
+    tok = 0
+    for b, L in enumerate(DQ_SEQ):
+        for h in range(HQ):
+            kv = h // 2
+            c = np.arange(L)
+            j = c // 64
+            blk_end = np.minimum(64 * j + 64, L)
+            keep = (blk_end > L - dpol["tail"]) | (j == 0) | ((L - 1) // 64 - j < dpol["b4"][kv])
+            qs = torch.from_numpy(q[b, h][None, None, :]).double()
+            ks = torch.from_numpy(np.ascontiguousarray(k[tok:tok + L, kv][keep]))[None].double()
+            vs = torch.from_numpy(np.ascontiguousarray(v[tok:tok + L, kv][keep]))[None].double()
+            ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs)[0, 0].numpy()
+            assert np.max(np.abs(Os[b, h] - ref)) < 1e-12, (b, h)
+        tok += L
+    assert np.max(np.abs(Os - Od)) > 1e-4
