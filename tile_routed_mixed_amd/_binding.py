@@ -262,6 +262,8 @@ def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bo
            "tm_select_vertical")
     per_list = np.repeat(cnt, nl)
     sel_off = np.concatenate([[0], np.cumsum(per_list)]).astype(np.int32)
+    if stream is not None:   # the copy below runs on the current stream: order it after the kernels
+        torch.cuda.current_stream().wait_stream(stream)
     return mass, sel_off, sel[:total].cpu().numpy().astype(np.int32)
 
 
@@ -341,6 +343,10 @@ class DPolicy:
         self.sel_idx = np.ascontiguousarray(np.asarray(sel_idx, dtype=np.int32))
         self.c.sel_off = self.sel_off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         self.c.sel_idx = self.sel_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        # the device buffer was built for other lists: tm_decode refuses to run
+        # (TM_E_ARG) until tm_decode_select has filled one for these
+        self.sel_buf = None
+        self.c.sel_buf = None
 
 
 def decode_sel_bytes(shape: "Shape", dpol: "DPolicy") -> int:

@@ -103,7 +103,6 @@ __device__ inline SeqOfBlock find_block_seq(const int32_t* __restrict__ cu, int 
   return r;
 }
 
-// Block start of sequence `seq` (sum of ceil(len/64) over earlier sequences).
 // s_waitcnt vmcnt(n) with the other counters left alone (n <= 15).
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
@@ -174,6 +173,7 @@ __device__ __forceinline__ uint64_t sload64(const uint64_t* p, size_t i) {
   return ((cu64*)(p))[i];
 }
 
+// Block start of sequence `seq` (sum of ceil(len/64) over earlier sequences).
 __device__ inline int seq_blk_start(const int32_t* __restrict__ cu, int seq) {
   const int lane = threadIdx.x & 63;
   int acc = 0;

@@ -154,13 +154,19 @@ class DecodePipeline:
         import torch
         L = self.dpol.lengths.copy()
         cu = self.shape.cu_host
+        cap = cu[1:] - cu[:-1]
+        full = np.nonzero(L >= cap)[0]
+        if full.size:
+            raise ValueError(f"append: sequences {full.tolist()} are at their capacity {cap[full].tolist()}")
         rows = torch.as_tensor((cu[:-1] + L).astype(np.int64), device=self.device)
-        self.k[rows] = _dev_bits(k_bits, self.device)
-        self.v[rows] = _dev_bits(v_bits, self.device)
+        # the row writes run on `stream` too, so tm_cache_append sees them
+        with torch.cuda.stream(stream):   # (None: the current stream)
+            self.k[rows] = _dev_bits(k_bits, self.device)
+            self.v[rows] = _dev_bits(v_bits, self.device)
         L += 1
-        self.dpol.set_lengths(L)
         B.tm_cache_append(self.shape, L, self.k, self.kq, stream)
         B.tm_cache_append(self.shape, L, self.v, self.vq, stream)
+        self.dpol.set_lengths(L)   # only once both appends were accepted
         if q_bits is not None:
             self.q = _dev_bits(q_bits, self.device)
 
