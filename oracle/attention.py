@@ -66,7 +66,7 @@ def _rows_scores(r0, r1, h, kv, tok0, grid_h, bq, bk, q64, k64, qq, kq, blk0, ta
 
 
 def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
-            rows=None, return_p=False, qtiles=None):
+            rows=None, return_p=False, qtiles=None, compact=False):
     """Oracle prefill output.
 
     q64 [T][hq][d], k64/v64 [T][hkv][d]: float64 copies of the 16-bit inputs.
@@ -75,13 +75,16 @@ def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
     qtiles: alternatively, an iterable of (seq, head, query tile) triples whose
     rows are computed (used to time a bounded sample of a workload).
     Returns (O, lse) with O [T][hq][d] and lse [hq][T] (NaN where not computed),
-    plus the list of probability rows when return_p is set.
+    plus the list of probability rows when return_p is set.  With ``compact``
+    nothing of size T is allocated: the result is a list of
+    ((seq, head, r0, r1), O rows [r1 - r0][d], lse rows [r1 - r0]).
     """
     tau = _tau(d, tau)
     T = int(np.sum(seqlens))
     grp = hq // hkv
-    O = np.full((T, hq, d), np.nan)
-    lse = np.full((hq, T), np.nan)
+    O = None if compact else np.full((T, hq, d), np.nan)
+    lse = None if compact else np.full((hq, T), np.nan)
+    blocks = []
     hyb = int(pol["kind"]) == 3
     gs = None if hyb else P.grids(seqlens, hq, bq, bk, pol)
     cu = np.concatenate([[0], np.cumsum(seqlens)])
@@ -115,10 +118,16 @@ def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
             assert np.all(np.isfinite(m)), "a row with no executed key"
             p = np.exp(Sc - m[:, None])
             l = np.sum(p, axis=1)
-            O[tok0 + r0:tok0 + r1, h] = (p / l[:, None]) @ v64[tok0:tok0 + r1, kv]
-            lse[h, tok0 + r0:tok0 + r1] = m + np.log(l)
+            ob = (p / l[:, None]) @ v64[tok0:tok0 + r1, kv]
+            if compact:
+                blocks.append(((s, h, r0, r1), ob, m + np.log(l)))
+            else:
+                O[tok0 + r0:tok0 + r1, h] = ob
+                lse[h, tok0 + r0:tok0 + r1] = m + np.log(l)
             if return_p:
                 plist.append(((s, h, r0, r1), p / l[:, None]))
+    if compact:
+        return blocks
     if return_p:
         return O, lse, plist
     return O, lse
@@ -155,7 +164,7 @@ def int_tile_scores(qq, kq, seq, head, kv, qtile, ktile, bq, bk, prec, seqlens):
 
 
 def prefill_unquantized(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, tau=None,
-                        rows=None, dense=False):
+                        rows=None, dense=False, compact=False):
     """Error reference, reported and never gated: softmax attention computed
     on the unquantized 16-bit values ([TriAttention] abstract: the routed
     attention keeps quality comparable to the original model; these figures
@@ -166,28 +175,36 @@ def prefill_unquantized(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, tau=Non
     quantization error alone.  dense=True: every key c <= r (plain causal
     attention), which adds the error of the skipped tiles.  Bitmask and
     hybrid policies skip nothing, so both readings coincide for them.
-    rows: iterable of (seq, head, row); None for every row.  Returns O
-    [T][hq][d] (NaN where not computed)."""
+    rows: iterable of (seq, head, row); None for every row.  q64, k64, v64
+    may be float32 copies of the 16-bit values (they are widened exactly, row
+    by row).  Returns O [T][hq][d] (NaN where not computed), or with
+    ``compact`` the listed rows only, [len(rows)][d] in their order."""
     tau = _tau(d, tau)
     grp = hq // hkv
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     skips = (not dense) and int(pol["kind"]) in (0, 2)
     gs = P.grids(seqlens, hq, bq, bk, pol) if skips else None
     T = int(cu[-1])
-    O = np.full((T, hq, d), np.nan)
     if rows is None:
         rows = [(s, h, r) for s in range(len(seqlens)) for h in range(hq) for r in range(int(seqlens[s]))]
-    for s, h, r in rows:
+    rows = list(rows)
+    O = np.full((len(rows), d) if compact else (T, hq, d), np.nan)
+    for n, (s, h, r) in enumerate(rows):
         tok0 = int(cu[s])
         kv = h // grp
         keys = np.arange(r + 1)
-        sc = tau * (k64[tok0 + keys, kv] @ q64[tok0 + r, h])
+        kk = np.asarray(k64[tok0 + keys, kv], np.float64)
+        sc = tau * (kk @ np.asarray(q64[tok0 + r, h], np.float64))
         if skips:
             prec = gs[s][h][r // bq, keys // bk]
             sc = np.where(prec == P.SKIP, -np.inf, sc)
         m = np.max(sc)
         p = np.exp(sc - m)
-        O[tok0 + r, h] = (p / p.sum()) @ v64[tok0 + keys, kv]
+        o = (p / p.sum()) @ np.asarray(v64[tok0 + keys, kv], np.float64)
+        if compact:
+            O[n] = o
+        else:
+            O[tok0 + r, h] = o
     return O
 
 
@@ -219,10 +236,10 @@ def decode_unquantized(seqlens, hq, hkv, d, q64, k64, v64, dpol, tau=None, dense
                     lst = dpol["sel_idx"][int(dpol["sel_off"][r]):int(dpol["sel_off"][r + 1])]
                     keep[np.asarray(lst, np.int64)] = True
             keys = np.nonzero(keep)[0]
-            sc = tau * (k64[cu[b] + keys, kv] @ q64[b, h])
+            sc = tau * (np.asarray(k64[cu[b] + keys, kv], np.float64) @ np.asarray(q64[b, h], np.float64))
             m = np.max(sc)
             p = np.exp(sc - m)
-            O[b, h] = (p / p.sum()) @ v64[cu[b] + keys, kv]
+            O[b, h] = (p / p.sum()) @ np.asarray(v64[cu[b] + keys, kv], np.float64)
     return O
 
 

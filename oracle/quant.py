@@ -137,3 +137,22 @@ def dequantize_rows(qt: dict, bits: int, seqlens) -> np.ndarray:
         blk = c[:, b0:b0 + nb].astype(np.float64) * s[:, b0:b0 + nb, None, None].astype(np.float64)
         outs.append(blk.transpose(1, 2, 0, 3).reshape(nb * BLOCK, H, d)[:int(S)])
     return np.concatenate(outs, axis=0)
+
+
+def quantize_blocks(x: np.ndarray, seqlens, blocks):
+    """Rows-layout codes for the listed (sequence, block) pairs only, zero
+    elsewhere: each 64-token block is quantized on its own (blocks are
+    independent, so this equals the listed blocks of ``quantize``)."""
+    starts, nblk = block_starts(seqlens)
+    T, H, d = x.shape
+    out = dict(c8=np.zeros((H, nblk, BLOCK, d), np.int8), c4=np.zeros((H, nblk, BLOCK, d), np.int8),
+               s8=np.zeros((H, nblk), np.float32), s4=np.zeros((H, nblk), np.float32), blk_start=starts, nblk=nblk)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    for s, b in sorted(blocks):
+        t0 = int(cu[s]) + BLOCK * b
+        t1 = min(t0 + BLOCK, int(cu[s + 1]))
+        blk = quantize(x[t0:t1], [t1 - t0])
+        g = int(starts[s]) + b
+        for key in ("c8", "c4", "s8", "s4"):
+            out[key][:, g] = blk[key][:, 0]
+    return out

@@ -16,7 +16,8 @@ from oracle import attention as OA
 from oracle import policy as OP
 from oracle import quant as OQ
 
-from _gpu_helpers import TOL_MAX, check_int_scores, compare, int_tiles, run_prefill, say
+from _gpu_helpers import (TOL_MAX, assert_all_written, check_int_scores, compare, guard_decode, guard_prefill,
+                          int_tiles, run_prefill, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,9 +69,15 @@ def _full_prefill(name, n_random=24, n_tiles=8):
     c = OP.census(OP.grids(w.seqlens, w.hq, w.bq, w.bk, pol))
     assert {kk: census[kk] for kk in c} == c
     o16_dtype = T.TM_BF16 if w.dtype == "bf16" else T.TM_F16
-    o16, _ = p.prefill(o16_dtype)
     import torch
+    p.o = p.guards.alloc((w.total_tokens, w.hq, w.d), torch.bfloat16 if w.dtype == "bf16" else torch.float16,
+                         float("nan"))
+    p.o_dtype = o16_dtype
+    p.guards.poison()
+    o16, _ = p.prefill(o16_dtype)
     torch.cuda.synchronize()
+    p.guards.check()
+    assert_all_written(o16, f"{name} 16-bit O")
     o16 = o16.float().cpu().numpy()
     rows = _sample_rows(w, n_random)
     need = set((s, r // 64) for s, h, r in rows)
@@ -115,9 +122,12 @@ def test_decode16x32k_full():
     dq = W.make_decode_query(w)
     p = T.DecodePipeline(w.seqlens, w.hq, w.hkv, w.d, dpol, dtype=w.dtype)
     p.upload(dq[0], k[0], v[0])
+    g = guard_decode(p)
     p.build_cache()
     o = p.decode()
     torch.cuda.synchronize()
+    g.check()
+    assert_all_written(o, "decode16x32k O")
     o = o.cpu().numpy()
     cu = w.cu_seqlens
     for b in (0, 7, 15):
@@ -144,6 +154,7 @@ def test_gqa8k_hybrid_full():
     q, k, v = W.make_qkv(w)
     p = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, W.make_policy(w))
     p.upload(q[0], k[0], v[0])
+    g = guard_prefill(p, T.TM_F32)
     p.quantize()
     pol = p.vertical_policy(0.05, 128)
     S = w.seqlens[0]
@@ -167,6 +178,8 @@ def test_gqa8k_hybrid_full():
     assert census["int8"] == w.hq * (n_edge + n_none)
     o32, _ = p.prefill(T.TM_F32)
     torch.cuda.synchronize()
+    g.check()
+    assert_all_written(o32, "hybrid O")
     o32 = o32.cpu().numpy()
     lse = p.lse.cpu().numpy()
     rows = _sample_rows(w, 24)
@@ -194,10 +207,13 @@ def test_decode16x32k_selected_full():
     sel_off, sel_idx = W.make_decode_selection(w, 0.05)
     p = T.DecodePipeline(w.seqlens, w.hq, w.hkv, w.d, dpol, dtype=w.dtype)
     p.upload(dq[0], k[0], v[0])
+    g = guard_decode(p)
     p.build_cache()
     p.select(sel_off, sel_idx)
     o = p.decode()
     torch.cuda.synchronize()
+    g.check()
+    assert_all_written(o, "decode16x32k O with selected tokens")
     o = o.cpu().numpy()
     cu = w.cu_seqlens
     for b in (0, 9, 15):
@@ -214,28 +230,70 @@ def test_decode16x32k_selected_full():
         compare(o[b], O[0], what=f"decode16x32k with selected tokens, seq {b}")
 
 
-@pytest.mark.parametrize("name", ["gqa8k", "varlen32k"])
+def _check_codes_chunked(x16, seqlens, qt, layout, what, chunk=16384):
+    """Every code, scale (and fp16 copy) of a block-major device QTensor
+    against the oracle's binary32 quantizer, a chunk of whole 64-token blocks
+    at a time (blocks are independent, so quantizing a chunk on its own gives
+    the oracle's codes for those blocks)."""
+    starts, _ = OQ.block_starts(seqlens)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    n = 0
+    for s, S in enumerate(seqlens):
+        for t0 in range(0, S, chunk):
+            t1 = min(S, t0 + chunk)
+            ref = OQ.quantize(x16[cu[s] + t0:cu[s] + t1], [t1 - t0], layout=layout, with_t16=(layout == "cols"))
+            b0 = int(starts[s]) + t0 // 64
+            b1 = b0 + -(-(t1 - t0) // 64)
+
+            def hm(t):   # block-major on the GPU, head-major in the oracle
+                return np.swapaxes(t[b0:b1].cpu().numpy(), 0, 1)
+            assert np.array_equal(hm(qt.s8).view(np.uint32), ref["s8"].view(np.uint32)), (what, s, t0, "s8")
+            assert np.array_equal(hm(qt.s4).view(np.uint32), ref["s4"].view(np.uint32)), (what, s, t0, "s4")
+            assert np.array_equal(hm(qt.c8), ref["c8p"]), (what, s, t0, "c8")
+            assert np.array_equal(hm(qt.c4), ref["c4p"]), (what, s, t0, "c4")
+            if layout == "cols":
+                assert np.array_equal(hm(qt.t16).view(np.uint16), ref["t16"].view(np.uint16)), (what, s, t0)
+            n += t1 - t0
+    assert n == sum(seqlens)
+
+
+@pytest.mark.parametrize("name", ["gqa8k", "varlen32k", "long128k"])
 def test_quantize_full_bitexact(name):
     """Every code and scale of Q, K and V at full size (bf16 8K x 32/8 heads;
-    fp16 varlen 32K), bit for bit against the oracle's binary32 quantizer."""
+    fp16 varlen 32K; bf16 128K x 32/8 heads with outlier channels), bit for
+    bit against the oracle's binary32 quantizer."""
     import torch
     import tile_routed_mixed_amd as T
     w = W.get(name)
+    say(f"[gpu] full-size quantize {name}: generating inputs")
     q, k, v = W.make_qkv(w)
     p = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, W.make_policy(w))
     p.upload(q[0], k[0], v[0])
+    g = guard_prefill(p, T.TM_F32)
     say(f"[gpu] full-size quantize {name}")
     p.quantize()
     torch.cuda.synchronize()
-    for x, qt, layout in ((q, p.qq, "rows"), (k, p.kq, "rows"), (v, p.vq, "cols")):
-        ref = OQ.quantize(x[1], w.seqlens, layout=layout, with_t16=(layout == "cols"))
+    g.check()
+    for x, qt, layout, what in ((q, p.qq, "rows", "Q"), (k, p.kq, "rows", "K"), (v, p.vq, "cols", "V")):
+        say(f"[gpu] full-size quantize {name}: checking {what}")
+        _check_codes_chunked(x[1], w.seqlens, qt, layout, f"{name} {what}")
 
-        def hm(t):   # block-major on the GPU, head-major in the oracle
-            return np.swapaxes(t.cpu().numpy(), 0, 1)
-        assert np.array_equal(hm(qt.s8).view(np.uint32), ref["s8"].view(np.uint32)), (name, layout)
-        assert np.array_equal(hm(qt.s4).view(np.uint32), ref["s4"].view(np.uint32)), (name, layout)
-        assert np.array_equal(hm(qt.c8), ref["c8p"]), (name, layout, "c8")
-        assert np.array_equal(hm(qt.c4), ref["c4p"]), (name, layout, "c4")
-        if layout == "cols":
-            assert np.array_equal(hm(qt.t16).view(np.uint16), ref["t16"].view(np.uint16)), name
-        del ref
+
+def test_decode_cache_full_bitexact():
+    """The 16 x 32768-token decode cache: every K (rows) and V (transposed,
+    with its fp16 copy) code and scale bit for bit against the oracle."""
+    import torch
+    import tile_routed_mixed_amd as T
+    w = W.get("decode16x32k")
+    say("[gpu] full-size decode cache: generating inputs")
+    _, k, v = W.make_qkv(w)
+    dq = W.make_decode_query(w)
+    p = T.DecodePipeline(w.seqlens, w.hq, w.hkv, w.d, W.make_decode_policy(w), dtype=w.dtype)
+    p.upload(dq[0], k[0], v[0])
+    g = guard_decode(p)
+    p.build_cache()
+    torch.cuda.synchronize()
+    g.check()
+    for x, qt, layout, what in ((k, p.kq, "rows", "K"), (v, p.vq, "cols", "V")):
+        say(f"[gpu] full-size decode cache: checking {what}")
+        _check_codes_chunked(x[1], w.seqlens, qt, layout, f"decode16x32k {what}")

@@ -16,7 +16,8 @@ from oracle import attention as OA
 from oracle import policy as OP
 from oracle import quant as OQ
 
-from _gpu_helpers import (TOL_LSE, TOL_MAX, check_int_scores, compare, int_tiles, oracle_prefill, run_prefill, say)
+from _gpu_helpers import (TOL_LSE, TOL_MAX, assert_all_written, check_int_scores, compare, guard_decode,
+                          guard_prefill, int_tiles, oracle_prefill, run_prefill, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,9 +45,11 @@ def test_quantize_bitexact(dtype, d, seqlens):
     q, k, v = _inputs(w)
     p = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, dict(kind=0, b8=[1] * 4, b4=[2] * 4, sink=0))
     p.upload(q[0], k[0], v[0])
+    g = guard_prefill(p, T.TM_F32)
     say(f"[gpu] quantize {dtype} d={d} {seqlens}")
     p.quantize()
     torch.cuda.synchronize()
+    g.check()
     for x, qt, layout in ((q, p.qq, "rows"), (k, p.kq, "rows"), (v, p.vq, "cols")):
         ref = OQ.quantize(x[1], w.seqlens, layout=layout, with_t16=(layout == "cols"))
         # the library stores blocks block-major ([nblk][heads]...), the oracle head-major
@@ -400,6 +403,15 @@ def test_deterministic():
 
 # ---------------------------------------------------------------------------- decode (small)
 
+def _with_sel(dp, sel):
+    """A copy of a binding DPolicy carrying the lists `sel` (for size queries)."""
+    import copy
+    d = copy.copy(dp)
+    d.c = type(dp.c).from_buffer_copy(dp.c)
+    d.set_selection(*sel)
+    return d
+
+
 def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, dtype="f16", sel=None):
     """sel: (sel_off, sel_idx) selected tokens per (sequence, KV head), or None."""
     import torch
@@ -411,12 +423,17 @@ def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, dtype="f16", sel=None):
         f"{'' if sel is None else str(len(sel[1])) + ' selected'}")
     p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol, dtype=dtype)
     p.upload(dq[0], k[0], v[0])
+    g = guard_decode(p)
     p.build_cache()
     if sel is not None:
+        p.sel_buf = g.alloc((max(256, T._binding.decode_sel_bytes(p.shape, _with_sel(p.dpol, sel))),), torch.uint8,
+                            0xFF, role="sel")
         p.select(*sel)
         dpol = dict(dpol, sel_off=sel[0], sel_idx=sel[1])
     o = p.decode()
     torch.cuda.synchronize()
+    g.check()
+    assert_all_written(o, "decode O")
     kq = OQ.quantize(k[1], w.seqlens)
     vq = OQ.quantize(v[1], w.seqlens, layout="cols")
     O = OA.decode(w.seqlens, hq, hkv, d, dq[1].astype(np.float64), kq, vq, k[1].astype(np.float64),
@@ -477,13 +494,17 @@ def test_decode_selected_tokens_growing_cache():
     say(f"[gpu] decode growing cache with {len(sel[1])} selected tokens")
     p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol)
     p.upload(dq[0], k[0], v[0])
+    g = guard_decode(p)
     p.start(start)
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     L = start.copy()
     for step in range(3):
         p.select(*sel)
+        g.poison()
         o = p.decode()
         torch.cuda.synchronize()
+        g.check()
+        assert_all_written(o, "decode O")
         rows = np.concatenate([np.arange(cu[s_], cu[s_] + L[s_]) for s_ in range(len(seqlens))])
         kq = OQ.quantize(k[1][rows], list(L))
         vq = OQ.quantize(v[1][rows], list(L), layout="cols")
@@ -539,11 +560,16 @@ def test_decode_deterministic_long_splits(d):
     say(f"[gpu] decode determinism {seqlens} d={d} {dpol}")
     p = T.DecodePipeline(w.seqlens, 8, 2, d, dpol, dtype="f16")
     p.upload(dq[0], k[0], v[0])
+    g = guard_decode(p)
     p.build_cache()
     outs = []
     for _ in range(3):
+        g.poison()
+        g.poison("ws")
         o = p.decode()
         torch.cuda.synchronize()
+        g.check()
+        assert_all_written(o, "decode O")
         outs.append(o.cpu().numpy().copy())
     assert all(np.array_equal(outs[0], x) for x in outs[1:])
     kq = OQ.quantize(k[1], w.seqlens)
@@ -572,12 +598,16 @@ def test_decode_growing_cache_matches_rebuilt_oracle():
     say(f"[gpu] growing cache {caps} from {L0.tolist()}, {steps} steps")
     p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol, dtype="f16")
     p.upload(queries[0][0], k[0], v[0])
+    g = guard_decode(p)
     p.start(L0)
     for step in range(steps + 1):
         L = L0 + step
         if step % 20 == 0:
+            g.poison()
             o = p.decode()
             torch.cuda.synchronize()
+            g.check()
+            assert_all_written(o, "decode O")
             o = o.cpu().numpy()
             for b in range(2):
                 sl = slice(int(cu[b]), int(cu[b]) + int(L[b]))

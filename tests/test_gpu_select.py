@@ -16,7 +16,7 @@ import pytest
 import workloads as W
 from oracle import policy as OP
 
-from _gpu_helpers import compare, oracle_prefill, run_prefill, say
+from _gpu_helpers import Guards, assert_all_written, compare, oracle_prefill, run_prefill, say
 
 pytestmark = pytest.mark.gpu
 
@@ -30,8 +30,15 @@ def _run(w, n_obs, counts, per_kv):
     dq = torch.from_numpy(q[0].view(np.int16).copy()).to("cuda:0")
     dk = torch.from_numpy(k[0].view(np.int16).copy()).to("cuda:0")
     say(f"[gpu] select seqlens={w.seqlens} hq={w.hq} hkv={w.hkv} d={w.d} n_obs={n_obs} counts={counts} per_kv={per_kv}")
-    mass, off, idx = T.tm_select_vertical(shape, dq, dk, n_obs, counts, per_kv)
+    g = Guards()
+    nl = w.hkv if per_kv else w.hq
+    total = nl * int(np.sum(counts))
+    mass_out = g.alloc((shape.T, w.hq), torch.float32, float("nan"))
+    sel_out = g.alloc((max(total, 1),), torch.int32, -1)
+    mass, off, idx = T.tm_select_vertical(shape, dq, dk, n_obs, counts, per_kv, mass_out=mass_out, sel_out=sel_out)
     torch.cuda.synchronize()
+    g.check()
+    assert_all_written(mass, "key masses")
     return (q, k, v), mass.cpu().numpy(), off, idx
 
 

@@ -483,3 +483,14 @@ def test_decode_unquantized_references():
             assert np.max(np.abs(Os[b, h] - ref)) < 1e-12, (b, h)
         tok += L
     assert np.max(np.abs(Os - Od)) > 1e-4
+
+
+def test_unquantized_compact_rows_match_full():
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 24)
+    pol = dict(kind=0, b8=[1, 0, 2, 1], b4=[2, 1, 3, 2], sink=1)
+    rows = [(2, 3, 299), (0, 0, 0), (1, 2, 76), (2, 1, 130)]
+    full = A.prefill_unquantized(SEQ, HQ, HKV, D, 128, 64, pol, q, k, v)
+    comp = A.prefill_unquantized(SEQ, HQ, HKV, D, 128, 64, pol, q, k, v, rows=rows, compact=True)
+    cu = np.concatenate([[0], np.cumsum(SEQ)])
+    for n, (s, h, r) in enumerate(rows):
+        assert np.array_equal(comp[n], full[cu[s] + r, h])

@@ -230,14 +230,16 @@ def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, vq: "QTensor", s
 
 
 def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bool = False, stream=None,
-                       cache: Optional[dict] = None):
+                       cache: Optional[dict] = None, mass_out=None, sel_out=None):
     """Attention mass of each key from the last n_obs query rows, and the
     counts[s] keys of largest mass per list.  Returns (mass [T][hq] float32
     device tensor, sel_off (host int32), sel_idx (host int32)): the index
     lists of a hybrid prefill policy (per query head) or of a decode selection
     (per KV head).  `cache` (a dict the caller keeps) holds the workspace and
     output buffers between calls of the same sizes; a returned mass tensor is
-    then overwritten by the next call."""
+    then overwritten by the next call.  mass_out ([T][hq] float32) and sel_out
+    (int32, at least the lists' total length) are caller buffers to write
+    instead of the cached or new ones."""
     import torch
     cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
     cp = cnt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
@@ -257,6 +259,12 @@ def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bo
         if cache is not None:
             cache.clear()
             cache.update(key=key, ws=ws, mass=mass, sel=sel, ws_bytes=int(n.value))
+    if mass_out is not None:
+        assert mass_out.dtype == torch.float32 and mass_out.numel() == shape.T * shape.hq
+        mass = mass_out
+    if sel_out is not None:
+        assert sel_out.dtype == torch.int32 and sel_out.numel() >= total
+        sel = sel_out
     _check(lib().tm_select_vertical(ctypes.byref(shape.c), _ptr(q), _ptr(k), int(n_obs), cp, int(per_kv_head),
                                     _ptr(mass), _ptr(sel), _ptr(ws), ctypes.byref(n), _stream(stream)),
            "tm_select_vertical")
@@ -293,18 +301,22 @@ def tm_build_traversal(shape: Shape, policy: Policy, trav=None, census: bool = T
 
 
 def tm_prefill(shape: Shape, trav, policy_kind: int, q, k, qq: QTensor, kq: QTensor, vq: QTensor, o=None,
-               o_dtype=TM_F32, lse=None, dbg_tiles=None, stream=None):
-    """Returns (o, lse, dbg_qk).  dbg_tiles: int32 device tensor [n][4] or None."""
+               o_dtype=TM_F32, lse=None, dbg_tiles=None, stream=None, dbg=None):
+    """Returns (o, lse, dbg_qk).  dbg_tiles: int32 device tensor [n][4] or None;
+    dbg: int32 device tensor [n][bq][64] to capture into (else a new one)."""
     import torch
     dev = q.device
     if o is None:
         tdt = {TM_F32: torch.float32, TM_F16: torch.float16, TM_BF16: torch.bfloat16}[o_dtype]
         o = torch.empty((shape.T, shape.hq, shape.d), dtype=tdt, device=dev)
-    dbg = None
     n_dbg = 0
     if dbg_tiles is not None:
         n_dbg = int(dbg_tiles.shape[0])
-        dbg = torch.zeros((n_dbg, shape.bq, 64), dtype=torch.int32, device=dev)
+        if dbg is None:
+            dbg = torch.zeros((n_dbg, shape.bq, 64), dtype=torch.int32, device=dev)
+        assert dbg.dtype == torch.int32 and dbg.numel() == n_dbg * shape.bq * 64
+    else:
+        dbg = None
     _check(lib().tm_prefill(ctypes.byref(shape.c), _ptr(trav), int(policy_kind), _ptr(q), _ptr(k), ctypes.byref(qq.c),
                             ctypes.byref(kq.c), ctypes.byref(vq.c), _ptr(o), o_dtype, _ptr(lse), _ptr(dbg),
                             _ptr(dbg_tiles), n_dbg, _stream(stream)), "tm_prefill")

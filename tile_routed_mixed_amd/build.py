@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtm.so")
+CEILING = os.path.join(HERE, "tm_ceiling")   # hardware-ceiling microbenchmarks (bench.py --ceiling)
 SOURCES = ["tm_api.hip", "k_quant.hip", "k_trav.hip", "k_prefill.hip", "k_decode.hip", "k_select.hip"]
 ARCH = "gfx950"
 
@@ -61,6 +62,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, OUT)
+    # the ceiling microbenchmarks: a separate executable, not part of libtm
+    tmp = CEILING + ".tmp"
+    r = subprocess.run([cc] + flags() + [os.path.join(CSRC, "ceiling.hip"), "-o", tmp], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on ceiling.hip:\n" + r.stdout + r.stderr)
+    os.replace(tmp, CEILING)
     return OUT
 
 

@@ -73,7 +73,7 @@ class PrefillPipeline:
             B.tm_gather_selected(self.shape, self.policy, self.trav, self.k, self.vq, stream)
         return c
 
-    def prefill(self, o_dtype=B.TM_F32, dbg_tiles=None, stream=None, with_lse=True):
+    def prefill(self, o_dtype=B.TM_F32, dbg_tiles=None, stream=None, with_lse=True, dbg=None):
         if self.o is None or self.o_dtype != o_dtype:
             import torch
             tdt = {B.TM_F32: torch.float32, B.TM_F16: torch.float16, B.TM_BF16: torch.bfloat16}[o_dtype]
@@ -81,7 +81,7 @@ class PrefillPipeline:
             self.o_dtype = o_dtype
         _, _, dbg = B.tm_prefill(self.shape, self.trav, self.policy.kind, self.q, self.k, self.qq, self.kq, self.vq, o=self.o,
                                  o_dtype=o_dtype, lse=self.lse if with_lse else None, dbg_tiles=dbg_tiles,
-                                 stream=stream)
+                                 stream=stream, dbg=dbg)
         return self.o, dbg
 
     def step(self, o_dtype=B.TM_F32, stream=None):
