@@ -31,13 +31,15 @@
  *  - Pointers named *_dev or documented as "device" are device memory owned by
  *    the caller (e.g. PyTorch tensors).  Pointers documented as "host" are host
  *    memory read during the call only.  The library allocates no device
- *    memory, frees nothing and keeps no pointer after a call returns (calls
+ *    memory (beyond one fixed array in its code object, for
+ *    tm_decode_noalloc), frees nothing and keeps no pointer after a call returns (calls
  *    that stage small host tables copy them into caller buffers and
  *    synchronize the stream before returning).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    is asynchronous: buffers must stay valid until the stream has finished.
  *    Calls on different streams are independent (the library has no mutable
- *    global state apart from the lazily loaded code object).
+ *    global state apart from the lazily loaded code object and the scratch
+ *    array of tm_decode_noalloc, which that entry point alone uses).
  *  - Every argument is validated on the host before anything is enqueued; on
  *    a nonzero status nothing has been enqueued and outputs are untouched.
  *    Launch failures return TM_E_HIP.  Faults inside kernels surface at the
@@ -406,6 +408,29 @@ tm_status tm_decode(const tm_shape* cache, const void* q,
                     const tm_qtensor* kq, const tm_qtensor* vq, const void* k16,
                     const tm_dpolicy* policy, void* o, int32_t o_dtype,
                     void* ws, size_t* ws_bytes, void* stream);
+
+/* tm_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and errors as tm_decode;
+ * the split-K partials live in a library-owned 8 MiB device array
+ * (tm_decode_noalloc_max_workspace()), one per GPU, held until the process
+ * ends.  The call allocates and frees nothing.  A request whose workspace
+ * (the size tm_decode reports for the same arguments) exceeds 8 MiB returns
+ * TM_E_SPACE before any GPU work; as a guide, 32 query heads of d = 128 fit
+ * up to about 480 sequences.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (on different streams, or from
+ * different host threads without ordering) race and give wrong outputs.
+ * Consecutive calls on one stream are safe (nothing in the array needs to
+ * start at zero; each call writes the partials it reads).  The first call on
+ * a device looks the array's device address up (hipGetSymbolAddress) with
+ * that device current.  Errors: those of tm_decode, TM_E_SPACE as above,
+ * TM_E_HIP if the address lookup fails. */
+tm_status tm_decode_noalloc(const tm_shape* cache, const void* q,
+                            const tm_qtensor* kq, const tm_qtensor* vq, const void* k16,
+                            const tm_dpolicy* policy, void* o, int32_t o_dtype, void* stream);
+
+/* Size in bytes of tm_decode_noalloc's device array (host only). */
+size_t tm_decode_noalloc_max_workspace(void);
 
 /* Cache append during generation ([TriAttention] abstract: the codes made
  * during prefill are reused as the decode cache; [HyQuant] "How HyQuant

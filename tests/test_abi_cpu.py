@@ -440,3 +440,23 @@ def test_growing_cache_validation(B):
     assert L.tm_cache_append(ctypes.byref(s.c), ptr(ln), FAKE, 2, ctypes.byref(wrong), None) == B.TM_E_SHAPE
     vrows_t16 = _qt(B, 2, 0, nb, True)       # rows layout with an fp16 copy is not a valid target
     assert L.tm_cache_append(ctypes.byref(s.c), ptr(ln), FAKE, 2, ctypes.byref(vrows_t16), None) == B.TM_E_ARG
+
+
+def test_decode_noalloc_rejects_workspace_beyond_its_array(B):
+    """A decode whose split-K workspace exceeds the library's 8 MiB scratch
+    array is refused with TM_E_SPACE before any HIP call (so this runs
+    without a GPU): 4096 sequences x 32 query heads need 4096 * 32 * 130 * 4
+    bytes of partials even with one split each."""
+    L = B.lib()
+    assert L.tm_decode_noalloc_max_workspace() == 8 << 20
+    s = _shape(B, [2] * 4096, hq=32, hkv=8, d=128)
+    dp = B.DPolicy(dict(b8=[1] * 8, b4=[2] * 8, sink=1, tail=128))
+    need = ctypes.c_size_t(0)
+    assert L.tm_decode(ctypes.byref(s.c), None, None, None, None, ctypes.byref(dp.c), None, B.TM_F32, None,
+                       ctypes.byref(need), None) == B.TM_OK
+    assert need.value > 8 << 20
+    qt = B.tm_qtensor(FAKE, FAKE, FAKE, FAKE, FAKE, 8, B.TM_COLS, 4096)
+    kt = B.tm_qtensor(FAKE, FAKE, FAKE, FAKE, None, 8, B.TM_ROWS, 4096)
+    st = L.tm_decode_noalloc(ctypes.byref(s.c), FAKE, ctypes.byref(kt), ctypes.byref(qt), FAKE, ctypes.byref(dp.c),
+                             FAKE, B.TM_F32, None)
+    assert st == B.TM_E_SPACE

@@ -106,6 +106,11 @@ def lib():
         L.tm_decode_select.restype = i32
         L.tm_decode_select.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_dpolicy), vp,
                                        ctypes.POINTER(tm_qtensor), vp, ctypes.POINTER(ctypes.c_size_t), vp]
+        L.tm_decode_noalloc.restype = i32
+        L.tm_decode_noalloc.argtypes = [ctypes.POINTER(tm_shape), vp, ctypes.POINTER(tm_qtensor),
+                                        ctypes.POINTER(tm_qtensor), vp, ctypes.POINTER(tm_dpolicy), vp, i32, vp]
+        L.tm_decode_noalloc_max_workspace.restype = ctypes.c_size_t
+        L.tm_decode_noalloc_max_workspace.argtypes = []
         L.tm_decode.restype = i32
         L.tm_decode.argtypes = [ctypes.POINTER(tm_shape), vp, ctypes.POINTER(tm_qtensor),
                                 ctypes.POINTER(tm_qtensor), vp, ctypes.POINTER(tm_dpolicy), vp, i32, vp,
@@ -409,6 +414,16 @@ def tm_decode(shape: Shape, q, kq: QTensor, vq: QTensor, k16, dpol: DPolicy, o=N
     _check(lib().tm_decode(ctypes.byref(shape.c), _ptr(q), ctypes.byref(kq.c), ctypes.byref(vq.c), _ptr(k16),
                            ctypes.byref(dpol.c), _ptr(o), o_dtype, _ptr(ws), ctypes.byref(n), _stream(stream)),
            "tm_decode")
+    return o
+
+
+def tm_decode_noalloc(shape: Shape, q, kq: QTensor, vq: QTensor, k16, dpol: DPolicy, o, o_dtype=TM_F32,
+                      stream=None):
+    """tm_decode with the library's own scratch array as workspace (o must be
+    given: the call allocates nothing)."""
+    _check(lib().tm_decode_noalloc(ctypes.byref(shape.c), _ptr(q), ctypes.byref(kq.c), ctypes.byref(vq.c),
+                                   _ptr(k16), ctypes.byref(dpol.c), _ptr(o), o_dtype, _stream(stream)),
+           "tm_decode_noalloc")
     return o
 
 

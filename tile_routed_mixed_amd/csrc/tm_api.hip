@@ -5,6 +5,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "tm_kernels.h"
@@ -247,6 +248,46 @@ DecodePlan decode_plan(const tm_shape* s, const tm_dpolicy* p, const std::vector
   d.nsplit = ns;
   d.ws_bytes = static_cast<size_t>(s->nseq) * s->hq * ns * (s->d + 2) * sizeof(float);
   return d;
+}
+
+// Workspace of tm_decode_noalloc: one file-scope device array, 8 MiB on every
+// GPU the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol): it uses the device address hipGetSymbolAddress returns, taken
+// once per device with that device current and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the device that runs `stream`.
+tm_status scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return TM_E_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return TM_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return TM_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return TM_E_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return TM_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return TM_E_HIP;
+    if (e != hipSuccess || p == nullptr) return TM_E_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return TM_OK;
 }
 
 }  // namespace
@@ -799,5 +840,20 @@ tm_status tm_cache_append(const tm_shape* cache, const int32_t* lengths, const v
   }
   return TM_OK;
 }
+
+tm_status tm_decode_noalloc(const tm_shape* cache, const void* q, const tm_qtensor* kq, const tm_qtensor* vq,
+                            const void* k16, const tm_dpolicy* policy, void* o, int32_t o_dtype, void* stream) {
+  // size first: a request beyond the scratch array is refused before any HIP call
+  size_t need = 0;
+  tm_status st = tm_decode(cache, q, kq, vq, k16, policy, o, o_dtype, nullptr, &need, stream);
+  if (st != TM_OK) return st;
+  if (need > kScratchBytes) return TM_E_SPACE;
+  void* ws = nullptr;
+  if ((st = scratch_for(static_cast<hipStream_t>(stream), &ws)) != TM_OK) return st;
+  size_t cap = kScratchBytes;
+  return tm_decode(cache, q, kq, vq, k16, policy, o, o_dtype, ws, &cap, stream);
+}
+
+size_t tm_decode_noalloc_max_workspace(void) { return kScratchBytes; }
 
 }  // extern "C"
