@@ -94,8 +94,17 @@ def pmc_traffic(summary, sources):
     return s.get("hbm_bytes_per_launch")
 
 
-def prefill_roofline(w, census, t_ms, traffic=None):
-    """Roofline of prefill_kernel: executed ops (both contractions of every
+def prefill_kernel_of(w, hybrid=False):
+    """The prefill kernel a workload's policy runs, and its source files:
+    boundary policies run the software-pipelined kernel, the other kinds
+    (bitmask, four-way, hybrid) prefill_kernel."""
+    if w.policy == "boundaries" and not hybrid:
+        return "prefill_pipe_kernel", ("k_prefill_pipe.hip", "k_prefill_common.h")
+    return "prefill_kernel", ("k_prefill.hip", "k_prefill_common.h")
+
+
+def prefill_roofline(w, census, t_ms, traffic=None, hybrid=False):
+    """Roofline of the prefill kernel: executed ops (both contractions of every
     executed tile, masked elements included) over the measured launch time,
     against the precision-weighted MFMA peak of this workload's tiles (INT8
     and INT4 QK at the int8 rate, FP16 QK and every PV at the fp16 rate)."""
@@ -107,7 +116,7 @@ def prefill_roofline(w, census, t_ms, traffic=None):
     achieved = ops / (t_ms * 1e-3) / 1e12
     peak = ops / t_peak / 1e12
     return {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-            "traffic": traffic, "kernel": "prefill_kernel", "ops_per_launch": ops,
+            "traffic": traffic, "kernel": prefill_kernel_of(w, hybrid)[0], "ops_per_launch": ops,
             "peak_note": "precision-weighted: INT8/INT4 QK at 5.0 POP/s, FP16 QK and every PV at 2.5 PFLOP/s, "
                          "over the executed tiles of this workload"}
 
@@ -213,7 +222,8 @@ def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48):
     torch.cuda.synchronize()
     t = stats(events_ms(lambda: pp.prefill(o_dtype), steps))
     roof = prefill_roofline(w, census, t["mean"],
-                            pmc_traffic(f"prefill_{name}_pmc.json", ("k_prefill.hip",)) if hybrid is None else None)
+                            pmc_traffic(f"prefill_{name}_pmc.json", prefill_kernel_of(w)[1]) if hybrid is None else None,
+                            hybrid=hybrid is not None)
     res = {"workload": describe(w, hybrid), "prefill_ms": t["mean"], "prefill_ms_median": t["median"],
            "prefill_ms_min": t["min"],
            "effective_tflops_dense_causal": dense_causal_flops(w) / (t["mean"] * 1e-3) / 1e12,
@@ -568,7 +578,7 @@ def main():
     flops = dense_causal_flops(w)
     value = flops / (ms_step * 1e-3) / 1e12
     roof = prefill_roofline(w, census, k_mean["prefill"],
-                            pmc_traffic(f"prefill_{w.name}_pmc.json", ("k_prefill.hip",)))
+                            pmc_traffic(f"prefill_{w.name}_pmc.json", prefill_kernel_of(w)[1]))
     log(f"[bench] prefill_kernel {k_mean['prefill']:.3f} ms: {roof['achieved']:.0f} of {roof['peak']:.0f} TFLOP/s "
         f"({roof['frac'] * 100:.1f} % of the precision-weighted peak)")
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

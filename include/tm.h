@@ -121,6 +121,11 @@ typedef struct tm_shape {
  *            transposed, [nblk][heads][d][64] (bf16 input rounded to nearest
  *            even fp16; zeros past the sequence end).
  *   s8, s4 [nblk][heads] float.
+ *   c4x (optional, TM_ROWS only): the INT4 codes once more, one per byte
+ *            (int8, -7..7), [nblk][heads][64][d] like c8.  tm_prefill
+ *            requires it for K under boundary policies (the
+ *            prefill kernel feeds these bytes to the int8 matrix cores as
+ *            they are, without unpacking nibbles on every tile).
  * nblk must equal sum over sequences of ceil(len / 64) (tm_num_blocks). */
 typedef struct tm_qtensor {
   int8_t* c8;
@@ -131,6 +136,7 @@ typedef struct tm_qtensor {
   int32_t heads;
   int32_t layout;
   int64_t nblk;
+  int8_t* c4x;
 } tm_qtensor;
 
 /* Tile policy ([TriAttention] abstract: two diagonal-distance boundaries per
@@ -356,6 +362,7 @@ tm_status tm_select_vertical(const tm_shape* shape, const void* q, const void* k
  * to fp16 for the PV product ([TriAttention] abstract: one normalized output
  * from both QK precisions; [TileMix] abstract: shared online-softmax state).
  * Errors: TM_E_ARG, TM_E_SHAPE (tensors not matching the shape),
+ * TM_E_ARG also when kq has no c4x under a boundary policy;
  * TM_E_UNSUPPORTED (a sequence whose 16-bit keys, or whose fp16 V copy, span
  * 2 GiB or more: len * hkv * d * 2 >= 2^31, or ceil(len / 64) * 64 * hkv * d
  * * 2 >= 2^31), TM_E_HIP. */

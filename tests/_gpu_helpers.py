@@ -81,7 +81,7 @@ class Guards:
             assert bad == 0, f"guard band of a {r} buffer of {n} elements overwritten ({bad} elements)"
 
 
-def guarded_qtensor(g, shape, heads, layout, with_t16, role="codes"):
+def guarded_qtensor(g, shape, heads, layout, with_t16, role="codes", with_c4x=False):
     """A QTensor (see the binding) whose buffers carry guard bands and
     poison: codes that the quantizer never writes, NaN scales and copies."""
     import torch
@@ -98,8 +98,10 @@ def guarded_qtensor(g, shape, heads, layout, with_t16, role="codes"):
     qt.s8 = g.alloc((nblk, heads), torch.float32, float("nan"), role)
     qt.s4 = g.alloc((nblk, heads), torch.float32, float("nan"), role)
     qt.t16 = g.alloc((nblk, heads, d, 64), torch.float16, float("nan"), role) if with_t16 else None
+    qt.c4x = g.alloc((nblk, heads, 64, d), torch.int8, -128, role) if with_c4x else None
     ptr = lambda t: None if t is None else int(t.data_ptr())
-    qt.c = B.tm_qtensor(ptr(qt.c8), ptr(qt.c4), ptr(qt.s8), ptr(qt.s4), ptr(qt.t16), heads, layout, nblk)
+    qt.c = B.tm_qtensor(ptr(qt.c8), ptr(qt.c4), ptr(qt.s8), ptr(qt.s4), ptr(qt.t16), heads, layout, nblk,
+                        ptr(qt.c4x))
     return qt
 
 
@@ -111,7 +113,7 @@ def guard_prefill(p, o_dtype):
     g = Guards(p.device)
     sh = p.shape
     p.qq = guarded_qtensor(g, sh, sh.hq, B.TM_ROWS, False)
-    p.kq = guarded_qtensor(g, sh, sh.hkv, B.TM_ROWS, False)
+    p.kq = guarded_qtensor(g, sh, sh.hkv, B.TM_ROWS, False, with_c4x=True)
     p.vq = guarded_qtensor(g, sh, sh.hkv, B.TM_COLS, True)
     tdt = {B.TM_F32: torch.float32, B.TM_F16: torch.float16, B.TM_BF16: torch.bfloat16}[o_dtype]
     p.o = g.alloc((sh.T, sh.hq, sh.d), tdt, float("nan"))

@@ -236,8 +236,8 @@ def test_traversal_capacity(B):
                                 None) == B.TM_E_SPACE
 
 
-def _qt(B, heads, layout, nblk, t16=True):
-    return B.tm_qtensor(FAKE, FAKE, FAKE, FAKE, FAKE if t16 else None, heads, layout, nblk)
+def _qt(B, heads, layout, nblk, t16=True, c4x=False):
+    return B.tm_qtensor(FAKE, FAKE, FAKE, FAKE, FAKE if t16 else None, heads, layout, nblk, FAKE if c4x else None)
 
 
 def test_quantize_validation(B):
@@ -256,6 +256,8 @@ def test_quantize_validation(B):
     s2 = _shape(B, [100, 30], dev=False)
     q = _qt(B, 4, B.TM_ROWS, nb, t16=False)
     assert L.tm_quantize_pack(ctypes.byref(s2.c), FAKE, 4, ctypes.byref(q), None) == B.TM_E_ARG
+    q = _qt(B, 4, B.TM_COLS, nb, t16=True, c4x=True)    # the one-byte INT4 copy exists in the rows layout only
+    assert L.tm_quantize_pack(ctypes.byref(s.c), FAKE, 4, ctypes.byref(q), None) == B.TM_E_ARG
 
 
 def test_prefill_validation(B):
@@ -279,6 +281,8 @@ def test_prefill_validation(B):
     assert call(args(vq=_qt(B, 2, 0, nb, True))) == B.TM_E_SHAPE
     assert call(args(kq=_qt(B, 4, 0, nb, False))) == B.TM_E_SHAPE
     assert call(args(qq=_qt(B, 4, 0, nb - 1, False))) == B.TM_E_SHAPE
+    # boundary policies read K's one-byte INT4 copy: refused without it
+    assert call(args(kq=_qt(B, 2, 0, nb, False, c4x=False))) == B.TM_E_ARG
 
 
 def test_decode_validation_and_workspace(B):

@@ -251,6 +251,8 @@ def _check_codes_chunked(x16, seqlens, qt, layout, what, chunk=16384):
             assert np.array_equal(hm(qt.s4).view(np.uint32), ref["s4"].view(np.uint32)), (what, s, t0, "s4")
             assert np.array_equal(hm(qt.c8), ref["c8p"]), (what, s, t0, "c8")
             assert np.array_equal(hm(qt.c4), ref["c4p"]), (what, s, t0, "c4")
+            if getattr(qt, "c4x", None) is not None:
+                assert np.array_equal(hm(qt.c4x), ref["c4"]), (what, s, t0, "c4x")
             if layout == "cols":
                 assert np.array_equal(hm(qt.t16).view(np.uint16), ref["t16"].view(np.uint16)), (what, s, t0)
             n += t1 - t0

@@ -59,6 +59,8 @@ def test_quantize_bitexact(dtype, d, seqlens):
         assert np.array_equal(hm(qt.s4).view(np.uint32), ref["s4"].view(np.uint32))
         assert np.array_equal(hm(qt.c8), ref["c8p"])
         assert np.array_equal(hm(qt.c4), ref["c4p"])
+        if qt.c4x is not None:   # K's INT4 codes one per byte
+            assert np.array_equal(hm(qt.c4x), ref["c4"])
         if layout == "cols":
             assert np.array_equal(hm(qt.t16).view(np.uint16), ref["t16"].view(np.uint16))
 
@@ -242,18 +244,24 @@ def test_boundaries_all_int8_equals_zero_bitmask():
 
 
 def test_fourway_reduces_to_boundaries_and_bitmask():
-    """The four-way kernel on all-zero codes computes the boundary policy, and
-    on codes from {2, 3} the bitmask policy: same outputs bit for bit as the
-    kernels of those kinds."""
+    """The four-way kernel on all-zero codes computes the boundary policy
+    (the same tiles at the same precisions; the boundary kernel orders the
+    tiles and sums the rows its own way, so the two agree within the fp32
+    gate, and both with the oracle), and on codes from {2, 3} the bitmask
+    policy: same outputs bit for bit as the bitmask kernel."""
     rng = np.random.default_rng(77)
     w = W.small("gqa8k", [900, 300], hq=4, hkv=2)
     q, k, v = _inputs(w)
     b = dict(kind=0, b8=[1, 2, 0, 3], b4=[2, 5, 4, 3], sink=1)
     _, tot = OP.fourway_row_base(w.seqlens, w.hq, w.bq, w.bk, 2)
     zero = dict(b, kind=2, group=2, words=np.zeros(tot, np.uint32))
-    _, _, o0, l0, _ = run_prefill(w, b, q, k, v)
-    _, _, o2, l2, _ = run_prefill(w, zero, q, k, v)
-    assert np.array_equal(o0, o2) and np.array_equal(l0, l2)
+    _, c0, o0, l0, _ = run_prefill(w, b, q, k, v)
+    _, c2, o2, l2, _ = run_prefill(w, zero, q, k, v)
+    assert all(c0[key] == c2[key] for key in ("legal", "int8", "int4", "fp16", "skip"))
+    compare(o0, o2.astype(np.float64), l0, l2.astype(np.float64), what="four-way zero codes vs boundaries")
+    O, L, _, _ = oracle_prefill(w, b, q, k, v)
+    compare(o0, O, l0, L, what="boundaries")
+    compare(o2, O, l2, L, what="four-way zero codes")
     # codes 2/3 <-> bitmask bits 0/1 of the same groups
     _, tot1 = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 2)
     bases4, _ = OP.fourway_row_base(w.seqlens, w.hq, w.bq, w.bk, 2)
@@ -350,8 +358,9 @@ def test_hybrid_prefill(case):
 
 def test_hybrid_reduces_to_fp16_and_int8_kernels():
     """No selected key: a window covering every row runs the bitmask kernel's
-    all-FP16 work, a zero window the boundary kernel's all-INT8 work, tile for
-    tile in the same order: same outputs bit for bit."""
+    all-FP16 work, tile for tile in the same order (same outputs bit for bit),
+    and a zero window the all-INT8 work of the boundary policy (computed by
+    the boundary kernel in its own tile order: within the fp32 gate)."""
     w = W.small("gqa8k", [900, 300], hq=4, hkv=2)
     q, k, v = _inputs(w)
     none = dict(kind=3, sel_off=np.zeros(len(w.seqlens) * w.hq + 1, np.int32), sel_idx=np.zeros(0, np.int32))
@@ -361,7 +370,7 @@ def test_hybrid_reduces_to_fp16_and_int8_kernels():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     _, _, o3, l3, _ = run_prefill(w, dict(kind=0, b8=[10 ** 6] * 4, b4=[10 ** 6] * 4, sink=0), q, k, v)
     _, _, o4, l4, _ = run_prefill(w, dict(none, window=0), q, k, v)
-    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+    compare(o3, o4.astype(np.float64), l3, l4.astype(np.float64), what="hybrid zero window vs all-INT8 boundaries")
 
 
 def test_varlen_permutation_equivariance():

@@ -37,7 +37,7 @@ class tm_shape(ctypes.Structure):
 class tm_qtensor(ctypes.Structure):
     _fields_ = [("c8", ctypes.c_void_p), ("c4", ctypes.c_void_p), ("s8", ctypes.c_void_p),
                 ("s4", ctypes.c_void_p), ("t16", ctypes.c_void_p), ("heads", ctypes.c_int32),
-                ("layout", ctypes.c_int32), ("nblk", ctypes.c_int64)]
+                ("layout", ctypes.c_int32), ("nblk", ctypes.c_int64), ("c4x", ctypes.c_void_p)]
 
 
 class tm_policy(ctypes.Structure):
@@ -165,7 +165,7 @@ class Shape:
 class QTensor:
     """Device buffers of one quantized tensor (see tm_qtensor in include/tm.h)."""
 
-    def __init__(self, shape: Shape, heads: int, layout: int, with_t16: bool, device):
+    def __init__(self, shape: Shape, heads: int, layout: int, with_t16: bool, device, with_c4x: bool = False):
         import torch
         nblk, d = shape.nblk(), shape.d
         self.heads, self.layout, self.nblk = heads, layout, nblk
@@ -180,8 +180,10 @@ class QTensor:
         self.s4 = torch.empty((nblk, heads), dtype=torch.float32, device=device)
         self.t16 = (torch.empty((nblk, heads, d, 64), dtype=torch.float16, device=device)
                     if with_t16 else None)
+        self.c4x = (torch.empty((nblk, heads, 64, d), dtype=torch.int8, device=device)
+                    if with_c4x else None)
         self.c = tm_qtensor(_ptr(self.c8), _ptr(self.c4), _ptr(self.s8), _ptr(self.s4), _ptr(self.t16),
-                            heads, layout, nblk)
+                            heads, layout, nblk, _ptr(self.c4x))
 
 
 # ----------------------------------------------------------------------------- entry points

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtm.so")
 CEILING = os.path.join(HERE, "tm_ceiling")   # hardware-ceiling microbenchmarks (bench.py --ceiling)
-SOURCES = ["tm_api.hip", "k_quant.hip", "k_trav.hip", "k_prefill.hip", "k_decode.hip", "k_select.hip"]
+SOURCES = ["tm_api.hip", "k_quant.hip", "k_trav.hip", "k_prefill.hip", "k_prefill_pipe.hip", "k_decode.hip",
+           "k_select.hip"]
 ARCH = "gfx950"
 
 

@@ -109,6 +109,22 @@ __device__ __forceinline__ void quant_block(const QuantArgs& a, int b, int h, si
       }
       *reinterpret_cast<u32x4*>(d8 + v * 16) = pk;
     }
+    if (a.c4x != nullptr) {   // the INT4 codes again, one per byte, in the INT8 codes' layout
+      int8_t* dx = a.c4x + (blk * kBlock + row) * D + col0;
+#pragma unroll
+      for (int v = 0; v < EPT / 16; ++v) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int o = v * 16 + e * 4;
+          pk[e] = (static_cast<uint32_t>(static_cast<uint8_t>(c4v[o]))) |
+                  (static_cast<uint32_t>(static_cast<uint8_t>(c4v[o + 1])) << 8) |
+                  (static_cast<uint32_t>(static_cast<uint8_t>(c4v[o + 2])) << 16) |
+                  (static_cast<uint32_t>(static_cast<uint8_t>(c4v[o + 3])) << 24);
+        }
+        *reinterpret_cast<u32x4*>(dx + v * 16) = pk;
+      }
+    }
     uint8_t* d4 = a.c4 + (blk * kBlock + row) * (D / 2) + col0 / 2;
 #pragma unroll
     for (int v = 0; v < EPT / 16; ++v) {

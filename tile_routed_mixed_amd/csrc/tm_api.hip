@@ -322,6 +322,7 @@ tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads, 
   if (shape->cu_seqlens_dev == nullptr || x == nullptr || out == nullptr || heads < 1) return TM_E_ARG;
   if (out->layout != TM_ROWS && out->layout != TM_COLS) return TM_E_ARG;
   if (out->layout == TM_ROWS && out->t16 != nullptr) return TM_E_ARG;
+  if (out->layout == TM_COLS && out->c4x != nullptr) return TM_E_ARG;
   st = check_qtensor(out, heads, out->layout, si.nblk, false);
   if (st != TM_OK) return st;
   if (si.nblk == 0) return TM_OK;
@@ -336,6 +337,7 @@ tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads, 
   a.s8 = out->s8;
   a.s4 = out->s4;
   a.t16 = out->t16;
+  a.c4x = out->c4x;
   const hipError_t e = launch_quantize(a, shape->d, shape->dtype == TM_BF16, out->layout == TM_COLS,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TM_OK : TM_E_HIP;
@@ -546,6 +548,7 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
   if ((st = check_qtensor(qq, shape->hq, TM_ROWS, si.nblk, false)) != TM_OK) return st;
   if ((st = check_qtensor(kq, shape->hkv, TM_ROWS, si.nblk, false)) != TM_OK) return st;
   if ((st = check_qtensor(vq, shape->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
+  if (policy_kind == TM_POLICY_BOUNDARIES && kq->c4x == nullptr) return TM_E_ARG;
   // the kernel addresses one (sequence, KV head)'s K and V^T tiles through
   // 32-bit buffer offsets: keep every such range below 2 GiB
   for (int s = 0; s < shape->nseq; ++s) {
@@ -565,6 +568,7 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
   a.qs4 = qq->s4;
   a.k8 = kq->c8;
   a.k4 = kq->c4;
+  a.k4x = kq->c4x;
   a.ks8 = kq->s8;
   a.ks4 = kq->s4;
   a.vt16 = vq->t16;
@@ -806,6 +810,7 @@ tm_status tm_cache_append(const tm_shape* cache, const int32_t* lengths, const v
   if (lengths == nullptr || x == nullptr || out == nullptr || heads < 1) return TM_E_ARG;
   if (out->layout != TM_ROWS && out->layout != TM_COLS) return TM_E_ARG;
   if (out->layout == TM_ROWS && out->t16 != nullptr) return TM_E_ARG;
+  if (out->layout == TM_COLS && out->c4x != nullptr) return TM_E_ARG;
   if ((st = check_qtensor(out, heads, out->layout, si.nblk, false)) != TM_OK) return st;
   for (int b = 0; b < cache->nseq; ++b) {
     const int32_t cap = cache->cu_seqlens[b + 1] - cache->cu_seqlens[b];
@@ -821,6 +826,7 @@ tm_status tm_cache_append(const tm_shape* cache, const int32_t* lengths, const v
   p.q.s8 = out->s8;
   p.q.s4 = out->s4;
   p.q.t16 = out->t16;
+  p.q.c4x = out->c4x;
   int64_t blk = 0;
   for (int s0 = 0; s0 < cache->nseq; s0 += kMaxSeqArg) {
     const int n = std::min(kMaxSeqArg, cache->nseq - s0);

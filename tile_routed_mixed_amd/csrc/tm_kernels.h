@@ -21,6 +21,7 @@ struct QuantArgs {
   float* s8;
   float* s4;
   uint16_t* t16;
+  int8_t* c4x;     // rows layout only, may be null: INT4 codes one per byte
 };
 
 struct AppendArgs {
@@ -64,6 +65,7 @@ struct PrefillArgs {
   const float* qs4;
   const int8_t* k8;
   const uint8_t* k4;
+  const int8_t* k4x;       // K's INT4 codes one per byte (boundary policies)
   const float* ks8;
   const float* ks4;
   const uint16_t* vt16;
@@ -142,6 +144,8 @@ hipError_t launch_traversal(const TravArgs& a, bool census, hipStream_t st);   /
 hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int d, int maxnt, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
+// boundary policies: the software-pipelined kernel (k_prefill_pipe.hip)
+hipError_t launch_prefill_pipe(const PrefillArgs& a, int d, int bq, hipStream_t st);
 hipError_t launch_decode_split(const DecodeArgs& a, int ncls, bool small, int d, bool bf16, hipStream_t st);
 // (a.sel selects the variant that reads selected tokens)
 hipError_t launch_decode_combine(const DecodeArgs& a, int d, hipStream_t st);

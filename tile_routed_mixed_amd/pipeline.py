@@ -28,7 +28,7 @@ class PrefillPipeline:
         self.device = device
         self.policy = B.Policy(policy, device=device)
         self.qq = B.QTensor(self.shape, hq, B.TM_ROWS, False, device)
-        self.kq = B.QTensor(self.shape, hkv, B.TM_ROWS, False, device)
+        self.kq = B.QTensor(self.shape, hkv, B.TM_ROWS, False, device, with_c4x=True)
         self.vq = B.QTensor(self.shape, hkv, B.TM_COLS, True, device)
         import torch
         self.trav = torch.empty(B.traversal_bytes(self.shape, self.policy), dtype=torch.uint8, device=device)
