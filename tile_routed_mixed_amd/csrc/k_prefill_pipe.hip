@@ -13,28 +13,28 @@
 // Same work decomposition, operand layouts and numerics as prefill_kernel
 // (k_prefill.hip): one workgroup of 4 waves per (sequence, query head, query
 // tile), S^T = K Q^T on the int8 matrix cores, O^T += V^T P^T on the fp16
-// ones with P rounded to fp16, a lazily re-based running maximum.  What
-// differs is the schedule, made for gfx950, where a wave's VALU work hides
-// under matrix-core issue only when the two are interleaved and independent:
+// ones with P rounded to fp16, row sums on a ones-MFMA, a lazily re-based
+// running maximum.  What differs is the schedule and the VALU work per score,
+// made for gfx950, where a wave's VALU work competes with its own matrix-core
+// issue and hides under it only when the two are interleaved and independent:
 //
-//  * iteration t runs two phases.  Phase A issues the 16 QK MFMAs of tile t+1
-//    and, between them, the exponentials of tile t (scale, exp2, fp16 pack,
-//    row sums); phase B issues the 32 PV MFMAs of tile t and, between them,
-//    the integer row maxima and the int-to-float conversion of tile t+1.
-//    Neither phase waits on its own results;
-//  * row sums are VALU dot products of the same fp16 probabilities with ones
-//    (v_dot2_f32_f16), kept per lane and reduced over the four lanes of a row
-//    at the end, so PV carries no extra ones-MFMA;
+//  * iteration t runs three phases.  Phase A issues the QK MFMAs of tile t+1
+//    and, between them, the exponentials of tile t's first 32 keys (scale
+//    FMA, exp2, fp16 pack); phase B1 issues the PV MFMAs of those 32 keys
+//    and, between them, the exponentials of the last 32; phase B2 issues the
+//    PV MFMAs of the last 32 keys and, between them, the integer row maxima
+//    of tile t+1.  No phase waits on its own results;
+//  * scores accumulate onto the bit pattern of 1.5 * 2^23, so they are read
+//    as floats with no conversion instruction (see sm_half);
 //  * INT4 tiles read K's INT4 codes from their one-byte copy (quantize pass),
 //    so INT4 and INT8 tiles are the same i8 MFMA work with different Q
-//    operands (Q's INT4 codes widened to 16 x code once per item) and scales;
+//    operands (Q's INT4 codes widened to 16 x code) and scales;
 //  * LDS holds two K slots and two V slots: iteration t reads K(t+1) and
 //    V(t), and issues the direct-to-LDS copies of K(t+2) and V(t+1) right
 //    after its one barrier, a whole iteration ahead of their use;
 //  * the at most BQ/64 tiles that cross the diagonal or the sequence end (the
 //    only ones that need masks) run first, through masked variants of the
 //    phases; the rest of the item runs unmasked.
-#include <climits>
 #include <type_traits>
 
 #include "k_prefill_common.h"
@@ -236,10 +236,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   i32x4 sc[2][4][QB];
   uint32_t xm[QB];        // excluded (row, key) pairs of a masked tile: bit 4 kb + i
-  const i32x4 kmag = {KMAG, KMAG, KMAG, KMAG};
+  i32x4 kmag = {KMAG, KMAG, KMAG, KMAG};
   f16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = static_cast<_Float16>(1.0f);
+  // (kept in VGPRs for the whole item: otherwise the compiler rebuilds them
+  // from scalar registers with VALU moves at every use)
+  asm volatile("" : "+v"(kmag), "+v"(ones));
+  // masked products enter the maxima as this biased value: below every real
+  // one (|product| < 2^21), and its float view is tiny, so the lane maximum
+  // of an all-masked lane comes out near -1.5 * 2^23 cs
+  constexpr int KMASK = KMAG - (1 << 30);
 
   constexpr int NA = 4 * NC8;   // phase A chunks: one K operand, QB QK MFMAs
   using I0 = std::integral_constant<int, 0>;
@@ -287,7 +294,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int key = key0 + sigma(kb, 4 * g + i);
         const bool x = key > row || key >= len;
         xm[qb] |= static_cast<uint32_t>(x) << (4 * kb + i);
-        if (x) v[i] = INT_MIN;
+        if (x) v[i] = KMASK;
       }
     }
     mp[qb] = max(max(mp[qb], v[0]), v[1]);
@@ -350,7 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (h == 1 && VW) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        mp[qb] = INT_MIN;
+        mp[qb] = KMASK;
         if constexpr (decltype(masked)::value) xm[qb] = 0u;
       }
     }
@@ -378,10 +385,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // lane maxima -> log2-domain maxima of the lane's scores (scale cs)
+  // (one FMA on the float view: -1.5 * 2^23 cs is exact, as in sm_half)
   auto lane_max = [&](const int (&mp)[QB], float cs, float (&tl)[QB]) {
+    const float b = -KMAGF * cs;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      tl[qb] = mp[qb] == INT_MIN ? -INFINITY : static_cast<float>(mp[qb] - KMAG) * cs;
+    for (int qb = 0; qb < QB; ++qb) tl[qb] = __builtin_fmaf(__int_as_float(mp[qb]), cs, b);
   };
 
   // QK of tile 0 (K slot 0) into sc[0] and its maxima (the first tile of an item)
@@ -397,7 +405,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int mp[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      mp[qb] = INT_MIN;
+      mp[qb] = KMASK;
       if constexpr (decltype(masked)::value) xm[qb] = 0u;
     }
 #pragma unroll
