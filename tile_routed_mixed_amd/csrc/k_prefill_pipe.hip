@@ -313,7 +313,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NH = 4 * QB;   // half-blocks: (kb 0..1) x (qb) x 2
     const uint8_t* kl = lds + (1 - p) * KB;
     i32x4 av[NA];
-    auto rd = [&](int i) { av[i] = *reinterpret_cast<const i32x4*>(kl + krow(i / NC8) * D + kb8[i % NC8]); };
+    // (chunk i = key block i % 4, k-chunk i / 4: the two products of one
+    // accumulator are four chunks apart)
+    auto rd = [&](int i) { av[i] = *reinterpret_cast<const i32x4*>(kl + krow(i % 4) * D + kb8[i / 4]); };
     if constexpr (QK) {
 #pragma unroll
       for (int i = 0; i < LA && i < NA; ++i) rd(i);
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < NA; ++i) {
       if constexpr (QK) {
         if (i + LA < NA) rd(i + LA);
-        const int kb = i / NC8, c = i % NC8;
+        const int kb = i % 4, c = i / 4;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sc[1 - p][kb][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], qop[qb][c], c == 0 ? kmag : sc[1 - p][kb][qb],
