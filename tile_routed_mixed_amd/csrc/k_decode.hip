@@ -121,6 +121,13 @@ constexpr int kRowShr = 0x110, kRowShl = 0x100, kRowRor = 0x120;
 // l16's scores in lanes l16 < 4 only (16 values a lane); they are first moved
 // four to a lane, so that the softmax works on every lane and on a quarter of
 // the values.  SEL: the step reads selected tokens (a.sel).
+// Cache policy of the streamed code loads (INT8 and INT4 blocks):
+// non-temporal.  Each code is read once per step, and the read set of a long
+// cache exceeds the last-level cache; measured at 16 x 32K: 85.3 us per step
+// against 90.2 us with the default policy.  (The FP16 window's strided key
+// rows measured slower with it, so they keep the default.)
+constexpr int kStream = 2;
+
 template <int D, bool BF16, bool SMALLG, bool SEL>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int NC = D / 32;          // k-chunks of the QK MFMA (lane group g owns channels DG*g ..)
@@ -249,16 +256,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       for (int i = 0; i < 8; ++i) {
         const uint32_t o = kb8 + static_cast<uint32_t>(dsig(i >> 1, 0) * D + (i & 1) * (D / 2));
         if constexpr (KW == 16) {
-          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kStream));
         } else {
-          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0));
+          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, kStream));
           r.k[i] = u32x4{x[0], x[1], 0u, 0u};
         }
       }
 #pragma unroll
       for (int db = 0; db < ND; ++db) {   // keys 16g .. 16g+15 of V^T row 16 db + l16: one 16-byte load
         const u32x4 x = as<u32x4>(
-            __builtin_amdgcn_raw_buffer_load_b128(rv, vb8 + static_cast<uint32_t>(db * 1024), 0, 0));
+            __builtin_amdgcn_raw_buffer_load_b128(rv, vb8 + static_cast<uint32_t>(db * 1024), 0, kStream));
         r.v[2 * db] = u32x2{x[0], x[1]};
         r.v[2 * db + 1] = u32x2{x[2], x[3]};
       }
@@ -277,16 +284,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       for (int i = 0; i < 8; ++i) {
         const uint32_t o = kb4 + static_cast<uint32_t>(dsig(i & 3, 0) * (D / 2));
         if constexpr (KW == 16) {
-          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128((i >> 2) ? rk1 : rk0, o, 0, 0));
+          r.k[i] = as<u32x4>(__builtin_amdgcn_raw_buffer_load_b128((i >> 2) ? rk1 : rk0, o, 0, kStream));
         } else {
-          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64((i >> 2) ? rk1 : rk0, o, 0, 0));
+          const u32x2 x = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64((i >> 2) ? rk1 : rk0, o, 0, kStream));
           r.k[i] = u32x4{x[0], x[1], 0u, 0u};
         }
       }
 #pragma unroll
       for (int i = 0; i < 2 * ND; ++i)
         r.v[i] = as<u32x2>(__builtin_amdgcn_raw_buffer_load_b64((i & 1) ? rv1 : rv0,
-                                                                vb4 + static_cast<uint32_t>((i >> 1) * 512), 0, 0));
+                                                                vb4 + static_cast<uint32_t>((i >> 1) * 512), 0, kStream));
       r.sk[0] = sload(ks4, jo);
       r.sv[0] = sload(vs4, jo);
       r.sk[1] = sload(ks4, jo1);
