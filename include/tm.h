@@ -119,7 +119,8 @@ typedef struct tm_shape {
  *   TM_COLS: c8 [nblk][heads][d][64]   c4 [nblk][heads][d][32]
  *            t16 (optional, TM_COLS only): the block's values as fp16,
  *            transposed, [nblk][heads][d][64] (bf16 input rounded to nearest
- *            even fp16; zeros past the sequence end).
+ *            even fp16, magnitudes beyond 65504 saturated to +-65504, NaN kept;
+ *            zeros past the sequence end).
  *   s8, s4 [nblk][heads] float.
  *   c4x (optional, TM_ROWS only): the INT4 codes once more, one per byte
  *            (int8, -7..7), [nblk][heads][64][d] like c8.  tm_prefill
@@ -377,8 +378,8 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
  *  cache: shape of the cached sequences (nseq = batch, len = cache length L
  *    including the new token, or the capacity of a growing cache whose
  *    current lengths policy->lengths gives); dtype TM_F16 or TM_BF16 (type of q and k16;
- *    bf16 values are widened to fp16 for the MFMA, exact for magnitudes in
- *    [2^-14, 65504]); hq/hkv <= 16.
+ *    bf16 values are narrowed to fp16 for the MFMA, exact for magnitudes in
+ *    [2^-14, 65504] and saturated to +-65504 beyond it); hq/hkv <= 16.
  *  q [nseq][hq][d] 16-bit (device).
  *  kq (TM_ROWS, hkv heads), vq (TM_COLS, hkv heads, t16 set): the cache, as
  *    produced by tm_quantize_pack over the cached tokens.

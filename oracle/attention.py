@@ -15,6 +15,14 @@ is computed here, row by row, in float64:
 * m = max score, p = exp(score - m), l = sum p, O_r = sum_c (p / l) v_c with the
   unquantized 16-bit V; lse_r = m + ln l.
 
+The method multiplies P with an fp16 copy of V ([TriAttention] abstract: one
+normalized output from the unquantized values; the precision of that copy is
+a reading).  A bf16 value beyond the fp16 range takes the nearest finite fp16
+value, +-65504, in every fp16 copy (fp16_copy): V in the prefill's PV; the
+query, and the FP16 blocks' and selected tokens' keys and values, in decode.
+The INT8/INT4 codes keep the true values through their scales.  For fp16
+inputs this changes nothing.
+
 tau = 1/sqrt(d) unless given.  Query head h reads key/value head h // (hq/hkv)
 (grouped-query attention, [TileMix] abstract).
 """
@@ -26,6 +34,14 @@ import numpy as np
 
 from . import policy as P
 from .quant import BLOCK
+
+
+def fp16_copy(x):
+    """Values as their fp16 copy holds them, for inputs already exact in fp16
+    or bf16: magnitudes beyond 65504 saturate to +-65504 (NaN stays NaN).
+    Rounding of bf16 values below the fp16 normal range is not modelled (it
+    moves an output by at most about 3e-8 per unit of weight)."""
+    return np.clip(x, -65504.0, 65504.0)
 
 
 def _tau(d, tau):
@@ -118,7 +134,7 @@ def prefill(seqlens, hq, hkv, d, bq, bk, pol, q64, k64, v64, qq, kq, tau=None,
             assert np.all(np.isfinite(m)), "a row with no executed key"
             p = np.exp(Sc - m[:, None])
             l = np.sum(p, axis=1)
-            ob = (p / l[:, None]) @ v64[tok0:tok0 + r1, kv]
+            ob = (p / l[:, None]) @ fp16_copy(v64[tok0:tok0 + r1, kv])
             if compact:
                 blocks.append(((s, h, r0, r1), ob, m + np.log(l)))
             else:
@@ -285,15 +301,16 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
                 lst = dpol["sel_idx"][int(dpol["sel_off"][r]):int(dpol["sel_off"][r + 1])]
                 chosen[np.asarray(lst, np.int64)] = True
             sc_list, val_list = [], []
+            qh = fp16_copy(q64[b, h])
             for j, t in enumerate(tags):
                 n = min(BLOCK, L - j * BLOCK)
                 keep = ~chosen[j * BLOCK: j * BLOCK + n]      # selected keys are read in FP16 below
                 if t == P.SKIP:
                     continue
                 if t == P.FP16:
-                    kk = k64[cu[b] + j * BLOCK: cu[b] + j * BLOCK + n, kv]
-                    vv = v64[cu[b] + j * BLOCK: cu[b] + j * BLOCK + n, kv]
-                    sc_list.append((tau * (kk @ q64[b, h]))[keep])
+                    kk = fp16_copy(k64[cu[b] + j * BLOCK: cu[b] + j * BLOCK + n, kv])
+                    vv = fp16_copy(v64[cu[b] + j * BLOCK: cu[b] + j * BLOCK + n, kv])
+                    sc_list.append((tau * (kk @ qh))[keep])
                     val_list.append(vv[keep])
                 else:
                     ck = kq["c8"] if t == P.INT8 else kq["c4"]
@@ -302,12 +319,12 @@ def decode(seqlens, hq, hkv, d, q64, kq, vq, k64, v64, dpol, tau=None, return_ta
                     sv = vq["s8"] if t == P.INT8 else vq["s4"]
                     kc = ck[kv, blk0 + j, :n].astype(np.float64)
                     vc = cv[kv, blk0 + j, :n].astype(np.float64)
-                    sc_list.append((tau * float(sk[kv, blk0 + j]) * (kc @ q64[b, h]))[keep])
+                    sc_list.append((tau * float(sk[kv, blk0 + j]) * (kc @ qh))[keep])
                     val_list.append((float(sv[kv, blk0 + j]) * vc)[keep])
             sel = np.nonzero(chosen)[0]
             if len(sel):
-                sc_list.append(tau * (k64[cu[b] + sel, kv] @ q64[b, h]))
-                val_list.append(v64[cu[b] + sel, kv])
+                sc_list.append(tau * (fp16_copy(k64[cu[b] + sel, kv]) @ qh))
+                val_list.append(fp16_copy(v64[cu[b] + sel, kv]))
             sc = np.concatenate(sc_list)
             vals = np.concatenate(val_list, axis=0)
             m = np.max(sc)

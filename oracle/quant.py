@@ -22,7 +22,8 @@ Layouts (``heads`` = H, ``nblk`` = sum over sequences of ceil(len / 64)):
 * cols (transposed, for V): c8 [H][nblk][d][64]; c4 packed [H][nblk][d][32]
          with token 2t low / 2t+1 high; f16 copy of the block, transposed,
          ``t16`` [H][nblk][d][64] (bf16 inputs converted to fp16, round to
-         nearest even; padding rows zero);
+         nearest even, magnitudes beyond 65504 saturated to +-65504; padding
+         rows zero);
 * s8, s4 [H][nblk] float32 in both layouts.
 """
 from __future__ import annotations
@@ -97,7 +98,8 @@ def quantize(x: np.ndarray, seqlens, layout: str = "rows", with_t16: bool = Fals
     else:
         raise ValueError(layout)
     if with_t16:
-        t16 = xpad_all.astype(np.float16)                               # round to nearest even
+        # round to nearest even; beyond the fp16 range the nearest finite value
+        t16 = np.clip(xpad_all, -65504.0, 65504.0).astype(np.float16)
         out["t16"] = np.ascontiguousarray(t16.transpose(0, 1, 3, 2))
     return out
 

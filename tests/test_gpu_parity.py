@@ -421,13 +421,16 @@ def _with_sel(dp, sel):
     return d
 
 
-def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, dtype="f16", sel=None):
-    """sel: (sel_off, sel_idx) selected tokens per (sequence, KV head), or None."""
+def _decode_case(seqlens, dpol, hq=8, hkv=2, d=128, dtype="f16", sel=None, plant=None):
+    """sel: (sel_off, sel_idx) selected tokens per (sequence, KV head), or None.
+    plant: a function of (decode query, K, V) input pairs returning new ones."""
     import torch
     import tile_routed_mixed_amd as T
     w = W.small("decode16x32k", seqlens, hq=hq, hkv=hkv, d=d, dtype=dtype)
     q, k, v = W.make_qkv(w)
     dq = W.make_decode_query(w)
+    if plant is not None:
+        dq, k, v = plant(dq, k, v)
     say(f"[gpu] decode {seqlens} hq={hq} hkv={hkv} d={d} {dtype} {dpol} "
         f"{'' if sel is None else str(len(sel[1])) + ' selected'}")
     p = T.DecodePipeline(w.seqlens, hq, hkv, d, dpol, dtype=dtype)
@@ -628,3 +631,73 @@ def test_decode_growing_cache_matches_rebuilt_oracle():
         if step < steps:
             rows = cu[:-1] + L
             p.append(k[0][rows], v[0][rows], q_bits=queries[step + 1][0])
+
+
+# ------------------------------------------------- bf16 values beyond the fp16 range
+
+def _plant16(pair, seed, vals, dtype="bf16"):
+    """The (bits, values) input pair with bf16 values beyond the fp16 range
+    planted at a few seeded places."""
+    y = np.array(pair[1], np.float32)
+    flat = y.reshape(-1)
+    rng = np.random.default_rng(seed)
+    for i, val in zip(rng.choice(flat.size, len(vals), replace=False), vals):
+        flat[i] = val
+    return W.round16(y, dtype)
+
+
+def _near(o, ref, big, what):
+    """Gate plus 2^-11 of the largest |value| the output mixes (big, broadcast
+    to o's shape): fp16 probabilities carry a relative error of 2^-12, which a
+    channel holding values near 65504 turns into absolute error."""
+    m = ~np.isnan(ref)
+    assert np.all(np.isfinite(o[m])), what
+    err = np.abs(o - ref)[m]
+    tol = (TOL_MAX + 2.0 ** -11 * big)[m]
+    say(f"[cmp] {what}: max err/tol {float(np.max(err / tol)):.3f}")
+    assert np.all(err <= tol), what
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_bf16_beyond_fp16_range_prefill(kind):
+    """bf16 V values beyond the fp16 range (1e5, -3e38, ...): the fp16 V^T
+    copy saturates them to +-65504 (bit-exact with the oracle quantizer, which
+    takes the same reading), and both prefill kernels give finite outputs that
+    match the oracle."""
+    w = W.small("gqa8k", [700, 129], hq=4, hkv=2)
+    q, k, v = _inputs(w)
+    v = _plant16(v, 31, [1.0e5, -3.0e38, 7.0e4, -9.0e4, 6.6e4])
+    assert np.max(np.abs(v[1])) > 65504
+    if kind == 0:
+        pol = dict(kind=0, b8=[1, 2, 0, 3], b4=[2, 5, 4, 3], sink=1)
+    else:
+        _, tot = OP.bitmask_row_base(w.seqlens, w.hq, w.bq, w.bk, 4)
+        pol = dict(kind=1, group=4, words=np.full(tot, 0xFFFFFFFF, np.uint32))
+    p, _, o, lse, _ = run_prefill(w, pol, q, k, v)
+    ref = OQ.quantize(v[1], w.seqlens, layout="cols", with_t16=True)
+    t16 = np.swapaxes(p.vq.t16.cpu().numpy(), 0, 1)
+    assert np.array_equal(t16.view(np.uint16), ref["t16"].view(np.uint16))
+    O, L, _, _ = oracle_prefill(w, pol, q, k, v)
+    big = np.max(np.abs(np.clip(v[1], -65504, 65504)), axis=0)          # [hkv][d]
+    grp = w.hq // w.hkv
+    _near(o, O, np.broadcast_to(np.repeat(big, grp, axis=0)[None], o.shape), f"prefill kind {kind}")
+    assert np.all(np.isfinite(lse[~np.isnan(L)]))
+
+
+def test_bf16_beyond_fp16_range_decode():
+    """bf16 values beyond the fp16 range in the decode query and in the cache
+    (FP16 window and quantized blocks): finite outputs matching the oracle,
+    whose fp16 copies saturate as the kernel's do."""
+    dpol = dict(b8=[4, 8], b4=[20, 30], sink=1, tail=128)
+    seqlens, hq, hkv = [1500, 3000], 8, 2
+    held = {}
+
+    def plant(dq, k, v):
+        held["v"] = _plant16(v, 43, [1.0e5, -3.0e38, 7.0e4], "bf16")
+        return _plant16(dq, 41, [1.0e5], "bf16"), _plant16(k, 42, [2.0e5, -7.0e4], "bf16"), held["v"]
+    o, O = _decode_case(seqlens, dpol, hq=hq, hkv=hkv, dtype="bf16", plant=plant)
+    vv = np.abs(np.clip(held["v"][1], -65504, 65504))
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    big = np.stack([np.repeat(np.max(vv[cu[b]:cu[b + 1]], axis=0), hq // hkv, axis=0) for b in range(len(seqlens))])
+    assert np.max(big) == 65504.0
+    _near(o, O, big, "decode")

@@ -494,3 +494,57 @@ def test_unquantized_compact_rows_match_full():
     cu = np.concatenate([[0], np.cumsum(SEQ)])
     for n, (s, h, r) in enumerate(rows):
         assert np.array_equal(comp[n], full[cu[s] + r, h])
+
+
+# ---------------------------------------------------------------- fp16 copies of bf16 values
+
+def _plant_big(x, seed, vals=(1.0e5, -3.0e38, 70000.0)):
+    """bf16 values beyond the fp16 range planted at a few seeded places."""
+    rng = np.random.default_rng(seed)
+    y = x.copy()
+    flat = y.reshape(-1)
+    for i, val in zip(rng.choice(flat.size, len(vals), replace=False), vals):
+        flat[i] = W.round16(np.array([val], np.float32), "bf16")[1][0]
+    return y
+
+
+def test_fp16_copy_saturates_and_keeps_nan():
+    x = np.array([65504.0, 65505.0, -1e5, 3e38, -65504.0, 1.0, np.nan])
+    y = A.fp16_copy(x)
+    assert list(y[:6]) == [65504.0, 65504.0, -65504.0, 65504.0, -65504.0, 1.0] and np.isnan(y[6])
+
+
+def test_bf16_beyond_fp16_range_prefill_is_attention_with_saturated_v():
+    """All-FP16 policy over bf16 inputs whose V holds values beyond the fp16
+    range: causal SDPA with V saturated to +-65504 (the fp16 copy PV uses)."""
+    q, k, v = _inputs(SEQ, HQ, HKV, D, 21, dtype="bf16")
+    v = _plant_big(v, 22)
+    assert np.max(np.abs(v)) > 65504
+    qq, kq = _quant(q, k)
+    _, tot = P.bitmask_row_base(SEQ, HQ, 128, 64, 4)
+    pol = dict(kind=1, group=4, words=np.full(tot, 0xFFFFFFFF, np.uint32))
+    O, _ = A.prefill(SEQ, HQ, HKV, D, 128, 64, pol, q.astype(np.float64), k.astype(np.float64),
+                     v.astype(np.float64), qq, kq)
+    ref = _sdpa(q, k, np.clip(v.astype(np.float64), -65504.0, 65504.0), SEQ, HQ, HKV)
+    assert np.all(np.isfinite(O))
+    assert np.max(np.abs(O - ref)) < 1e-9
+    # and the quantizer's fp16 copy holds the same saturated values
+    vq = Q.quantize(v, SEQ, layout="cols", with_t16=True)
+    t = vq["t16"].astype(np.float64)
+    assert np.max(np.abs(t)) == 65504.0 and np.all(np.isfinite(t))
+
+
+def test_bf16_beyond_fp16_range_decode_is_attention_with_saturated_q_and_window():
+    """All-FP16 decode (every block in the window) over bf16 values beyond the
+    fp16 range in q, K and V: one-query SDPA on the saturated values."""
+    q, k, v = _decode_inputs(23)
+    q, k, v = (W.round16(x.astype(np.float32), "bf16")[1] for x in (q, k, v))
+    q, k, v = _plant_big(q, 24, (1.0e5,)), _plant_big(k, 25), _plant_big(v, 26)
+    kq, vq = Q.quantize(k, DQ_SEQ), Q.quantize(v, DQ_SEQ, layout="cols")
+    dpol = dict(b8=[0, 0], b4=[0, 0], sink=0, tail=10 ** 6)
+    f64 = lambda x: x.astype(np.float64)
+    O = A.decode(DQ_SEQ, HQ, HKV, D, f64(q), kq, vq, f64(k), f64(v), dpol)
+    c = lambda x: np.clip(f64(x), -65504.0, 65504.0)
+    ref = _sdpa_one(c(q), c(k), c(v))
+    assert np.all(np.isfinite(O))
+    assert np.max(np.abs(O - ref)) < 1e-9 * max(1.0, float(np.max(np.abs(ref))))

@@ -33,16 +33,17 @@
 
 namespace tmx {
 
-// Eight 16-bit values (fp16, or bf16 widened to fp16: exact for magnitudes in
-// [2^-14, 65504], the range of normal fp16 numbers) as an fp16 MFMA operand.
+// Eight 16-bit values (fp16, or bf16 narrowed to fp16: exact for magnitudes
+// in [2^-14, 65504], the range of normal fp16 numbers, and saturated beyond
+// it) as an fp16 MFMA operand.
 template <bool BF16>
 __device__ __forceinline__ f16x8 to_f16x8(u32x4 raw) {
   f16x8 v;
   if constexpr (BF16) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[2 * e] = static_cast<_Float16>(__uint_as_float(raw[e] << 16));
-      v[2 * e + 1] = static_cast<_Float16>(__uint_as_float(raw[e] & 0xFFFF0000u));
+      v[2 * e] = to_f16_sat(__uint_as_float(raw[e] << 16));
+      v[2 * e + 1] = to_f16_sat(__uint_as_float(raw[e] & 0xFFFF0000u));
     }
   } else {
     __builtin_memcpy(&v, &raw, 16);

@@ -152,7 +152,7 @@ __device__ __forceinline__ void quant_block(const QuantArgs& a, int b, int h, si
     for (int e = 0; e < EPT; ++e) {
       s_c8[row][col0 + e] = c8v[e];
       s_c4[row][col0 + e] = c4v[e];
-      s_h[row][col0 + e] = static_cast<_Float16>(xv[e]);
+      s_h[row][col0 + e] = to_f16_sat(xv[e]);
     }
     __syncthreads();
     constexpr int TPR = 256 / D;          // threads per output row (channel)

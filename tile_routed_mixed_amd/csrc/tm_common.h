@@ -103,6 +103,15 @@ __device__ inline SeqOfBlock find_block_seq(const int32_t* __restrict__ cu, int 
   return r;
 }
 
+// A widened 16-bit input as fp16, saturated: a bf16 value beyond the fp16
+// range takes the nearest finite fp16 value (+-65504) instead of becoming
+// infinite; NaN stays NaN (its comparison is false).  Every fp16 copy of a
+// 16-bit input (the V^T copy, decode's q and FP16-window operands) goes
+// through it.
+__device__ __forceinline__ _Float16 to_f16_sat(float x) {
+  return static_cast<_Float16>(__builtin_fabsf(x) > 65504.0f ? __builtin_copysignf(65504.0f, x) : x);
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (n <= 15).
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
