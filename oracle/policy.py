@@ -150,7 +150,7 @@ def precision_grid(S, bq, bk, head, pol, seq=0, seqlens=None, hq=None):
         dl = np.maximum(0, (i * bq - j * bk) // bk)
         b8, b4 = int(pol["b8"][head]), int(pol["b4"][head])
         p = np.where(dl < b8, INT8, np.where(dl < b4, INT4, SKIP))
-        if int(pol["sink"]):
+        if int(pol["sink"]) and nk > 0:   # (an empty sequence has no tiles)
             p[:, 0] = INT8
         if pol["kind"] == 2:
             G = pol["group"]
