@@ -208,13 +208,20 @@ def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48):
     pp = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, pol)
     pp.upload(q[0], k[0], v[0])
     pp.quantize()
-    sel = None
+    sel = trv = None
     if hybrid is not None:
-        pol = pp.vertical_policy(hybrid[0], hybrid[1])
+        # the lists stay in device memory: selection, traversal and gather run
+        # back to back with no copy to the host and no wait
+        pol = pp.vertical_policy(hybrid[0], hybrid[1], on_device=True)
         torch.cuda.synchronize()
-        ms = [x for x in events_ms(lambda: pp.vertical_policy(hybrid[0], hybrid[1]), 6)][1:]
-        sel = stats(ms)
+        sel = stats(events_ms(lambda: pp.vertical_policy(hybrid[0], hybrid[1], on_device=True), 7)[2:])
         pp.set_policy(pol)
+        pp.traversal()
+        torch.cuda.synchronize()
+        trv = stats(events_ms(lambda: pp.traversal(), 7)[2:])
+        n_sel = int(pol["sel_off"][-1])
+        pol_host = dict(kind=pol["kind"], window=pol["window"], sel_off=pol["sel_off"],
+                        sel_idx=pol["sel_idx_dev"][:n_sel].cpu().numpy())   # for the oracle, untimed
     census = pp.traversal(census=True)
     o_dtype = T.TM_BF16 if w.dtype == "bf16" else T.TM_F16
     for _ in range(warmup):
@@ -229,8 +236,13 @@ def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48):
            "effective_tflops_dense_causal": dense_causal_flops(w) / (t["mean"] * 1e-3) / 1e12,
            "roofline": roof, "census": census}
     if sel is not None:
-        res["selection_ms_incl_host"] = sel["mean"]
-        res["selection_frac_of_prefill"] = sel["mean"] / t["mean"]
+        res["selection_ms"] = sel["mean"]
+        res["hybrid_traversal_ms"] = trv["mean"]
+        res["selection_plus_traversal_frac_of_prefill"] = (sel["mean"] + trv["mean"]) / t["mean"]
+        res["selection_note"] = ("tm_select_vertical (lists left in device memory), then tm_build_traversal and "
+                                 "tm_gather_selected on those lists: no host copy, no stream wait; event-timed "
+                                 "on the launch stream")
+        pol = pol_host
     if fp64_rows:
         res["fp64_error"] = prefill_fp64_error(w, pol, pp, q, k, v, fp64_rows)
     del pp
@@ -491,6 +503,9 @@ def main():
                     help="only run the decode sub-benchmark (16 x 32768-token cache) and print its JSON")
     ap.add_argument("--prefill-only", metavar="WORKLOAD",
                     help="only run the prefill line of one workload and print its JSON")
+    ap.add_argument("--hybrid", type=float, default=None, metavar="FRAC",
+                    help="with --prefill-only: the hybrid policy with FRAC of the keys selected by the "
+                         "vertical-line pass and a 128-token window")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain elementwise copy of BYTES bytes (read BYTES, write BYTES) 5 times, "
                          "to scale HBM byte counters; prints nothing else")
@@ -514,8 +529,9 @@ def main():
         print(json.dumps(decode_bench(max(5, args.steps))), flush=True)
         return
     if args.prefill_only:
+        hyb = None if args.hybrid is None else (args.hybrid, 128)
         print(json.dumps(prefill_line(args.prefill_only, steps=max(3, args.steps), warmup=args.warmup,
-                                      fp64_rows=8)), flush=True)
+                                      hybrid=hyb, fp64_rows=8)), flush=True)
         return
 
     import torch
@@ -626,7 +642,9 @@ def main():
             out["other_configs"].append(r)
             log(f"[bench] {name}{' hybrid' if hyb else ''}: prefill {r['prefill_ms']:.4f} ms, "
                 f"{r['effective_tflops_dense_causal']:.1f} TFLOP/s dense-causal, "
-                f"{r['roofline']['frac'] * 100:.1f} % of the weighted MFMA peak")
+                f"{r['roofline']['frac'] * 100:.1f} % of the weighted MFMA peak"
+                + (f"; selection {r['selection_ms']:.4f} ms + traversal {r['hybrid_traversal_ms']:.4f} ms = "
+                   f"{r['selection_plus_traversal_frac_of_prefill'] * 100:.1f} % of the prefill" if hyb else ""))
             if "fp64_error" in r and "fp64_error" in out:
                 out["fp64_error"][name + ("_hybrid" if hyb else "")] = r["fp64_error"]
     if not args.no_ceiling:

@@ -185,6 +185,16 @@ typedef struct tm_policy {
   const int32_t* sel_off;   /* [nseq*hq + 1]: list of row s*hq + h is sel_idx[sel_off[r], sel_off[r+1]) */
   const int32_t* sel_idx;   /* selected key positions within the sequence, strictly increasing per list */
   int32_t window;           /* sliding-window length in tokens, >= 0 */
+  /* Hybrid lists in device memory instead (sel_idx == NULL): sel_idx_dev holds
+   * the positions and sel_off_dev a device copy of sel_off (which is still
+   * given on the host: it sizes the traversal).  The tables are then built by
+   * a kernel, with no host copy and no wait, e.g. straight from the output of
+   * tm_select_vertical.  The positions are not checked: lists must be
+   * strictly increasing positions within their sequence (as
+   * tm_select_vertical writes them); other lists give unspecified outputs,
+   * but no access outside the buffers. */
+  const int32_t* sel_off_dev;
+  const int32_t* sel_idx_dev;
 } tm_policy;
 
 /* Tile counts of a traversal (host). */
@@ -228,6 +238,15 @@ typedef struct tm_dpolicy {
   const int32_t* sel_off;
   const int32_t* sel_idx;
   const void* sel_buf;
+  /* Selected lists in device memory instead (sel_idx == NULL, read by
+   * tm_decode_select only): positions sel_idx_dev and a device copy
+   * sel_off_dev of sel_off (still given on the host).  tm_decode_select then
+   * builds the tables with a kernel, with no host copy and no wait; the
+   * positions are not checked (lists must be strictly increasing positions
+   * below the current length; other lists give unspecified outputs but no
+   * access outside the buffers). */
+  const int32_t* sel_off_dev;
+  const int32_t* sel_idx_dev;
 } tm_dpolicy;
 
 /* Traversal buffer layout (device, written by tm_build_traversal, read by
@@ -301,7 +320,8 @@ tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads,
  * (b8 > b4, negative boundaries, b4 == 0 without sink, group < 1, n_words too
  * small; hybrid: window < 0, offsets not starting at 0 or decreasing, a list
  * not strictly increasing or outside its sequence), TM_E_SPACE, TM_E_HIP.
- * Hybrid policies synchronize `stream` (the lists are staged from the host).
+ * Hybrid policies with host lists synchronize `stream` (the lists are staged
+ * from the host); with device lists (sel_idx_dev) the call does not wait.
  * ([TriAttention] abstract: boundaries generate precision-grouped traversals;
  * [TileMix] abstract: compact bitmasks, one bit per group of key tiles.) */
 tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
@@ -406,9 +426,10 @@ tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kin
  * gathered into tiles of 64.  sel_buf == NULL: write the required size to
  * *sel_bytes and return TM_OK without GPU work; otherwise *sel_bytes is its
  * capacity (TM_E_SPACE if too small).  Call again after the listed tokens'
- * K or V change.  Synchronizes `stream` (the tables are staged from the
- * host).  Errors: TM_E_ARG, TM_E_SHAPE, TM_E_POLICY (lists), TM_E_SPACE,
- * TM_E_HIP. */
+ * K or V change.  With host lists it synchronizes `stream` (the tables are
+ * staged from the host); with device lists (sel_idx_dev) the tables are built
+ * by a kernel and the call does not wait.  Errors: TM_E_ARG, TM_E_SHAPE,
+ * TM_E_POLICY (lists), TM_E_SPACE, TM_E_HIP. */
 tm_status tm_decode_select(const tm_shape* cache, const tm_dpolicy* policy, const void* k16,
                            const tm_qtensor* vq, void* sel_buf, size_t* sel_bytes, void* stream);
 

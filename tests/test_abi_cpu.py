@@ -213,6 +213,20 @@ def test_hybrid_validation_and_size(B):
     bad = _hybrid(B, 0, lists)
     bad.c.sel_off = None
     assert st(bad) == B.TM_E_ARG
+    # lists in device memory (sel_idx NULL, device arrays set): the positions
+    # are not read on the host, so the same size comes out and only the
+    # offsets are checked
+    dv = _hybrid(B, 128, lists)
+    dv.c.sel_idx = None
+    dv.c.sel_idx_dev = FAKE
+    dv.c.sel_off_dev = FAKE
+    n.value = 0
+    assert st(dv) == B.TM_OK and n.value == end
+    dv.c.sel_idx_dev = None                                                  # neither host nor device lists
+    assert st(dv) == B.TM_E_ARG
+    dv = _hybrid(B, 0, [[], [], list(range(131)), []])                      # longer than its sequence
+    dv.c.sel_idx, dv.c.sel_idx_dev, dv.c.sel_off_dev = None, FAKE, FAKE
+    assert st(dv) == B.TM_E_POLICY
     # gather: hybrid policies only, device pointers required
     nb = s.nblk()
     vq = _qt(B, 1, 1, nb, True)

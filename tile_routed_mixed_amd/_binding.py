@@ -45,7 +45,7 @@ class tm_policy(ctypes.Structure):
                 ("b4", ctypes.POINTER(ctypes.c_int32)), ("sink", ctypes.c_int32),
                 ("bits", ctypes.c_void_p), ("n_words", ctypes.c_int64), ("group", ctypes.c_int32),
                 ("sel_off", ctypes.POINTER(ctypes.c_int32)), ("sel_idx", ctypes.POINTER(ctypes.c_int32)),
-                ("window", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("sel_off_dev", ctypes.c_void_p), ("sel_idx_dev", ctypes.c_void_p)]
 
 
 class tm_census(ctypes.Structure):
@@ -59,7 +59,7 @@ class tm_dpolicy(ctypes.Structure):
                 ("sink", ctypes.c_int32), ("tail_tokens", ctypes.c_int32),
                 ("lengths", ctypes.POINTER(ctypes.c_int32)), ("per_q_head", ctypes.c_int32),
                 ("sel_off", ctypes.POINTER(ctypes.c_int32)), ("sel_idx", ctypes.POINTER(ctypes.c_int32)),
-                ("sel_buf", ctypes.c_void_p)]
+                ("sel_buf", ctypes.c_void_p), ("sel_off_dev", ctypes.c_void_p), ("sel_idx_dev", ctypes.c_void_p)]
 
 
 class TMError(RuntimeError):
@@ -196,10 +196,21 @@ def tm_quantize_pack(shape: Shape, x, out: QTensor, stream=None) -> QTensor:
     return out
 
 
+def _dev_offsets(off: np.ndarray, device, given=None):
+    """Device copy of list offsets (int32 tensor), or `given` when it is one."""
+    import torch
+    if given is not None:
+        assert given.dtype == torch.int32 and given.numel() == off.size
+        return given
+    return torch.from_numpy(off.copy()).to(device)
+
+
 class Policy:
     """Host/device copies of a tile policy: dict(kind=0, b8, b4, sink),
     dict(kind=1, group, words), dict(kind=2, b8, b4, sink, group, words) or
-    dict(kind=3, window, sel_off, sel_idx)."""
+    dict(kind=3, window, sel_off, sel_idx).  A hybrid policy may hold its
+    lists in device memory instead: dict(kind=3, window, sel_off, sel_idx_dev
+    [, sel_off_dev]) with int32 device tensors (sel_off stays on the host)."""
 
     def __init__(self, pol: dict, device=None):
         self.kind = int(pol["kind"])
@@ -221,12 +232,20 @@ class Policy:
             self.bits = torch.from_numpy(words.view(np.int32).copy()).to(device) if device is not None else None
             n_words, group = int(words.size), int(pol["group"])
         self.c = tm_policy(self.kind, b8p, b4p, sink, _ptr(self.bits), n_words, group)
+        self.sel_idx_dev = self.sel_off_dev = None
         if self.kind == TM_POLICY_HYBRID:
             self.sel_off = np.ascontiguousarray(np.asarray(pol["sel_off"], dtype=np.int32))
-            self.sel_idx = np.ascontiguousarray(np.asarray(pol["sel_idx"], dtype=np.int32))
             self.c.sel_off = self.sel_off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-            self.c.sel_idx = self.sel_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
             self.c.window = int(pol["window"])
+            if pol.get("sel_idx_dev") is not None:
+                self.sel_idx_dev = pol["sel_idx_dev"]
+                assert self.sel_idx_dev.dtype.itemsize == 4 and self.sel_idx_dev.is_contiguous()
+                self.sel_off_dev = _dev_offsets(self.sel_off, self.sel_idx_dev.device, pol.get("sel_off_dev"))
+                self.c.sel_idx_dev = _ptr(self.sel_idx_dev)
+                self.c.sel_off_dev = _ptr(self.sel_off_dev)
+            else:
+                self.sel_idx = np.ascontiguousarray(np.asarray(pol["sel_idx"], dtype=np.int32))
+                self.c.sel_idx = self.sel_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
 def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, vq: "QTensor", stream=None):
@@ -237,16 +256,18 @@ def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, vq: "QTensor", s
 
 
 def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bool = False, stream=None,
-                       cache: Optional[dict] = None, mass_out=None, sel_out=None):
+                       cache: Optional[dict] = None, mass_out=None, sel_out=None, on_device: bool = False):
     """Attention mass of each key from the last n_obs query rows, and the
     counts[s] keys of largest mass per list.  Returns (mass [T][hq] float32
     device tensor, sel_off (host int32), sel_idx (host int32)): the index
     lists of a hybrid prefill policy (per query head) or of a decode selection
-    (per KV head).  `cache` (a dict the caller keeps) holds the workspace and
-    output buffers between calls of the same sizes; a returned mass tensor is
-    then overwritten by the next call.  mass_out ([T][hq] float32) and sel_out
-    (int32, at least the lists' total length) are caller buffers to write
-    instead of the cached or new ones."""
+    (per KV head).  on_device: sel_idx is the int32 device tensor the kernel
+    wrote (its first sel_off[-1] entries), with no copy to the host and no
+    wait.  `cache` (a dict the caller keeps) holds the workspace and
+    output buffers between calls of the same sizes; a returned mass tensor (or
+    device list) is then overwritten by the next call.  mass_out ([T][hq]
+    float32) and sel_out (int32, at least the lists' total length) are caller
+    buffers to write instead of the cached or new ones."""
     import torch
     cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
     cp = cnt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
@@ -277,6 +298,8 @@ def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bo
            "tm_select_vertical")
     per_list = np.repeat(cnt, nl)
     sel_off = np.concatenate([[0], np.cumsum(per_list)]).astype(np.int32)
+    if on_device:
+        return mass, sel_off, sel
     if stream is not None:   # the copy below runs on the current stream: order it after the kernels
         torch.cuda.current_stream().wait_stream(stream)
     return mass, sel_off, sel[:total].cpu().numpy().astype(np.int32)
@@ -350,18 +373,32 @@ class DPolicy:
             self.lengths = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
             self.c.lengths = self.lengths.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
-    def set_selection(self, sel_off, sel_idx):
+    def set_selection(self, sel_off, sel_idx, sel_off_dev=None):
         """Selected tokens kept in FP16: lists per (sequence, KV head), or
-        sel_off None for none.  The device buffer comes from tm_decode_select."""
+        sel_off None for none.  sel_idx: host positions, or an int32 device
+        tensor (lists in device memory; sel_off_dev, a device copy of sel_off,
+        is made when not given).  The device buffer comes from
+        tm_decode_select."""
+        self.sel_idx_dev = self.sel_off_dev = None
+        self.c.sel_idx_dev = self.c.sel_off_dev = None
         if sel_off is None:
             self.sel_off = self.sel_idx = None
             self.c.sel_off = self.c.sel_idx = None
             self.c.sel_buf = None
             return
         self.sel_off = np.ascontiguousarray(np.asarray(sel_off, dtype=np.int32))
-        self.sel_idx = np.ascontiguousarray(np.asarray(sel_idx, dtype=np.int32))
         self.c.sel_off = self.sel_off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-        self.c.sel_idx = self.sel_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        if hasattr(sel_idx, "data_ptr"):
+            assert sel_idx.dtype.itemsize == 4 and sel_idx.is_contiguous()
+            self.sel_idx = None
+            self.c.sel_idx = None
+            self.sel_idx_dev = sel_idx
+            self.sel_off_dev = _dev_offsets(self.sel_off, sel_idx.device, sel_off_dev)
+            self.c.sel_idx_dev = _ptr(self.sel_idx_dev)
+            self.c.sel_off_dev = _ptr(self.sel_off_dev)
+        else:
+            self.sel_idx = np.ascontiguousarray(np.asarray(sel_idx, dtype=np.int32))
+            self.c.sel_idx = self.sel_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         # the device buffer was built for other lists: tm_decode refuses to run
         # (TM_E_ARG) until tm_decode_select has filled one for these
         self.sel_buf = None

@@ -282,8 +282,105 @@ __global__ __launch_bounds__(256) void trav_census_kernel(uint8_t* trav, uint32_
   }
 }
 
+// Selected-key tables from lists in device memory: one workgroup per list
+// (sequence s, head h of the list's kind).  It writes the list's table entry,
+// the column masks of every key tile of its sequence (bit k of tile j set
+// when key 64 j + k is listed), and the headers and positions of its
+// gathered tiles; a traversal also gets a copy of the positions.  The list's
+// first gathered tile and its sequence's first block are sums over the lists
+// and sequences before it, reduced by the workgroup.  The lists are meant to
+// be strictly increasing positions inside their sequence, as the selection
+// pass writes them; they are not checked, but a position outside the
+// sequence is written as INT32_MAX (an empty slot: never gathered, and past
+// every causal row) and no read or write leaves the buffers.
+__device__ __forceinline__ int2 list_span(const SelTabArgs& a, int r) {
+  const int32_t lo = min(max(a.off[r], 0), static_cast<int32_t>(a.n_sel));
+  const int32_t hi = min(max(a.off[r + 1], lo), static_cast<int32_t>(a.n_sel));
+  return make_int2(lo, hi - lo);
+}
+
+__device__ __forceinline__ int block_sum256(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(256) void sel_tables_kernel(SelTabArgs a) {
+  __shared__ int red[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int s = r / a.lists_per_seq, h = r % a.lists_per_seq;
+  int blk = 0, gb = 0;
+  for (int u = tid; u < s; u += 256) blk += (a.cu[u + 1] - a.cu[u] + kBlock - 1) / kBlock;
+  for (int u = tid; u < r; u += 256) gb += (list_span(a, u).y + kBlock - 1) / kBlock;
+  blk = block_sum256(blk, red);
+  gb = min(block_sum256(gb, red), static_cast<int>(a.n_gt));
+  const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0, nk = (len + kBlock - 1) / kBlock;
+  const int2 sp = list_span(a, r);
+  const int start = sp.x;
+  const int cnt = min(sp.y, (static_cast<int>(a.n_gt) - gb) * kBlock);
+  const int32_t* li = a.idx + start;
+  auto pos_of = [&](int e) {
+    const int32_t c = li[e];
+    return (c >= 0 && c < len) ? c : INT32_MAX;
+  };
+  const int cm_base = a.decode ? 0 : a.lists_per_seq * blk + h * nk;
+  if (tid == 0) {
+    uint32_t* te = reinterpret_cast<uint32_t*>(a.buf + a.tab_off);
+    if (a.decode) {
+      te[2 * r] = static_cast<uint32_t>(gb);
+      te[2 * r + 1] = static_cast<uint32_t>(cnt);
+    } else {
+      reinterpret_cast<SelEntry*>(te)[r] = SelEntry{static_cast<uint32_t>(start), static_cast<uint32_t>(cnt),
+                                                    static_cast<uint32_t>(gb), static_cast<uint32_t>(cm_base)};
+    }
+  }
+  if (!a.decode) {
+    int32_t* dst = reinterpret_cast<int32_t*>(a.buf + a.idx_off) + start;
+    for (int e = tid; e < cnt; e += 256) dst[e] = pos_of(e);
+  }
+  // column masks: the entries of key tile j are contiguous in a sorted list
+  uint64_t* cm = reinterpret_cast<uint64_t*>(a.buf + a.cm_off);
+  for (int j = tid; j < nk; j += 256) {
+    const int k0 = j * kBlock;
+    int lo = 0, hi = cnt;   // first entry >= k0
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (li[mid] < k0) lo = mid + 1; else hi = mid;
+    }
+    uint64_t m = 0;
+    for (int e = lo; e < cnt; ++e) {
+      const int c = li[e];
+      if (c < k0 || c >= k0 + kBlock) break;
+      if (c < len) m |= uint64_t(1) << (c - k0);
+    }
+    cm[a.decode ? static_cast<size_t>(blk + j) * a.hkv + h : static_cast<size_t>(cm_base) + j] = m;
+  }
+  // gathered tiles: header {first token, first block, KV head, keys} and 64 positions
+  const int ng = (cnt + kBlock - 1) / kBlock;
+  const uint32_t kv = static_cast<uint32_t>(h / a.grp);
+  for (int u = tid; u < ng * kBlock; u += 256) {
+    const int t = u / kBlock, k = u % kBlock;
+    uint8_t* gh = a.buf + a.gh_off + static_cast<size_t>(gb + t) * kGatherHdr;
+    const int keys = min(kBlock, cnt - kBlock * t);
+    if (k == 0)
+      *reinterpret_cast<GatherEntry*>(gh) =
+          GatherEntry{static_cast<uint32_t>(tok0), static_cast<uint32_t>(blk), kv, static_cast<uint32_t>(keys)};
+    reinterpret_cast<int32_t*>(gh + 16)[k] = k < keys ? pos_of(kBlock * t + k) : INT32_MAX;
+  }
+}
+
+hipError_t launch_sel_tables(const SelTabArgs& a, int n_lists, hipStream_t st) {
+  if (n_lists <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_tables_kernel, dim3(n_lists), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // Hybrid policies: fill gathered tile t with its selected keys' 16-bit K rows
-// ([64][D]) and fp16 V columns (V^T [D][64]); slots past the list are zero.
+// ([64][D]) and fp16 V columns (V^T [D][64]); slots past the list, and empty
+// slots (position INT32_MAX), are zero.
 template <int D>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const uint32_t t = blockIdx.x;
@@ -297,7 +394,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   for (int u = threadIdx.x; u < kBlock * CPR; u += 256) {
     const int row = u / CPR, ch = u % CPR;
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (row < static_cast<int>(ge.keys)) {
+    if (row < static_cast<int>(ge.keys) && pos[row] != INT32_MAX) {
       const size_t tok = static_cast<size_t>(ge.tok_start) + pos[row];
       v = *reinterpret_cast<const u32x4*>(a.k + (tok * a.hkv + ge.kv) * D + ch * 8);
     }
@@ -305,7 +402,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   }
   // V^T: channel rows of 64 slots; thread (slot, channel quarter) copies D/4 channels
   const int slot = threadIdx.x & 63, c0 = threadIdx.x >> 6;
-  const bool ok = slot < static_cast<int>(ge.keys);
+  const bool ok = slot < static_cast<int>(ge.keys) && pos[slot] != INT32_MAX;
   const int key = ok ? pos[slot] : 0;
   const uint16_t* src = a.vt16 + ((static_cast<size_t>(ge.blk_start) + key / kBlock) * a.hkv + ge.kv) * D * kBlock +
                         key % kBlock;

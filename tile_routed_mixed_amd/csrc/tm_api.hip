@@ -82,9 +82,16 @@ struct HybridPlan {
   int64_t n_sel = 0, n_gt = 0, n_cm = 0;
 };
 
+// Lists on the device (sel_idx NULL, both device arrays set): the positions
+// are not read on the host.
+bool hybrid_dev_lists(const tm_policy* p) {
+  return p->sel_idx == nullptr && p->sel_idx_dev != nullptr && p->sel_off_dev != nullptr;
+}
+
 tm_status hybrid_plan(const tm_shape* s, const tm_policy* p, HybridPlan* hp) {
   if (p->sel_off == nullptr) return TM_E_ARG;
   if (p->window < 0 || p->sel_off[0] != 0) return TM_E_POLICY;
+  const bool dev = hybrid_dev_lists(p);
   const int64_t nr = static_cast<int64_t>(s->nseq) * s->hq;
   hp->rows.assign(static_cast<size_t>(nr), SelEntry{0, 0, 0, 0});
   int64_t gt = 0, cm = 0;
@@ -94,9 +101,9 @@ tm_status hybrid_plan(const tm_shape* s, const tm_policy* p, HybridPlan* hp) {
     for (int h = 0; h < s->hq; ++h) {
       const int64_t r = static_cast<int64_t>(sq) * s->hq + h;
       const int64_t a = p->sel_off[r], b = p->sel_off[r + 1];
-      if (b < a) return TM_E_POLICY;
-      if (b > a && p->sel_idx == nullptr) return TM_E_ARG;
-      for (int64_t e = a; e < b; ++e) {
+      if (b < a || b - a > len) return TM_E_POLICY;
+      if (b > a && p->sel_idx == nullptr && !dev) return TM_E_ARG;
+      for (int64_t e = a; !dev && e < b; ++e) {
         const int64_t c = p->sel_idx[e];
         if (c < 0 || c >= len || (e > a && c <= p->sel_idx[e - 1])) return TM_E_POLICY;
       }
@@ -418,9 +425,29 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
     a.gh_off = static_cast<uint32_t>(L.gh_off);
     a.gk_off = static_cast<uint32_t>(L.gk_off);
     a.gv_off = static_cast<uint32_t>(L.gv_off);
-    // stage the list tables (pageable host memory: wait for the copy before
-    // the staging buffer goes away)
-    const std::vector<uint8_t> tab = hybrid_tables(shape, policy, hp, L);
+    if (hybrid_dev_lists(policy)) {
+      // lists in device memory: the tables are built by a kernel, no wait
+      SelTabArgs t;
+      t.buf = static_cast<uint8_t*>(trav);
+      t.cu = shape->cu_seqlens_dev;
+      t.off = policy->sel_off_dev;
+      t.idx = policy->sel_idx_dev;
+      t.lists_per_seq = shape->hq;
+      t.grp = shape->hq / shape->hkv;
+      t.hkv = shape->hkv;
+      t.decode = 0;
+      t.n_sel = static_cast<uint32_t>(hp.n_sel);
+      t.n_gt = static_cast<uint32_t>(hp.n_gt);
+      t.tab_off = static_cast<uint32_t>(L.sel_tab_off);
+      t.idx_off = static_cast<uint32_t>(L.sel_idx_off);
+      t.cm_off = static_cast<uint32_t>(L.cm_off);
+      t.gh_off = static_cast<uint32_t>(L.gh_off);
+      if (launch_sel_tables(t, static_cast<int>(hp.rows.size()), hs) != hipSuccess) return TM_E_HIP;
+    }
+    // host lists: stage the tables (pageable host memory: wait for the copy
+    // before the staging buffer goes away)
+    const std::vector<uint8_t> tab =
+        hybrid_dev_lists(policy) ? std::vector<uint8_t>() : hybrid_tables(shape, policy, hp, L);
     if (!tab.empty()) {
       if (hipMemcpyAsync(static_cast<uint8_t*>(trav) + L.sel_tab_off, tab.data(), tab.size(), hipMemcpyHostToDevice,
                          hs) != hipSuccess)
@@ -600,9 +627,15 @@ struct DecodeSel {
 // positions: check every listed position (tm_decode_select); the decode step
 // itself needs only the list lengths (its reads are bounded by the buffer the
 // select call built)
+bool decode_dev_lists(const tm_dpolicy* p) {
+  return p->sel_idx == nullptr && p->sel_idx_dev != nullptr && p->sel_off_dev != nullptr;
+}
+
 tm_status decode_sel_plan(const tm_shape* s, const tm_dpolicy* p, const ShapeInfo& si, DecodeSel* ds,
                           bool positions) {
-  if (p->sel_idx == nullptr && p->sel_off[static_cast<size_t>(s->nseq) * s->hkv] > 0) return TM_E_ARG;
+  if (decode_dev_lists(p)) positions = false;   // device lists are not read on the host
+  else if (positions && p->sel_idx == nullptr && p->sel_off[static_cast<size_t>(s->nseq) * s->hkv] > 0)
+    return TM_E_ARG;
   if (p->sel_off[0] != 0) return TM_E_POLICY;
   ds->tab.assign(2 * static_cast<size_t>(s->nseq) * s->hkv, 0u);
   int64_t gt = 0;
@@ -654,6 +687,37 @@ tm_status tm_decode_select(const tm_shape* cache, const tm_dpolicy* policy, cons
   if (*sel_bytes < ds.bytes) return TM_E_SPACE;
   if (k16 == nullptr) return TM_E_ARG;
   if ((st = check_qtensor(vq, cache->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  GatherArgs g;
+  g.trav = static_cast<uint8_t*>(sel_buf);
+  g.k = static_cast<const uint16_t*>(k16);
+  g.vt16 = vq->t16;
+  g.hkv = cache->hkv;
+  g.n_gtiles = static_cast<uint32_t>(ds.n_gt);
+  g.gh_off = static_cast<uint32_t>(ds.gh_off);
+  g.gk_off = static_cast<uint32_t>(ds.gk_off);
+  g.gv_off = static_cast<uint32_t>(ds.gv_off);
+  if (decode_dev_lists(policy)) {
+    // lists in device memory: tables by a kernel, then the gather; no wait
+    if (cache->cu_seqlens_dev == nullptr) return TM_E_ARG;
+    SelTabArgs t;
+    t.buf = static_cast<uint8_t*>(sel_buf);
+    t.cu = cache->cu_seqlens_dev;
+    t.off = policy->sel_off_dev;
+    t.idx = policy->sel_idx_dev;
+    t.lists_per_seq = cache->hkv;
+    t.grp = 1;
+    t.hkv = cache->hkv;
+    t.decode = 1;
+    t.n_sel = static_cast<uint32_t>(policy->sel_off[static_cast<size_t>(cache->nseq) * cache->hkv]);
+    t.n_gt = static_cast<uint32_t>(ds.n_gt);
+    t.tab_off = static_cast<uint32_t>(ds.tab_off);
+    t.idx_off = 0;
+    t.cm_off = static_cast<uint32_t>(ds.cm_off);
+    t.gh_off = static_cast<uint32_t>(ds.gh_off);
+    if (launch_sel_tables(t, cache->nseq * cache->hkv, hs) != hipSuccess) return TM_E_HIP;
+    return launch_gather(g, cache->d, hs) == hipSuccess ? TM_OK : TM_E_HIP;
+  }
   // host staging of the list table, the column masks and the tile headers
   std::vector<uint8_t> buf(ds.gk_off, 0);
   std::memcpy(buf.data() + ds.tab_off, ds.tab.data(), 4 * ds.tab.size());
@@ -679,18 +743,8 @@ tm_status tm_decode_select(const tm_shape* cache, const tm_dpolicy* policy, cons
     }
     blk += (cap + 63) / 64;
   }
-  hipStream_t hs = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(sel_buf, buf.data(), buf.size(), hipMemcpyHostToDevice, hs) != hipSuccess) return TM_E_HIP;
   if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;
-  GatherArgs g;
-  g.trav = static_cast<uint8_t*>(sel_buf);
-  g.k = static_cast<const uint16_t*>(k16);
-  g.vt16 = vq->t16;
-  g.hkv = cache->hkv;
-  g.n_gtiles = static_cast<uint32_t>(ds.n_gt);
-  g.gh_off = static_cast<uint32_t>(ds.gh_off);
-  g.gk_off = static_cast<uint32_t>(ds.gk_off);
-  g.gv_off = static_cast<uint32_t>(ds.gv_off);
   return launch_gather(g, cache->d, hs) == hipSuccess ? TM_OK : TM_E_HIP;
 }
 

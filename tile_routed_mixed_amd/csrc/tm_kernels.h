@@ -55,6 +55,23 @@ struct GatherArgs {
   uint32_t n_gtiles, gh_off, gk_off, gv_off;
 };
 
+// Selected-key tables built on the GPU from device-resident lists (hybrid
+// traversals and decode selection buffers).  n_sel and n_gt are the list
+// entries and gathered tiles the host sized the buffer for: every write and
+// every list read stays below them whatever the device offsets hold.
+struct SelTabArgs {
+  uint8_t* buf;
+  const int32_t* cu;        // device cu_seqlens
+  const int32_t* off;       // device list offsets [nseq * lists_per_seq + 1]
+  const int32_t* idx;       // device positions
+  int lists_per_seq;        // hq (prefill: lists per query head) or hkv (decode)
+  int grp;                  // query heads per KV head (prefill), 1 (decode)
+  int hkv;
+  int decode;               // 0: traversal tables; 1: decode selection buffer
+  uint32_t n_sel, n_gt;
+  uint32_t tab_off, idx_off, cm_off, gh_off;
+};
+
 struct PrefillArgs {
   const uint8_t* trav;
   const uint16_t* q;
@@ -142,6 +159,7 @@ hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipS
 hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_traversal(const TravArgs& a, bool census, hipStream_t st);   // census: also sum the counts into the header
 hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);
+hipError_t launch_sel_tables(const SelTabArgs& a, int n_lists, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int d, int maxnt, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
 // boundary policies: the software-pipelined kernel (k_prefill_pipe.hip)

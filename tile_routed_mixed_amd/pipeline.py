@@ -46,14 +46,24 @@ class PrefillPipeline:
         if self.trav.numel() < need:
             self.trav = torch.empty(need, dtype=torch.uint8, device=self.device)
 
-    def vertical_policy(self, frac: float, window: int, n_obs: int = 64, stream=None):
+    def vertical_policy(self, frac: float, window: int, n_obs: int = 64, stream=None, on_device: bool = False):
         """Hybrid policy whose selected keys are, per (sequence, query head),
         the round(frac * len) keys of largest attention mass from the last
-        n_obs query rows (tm_select_vertical over the uploaded Q and K)."""
+        n_obs query rows (tm_select_vertical over the uploaded Q and K).
+        on_device: the lists stay where the selection wrote them (sel_idx_dev,
+        overwritten by the next selection of this pipeline) and nothing waits
+        for the GPU; otherwise they are copied to the host (sel_idx)."""
         counts = [int(round(frac * S)) for S in self.shape.seqlens]
         _, off, idx = B.tm_select_vertical(self.shape, self.q, self.k, n_obs, counts, False, stream,
-                                           cache=self._sel_cache)
-        return dict(kind=B.TM_POLICY_HYBRID, window=int(window), sel_off=off, sel_idx=idx)
+                                           cache=self._sel_cache, on_device=on_device)
+        if not on_device:
+            return dict(kind=B.TM_POLICY_HYBRID, window=int(window), sel_off=off, sel_idx=idx)
+        key = off.tobytes()
+        if self._sel_cache.get("off_key") != key:   # device offsets: uploaded once per list sizes
+            self._sel_cache["off_key"] = key
+            self._sel_cache["off_dev"] = B._dev_offsets(off, self.device)
+        return dict(kind=B.TM_POLICY_HYBRID, window=int(window), sel_off=off, sel_idx_dev=idx,
+                    sel_off_dev=self._sel_cache["off_dev"])
 
     def upload(self, q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray):
         self.q = _dev_bits(q_bits, self.device)
@@ -115,11 +125,12 @@ class DecodePipeline:
         B.tm_quantize_pack(self.shape, self.k, self.kq, stream)
         B.tm_quantize_pack(self.shape, self.v, self.vq, stream)
 
-    def select(self, sel_off, sel_idx, stream=None):
+    def select(self, sel_off, sel_idx, stream=None, sel_off_dev=None):
         """Keep the listed tokens in FP16 (lists per (sequence, KV head), after
-        build_cache / start); call again when the lists or lengths change."""
+        build_cache / start); call again when the lists or lengths change.
+        sel_idx may be an int32 device tensor (lists in device memory)."""
         import torch
-        self.dpol.set_selection(sel_off, sel_idx)
+        self.dpol.set_selection(sel_off, sel_idx, sel_off_dev)
         if sel_off is None:
             return
         n = B.decode_sel_bytes(self.shape, self.dpol)
