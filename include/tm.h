@@ -168,8 +168,8 @@ typedef struct tm_qtensor {
  *   (run twice: FP16 on the pairs inside, INT8 on the rest), and the
  *   item's visible selected keys gathered into compact FP16 tiles of 64;
  *   selected keys are masked out of the regular tiles.  Lists are copied
- *   into the traversal buffer; tm_gather_selected fills the gathered tiles
- *   before tm_prefill.
+ *   into the traversal buffer and its tables built by one kernel;
+ *   tm_gather_selected fills the gathered tiles before tm_prefill.
  *  A tile is legal iff j*bk <= min((i+1)*bq, len) - 1; inside a legal tile key
  *  c is visible from row r iff c <= r. */
 typedef struct tm_policy {
@@ -272,6 +272,8 @@ typedef struct tm_dpolicy {
  *  the byte offsets of the tables below):
  *   sel table      nseq*hq x uint32[4] {list start, list length, first
  *                  gathered tile, first column-mask word};
+ *   sel off        nseq*hq + 1 int32: the list offsets, staged from host
+ *                  lists (unused with device lists);
  *   sel idx        the selected positions (int32);
  *   column masks   u64 per (sequence, query head, key tile): bit k set when
  *                  key 64j + k is selected (masked out of regular tiles);
@@ -329,14 +331,16 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
                              void* stream);
 
 /* Hybrid policies only: copy each selected key's 16-bit K row (from k
- * [T][hkv][d], device) and fp16 V column (from vq->t16, TM_COLS) into the
- * gathered tiles of a traversal built from `policy` for this shape.  Call
- * after tm_quantize_pack of V and before tm_prefill; K and V must not change
- * in between.  ([HyQuant] "How HyQuant works": selected tokens kept in FP16.)
+ * [T][hkv][d], device) and V row (from v [T][hkv][d], the same 16-bit V that
+ * tm_prefill's fp16 copy is made from: converted to fp16 the same way, bf16
+ * saturated to +-65504, and transposed) into the gathered tiles of a
+ * traversal built from `policy` for this shape.  Call after
+ * tm_build_traversal and before tm_prefill; K and V must not change in
+ * between.  ([HyQuant] "How HyQuant works": selected tokens kept in FP16.)
  * Errors: TM_E_ARG (NULL pointers, policy not hybrid), TM_E_SHAPE, TM_E_POLICY
  * (invalid lists), TM_E_HIP. */
 tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, void* trav,
-                             const void* k, const tm_qtensor* vq, void* stream);
+                             const void* k, const void* v, void* stream);
 
 /* Vertical-line token selection for the hybrid policies ([HyQuant] "The
  * observation behind the method" and "How HyQuant works": a few key positions

@@ -197,6 +197,7 @@ def test_hybrid_validation_and_size(B):
     end = align(align(align(256 + 2 * 16) + 32 * n_items) + 8 * n_items * 5)   # 5 runs per item
     n_gt = 1 + 2 + 0 + 1                                   # ceil(len / 64) per list
     end = align(end + 16 * 4)                              # list table
+    end = align(end + 4 * (4 + 1))                         # staged list offsets
     end = align(end + 4 * (3 + 70 + 0 + 1))                # positions
     end = align(end + 8 * (2 * 16 + 2 * 3))                # column masks: hq * nk per sequence
     end = align(end + 512 * n_gt)                          # gathered tile headers
@@ -228,13 +229,10 @@ def test_hybrid_validation_and_size(B):
     dv.c.sel_idx, dv.c.sel_idx_dev, dv.c.sel_off_dev = None, FAKE, FAKE
     assert st(dv) == B.TM_E_POLICY
     # gather: hybrid policies only, device pointers required
-    nb = s.nblk()
-    vq = _qt(B, 1, 1, nb, True)
-    assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(p.c), FAKE, None, ctypes.byref(vq), None) == \
-        B.TM_E_ARG
+    assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(p.c), FAKE, None, FAKE, None) == B.TM_E_ARG
+    assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(p.c), FAKE, FAKE, None, None) == B.TM_E_ARG
     b = B.Policy(dict(kind=0, b8=[1, 1], b4=[2, 2], sink=0))
-    assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(b.c), FAKE, FAKE, ctypes.byref(vq), None) == \
-        B.TM_E_ARG
+    assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(b.c), FAKE, FAKE, FAKE, None) == B.TM_E_ARG
 
 
 def test_traversal_capacity(B):

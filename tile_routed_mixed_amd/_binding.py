@@ -91,8 +91,7 @@ def lib():
         L.tm_build_traversal.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp,
                                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(tm_census), vp]
         L.tm_gather_selected.restype = i32
-        L.tm_gather_selected.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp, vp,
-                                         ctypes.POINTER(tm_qtensor), vp]
+        L.tm_gather_selected.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp, vp, vp, vp]
         L.tm_select_vertical.restype = i32
         L.tm_select_vertical.argtypes = [ctypes.POINTER(tm_shape), vp, vp, i32, ctypes.POINTER(ctypes.c_int32), i32,
                                          vp, vp, vp, ctypes.POINTER(ctypes.c_size_t), vp]
@@ -248,11 +247,11 @@ class Policy:
                 self.c.sel_idx = self.sel_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, vq: "QTensor", stream=None):
-    """Hybrid policies: copy the selected keys' K rows and V columns into the
-    traversal's gathered tiles."""
-    _check(lib().tm_gather_selected(ctypes.byref(shape.c), ctypes.byref(policy.c), _ptr(trav), _ptr(k),
-                                    ctypes.byref(vq.c), _stream(stream)), "tm_gather_selected")
+def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, v, stream=None):
+    """Hybrid policies: copy the selected keys' K rows and V columns (k, v:
+    [T][hkv][d] 16-bit device tensors) into the traversal's gathered tiles."""
+    _check(lib().tm_gather_selected(ctypes.byref(shape.c), ctypes.byref(policy.c), _ptr(trav), _ptr(k), _ptr(v),
+                                    _stream(stream)), "tm_gather_selected")
 
 
 def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bool = False, stream=None,

@@ -64,14 +64,8 @@ __global__ __launch_bounds__(256) void trav_items_kernel(TravArgs a) {
     h->item_off = a.item_off;
     h->run_off = a.run_off;
     h->bits_off = a.bits_off;
-    h->window = a.window;
-    h->n_gtiles = a.n_gtiles;
-    h->sel_tab_off = a.sel_tab_off;
-    h->sel_idx_off = a.sel_idx_off;
-    h->cm_off = a.cm_off;
-    h->gh_off = a.gh_off;
-    h->gk_off = a.gk_off;
-    h->gv_off = a.gv_off;
+    h->window = h->n_gtiles = 0u;   // (hybrid traversals come from hyb_build_kernel)
+    h->sel_tab_off = h->sel_idx_off = h->cm_off = h->gh_off = h->gk_off = h->gv_off = 0u;
   }
   if (k < static_cast<uint32_t>(a.nseq)) {
     SeqEntry* st = reinterpret_cast<SeqEntry*>(a.trav + a.seq_off);
@@ -109,32 +103,7 @@ __global__ __launch_bounds__(256) void trav_items_kernel(TravArgs a) {
   RunEntry* runs = reinterpret_cast<RunEntry*>(a.trav + a.run_off) + static_cast<size_t>(k) * a.max_runs;
   uint32_t nr = 0, n8 = 0, n4 = 0, n16 = 0;
 
-  if (a.kind == TM_POLICY_HYBRID) {
-    // window classes are contiguous in j: every causal (row, key) pair of key
-    // tile j lies within the window from jfull on, none of them before jedge
-    const int W = static_cast<int>(a.window);
-    const int r0 = qt * a.bq, rl = min((qt + 1) * a.bq, len) - 1;
-    auto fdiv = [](int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); };
-    const int jfull = min(legal, max(0, fdiv(rl - W, a.bk) + 1));
-    const int jedge = W > 0 ? min(jfull, max(0, fdiv(r0 - W - (a.bk - 1), a.bk) + 1)) : jfull;
-    const uint32_t ce = static_cast<uint32_t>(jfull - jedge);
-    put_run(runs, nr, jfull, static_cast<uint32_t>(legal - jfull), TM_FP16, a.max_runs);
-    put_run(runs, nr, jedge, ce, TM_FP16 | kRunEdge, a.max_runs);
-    put_run(runs, nr, jedge, ce, TM_INT8 | kRunEdge, a.max_runs);
-    put_run(runs, nr, 0, static_cast<uint32_t>(jedge), TM_INT8, a.max_runs);
-    // selected keys visible from this query tile (positions <= rl), gathered
-    const SelEntry se = reinterpret_cast<const SelEntry*>(a.trav + a.sel_tab_off)[seq * a.hq + head];
-    const int32_t* idx = reinterpret_cast<const int32_t*>(a.trav + a.sel_idx_off) + se.start;
-    uint32_t lo = 0, hi = se.count;                 // first entry > rl
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (idx[mid] <= rl) lo = mid + 1; else hi = mid;
-    }
-    const uint32_t ng = (lo + 63) / 64;
-    put_run(runs, nr, se.gbase, ng, TM_FP16 | kRunGather, a.max_runs);
-    n16 = static_cast<uint32_t>(legal - jfull) + ce + ng;
-    n8 = ce + static_cast<uint32_t>(jedge);
-  } else if (a.kind == TM_POLICY_BOUNDARIES) {
+  if (a.kind == TM_POLICY_BOUNDARIES) {
     const int b8 = a.b8[head], b4 = a.b4[head];
     const int ri = qt * (a.bq / a.bk);
     // INT8 band [lo8, jmax]; INT4 band [lo4, hi4]; SKIP [0, lo4)
@@ -251,7 +220,7 @@ __global__ __launch_bounds__(256) void trav_items_kernel(TravArgs a) {
   it->n8 = n8;
   it->n4 = n4;
   it->n16 = n16;
-  it->nskip = a.kind == TM_POLICY_HYBRID ? 0u : static_cast<uint32_t>(legal) - n8 - n4 - n16;
+  it->nskip = static_cast<uint32_t>(legal) - n8 - n4 - n16;
 }
 
 // Deterministic census: one workgroup sums the per-item counts.
@@ -282,20 +251,15 @@ __global__ __launch_bounds__(256) void trav_census_kernel(uint8_t* trav, uint32_
   }
 }
 
-// Selected-key tables from lists in device memory: one workgroup per list
-// (sequence s, head h of the list's kind).  It writes the list's table entry,
-// the column masks of every key tile of its sequence (bit k of tile j set
-// when key 64 j + k is listed), and the headers and positions of its
-// gathered tiles; a traversal also gets a copy of the positions.  The list's
-// first gathered tile and its sequence's first block are sums over the lists
-// and sequences before it, reduced by the workgroup.  The lists are meant to
-// be strictly increasing positions inside their sequence, as the selection
-// pass writes them; they are not checked, but a position outside the
-// sequence is written as INT32_MAX (an empty slot: never gathered, and past
-// every causal row) and no read or write leaves the buffers.
-__device__ __forceinline__ int2 list_span(const SelTabArgs& a, int r) {
-  const int32_t lo = min(max(a.off[r], 0), static_cast<int32_t>(a.n_sel));
-  const int32_t hi = min(max(a.off[r + 1], lo), static_cast<int32_t>(a.n_sel));
+// Position of entry e of a list, or INT32_MAX (an empty slot: never
+// gathered, and past every causal row) when it lies outside [0, len).
+__device__ __forceinline__ int32_t clean_pos(int32_t c, int len) { return (c >= 0 && c < len) ? c : INT32_MAX; }
+
+// A list's entries [lo, lo + n) of the positions, clamped to the n_sel
+// entries the buffers were sized for.
+__device__ __forceinline__ int2 list_span(const int32_t* off, int r, uint32_t n_sel) {
+  const int32_t lo = min(max(off[r], 0), static_cast<int32_t>(n_sel));
+  const int32_t hi = min(max(off[r + 1], lo), static_cast<int32_t>(n_sel));
   return make_int2(lo, hi - lo);
 }
 
@@ -308,40 +272,53 @@ __device__ __forceinline__ int block_sum256(int v, int* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// Exclusive prefix of v over the 256 threads of a workgroup; *total = sum.
+__device__ __forceinline__ int block_scan256(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = x;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) base += u < w ? red[u] : 0;
+  *total = red[0] + red[1] + red[2] + red[3];
+  return base + x - v;
+}
+
+// Decode selection tables from lists in device memory: one workgroup per list
+// (sequence s, KV head g).  It writes the list's entry {first gathered tile,
+// keys}, the column masks of its sequence's cache blocks (bit k of block j set
+// when key 64 j + k is listed) and the headers and positions of its gathered
+// tiles.  The list's first gathered tile and its sequence's first block are
+// sums over the lists and sequences before it, reduced by the workgroup.  The
+// lists are meant to be strictly increasing positions inside their sequence;
+// they are not checked, but a position outside the sequence becomes an empty
+// slot and no read or write leaves the buffers.
 __global__ __launch_bounds__(256) void sel_tables_kernel(SelTabArgs a) {
   __shared__ int red[4];
   const int r = blockIdx.x, tid = threadIdx.x;
-  const int s = r / a.lists_per_seq, h = r % a.lists_per_seq;
+  const int s = r / a.hkv, h = r % a.hkv;
   int blk = 0, gb = 0;
   for (int u = tid; u < s; u += 256) blk += (a.cu[u + 1] - a.cu[u] + kBlock - 1) / kBlock;
-  for (int u = tid; u < r; u += 256) gb += (list_span(a, u).y + kBlock - 1) / kBlock;
+  for (int u = tid; u < r; u += 256) gb += (list_span(a.off, u, a.n_sel).y + kBlock - 1) / kBlock;
   blk = block_sum256(blk, red);
   gb = min(block_sum256(gb, red), static_cast<int>(a.n_gt));
   const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0, nk = (len + kBlock - 1) / kBlock;
-  const int2 sp = list_span(a, r);
-  const int start = sp.x;
+  const int2 sp = list_span(a.off, r, a.n_sel);
   const int cnt = min(sp.y, (static_cast<int>(a.n_gt) - gb) * kBlock);
-  const int32_t* li = a.idx + start;
-  auto pos_of = [&](int e) {
-    const int32_t c = li[e];
-    return (c >= 0 && c < len) ? c : INT32_MAX;
-  };
-  const int cm_base = a.decode ? 0 : a.lists_per_seq * blk + h * nk;
+  const int32_t* li = a.idx + sp.x;
   if (tid == 0) {
     uint32_t* te = reinterpret_cast<uint32_t*>(a.buf + a.tab_off);
-    if (a.decode) {
-      te[2 * r] = static_cast<uint32_t>(gb);
-      te[2 * r + 1] = static_cast<uint32_t>(cnt);
-    } else {
-      reinterpret_cast<SelEntry*>(te)[r] = SelEntry{static_cast<uint32_t>(start), static_cast<uint32_t>(cnt),
-                                                    static_cast<uint32_t>(gb), static_cast<uint32_t>(cm_base)};
-    }
+    te[2 * r] = static_cast<uint32_t>(gb);
+    te[2 * r + 1] = static_cast<uint32_t>(cnt);
   }
-  if (!a.decode) {
-    int32_t* dst = reinterpret_cast<int32_t*>(a.buf + a.idx_off) + start;
-    for (int e = tid; e < cnt; e += 256) dst[e] = pos_of(e);
-  }
-  // column masks: the entries of key tile j are contiguous in a sorted list
+  // column masks: the entries of block j are contiguous in a sorted list
   uint64_t* cm = reinterpret_cast<uint64_t*>(a.buf + a.cm_off);
   for (int j = tid; j < nk; j += 256) {
     const int k0 = j * kBlock;
@@ -356,19 +333,18 @@ __global__ __launch_bounds__(256) void sel_tables_kernel(SelTabArgs a) {
       if (c < k0 || c >= k0 + kBlock) break;
       if (c < len) m |= uint64_t(1) << (c - k0);
     }
-    cm[a.decode ? static_cast<size_t>(blk + j) * a.hkv + h : static_cast<size_t>(cm_base) + j] = m;
+    cm[static_cast<size_t>(blk + j) * a.hkv + h] = m;
   }
   // gathered tiles: header {first token, first block, KV head, keys} and 64 positions
   const int ng = (cnt + kBlock - 1) / kBlock;
-  const uint32_t kv = static_cast<uint32_t>(h / a.grp);
   for (int u = tid; u < ng * kBlock; u += 256) {
     const int t = u / kBlock, k = u % kBlock;
     uint8_t* gh = a.buf + a.gh_off + static_cast<size_t>(gb + t) * kGatherHdr;
     const int keys = min(kBlock, cnt - kBlock * t);
     if (k == 0)
-      *reinterpret_cast<GatherEntry*>(gh) =
-          GatherEntry{static_cast<uint32_t>(tok0), static_cast<uint32_t>(blk), kv, static_cast<uint32_t>(keys)};
-    reinterpret_cast<int32_t*>(gh + 16)[k] = k < keys ? pos_of(kBlock * t + k) : INT32_MAX;
+      *reinterpret_cast<GatherEntry*>(gh) = GatherEntry{static_cast<uint32_t>(tok0), static_cast<uint32_t>(blk),
+                                                        static_cast<uint32_t>(h), static_cast<uint32_t>(keys)};
+    reinterpret_cast<int32_t*>(gh + 16)[k] = k < keys ? clean_pos(li[kBlock * t + k], len) : INT32_MAX;
   }
 }
 
@@ -378,9 +354,249 @@ hipError_t launch_sel_tables(const SelTabArgs& a, int n_lists, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Hybrid policies: fill gathered tile t with its selected keys' 16-bit K rows
-// ([64][D]) and fp16 V columns (V^T [D][64]); slots past the list, and empty
-// slots (position INT32_MAX), are zero.
+// Hybrid traversal in one launch: one workgroup per (sequence s, query head
+// h) list.  It writes the list entry {start, keys, first gathered tile, first
+// column-mask word}, the positions (copied in from device lists), the column
+// masks of the list's key tiles, the gathered-tile headers, and the work item
+// and runs of every query tile of (s, h) (sequence and traversal headers from
+// the first workgroups).  The column masks are built in LDS, kHybChunk key
+// tiles at a time, with a popcount prefix over them, so each query tile's
+// count of selected keys it can see (positions up to its last row) is read
+// off the prefix: no search over the list.  Item k of (s, h, query tile i)
+// keeps the heavy-first order of the other kinds (descending i, then
+// sequence, then head).  The window classes of a query tile (key tiles wholly
+// inside the window, crossed by its edge, wholly outside) are contiguous in
+// the key-tile index.  Lists are meant to be strictly increasing positions
+// inside their sequence (host lists are checked before the launch, device
+// lists are not); a position outside the sequence becomes an empty slot and
+// every write stays inside the sizes the host computed.
+constexpr int kHybChunk = 1024;
+
+__device__ __forceinline__ int fdiv_floor(int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); }
+
+__global__ __launch_bounds__(256) void hyb_build_kernel(HybArgs a) {
+  __shared__ int red[4];
+  __shared__ unsigned long long cml[kHybChunk];
+  __shared__ int cum[kHybChunk];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int s = r / a.hq, h = r % a.hq;
+  // first cache block of s; first gathered tile of list r
+  int blk = 0, gb = 0;
+  for (int u = tid; u < s; u += 256) blk += (a.cu[u + 1] - a.cu[u] + kBlock - 1) / kBlock;
+  for (int u = tid; u < r; u += 256) gb += (list_span(a.off, u, a.n_sel).y + kBlock - 1) / kBlock;
+  blk = block_sum256(blk, red);
+  gb = min(block_sum256(gb, red), static_cast<int>(a.n_gt));
+  const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
+  const int nk = (len + a.bk - 1) / a.bk, nq = (len + a.bq - 1) / a.bq;
+  const int2 sp = list_span(a.off, r, a.n_sel);
+  const int start = sp.x;
+  const int cnt = min(sp.y, (static_cast<int>(a.n_gt) - gb) * kBlock);
+  const int ng = (cnt + kBlock - 1) / kBlock;
+  const int cm_base = a.hq * blk + h * nk;
+  const int32_t* li = a.idx + start;
+  int32_t* dst = reinterpret_cast<int32_t*>(a.trav + a.sel_idx_off) + start;
+  if (tid == 0) {
+    reinterpret_cast<SelEntry*>(a.trav + a.sel_tab_off)[r] =
+        SelEntry{static_cast<uint32_t>(start), static_cast<uint32_t>(cnt), static_cast<uint32_t>(gb),
+                 static_cast<uint32_t>(cm_base)};
+    if (h == 0)
+      reinterpret_cast<SeqEntry*>(a.trav + a.seq_off)[s] =
+          SeqEntry{static_cast<uint32_t>(tok0), static_cast<uint32_t>(len), static_cast<uint32_t>(blk),
+                   static_cast<uint32_t>(nq)};
+    if (r == 0) {
+      TravHeader* th = reinterpret_cast<TravHeader*>(a.trav);
+      th->magic = TM_TRAV_MAGIC;
+      th->version = TM_TRAV_VERSION;
+      th->kind = TM_POLICY_HYBRID;
+      th->n_items = a.n_items;
+      th->max_runs = a.max_runs;
+      th->nseq = a.nseq;
+      th->hq = a.hq;
+      th->hkv = a.hkv;
+      th->bq = a.bq;
+      th->bk = a.bk;
+      th->d = a.d;
+      th->nblk = a.nblk;
+      th->seq_off = a.seq_off;
+      th->item_off = a.item_off;
+      th->run_off = a.run_off;
+      th->bits_off = 0;
+      th->window = a.window;
+      th->n_gtiles = a.n_gt;
+      th->sel_tab_off = a.sel_tab_off;
+      th->sel_idx_off = a.sel_idx_off;
+      th->cm_off = a.cm_off;
+      th->gh_off = a.gh_off;
+      th->gk_off = a.gk_off;
+      th->gv_off = a.gv_off;
+    }
+  }
+  if (a.copy_idx)
+    for (int e = tid; e < cnt; e += 256) dst[e] = clean_pos(li[e], len);
+  // gathered tiles: header {first token, first block, KV head, keys} and 64 positions
+  const uint32_t kv = static_cast<uint32_t>(h / (a.hq / a.hkv));
+  for (int u = tid; u < ng * kBlock; u += 256) {
+    const int t = u / kBlock, k = u % kBlock;
+    uint8_t* gh = a.trav + a.gh_off + static_cast<size_t>(gb + t) * kGatherHdr;
+    const int keys = min(kBlock, cnt - kBlock * t);
+    if (k == 0)
+      *reinterpret_cast<GatherEntry*>(gh) =
+          GatherEntry{static_cast<uint32_t>(tok0), static_cast<uint32_t>(blk), kv, static_cast<uint32_t>(keys)};
+    reinterpret_cast<int32_t*>(gh + 16)[k] = k < keys ? clean_pos(li[kBlock * t + k], len) : INT32_MAX;
+  }
+  // items at or above level x (query-tile index), over all sequences
+  auto items_from = [&](int x) {
+    int64_t n = 0;
+    for (int u = 0; u < a.nseq; ++u) {
+      const int q = (a.cu[u + 1] - a.cu[u] + a.bq - 1) / a.bq;
+      if (q > x) n += q - x;
+    }
+    return n * a.hq;
+  };
+  uint64_t* cm = reinterpret_cast<uint64_t*>(a.trav + a.cm_off) + cm_base;
+  const int W = static_cast<int>(a.window);
+  int carry = 0;   // selected keys in the chunks before this one
+  for (int j0 = 0; j0 < nk; j0 += kHybChunk) {
+    const int jn = min(kHybChunk, nk - j0);
+    for (int j = tid; j < kHybChunk; j += 256) cml[j] = 0ull;
+    __syncthreads();
+    for (int e = tid; e < cnt; e += 256) {
+      const int c = li[e];
+      const int j = (c >> 6) - j0;
+      if (c >= 0 && c < len && j >= 0 && j < jn) atomicOr(&cml[j], 1ull << (c & 63));
+    }
+    __syncthreads();
+    // masks out; inclusive popcount prefix (thread t owns tiles 4t .. 4t+3)
+    int pc[4], tsum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = 4 * tid + u;
+      const uint64_t m = j < jn ? cml[j] : 0ull;
+      if (j < jn) cm[j0 + j] = m;
+      pc[u] = __popcll(m);
+      tsum += pc[u];
+    }
+    int ctot;
+    int base = block_scan256(tsum, red, &ctot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      base += pc[u];
+      cum[4 * tid + u] = base;
+    }
+    __syncthreads();
+    // the query tiles whose last row falls in this chunk
+    for (int i = tid; i < nq; i += 256) {
+      const int r0 = i * a.bq, rl = min((i + 1) * a.bq, len) - 1;
+      const int jl = (rl >> 6) - j0;
+      if (jl < 0 || jl >= jn) continue;
+      const uint64_t lowm = (rl & 63) == 63 ? ~0ull : ((1ull << ((rl & 63) + 1)) - 1ull);
+      const int vis = carry + (jl > 0 ? cum[jl - 1] : 0) + __popcll(cml[jl] & lowm);
+      int rank = 0;
+      for (int u = 0; u < s; ++u) rank += (a.cu[u + 1] - a.cu[u] + a.bq - 1) / a.bq > i;
+      const uint32_t k = static_cast<uint32_t>(items_from(i + 1) + static_cast<int64_t>(rank) * a.hq + h);
+      if (k >= a.n_items) continue;
+      const int legal = rl / a.bk + 1;
+      const int jfull = min(legal, max(0, fdiv_floor(rl - W, a.bk) + 1));
+      const int jedge = W > 0 ? min(jfull, max(0, fdiv_floor(r0 - W - (a.bk - 1), a.bk) + 1)) : jfull;
+      const uint32_t ce = static_cast<uint32_t>(jfull - jedge);
+      const uint32_t ngi = static_cast<uint32_t>((min(vis, cnt) + kBlock - 1) / kBlock);
+      RunEntry* runs = reinterpret_cast<RunEntry*>(a.trav + a.run_off) + static_cast<size_t>(k) * a.max_runs;
+      uint32_t nr = 0;
+      put_run(runs, nr, static_cast<uint32_t>(jfull), static_cast<uint32_t>(legal - jfull), TM_FP16, a.max_runs);
+      put_run(runs, nr, static_cast<uint32_t>(jedge), ce, TM_FP16 | kRunEdge, a.max_runs);
+      put_run(runs, nr, static_cast<uint32_t>(jedge), ce, TM_INT8 | kRunEdge, a.max_runs);
+      put_run(runs, nr, 0u, static_cast<uint32_t>(jedge), TM_INT8, a.max_runs);
+      put_run(runs, nr, static_cast<uint32_t>(gb), ngi, TM_FP16 | kRunGather, a.max_runs);
+      ItemEntry* it = reinterpret_cast<ItemEntry*>(a.trav + a.item_off) + k;
+      it->seq = static_cast<uint32_t>(s);
+      it->head = static_cast<uint32_t>(h);
+      it->qtile = static_cast<uint32_t>(i);
+      it->nruns = nr;
+      it->n8 = ce + static_cast<uint32_t>(jedge);
+      it->n4 = 0u;
+      it->n16 = static_cast<uint32_t>(legal - jfull) + ce + ngi;
+      it->nskip = 0u;
+    }
+    carry += ctot;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_hybrid_build(const HybArgs& a, bool census, hipStream_t st) {
+  const int n_lists = a.nseq * a.hq;
+  if (n_lists <= 0) return hipSuccess;
+  hipLaunchKernelGGL(hyb_build_kernel, dim3(n_lists), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !census) return e;
+  hipLaunchKernelGGL(trav_census_kernel, dim3(1), dim3(256), 0, st, a.trav, a.item_off, a.n_items);
+  return hipGetLastError();
+}
+
+// Hybrid traversals: fill gathered tile t with its selected keys' 16-bit K
+// rows ([64][D]) and fp16 V columns (V^T [D][64]), both read from the
+// token-major 16-bit inputs (each key's row is contiguous; V is converted to
+// fp16, bf16 saturated to the fp16 range, and transposed through LDS).
+// Slots past the list and empty slots (position INT32_MAX) are zero.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int VP = D + 8;     // LDS row pitch (fp16): rows start on different banks
+  __shared__ _Float16 vl[kBlock * VP];
+  const uint32_t t = blockIdx.x;
+  const uint8_t* gh = a.trav + a.gh_off + static_cast<size_t>(t) * kGatherHdr;
+  const GatherEntry ge = *reinterpret_cast<const GatherEntry*>(gh);
+  const int32_t* pos = reinterpret_cast<const int32_t*>(gh + 16);
+  uint16_t* gk = reinterpret_cast<uint16_t*>(a.trav + a.gk_off) + static_cast<size_t>(t) * kBlock * D;
+  uint16_t* gv = reinterpret_cast<uint16_t*>(a.trav + a.gv_off) + static_cast<size_t>(t) * D * kBlock;
+  for (int u = threadIdx.x; u < kBlock * CPR; u += 256) {
+    const int row = u / CPR, ch = u % CPR;
+    u32x4 kx = u32x4{0u, 0u, 0u, 0u}, vx = u32x4{0u, 0u, 0u, 0u};
+    if (row < static_cast<int>(ge.keys) && pos[row] != INT32_MAX) {
+      const size_t off = ((static_cast<size_t>(ge.tok_start) + pos[row]) * a.hkv + ge.kv) * D + ch * 8;
+      kx = *reinterpret_cast<const u32x4*>(a.k + off);
+      vx = *reinterpret_cast<const u32x4*>(a.v + off);
+    }
+    *reinterpret_cast<u32x4*>(gk + row * D + ch * 8) = kx;
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (BF16) {
+        h[2 * e] = to_f16_sat(__uint_as_float(vx[e] << 16));
+        h[2 * e + 1] = to_f16_sat(__uint_as_float(vx[e] & 0xFFFF0000u));
+      } else {
+        h[2 * e] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(vx[e] & 0xFFFFu));
+        h[2 * e + 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(vx[e] >> 16));
+      }
+    }
+    *reinterpret_cast<f16x8*>(vl + row * VP + ch * 8) = h;
+  }
+  __syncthreads();
+  // V^T: channel rows of 64 slots, two slots per thread step
+  for (int u = threadIdx.x; u < D * (kBlock / 2); u += 256) {
+    const int c = u / (kBlock / 2), sl = 2 * (u % (kBlock / 2));
+    f16x2 pr;
+    pr[0] = vl[sl * VP + c];
+    pr[1] = vl[(sl + 1) * VP + c];
+    *reinterpret_cast<f16x2*>(gv + c * kBlock + sl) = pr;
+  }
+}
+
+hipError_t launch_gather_rows(const GatherArgs& a, int d, hipStream_t st) {
+  if (a.n_gtiles == 0) return hipSuccess;
+  if (d == 128) {
+    if (a.bf16) hipLaunchKernelGGL((gather_rows_kernel<128, true>), dim3(a.n_gtiles), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((gather_rows_kernel<128, false>), dim3(a.n_gtiles), dim3(256), 0, st, a);
+  } else {
+    if (a.bf16) hipLaunchKernelGGL((gather_rows_kernel<64, true>), dim3(a.n_gtiles), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((gather_rows_kernel<64, false>), dim3(a.n_gtiles), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+// Decode selection buffers: fill gathered tile t with its selected keys'
+// 16-bit K rows ([64][D]) and fp16 V columns (V^T [D][64], from the cache's
+// fp16 V^T copy); slots past the list, and empty slots (position INT32_MAX),
+// are zero.
 template <int D>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const uint32_t t = blockIdx.x;

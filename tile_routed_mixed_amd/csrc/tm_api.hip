@@ -72,14 +72,14 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct TravLayout {
   size_t seq_off, item_off, run_off, bytes;
-  size_t sel_tab_off = 0, sel_idx_off = 0, cm_off = 0, gh_off = 0, gk_off = 0, gv_off = 0;
+  size_t sel_tab_off = 0, sel_off_off = 0, sel_idx_off = 0, cm_off = 0, gh_off = 0, gk_off = 0, gv_off = 0;
   uint32_t max_runs;
 };
 
-// Hybrid policy tables, built on the host from the selected lists.
+// Sizes of a hybrid policy's tables (the tables themselves are built on the
+// GPU by hyb_build_kernel).
 struct HybridPlan {
-  std::vector<SelEntry> rows;   // per (sequence, query head)
-  int64_t n_sel = 0, n_gt = 0, n_cm = 0;
+  int64_t n_rows = 0, n_sel = 0, n_gt = 0, n_cm = 0;
 };
 
 // Lists on the device (sel_idx NULL, both device arrays set): the positions
@@ -93,7 +93,6 @@ tm_status hybrid_plan(const tm_shape* s, const tm_policy* p, HybridPlan* hp) {
   if (p->window < 0 || p->sel_off[0] != 0) return TM_E_POLICY;
   const bool dev = hybrid_dev_lists(p);
   const int64_t nr = static_cast<int64_t>(s->nseq) * s->hq;
-  hp->rows.assign(static_cast<size_t>(nr), SelEntry{0, 0, 0, 0});
   int64_t gt = 0, cm = 0;
   for (int sq = 0; sq < s->nseq; ++sq) {
     const int64_t len = s->cu_seqlens[sq + 1] - s->cu_seqlens[sq];
@@ -107,13 +106,11 @@ tm_status hybrid_plan(const tm_shape* s, const tm_policy* p, HybridPlan* hp) {
         const int64_t c = p->sel_idx[e];
         if (c < 0 || c >= len || (e > a && c <= p->sel_idx[e - 1])) return TM_E_POLICY;
       }
-      hp->rows[static_cast<size_t>(r)] =
-          SelEntry{static_cast<uint32_t>(a), static_cast<uint32_t>(b - a), static_cast<uint32_t>(gt),
-                   static_cast<uint32_t>(cm)};
       gt += (b - a + 63) / 64;
       cm += nk;
     }
   }
+  hp->n_rows = nr;
   hp->n_sel = p->sel_off[nr];
   hp->n_gt = gt;
   hp->n_cm = cm;
@@ -141,7 +138,9 @@ TravLayout trav_layout(const tm_shape* s, const ShapeInfo& si, const tm_policy* 
   if (p->kind == TM_POLICY_HYBRID) {
     const size_t d = static_cast<size_t>(s->d);
     L.sel_tab_off = end;
-    end = align256(end + sizeof(SelEntry) * hp->rows.size());
+    end = align256(end + sizeof(SelEntry) * static_cast<size_t>(hp->n_rows));
+    L.sel_off_off = end;
+    end = align256(end + 4 * static_cast<size_t>(hp->n_rows + 1));
     L.sel_idx_off = end;
     end = align256(end + 4 * static_cast<size_t>(hp->n_sel));
     L.cm_off = end;
@@ -155,38 +154,6 @@ TravLayout trav_layout(const tm_shape* s, const ShapeInfo& si, const tm_policy* 
   }
   L.bytes = end;
   return L;
-}
-
-// The hybrid tables staged on the host, in traversal order from sel_tab_off
-// to gk_off: list entries, positions, column masks, gathered-tile headers.
-std::vector<uint8_t> hybrid_tables(const tm_shape* s, const tm_policy* p, const HybridPlan& hp,
-                                   const TravLayout& L) {
-  std::vector<uint8_t> buf(L.gk_off - L.sel_tab_off, 0);
-  uint8_t* base = buf.data() - L.sel_tab_off;
-  std::memcpy(base + L.sel_tab_off, hp.rows.data(), sizeof(SelEntry) * hp.rows.size());
-  if (hp.n_sel > 0) std::memcpy(base + L.sel_idx_off, p->sel_idx, 4 * static_cast<size_t>(hp.n_sel));
-  uint64_t* cm = reinterpret_cast<uint64_t*>(base + L.cm_off);
-  const int grp = s->hq / s->hkv;
-  int64_t blk = 0;
-  for (int sq = 0; sq < s->nseq; ++sq) {
-    const int64_t len = s->cu_seqlens[sq + 1] - s->cu_seqlens[sq];
-    for (int h = 0; h < s->hq; ++h) {
-      const SelEntry& e = hp.rows[static_cast<size_t>(sq) * s->hq + h];
-      const int32_t* idx = p->sel_idx + e.start;
-      for (uint32_t u = 0; u < e.count; ++u) cm[e.cm_base + idx[u] / 64] |= uint64_t(1) << (idx[u] % 64);
-      for (uint32_t t = 0; t * 64 < e.count; ++t) {
-        uint8_t* gh = base + L.gh_off + static_cast<size_t>(e.gbase + t) * kGatherHdr;
-        const uint32_t keys = std::min<uint32_t>(64, e.count - 64 * t);
-        const GatherEntry ge{static_cast<uint32_t>(s->cu_seqlens[sq]), static_cast<uint32_t>(blk),
-                             static_cast<uint32_t>(h / grp), keys};
-        std::memcpy(gh, &ge, sizeof(ge));
-        int32_t* pos = reinterpret_cast<int32_t*>(gh + 16);
-        for (uint32_t k = 0; k < 64; ++k) pos[k] = k < keys ? idx[64 * t + k] : INT32_MAX;
-      }
-    }
-    blk += (len + 63) / 64;
-  }
-  return buf;
 }
 
 // Words of a bitmask (per_word = 32 one-bit codes) or four-way code map
@@ -417,45 +384,54 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (kind == TM_POLICY_HYBRID) {
-    a.window = static_cast<uint32_t>(policy->window);
-    a.n_gtiles = static_cast<uint32_t>(hp.n_gt);
-    a.sel_tab_off = static_cast<uint32_t>(L.sel_tab_off);
-    a.sel_idx_off = static_cast<uint32_t>(L.sel_idx_off);
-    a.cm_off = static_cast<uint32_t>(L.cm_off);
-    a.gh_off = static_cast<uint32_t>(L.gh_off);
-    a.gk_off = static_cast<uint32_t>(L.gk_off);
-    a.gv_off = static_cast<uint32_t>(L.gv_off);
+    HybArgs y;
+    y.trav = a.trav;
+    y.cu = shape->cu_seqlens_dev;
+    y.nseq = shape->nseq;
+    y.hq = shape->hq;
+    y.hkv = shape->hkv;
+    y.d = shape->d;
+    y.bq = shape->bq;
+    y.bk = shape->bk;
+    y.n_items = a.n_items;
+    y.max_runs = L.max_runs;
+    y.nblk = a.nblk;
+    y.seq_off = a.seq_off;
+    y.item_off = a.item_off;
+    y.run_off = a.run_off;
+    y.window = static_cast<uint32_t>(policy->window);
+    y.n_sel = static_cast<uint32_t>(hp.n_sel);
+    y.n_gt = static_cast<uint32_t>(hp.n_gt);
+    y.sel_tab_off = static_cast<uint32_t>(L.sel_tab_off);
+    y.sel_idx_off = static_cast<uint32_t>(L.sel_idx_off);
+    y.cm_off = static_cast<uint32_t>(L.cm_off);
+    y.gh_off = static_cast<uint32_t>(L.gh_off);
+    y.gk_off = static_cast<uint32_t>(L.gk_off);
+    y.gv_off = static_cast<uint32_t>(L.gv_off);
     if (hybrid_dev_lists(policy)) {
-      // lists in device memory: the tables are built by a kernel, no wait
-      SelTabArgs t;
-      t.buf = static_cast<uint8_t*>(trav);
-      t.cu = shape->cu_seqlens_dev;
-      t.off = policy->sel_off_dev;
-      t.idx = policy->sel_idx_dev;
-      t.lists_per_seq = shape->hq;
-      t.grp = shape->hq / shape->hkv;
-      t.hkv = shape->hkv;
-      t.decode = 0;
-      t.n_sel = static_cast<uint32_t>(hp.n_sel);
-      t.n_gt = static_cast<uint32_t>(hp.n_gt);
-      t.tab_off = static_cast<uint32_t>(L.sel_tab_off);
-      t.idx_off = static_cast<uint32_t>(L.sel_idx_off);
-      t.cm_off = static_cast<uint32_t>(L.cm_off);
-      t.gh_off = static_cast<uint32_t>(L.gh_off);
-      if (launch_sel_tables(t, static_cast<int>(hp.rows.size()), hs) != hipSuccess) return TM_E_HIP;
-    }
-    // host lists: stage the tables (pageable host memory: wait for the copy
-    // before the staging buffer goes away)
-    const std::vector<uint8_t> tab =
-        hybrid_dev_lists(policy) ? std::vector<uint8_t>() : hybrid_tables(shape, policy, hp, L);
-    if (!tab.empty()) {
-      if (hipMemcpyAsync(static_cast<uint8_t*>(trav) + L.sel_tab_off, tab.data(), tab.size(), hipMemcpyHostToDevice,
-                         hs) != hipSuccess)
+      // lists in device memory: read (and copied into the traversal) by the kernel, no wait
+      y.off = policy->sel_off_dev;
+      y.idx = policy->sel_idx_dev;
+      y.copy_idx = 1;
+    } else {
+      // host lists (checked above): stage the offsets and positions into the
+      // traversal (pageable host memory: wait for the copies before returning)
+      uint8_t* tb = static_cast<uint8_t*>(trav);
+      if (hipMemcpyAsync(tb + L.sel_off_off, policy->sel_off, 4 * static_cast<size_t>(hp.n_rows + 1),
+                         hipMemcpyHostToDevice, hs) != hipSuccess)
+        return TM_E_HIP;
+      if (hp.n_sel > 0 && hipMemcpyAsync(tb + L.sel_idx_off, policy->sel_idx, 4 * static_cast<size_t>(hp.n_sel),
+                                         hipMemcpyHostToDevice, hs) != hipSuccess)
         return TM_E_HIP;
       if (hipStreamSynchronize(hs) != hipSuccess) return TM_E_HIP;
+      y.off = reinterpret_cast<const int32_t*>(tb + L.sel_off_off);
+      y.idx = reinterpret_cast<const int32_t*>(tb + L.sel_idx_off);
+      y.copy_idx = 0;
     }
+    if (launch_hybrid_build(y, census != nullptr, hs) != hipSuccess) return TM_E_HIP;
+  } else if (launch_traversal(a, census != nullptr, hs) != hipSuccess) {
+    return TM_E_HIP;
   }
-  if (launch_traversal(a, census != nullptr, hs) != hipSuccess) return TM_E_HIP;
   if (census != nullptr) {
     TravHeader h;
     if (hipMemcpyAsync(&h, trav, sizeof(h), hipMemcpyDeviceToHost, hs) != hipSuccess) return TM_E_HIP;
@@ -472,12 +448,12 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
 }
 
 tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, void* trav, const void* k,
-                             const tm_qtensor* vq, void* stream) {
+                             const void* v, void* stream) {
   ShapeInfo si;
   tm_status st = check_shape(shape, true, &si);
   if (st != TM_OK) return st;
-  if (policy == nullptr || trav == nullptr || k == nullptr || policy->kind != TM_POLICY_HYBRID) return TM_E_ARG;
-  if ((st = check_qtensor(vq, shape->hkv, TM_COLS, si.nblk, true)) != TM_OK) return st;
+  if (policy == nullptr || trav == nullptr || k == nullptr || v == nullptr || policy->kind != TM_POLICY_HYBRID)
+    return TM_E_ARG;
   HybridPlan hp;
   if ((st = hybrid_plan(shape, policy, &hp)) != TM_OK) return st;
   const TravLayout L = trav_layout(shape, si, policy, &hp);
@@ -486,13 +462,15 @@ tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, voi
   GatherArgs g;
   g.trav = static_cast<uint8_t*>(trav);
   g.k = static_cast<const uint16_t*>(k);
-  g.vt16 = vq->t16;
+  g.vt16 = nullptr;
+  g.v = static_cast<const uint16_t*>(v);
   g.hkv = shape->hkv;
+  g.bf16 = shape->dtype == TM_BF16;
   g.n_gtiles = static_cast<uint32_t>(hp.n_gt);
   g.gh_off = static_cast<uint32_t>(L.gh_off);
   g.gk_off = static_cast<uint32_t>(L.gk_off);
   g.gv_off = static_cast<uint32_t>(L.gv_off);
-  return launch_gather(g, shape->d, static_cast<hipStream_t>(stream)) == hipSuccess ? TM_OK : TM_E_HIP;
+  return launch_gather_rows(g, shape->d, static_cast<hipStream_t>(stream)) == hipSuccess ? TM_OK : TM_E_HIP;
 }
 
 tm_status tm_select_vertical(const tm_shape* shape, const void* q, const void* k, int32_t n_obs,
@@ -692,7 +670,9 @@ tm_status tm_decode_select(const tm_shape* cache, const tm_dpolicy* policy, cons
   g.trav = static_cast<uint8_t*>(sel_buf);
   g.k = static_cast<const uint16_t*>(k16);
   g.vt16 = vq->t16;
+  g.v = nullptr;
   g.hkv = cache->hkv;
+  g.bf16 = cache->dtype == TM_BF16;
   g.n_gtiles = static_cast<uint32_t>(ds.n_gt);
   g.gh_off = static_cast<uint32_t>(ds.gh_off);
   g.gk_off = static_cast<uint32_t>(ds.gk_off);
@@ -705,14 +685,10 @@ tm_status tm_decode_select(const tm_shape* cache, const tm_dpolicy* policy, cons
     t.cu = cache->cu_seqlens_dev;
     t.off = policy->sel_off_dev;
     t.idx = policy->sel_idx_dev;
-    t.lists_per_seq = cache->hkv;
-    t.grp = 1;
     t.hkv = cache->hkv;
-    t.decode = 1;
     t.n_sel = static_cast<uint32_t>(policy->sel_off[static_cast<size_t>(cache->nseq) * cache->hkv]);
     t.n_gt = static_cast<uint32_t>(ds.n_gt);
     t.tab_off = static_cast<uint32_t>(ds.tab_off);
-    t.idx_off = 0;
     t.cm_off = static_cast<uint32_t>(ds.cm_off);
     t.gh_off = static_cast<uint32_t>(ds.gh_off);
     if (launch_sel_tables(t, cache->nseq * cache->hkv, hs) != hipSuccess) return TM_E_HIP;

@@ -40,9 +40,6 @@ struct TravArgs {
   int kind, sink, group;
   uint32_t n_items, max_runs, nblk;
   uint32_t seq_off, item_off, run_off, bits_off;
-  // hybrid policies (the tables are already in trav; the items kernel records
-  // the offsets in the header)
-  uint32_t window, n_gtiles, sel_tab_off, sel_idx_off, cm_off, gh_off, gk_off, gv_off;
   int32_t b8[kMaxHeadsArg];
   int32_t b4[kMaxHeadsArg];
 };
@@ -50,26 +47,42 @@ struct TravArgs {
 struct GatherArgs {
   uint8_t* trav;
   const uint16_t* k;        // [T][hkv][D] 16-bit
-  const uint16_t* vt16;     // [nblk][hkv][D][64] fp16
-  int hkv;
+  const uint16_t* vt16;     // [nblk][hkv][D][64] fp16 (decode selection buffers)
+  const uint16_t* v;        // [T][hkv][D] 16-bit (hybrid traversals), or null
+  int hkv, bf16;
   uint32_t n_gtiles, gh_off, gk_off, gv_off;
 };
 
-// Selected-key tables built on the GPU from device-resident lists (hybrid
-// traversals and decode selection buffers).  n_sel and n_gt are the list
-// entries and gathered tiles the host sized the buffer for: every write and
-// every list read stays below them whatever the device offsets hold.
+// Hybrid traversal, built in one launch from the selected lists: one
+// workgroup per (sequence, query head) list writes its list entry, positions,
+// column masks, gathered-tile headers and the work items and runs of every
+// query tile of that head (the TravArgs fields of the other kinds, plus the
+// list tables).  off / idx: list offsets and positions in device memory, or
+// the traversal's own staged copies (copy_idx = 0).
+struct HybArgs {
+  uint8_t* trav;
+  const int32_t* cu;
+  const int32_t* off;
+  const int32_t* idx;
+  int nseq, hq, hkv, d, bq, bk;
+  uint32_t n_items, max_runs, nblk;
+  uint32_t seq_off, item_off, run_off;
+  uint32_t window, n_sel, n_gt, sel_tab_off, sel_idx_off, cm_off, gh_off, gk_off, gv_off;
+  int copy_idx;
+};
+
+// Decode selection tables built on the GPU from device-resident lists (one
+// list per (sequence, KV head)).  n_sel and n_gt are the list entries and
+// gathered tiles the host sized the buffer for: every write and every list
+// read stays below them whatever the device offsets hold.
 struct SelTabArgs {
   uint8_t* buf;
   const int32_t* cu;        // device cu_seqlens
-  const int32_t* off;       // device list offsets [nseq * lists_per_seq + 1]
+  const int32_t* off;       // device list offsets [nseq * hkv + 1]
   const int32_t* idx;       // device positions
-  int lists_per_seq;        // hq (prefill: lists per query head) or hkv (decode)
-  int grp;                  // query heads per KV head (prefill), 1 (decode)
   int hkv;
-  int decode;               // 0: traversal tables; 1: decode selection buffer
   uint32_t n_sel, n_gt;
-  uint32_t tab_off, idx_off, cm_off, gh_off;
+  uint32_t tab_off, cm_off, gh_off;
 };
 
 struct PrefillArgs {
@@ -158,8 +171,10 @@ __device__ __forceinline__ int sel_tab(const SelectArgs& a, int which, int b) {
 hipError_t launch_quantize(const QuantArgs& a, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_append(const AppendArgs& p, int d, bool bf16, bool cols, hipStream_t st);
 hipError_t launch_traversal(const TravArgs& a, bool census, hipStream_t st);   // census: also sum the counts into the header
-hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);        // V from the fp16 V^T copy
+hipError_t launch_gather_rows(const GatherArgs& a, int d, hipStream_t st);   // V from 16-bit rows
 hipError_t launch_sel_tables(const SelTabArgs& a, int n_lists, hipStream_t st);
+hipError_t launch_hybrid_build(const HybArgs& a, bool census, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int d, int maxnt, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
 // boundary policies: the software-pipelined kernel (k_prefill_pipe.hip)

@@ -80,7 +80,7 @@ class PrefillPipeline:
         keys' K rows and V columns (after quantize())."""
         _, c = B.tm_build_traversal(self.shape, self.policy, self.trav, census=census, stream=stream)
         if self.policy.kind == B.TM_POLICY_HYBRID:
-            B.tm_gather_selected(self.shape, self.policy, self.trav, self.k, self.vq, stream)
+            B.tm_gather_selected(self.shape, self.policy, self.trav, self.k, self.v, stream)
         return c
 
     def prefill(self, o_dtype=B.TM_F32, dbg_tiles=None, stream=None, with_lse=True, dbg=None):
