@@ -121,11 +121,17 @@ def prefill_roofline(w, census, t_ms, traffic=None, hybrid=False):
                          "over the executed tiles of this workload"}
 
 
-def events_ms(fn, n):
+def events_ms(fn, n, queue_ahead=False):
     """Per-call times (ms) of n calls of fn, from HIP events recorded on the
-    current stream (the stream the library's kernels are launched on)."""
+    current stream (the stream the library's kernels are launched on).
+    queue_ahead: a spin kernel keeps the GPU busy while the host enqueues the
+    n calls, so that calls shorter than their host-side launch cost are timed
+    on the device (back to back, as behind a long prefill) rather than at the
+    host's pace."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    if queue_ahead:
+        torch.cuda._sleep(5_000_000)
     for a, b in ev:
         a.record()
         fn()
@@ -214,11 +220,12 @@ def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48):
         # back to back with no copy to the host and no wait
         pol = pp.vertical_policy(hybrid[0], hybrid[1], on_device=True)
         torch.cuda.synchronize()
-        sel = stats(events_ms(lambda: pp.vertical_policy(hybrid[0], hybrid[1], on_device=True), 7)[2:])
+        sel = stats(events_ms(lambda: pp.vertical_policy(hybrid[0], hybrid[1], on_device=True), 7,
+                              queue_ahead=True)[2:])
         pp.set_policy(pol)
         pp.traversal()
         torch.cuda.synchronize()
-        trv = stats(events_ms(lambda: pp.traversal(), 7)[2:])
+        trv = stats(events_ms(lambda: pp.traversal(), 7, queue_ahead=True)[2:])
         n_sel = int(pol["sel_off"][-1])
         pol_host = dict(kind=pol["kind"], window=pol["window"], sel_off=pol["sel_off"],
                         sel_idx=pol["sel_idx_dev"][:n_sel].cpu().numpy())   # for the oracle, untimed
@@ -241,7 +248,8 @@ def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48):
         res["selection_plus_traversal_frac_of_prefill"] = (sel["mean"] + trv["mean"]) / t["mean"]
         res["selection_note"] = ("tm_select_vertical (lists left in device memory), then tm_build_traversal and "
                                  "tm_gather_selected on those lists: no host copy, no stream wait; event-timed "
-                                 "on the launch stream")
+                                 "on the launch stream, enqueued behind a spin kernel so that the device time "
+                                 "is measured, not the host's launch pace")
         pol = pol_host
     if fp64_rows:
         res["fp64_error"] = prefill_fp64_error(w, pol, pp, q, k, v, fp64_rows)

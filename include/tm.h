@@ -348,7 +348,8 @@ tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, voi
  * attention-pattern signals).  For every (sequence s, query head h) the
  * attention mass each key receives from the last min(n_obs, len_s) query rows
  * (softmax over each row's keys of scale * q . k on the 16-bit values, fp32):
- *   mass[t][h] (device float [T][hq], written).
+ *   mass[h][t] (device float [hq][T], written; head-major, so that a list's
+ *   keys are contiguous).
  * sel_idx (device int32, may be NULL): the counts[s] keys of largest mass of
  * each list, ascending (ties to the lower position); lists are per query head
  * (per_kv_head = 0: mass of the head) or per KV head (per_kv_head = 1: mass

@@ -33,7 +33,7 @@ def _run(w, n_obs, counts, per_kv):
     g = Guards()
     nl = w.hkv if per_kv else w.hq
     total = nl * int(np.sum(counts))
-    mass_out = g.alloc((shape.T, w.hq), torch.float32, float("nan"))
+    mass_out = g.alloc((w.hq, shape.T), torch.float32, float("nan"))
     sel_out = g.alloc((max(total, 1),), torch.int32, -1)
     mass, off, idx = T.tm_select_vertical(shape, dq, dk, n_obs, counts, per_kv, mass_out=mass_out, sel_out=sel_out)
     torch.cuda.synchronize()
@@ -53,7 +53,7 @@ def _check(w, qkv, mass, off, idx, n_obs, counts, per_kv):
         for h in range(w.hq):
             ref = OP.vline_importance(q[1][cu[s]:cu[s + 1], h].astype(np.float64),
                                       k[1][cu[s]:cu[s + 1], h // grp].astype(np.float64), n_obs, tau)
-            got = mass[cu[s]:cu[s + 1], h]
+            got = mass[h, cu[s]:cu[s + 1]]
             assert np.all(np.abs(got - ref) <= 1e-5 + 1e-4 * ref), (s, h, float(np.abs(got - ref).max()))
             imps.append(ref)
         for g in range(nl):
@@ -80,6 +80,13 @@ def _check(w, qkv, mass, off, idx, n_obs, counts, per_kv):
     ("varlen32k", [129, 1], dict(hq=2, hkv=2), 64, 1.0, False),
     # more sequences than the kernel arguments carry: the table is staged
     ("varlen32k", [1 + (37 * i) % 150 for i in range(70)], dict(hq=2, hkv=1), 16, 0.1, True),
+    # 8 query heads per KV head: two workgroups of 4 heads share its keys
+    ("gqa8k", [300, 2000, 77], dict(hq=8, hkv=1), 64, 0.05, False),
+    # 3 query heads per KV head: one head per workgroup, lists summed over 3
+    ("gqa8k", [500, 1300], dict(hq=3, hkv=1), 33, 0.1, True),
+    # a sequence long enough for several key tiles per workgroup, and a list
+    # longer than the top-k holds in registers
+    ("long128k", [70000], dict(hq=4, hkv=1, d=64), 64, 0.02, False),
 ])
 def test_vertical_selection(name, seqlens, kw, n_obs, frac, per_kv):
     w = W.small(name, seqlens, **kw)
@@ -127,3 +134,27 @@ def test_pipeline_selection_buffers_follow_the_sizes():
         counts = [int(round(f * S)) for S in w.seqlens]
         _, off, idx = T.tm_select_vertical(pp.shape, pp.q, pp.k, 64, counts, False)
         assert np.array_equal(pol["sel_off"], off) and np.array_equal(pol["sel_idx"], idx), f
+
+
+def test_selection_ties_go_to_lower_positions():
+    """Zero keys: every probe row spreads its attention evenly, so all keys up
+    to the first probe row receive exactly the same mass (each the same sum
+    of the same terms) and the later ones less; the lists must be the first
+    counts[s] positions."""
+    import torch
+    import tile_routed_mixed_amd as T
+    w = W.small("gqa8k", [900, 200], hq=4, hkv=1)
+    q, _, _ = W.make_qkv(w)
+    shape = T.Shape(w.seqlens, w.hq, w.hkv, w.d, w.bq, 64, T.TM_BF16 if w.dtype == "bf16" else T.TM_F16,
+                    device="cuda:0")
+    dq = torch.from_numpy(q[0].view(np.int16).copy()).to("cuda:0")
+    dk = torch.zeros((shape.T, w.hkv, w.d), dtype=torch.int16, device="cuda:0")
+    counts = [100, 20]
+    say("[gpu] selection ties on zero keys")
+    for per_kv in (False, True):
+        _, off, idx = T.tm_select_vertical(shape, dq, dk, 64, counts, per_kv)
+        nl = w.hkv if per_kv else w.hq
+        for s, c in enumerate(counts):
+            for g in range(nl):
+                r = s * nl + g
+                assert np.array_equal(idx[off[r]:off[r + 1]], np.arange(c)), (per_kv, s, g)

@@ -257,14 +257,14 @@ def tm_gather_selected(shape: "Shape", policy: Policy, trav, k, v, stream=None):
 def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bool = False, stream=None,
                        cache: Optional[dict] = None, mass_out=None, sel_out=None, on_device: bool = False):
     """Attention mass of each key from the last n_obs query rows, and the
-    counts[s] keys of largest mass per list.  Returns (mass [T][hq] float32
+    counts[s] keys of largest mass per list.  Returns (mass [hq][T] float32
     device tensor, sel_off (host int32), sel_idx (host int32)): the index
     lists of a hybrid prefill policy (per query head) or of a decode selection
     (per KV head).  on_device: sel_idx is the int32 device tensor the kernel
     wrote (its first sel_off[-1] entries), with no copy to the host and no
     wait.  `cache` (a dict the caller keeps) holds the workspace and
     output buffers between calls of the same sizes; a returned mass tensor (or
-    device list) is then overwritten by the next call.  mass_out ([T][hq]
+    device list) is then overwritten by the next call.  mass_out ([hq][T]
     float32) and sel_out (int32, at least the lists' total length) are caller
     buffers to write instead of the cached or new ones."""
     import torch
@@ -281,7 +281,7 @@ def tm_select_vertical(shape: "Shape", q, k, n_obs: int, counts, per_kv_head: bo
                                         None, None, ctypes.byref(n), None), "tm_select_vertical(size)")
         dev = q.device
         ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
-        mass = torch.empty((shape.T, shape.hq), dtype=torch.float32, device=dev)
+        mass = torch.empty((shape.hq, shape.T), dtype=torch.float32, device=dev)
         sel = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
         if cache is not None:
             cache.clear()

@@ -8,160 +8,256 @@
 // each key receives from the last n_obs query rows of its sequence (16-bit
 // scores, fp32 arithmetic); the k keys of largest mass are selected.
 //
-// Passes 1 and 3 run one wave per (key tile of 64, sequence, query head), so a
-// sequence of S tokens spreads over S/64 x hq waves; their probe scores come
-// from the matrix cores (recomputed in pass 3, cheaper than storing them):
+// Passes 1 and 3 run one workgroup per (run of key tiles of 64, sequence, KV
+// head, up to 4 of its query heads): the query heads of a KV head share each
+// key tile, staged once through LDS.  The probe scores come from the matrix
+// cores (recomputed in pass 3, cheaper than storing them):
 //   1. probe scores of the tile's keys -> per probe row a partial (max, sum);
 //   2. (one workgroup per (sequence, head)) partials -> each row's (m, l);
 //   3. probe scores again -> mass of each key, sum over the probe rows of
 //      exp(s - m) / l.
 // Then a top-k pass per list: an MSB-first radix select on the (non-negative)
 // float bits finds the k-th largest mass; keys above it, and the lowest
-// positions among those equal to it, are written in ascending order.
+// positions among those equal to it, are written in ascending order.  Masses
+// are stored head-major ([hq][T]): pass 3 stores a tile's 64 keys in one
+// coalesced write and a list's keys are contiguous for the top-k.
 #include "tm_kernels.h"
 
 namespace tmx {
 
 constexpr int kProbe = 64;   // most probe rows per sequence
 
-// One wave's probe scores: all probe rows of (sequence b, head h) against the
-// 64 keys of tile j, on the matrix cores, S^T = K Q^T with
-// v_mfma_f32_16x16x32_{f16,bf16}.  The Q operands (the probe rows, B columns)
-// are loaded once per wave by probe_q and serve every tile the wave takes;
-// the tile's 4 blocks of 16 keys are the A rows, loaded straight from global
-// memory.  Lane (l16, g) gets probe row 16qb + l16 and key 16kb + 4g + i in
-// s[kb][qb][i] (log2 units); keys past the row (causal) or the sequence end,
-// and rows past the probe, score -inf.
-template <int D, bool BF16>
-struct ProbeQ {
-  typedef typename std::conditional<BF16, bf16x8, f16x8>::type op_t;
-  static constexpr int NC = D / 32;
-  op_t q[4][NC];
-};
-
 struct ProbeSeq {
-  int tok0, len, nobs, r0, kv;
+  int tok0, len, nobs, r0;
 };
 
-__device__ __forceinline__ ProbeSeq probe_seq(const SelectArgs& a, int b, int h) {
+__device__ __forceinline__ ProbeSeq probe_seq(const SelectArgs& a, int b) {
   ProbeSeq p;
   p.tok0 = a.cu[b];
   p.len = a.cu[b + 1] - p.tok0;
   p.nobs = min(a.n_obs, p.len);
   p.r0 = p.len - p.nobs;
-  p.kv = h / (a.hq / a.hkv);
   return p;
 }
 
-template <int D, bool BF16>
-__device__ __forceinline__ void probe_q(const SelectArgs& a, const ProbeSeq& ps, int h, ProbeQ<D, BF16>& pq) {
+// Work split of passes 1 and 3.  A workgroup of 4 waves takes QB query heads
+// of one KV head (they share its keys) and a.tw consecutive key tiles of one
+// sequence; each wave computes QB blocks of 16 probe rows of one head, so a
+// head's 64 probe rows span 4 / QB waves.  Each key tile is staged once
+// through LDS for all the waves, double-buffered: the next tile's loads are
+// in flight while the current one is multiplied.
+constexpr int kProbeThreads = 256;
+
+template <int D>
+struct KTile {
+  static constexpr int PITCH = 2 * D + 16;               // bytes per key row: the padding puts the
+                                                          // 16 rows of an operand read in distinct banks
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  static constexpr int PER = 64 * CPR / kProbeThreads;   // chunks per thread
+  static constexpr int BYTES = 64 * PITCH;
+};
+
+// loads of key tile j (keys past the sequence end read as zeros)
+template <int D>
+__device__ __forceinline__ void ktile_load(const SelectArgs& a, const ProbeSeq& ps, int kv, int j,
+                                           u32x4 (&r)[KTile<D>::PER]) {
+#pragma unroll
+  for (int u = 0; u < KTile<D>::PER; ++u) {
+    const int i = static_cast<int>(threadIdx.x) + kProbeThreads * u;
+    const int row = i / KTile<D>::CPR, col = i % KTile<D>::CPR, key = j * kBlock + row;
+    r[u] = u32x4{0u, 0u, 0u, 0u};
+    if (key < ps.len)
+      r[u] = *reinterpret_cast<const u32x4*>(a.k + (static_cast<size_t>(ps.tok0 + key) * a.hkv + kv) * D + 8 * col);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void ktile_store(uint8_t* buf, const u32x4 (&r)[KTile<D>::PER]) {
+#pragma unroll
+  for (int u = 0; u < KTile<D>::PER; ++u) {
+    const int i = static_cast<int>(threadIdx.x) + kProbeThreads * u;
+    *reinterpret_cast<u32x4*>(buf + (i / KTile<D>::CPR) * KTile<D>::PITCH + 16 * (i % KTile<D>::CPR)) = r[u];
+  }
+}
+
+// A wave's probe-row operands: rows 16 (qb0 + q) + l16, q < QB, of head h
+// (rows past the probe are zeros), loaded once for all the wave's tiles.
+template <int D, bool BF16, int QB>
+struct ProbeQ {
+  typedef typename std::conditional<BF16, bf16x8, f16x8>::type op_t;
+  static constexpr int NC = D / 32;
+  op_t q[QB][NC];
+};
+
+template <int D, bool BF16, int QB>
+__device__ __forceinline__ void probe_q(const SelectArgs& a, const ProbeSeq& ps, int h, int qb0,
+                                        ProbeQ<D, BF16, QB>& pq) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const int row = 16 * qb + l16;
+  for (int q = 0; q < QB; ++q) {
+    const int row = 16 * (qb0 + q) + l16;
 #pragma unroll
-    for (int c = 0; c < ProbeQ<D, BF16>::NC; ++c) {
+    for (int c = 0; c < ProbeQ<D, BF16, QB>::NC; ++c) {
       u32x4 raw = u32x4{0u, 0u, 0u, 0u};
       if (row < ps.nobs)
         raw = *reinterpret_cast<const u32x4*>(a.q + (static_cast<size_t>(ps.tok0 + ps.r0 + row) * a.hq + h) * D +
                                               32 * c + 8 * g);
-      __builtin_memcpy(&pq.q[qb][c], &raw, 16);
+      __builtin_memcpy(&pq.q[q][c], &raw, 16);
     }
   }
 }
 
-template <int D, bool BF16>
-__device__ __forceinline__ void probe_scores(const SelectArgs& a, const ProbeSeq& ps, const ProbeQ<D, BF16>& pq, int j,
-                                             f32x4 (&s)[4][4]) {
-  typedef typename ProbeQ<D, BF16>::op_t op_t;
-  constexpr int NC = ProbeQ<D, BF16>::NC;
+// One wave's raw probe products (no scale, no mask) with the staged key tile,
+// on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}).  The same registers
+// serve as either operand, so the product comes in either orientation:
+//   TRANS: S^T = K Q^T, lane (l16, g) holds probe row 16 (qb0 + q) + l16 and
+//          keys 16 kb + 4 g + i in s[kb][q][i] (a row's keys in the lane: row
+//          statistics reduce in registers);
+//   else:  S = Q K^T, lane (l16, g) holds key 16 kb + l16 and probe rows
+//          16 (qb0 + q) + 4 g + i (a key's rows in the lane: column sums
+//          reduce in registers).
+template <int D, bool BF16, int QB, bool TRANS>
+__device__ __forceinline__ void probe_raw(const uint8_t* buf, const ProbeQ<D, BF16, QB>& pq, f32x4 (&s)[4][QB]) {
+  typedef typename ProbeQ<D, BF16, QB>::op_t op_t;
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-  u32x4 kraw[4][NC];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int q = 0; q < QB; ++q) s[kb][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the next block of 16 keys' operands is read from LDS while the current
+  // block's products run
+  constexpr int NC = ProbeQ<D, BF16, QB>::NC;
+  const uint8_t* base = buf + l16 * KTile<D>::PITCH + 16 * g;
+  u32x4 kr[2][NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kr[0][c] = *reinterpret_cast<const u32x4*>(base + 64 * c);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const int key = j * kBlock + 16 * kb + l16;
+    if (kb + 1 < 4) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kraw[kb][c] = u32x4{0u, 0u, 0u, 0u};
-      if (key < ps.len)
-        kraw[kb][c] = *reinterpret_cast<const u32x4*>(a.k + (static_cast<size_t>(ps.tok0 + key) * a.hkv + ps.kv) * D +
-                                                      32 * c + 8 * g);
+      for (int c = 0; c < NC; ++c)
+        kr[(kb + 1) & 1][c] = *reinterpret_cast<const u32x4*>(base + 16 * (kb + 1) * KTile<D>::PITCH + 64 * c);
     }
-  }
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       op_t kop;
-      __builtin_memcpy(&kop, &kraw[kb][c], 16);
+      __builtin_memcpy(&kop, &kr[kb & 1][c], 16);
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        if constexpr (BF16) s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, pq.q[qb][c], s[kb][qb], 0, 0, 0);
-        else s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, pq.q[qb][c], s[kb][qb], 0, 0, 0);
+      for (int q = 0; q < QB; ++q) {
+        const op_t& x = TRANS ? kop : pq.q[q][c];
+        const op_t& y = TRANS ? pq.q[q][c] : kop;
+        if constexpr (BF16) s[kb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, s[kb][q], 0, 0, 0);
+        else s[kb][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, s[kb][q], 0, 0, 0);
       }
     }
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * qb + l16, key = j * kBlock + 16 * kb + 4 * g + i;
-        const bool ok = row < ps.nobs && key <= ps.r0 + row && key < ps.len;
-        s[kb][qb][i] = ok ? s[kb][qb][i] * a.tau_log2e : -INFINITY;
-      }
+  }
 }
 
-// Passes 1 and 3 give each wave kTilesPerWave consecutive key tiles (the
-// probe rows' operands are loaded once for all of them): workgroup x covers
-// tiles 4 kTilesPerWave x onwards of (sequence z, head y).
-constexpr int kProbeWaves = 4;
-constexpr int kTilesPerWave = 2;
+// A key tile needs the (row, key) mask when some of its keys lie after the
+// first probe row or past the sequence end, or the probe is shorter than 64
+// rows; the other tiles are whole for every probe row.
+__device__ __forceinline__ bool probe_tile_masked(const ProbeSeq& ps, int j) {
+  return j * kBlock + kBlock - 1 > ps.r0 || j * kBlock + kBlock > ps.len || ps.nobs < kProbe;
+}
 
-// pass 1: per (row, tile) partial max and sum (log2 units)
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void probe_partial_kernel(SelectArgs a) {
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int j0 = (blockIdx.x * kProbeWaves + (threadIdx.x >> 6)) * kTilesPerWave;
-  const ProbeSeq ps = probe_seq(a, b, h);
-  if (j0 * kBlock >= ps.len) return;   // whole wave
-  ProbeQ<D, BF16> pq;
-  probe_q<D, BF16>(a, ps, h, pq);
-  const int lane = threadIdx.x & 63, l16 = lane & 15;
-  for (int j = j0; j < j0 + kTilesPerWave && j * kBlock < ps.len; ++j) {
-    f32x4 s[4][4];
-    probe_scores<D, BF16>(a, ps, pq, j, s);
-    float* dst = a.part + ((static_cast<size_t>(sel_tab(a, 0, b)) + j) * a.hq + h) * (2 * kProbe);
+// max and sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (one row's lane groups)
+__device__ __forceinline__ float probe_max4(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float probe_sum4(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The workgroup's place: sequence b, KV head kv, the wave's head h and first
+// row block qb0, its tiles [j0, jn).  Returns false for a workgroup past the
+// sequence's tiles.
+struct ProbeWork {
+  int b, kv, h, qb0, j0, jn;
+  ProbeSeq ps;
+};
+template <int QB>
+__device__ __forceinline__ bool probe_work(const SelectArgs& a, ProbeWork& pw) {
+  const int grp = a.hq / a.hkv, wph = 4 / QB, w = threadIdx.x >> 6;
+  pw.b = blockIdx.z;
+  pw.kv = blockIdx.y / (grp / QB);
+  pw.h = pw.kv * grp + (blockIdx.y % (grp / QB)) * QB + w / wph;
+  pw.qb0 = (w % wph) * QB;
+  pw.ps = probe_seq(a, pw.b);
+  pw.j0 = blockIdx.x * a.tw;
+  pw.jn = min(pw.j0 + a.tw, (pw.ps.len + kBlock - 1) / kBlock);
+  return pw.j0 < pw.jn;
+}
+
+// pass 1: per (row, tile) partial max and sum (log2 units), from S^T
+template <int D, bool BF16, int QB>
+__global__ __launch_bounds__(kProbeThreads, 2) void probe_partial_kernel(SelectArgs a) {
+  ProbeWork pw;
+  if (!probe_work<QB>(a, pw)) return;   // whole workgroup
+  const ProbeSeq& ps = pw.ps;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KTile<D>::BYTES];
+  // the probe rows' loads go first: the wait before the first tile's LDS
+  // store then covers them, and no load in the loop waits behind them
+  ProbeQ<D, BF16, QB> pq;
+  probe_q<D, BF16, QB>(a, ps, pw.h, pw.qb0, pq);
+  u32x4 pre[KTile<D>::PER];
+  ktile_load<D>(a, ps, pw.kv, pw.j0, pre);
+  ktile_store<D>(kbuf[0], pre);
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  const float tau = a.tau_log2e;
+  // (uniform: kept in scalar registers, so no vector load in the loop waits
+  // on the next tile's loads)
+  const int tile0 = __builtin_amdgcn_readfirstlane(sel_tab(a, 0, pw.b));
+  for (int j = pw.j0; j < pw.jn; ++j) {
+    __syncthreads();   // tile j staged; every wave is done with the other buffer
+    const bool more = j + 1 < pw.jn;
+    if (more) ktile_load<D>(a, ps, pw.kv, j + 1, pre);
+    f32x4 s[4][QB];
+    probe_raw<D, BF16, QB, true>(kbuf[(j - pw.j0) & 1], pq, s);
+    if (probe_tile_masked(ps, j)) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      // row 16qb + l16: 16 keys in the lane, the rest in lanes l16 + 16, 32, 48
-      float m = s[0][qb][0];
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 1; e < 16; ++e) m = fmaxf(m, s[e >> 2][qb][e & 3]);
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
+        for (int q = 0; q < QB; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * (pw.qb0 + q) + l16, key = j * kBlock + 16 * kb + 4 * g + i;
+            if (!(row < ps.nobs && key <= ps.r0 + row && key < ps.len)) s[kb][q][i] = -INFINITY;
+          }
+    }
+    float* dst = a.part + ((static_cast<size_t>(tile0) + j) * a.hq + pw.h) * (2 * kProbe);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      // row 16 (qb0 + q) + l16: 16 products in the lane, the rest in lanes l16 + 16, 32, 48
+      float m = fmaxf(fmaxf(s[0][q][0], s[0][q][1]), s[0][q][2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2) m = fmaxf(fmaxf(m, s[e >> 2][q][e & 3]), s[(e + 1) >> 2][q][(e + 1) & 3]);
+      m = fmaxf(m, s[3][q][3]);
+      m = probe_max4(m) * tau;   // (tau > 0: the maximum of the scaled scores)
       float l = 0.0f;
       if (m > -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) l += __builtin_amdgcn_exp2f(s[e >> 2][qb][e & 3] - m);
+        for (int e = 0; e < 16; ++e) l += __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][q][e & 3], tau, -m));
       }
-      l += __shfl_xor(l, 16, 64);
-      l += __shfl_xor(l, 32, 64);
-      const int row = 16 * qb + l16;
+      l = probe_sum4(l);
+      const int row = 16 * (pw.qb0 + q) + l16;
       if (lane < 16 && row < ps.nobs) {
         dst[2 * row] = m;
         dst[2 * row + 1] = l;
       }
     }
+    if (more) ktile_store<D>(kbuf[(j + 1 - pw.j0) & 1], pre);
   }
 }
 
 // pass 2: each probe row's (m, l) over all tiles; thread (row, q) merges the
-// tiles q, q + 16, ..., then the 16 parts are merged through LDS
+// tiles q, q + 16, ..., then the 16 parts are merged through LDS.  Stored as
+// (m, log2 l), the pair pass 3 subtracts.
 constexpr int kRowParts = 16;
 __global__ __launch_bounds__(64 * kRowParts) void probe_rows_kernel(SelectArgs a) {
   const int b = blockIdx.y, h = blockIdx.x;
@@ -200,238 +296,278 @@ __global__ __launch_bounds__(64 * kRowParts) void probe_rows_kernel(SelectArgs a
     for (int u = 0; u < kRowParts; ++u) merge(sm[u][r], sl[u][r]);
     float* dst = a.rows + (static_cast<size_t>(b) * a.hq + h) * (2 * kProbe) + 2 * r;
     dst[0] = M;
-    dst[1] = L;
+    dst[1] = M > -INFINITY ? __builtin_amdgcn_logf(L) : 0.0f;
   }
 }
 
-// pass 3: mass of each key of tile j: the sum over the probe rows of
-// exp2(s - m) / l, first over the lane's 4 rows, then across the 16 lanes of
-// each lane group
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void probe_mass_kernel(SelectArgs a) {
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int j0 = (blockIdx.x * kProbeWaves + (threadIdx.x >> 6)) * kTilesPerWave;
-  const ProbeSeq ps = probe_seq(a, b, h);
-  if (j0 * kBlock >= ps.len) return;   // whole wave
-  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-  float m[4], inv[4];
-  const float* st = a.rows + (static_cast<size_t>(b) * a.hq + h) * (2 * kProbe);
+// pass 3: mass of each key of tile j, the sum over the probe rows of
+// exp2(tau s - m - log2 l), from S = Q K^T: a lane holds one key's products
+// with 4 QB of the rows, summed in registers, then over the 4 lane groups;
+// with QB < 4 the 4 / QB waves of a head add their sums through LDS
+template <int D, bool BF16, int QB>
+__global__ __launch_bounds__(kProbeThreads, 2) void probe_mass_kernel(SelectArgs a) {
+  ProbeWork pw;
+  if (!probe_work<QB>(a, pw)) return;   // whole workgroup
+  const ProbeSeq& ps = pw.ps;
+  constexpr int wph = 4 / QB;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KTile<D>::BYTES];
+  __shared__ float part[wph > 1 ? 4 : 1][64];
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4, w = threadIdx.x >> 6;
+  // the lane's rows 16 (qb0 + q) + 4 g + i: bias -(m + log2 l), -inf past the probe
+  float bias[QB][4];
+  const float* st = a.rows + (static_cast<size_t>(pw.b) * a.hq + pw.h) * (2 * kProbe);
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const int row = 16 * qb + l16;
-    m[qb] = 0.0f;
-    inv[qb] = 0.0f;
-    if (row < ps.nobs) {
-      m[qb] = st[2 * row];
-      inv[qb] = 1.0f / st[2 * row + 1];
-    }
-  }
-  ProbeQ<D, BF16> pq;
-  probe_q<D, BF16>(a, ps, h, pq);
-  for (int j = j0; j < j0 + kTilesPerWave && j * kBlock < ps.len; ++j) {
-    f32x4 s[4][4];
-    probe_scores<D, BF16>(a, ps, pq, j, s);
-    float p[16];
+  for (int q = 0; q < QB; ++q)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const float x = s[e >> 2][qb][e & 3];
-        acc += x > -INFINITY ? __builtin_amdgcn_exp2f(x - m[qb]) * inv[qb] : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * (pw.qb0 + q) + 4 * g + i;
+      bias[q][i] = -INFINITY;
+      if (row < ps.nobs) {
+        const float2 ml = *reinterpret_cast<const float2*>(st + 2 * row);
+        bias[q][i] = -(ml.x + ml.y);
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o, 64);
-      p[e] = acc;
     }
-    if (l16 == 0) {
+  ProbeQ<D, BF16, QB> pq;
+  probe_q<D, BF16, QB>(a, ps, pw.h, pw.qb0, pq);
+  u32x4 pre[KTile<D>::PER];
+  ktile_load<D>(a, ps, pw.kv, pw.j0, pre);
+  ktile_store<D>(kbuf[0], pre);   // (the wait before it covers the loads above)
+  const float tau = a.tau_log2e;
+  for (int j = pw.j0; j < pw.jn; ++j) {
+    __syncthreads();   // tile j staged; every wave is done with the other buffer and the sums
+    const bool more = j + 1 < pw.jn;
+    if (more) ktile_load<D>(a, ps, pw.kv, j + 1, pre);
+    f32x4 s[4][QB];
+    probe_raw<D, BF16, QB, false>(kbuf[(j - pw.j0) & 1], pq, s);
+    float p[4];
+    if (j * kBlock + kBlock - 1 > ps.r0) {
+      // keys after the first probe row: row 16 (qb0 + q) + 4 g + i sees key c
+      // when c <= r0 + row (rows past the probe have bias -inf)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb) {
+        const int lim = j * kBlock + 16 * kb + l16 - ps.r0 - 4 * g - 16 * pw.qb0;   // visible: 16 q + i >= lim
+        float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = j * kBlock + 16 * kb + 4 * g + i;
-          if (key < ps.len) a.mass[(static_cast<size_t>(ps.tok0) + key) * a.hq + h] = p[4 * kb + i];
-        }
+        for (int q = 0; q < QB; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][q][i], tau, bias[q][i]));
+            acc += 16 * q + i >= lim ? e : 0.0f;
+          }
+        p[kb] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][q][i], tau, bias[q][i]));
+        p[kb] = acc;
+      }
     }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) p[kb] = probe_sum4(p[kb]);
+    // every lane group holds the 64 sums; group g takes keys 16 g + l16
+    float v = g == 0 ? p[0] : g == 1 ? p[1] : g == 2 ? p[2] : p[3];
+    const int key = j * kBlock + 16 * g + l16;
+    if constexpr (wph > 1) {
+      part[w][lane] = v;
+      __syncthreads();
+      if (w % wph == 0) {
+#pragma unroll
+        for (int u = 1; u < wph; ++u) v += part[w + u][lane];
+        if (key < ps.len) a.mass[static_cast<size_t>(pw.h) * a.T + ps.tok0 + key] = v;
+      }
+    } else {
+      if (key < ps.len) a.mass[static_cast<size_t>(pw.h) * a.T + ps.tok0 + key] = v;
+    }
+    if (more) ktile_store<D>(kbuf[(j + 1 - pw.j0) & 1], pre);
   }
 }
 
-// Block-wide exclusive prefix sum of one value per thread (NT threads);
-// returns the prefix and sets *total.
+// Inclusive prefix sum over the 64 lanes of a wave, on the DPP cross-lane
+// paths: shifts by 1, 2, 4, 8 lanes within each row of 16 (lanes whose source
+// lies outside the row add 0), then the last lane of row 0 (row 2) is
+// broadcast into row 1 (row 3), and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2 and 3
+  return x;
+}
+
+// Block-wide exclusive prefix sums of two values per thread (NT threads);
+// sets the totals.  Uses its LDS once per kernel.
 template <int NT>
-__device__ __forceinline__ int block_scan(int v, int* total) {
-  __shared__ int warp_tot[NT / 64];
+__device__ __forceinline__ int2 block_scan2(int x, int y, int2* total) {
+  __shared__ int2 wtot[NT / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) warp_tot[w] = x;
+  const int ix = wave_incl_scan(x), iy = wave_incl_scan(y);
+  if (lane == 63) wtot[w] = make_int2(ix, iy);
   __syncthreads();
-  int base = 0, tot = 0;
+  int2 base = make_int2(0, 0), tot = make_int2(0, 0);
 #pragma unroll
   for (int u = 0; u < NT / 64; ++u) {
-    if (u < w) base += warp_tot[u];
-    tot += warp_tot[u];
+    const int2 t = wtot[u];
+    if (u < w) {
+      base.x += t.x;
+      base.y += t.y;
+    }
+    tot.x += t.x;
+    tot.y += t.y;
   }
-  __syncthreads();
   *total = tot;
-  return base + x - v;
+  return make_int2(base.x + ix - x, base.y + iy - y);
 }
 
-// top-k of one list: (sequence b, list head g): the mass of query head g, or
-// the sum over KV head g's query heads
+// top-k of one list, (sequence b, list head g): the mass of query head g, or
+// the sum over KV head g's query heads.  Thread t owns the list positions
+// [t per, (t + 1) per).  The k-th largest value is found by an MSB-first
+// radix select on the float bits (non-negative, so the bits order as the
+// values) in three digits: bits 30..20, 19..10, 9..0; each digit's histogram
+// of the keys that match the digits found so far is built with LDS atomics,
+// and wave 0 finds the digit where the count from the top reaches k.  Then
+// the keys above the threshold and the lowest positions among those equal to
+// it are written in ascending order.  PER > 0: lists of up to PER x 1024
+// keys, held in registers; PER = 0: any length, re-read from global memory.
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkLds = 12288;   // keys of a list held in LDS (48 KiB)
-__global__ __launch_bounds__(1024) void topk_kernel(SelectArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int tok0 = a.cu[b], len = a.cu[b + 1] - a.cu[b];
-  const int k = sel_tab(a, 1, b);
-  int32_t* out = a.sel + sel_tab(a, 2, b) + static_cast<size_t>(g) * k;
-  const int grp = a.hq / a.hkv;
-  auto value = [&](int c) -> uint32_t {
-    float v;
-    if (a.per_kv) {
-      v = 0.0f;
-      for (int u = 0; u < grp; ++u) v += a.mass[(static_cast<size_t>(tok0) + c) * a.hq + g * grp + u];
-    } else {
-      v = a.mass[(static_cast<size_t>(tok0) + c) * a.hq + g];
-    }
-    return __float_as_uint(fmaxf(v, 0.0f));   // non-negative: the bits order as the values
-  };
-  if (k <= 0) return;
+constexpr int kTopkPer = 12;
+template <int PER>
+__device__ __forceinline__ void topk_list(const SelectArgs& a, const float* src, int nsum, int len, int k,
+                                          int32_t* out) {
   constexpr int NT = kTopkThreads;
   const int lane = threadIdx.x & 63;
-  // a list of up to kTopkLds keys is read from global memory once and kept
-  // in LDS for the radix passes and the compaction
-  __shared__ uint32_t sv[kTopkLds];
-  const bool in_lds = len <= kTopkLds;
-  if (in_lds) {
-    for (int c = threadIdx.x; c < len; c += NT) sv[c] = value(c);
-    __syncthreads();
-  }
-  auto get = [&](int c) -> uint32_t { return in_lds ? sv[c] : value(c); };
-  // radix select of the k-th largest, 8 bits at a time from the top
-  __shared__ int hist[256];
-  __shared__ int pick, above;
-  uint32_t prefix = 0, pmask = 0;
-  int want = k;   // rank (1-based, from the top) of the k-th largest among values matching prefix
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int c0 = 0; c0 < len; c0 += 4 * NT) {
-      uint32_t v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
-        v[u] = c < len ? get(c) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
-        bool pend = c < len && (v[u] & pmask) == prefix;
-        const uint32_t bin = (v[u] >> shift) & 255u;
-        // lanes that share the first pending lane's digit add once (masses
-        // cluster in a few digits, which would serialize the LDS atomics);
-        // two rounds, then one atomic per remaining lane
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          const uint64_t act = __ballot(pend);
-          if (act == 0) break;
-          const int leader = __builtin_ctzll(act);
-          const uint32_t lb = static_cast<uint32_t>(__shfl(static_cast<int>(bin), leader, 64));
-          const bool same = pend && bin == lb;
-          const uint64_t mm = __ballot(same);
-          if (lane == leader) atomicAdd(&hist[lb], __popcll(mm));
-          if (same) pend = false;
-        }
-        if (pend) atomicAdd(&hist[bin], 1);
-      }
-    }
-    __syncthreads();
-    // digit d: the largest with count(digits >= d) >= want.  Lane l of wave 0
-    // holds digits 255 - 4l .. 252 - 4l (descending); a scan over the lanes
-    // gives the count above each lane, and the lowest lane whose digits reach
-    // want holds d (digit 0 when none of 255..1 does)
-    if (threadIdx.x < 64) {
-      int c[4], t = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        c[u] = hist[255 - 4 * lane - u];
-        t += c[u];
-      }
-      int incl = t;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
-      int acc = incl - t, fd = -1, fa = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int d = 255 - 4 * lane - u;
-        if (d == 0) break;
-        if (fd < 0 && acc + c[u] >= want) {
-          fd = d;
-          fa = acc;
-        }
-        acc += c[u];
-      }
-      const uint64_t found = __ballot(fd >= 0);
-      if (found == 0) {
-        if (lane == 63) {   // acc = count of digits 255..1
-          pick = 0;
-          above = acc;
-        }
-      } else if (lane == __builtin_ctzll(found)) {
-        pick = fd;
-        above = fa;
-      }
-    }
-    __syncthreads();
-    prefix |= static_cast<uint32_t>(pick) << shift;
-    pmask |= 255u << shift;
-    want -= above;
-    __syncthreads();
-  }
-  const uint32_t thr = prefix;   // the k-th largest value's bits
-  // keys above the threshold, then the first `want` equal ones, in position
-  // order: thread t owns the contiguous positions [t per, (t + 1) per)
   const int per = (len + NT - 1) / NT;
-  const int c_lo = min(len, static_cast<int>(threadIdx.x) * per), c_hi = min(len, c_lo + per);
+  const int c_lo = min(len, static_cast<int>(threadIdx.x) * per);
+  const int n_mine = min(len, c_lo + per) - c_lo;
+  auto value = [&](int c) -> uint32_t {
+    float v = 0.0f;
+    for (int u = 0; u < nsum; ++u) v += src[static_cast<size_t>(u) * a.T + c];
+    return __float_as_uint(fmaxf(v, 0.0f));
+  };
+  uint32_t rv[PER > 0 ? PER : 1];
+  if constexpr (PER > 0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) rv[u] = u < n_mine ? value(c_lo + u) : 0u;
+  }
+  // calls f(position, bits) for the thread's keys
+  auto each = [&](auto&& f) {
+    if constexpr (PER > 0) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        if (u < n_mine) f(c_lo + u, rv[u]);
+    } else {
+      for (int u = 0; u < n_mine; ++u) f(c_lo + u, value(c_lo + u));
+    }
+  };
+  __shared__ int hist[2048 + 1024 + 1024];
+  __shared__ int pick_d, pick_above;
+  for (int i = threadIdx.x; i < 4096; i += NT) hist[i] = 0;
+  __syncthreads();
+  uint32_t prefix = 0, pmask = 0;
+  int want = k;   // rank (from the top) of the k-th largest among the keys matching prefix
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : pass == 1 ? 10 : 0;
+    const int nb = pass == 0 ? 2048 : 1024;
+    int* h = hist + (pass == 0 ? 0 : pass == 1 ? 2048 : 3072);
+    // runs of equal digits among the thread's consecutive keys are added at
+    // once (clustered masses share few digits: fewer atomics on one address)
+    int run_bin = 0, run_n = 0;
+    each([&](int, uint32_t v) {
+      if ((v & pmask) == prefix) {
+        const int bin = static_cast<int>((v >> shift) & static_cast<uint32_t>(nb - 1));
+        if (run_n > 0 && bin != run_bin) {
+          atomicAdd(&h[run_bin], run_n);
+          run_n = 0;
+        }
+        run_bin = bin;
+        ++run_n;
+      }
+    });
+    if (run_n > 0) atomicAdd(&h[run_bin], run_n);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l holds the digits top - u, u < B (descending); the sum is read
+      // in a lane-rotated order so the lanes' reads fall in different banks
+      const int B = nb >> 6, top = nb - 1 - B * lane;
+      int t = 0;
+      for (int u = 0; u < B; ++u) t += h[top - ((u + lane) & (B - 1))];
+      const int incl = wave_incl_scan(t);
+      int acc = incl - t;
+      if (acc < want && incl >= want) {   // the one lane where the count from the top reaches want
+        // (its counts read at once, then searched in registers)
+        constexpr int BM = 2048 / 64;
+        int cnt[BM];
+#pragma unroll
+        for (int u = 0; u < BM; ++u) cnt[u] = u < B ? h[top - u] : 0;
+        bool found = false;
+#pragma unroll
+        for (int u = 0; u < BM; ++u) {
+          if (!found && u < B && acc + cnt[u] >= want) {
+            found = true;
+            pick_d = top - u;
+            pick_above = acc;
+          }
+          acc += cnt[u];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(pick_d) << shift;
+    pmask |= static_cast<uint32_t>(nb - 1) << shift;
+    want -= pick_above;
+  }
+  const uint32_t thr = prefix;   // the k-th largest value's bits; want = how many keys equal to it to take
   int ngt = 0, neq = 0;
-  for (int c = c_lo; c < c_hi; ++c) {
-    const uint32_t v = get(c);
+  each([&](int, uint32_t v) {
     ngt += v > thr;
     neq += v == thr;
-  }
-  int eq_tot;
-  int eq_rank = block_scan<NT>(neq, &eq_tot);   // equal keys before this thread's range
-  const int ntake = ngt + max(0, min(neq, want - eq_rank));
-  int take_tot;
-  int pos = block_scan<NT>(ntake, &take_tot);
-  for (int c = c_lo; c < c_hi; ++c) {
-    const uint32_t v = get(c);
+  });
+  int2 tot;
+  const int2 ex = block_scan2<NT>(ngt, neq, &tot);
+  int pos = ex.x + min(ex.y, want), eq_rank = ex.y;
+  each([&](int c, uint32_t v) {
     bool take = v > thr;
     if (v == thr) take = eq_rank++ < want;
     if (take) {
       if (pos < k) out[pos] = c;
       ++pos;
     }
-  }
+  });
 }
 
-template <int D, bool BF16>
-static hipError_t launch_select_t(const SelectArgs& a, int maxnt, hipStream_t st) {
-  const dim3 g3((maxnt + kProbeWaves * kTilesPerWave - 1) / (kProbeWaves * kTilesPerWave), a.hq, a.nseq);
-  hipLaunchKernelGGL((probe_partial_kernel<D, BF16>), g3, dim3(64 * kProbeWaves), 0, st, a);
+__global__ __launch_bounds__(1024) void topk_kernel(SelectArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tok0 = a.cu[b], len = a.cu[b + 1] - tok0;
+  const int k = sel_tab(a, 1, b);
+  if (k <= 0) return;
+  int32_t* out = a.sel + sel_tab(a, 2, b) + static_cast<size_t>(g) * k;
+  const int grp = a.hq / a.hkv;
+  const float* src = a.mass + static_cast<size_t>(a.per_kv ? g * grp : g) * a.T + tok0;
+  if (len <= kTopkPer * kTopkThreads) topk_list<kTopkPer>(a, src, a.per_kv ? grp : 1, len, k, out);
+  else topk_list<0>(a, src, a.per_kv ? grp : 1, len, k, out);
+}
+
+template <int D, bool BF16, int QB>
+static hipError_t launch_select_t(const SelectArgs& a0, int maxnt, int64_t tiles, hipStream_t st) {
+  SelectArgs a = a0;
+  // tiles per workgroup: enough workgroups for two per compute unit where
+  // the sequences allow it, up to 8 tiles each
+  const int64_t wg1 = tiles * a.hkv * (a.hq / a.hkv / QB);
+  a.tw = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(8, wg1 / 512)));
+  const dim3 g3((maxnt + a.tw - 1) / a.tw, a.hkv * (a.hq / a.hkv / QB), a.nseq);
+  hipLaunchKernelGGL((probe_partial_kernel<D, BF16, QB>), g3, dim3(kProbeThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(probe_rows_kernel, dim3(a.hq, a.nseq), dim3(64 * kRowParts), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((probe_mass_kernel<D, BF16>), g3, dim3(64 * kProbeWaves), 0, st, a);
+  hipLaunchKernelGGL((probe_mass_kernel<D, BF16, QB>), g3, dim3(kProbeThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.sel != nullptr) {
     hipLaunchKernelGGL(topk_kernel, dim3(a.per_kv ? a.hkv : a.hq, a.nseq), dim3(kTopkThreads), 0, st, a);
@@ -440,9 +576,19 @@ static hipError_t launch_select_t(const SelectArgs& a, int maxnt, hipStream_t st
   return e;
 }
 
-hipError_t launch_select(const SelectArgs& a, int d, int maxnt, hipStream_t st) {
-  if (d == 128) return a.bf16 ? launch_select_t<128, true>(a, maxnt, st) : launch_select_t<128, false>(a, maxnt, st);
-  return a.bf16 ? launch_select_t<64, true>(a, maxnt, st) : launch_select_t<64, false>(a, maxnt, st);
+template <int D, bool BF16>
+static hipError_t launch_select_qb(const SelectArgs& a, int maxnt, int64_t tiles, hipStream_t st) {
+  // query heads per workgroup: 4 when the KV head's group allows, else 2 or 1
+  const int grp = a.hq / a.hkv;
+  if (grp % 4 == 0) return launch_select_t<D, BF16, 4>(a, maxnt, tiles, st);
+  if (grp % 2 == 0) return launch_select_t<D, BF16, 2>(a, maxnt, tiles, st);
+  return launch_select_t<D, BF16, 1>(a, maxnt, tiles, st);
+}
+
+hipError_t launch_select(const SelectArgs& a, int d, int maxnt, int64_t tiles, hipStream_t st) {
+  if (d == 128)
+    return a.bf16 ? launch_select_qb<128, true>(a, maxnt, tiles, st) : launch_select_qb<128, false>(a, maxnt, tiles, st);
+  return a.bf16 ? launch_select_qb<64, true>(a, maxnt, tiles, st) : launch_select_qb<64, false>(a, maxnt, tiles, st);
 }
 
 }  // namespace tmx

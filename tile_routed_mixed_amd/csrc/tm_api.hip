@@ -534,8 +534,9 @@ tm_status tm_select_vertical(const tm_shape* shape, const void* q, const void* k
   a.part = reinterpret_cast<float*>(w);
   a.rows = reinterpret_cast<float*>(w + part_b);
   a.mass = mass;
+  a.T = si.T;
   a.sel = sel_idx;
-  return launch_select(a, shape->d, maxnt, hs) == hipSuccess ? TM_OK : TM_E_HIP;
+  return launch_select(a, shape->d, maxnt, tiles, hs) == hipSuccess ? TM_OK : TM_E_HIP;
 }
 
 tm_status tm_prefill(const tm_shape* shape, const void* trav, int32_t policy_kind, const void* q, const void* k,

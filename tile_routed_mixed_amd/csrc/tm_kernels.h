@@ -154,8 +154,10 @@ struct SelectArgs {
   int nseq, hq, hkv, n_obs, bf16, per_kv;
   float tau_log2e;
   float* part;              // [tiles][hq][64][2] partial (max, sum) per probe row
-  float* rows;              // [nseq][hq][64][2] each probe row's (max, sum)
-  float* mass;              // [T][hq] attention mass of each key
+  float* rows;              // [nseq][hq][64][2] each probe row's (max, log2 sum)
+  float* mass;              // [hq][T] attention mass of each key
+  int64_t T;                // total tokens
+  int tw;                   // key tiles per workgroup of passes 1 and 3 (set at launch)
   // per sequence: first tile, keys to select per list, first output entry of
   // its lists; as tab[3][nseq] in the workspace, or (nseq <= kSelInline,
   // tab == null) in itab, carried by the kernel arguments
@@ -175,7 +177,7 @@ hipError_t launch_gather(const GatherArgs& a, int d, hipStream_t st);        // 
 hipError_t launch_gather_rows(const GatherArgs& a, int d, hipStream_t st);   // V from 16-bit rows
 hipError_t launch_sel_tables(const SelTabArgs& a, int n_lists, hipStream_t st);
 hipError_t launch_hybrid_build(const HybArgs& a, bool census, hipStream_t st);
-hipError_t launch_select(const SelectArgs& a, int d, int maxnt, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, int d, int maxnt, int64_t tiles, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int bq, int kind, bool bf16, hipStream_t st);
 // boundary policies: the software-pipelined kernel (k_prefill_pipe.hip)
 hipError_t launch_prefill_pipe(const PrefillArgs& a, int d, int bq, hipStream_t st);
