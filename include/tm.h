@@ -342,6 +342,20 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy,
 tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, void* trav,
                              const void* k, const void* v, void* stream);
 
+/* tm_build_traversal followed by tm_gather_selected, for hybrid policies, in
+ * one launch: one workgroup per list builds the tables as tm_build_traversal
+ * does, one workgroup per gathered tile fills it as tm_gather_selected does
+ * (both find the tile's keys from the same lists), so the traversal holds the
+ * same bytes as after the two calls.  Arguments as for the two calls; trav ==
+ * NULL is the size query of tm_build_traversal.  Waits as tm_build_traversal
+ * does (host lists and census: yes; device lists: no).
+ * Errors: those of the two calls; TM_E_ARG for a policy that is not hybrid or
+ * NULL k or v.  ([HyQuant] "How HyQuant works": selected tokens kept in
+ * FP16.) */
+tm_status tm_build_traversal_gather(const tm_shape* shape, const tm_policy* policy, void* trav,
+                                    size_t* trav_bytes, tm_census* census, const void* k,
+                                    const void* v, void* stream);
+
 /* Vertical-line token selection for the hybrid policies ([HyQuant] "The
  * observation behind the method" and "How HyQuant works": a few key positions
  * are attended by many queries; tokens to keep in FP16 are picked from

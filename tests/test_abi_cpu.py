@@ -233,6 +233,16 @@ def test_hybrid_validation_and_size(B):
     assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(p.c), FAKE, FAKE, None, None) == B.TM_E_ARG
     b = B.Policy(dict(kind=0, b8=[1, 1], b4=[2, 2], sink=0))
     assert L.tm_gather_selected(ctypes.byref(s.c), ctypes.byref(b.c), FAKE, FAKE, FAKE, None) == B.TM_E_ARG
+    # build and gather in one launch: the same size query and checks, hybrid
+    # policies only, K and V required when a traversal is given
+    fused = lambda pp, k, v, t=None: L.tm_build_traversal_gather(ctypes.byref(s.c), ctypes.byref(pp.c), t,
+                                                                 ctypes.byref(n), None, k, v, None)
+    n.value = 0
+    assert fused(p, None, None) == B.TM_OK and n.value == end
+    assert fused(_hybrid(B, -1, lists), FAKE, FAKE) == B.TM_E_POLICY
+    assert fused(p, None, FAKE, FAKE) == B.TM_E_ARG
+    assert fused(p, FAKE, None, FAKE) == B.TM_E_ARG
+    assert fused(b, FAKE, FAKE) == B.TM_E_ARG
 
 
 def test_traversal_capacity(B):

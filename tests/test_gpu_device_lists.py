@@ -184,3 +184,27 @@ def test_decode_device_lists_match_host_lists(seqlens, dpol, frac):
     ha = a[gh0:gh0 + 512 * n_gt].reshape(max(n_gt, 0), 512)[:, :16 + 4 * 64]
     hb = b[gh0:gh0 + 512 * n_gt].reshape(max(n_gt, 0), 512)[:, :16 + 4 * 64]
     assert np.array_equal(ha, hb)
+
+
+@pytest.mark.parametrize("case", list(HYBRID_CASES))
+@pytest.mark.parametrize("device", [False, True])
+def test_build_and_gather_in_one_launch_equals_two_calls(case, device):
+    """tm_build_traversal_gather leaves the traversal buffer byte for byte as
+    tm_build_traversal followed by tm_gather_selected does."""
+    import torch
+    import tile_routed_mixed_amd as T
+    w, pol = _hyb_case(case)
+    if device:
+        pol = dict(kind=3, window=pol["window"], sel_off=pol["sel_off"], sel_idx_dev=_dev(pol["sel_idx"]))
+    q, k, v = W.make_qkv(w)
+    say(f"[gpu] hybrid {case}: build + gather in one launch vs two calls (device lists: {device})")
+    p = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, pol)
+    p.upload(q[0], k[0], v[0])
+    bufs = []
+    for fused in (False, True):
+        p.trav.fill_(0xA5)
+        c = p.traversal(census=True, fused=fused)
+        torch.cuda.synchronize()
+        bufs.append((c, p.trav.cpu().numpy().copy()))
+    assert bufs[0][0] == bufs[1][0]
+    assert np.array_equal(bufs[0][1], bufs[1][1])

@@ -90,6 +90,10 @@ def lib():
         L.tm_build_traversal.restype = i32
         L.tm_build_traversal.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp,
                                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(tm_census), vp]
+        L.tm_build_traversal_gather.restype = i32
+        L.tm_build_traversal_gather.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp,
+                                                ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(tm_census), vp, vp,
+                                                vp]
         L.tm_gather_selected.restype = i32
         L.tm_gather_selected.argtypes = [ctypes.POINTER(tm_shape), ctypes.POINTER(tm_policy), vp, vp, vp, vp]
         L.tm_select_vertical.restype = i32
@@ -311,17 +315,24 @@ def traversal_bytes(shape: Shape, policy: Policy) -> int:
     return int(n.value)
 
 
-def tm_build_traversal(shape: Shape, policy: Policy, trav=None, census: bool = True, stream=None):
-    """Returns (trav uint8 device tensor, census dict or None)."""
+def tm_build_traversal(shape: Shape, policy: Policy, trav=None, census: bool = True, stream=None, k=None, v=None):
+    """Returns (trav uint8 device tensor, census dict or None).  k, v (hybrid
+    policies): also gather the selected keys' rows in the same launch
+    (tm_build_traversal_gather)."""
     import torch
     need = traversal_bytes(shape, policy)
     if trav is None:
         trav = torch.empty(need, dtype=torch.uint8, device=shape.cu_dev.device)
     n = ctypes.c_size_t(trav.numel())
     cen = tm_census()
-    _check(lib().tm_build_traversal(ctypes.byref(shape.c), ctypes.byref(policy.c), _ptr(trav), ctypes.byref(n),
-                                    ctypes.byref(cen) if census else None, _stream(stream)),
-           "tm_build_traversal")
+    cp = ctypes.byref(cen) if census else None
+    if k is not None:
+        _check(lib().tm_build_traversal_gather(ctypes.byref(shape.c), ctypes.byref(policy.c), _ptr(trav),
+                                               ctypes.byref(n), cp, _ptr(k), _ptr(v), _stream(stream)),
+               "tm_build_traversal_gather")
+    else:
+        _check(lib().tm_build_traversal(ctypes.byref(shape.c), ctypes.byref(policy.c), _ptr(trav), ctypes.byref(n),
+                                        cp, _stream(stream)), "tm_build_traversal")
     out = None
     if census:
         out = dict(legal=cen.legal, int8=cen.n_int8, int4=cen.n_int4, fp16=cen.n_fp16, skip=cen.n_skip,

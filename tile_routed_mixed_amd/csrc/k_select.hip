@@ -452,8 +452,20 @@ __device__ __forceinline__ void topk_list(const SelectArgs& a, const float* src,
   };
   uint32_t rv[PER > 0 ? PER : 1];
   if constexpr (PER > 0) {
+    // every load issued before the first add: one memory latency per head
+    float acc[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) rv[u] = u < n_mine ? value(c_lo + u) : 0u;
+    for (int u = 0; u < PER; ++u) acc[u] = 0.0f;
+    for (int hh = 0; hh < nsum; ++hh) {
+      const float* p = src + static_cast<size_t>(hh) * a.T + c_lo;
+      float x[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) x[u] = u < n_mine ? p[u] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] += x[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) rv[u] = __float_as_uint(fmaxf(acc[u], 0.0f));
   }
   // calls f(position, bits) for the thread's keys
   auto each = [&](auto&& f) {

@@ -370,7 +370,100 @@ hipError_t launch_sel_tables(const SelTabArgs& a, int n_lists, hipStream_t st) {
 // inside their sequence (host lists are checked before the launch, device
 // lists are not); a position outside the sequence becomes an empty slot and
 // every write stays inside the sizes the host computed.
+// Fill gathered tile t with the 16-bit K rows ([64][D]) and the fp16 V
+// columns (V^T [D][64]) of the keys pos(0 .. keys - 1) of the sequence whose
+// tokens start at tok0, KV head kv; both come from the token-major 16-bit
+// inputs (each key's row is contiguous; V is converted to fp16, bf16
+// saturated to the fp16 range, and transposed through LDS).  Slots past the
+// keys and empty slots (position INT32_MAX) are zero.
+template <int D, bool BF16, class Pos>
+__device__ __forceinline__ void gather_rows_tile(uint8_t* trav, uint32_t gk_off, uint32_t gv_off, uint32_t t,
+                                                 const uint16_t* k, const uint16_t* v, int hkv, uint32_t tok0,
+                                                 uint32_t kv, int keys, Pos pos, _Float16* vl) {
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int VP = D + 8;     // LDS row pitch (fp16): rows start on different banks
+  uint16_t* gk = reinterpret_cast<uint16_t*>(trav + gk_off) + static_cast<size_t>(t) * kBlock * D;
+  uint16_t* gv = reinterpret_cast<uint16_t*>(trav + gv_off) + static_cast<size_t>(t) * D * kBlock;
+  for (int u = threadIdx.x; u < kBlock * CPR; u += 256) {
+    const int row = u / CPR, ch = u % CPR;
+    u32x4 kx = u32x4{0u, 0u, 0u, 0u}, vx = u32x4{0u, 0u, 0u, 0u};
+    const int32_t p = row < keys ? pos(row) : INT32_MAX;
+    if (p != INT32_MAX) {
+      const size_t off = ((static_cast<size_t>(tok0) + p) * hkv + kv) * D + ch * 8;
+      kx = *reinterpret_cast<const u32x4*>(k + off);
+      vx = *reinterpret_cast<const u32x4*>(v + off);
+    }
+    *reinterpret_cast<u32x4*>(gk + row * D + ch * 8) = kx;
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (BF16) {
+        h[2 * e] = to_f16_sat(__uint_as_float(vx[e] << 16));
+        h[2 * e + 1] = to_f16_sat(__uint_as_float(vx[e] & 0xFFFF0000u));
+      } else {
+        h[2 * e] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(vx[e] & 0xFFFFu));
+        h[2 * e + 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(vx[e] >> 16));
+      }
+    }
+    *reinterpret_cast<f16x8*>(vl + row * VP + ch * 8) = h;
+  }
+  __syncthreads();
+  // V^T: channel rows of 64 slots, two slots per thread step
+  for (int u = threadIdx.x; u < D * (kBlock / 2); u += 256) {
+    const int c = u / (kBlock / 2), sl = 2 * (u % (kBlock / 2));
+    f16x2 pr;
+    pr[0] = vl[sl * VP + c];
+    pr[1] = vl[(sl + 1) * VP + c];
+    *reinterpret_cast<f16x2*>(gv + c * kBlock + sl) = pr;
+  }
+}
+
 constexpr int kHybChunk = 1024;
+
+// Workgroup g past the lists (when the gather sources are given) fills
+// gathered tile g, as gather_rows_kernel does, from the list's positions:
+// the lists' gathered tiles are numbered in list order, ceil(keys / 64) each,
+// so the workgroup finds its list by a prefix over the list lengths (the
+// numbering hyb_build_kernel gives the headers).
+__device__ void hyb_gather(const HybArgs& a, int g, int* red) {
+  __shared__ int hit[2];
+  __shared__ _Float16 vl[kBlock * (128 + 8)];
+  const int nl = a.nseq * a.hq, tid = threadIdx.x;
+  if (tid == 0) hit[0] = -1;
+  int carry = 0;
+  for (int u0 = 0; u0 < nl; u0 += 256) {
+    const int u = u0 + tid;
+    const int nt = u < nl ? (list_span(a.off, u, a.n_sel).y + kBlock - 1) / kBlock : 0;
+    int tot;
+    const int ex = carry + block_scan256(nt, red, &tot);   // (synchronizes before writing red)
+    if (nt > 0 && ex <= g && g < ex + nt) {
+      hit[0] = u;
+      hit[1] = ex;
+    }
+    carry += tot;
+    __syncthreads();
+    if (hit[0] >= 0 || carry > g) break;
+  }
+  const int r = hit[0];
+  if (r < 0) return;   // (no list holds tile g: the host sized n_gt from the same lists)
+  const int gb = hit[1], s = r / a.hq, h = r % a.hq;
+  const uint32_t kv = static_cast<uint32_t>(h / (a.hq / a.hkv));
+  const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
+  const int2 sp = list_span(a.off, r, a.n_sel);
+  const int cnt = min(sp.y, (static_cast<int>(a.n_gt) - gb) * kBlock);
+  const int tl = g - gb;
+  const int keys = min(kBlock, cnt - kBlock * tl);
+  const int32_t* li = a.idx + sp.x + kBlock * tl;
+  auto pos = [&](int row) { return clean_pos(li[row], len); };
+  const uint32_t tok = static_cast<uint32_t>(tok0);
+  if (a.d == 128) {
+    if (a.bf16) gather_rows_tile<128, true>(a.trav, a.gk_off, a.gv_off, g, a.gk_src, a.gv_src, a.hkv, tok, kv, keys, pos, vl);
+    else gather_rows_tile<128, false>(a.trav, a.gk_off, a.gv_off, g, a.gk_src, a.gv_src, a.hkv, tok, kv, keys, pos, vl);
+  } else {
+    if (a.bf16) gather_rows_tile<64, true>(a.trav, a.gk_off, a.gv_off, g, a.gk_src, a.gv_src, a.hkv, tok, kv, keys, pos, vl);
+    else gather_rows_tile<64, false>(a.trav, a.gk_off, a.gv_off, g, a.gk_src, a.gv_src, a.hkv, tok, kv, keys, pos, vl);
+  }
+}
 
 __device__ __forceinline__ int fdiv_floor(int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); }
 
@@ -378,6 +471,10 @@ __global__ __launch_bounds__(256) void hyb_build_kernel(HybArgs a) {
   __shared__ int red[4];
   __shared__ unsigned long long cml[kHybChunk];
   __shared__ int cum[kHybChunk];
+  if (static_cast<int>(blockIdx.x) >= a.nseq * a.hq) {
+    hyb_gather(a, static_cast<int>(blockIdx.x) - a.nseq * a.hq, red);
+    return;
+  }
   const int r = blockIdx.x, tid = threadIdx.x;
   const int s = r / a.hq, h = r % a.hq;
   // first cache block of s; first gathered tile of list r
@@ -525,60 +622,25 @@ __global__ __launch_bounds__(256) void hyb_build_kernel(HybArgs a) {
 hipError_t launch_hybrid_build(const HybArgs& a, bool census, hipStream_t st) {
   const int n_lists = a.nseq * a.hq;
   if (n_lists <= 0) return hipSuccess;
-  hipLaunchKernelGGL(hyb_build_kernel, dim3(n_lists), dim3(256), 0, st, a);
+  const unsigned n_wg = static_cast<unsigned>(n_lists) + (a.gk_src != nullptr ? a.n_gt : 0u);
+  hipLaunchKernelGGL(hyb_build_kernel, dim3(n_wg), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !census) return e;
   hipLaunchKernelGGL(trav_census_kernel, dim3(1), dim3(256), 0, st, a.trav, a.item_off, a.n_items);
   return hipGetLastError();
 }
 
-// Hybrid traversals: fill gathered tile t with its selected keys' 16-bit K
-// rows ([64][D]) and fp16 V columns (V^T [D][64]), both read from the
-// token-major 16-bit inputs (each key's row is contiguous; V is converted to
-// fp16, bf16 saturated to the fp16 range, and transposed through LDS).
-// Slots past the list and empty slots (position INT32_MAX) are zero.
+// Hybrid traversals: fill gathered tile t (its header written by
+// hyb_build_kernel) with its selected keys' K rows and V^T.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
-  constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int VP = D + 8;     // LDS row pitch (fp16): rows start on different banks
-  __shared__ _Float16 vl[kBlock * VP];
+  __shared__ _Float16 vl[kBlock * (D + 8)];
   const uint32_t t = blockIdx.x;
   const uint8_t* gh = a.trav + a.gh_off + static_cast<size_t>(t) * kGatherHdr;
   const GatherEntry ge = *reinterpret_cast<const GatherEntry*>(gh);
   const int32_t* pos = reinterpret_cast<const int32_t*>(gh + 16);
-  uint16_t* gk = reinterpret_cast<uint16_t*>(a.trav + a.gk_off) + static_cast<size_t>(t) * kBlock * D;
-  uint16_t* gv = reinterpret_cast<uint16_t*>(a.trav + a.gv_off) + static_cast<size_t>(t) * D * kBlock;
-  for (int u = threadIdx.x; u < kBlock * CPR; u += 256) {
-    const int row = u / CPR, ch = u % CPR;
-    u32x4 kx = u32x4{0u, 0u, 0u, 0u}, vx = u32x4{0u, 0u, 0u, 0u};
-    if (row < static_cast<int>(ge.keys) && pos[row] != INT32_MAX) {
-      const size_t off = ((static_cast<size_t>(ge.tok_start) + pos[row]) * a.hkv + ge.kv) * D + ch * 8;
-      kx = *reinterpret_cast<const u32x4*>(a.k + off);
-      vx = *reinterpret_cast<const u32x4*>(a.v + off);
-    }
-    *reinterpret_cast<u32x4*>(gk + row * D + ch * 8) = kx;
-    f16x8 h;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (BF16) {
-        h[2 * e] = to_f16_sat(__uint_as_float(vx[e] << 16));
-        h[2 * e + 1] = to_f16_sat(__uint_as_float(vx[e] & 0xFFFF0000u));
-      } else {
-        h[2 * e] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(vx[e] & 0xFFFFu));
-        h[2 * e + 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(vx[e] >> 16));
-      }
-    }
-    *reinterpret_cast<f16x8*>(vl + row * VP + ch * 8) = h;
-  }
-  __syncthreads();
-  // V^T: channel rows of 64 slots, two slots per thread step
-  for (int u = threadIdx.x; u < D * (kBlock / 2); u += 256) {
-    const int c = u / (kBlock / 2), sl = 2 * (u % (kBlock / 2));
-    f16x2 pr;
-    pr[0] = vl[sl * VP + c];
-    pr[1] = vl[(sl + 1) * VP + c];
-    *reinterpret_cast<f16x2*>(gv + c * kBlock + sl) = pr;
-  }
+  gather_rows_tile<D, BF16>(a.trav, a.gk_off, a.gv_off, t, a.k, a.v, a.hkv, ge.tok_start, ge.kv,
+                            static_cast<int>(ge.keys), [&](int row) { return pos[row]; }, vl);
 }
 
 hipError_t launch_gather_rows(const GatherArgs& a, int d, hipStream_t st) {

@@ -317,8 +317,10 @@ tm_status tm_quantize_pack(const tm_shape* shape, const void* x, int32_t heads, 
   return e == hipSuccess ? TM_OK : TM_E_HIP;
 }
 
-tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, void* trav, size_t* trav_bytes,
-                             tm_census* census, void* stream) {
+// tm_build_traversal, and (gk, gv non-null, hybrid policies) the gather of
+// tm_gather_selected in the same launch.
+static tm_status build_traversal(const tm_shape* shape, const tm_policy* policy, void* trav, size_t* trav_bytes,
+                                 tm_census* census, const void* gk, const void* gv, void* stream) {
   ShapeInfo si;
   tm_status st = check_shape(shape, true, &si);
   if (st != TM_OK) return st;
@@ -408,6 +410,9 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
     y.gh_off = static_cast<uint32_t>(L.gh_off);
     y.gk_off = static_cast<uint32_t>(L.gk_off);
     y.gv_off = static_cast<uint32_t>(L.gv_off);
+    y.gk_src = static_cast<const uint16_t*>(gk);
+    y.gv_src = static_cast<const uint16_t*>(gv);
+    y.bf16 = shape->dtype == TM_BF16;
     if (hybrid_dev_lists(policy)) {
       // lists in device memory: read (and copied into the traversal) by the kernel, no wait
       y.off = policy->sel_off_dev;
@@ -445,6 +450,18 @@ tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, voi
     census->max_runs = L.max_runs;
   }
   return TM_OK;
+}
+
+tm_status tm_build_traversal(const tm_shape* shape, const tm_policy* policy, void* trav, size_t* trav_bytes,
+                             tm_census* census, void* stream) {
+  return build_traversal(shape, policy, trav, trav_bytes, census, nullptr, nullptr, stream);
+}
+
+tm_status tm_build_traversal_gather(const tm_shape* shape, const tm_policy* policy, void* trav, size_t* trav_bytes,
+                                    tm_census* census, const void* k, const void* v, void* stream) {
+  if (policy == nullptr || policy->kind != TM_POLICY_HYBRID || (trav != nullptr && (k == nullptr || v == nullptr)))
+    return TM_E_ARG;
+  return build_traversal(shape, policy, trav, trav_bytes, census, k, v, stream);
 }
 
 tm_status tm_gather_selected(const tm_shape* shape, const tm_policy* policy, void* trav, const void* k,

@@ -69,6 +69,11 @@ struct HybArgs {
   uint32_t seq_off, item_off, run_off;
   uint32_t window, n_sel, n_gt, sel_tab_off, sel_idx_off, cm_off, gh_off, gk_off, gv_off;
   int copy_idx;
+  // gather sources (16-bit K and V rows), or null: with them the same launch
+  // also fills the gathered tiles, one workgroup per tile after the lists'
+  const uint16_t* gk_src;
+  const uint16_t* gv_src;
+  int bf16;
 };
 
 // Decode selection tables built on the GPU from device-resident lists (one

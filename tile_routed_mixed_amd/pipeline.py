@@ -75,11 +75,17 @@ class PrefillPipeline:
         B.tm_quantize_pack(self.shape, self.k, self.kq, stream)
         B.tm_quantize_pack(self.shape, self.v, self.vq, stream)
 
-    def traversal(self, census=False, stream=None):
+    def traversal(self, census=False, stream=None, fused=True):
         """Build the traversal; under a hybrid policy also gather the selected
-        keys' K rows and V columns (after quantize())."""
+        keys' K rows and V columns, in the same launch (fused) or by
+        tm_gather_selected after the build."""
+        hyb = self.policy.kind == B.TM_POLICY_HYBRID
+        if hyb and fused:
+            _, c = B.tm_build_traversal(self.shape, self.policy, self.trav, census=census, stream=stream, k=self.k,
+                                        v=self.v)
+            return c
         _, c = B.tm_build_traversal(self.shape, self.policy, self.trav, census=census, stream=stream)
-        if self.policy.kind == B.TM_POLICY_HYBRID:
+        if hyb:
             B.tm_gather_selected(self.shape, self.policy, self.trav, self.k, self.v, stream)
         return c
 
