@@ -174,6 +174,14 @@ __device__ __forceinline__ float probe_sum4(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// sum of the QB per-row-block partial sums, as a tree
+template <int QB>
+__device__ __forceinline__ float probe_tree(const float (&x)[QB]) {
+  if constexpr (QB == 4) return (x[0] + x[1]) + (x[2] + x[3]);
+  else if constexpr (QB == 2) return x[0] + x[1];
+  else return x[0];
+}
+
 // The workgroup's place: sequence b, KV head kv, the wave's head h and first
 // row block qb0, its tiles [j0, jn).  Returns false for a workgroup past the
 // sequence's tiles.
@@ -220,6 +228,9 @@ __global__ __launch_bounds__(kProbeThreads, 2) void probe_partial_kernel(SelectA
     f32x4 s[4][QB];
     probe_raw<D, BF16, QB, true>(kbuf[(j - pw.j0) & 1], pq, s);
     if (probe_tile_masked(ps, j)) {
+      // (an opaque statement keeps this a branch taken by the few boundary
+      // tiles, instead of selects executed on every tile)
+      __asm__ volatile("");
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -231,24 +242,41 @@ __global__ __launch_bounds__(kProbeThreads, 2) void probe_partial_kernel(SelectA
           }
     }
     float* dst = a.part + ((static_cast<size_t>(tile0) + j) * a.hq + pw.h) * (2 * kProbe);
+    // row 16 (qb0 + q) + l16: 16 products in the lane, the rest in lanes
+    // l16 + 16, 32, 48.  The row blocks are independent (no branch between
+    // them) and each sum runs in 4 partial chains, for instruction-level
+    // parallelism.
+    float mrow[QB], lrow[QB];
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      // row 16 (qb0 + q) + l16: 16 products in the lane, the rest in lanes l16 + 16, 32, 48
-      float m = fmaxf(fmaxf(s[0][q][0], s[0][q][1]), s[0][q][2]);
+      float m4[4];
 #pragma unroll
-      for (int e = 3; e < 15; e += 2) m = fmaxf(fmaxf(m, s[e >> 2][q][e & 3]), s[(e + 1) >> 2][q][(e + 1) & 3]);
-      m = fmaxf(m, s[3][q][3]);
-      m = probe_max4(m) * tau;   // (tau > 0: the maximum of the scaled scores)
-      float l = 0.0f;
-      if (m > -INFINITY) {
+      for (int kb = 0; kb < 4; ++kb) m4[kb] = fmaxf(fmaxf(s[kb][q][0], s[kb][q][1]), fmaxf(s[kb][q][2], s[kb][q][3]));
+      mrow[q] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) l += __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][q][e & 3], tau, -m));
+    for (int q = 0; q < QB; ++q) mrow[q] = probe_max4(mrow[q]) * tau;   // (tau > 0: the maximum of the scaled scores)
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      // a row with no visible key (-inf) sums exp2(-inf) = 0 against offset 0
+      const float off = mrow[q] > -INFINITY ? -mrow[q] : 0.0f;
+      float l4[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        l4[kb] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][q][0], tau, off));
+#pragma unroll
+        for (int i = 1; i < 4; ++i) l4[kb] += __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][q][i], tau, off));
       }
-      l = probe_sum4(l);
+      lrow[q] = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) lrow[q] = probe_sum4(lrow[q]);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
       const int row = 16 * (pw.qb0 + q) + l16;
       if (lane < 16 && row < ps.nobs) {
-        dst[2 * row] = m;
-        dst[2 * row + 1] = l;
+        dst[2 * row] = mrow[q];
+        dst[2 * row + 1] = lrow[q];
       }
     }
     if (more) ktile_store<D>(kbuf[(j + 1 - pw.j0) & 1], pre);
@@ -343,28 +371,33 @@ __global__ __launch_bounds__(kProbeThreads, 2) void probe_mass_kernel(SelectArgs
     if (j * kBlock + kBlock - 1 > ps.r0) {
       // keys after the first probe row: row 16 (qb0 + q) + 4 g + i sees key c
       // when c <= r0 + row (rows past the probe have bias -inf)
+      __asm__ volatile("");   // (a branch for the boundary tiles, as in pass 1)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int lim = j * kBlock + 16 * kb + l16 - ps.r0 - 4 * g - 16 * pw.qb0;   // visible: 16 q + i >= lim
-        float acc = 0.0f;
+        float acc[QB];
 #pragma unroll
-        for (int q = 0; q < QB; ++q)
+        for (int q = 0; q < QB; ++q) {
+          acc[q] = 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][q][i], tau, bias[q][i]));
-            acc += 16 * q + i >= lim ? e : 0.0f;
+            acc[q] += 16 * q + i >= lim ? e : 0.0f;
           }
-        p[kb] = acc;
+        }
+        p[kb] = probe_tree<QB>(acc);
       }
     } else {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        float acc = 0.0f;
+        float acc[QB];
 #pragma unroll
-        for (int q = 0; q < QB; ++q)
+        for (int q = 0; q < QB; ++q) {
+          acc[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][q][0], tau, bias[q][0]));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][q][i], tau, bias[q][i]));
-        p[kb] = acc;
+          for (int i = 1; i < 4; ++i) acc[q] += __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][q][i], tau, bias[q][i]));
+        }
+        p[kb] = probe_tree<QB>(acc);
       }
     }
 #pragma unroll
