@@ -246,8 +246,9 @@ def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48):
         res["selection_ms"] = sel["mean"]
         res["hybrid_traversal_ms"] = trv["mean"]
         res["selection_plus_traversal_frac_of_prefill"] = (sel["mean"] + trv["mean"]) / t["mean"]
-        res["selection_note"] = ("tm_select_vertical (lists left in device memory), then tm_build_traversal and "
-                                 "tm_gather_selected on those lists: no host copy, no stream wait; event-timed "
+        res["selection_note"] = ("tm_select_vertical (lists left in device memory), then "
+                                 "tm_build_traversal_gather on those lists (tables and gathered rows in one "
+                                 "launch): no host copy, no stream wait; event-timed "
                                  "on the launch stream, enqueued behind a spin kernel so that the device time "
                                  "is measured, not the host's launch pace")
         pol = pol_host
