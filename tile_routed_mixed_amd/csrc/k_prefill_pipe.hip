@@ -219,6 +219,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  // Q operands for a tile of precision is8, loaded only when the operands in
+  // registers are of the other precision: an item's tiles change precision
+  // at most three times, and each load is a memory round trip the first
+  // tiles would otherwise wait for.  (Uniform: the precision comes from the
+  // wave's scalar run entries.)
+  int q_prec = -1;
+  auto need_q = [&](bool is8) {
+    if (q_prec != static_cast<int>(is8)) {
+      load_q(is8);
+      q_prec = static_cast<int>(is8);
+    }
+  };
+
   // ---- softmax state.  The i8 products accumulate onto the bit pattern of
   // 1.5 * 2^23, so a score's int32 bits, read as a float, are exactly
   // 1.5 * 2^23 + product (|product| < 2^21 for INT8 codes and for 16 x INT4
@@ -490,15 +503,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
 
-    // prologue: K(0), V(0), K(1); scores and maxima of tile 0
+    // prologue: K(0), V(0), K(1) and tile 0's Q operands, all in flight
+    // together; scores and maxima of tile 0
     issue_k(e0, 0);
     issue_v(e0, 0);
     if (n > 1) issue_k(e1, 1);
+    need_q((e0 >> 24) == TM_INT8);
     wait_vm(0);
     __syncthreads();
     {
       float tl[QB];
-      load_q((e0 >> 24) == TM_INT8);
       if (n_m > 0) qk_alone(T_{}, c0, e0, tl);
       else qk_alone(F_{}, c0, e0, tl);
       capture(e0, sc[0]);
@@ -536,11 +550,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     int t = 0;
     if (n_m > 0 && n > 1) {   // the masked tiles (at most two)
-      load_q((e1 >> 24) == TM_INT8);
+      need_q((e1 >> 24) == TM_INT8);
       iteration(0, I0{}, T_{}, T_{});
       t = 1;
       if (n_m > 1 && n > 2) {
-        load_q((e1 >> 24) == TM_INT8);
+        need_q((e1 >> 24) == TM_INT8);
         iteration(1, I1{}, T_{}, T_{});
         t = 2;
       }
@@ -550,7 +564,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // iterations (both parities) per trip
     while (t + 1 < n) {
       const uint32_t pr = e1 >> 24;
-      load_q(pr == TM_INT8);
+      need_q(pr == TM_INT8);
       if (t & 1) {
         iteration(t, I1{}, F_{}, F_{});
         ++t;
