@@ -603,19 +603,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   }
 }
 
-// Merge of one query head's split results by log-sum-exp: one wave per head.
-// Splits are taken 16 at a time with every load of a group (their maxima and
-// sums through scalar loads, the lane's output channels through vector loads)
-// in flight together, and folded into a running (max, sum, O) state.
+// Merge of one query head's split results by log-sum-exp: one workgroup of
+// kCombWaves waves per head, wave w folding splits w, w + kCombWaves, ...
+// (a sequence alone on the GPU has hundreds of splits per head, so one wave
+// would wait on each group of loads in turn), then the waves' states merged
+// through LDS.  Splits are taken 16 at a time per wave with every load of a
+// group (their maxima and sums through scalar loads, the lane's output
+// channels through vector loads) in flight together, and folded into a
+// running (max, sum, O) state.
+constexpr int kCombWaves = 4;
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeArgs a) {
   constexpr int PER = D / 64, G = 16;
-  const int bh = blockIdx.x, lane = threadIdx.x, ns = a.nsplit;
+  const int bh = blockIdx.x, lane = threadIdx.x & 63, ns = a.nsplit;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const float* const src = pin_sgpr(a.ws + static_cast<size_t>(bh) * ns * (D + 2));
   float M = kNegBig, lsum = 0.0f, ov[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) ov[p] = 0.0f;
-  for (int c0 = 0; c0 < ns; c0 += G) {
+  for (int c0 = w * G; c0 < ns; c0 += kCombWaves * G) {
     float m[G], l[G], x[G][PER];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
@@ -641,6 +647,30 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
       for (int p = 0; p < PER; ++p) ov[p] += x[u][p] * f;
     }
     M = mn;
+  }
+  // the waves' states, merged by wave 0 (a wave with no split keeps
+  // M = kNegBig and zero sums, which weigh nothing)
+  __shared__ float sm[kCombWaves], sl[kCombWaves], so[kCombWaves][D];
+  if (lane == 0) {
+    sm[w] = M;
+    sl[w] = lsum;
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) so[w][64 * p + lane] = ov[p];
+  __syncthreads();
+  if (w != 0) return;
+  float mx = sm[0];
+#pragma unroll
+  for (int u = 1; u < kCombWaves; ++u) mx = fmaxf(mx, sm[u]);
+  lsum = 0.0f;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) ov[p] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kCombWaves; ++u) {
+    const float f = __builtin_amdgcn_exp2f(sm[u] - mx);
+    lsum += sl[u] * f;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) ov[p] += so[u][64 * p + lane] * f;
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
@@ -677,8 +707,8 @@ hipError_t launch_decode_split(const DecodeArgs& a, int ncls, bool small, int d,
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, int d, hipStream_t st) {
-  if (d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.nseq * a.hq), dim3(64), 0, st, a);
-  else hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.nseq * a.hq), dim3(64), 0, st, a);
+  if (d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.nseq * a.hq), dim3(64 * kCombWaves), 0, st, a);
+  else hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.nseq * a.hq), dim3(64 * kCombWaves), 0, st, a);
   return hipGetLastError();
 }
 
