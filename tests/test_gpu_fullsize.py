@@ -58,10 +58,11 @@ def _sparse_q_codes(q32, seqlens, rows_blocks):
     return out
 
 
-def _full_prefill(name, n_random=24, n_tiles=8):
+def _full_prefill(name, n_random=24, n_tiles=8, pol=None, label=None):
     import tile_routed_mixed_amd as T
     w = W.get(name)
-    pol = W.make_policy(w)
+    pol = W.make_policy(w) if pol is None else pol
+    name = label or name
     say(f"[gpu] full-size {name}: generating inputs")
     q, k, v = W.make_qkv(w)
     tiles = int_tiles(w, pol, limit=n_tiles, seed=1)
@@ -110,6 +111,23 @@ def test_varlen32k_full():
 
 def test_long128k_full():
     _full_prefill("long128k", n_random=40, n_tiles=6)
+
+
+def test_fourway_gqa8k_full():
+    """The four-way policy at the 8K layer's full size: the layer's per-head
+    boundaries with the sink tile, plus a seeded 2-bit code per group of 4 key
+    tiles (0 = the boundary rule with probability 1/2, else INT4, INT8 or FP16
+    uniformly), so every precision and SKIP occur in every long row."""
+    w = W.get("gqa8k")
+    b = W.make_policy(w)
+    rng = np.random.default_rng([w.wid, 40])
+    _, tot = OP.fourway_row_base(w.seqlens, w.hq, w.bq, w.bk, 4)
+    codes = np.where(rng.random((tot, 16)) < 0.5, 0, rng.integers(1, 4, size=(tot, 16))).astype(np.uint64)
+    words = (codes << (2 * np.arange(16, dtype=np.uint64))).sum(axis=1).astype(np.uint32)
+    pol = dict(kind=2, b8=b["b8"], b4=b["b4"], sink=1, group=4, words=words)
+    c = OP.census(OP.grids(w.seqlens, w.hq, w.bq, w.bk, pol))
+    assert min(c["int8"], c["int4"], c["fp16"], c["skip"]) > 0, c
+    _full_prefill("gqa8k", pol=pol, label="gqa8k four-way")
 
 
 def test_decode16x32k_full():
