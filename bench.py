@@ -48,17 +48,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def describe(w, hybrid=None):
+def describe(w, hybrid=None, fourway=False):
     if hybrid is not None:
         pol = (f"hybrid: {hybrid[0] * 100:.0f} % of keys per head selected by the vertical-line pass (attention "
                f"mass from the last 64 rows), {hybrid[1]}-token window in FP16, the rest INT8")
+    elif fourway:
+        pol = ("four-way: per-head diagonal-distance boundaries plus a 2-bit code per group of 4 key tiles "
+               "(0 = the boundaries with probability 1/2, else INT4, INT8 or FP16)")
     elif w.policy == "boundaries":
         pol = "per-head diagonal-distance boundaries"
     else:
         pol = f"packed bitmask, {w.group} key tiles per bit, P(FP16)={w.p_fp16}"
     seqs = w.seqlens if len(w.seqlens) <= 4 else f"{len(w.seqlens)}x{w.seqlens[0]}"
     return (f"{w.name}: seqs {seqs}, {w.hq}/{w.hkv} heads, d={w.d}, {w.dtype}, {w.bq}x{w.bk} tiles, {pol}"
-            + (", key tile 0 INT8" if w.sink and hybrid is None else "")
+            + (", key tile 0 INT8" if (w.sink or fourway) and hybrid is None else "")
             + (f", K outliers {w.outliers}x{w.outlier_scale:g}" if w.outliers else ""))
 
 
@@ -94,16 +97,16 @@ def pmc_traffic(summary, sources):
     return s.get("hbm_bytes_per_launch")
 
 
-def prefill_kernel_of(w, hybrid=False):
+def prefill_kernel_of(w, hybrid=False, fourway=False):
     """The prefill kernel a workload's policy runs, and its source files:
     boundary policies run the software-pipelined kernel, the other kinds
     (bitmask, four-way, hybrid) prefill_kernel."""
-    if w.policy == "boundaries" and not hybrid:
+    if w.policy == "boundaries" and not hybrid and not fourway:
         return "prefill_pipe_kernel", ("k_prefill_pipe.hip", "k_prefill_common.h")
     return "prefill_kernel", ("k_prefill.hip", "k_prefill_common.h")
 
 
-def prefill_roofline(w, census, t_ms, traffic=None, hybrid=False):
+def prefill_roofline(w, census, t_ms, traffic=None, hybrid=False, fourway=False):
     """Roofline of the prefill kernel: executed ops (both contractions of every
     executed tile, masked elements included) over the measured launch time,
     against the precision-weighted MFMA peak of this workload's tiles (INT8
@@ -116,7 +119,7 @@ def prefill_roofline(w, census, t_ms, traffic=None, hybrid=False):
     achieved = ops / (t_ms * 1e-3) / 1e12
     peak = ops / t_peak / 1e12
     return {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-            "traffic": traffic, "kernel": prefill_kernel_of(w, hybrid)[0], "ops_per_launch": ops,
+            "traffic": traffic, "kernel": prefill_kernel_of(w, hybrid, fourway)[0], "ops_per_launch": ops,
             "peak_note": "precision-weighted: INT8/INT4 QK at 5.0 POP/s, FP16 QK and every PV at 2.5 PFLOP/s, "
                          "over the executed tiles of this workload"}
 
@@ -198,19 +201,22 @@ def prefill_fp64_error(w, pol, pp, q, k, v, n_rows):
 
 # ----------------------------------------------------------------------------- prefill lines
 
-def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48):
+def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48, fourway=False):
     """Prefill alone on one workload: time per launch (HIP events on the
     launch stream), effective dense-causal rate, roofline against the
     precision-weighted MFMA peak of its executed tiles, and its error against
     unquantized attention.  hybrid = (fraction selected, window): the
     workload's shape under the token-granular policy, with the selected keys
-    picked on the GPU by the vertical-line pass (tm_select_vertical)."""
+    picked on the GPU by the vertical-line pass (tm_select_vertical).
+    fourway: the workload's boundaries plus seeded 2-bit group codes."""
     import torch
     import tile_routed_mixed_amd as T
     import workloads as W
     w = W.get(name)
     q, k, v = W.make_qkv(w)
     pol = W.make_policy(w) if hybrid is None else W.make_selection(w, hybrid[0], hybrid[1])
+    if fourway:
+        pol = W.make_fourway_policy(w)
     pp = T.PrefillPipeline(w.seqlens, w.hq, w.hkv, w.d, w.bq, w.dtype, pol)
     pp.upload(q[0], k[0], v[0])
     pp.quantize()
@@ -236,9 +242,10 @@ def prefill_line(name, steps=10, warmup=2, hybrid=None, fp64_rows=48):
     torch.cuda.synchronize()
     t = stats(events_ms(lambda: pp.prefill(o_dtype), steps))
     roof = prefill_roofline(w, census, t["mean"],
-                            pmc_traffic(f"prefill_{name}_pmc.json", prefill_kernel_of(w)[1]) if hybrid is None else None,
-                            hybrid=hybrid is not None)
-    res = {"workload": describe(w, hybrid), "prefill_ms": t["mean"], "prefill_ms_median": t["median"],
+                            pmc_traffic(f"prefill_{name}_pmc.json", prefill_kernel_of(w)[1])
+                            if hybrid is None and not fourway else None,
+                            hybrid=hybrid is not None, fourway=fourway)
+    res = {"workload": describe(w, hybrid, fourway), "prefill_ms": t["mean"], "prefill_ms_median": t["median"],
            "prefill_ms_min": t["min"],
            "effective_tflops_dense_causal": dense_causal_flops(w) / (t["mean"] * 1e-3) / 1e12,
            "roofline": roof, "census": census}
@@ -283,21 +290,45 @@ def decode_block_counts(L, b8, b4, sink, tail):
 def decode_bytes(w, dpol, d):
     """Algorithmic bytes of one decode step: codes and the two scales of every
     INT block read (K and V), 16-bit K and V^T of every FP16 block, per
-    (sequence, KV head); q and o are negligible."""
+    (sequence, KV head); q and o are negligible.  Per-query-head maps: a
+    (sequence, KV head) reads each block once at every precision some query
+    head of its group needs it in (the distinct (block, precision) pairs)."""
     per = {"int8": 64 * d * 2 + 8, "int4": 64 * d + 8, "fp16": 64 * d * 2 * 2, "skip": 0}
     counts = {"int8": 0, "int4": 0, "fp16": 0, "skip": 0}
+    grp = w.hq // w.hkv
     for L in w.seqlens:
         for g in range(w.hkv):
-            for t, n in decode_block_counts(L, int(dpol["b8"][g]), int(dpol["b4"][g]), dpol["sink"],
-                                            dpol["tail"]).items():
-                counts[t] += n
+            if not dpol.get("per_q_head", 0):
+                for t, n in decode_block_counts(L, int(dpol["b8"][g]), int(dpol["b4"][g]), dpol["sink"],
+                                                dpol["tail"]).items():
+                    counts[t] += n
+                continue
+            # (b8, b4) bands of the group's heads: a block is INT8 for some head
+            # if its distance is below the largest b8, INT4 for some head if it
+            # lies in [b8_h, b4_h) for one of them
+            maps = [(int(dpol["b8"][h]), int(dpol["b4"][h])) for h in range(g * grp, (g + 1) * grp)]
+            nb = -(-L // 64)
+            last = (L - 1) // 64
+            first_tail = max(0, (L - dpol["tail"]) // 64) if dpol["tail"] > 0 else nb
+            counts["fp16"] += nb - first_tail
+            for j in range(first_tail):
+                if dpol["sink"] and j == 0:
+                    counts["int8"] += 1
+                    continue
+                dl = last - j
+                i8 = any(dl < b8 for b8, _ in maps)
+                i4 = any(b8 <= dl < b4 for b8, b4 in maps)
+                counts["int8"] += int(i8)
+                counts["int4"] += int(i4)
+                counts["skip"] += int(not i8 and not i4)
     return sum(per[t] * n for t, n in counts.items()), counts
 
 
-def decode_bench(steps, rotate=3, select_frac=None, tags=None, fp64_pairs=0):
+def decode_bench(steps, rotate=3, select_frac=None, tags=None, fp64_pairs=0, per_q_head=False):
     """Decode over a 16 x 32768-token compressed cache; returns timing, bytes
     and the HBM roofline.  select_frac: that fraction of every (sequence, KV
-    head)'s tokens (seeded) is kept in FP16 as selected tokens."""
+    head)'s tokens (seeded) is kept in FP16 as selected tokens.  per_q_head:
+    every query head with its own seeded (b8, b4) around the workload's."""
     import numpy as np
     import torch
     import tile_routed_mixed_amd as T
@@ -306,6 +337,8 @@ def decode_bench(steps, rotate=3, select_frac=None, tags=None, fp64_pairs=0):
     dpol = W.make_decode_policy(w)
     if tags is not None:   # another reading of the cache tags: (b8, b4) in blocks
         dpol = dict(dpol, b8=np.full(w.hkv, tags[0], np.int32), b4=np.full(w.hkv, tags[1], np.int32))
+    if per_q_head:
+        dpol = W.make_decode_policy_per_q_head(w)
     _, k, v = W.make_qkv(w)
     dq = W.make_decode_query(w)
     caches = []
@@ -341,11 +374,15 @@ def decode_bench(steps, rotate=3, select_frac=None, tags=None, fp64_pairs=0):
     b8t, b4t = int(dpol["b8"][0]), int(dpol["b4"][0])
     desc = describe(w) + f", cache tags (b8, b4) = ({b8t}, {b4t if b4t < 1 << 20 else 'never'}) blocks, " \
                          f"last 128 tokens FP16"
+    if per_q_head:
+        desc = describe(w) + (f", per-query-head cache tags: b8 {int(dpol['b8'].min())}-{int(dpol['b8'].max())}, "
+                              f"b4 {int(dpol['b4'].min())}-{int(dpol['b4'].max())} blocks (seeded per head), "
+                              f"last 128 tokens FP16; bytes count each (block, precision) a KV group needs once")
     if select_frac is not None:
         desc += f", {select_frac * 100:g} % of tokens per (sequence, KV head) selected and read in FP16 ({n_sel} in all)"
     gbs = nbytes / (mean * 1e-3) / 1e9
     traffic = pmc_traffic("decode16x32k_pmc.json", ("k_decode.hip",)) \
-        if (select_frac is None and tags is None) else None
+        if (select_frac is None and tags is None and not per_q_head) else None
     res = {"workload": desc, "bytes_per_step": nbytes, "ms_mean": mean, "ms_median_single": single["median"],
            "ms_min_single": single["min"], "GBps": gbs, "hbm_frac": gbs * 1e9 / PEAK_HBM,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
@@ -396,7 +433,11 @@ def decode_loop_bench(steps=64):
     """Generation loop over the 16 x 32768-token workload: the caches start
     `steps` tokens short of 32768 and every step decodes one query per
     sequence, then appends that step's token (tm_cache_append for K and V,
-    the new rows already in device memory).  Returns time per step."""
+    the new rows already in device memory).  Returns time per step twice:
+    device-paced (the steps enqueued behind a spin kernel, so they run back
+    to back on the GPU whatever the host's launch pace) and host-paced (the
+    loop as the host drives it, launch cost included)."""
+    import time as _time
     import numpy as np
     import torch
     import tile_routed_mixed_amd as T
@@ -410,22 +451,41 @@ def decode_loop_bench(steps=64):
     p.upload(dq[0], k[0], v[0])
     del k, v
     L0 = np.array(w.seqlens, np.int64) - steps
-    p.start(L0)
-    torch.cuda.synchronize()
     lens = [L0 + i for i in range(steps + 1)]
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(steps):
-        p.decode()
-        p.dpol.set_lengths(lens[i + 1])
-        B.tm_cache_append(p.shape, lens[i + 1], p.k, p.kq)
-        B.tm_cache_append(p.shape, lens[i + 1], p.v, p.vq)
-    ev1.record()
+
+    def run(spin_cycles):
+        p.start(L0)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if spin_cycles:
+            torch.cuda._sleep(spin_cycles)
+        t0 = _time.perf_counter()
+        ev0.record()
+        for i in range(steps):
+            p.decode()
+            p.dpol.set_lengths(lens[i + 1])
+            B.tm_cache_append(p.shape, lens[i + 1], p.k, p.kq)
+            B.tm_cache_append(p.shape, lens[i + 1], p.v, p.vq)
+        ev1.record()
+        t_enq = _time.perf_counter() - t0
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps, t_enq
+
+    host_ms, t_enq = run(0)
+    # spin length: the spin kernel's rate measured once, then enough cycles to
+    # cover twice the host's enqueue time of the loop
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1_000_000)
+    e1.record()
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
+    cyc_per_ms = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    dev_ms, _ = run(int(min(2.0 * t_enq * 1e3 * cyc_per_ms, 2e9)))
     return {"workload": "decode16x32k generation loop: decode + K/V cache append per step, lengths "
-                        f"{int(L0[0])} -> {int(lens[-1][0])}", "steps": steps, "ms_per_step": ms,
-            "tokens_per_s": len(w.seqlens) / (ms * 1e-3)}
+                        f"{int(L0[0])} -> {int(lens[-1][0])}", "steps": steps, "ms_per_step": dev_ms,
+            "tokens_per_s": len(w.seqlens) / (dev_ms * 1e-3), "ms_per_step_host_paced": host_ms,
+            "note": "ms_per_step: the steps enqueued behind a spin kernel and run back to back on the GPU; "
+                    "ms_per_step_host_paced: the same loop at the host's launch pace"}
 
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
@@ -515,6 +575,8 @@ def main():
     ap.add_argument("--hybrid", type=float, default=None, metavar="FRAC",
                     help="with --prefill-only: the hybrid policy with FRAC of the keys selected by the "
                          "vertical-line pass and a 128-token window")
+    ap.add_argument("--fourway", action="store_true",
+                    help="with --prefill-only: the workload's boundaries plus seeded four-way group codes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain elementwise copy of BYTES bytes (read BYTES, write BYTES) 5 times, "
                          "to scale HBM byte counters; prints nothing else")
@@ -540,7 +602,7 @@ def main():
     if args.prefill_only:
         hyb = None if args.hybrid is None else (args.hybrid, 128)
         print(json.dumps(prefill_line(args.prefill_only, steps=max(3, args.steps), warmup=args.warmup,
-                                      hybrid=hyb, fp64_rows=8)), flush=True)
+                                      hybrid=hyb, fp64_rows=8, fourway=args.fourway)), flush=True)
         return
 
     import torch
@@ -632,6 +694,9 @@ def main():
         ds = decode_bench(max(20, args.steps), select_frac=0.05)
         out["decode_selected"] = ds
         log(f"[bench] decode with 5 % selected tokens {ds['ms_mean']:.4f} ms, {ds['GBps']:.1f} GB/s")
+        dq_ = decode_bench(max(20, args.steps), per_q_head=True)
+        out["decode_per_query_head"] = dq_
+        log(f"[bench] decode with per-query-head maps {dq_['ms_mean']:.4f} ms, {dq_['GBps']:.1f} GB/s")
         out["decode_tag_variants"] = []
         for tg in ((2, 5), (128, 1 << 30)):   # the literal toy bands; no skipped block
             dv = decode_bench(max(20, args.steps), tags=tg)
@@ -644,18 +709,19 @@ def main():
             f"{dl['tokens_per_s']:.0f} tokens/s")
     if not args.no_other_configs:
         out["other_configs"] = []
-        for name, hyb in (("toy512", None), ("gqa8k", None), ("varlen32k", None), ("gqa8k", (0.05, 128))):
-            if name == w.name and hyb is None:
+        for name, hyb, fw in (("toy512", None, False), ("gqa8k", None, False), ("varlen32k", None, False),
+                              ("gqa8k", (0.05, 128), False), ("gqa8k", None, True)):
+            if name == w.name and hyb is None and not fw:
                 continue
-            r = prefill_line(name, hybrid=hyb, fp64_rows=0 if args.no_fp64_error else 48)
+            r = prefill_line(name, hybrid=hyb, fp64_rows=0 if args.no_fp64_error else 48, fourway=fw)
             out["other_configs"].append(r)
-            log(f"[bench] {name}{' hybrid' if hyb else ''}: prefill {r['prefill_ms']:.4f} ms, "
+            log(f"[bench] {name}{' hybrid' if hyb else ''}{' four-way' if fw else ''}: prefill {r['prefill_ms']:.4f} ms, "
                 f"{r['effective_tflops_dense_causal']:.1f} TFLOP/s dense-causal, "
                 f"{r['roofline']['frac'] * 100:.1f} % of the weighted MFMA peak"
                 + (f"; selection {r['selection_ms']:.4f} ms + traversal {r['hybrid_traversal_ms']:.4f} ms = "
                    f"{r['selection_plus_traversal_frac_of_prefill'] * 100:.1f} % of the prefill" if hyb else ""))
             if "fp64_error" in r and "fp64_error" in out:
-                out["fp64_error"][name + ("_hybrid" if hyb else "")] = r["fp64_error"]
+                out["fp64_error"][name + ("_hybrid" if hyb else "") + ("_fourway" if fw else "")] = r["fp64_error"]
     if not args.no_ceiling:
         out["ceilings"] = ceilings()
     if not args.no_cpu_baseline:

@@ -119,12 +119,7 @@ def test_fourway_gqa8k_full():
     tiles (0 = the boundary rule with probability 1/2, else INT4, INT8 or FP16
     uniformly), so every precision and SKIP occur in every long row."""
     w = W.get("gqa8k")
-    b = W.make_policy(w)
-    rng = np.random.default_rng([w.wid, 40])
-    _, tot = OP.fourway_row_base(w.seqlens, w.hq, w.bq, w.bk, 4)
-    codes = np.where(rng.random((tot, 16)) < 0.5, 0, rng.integers(1, 4, size=(tot, 16))).astype(np.uint64)
-    words = (codes << (2 * np.arange(16, dtype=np.uint64))).sum(axis=1).astype(np.uint32)
-    pol = dict(kind=2, b8=b["b8"], b4=b["b4"], sink=1, group=4, words=words)
+    pol = W.make_fourway_policy(w)
     c = OP.census(OP.grids(w.seqlens, w.hq, w.bq, w.bk, pol))
     assert min(c["int8"], c["int4"], c["fp16"], c["skip"]) > 0, c
     _full_prefill("gqa8k", pol=pol, label="gqa8k four-way")

@@ -43,6 +43,7 @@ import numpy as np
 WORKLOAD_IDS = {"toy512": 1, "gqa8k": 2, "varlen32k": 3, "long128k": 4, "decode16x32k": 5, "local8k": 6}
 STREAM_Q, STREAM_K, STREAM_V, STREAM_POLICY, STREAM_OUTLIER, STREAM_DQ, STREAM_LOCAL, STREAM_SEL = 1, 2, 3, 4, 5, 6, 7, 8
 STREAM_DSEL = 9
+STREAM_FOURWAY, STREAM_QMAPS = 10, 11
 
 
 @dataclasses.dataclass
@@ -222,10 +223,49 @@ def make_policy(w: Workload):
     return dict(kind=1, group=w.group, words=np.concatenate(words).astype(np.uint32))
 
 
+def make_fourway_policy(w: Workload, p_zero: float = 0.5, group: int = 4):
+    """Four-way policy input: the workload's boundary policy (per-head b8, b4)
+    with the sink tile, plus per (sequence, query head, query tile) a row of
+    2-bit codes, one per group of `group` key tiles, 16 per uint32 word (LSB
+    first): 0 with probability p_zero, else 1, 2 or 3 uniformly.
+    dict(kind=2, b8, b4, sink, group, words)."""
+    b = make_policy(w)
+    assert b["kind"] == 0, "the four-way draw starts from a boundary workload"
+    rng = np.random.default_rng([w.wid, STREAM_FOURWAY])
+    words = []
+    for S in w.seqlens:
+        nq = -(-S // w.bq)
+        nk = -(-S // w.bk)
+        ng = -(-nk // group)
+        nw = -(-ng // 16)
+        codes = np.where(rng.random((w.hq, nq, nw * 16)) < p_zero, 0,
+                         rng.integers(1, 4, size=(w.hq, nq, nw * 16))).astype(np.uint64)
+        codes[:, :, ng:] = 0
+        packed = np.zeros((w.hq, nq, nw), dtype=np.uint64)
+        for c in range(16):
+            packed |= codes[:, :, c::16] << np.uint64(2 * c)
+        words.append(packed.astype(np.uint32).reshape(-1))
+    return dict(kind=2, b8=b["b8"], b4=b["b4"], sink=1, group=group,
+                words=np.concatenate(words).astype(np.uint32))
+
+
 def make_decode_policy(w: Workload):
     """Decode cache tags: per KV head (b8, b4) in 64-token blocks, sink, FP16 tail."""
     return dict(b8=np.full(w.hkv, w.dec_b8, np.int32), b4=np.full(w.hkv, w.dec_b4, np.int32),
                 sink=int(w.sink), tail=int(w.dec_tail))
+
+
+def make_decode_policy_per_q_head(w: Workload, d8: int = 32, d4: int = 64):
+    """Per-query-head decode cache tags: every query head draws its own
+    (b8, b4) around the workload's, b8 + U_int[-d8, d8] and b4 + U_int[-d4, d4]
+    (in 64-token blocks), so the query heads of a KV head read different block
+    sets.  dict(b8 [hq], b4 [hq], sink, tail, per_q_head=1)."""
+    rng = np.random.default_rng([w.wid, STREAM_QMAPS])
+    b8 = (w.dec_b8 + rng.integers(-d8, d8 + 1, size=w.hq)).astype(np.int32)
+    b4 = (w.dec_b4 + rng.integers(-d4, d4 + 1, size=w.hq)).astype(np.int32)
+    b8 = np.maximum(b8, 0)
+    b4 = np.maximum(b4, b8)
+    return dict(b8=b8, b4=b4, sink=int(w.sink), tail=int(w.dec_tail), per_q_head=1)
 
 
 def make_selection(w: Workload, frac: float, window: int, stream_offset: int = 0):
