@@ -355,9 +355,16 @@ def test_decode_per_query_head_maps_validation_and_workspace(B):
     # maps that agree inside every group: one class per KV head, the per-KV workspace
     same = B.DPolicy(dict(b8=[128] * 32, b4=[320] * 32, sink=1, tail=128, per_q_head=1))
     assert size(same) == B.TM_OK and n.value == 16 * 32 * 16 * 130 * 4
-    # all maps distinct: 32 classes -> 16 x 32 pairs -> 4 splits
+    # all maps distinct: one class per KV head over the union of its heads'
+    # bands, so the per-KV split count and workspace
     mixed = B.DPolicy(dict(b8=list(range(100, 132)), b4=[400] * 32, sink=1, tail=128, per_q_head=1))
-    assert size(mixed) == B.TM_OK and n.value == 16 * 32 * 4 * 130 * 4
+    assert size(mixed) == B.TM_OK and n.value == 16 * 32 * 16 * 130 * 4
+    # more query heads than the kernel arguments hold maps for: the groups are
+    # cut into runs of equal maps (128 classes -> 16 x 128 pairs -> 1 split)
+    s128 = _shape(B, [32768] * 16, hq=128, hkv=8, d=128)
+    many = B.DPolicy(dict(b8=[100 + h % 7 for h in range(128)], b4=[400] * 128, sink=1, tail=128, per_q_head=1))
+    assert L.tm_decode(ctypes.byref(s128.c), None, None, None, None, ctypes.byref(many.c), None, 2, None,
+                       ctypes.byref(n), None) == B.TM_OK and n.value == 16 * 128 * 1 * 130 * 4
     # the query-head maps are all checked (head 20 is past the 8 KV heads)
     bad = B.DPolicy(dict(b8=[1] * 20 + [9] + [1] * 11, b4=[4] * 32, sink=1, tail=128, per_q_head=1))
     assert size(bad) == B.TM_E_POLICY

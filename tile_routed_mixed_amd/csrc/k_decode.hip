@@ -142,7 +142,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int split = blockIdx.x, cl = blockIdx.y, b = blockIdx.z;
   // head class: grp consecutive query heads from h0, all reading KV head kv
   const int cls = a.cls[cl];
-  const int kv = cls & 1023, h0 = (cls >> 10) & 1023, grp = cls >> 20;
+  const int kv = cls & 1023, h0 = (cls >> 10) & 1023, grp = (cls >> 20) & 1023;
+  const bool uni = (cls >> 30) & 1;   // the KV head's whole group, one map per query head
 
   // this sequence's extent (kernel-argument tables: scalar loads)
   const int tok0 = a.cu[b];
@@ -154,14 +155,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int jst = min(max(0, nb - a.b4[cl]), jf);                    // delta < b4 from here
   const int j8lo = min(max(jst, nb - a.b8[cl]), jf);                 // INT8 band [j8lo, jf)
   const bool sinkb = a.sink && j8lo > 0;                             // block 0 INT8, ahead of the bands
-  const int j4lo = (sinkb && jst == 0) ? 1 : jst;                    // INT4 band [j4lo, j8lo)
+  const int j4lo = (sinkb && jst == 0) ? 1 : jst;                    // INT4 band [j4lo, j4hi)
+  // (a group of query heads with their own maps: the union of their bands,
+  // INT4 up to the last head's INT8 band start, each block read once at each
+  // precision some head needs; every lane then drops the blocks outside its
+  // own head's bands)
+  const int j4hi = uni ? min(max(jst, nb - a.b8min[cl]), jf) : j8lo;
+  int lj4lo = 0, lj8lo = 0;
+  if (uni) {
+    const int col = SMALLG ? (l16 & 3) : l16;   // this lane's query head (column) in the class
+    const int hl = h0 + min(col, grp - 1);
+    const int lst = min(max(0, nb - a.hb4[hl]), jf);
+    lj8lo = min(max(lst, nb - a.hb8[hl]), jf);
+    lj4lo = (a.sink && lj8lo > 0 && lst == 0) ? 1 : lst;
+  }
   // Each split takes an even share of the INT4 band and an even share of the
   // rest ([j8lo, nb): the INT8 band, then the FP16 window, whose blocks count
   // as kW16 INT8 blocks: twice the bytes, read without look-ahead), so every
   // split carries the same mix of work; split 0 also takes the sink.
   constexpr int kW16 = 3;
   const int ns = a.nsplit;
-  const int i4a = j4lo + (j8lo - j4lo) * split / ns, i4b = j4lo + (j8lo - j4lo) * (split + 1) / ns;
+  const int i4a = j4lo + (j4hi - j4lo) * split / ns, i4b = j4lo + (j4hi - j4lo) * (split + 1) / ns;
   const int n8 = jf - j8lo, wt = n8 + kW16 * (nb - jf);
   auto tail_at = [&](int s) {   // first tail entry of split s: INT8 entries [0, n8), then FP16
     const int t = wt * s / ns;
@@ -435,9 +449,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     }
     // score = tau log2e sk (2^24 acc - off sum(q)), off = 128 (INT8) or 8 (INT4)
     const float cs = a.tau_log2e * r.sk[bb];
+    // (a union group: a block outside this lane's head's band at this
+    // precision drops all its keys)
+    int klim = L;
+    if (uni && !(four ? (j >= lj4lo && j < lj8lo) : (j >= lj8lo || (a.sink && j == 0)))) klim = j * kBlock;
     f16x8 pb[2];
-    softmax(acc, cs * kTwo24, -(four ? 8.0f : 128.0f) * qsum * cs, r.sv[bb], j * kBlock, L, SEL ? r.xm[bb] : 0ull,
-            pb);
+    softmax(acc, cs * kTwo24, -(four ? 8.0f : 128.0f) * qsum * cs, r.sv[bb], j * kBlock, klim,
+            SEL ? r.xm[bb] : 0ull, pb);
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll

@@ -179,19 +179,46 @@ struct DecodePlan {
 // maps are per KV head, or when a group's per-query-head maps all agree).
 struct HeadClass {
   int kv, h0, n, b8, b4;
+  bool uni = false;   // a whole group with per-query-head maps (b8, b4 its largest)
+  int b8min = 0;      // the group's smallest b8 (uni)
 };
 
+// A KV head whose query heads do not all share one map becomes one class
+// over its whole group (uni): one wave per split reads the union of the
+// heads' bands, each (block, precision) once, and every head drops the blocks
+// outside its own bands.  (Beyond kMaxHeadArg query heads the maps do not fit
+// the kernel arguments, and such a group is cut into runs of equal maps,
+// each read on its own.)
 std::vector<HeadClass> head_classes(const tm_shape* s, const tm_dpolicy* p) {
   std::vector<HeadClass> out;
   const int grp = s->hq / s->hkv;
   for (int kv = 0; kv < s->hkv; ++kv) {
+    if (p->per_q_head && s->hq <= kMaxHeadArg) {
+      int lo8 = INT_MAX, hi8 = 0, hi4 = 0;
+      bool same = true;
+      for (int h = kv * grp; h < (kv + 1) * grp; ++h) {
+        lo8 = std::min(lo8, p->b8[h]);
+        hi8 = std::max(hi8, p->b8[h]);
+        hi4 = std::max(hi4, p->b4[h]);
+        same = same && p->b8[h] == p->b8[kv * grp] && p->b4[h] == p->b4[kv * grp];
+      }
+      if (!same) {
+        HeadClass c{kv, kv * grp, grp, hi8, hi4};
+        c.uni = true;
+        c.b8min = lo8;
+        out.push_back(c);
+        continue;
+      }
+    }
     for (int r = 0; r < grp;) {
       const int h = kv * grp + r;
       const int mi = p->per_q_head ? h : kv;
       int n = 1;
       while (r + n < grp && p->per_q_head && p->b8[h + n] == p->b8[h] && p->b4[h + n] == p->b4[h]) ++n;
       if (!p->per_q_head) n = grp;
-      out.push_back(HeadClass{kv, h, n, p->b8[mi], p->b4[mi]});
+      HeadClass c{kv, h, n, p->b8[mi], p->b4[mi]};
+      c.b8min = c.b8;
+      out.push_back(c);
       r += n;
     }
   }
@@ -804,6 +831,11 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
   a.tail = policy->tail_tokens;
   a.nblk = si.nblk;
   a.tau_log2e = tau_log2e(cache);
+  if (policy->per_q_head && cache->hq <= kMaxHeadArg)   // each query head's map, for union classes
+    for (int h = 0; h < cache->hq; ++h) {
+      a.hb8[h] = policy->b8[h];
+      a.hb4[h] = policy->b4[h];
+    }
   if (policy->sel_off != nullptr) {
     a.sel = static_cast<const uint8_t*>(policy->sel_buf);
     a.sel_tab = static_cast<uint32_t>(ds.tab_off);
@@ -837,9 +869,10 @@ tm_status tm_decode(const tm_shape* cache, const void* q, const tm_qtensor* kq, 
       const int nc = static_cast<int>(std::min<size_t>(kMaxClsArg, cls.size() - c0));
       for (int i = 0; i < nc; ++i) {
         const HeadClass& h = cls[c0 + i];
-        c.cls[i] = h.kv | (h.h0 << 10) | (h.n << 20);
+        c.cls[i] = h.kv | (h.h0 << 10) | (h.n << 20) | (static_cast<int32_t>(h.uni) << 30);
         c.b8[i] = h.b8;
         c.b4[i] = h.b4;
+        c.b8min[i] = h.b8min;
       }
       if (launch_decode_split(c, nc, small, cache->d, cache->dtype == TM_BF16, static_cast<hipStream_t>(stream)) !=
           hipSuccess)

@@ -9,6 +9,7 @@ constexpr int kMaxHeadsArg = 256;   // boundary tables passed by value
 constexpr int kMaxKvArg = 64;
 constexpr int kMaxClsArg = 64;     // decode head classes per launch (tables passed by value)
 constexpr int kMaxSeqArg = 128;    // sequences per decode launch (tables passed by value)
+constexpr int kMaxHeadArg = 64;    // query heads whose decode maps travel in the kernel arguments
 
 struct QuantArgs {
   const uint16_t* x;
@@ -136,10 +137,16 @@ struct DecodeArgs {
   float tau_log2e;
   // head classes: class c (grid y) is `n` consecutive query heads from h0,
   // all of KV head kv, with one cache map (b8[c], b4[c]);
-  // cls[c] = kv | h0 << 10 | n << 20
+  // cls[c] = kv | h0 << 10 | n << 20 | uni << 30.  uni: the class holds the
+  // whole group of a KV head whose query heads have different maps (hb8,
+  // hb4 per query head); b8[c], b4[c] are then the group's largest and
+  // b8min[c] its smallest b8
   int32_t cls[kMaxClsArg];
   int32_t b8[kMaxClsArg];
   int32_t b4[kMaxClsArg];
+  int32_t b8min[kMaxClsArg];
+  int32_t hb8[kMaxHeadArg];
+  int32_t hb4[kMaxHeadArg];
   // selected tokens (kept in FP16): buffer written by tm_decode_select, or
   // null; list entries {first gathered tile, keys} per (sequence, KV head),
   // column masks [nblk][hkv] u64, gathered K rows and V^T (byte offsets)
